@@ -1,0 +1,207 @@
+"""Seeded synthetic inputs for C = A.B, shared by the HIP path's tests/bench and the oracle.
+
+This module holds no GEMM arithmetic.  It only draws operand values, rounds them to
+bf16 bit patterns where a workload asks for bf16 inputs, and lays a logical matrix
+out in memory per (order, leading dimension).  Both sides of a parity test read the
+very same buffers it returns.
+
+Value recipes follow the pages' workloads:
+  * square, ragged and skinny shapes use i.i.d. uniform[-1, 1] entries;
+  * the LLM linear-layer shapes (the LLaMA-2-7B forward cited in "GEMM Optimization",
+    section "1. Why GEMM Matters"; hidden 4096, FFN 11008, 2K tokens) use activations
+    ~ N(0, 1) and weights ~ N(0, 0.02) (0.02 read as the standard deviation).
+No dataset or trained weights stand behind any of them: the values are synthetic.
+
+bf16 rounding is round-to-nearest-even of the fp32 value, done once here on the host.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+ROW_MAJOR = 0
+COL_MAJOR = 1
+
+
+@dataclass(frozen=True)
+class Workload:
+    """A GEMM problem: shape, input dtype, operand orders and value recipe."""
+    name: str
+    wid: int                 # small integer mixed into every seed
+    M: int
+    N: int
+    K: int
+    dtype: str               # "f32" or "bf16" (inputs); C is always fp32
+    order_a: int = ROW_MAJOR
+    order_b: int = ROW_MAJOR
+    order_c: int = ROW_MAJOR
+    dist: str = "uniform"    # "uniform" -> U[-1,1]; "llm" -> A~N(0,1), B~N(0,0.02)
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+# The workloads the pages' measurements are about (all synthetic).
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("square256_f32", 1, 256, 256, 256, "f32"),
+        Workload("probe16_f32", 1, 16, 16, 16, "f32"),
+        Workload("square4096_f32", 2, 4096, 4096, 4096, "f32"),
+        Workload("square4096_bf16", 3, 4096, 4096, 4096, "bf16", ROW_MAJOR, COL_MAJOR),
+        Workload("ragged1000_f32", 4, 1000, 1000, 1000, "f32"),
+        Workload("ragged1000_bf16", 4, 1000, 1000, 1000, "bf16", ROW_MAJOR, COL_MAJOR),
+        Workload("ragged4095x4097x1023_f32", 4, 4095, 4097, 1023, "f32"),
+        Workload("ragged4095x4097x1023_bf16", 4, 4095, 4097, 1023, "bf16", ROW_MAJOR, COL_MAJOR),
+        Workload("skinny16x4096x4096_f32", 4, 16, 4096, 4096, "f32"),
+        Workload("skinny16x4096x4096_bf16", 4, 16, 4096, 4096, "bf16", ROW_MAJOR, COL_MAJOR),
+        Workload("llm_attn_proj_2048x4096x4096", 5, 2048, 4096, 4096, "bf16", ROW_MAJOR, COL_MAJOR, ROW_MAJOR, "llm"),
+        Workload("llm_ffn_up_2048x11008x4096", 5, 2048, 11008, 4096, "bf16", ROW_MAJOR, COL_MAJOR, ROW_MAJOR, "llm"),
+        Workload("llm_ffn_down_2048x4096x11008", 5, 2048, 4096, 11008, "bf16", ROW_MAJOR, COL_MAJOR, ROW_MAJOR, "llm"),
+    ]
+}
+
+
+def rng_for(wid: int, M: int, N: int, K: int, operand: int, extra: int = 0) -> np.random.Generator:
+    """PCG64 stream for one operand (0 = A, 1 = B) of one problem."""
+    return np.random.default_rng([wid, M, N, K, operand, extra])
+
+
+def draw(rng: np.random.Generator, rows: int, cols: int, dist: str, operand: int) -> np.ndarray:
+    """Logical rows x cols fp32 matrix (row-major in logical order)."""
+    if dist == "uniform":
+        x = rng.uniform(-1.0, 1.0, (rows, cols))
+    elif dist == "llm":
+        sigma = 1.0 if operand == 0 else 0.02
+        x = rng.standard_normal((rows, cols)) * sigma
+    elif dist == "unit":          # [0, 1): the teaching module's lab inputs
+        x = rng.uniform(0.0, 1.0, (rows, cols))
+    else:
+        raise ValueError(f"unknown distribution {dist!r}")
+    return x.astype(np.float32)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (round to nearest, ties to even); returns uint16 bit patterns.
+
+    NaN stays NaN (quiet); finite values that round past the largest bf16 become inf,
+    as IEEE rounding prescribes.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    rounded = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    if nan.any():
+        rounded = rounded.copy()
+        rounded[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+    return rounded
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to fp32."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def lay_out(logical: np.ndarray, order: int, ld: int | None = None) -> tuple[np.ndarray, int]:
+    """Place a logical R x C matrix in a flat buffer with the given order and leading dim.
+
+    Row-major: element (r, c) at r*ld + c, ld >= C.  Column-major: at r + c*ld, ld >= R.
+    Padding slots (ld beyond the minimum) hold a sentinel so that a kernel reading them
+    produces visibly wrong results.  Returns (flat buffer, ld).
+    """
+    R, C = logical.shape
+    if order == ROW_MAJOR:
+        ld = C if ld is None else ld
+        assert ld >= max(1, C)
+        buf = np.full((max(R, 0), ld), _sentinel(logical.dtype), dtype=logical.dtype)
+        buf[:, :C] = logical
+        flat = buf.reshape(-1)
+    else:
+        ld = R if ld is None else ld
+        assert ld >= max(1, R)
+        buf = np.full((max(C, 0), ld), _sentinel(logical.dtype), dtype=logical.dtype)
+        buf[:, :R] = logical.T
+        flat = buf.reshape(-1)
+    if flat.size == 0:
+        flat = np.zeros(1, dtype=logical.dtype)   # never read; keeps pointers non-null
+    return flat, ld
+
+
+def _sentinel(dtype) -> object:
+    if dtype == np.uint16:
+        return np.uint16(0x7FC1)     # a bf16 NaN
+    return np.float32(np.nan)
+
+
+@dataclass
+class Problem:
+    """One seeded problem: logical operands plus their laid-out buffers."""
+    M: int
+    N: int
+    K: int
+    dtype: str
+    order_a: int
+    order_b: int
+    order_c: int
+    A_logical: np.ndarray    # fp32 (M, K) or uint16 bf16 bits (M, K)
+    B_logical: np.ndarray
+    A: np.ndarray            # flat buffer
+    lda: int
+    B: np.ndarray
+    ldb: int
+    ldc: int
+
+    def a_f32(self) -> np.ndarray:
+        return bf16_bits_to_f32(self.A_logical) if self.dtype == "bf16" else self.A_logical
+
+    def b_f32(self) -> np.ndarray:
+        return bf16_bits_to_f32(self.B_logical) if self.dtype == "bf16" else self.B_logical
+
+
+def make_problem(M: int, N: int, K: int, dtype: str = "f32", order_a: int = ROW_MAJOR,
+                 order_b: int = ROW_MAJOR, order_c: int = ROW_MAJOR, dist: str = "uniform",
+                 wid: int = 0, pad_a: int = 0, pad_b: int = 0, pad_c: int = 0,
+                 A_logical: np.ndarray | None = None, B_logical: np.ndarray | None = None) -> Problem:
+    """Draw (or take) logical A (M x K) and B (K x N) and lay them out.
+
+    pad_* adds that many slots to the minimum leading dimension.
+    A_logical / B_logical, if given, are fp32 matrices used instead of random draws
+    (rounded to bf16 when dtype == "bf16").
+    """
+    if A_logical is None:
+        A_logical = draw(rng_for(wid, M, N, K, 0), M, K, dist, 0)
+    if B_logical is None:
+        B_logical = draw(rng_for(wid, M, N, K, 1), K, N, dist, 1)
+    A_logical = np.asarray(A_logical, dtype=np.float32).reshape(M, K)
+    B_logical = np.asarray(B_logical, dtype=np.float32).reshape(K, N)
+    if dtype == "bf16":
+        A_logical = f32_to_bf16_bits(A_logical)
+        B_logical = f32_to_bf16_bits(B_logical)
+    elif dtype != "f32":
+        raise ValueError(dtype)
+    lda0 = K if order_a == ROW_MAJOR else M
+    ldb0 = N if order_b == ROW_MAJOR else K
+    ldc0 = N if order_c == ROW_MAJOR else M
+    A, lda = lay_out(A_logical, order_a, max(1, lda0) + pad_a)
+    B, ldb = lay_out(B_logical, order_b, max(1, ldb0) + pad_b)
+    return Problem(M, N, K, dtype, order_a, order_b, order_c, A_logical, B_logical,
+                   A, lda, B, ldb, max(1, ldc0) + pad_c)
+
+
+def workload_problem(name: str) -> Problem:
+    w = WORKLOADS[name]
+    return make_problem(w.M, w.N, w.K, w.dtype, w.order_a, w.order_b, w.order_c, w.dist, w.wid)
+
+
+def unpack_c(flat: np.ndarray, M: int, N: int, ldc: int, order_c: int) -> np.ndarray:
+    """Logical M x N view of a C buffer laid out with (ldc, order_c)."""
+    if order_c == ROW_MAJOR:
+        return flat.reshape(-1, ldc)[:M, :N] if M and N else np.zeros((M, N), flat.dtype)
+    return flat.reshape(-1, ldc)[:N, :M].T if M and N else np.zeros((M, N), flat.dtype)
+
+
+def c_buffer_size(M: int, N: int, ldc: int, order_c: int) -> int:
+    if M == 0 or N == 0:
+        return 1
+    return (M * ldc) if order_c == ROW_MAJOR else (N * ldc)

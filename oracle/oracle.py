@@ -1,0 +1,132 @@
+"""ctypes front end of the C oracle (oracle.c) -- TEST INFRASTRUCTURE ONLY.
+
+The oracle computes C[i][j] = sum_k A[i][k] * B[k][j] in double, k ascending, on the
+exact fp32 or bf16 input values, and D[i][j] = sum_k |A[i][k] * B[k][j]|, the scale the
+parity tolerance is normalised by.  See oracle.c for the cited definition.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+F32 = 0
+BF16 = 1
+
+
+def library_path() -> str:
+    return _LIB
+
+
+def build(src: str = _SRC, out: str = _LIB, extra_flags: tuple = ()) -> str:
+    """Compile the oracle with gcc (plain -O2, OpenMP, no fast-math)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Werror",
+           *extra_flags, src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def load(path: str | None = None):
+    """Load (building first if absent) the oracle library; returns the ctypes handle."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+            _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _bind(lib):
+    i64, vp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)
+    lib.oracle_gemm.argtypes = [i64, i64, i64, ctypes.c_int, vp, i64, ctypes.c_int,
+                                vp, i64, ctypes.c_int, dp, dp, ctypes.POINTER(i64)]
+    lib.oracle_gemm.restype = ctypes.c_int
+    lib.oracle_gemm_sampled.argtypes = [i64, i64, i64, ctypes.c_int, vp, i64, ctypes.c_int,
+                                        vp, i64, ctypes.c_int, ctypes.POINTER(i64),
+                                        ctypes.POINTER(i64), i64, dp, dp]
+    lib.oracle_gemm_sampled.restype = ctypes.c_int
+    lib.oracle_num_threads.restype = ctypes.c_int
+    return lib
+
+
+def _dtype_code(buf: np.ndarray) -> int:
+    if buf.dtype == np.float32:
+        return F32
+    if buf.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"oracle operands are fp32 or bf16 bits (uint16), got {buf.dtype}")
+
+
+def gemm(M, N, K, A, lda, order_a, B, ldb, order_b, lib=None, return_macs=False):
+    """Full product: returns (C, D) as M x N float64 arrays (and the MAC count if asked)."""
+    lib = lib or load()
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    dt = _dtype_code(A)
+    assert _dtype_code(B) == dt
+    C = np.zeros((M, N), dtype=np.float64)
+    D = np.zeros((M, N), dtype=np.float64)
+    macs = ctypes.c_int64(-1)
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = lib.oracle_gemm(M, N, K, dt, A.ctypes.data, lda, order_a, B.ctypes.data, ldb, order_b,
+                         C.ctypes.data_as(dp), D.ctypes.data_as(dp), ctypes.byref(macs))
+    if rc != 0:
+        raise ValueError("oracle_gemm rejected its arguments")
+    return (C, D, macs.value) if return_macs else (C, D)
+
+
+def gemm_sampled(M, N, K, A, lda, order_a, B, ldb, order_b, rows, cols, lib=None):
+    """C and D at the (rows[t], cols[t]) elements only."""
+    lib = lib or load()
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    dt = _dtype_code(A)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    C = np.zeros(rows.size, dtype=np.float64)
+    D = np.zeros(rows.size, dtype=np.float64)
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int64)
+    rc = lib.oracle_gemm_sampled(M, N, K, dt, A.ctypes.data, lda, order_a, B.ctypes.data, ldb,
+                                 order_b, rows.ctypes.data_as(ip), cols.ctypes.data_as(ip),
+                                 rows.size, C.ctypes.data_as(dp), D.ctypes.data_as(dp))
+    if rc != 0:
+        raise ValueError("oracle_gemm_sampled rejected its arguments")
+    return C, D
+
+
+def normalised_error(C_test: np.ndarray, C_ref: np.ndarray, D: np.ndarray) -> float:
+    """max over elements of |C_test - C_ref| / D.
+
+    Where D == 0 (every product is zero) the test value must be exactly zero (-0 counts
+    as zero); a mismatch there, or any NaN / inf in C_test, returns inf.
+    """
+    C_test = np.asarray(C_test, dtype=np.float64)
+    if C_test.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(C_test)):
+        return float("inf")
+    diff = np.abs(C_test - C_ref)
+    zero = D == 0
+    if np.any(diff[zero] != 0):
+        return float("inf")
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(zero, 0.0, diff / np.where(zero, 1.0, D))
+    return float(rel.max())
+
+
+def num_threads(lib=None) -> int:
+    return int((lib or load()).oracle_num_threads())

@@ -1,0 +1,235 @@
+"""Pins of the fp64 oracle against facts fixed outside the oracle itself.
+
+Each pin takes a loaded oracle library handle and raises AssertionError when the
+oracle disagrees with:
+  * exact rational arithmetic on tiny shapes (brute force with fractions.Fraction);
+  * numpy's float64 matmul on the logical matrices (a library routine the oracle does
+    not call);
+  * closed forms: all-ones operands give C = K; an all-ones A gives column sums of B;
+    identity and permutation operands reproduce / permute the other operand exactly;
+  * small-integer operands, whose product is exact under any summation order;
+  * invariants: (A.B)^T = B^T.A^T, and splitting K into two ranges and adding the
+    partial products gives the full product -- the 4 x 4, tile-2 worked example of
+    "GEMM" (Part 4 of How to make your models fast), section "A small example";
+  * the multiply-add count M*N*K (FLOPs = 2MNK: "How a Matrix Multiply Runs on a GPU",
+    section "The problem and the roofline"; "A06 - Tiled Matrix Multiply (GEMM)",
+    section "The derivation that explains everything").
+
+The same pins run against deliberately broken builds of the oracle (see
+test_oracle_mutants.py) to show that each plausible mistake fails at least one.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+import gemm_inputs as gi
+import oracle
+from gemm_inputs import COL_MAJOR, ROW_MAJOR
+
+ORDERS = [(oa, ob) for oa in (ROW_MAJOR, COL_MAJOR) for ob in (ROW_MAJOR, COL_MAJOR)]
+
+
+def _run(lib, p: gi.Problem, macs=False):
+    return oracle.gemm(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b,
+                       lib=lib, return_macs=macs)
+
+
+def _int_matrix(rng, r, c, lo=-4, hi=4):
+    return rng.integers(lo, hi + 1, size=(r, c)).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------------
+def pin_fraction_bruteforce(lib):
+    """Exact rational sums on tiny shapes: |C - exact| <= (K-1) * 2^-53 * D."""
+    shapes = [(1, 1, 1), (2, 3, 4), (3, 1, 5), (4, 4, 4), (5, 7, 3), (8, 8, 8), (1, 6, 8)]
+    for dtype in ("f32", "bf16"):
+        for (M, N, K) in shapes:
+            for oa, ob in ORDERS:
+                p = gi.make_problem(M, N, K, dtype, oa, ob, wid=101, pad_a=1, pad_b=2)
+                C, D = _run(lib, p)
+                a, b = p.a_f32(), p.b_f32()
+                for i in range(M):
+                    for j in range(N):
+                        exact = sum((Fraction(float(a[i, k])) * Fraction(float(b[k, j]))
+                                     for k in range(K)), Fraction(0))
+                        dabs = sum((abs(Fraction(float(a[i, k])) * Fraction(float(b[k, j])))
+                                    for k in range(K)), Fraction(0))
+                        err = abs(Fraction(C[i, j]) - exact)
+                        bound = Fraction(max(K - 1, 0)) * Fraction(2) ** -53 * dabs
+                        assert err <= bound, (dtype, M, N, K, oa, ob, i, j)
+                        assert abs(Fraction(D[i, j]) - dabs) <= bound, ("D", dtype, M, N, K, i, j)
+
+
+def pin_numpy_crosscheck(lib):
+    """numpy float64 matmul of the logical operands agrees to 1e-12 of D."""
+    for dtype in ("f32", "bf16"):
+        for (M, N, K) in [(37, 53, 129), (64, 32, 16), (3, 100, 257)]:
+            for oa, ob in ORDERS:
+                p = gi.make_problem(M, N, K, dtype, oa, ob, wid=102, pad_a=3, pad_b=1)
+                C, D = _run(lib, p)
+                a = p.a_f32().astype(np.float64)
+                b = p.b_f32().astype(np.float64)
+                ref = a @ b
+                dref = np.abs(a) @ np.abs(b)
+                assert oracle.normalised_error(C, ref, dref) <= 1e-12, (dtype, M, N, K, oa, ob)
+                assert np.max(np.abs(D - dref) / np.maximum(dref, 1e-300)) <= 1e-12
+
+
+def pin_ones(lib):
+    """A = ones, B = ones  =>  C == K exactly (16^3 is the pages' worked size)."""
+    for (M, N, K) in [(16, 16, 16), (32, 32, 32), (64, 64, 64), (37, 45, 67)]:
+        for dtype in ("f32", "bf16"):
+            for oa, ob in ORDERS:
+                p = gi.make_problem(M, N, K, dtype, oa, ob, A_logical=np.ones((M, K)),
+                                    B_logical=np.ones((K, N)))
+                C, D = _run(lib, p)
+                assert np.all(C == K) and np.all(D == K), (M, N, K, dtype, oa, ob)
+
+
+def pin_ones_column_sums(lib):
+    """A = ones  =>  C[i][j] = sum_k B[k][j] (integer-valued B: exact)."""
+    rng = np.random.default_rng(7)
+    for (M, N, K) in [(16, 16, 16), (5, 9, 33)]:
+        Bl = _int_matrix(rng, K, N)
+        colsum = Bl.astype(np.int64).sum(axis=0)
+        for oa, ob in ORDERS:
+            p = gi.make_problem(M, N, K, "f32", oa, ob, A_logical=np.ones((M, K)), B_logical=Bl)
+            C, _ = _run(lib, p)
+            assert np.array_equal(C, np.broadcast_to(colsum, (M, N)).astype(np.float64))
+
+
+def pin_identity(lib):
+    """A = I  =>  C == B bit for bit; B = I  =>  C == A bit for bit."""
+    for n, other in [(16, 16), (32, 19), (7, 40)]:
+        for dtype in ("f32", "bf16"):
+            for oa, ob in ORDERS:
+                p = gi.make_problem(n, other, n, dtype, oa, ob, wid=103, A_logical=np.eye(n))
+                C, _ = _run(lib, p)
+                assert np.array_equal(C, p.b_f32().astype(np.float64)), ("A=I", n, dtype, oa, ob)
+                q = gi.make_problem(other, n, n, dtype, oa, ob, wid=104, B_logical=np.eye(n))
+                C, _ = _run(lib, q)
+                assert np.array_equal(C, q.a_f32().astype(np.float64)), ("B=I", n, dtype, oa, ob)
+
+
+def pin_permutation(lib):
+    """A = P (permutation)  =>  rows of B permuted; B = P  =>  columns of A permuted."""
+    rng = np.random.default_rng(11)
+    for n, other in [(16, 16), (33, 20)]:
+        perm = rng.permutation(n)
+        P = np.zeros((n, n))
+        P[np.arange(n), perm] = 1.0           # (P.X)[i] = X[perm[i]]
+        for dtype in ("f32", "bf16"):
+            for oa, ob in ORDERS:
+                p = gi.make_problem(n, other, n, dtype, oa, ob, wid=105, A_logical=P)
+                C, _ = _run(lib, p)
+                assert np.array_equal(C, p.b_f32()[perm].astype(np.float64)), ("A=P", dtype, oa, ob)
+                q = gi.make_problem(other, n, n, dtype, oa, ob, wid=106, B_logical=P)
+                C, _ = _run(lib, q)
+                inv = np.argsort(perm)                # (X.P)[:, j] = X[:, inv[j]]
+                assert np.array_equal(C, q.a_f32()[:, inv].astype(np.float64)), ("B=P", dtype, oa, ob)
+
+
+def pin_small_integers(lib):
+    """Entries in {-4..4}: every partial sum is an exact integer, so C is the integer product."""
+    rng = np.random.default_rng(13)
+    for (M, N, K) in [(16, 16, 16), (33, 17, 65), (1, 40, 7), (50, 1, 3)]:
+        Al, Bl = _int_matrix(rng, M, K), _int_matrix(rng, K, N)
+        exact = (Al.astype(np.int64) @ Bl.astype(np.int64)).astype(np.float64)
+        dexact = (np.abs(Al).astype(np.int64) @ np.abs(Bl).astype(np.int64)).astype(np.float64)
+        for dtype in ("f32", "bf16"):
+            for oa, ob in ORDERS:
+                p = gi.make_problem(M, N, K, dtype, oa, ob, A_logical=Al, B_logical=Bl, pad_a=2)
+                C, D = _run(lib, p)
+                assert np.array_equal(C, exact), (M, N, K, dtype, oa, ob)
+                assert np.array_equal(D, dexact), (M, N, K, dtype, oa, ob)
+
+
+def pin_transpose(lib):
+    """(A.B)^T computed as B^T.A^T from the same buffers (order flags flipped) agrees bitwise."""
+    for dtype in ("f32", "bf16"):
+        for oa, ob in ORDERS:
+            p = gi.make_problem(23, 31, 41, dtype, oa, ob, wid=107, pad_b=5)
+            C, D = _run(lib, p)
+            Ct, Dt = oracle.gemm(p.N, p.M, p.K, p.B, p.ldb, 1 - p.order_b, p.A, p.lda,
+                                 1 - p.order_a, lib=lib)
+            assert np.array_equal(Ct, C.T) and np.array_equal(Dt, D.T), (dtype, oa, ob)
+
+
+def pin_k_split(lib):
+    """Split K at k0: C = A[:, :k0].B[:k0, :] + A[:, k0:].B[k0:, :].
+
+    The 4 x 4 case with tile 2 is the pages' worked example of a block walking along K;
+    small-integer entries make the identity exact.
+    """
+    rng = np.random.default_rng(17)
+    for (M, N, K, k0) in [(4, 4, 4, 2), (8, 5, 13, 6), (16, 16, 16, 4)]:
+        Al, Bl = _int_matrix(rng, M, K), _int_matrix(rng, K, N)
+        full, _ = _run(lib, gi.make_problem(M, N, K, "f32", A_logical=Al, B_logical=Bl))
+        lo, _ = _run(lib, gi.make_problem(M, N, k0, "f32", A_logical=Al[:, :k0], B_logical=Bl[:k0]))
+        hi, _ = _run(lib, gi.make_problem(M, N, K - k0, "f32", A_logical=Al[:, k0:], B_logical=Bl[k0:]))
+        assert np.array_equal(full, lo + hi), (M, N, K, k0)
+    # the worked example written out for C00 of the 4 x 4 case
+    Al, Bl = _int_matrix(rng, 4, 4), _int_matrix(rng, 4, 4)
+    C, _ = _run(lib, gi.make_problem(4, 4, 4, "f32", A_logical=Al, B_logical=Bl))
+    c00 = Al[0, 0] * Bl[0, 0] + Al[0, 1] * Bl[1, 0] + Al[0, 2] * Bl[2, 0] + Al[0, 3] * Bl[3, 0]
+    assert C[0, 0] == c00
+
+
+def pin_mac_count(lib):
+    """The loop nest performs exactly M*N*K multiply-adds."""
+    for (M, N, K) in [(1, 1, 1), (3, 5, 7), (16, 16, 16), (0, 4, 4), (4, 0, 4), (4, 4, 0)]:
+        p = gi.make_problem(M, N, K, "f32", wid=108)
+        C, D, macs = _run(lib, p, macs=True)
+        assert macs == M * N * K, (M, N, K, macs)
+
+
+def pin_degenerate(lib):
+    """K = 0 gives the empty sum C = 0; M or N = 0 gives an empty C."""
+    p = gi.make_problem(5, 6, 0, "f32")
+    C, D = _run(lib, p)
+    assert C.shape == (5, 6) and np.all(C == 0) and np.all(D == 0)
+    for (M, N) in [(0, 6), (5, 0)]:
+        C, D = _run(lib, gi.make_problem(M, N, 3, "f32"))
+        assert C.shape == (M, N)
+
+
+def pin_nonnegative_scale(lib):
+    """With nonnegative entries, D (sum of |products|) equals C bit for bit."""
+    for dtype in ("f32", "bf16"):
+        p = gi.make_problem(19, 21, 300, dtype, dist="unit", wid=109)
+        C, D = _run(lib, p)
+        assert np.array_equal(C, D)
+
+
+def pin_bf16_widening(lib):
+    """bf16 bit patterns are read as the values they encode: 1.0 (0x3F80) times
+    -2.5 (0xC020) plus 2^-126 (0x0080) times 3.0 (0x4040)."""
+    A = np.array([0x3F80, 0x0080], dtype=np.uint16)   # 1 x 2 row-major
+    B = np.array([0xC020, 0x4040], dtype=np.uint16)   # 2 x 1 row-major
+    C, D = oracle.gemm(1, 1, 2, A, 2, ROW_MAJOR, B, 1, ROW_MAJOR, lib=lib)
+    assert C[0, 0] == -2.5 + 3.0 * 2.0 ** -126
+    assert D[0, 0] == 2.5 + 3.0 * 2.0 ** -126
+
+
+def pin_sampled_matches_full(lib):
+    """The sampled entry point returns the full product's elements bit for bit."""
+    for dtype in ("f32", "bf16"):
+        for oa, ob in ORDERS:
+            p = gi.make_problem(29, 33, 77, dtype, oa, ob, wid=110, pad_a=1)
+            C, D = _run(lib, p)
+            rng = np.random.default_rng(19)
+            rows = rng.integers(0, p.M, 50)
+            cols = rng.integers(0, p.N, 50)
+            Cs, Ds = oracle.gemm_sampled(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb,
+                                         p.order_b, rows, cols, lib=lib)
+            assert np.array_equal(Cs, C[rows, cols]) and np.array_equal(Ds, D[rows, cols])
+
+
+ALL_PINS = [
+    pin_fraction_bruteforce, pin_numpy_crosscheck, pin_ones, pin_ones_column_sums,
+    pin_identity, pin_permutation, pin_small_integers, pin_transpose, pin_k_split,
+    pin_mac_count, pin_degenerate, pin_nonnegative_scale, pin_bf16_widening,
+    pin_sampled_matches_full,
+]

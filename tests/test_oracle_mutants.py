@@ -1,0 +1,73 @@
+"""Each plausible mistake planted in a copy of the oracle must fail at least one pin.
+
+The mutants are built on the CPU from oracle.c with one textual change each; the
+unmodified source is never touched.  A mutant that passes every pin would mean the
+pins could not tell that mistake from the correct oracle.
+"""
+import json
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.library_path()), "oracle.c")
+
+MUTANTS = {
+    "drop_last_term": ("for (int64_t k = 0; k < K; ++k) {\n                double a",
+                       "for (int64_t k = 0; k < K - 1; ++k) {\n                double a"),
+    "skip_first_term": ("for (int64_t k = 0; k < K; ++k) {\n                double a",
+                        "for (int64_t k = 1; k < K; ++k) {\n                double a"),
+    "transpose_b": ("a * element(B, dtype, k, j, ldb, order_b)",
+                    "a * element(B, dtype, j, k, ldb, order_b)"),
+    "wrong_sign": ("s[j] += p;", "s[j] -= p;"),
+    "col_major_as_row": ("r * ld + c : r + c * ld", "r * ld + c : r * ld + c"),
+    "row_major_as_col": ("r * ld + c : r + c * ld", "r + c * ld : r + c * ld"),
+    "bf16_shift": ("<< 16;", "<< 15;"),
+    "scale_without_abs": ("d[j] += fabs(p);", "d[j] += p;"),
+    "no_row_reset": ("s[j] = 0.0;\n                d[j] = 0.0;", "d[j] = 0.0;"),
+    "fp32_accumulator": ("double p = a * element(B, dtype, k, j, ldb, order_b);\n                    s[j] += p;",
+                         "double p = a * element(B, dtype, k, j, ldb, order_b);\n                    s[j] = (float)(s[j] + p);"),
+    "sampled_off_by_one": ("element(B, dtype, k, cols[t], ldb, order_b)",
+                           "element(B, dtype, k, cols[t] > 0 ? cols[t] - 1 : 0, ldb, order_b)"),
+    "mac_undercount": ("count += N;", "count += N - (k == 0);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_fails_a_pin(name):
+    before, after = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(before) >= 1, f"mutation site for {name} not found"
+    mutated = src.replace(before, after)
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "mutant.c")
+        with open(path, "w") as f:
+            f.write(mutated)
+        lib_path = oracle.build(src=path, out=os.path.join(d, "libmutant.so"))
+        # run the pins in a child process: a mutant may read out of bounds and crash
+        child = subprocess.run([sys.executable, "-c", _CHILD, lib_path], capture_output=True,
+                               text=True, timeout=600, cwd=os.path.dirname(__file__))
+        if child.returncode != 0:
+            return          # the mistake crashed a pin: detected
+        failed = json.loads(child.stdout.strip().splitlines()[-1])
+        assert failed, f"mutant {name} passed every pin"
+
+
+_CHILD = """
+import json, os, sys
+sys.path.insert(0, os.path.dirname(os.getcwd()))
+import oracle, oracle_pins
+lib = oracle.oracle.load(sys.argv[1])
+failed = []
+for pin in oracle_pins.ALL_PINS:
+    try:
+        pin(lib)
+    except Exception:
+        failed.append(pin.__name__)
+print(json.dumps(failed))
+"""

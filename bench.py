@@ -1,0 +1,190 @@
+#!/usr/bin/env python3
+"""Throughput of libgemm on one MI355X: GEMM TFLOP/s at 4096³ and fraction of peak.
+
+One step is one pass of the whole hot path over resident synthetic inputs: an FP32 GEMM
+(4096³, row-major A/B/C, uniform[-1, 1]) followed by a BF16-input, FP32-accumulate GEMM
+(4096³, row-major A, column-major B, uniform[-1, 1] rounded to bf16), each through the
+library's default kernel choice.  `value` is the FLOPs of the step (2MNK per GEMM, the
+count the pages use) over the step time.  Per-kernel times come from HIP events recorded
+between the launches on the launch stream; the roofline object prices the dominant
+kernel against MI355X's published matrix-core peak for its dtype.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--algo NAME]
+
+`--workload` picks another single workload from gemm_inputs.WORKLOADS (then one step is
+that one GEMM); `--algo` forces a kernel (gemm_f32_amd.Algo name).  Inputs rotate over
+`--sets` copies so that the 256 MB last-level cache cannot hold them across steps.
+The CPU baseline times the fp64 oracle on the host on a bounded sample of the same
+problems (the first rows of C) and scales it to TFLOP/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s at 4096³ (FP32, BF16→FP32) and % of MI355X peak"
+DEFAULT = "square4096"
+DEFAULT_LEGS = ["square4096_f32", "square4096_bf16"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT)
+    ap.add_argument("--algo", default="AUTO")
+    ap.add_argument("--sets", type=int, default=2)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target host time of the CPU-baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Leg:
+    """One GEMM of the step with its resident device buffers."""
+
+    def __init__(self, name, algo, sets):
+        import torch
+        import gemm_f32_amd as g
+        import gemm_inputs as gi
+        self.w = gi.WORKLOADS[name]
+        self.name = name
+        self.algo = g.Algo[algo]
+        self.problems = []
+        self.A, self.B = [], []
+        for s in range(sets):
+            w = self.w
+            p = gi.make_problem(w.M, w.N, w.K, w.dtype, w.order_a, w.order_b, w.order_c, w.dist,
+                                w.wid + 1000 * s)
+            self.problems.append(p)
+            conv = (lambda b: b.view(np.int16)) if w.dtype == "bf16" else (lambda b: b)
+            self.A.append(torch.from_numpy(conv(p.A)).to("cuda"))
+            self.B.append(torch.from_numpy(conv(p.B)).to("cuda"))
+        p = self.problems[0]
+        self.C = torch.empty(gi.c_buffer_size(p.M, p.N, p.ldc, p.order_c), dtype=torch.float32,
+                             device="cuda")
+        self.fn = g.gemm_f32_algo if w.dtype == "f32" else g.gemm_bf16_f32acc_algo
+        self.flops = 2 * w.M * w.N * w.K
+        self.kernel = None
+
+    def launch(self, s, stream):
+        p = self.problems[s % len(self.problems)]
+        self.fn(self.algo, p.M, p.N, p.K, self.A[s % len(self.A)].data_ptr(), p.lda, p.order_a,
+                self.B[s % len(self.B)].data_ptr(), p.ldb, p.order_b, self.C.data_ptr(), p.ldc,
+                p.order_c, stream)
+
+
+def cpu_baseline(legs, target_s):
+    """The oracle (as is) on the first R rows of each leg's problem, R sized to ~target_s."""
+    import oracle
+    threads = oracle.num_threads()
+
+    def run(rows):
+        t0 = time.perf_counter()
+        for leg in legs:
+            p = leg.problems[0]
+            a = p.A if p.order_a == 0 else None
+            if a is None:                      # a column-major A: take the sub-matrix's rows
+                sub = p.A_logical[:rows]
+                import gemm_inputs as gi
+                a, lda = gi.lay_out(sub, 1)
+            else:
+                lda = p.lda
+                a = p.A[: rows * p.lda]
+            oracle.gemm(rows, p.N, p.K, a, lda, p.order_a, p.B, p.ldb, p.order_b)
+        return time.perf_counter() - t0
+
+    probe = max(1, threads)
+    t_probe = run(probe)
+    rows = int(max(probe, min(min(l.w.M for l in legs), probe * target_s / max(t_probe, 1e-6))))
+    rows = max(probe, (rows // probe) * probe)
+    t = run(rows)
+    flops = sum(2 * rows * l.w.N * l.w.K for l in legs)
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(t, 3),
+            "sample": f"first {rows} rows of C for each of {', '.join(l.name for l in legs)} "
+                      f"({flops / 2:.3e} multiply-adds, fp64 oracle, {threads} OpenMP threads)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the library has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gemm_f32_amd as g
+    from gemm_f32_amd import roofline as rl
+
+    names = DEFAULT_LEGS if args.workload == DEFAULT else [args.workload]
+    legs = [Leg(n, args.algo, args.sets) for n in names]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    for i in range(args.warmup):
+        for leg in legs:
+            leg.launch(i, sh)
+            leg.kernel = g.gemm_last_kernel()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(legs) + 1)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for li, leg in enumerate(legs):
+            leg.launch(s, sh)
+            ev[s][li + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    total_ms = ev[0][0].elapsed_time(ev[-1][-1])
+    ms_step = total_ms / args.steps
+    step_flops = sum(l.flops for l in legs)
+    leg_info = {}
+    for li, leg in enumerate(legs):
+        ms = float(np.mean([ev[s][li].elapsed_time(ev[s][li + 1]) for s in range(args.steps)]))
+        peak = rl.mi355x_peak(leg.w.dtype)
+        tf = leg.flops / (ms * 1e-3) / 1e12
+        leg_info[leg.name] = {"kernel": leg.kernel, "ms": round(ms, 5), "tflops": round(tf, 2),
+                              "pct_peak": round(100 * tf * 1e12 / peak, 2),
+                              "M": leg.w.M, "N": leg.w.N, "K": leg.w.K, "dtype_in": leg.w.dtype}
+    dom = max(legs, key=lambda l: leg_info[l.name]["ms"])
+    di = leg_info[dom.name]
+    peak = rl.mi355x_peak(dom.w.dtype)
+    achieved = dom.flops / (di["ms"] * 1e-3)
+    roof = {"bound": "mfma", "kernel": di["kernel"], "achieved": round(achieved / 1e12, 2),
+            "peak": round(peak / 1e12, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+            "traffic": None,
+            "per_launch": f"2*M*N*K = {dom.flops:.4e} FLOP per launch ({dom.name})"}
+
+    value = step_flops / (ms_step * 1e-3) / 1e12
+    dtype = "+".join(sorted({"f32" if l.w.dtype == "f32" else "bf16->f32" for l in legs}))
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload if args.workload != DEFAULT else
+                   "4096^3 FP32 GEMM + 4096^3 BF16->FP32 GEMM per step",
+                   "legs": leg_info, "algo": args.algo, "input_sets": args.sets,
+                   "wall_s": round(wall, 3)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(legs, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

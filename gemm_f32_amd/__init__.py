@@ -1,0 +1,11 @@
+"""libgemm for MI355X: dense C = A.B with hand-written HIP kernels for gfx950.
+
+The entry points mirror include/gemm.h.  libgemm.so (built in-tree by
+gemm_f32_amd/build.py) is loaded on first use and its absence is an error: there is no
+fallback path.
+"""
+from .binding import (  # noqa: F401
+    EXPORTED, Algo, GemmError, Order, Status, gemm_bf16_f32acc, gemm_bf16_f32acc_algo,
+    gemm_f32, gemm_f32_algo, gemm_last_hip_error, gemm_last_kernel, gemm_status_string,
+    gemm_version, lib_handle, library_path, LibraryNotBuilt, matmul, operand_layout,
+)

@@ -1,0 +1,183 @@
+"""ctypes binding of libgemm.so: the C entry points under the same names.
+
+Argument marshalling only -- every step of C = A.B runs in the library's HIP kernels.
+The library is loaded on first use; if it is not built (gemm_f32_amd/build.py) that use
+raises LibraryNotBuilt: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import enum
+import os
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemm.so")
+
+
+class Order(enum.IntEnum):
+    ROW_MAJOR = 0
+    COL_MAJOR = 1
+
+
+class Algo(enum.IntEnum):
+    AUTO = 0
+    NAIVE_UNCOALESCED = 1
+    NAIVE = 2
+    TILED = 3
+    REGBLOCK = 4
+    MFMA = 5
+    MFMA_256x256 = 6
+    MFMA_256x128 = 7
+    MFMA_128x128 = 8
+    MFMA_64x64 = 9
+
+
+class Status(enum.IntEnum):
+    OK = 0
+    ERR_INVALID_VALUE = 1
+    ERR_UNSUPPORTED_DEVICE = 2
+    ERR_LAUNCH = 3
+
+
+class LibraryNotBuilt(ImportError):
+    pass
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = Status(status)
+        lib = lib_handle()
+        msg = lib.gemm_status_string(status).decode()
+        if self.status == Status.ERR_LAUNCH:
+            msg += f" (hipError_t {lib.gemm_last_hip_error()})"
+        super().__init__(f"{what}: {msg}")
+
+
+_lib = None
+
+
+def lib_handle():
+    """The loaded libgemm.so (loaded on first call)."""
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise LibraryNotBuilt(
+            f"{_LIB_PATH} is not built; build it with `python -m gemm_f32_amd.build` "
+            "(hipcc, gfx950). There is no non-HIP fallback.")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    args = [i64, i64, i64, vp, i64, ci, vp, i64, ci, vp, i64, ci, vp]
+    for name in ("gemm_f32", "gemm_bf16_f32acc"):
+        f = getattr(lib, name)
+        f.argtypes, f.restype = args, ci
+    for name in ("gemm_f32_algo", "gemm_bf16_f32acc_algo"):
+        f = getattr(lib, name)
+        f.argtypes, f.restype = [ci] + args, ci
+    lib.gemm_status_string.argtypes, lib.gemm_status_string.restype = [ci], ctypes.c_char_p
+    lib.gemm_last_hip_error.argtypes, lib.gemm_last_hip_error.restype = [], ci
+    lib.gemm_last_kernel.argtypes, lib.gemm_last_kernel.restype = [], ctypes.c_char_p
+    lib.gemm_version.argtypes, lib.gemm_version.restype = [], ctypes.c_char_p
+    return lib
+
+
+EXPORTED = ("gemm_f32", "gemm_bf16_f32acc", "gemm_f32_algo", "gemm_bf16_f32acc_algo",
+            "gemm_status_string", "gemm_last_hip_error", "gemm_last_kernel", "gemm_version")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise GemmError(rc, what)
+
+
+def gemm_f32(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, stream=0):
+    """C = A.B, FP32.  A, B, C are device pointers (ints); stream a hipStream_t (int)."""
+    _check(lib_handle().gemm_f32(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, stream),
+           "gemm_f32")
+
+
+def gemm_bf16_f32acc(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, stream=0):
+    """C = A.B with bf16 A and B (bit patterns), FP32 accumulate and FP32 C."""
+    _check(lib_handle().gemm_bf16_f32acc(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c,
+                                 stream), "gemm_bf16_f32acc")
+
+
+def gemm_f32_algo(algo, M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, stream=0):
+    _check(lib_handle().gemm_f32_algo(int(algo), M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc,
+                              order_c, stream), "gemm_f32_algo")
+
+
+def gemm_bf16_f32acc_algo(algo, M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c,
+                          stream=0):
+    _check(lib_handle().gemm_bf16_f32acc_algo(int(algo), M, N, K, A, lda, order_a, B, ldb, order_b, C,
+                                      ldc, order_c, stream), "gemm_bf16_f32acc_algo")
+
+
+def gemm_status_string(status: int) -> str:
+    return lib_handle().gemm_status_string(int(status)).decode()
+
+
+def gemm_last_hip_error() -> int:
+    return lib_handle().gemm_last_hip_error()
+
+
+def gemm_last_kernel() -> str:
+    return lib_handle().gemm_last_kernel().decode()
+
+
+def gemm_version() -> str:
+    return lib_handle().gemm_version().decode()
+
+
+# --- torch tensors -> (pointer, leading dimension, order) ------------------------------
+def operand_layout(t) -> tuple[int, int]:
+    """(ld, order) of a 2-D tensor whose memory is row- or column-major with padding."""
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    R, C = t.shape
+    s0, s1 = t.stride()
+    if s1 == 1 and s0 >= max(1, C):
+        return s0, Order.ROW_MAJOR
+    if s0 == 1 and s1 >= max(1, R):
+        return s1, Order.COL_MAJOR
+    if R <= 1 and s1 == 1:
+        return max(1, C), Order.ROW_MAJOR
+    if C <= 1 and s0 == 1:
+        return max(1, R), Order.COL_MAJOR
+    raise ValueError(f"strides {t.stride()} are neither row- nor column-major")
+
+
+def matmul(a, b, out=None, algo: Algo = Algo.AUTO, stream=None):
+    """out = a @ b for torch device tensors, through libgemm on the current stream.
+
+    a: (M, K), b: (K, N), both float32 (FP32 path) or both bfloat16 (BF16 inputs, FP32
+    accumulate).  out: float32 (M, N), row- or column-major; allocated row-major if None.
+    """
+    import torch
+    if a.dtype != b.dtype or a.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("a and b must both be float32 or both bfloat16")
+    M, K = a.shape
+    K2, N = b.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {a.shape} x {b.shape}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (M, N):
+        raise ValueError("out must be float32 of shape (M, N)")
+    lda, oa = operand_layout(a)
+    ldb, ob = operand_layout(b)
+    ldc, oc = operand_layout(out)
+    s = torch.cuda.current_stream(a.device).cuda_stream if stream is None else stream
+    args = (M, N, K, a.data_ptr(), lda, oa, b.data_ptr(), ldb, ob, out.data_ptr(), ldc, oc, s)
+    if a.dtype == torch.float32:
+        gemm_f32_algo(algo, *args)
+    else:
+        gemm_bf16_f32acc_algo(algo, *args)
+    return out

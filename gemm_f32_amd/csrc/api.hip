@@ -1,0 +1,231 @@
+// libgemm's C ABI: argument validation, normalisation of a column-major C, kernel choice
+// and launch.  The operation and its contract are documented in include/gemm.h.
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "gemm.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace gemm {
+namespace {
+
+thread_local int t_last_hip_error = 0;
+thread_local const char* t_last_kernel = "none";
+
+enum class In { F32, BF16 };
+
+struct DeviceInfo {
+    bool supported = false;
+    int cus = 0;
+};
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+DeviceInfo g_dev[kMaxDevices];
+
+// Per-device properties, queried once.  Returns false if the device cannot be queried.
+bool device_info(DeviceInfo& out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+    std::call_once(g_dev_once[dev], [dev] {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
+            g_dev[dev].supported = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+            g_dev[dev].cus = prop.multiProcessorCount;
+        }
+    });
+    out = g_dev[dev];
+    return true;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+gemm_status_t validate(In in, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                       int oa, const void* B, int64_t ldb, int ob, const void* C, int64_t ldc,
+                       int oc) {
+    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_VALUE;
+    if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return GEMM_ERR_INVALID_VALUE;
+    for (int o : {oa, ob, oc})
+        if (o != GEMM_ROW_MAJOR && o != GEMM_COL_MAJOR) return GEMM_ERR_INVALID_VALUE;
+    auto at_least = [](int64_t v) { return v > 1 ? v : 1; };
+    if (lda < at_least(oa == GEMM_ROW_MAJOR ? K : M)) return GEMM_ERR_INVALID_VALUE;
+    if (ldb < at_least(ob == GEMM_ROW_MAJOR ? N : K)) return GEMM_ERR_INVALID_VALUE;
+    if (ldc < at_least(oc == GEMM_ROW_MAJOR ? N : M)) return GEMM_ERR_INVALID_VALUE;
+    if (M > 0 && N > 0 && C == nullptr) return GEMM_ERR_INVALID_VALUE;
+    if (M > 0 && N > 0 && K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_INVALID_VALUE;
+    const uintptr_t e = in == In::F32 ? 4 : 2;
+    if (!aligned(A, e) || !aligned(B, e) || !aligned(C, 4)) return GEMM_ERR_INVALID_VALUE;
+    return GEMM_OK;
+}
+
+int pick_group_m(int tiles_m, int tiles_n) {
+    // Make the run of tiles that one XCD receives (total / 8 consecutive ids) cover a
+    // near-square patch of C: group_m x (per_xcd / group_m) tiles.
+    const int per_xcd = (tiles_m * tiles_n) / kNumXcds;
+    int g = 1;
+    while (2 * g <= tiles_m && (2 * g) * (2 * g) <= per_xcd) g *= 2;
+    return g;
+}
+
+int64_t tiles(int64_t M, int64_t N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
+
+// BF16 tile choice.  A block tile per CU and as few partial waves as possible: among the
+// tiles, estimate time as (waves of tiles over the CUs) x (work per tile / relative
+// efficiency of the tile size), and take the cheapest.
+void pick_bf16_tile(int64_t M, int64_t N, int cus, int& bm, int& bn) {
+    struct Opt { int bm, bn; double eff; };
+    const Opt opts[] = {{256, 256, 1.0}, {256, 128, 0.85}, {128, 128, 0.65}, {64, 64, 0.3}};
+    double best = 1e300;
+    for (const Opt& o : opts) {
+        const double n = (double)tiles(M, N, o.bm, o.bn);
+        const double waves = std::ceil(n / (cus > 0 ? cus : 256));
+        const double cost = waves * o.bm * o.bn / o.eff;
+        if (cost < best) { best = cost; bm = o.bm; bn = o.bn; }
+    }
+}
+
+template <typename Elem>
+gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, const Elem* A,
+                  int64_t lda, gemm_order_t oa, const Elem* B, int64_t ldb, gemm_order_t ob,
+                  float* C, int64_t ldc, gemm_order_t oc, hipStream_t stream) {
+    gemm_status_t st = validate(in, M, N, K, A, lda, oa, B, ldb, ob, C, ldc, oc);
+    if (st != GEMM_OK) return st;
+    const bool f32 = in == In::F32;
+    switch (algo) {
+        case GEMM_ALGO_AUTO: case GEMM_ALGO_MFMA: break;
+        case GEMM_ALGO_NAIVE_UNCOALESCED: case GEMM_ALGO_NAIVE: case GEMM_ALGO_TILED:
+        case GEMM_ALGO_REGBLOCK:
+            if (!f32) return GEMM_ERR_INVALID_VALUE;
+            break;
+        case GEMM_ALGO_MFMA_128x128: break;
+        case GEMM_ALGO_MFMA_256x256: case GEMM_ALGO_MFMA_256x128: case GEMM_ALGO_MFMA_64x64:
+            if (f32) return GEMM_ERR_INVALID_VALUE;
+            break;
+        default: return GEMM_ERR_INVALID_VALUE;
+    }
+    if (M == 0 || N == 0) {
+        t_last_kernel = "none";
+        return GEMM_OK;
+    }
+    DeviceInfo dev;
+    if (!device_info(dev) || !dev.supported) return GEMM_ERR_UNSUPPORTED_DEVICE;
+
+    // Column-major C: compute C^T = B^T A^T into the same memory viewed row-major.
+    Problem p{};
+    if (oc == GEMM_ROW_MAJOR) {
+        p = Problem{(int)M, (int)N, (int)K, A, lda, (int)oa, B, ldb, (int)ob, C, ldc};
+    } else {
+        p = Problem{(int)N, (int)M, (int)K, B, ldb, 1 - (int)ob, A, lda, 1 - (int)oa, C, ldc};
+    }
+    const unsigned vw = f32 ? 4 : 8;   // elements per 16-byte load
+    Launch l{};
+    l.stream = stream;
+    l.vec_a = (p.lda % vw == 0) && aligned(p.A, 16);
+    l.vec_b = (p.ldb % vw == 0) && aligned(p.B, 16);
+    l.vec_c = (p.ldc % 4 == 0) && aligned(p.C, 16);
+
+    hipError_t err = hipSuccess;
+    const char* name = "none";
+    if (K == 0) {
+        err = launch_zero_c(p, l);
+        name = "zero_c";
+    } else if (f32) {
+        switch (algo) {
+            case GEMM_ALGO_NAIVE_UNCOALESCED:
+                err = launch_naive(p, l, false); name = "f32_naive_uncoalesced"; break;
+            case GEMM_ALGO_NAIVE:
+                err = launch_naive(p, l, true); name = "f32_naive"; break;
+            case GEMM_ALGO_TILED:
+                err = launch_tiled(p, l); name = "f32_tiled32"; break;
+            case GEMM_ALGO_REGBLOCK: {
+                l.group_m = pick_group_m((p.M + kRegblockBM - 1) / kRegblockBM,
+                                         (p.N + kRegblockBN - 1) / kRegblockBN);
+                err = launch_regblock(p, l); name = "f32_regblock128x128"; break;
+            }
+            default: {
+                l.group_m = pick_group_m((p.M + kF32MfmaBM - 1) / kF32MfmaBM,
+                                         (p.N + kF32MfmaBN - 1) / kF32MfmaBN);
+                err = launch_f32_mfma(p, l); name = "f32_mfma128x128"; break;
+            }
+        }
+    } else {
+        int bm = 256, bn = 256;
+        switch (algo) {
+            case GEMM_ALGO_MFMA_256x256: bm = 256; bn = 256; break;
+            case GEMM_ALGO_MFMA_256x128: bm = 256; bn = 128; break;
+            case GEMM_ALGO_MFMA_128x128: bm = 128; bn = 128; break;
+            case GEMM_ALGO_MFMA_64x64: bm = 64; bn = 64; break;
+            default: pick_bf16_tile(p.M, p.N, dev.cus, bm, bn); break;
+        }
+        l.group_m = pick_group_m((p.M + bm - 1) / bm, (p.N + bn - 1) / bn);
+        err = launch_bf16_mfma(p, l, bm, bn);
+        static const char* names[] = {"bf16_mfma256x256", "bf16_mfma256x128", "bf16_mfma128x128",
+                                      "bf16_mfma64x64"};
+        name = names[bm == 256 ? (bn == 256 ? 0 : 1) : (bm == 128 ? 2 : 3)];
+    }
+    if (err != hipSuccess) {
+        t_last_hip_error = (int)err;
+        return GEMM_ERR_LAUNCH;
+    }
+    t_last_kernel = name;
+    return GEMM_OK;
+}
+
+}  // namespace
+}  // namespace gemm
+
+extern "C" {
+
+gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                       gemm_order_t order_a, const float* B, int64_t ldb, gemm_order_t order_b,
+                       float* C, int64_t ldc, gemm_order_t order_c, hipStream_t stream) {
+    return gemm::run(gemm::In::F32, GEMM_ALGO_AUTO, M, N, K, A, lda, order_a, B, ldb, order_b,
+                     C, ldc, order_c, stream);
+}
+
+gemm_status_t gemm_bf16_f32acc(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                               gemm_order_t order_a, const uint16_t* B, int64_t ldb,
+                               gemm_order_t order_b, float* C, int64_t ldc, gemm_order_t order_c,
+                               hipStream_t stream) {
+    return gemm::run(gemm::In::BF16, GEMM_ALGO_AUTO, M, N, K, A, lda, order_a, B, ldb, order_b,
+                     C, ldc, order_c, stream);
+}
+
+gemm_status_t gemm_f32_algo(gemm_algo_t algo, int64_t M, int64_t N, int64_t K, const float* A,
+                            int64_t lda, gemm_order_t order_a, const float* B, int64_t ldb,
+                            gemm_order_t order_b, float* C, int64_t ldc, gemm_order_t order_c,
+                            hipStream_t stream) {
+    return gemm::run(gemm::In::F32, algo, M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc,
+                     order_c, stream);
+}
+
+gemm_status_t gemm_bf16_f32acc_algo(gemm_algo_t algo, int64_t M, int64_t N, int64_t K,
+                                    const uint16_t* A, int64_t lda, gemm_order_t order_a,
+                                    const uint16_t* B, int64_t ldb, gemm_order_t order_b,
+                                    float* C, int64_t ldc, gemm_order_t order_c,
+                                    hipStream_t stream) {
+    return gemm::run(gemm::In::BF16, algo, M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc,
+                     order_c, stream);
+}
+
+const char* gemm_status_string(gemm_status_t status) {
+    switch (status) {
+        case GEMM_OK: return "GEMM_OK";
+        case GEMM_ERR_INVALID_VALUE: return "GEMM_ERR_INVALID_VALUE: invalid argument";
+        case GEMM_ERR_UNSUPPORTED_DEVICE: return "GEMM_ERR_UNSUPPORTED_DEVICE: current device is not gfx950";
+        case GEMM_ERR_LAUNCH: return "GEMM_ERR_LAUNCH: kernel launch failed";
+    }
+    return "unknown gemm_status_t";
+}
+
+int gemm_last_hip_error(void) { return gemm::t_last_hip_error; }
+
+const char* gemm_last_kernel(void) { return gemm::t_last_kernel; }
+
+const char* gemm_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Shared definitions of libgemm's kernels: the normalised problem descriptor and the
+// tile scheduler.  Everything here is device/host plumbing; no arithmetic of C = A.B.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gemm {
+
+enum Order : int { kRow = 0, kCol = 1 };
+
+// A problem after the host has normalised it: C is row-major M x N with leading
+// dimension ldc (a column-major C is handled by computing C^T = B^T A^T instead).
+// A (M x K) and B (K x N) keep their own order and leading dimension.  Sizes fit in
+// int32 (checked on the host); offsets are formed in int64.
+struct Problem {
+    int M, N, K;
+    const void* A;
+    int64_t lda;
+    int oa;
+    const void* B;
+    int64_t ldb;
+    int ob;
+    float* C;
+    int64_t ldc;
+};
+
+// Offset of logical element (r, c) in an operand with leading dimension ld and order o.
+__device__ __forceinline__ int64_t elem_offset(int64_t r, int64_t c, int64_t ld, int o) {
+    return o == kRow ? r * ld + c : r + c * ld;
+}
+
+// ---------------------------------------------------------------------------------------
+// Tile scheduler: linear workgroup id -> (tile row, tile column) of C.
+//
+// Two remaps, both bijections on [0, tiles):
+//  1. XCD grouping.  MI355X has 8 XCDs, each with its own L2, and the dispatcher hands
+//     consecutive workgroup ids to the XCDs in turn (id w runs on XCD w % 8).  The remap
+//     renumbers ids so that the workgroups resident on one XCD receive consecutive
+//     logical tile numbers, i.e. neighbouring tiles of C that share A row-panels and B
+//     column-panels sit behind the same L2.
+//  2. Group-M ordering.  Logical tile numbers run down a band of `group_m` tile rows
+//     before moving one tile column right, so a run of consecutive numbers covers a
+//     near-square patch of C instead of one long row.
+// The pages describe the second idea for one shared L2 ("GEMM Optimization", section "L2
+// Cache and Wave Analysis"; "GEMM, step by step", Concept: neighbouring blocks working on
+// the same rows and columns); the first is what it takes on a chip with eight L2s.
+// ---------------------------------------------------------------------------------------
+constexpr int kNumXcds = 8;
+
+__host__ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n,
+                                                     int group_m, int& tile_m, int& tile_n) {
+    const int total = tiles_m * tiles_n;
+    const int per_xcd = total / kNumXcds;
+    int id = wg;
+    if (wg < per_xcd * kNumXcds) id = (wg % kNumXcds) * per_xcd + wg / kNumXcds;
+    const int band = group_m * tiles_n;
+    const int first_m = (id / band) * group_m;
+    const int rows = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+    const int in_band = id % band;
+    tile_m = first_m + in_band % rows;
+    tile_n = in_band / rows;
+}
+
+// Launch options the host chooses per call.
+struct Launch {
+    hipStream_t stream;
+    int group_m;        // tile-scheduler band height (>= 1)
+    bool vec_a, vec_b;  // operand pointer and leading dimension allow 16-byte loads
+    bool vec_c;         // C pointer and ldc allow 16-byte stores
+};
+
+}  // namespace gemm

@@ -1,0 +1,29 @@
+// C = 0 for an empty sum (K == 0).  A plain store kernel rather than hipMemsetAsync so
+// that a strided C (ldc > N) is handled and so that the call stays a kernel node if a
+// caller captures it in a graph.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace gemm {
+namespace {
+
+__global__ __launch_bounds__(256) void k_zero_c(float* C, int M, int N, int64_t ldc) {
+    const int64_t total = (int64_t)M * N;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = e / N, c = e % N;
+        C[r * ldc + c] = 0.f;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_zero_c(const Problem& p, const Launch& l) {
+    const int64_t total = (int64_t)p.M * p.N;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(k_zero_c, dim3((unsigned)blocks), dim3(256), 0, l.stream, p.C, p.M, p.N, p.ldc);
+    return hipGetLastError();
+}
+
+}  // namespace gemm

@@ -1,0 +1,25 @@
+// Kernel launchers, one per kernel family.  Each takes a normalised Problem (row-major C)
+// and enqueues on l.stream; the host has already validated shapes and chosen options.
+#pragma once
+
+#include "common.hpp"
+
+namespace gemm {
+
+// FP32 ladder (f32_ladder.hip)
+hipError_t launch_naive(const Problem& p, const Launch& l, bool coalesced);
+hipError_t launch_tiled(const Problem& p, const Launch& l);
+// FP32 register-blocked VALU kernel (f32_regblock.hip)
+hipError_t launch_regblock(const Problem& p, const Launch& l);
+// FP32 matrix-core kernel (f32_mfma.hip)
+hipError_t launch_f32_mfma(const Problem& p, const Launch& l);
+// BF16 matrix-core kernel (bf16_mfma.hip); tile is one of 256x256, 256x128, 128x128, 64x64
+hipError_t launch_bf16_mfma(const Problem& p, const Launch& l, int bm, int bn);
+// C = 0 for K == 0 (fill.hip)
+hipError_t launch_zero_c(const Problem& p, const Launch& l);
+
+// Block-tile sizes, exported for the host's scheduler choices.
+constexpr int kRegblockBM = 128, kRegblockBN = 128;
+constexpr int kF32MfmaBM = 128, kF32MfmaBN = 128;
+
+}  // namespace gemm

@@ -1,0 +1,137 @@
+/*
+ * libgemm -- dense matrix multiply C = A.B for AMD Instinct MI355X (gfx950).
+ *
+ * The operation every page describes: A is M x K, B is K x N, C is M x N and
+ *     C[i][j] = sum over k = 0 .. K-1 of A[i][k] * B[k][j]
+ * ("GEMM", Part 4 of How to make your models fast, opening definition;
+ *  "GEMM Optimization", section "The Problem").  C is overwritten.
+ *
+ * Layout.  Each operand is a logical matrix with its own leading dimension and order:
+ * element (r, c) of a logical R x C operand X is X[r*ldx + c] when the order is
+ * GEMM_ROW_MAJOR and X[r + c*ldx] when it is GEMM_COL_MAJOR.  Leading dimensions must
+ * be at least:
+ *     A: K (row-major) or M (column-major);  B: N (row-major) or K (column-major);
+ *     C: N (row-major) or M (column-major);  and always at least 1.
+ * The matrix-core example of "How a Matrix Multiply Runs on a GPU" (section "Level 3:
+ * tensor cores") uses row-major A with column-major B (ld = K); any mix is accepted.
+ *
+ * Degenerate sizes.  M == 0 or N == 0: nothing is launched, GEMM_OK.  K == 0: C is set
+ * to zero (the empty sum; zero is the additive identity, as the teaching module's
+ * boundary discussion puts it in "A06 - Tiled Matrix Multiply (GEMM)", section "The
+ * tiled kernel, and what each line is protecting").
+ *
+ * Ownership.  All matrix pointers are device pointers owned by the caller; A and B are
+ * only read, C is only written, and C must not overlap A or B.  Pointers need only their
+ * element's natural alignment (4 bytes for float, 2 for bf16); wider alignment of the
+ * pointers and leading dimensions lets the library pick wider loads.  The library
+ * allocates no device memory and keeps no state beyond a per-device property cache.
+ *
+ * Streams and errors.  Work is enqueued on `stream` (0 = the null stream) of the
+ * current device and the call returns without waiting for it.  Argument errors are
+ * detected before anything is enqueued and leave C untouched:
+ *     GEMM_ERR_INVALID_VALUE      negative size, leading dimension too small, unknown
+ *                                 order or algorithm, null pointer for a non-empty
+ *                                 operand, or a shape the chosen algorithm cannot run;
+ *     GEMM_ERR_UNSUPPORTED_DEVICE the current device is not gfx950;
+ *     GEMM_ERR_LAUNCH             the HIP runtime refused the launch (see
+ *                                 gemm_last_hip_error).
+ */
+#ifndef LIBGEMM_GEMM_H
+#define LIBGEMM_GEMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1 } gemm_order_t;
+
+typedef enum {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_VALUE = 1,
+    GEMM_ERR_UNSUPPORTED_DEVICE = 2,
+    GEMM_ERR_LAUNCH = 3
+} gemm_status_t;
+
+/*
+ * Kernel choice.  GEMM_ALGO_AUTO lets the library pick from the shape, dtype and
+ * alignment.  The others force one kernel; they exist so that each step of the pages'
+ * ladder can be run, checked and measured on its own:
+ *   NAIVE_UNCOALESCED  one thread per output, the thread's fast index walks rows of C
+ *                      ("GEMM", Part 4, the first direct kernel);
+ *   NAIVE              one thread per output, fast index along columns of C
+ *                      ("How a Matrix Multiply Runs on a GPU", "Level 0");
+ *   TILED              32 x 32 tiles staged in LDS, one output per thread ("Level 1");
+ *   REGBLOCK           128 x 128 block tiles, 8 x 8 outputs per thread on the vector
+ *                      ALUs, double-buffered LDS ("Level 2"; "GEMM Optimization", V2/V3);
+ *   MFMA               matrix-core kernel: v_mfma_f32_32x32x2_f32 for FP32 inputs,
+ *                      v_mfma_f32_32x32x16_bf16 for BF16 inputs, FP32 accumulate
+ *                      ("A06 - Tiled Matrix Multiply (GEMM)", "Matrix cores: MFMA and
+ *                      Tensor Cores"); tile shape picked from the problem;
+ *   MFMA_256x256, MFMA_256x128, MFMA_128x128, MFMA_64x64
+ *                      the MFMA kernel with that block tile forced.
+ * The FP32 entry point accepts every algorithm; the BF16 entry point only AUTO and the
+ * MFMA ones (others give GEMM_ERR_INVALID_VALUE).
+ */
+typedef enum {
+    GEMM_ALGO_AUTO = 0,
+    GEMM_ALGO_NAIVE_UNCOALESCED = 1,
+    GEMM_ALGO_NAIVE = 2,
+    GEMM_ALGO_TILED = 3,
+    GEMM_ALGO_REGBLOCK = 4,
+    GEMM_ALGO_MFMA = 5,
+    GEMM_ALGO_MFMA_256x256 = 6,
+    GEMM_ALGO_MFMA_256x128 = 7,
+    GEMM_ALGO_MFMA_128x128 = 8,
+    GEMM_ALGO_MFMA_64x64 = 9
+} gemm_algo_t;
+
+/* FP32 inputs, FP32 arithmetic, FP32 C.  Same as gemm_f32_algo(GEMM_ALGO_AUTO, ...). */
+gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K,
+                       const float *A, int64_t lda, gemm_order_t order_a,
+                       const float *B, int64_t ldb, gemm_order_t order_b,
+                       float *C, int64_t ldc, gemm_order_t order_c,
+                       hipStream_t stream);
+
+/* BF16 inputs (raw bit patterns, 2 bytes each), products and sums in FP32, FP32 C.
+ * Same as gemm_bf16_f32acc_algo(GEMM_ALGO_AUTO, ...). */
+gemm_status_t gemm_bf16_f32acc(int64_t M, int64_t N, int64_t K,
+                               const uint16_t *A, int64_t lda, gemm_order_t order_a,
+                               const uint16_t *B, int64_t ldb, gemm_order_t order_b,
+                               float *C, int64_t ldc, gemm_order_t order_c,
+                               hipStream_t stream);
+
+/* As gemm_f32, with the kernel forced (see gemm_algo_t). */
+gemm_status_t gemm_f32_algo(gemm_algo_t algo, int64_t M, int64_t N, int64_t K,
+                            const float *A, int64_t lda, gemm_order_t order_a,
+                            const float *B, int64_t ldb, gemm_order_t order_b,
+                            float *C, int64_t ldc, gemm_order_t order_c,
+                            hipStream_t stream);
+
+/* As gemm_bf16_f32acc, with the kernel forced (AUTO or one of the MFMA values). */
+gemm_status_t gemm_bf16_f32acc_algo(gemm_algo_t algo, int64_t M, int64_t N, int64_t K,
+                                    const uint16_t *A, int64_t lda, gemm_order_t order_a,
+                                    const uint16_t *B, int64_t ldb, gemm_order_t order_b,
+                                    float *C, int64_t ldc, gemm_order_t order_c,
+                                    hipStream_t stream);
+
+/* Static, never-null description of a status code. */
+const char *gemm_status_string(gemm_status_t status);
+
+/* hipError_t of this thread's last GEMM_ERR_LAUNCH (0 if none yet). */
+int gemm_last_hip_error(void);
+
+/* Name of the kernel the last successful call on this thread enqueued (static string,
+ * "none" before any call); for tests and the bench. */
+const char *gemm_last_kernel(void);
+
+/* Library version, e.g. "0.1.0". */
+const char *gemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBGEMM_GEMM_H */

@@ -27,3 +27,15 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def _ensure_built():
+    """Build libgemm.so (and the oracle) in-tree if absent, so a fresh checkout can test."""
+    lib = os.path.join(ROOT, "gemm_f32_amd", "libgemm.so")
+    if not os.path.exists(lib):
+        from gemm_f32_amd import build as _b
+        _b.build()
+
+
+def pytest_sessionstart(session):
+    _ensure_built()

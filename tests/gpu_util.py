@@ -1,0 +1,79 @@
+"""Helpers for the GPU parity tests: run one problem through libgemm's C ABI and compare
+with the fp64 oracle on the same seeded buffers."""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+
+import gemm_f32_amd as g
+import gemm_inputs as gi
+import oracle
+
+TOL = {"f32": 1e-5, "bf16": 1e-4}   # max |C - C_ref| / sum_k |A_ik B_kj|
+
+
+def to_device(buf: np.ndarray):
+    import torch
+    if buf.dtype == np.uint16:
+        buf = buf.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(buf)).to("cuda")
+
+
+def run(p: gi.Problem, algo=g.Algo.AUTO, A=None, B=None):
+    """C buffer (flat, float32 numpy) after one libgemm call; C starts as NaN everywhere."""
+    import torch
+    A = to_device(p.A) if A is None else A
+    B = to_device(p.B) if B is None else B
+    n = gi.c_buffer_size(p.M, p.N, p.ldc, p.order_c)
+    C = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    fn = g.gemm_f32_algo if p.dtype == "f32" else g.gemm_bf16_f32acc_algo
+    print(f"[gpu] {p.dtype} algo={int(algo)} M={p.M} N={p.N} K={p.K} orders=({p.order_a},"
+          f"{p.order_b},{p.order_c}) ld=({p.lda},{p.ldb},{p.ldc})", flush=True)
+    fn(algo, p.M, p.N, p.K, A.data_ptr(), p.lda, p.order_a, B.data_ptr(), p.ldb, p.order_b,
+       C.data_ptr(), p.ldc, p.order_c, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return C.cpu().numpy()
+
+
+def logical_c(p: gi.Problem, flat: np.ndarray) -> np.ndarray:
+    return gi.unpack_c(flat, p.M, p.N, p.ldc, p.order_c)
+
+
+def padding_untouched(p: gi.Problem, flat: np.ndarray) -> bool:
+    """Slots of C beyond the logical matrix (ldc padding) still hold the NaN fill."""
+    if p.M == 0 or p.N == 0:
+        return bool(np.all(np.isnan(flat)))
+    inner = p.N if p.order_c == gi.ROW_MAJOR else p.M
+    return bool(np.all(np.isnan(flat.reshape(-1, p.ldc)[:, inner:])))
+
+
+@functools.lru_cache(maxsize=64)
+def _oracle_cached(key):
+    p = _PROBLEMS[key]
+    return oracle.gemm(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b)
+
+
+_PROBLEMS: dict = {}
+
+
+def reference(p: gi.Problem, key=None):
+    """(C_ref, D) from the oracle; cached per key when one is given."""
+    if key is None:
+        return oracle.gemm(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b)
+    _PROBLEMS[key] = p
+    return _oracle_cached(key)
+
+
+def check(p: gi.Problem, algo=g.Algo.AUTO, key=None, exact=False):
+    """Run and compare element by element; returns the normalised error."""
+    flat = run(p, algo)
+    C = logical_c(p, flat)
+    ref, D = reference(p, key)
+    assert padding_untouched(p, flat), "C written outside the logical matrix"
+    if exact:
+        assert np.array_equal(C.astype(np.float64), ref), "expected a bit-exact result"
+        return 0.0
+    err = oracle.normalised_error(C, ref, D)
+    assert err <= TOL[p.dtype], f"normalised error {err:.3e} > {TOL[p.dtype]:.0e}"
+    return err

@@ -1,0 +1,167 @@
+"""Host-side checks of the C ABI (no kernel runs): exports, argument validation, the
+tile scheduler and the torch-stride marshalling."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import gemm_f32_amd as g
+from conftest import ROOT, gpu_available
+
+HEADER = os.path.join(ROOT, "include", "gemm.h")
+F32, BF16 = g.gemm_f32_algo, g.gemm_bf16_f32acc_algo
+R, C_ = g.Order.ROW_MAJOR, g.Order.COL_MAJOR
+INVALID = g.Status.ERR_INVALID_VALUE
+FAKE = 1 << 20          # a non-null, aligned address; never dereferenced by these calls
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(g.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(g.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", g.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (gemm_\w+)$", out, flags=re.M))
+    assert exported == set(declared_functions())
+
+
+def test_strings():
+    assert g.gemm_version() == "0.1.0"
+    assert g.gemm_status_string(0) == "GEMM_OK"
+    for s in (1, 2, 3):
+        assert g.gemm_status_string(s).startswith(g.Status(s).name.replace("ERR", "GEMM_ERR", 1))
+    assert "unknown" in g.gemm_status_string(99)
+
+
+def _status(fn, *args):
+    try:
+        fn(*args)
+    except g.GemmError as e:
+        return e.status
+    return g.Status.OK
+
+
+def args(M=8, N=8, K=8, A=FAKE, lda=8, oa=R, B=FAKE, ldb=8, ob=R, C=FAKE, ldc=8, oc=R):
+    return (M, N, K, A, lda, oa, B, ldb, ob, C, ldc, oc, 0)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(M=-1), dict(N=-1), dict(K=-1), dict(M=2**31), dict(K=2**31),
+    dict(lda=7), dict(oa=C_, lda=7), dict(ldb=7), dict(ob=C_, ldb=7), dict(ldc=7),
+    dict(oc=C_, ldc=7), dict(lda=0, K=0), dict(oa=2), dict(ob=-1), dict(oc=5),
+    dict(A=0), dict(B=0), dict(C=0), dict(C=FAKE + 2), dict(A=FAKE + 1),
+], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+@pytest.mark.parametrize("fn", [F32, BF16], ids=["f32", "bf16"])
+def test_invalid_arguments_rejected_before_launch(fn, bad):
+    if fn is BF16 and bad.get("A") == FAKE + 1:
+        pytest.skip("odd address is 2-byte aligned: valid for bf16")
+    assert _status(fn, g.Algo.AUTO, *args(**bad)) == INVALID
+
+
+def test_f32_needs_4_byte_alignment_bf16_needs_2():
+    assert _status(F32, g.Algo.AUTO, *args(A=FAKE + 2)) == INVALID
+    assert _status(BF16, g.Algo.AUTO, *args(A=FAKE + 1)) == INVALID
+
+
+@pytest.mark.parametrize("algo", [1, 2, 3, 4])
+def test_bf16_rejects_vector_alu_ladder(algo):
+    assert _status(BF16, algo, *args()) == INVALID
+
+
+@pytest.mark.parametrize("algo", [6, 7, 9, 10, -1])
+def test_f32_rejects_unknown_tiles(algo):
+    assert _status(F32, algo, *args()) == INVALID
+
+
+def test_bf16_rejects_unknown_algo():
+    assert _status(BF16, 10, *args()) == INVALID
+
+
+@pytest.mark.parametrize("shape", [(0, 8, 8), (8, 0, 8), (0, 0, 0)])
+def test_empty_output_is_ok_without_launch(shape):
+    M, N, K = shape
+    # nothing to do: no pointer is touched, no device is needed
+    assert _status(F32, 0, *args(M, N, K, A=0, B=0, C=0, lda=max(K, 1), ldb=max(N, 1),
+                                 ldc=max(N, 1))) == g.Status.OK
+    assert g.gemm_last_kernel() == "none"
+
+
+@pytest.mark.skipif(gpu_available(), reason="checks the no-GPU path")
+def test_valid_call_without_gpu_reports_unsupported_device():
+    assert _status(F32, 0, *args()) == g.Status.ERR_UNSUPPORTED_DEVICE
+
+
+def test_operand_layout_from_torch_strides():
+    torch = pytest.importorskip("torch")
+    a = torch.empty(6, 10)
+    assert g.operand_layout(a) == (10, R)
+    assert g.operand_layout(a.t()) == (10, C_)
+    assert g.operand_layout(torch.empty(6, 16)[:, :10]) == (16, R)
+    assert g.operand_layout(torch.empty(10, 16)[:, :6].t()) == (16, C_)
+    assert g.operand_layout(torch.empty(1, 5)) == (5, R)
+    assert g.operand_layout(torch.empty(5, 1)) == (1, R)
+    with pytest.raises(ValueError):
+        g.operand_layout(torch.empty(6, 10)[:, ::2])
+    with pytest.raises(ValueError):
+        g.operand_layout(torch.empty(2, 3, 4))
+
+
+SCHED_CHECK = r"""
+#include "common.hpp"
+#include <cstdio>
+#include <vector>
+// For each grid: every workgroup id maps to a distinct in-range tile, and the ids one XCD
+// receives (w % 8 equal) cover tiles that share few row/column panels.
+int main() {
+    const int shapes[][3] = {{16,16,4},{16,16,1},{1,1,1},{3,5,2},{8,43,4},{16,86,8},{33,17,4},
+                             {1,64,1},{7,9,8},{32,32,4},{2,344,2}};
+    for (auto& s : shapes) {
+        const int tm_ = s[0], tn_ = s[1], gm = s[2];
+        std::vector<int> seen(tm_ * tn_, 0);
+        for (int w = 0; w < tm_ * tn_; ++w) {
+            int a, b;
+            gemm::tile_coords(w, tm_, tn_, gm, a, b);
+            if (a < 0 || a >= tm_ || b < 0 || b >= tn_) { printf("range %d %d %d\n", tm_, tn_, w); return 1; }
+            if (seen[a * tn_ + b]++) { printf("dup %d %d %d\n", tm_, tn_, w); return 1; }
+        }
+    }
+    // 4096^2 output in 256^2 tiles, group 4: XCD x gets a 4 x 8 block of tiles
+    for (int x = 0; x < 8; ++x) {
+        int rmin = 99, rmax = -1, cmin = 99, cmax = -1;
+        for (int w = x; w < 256; w += 8) {
+            int a, b;
+            gemm::tile_coords(w, 16, 16, 4, a, b);
+            rmin = a < rmin ? a : rmin; rmax = a > rmax ? a : rmax;
+            cmin = b < cmin ? b : cmin; cmax = b > cmax ? b : cmax;
+        }
+        if (rmax - rmin != 3 || cmax - cmin != 7) { printf("xcd %d block %d x %d\n", x, rmax-rmin+1, cmax-cmin+1); return 1; }
+    }
+    printf("ok\n");
+    return 0;
+}
+"""
+
+
+def test_tile_scheduler_is_a_bijection_with_xcd_blocks():
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "sched.hip")
+        exe = os.path.join(d, "sched")
+        open(src, "w").write(SCHED_CHECK)
+        subprocess.run(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O1",
+                        f"-I{os.path.join(ROOT, 'gemm_f32_amd', 'csrc')}", src, "-o", exe],
+                       check=True, capture_output=True)
+        r = subprocess.run([exe], capture_output=True, text=True)
+        assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout

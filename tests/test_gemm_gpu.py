@@ -1,0 +1,155 @@
+"""GPU parity: every libgemm kernel against the fp64 oracle on the same seeded inputs.
+
+Tolerance: max over C of |C_gpu - C_ref| / sum_k |A_ik B_kj|  <=  1e-5 (FP32) and
+<= 1e-4 (BF16 inputs, FP32 accumulate).  Closed-form and small-integer cases must be
+bit-exact, because any summation order gives the exact result there.
+"""
+import numpy as np
+import pytest
+
+import gemm_f32_amd as g
+import gemm_inputs as gi
+import oracle
+from gemm_inputs import COL_MAJOR, ROW_MAJOR
+from gpu_util import TOL, check, logical_c, padding_untouched, run, to_device
+
+pytestmark = pytest.mark.gpu
+
+F32_ALGOS = [g.Algo.NAIVE_UNCOALESCED, g.Algo.NAIVE, g.Algo.TILED, g.Algo.REGBLOCK,
+             g.Algo.MFMA, g.Algo.AUTO]
+BF16_ALGOS = [g.Algo.MFMA_256x256, g.Algo.MFMA_256x128, g.Algo.MFMA_128x128,
+              g.Algo.MFMA_64x64, g.Algo.AUTO]
+CASES = [("f32", a) for a in F32_ALGOS] + [("bf16", a) for a in BF16_ALGOS]
+CASE_IDS = [f"{d}-{a.name}" for d, a in CASES]
+ORDERS3 = [(a, b, c) for a in (ROW_MAJOR, COL_MAJOR) for b in (ROW_MAJOR, COL_MAJOR)
+           for c in (ROW_MAJOR, COL_MAJOR)]
+
+
+# --- closed forms at the pages' 16 x 16 x 16 worked size and beyond ---------------------
+@pytest.mark.parametrize("dtype,algo", CASES, ids=CASE_IDS)
+@pytest.mark.parametrize("n", [16, 64, 129])
+def test_closed_forms(dtype, algo, n):
+    ones = gi.make_problem(n, n, n, dtype, A_logical=np.ones((n, n)), B_logical=np.ones((n, n)))
+    C = logical_c(ones, run(ones, algo))
+    assert np.all(C == n), "A = B = ones must give C = K"
+    ident = gi.make_problem(n, n, n, dtype, wid=31, A_logical=np.eye(n))
+    C = logical_c(ident, run(ident, algo))
+    assert np.array_equal(C, ident.b_f32()), "A = I must reproduce B bit for bit"
+    perm = np.random.default_rng(n).permutation(n)
+    P = np.zeros((n, n)); P[np.arange(n), perm] = 1.0
+    pb = gi.make_problem(n, n, n, dtype, wid=32, B_logical=P)
+    C = logical_c(pb, run(pb, algo))
+    assert np.array_equal(C, pb.a_f32()[:, np.argsort(perm)]), "B = P must permute columns of A"
+    pa = gi.make_problem(n, n, n, dtype, wid=33, A_logical=P)
+    C = logical_c(pa, run(pa, algo))
+    assert np.array_equal(C, pa.b_f32()[perm]), "A = P must permute rows of B"
+
+
+# --- small integers: exact under any summation order, so GPU == oracle bit for bit ------
+@pytest.mark.parametrize("dtype,algo", CASES, ids=CASE_IDS)
+@pytest.mark.parametrize("shape", [(64, 64, 64), (300, 257, 129), (33, 517, 1000)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_small_integer_exact(dtype, algo, shape):
+    M, N, K = shape
+    rng = np.random.default_rng(M * 7 + N)
+    A = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    B = rng.integers(-4, 5, (K, N)).astype(np.float32)
+    p = gi.make_problem(M, N, K, dtype, A_logical=A, B_logical=B)
+    check(p, algo, exact=True)
+
+
+# --- random inputs, every order combination, ragged shapes ------------------------------
+SHAPES = [(1, 1, 1), (256, 256, 256), (257, 259, 65), (5, 300, 7), (300, 5, 1000),
+          (129, 67, 300)]
+
+
+@pytest.mark.parametrize("dtype,algo", CASES, ids=CASE_IDS)
+@pytest.mark.parametrize("orders", ORDERS3, ids=lambda o: "".join("RC"[x] for x in o))
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_parity_random(dtype, algo, orders, shape):
+    M, N, K = shape
+    p = gi.make_problem(M, N, K, dtype, *orders, wid=40)
+    check(p, algo, key=("rand", dtype, orders, shape))
+
+
+# --- the teaching module's boundary trio: only a ragged K exposes a missing zero fill ---
+@pytest.mark.parametrize("dtype,algo", CASES, ids=CASE_IDS)
+@pytest.mark.parametrize("shape", [(1024, 1024, 1024), (1000, 700, 1024), (1000, 700, 1000)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_boundary_trio(dtype, algo, shape):
+    if algo in (g.Algo.NAIVE_UNCOALESCED,) and shape[0] > 512:
+        pytest.skip("uncoalesced rung is slow; covered at the smaller shapes")
+    M, N, K = shape
+    oa, ob = (ROW_MAJOR, ROW_MAJOR) if dtype == "f32" else (ROW_MAJOR, COL_MAJOR)
+    p = gi.make_problem(M, N, K, dtype, oa, ob, dist="unit", wid=41)
+    check(p, algo, key=("trio", dtype, shape))
+
+
+# --- K below the tile depth, K = 0, empty outputs ---------------------------------------
+@pytest.mark.parametrize("dtype,algo", CASES, ids=CASE_IDS)
+@pytest.mark.parametrize("K", [1, 3, 8, 15, 31, 63])
+def test_k_below_tile(dtype, algo, K):
+    p = gi.make_problem(130, 200, K, dtype, ROW_MAJOR, COL_MAJOR if dtype == "bf16" else ROW_MAJOR, wid=42)
+    check(p, algo)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("oc", [ROW_MAJOR, COL_MAJOR])
+def test_k_zero_sets_c_to_zero(dtype, oc):
+    p = gi.make_problem(37, 45, 0, dtype, order_c=oc, pad_c=3)
+    flat = run(p)
+    C = logical_c(p, flat)
+    assert np.all(C == 0) and padding_untouched(p, flat)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(0, 5, 7), (5, 0, 7), (0, 0, 0)])
+def test_empty_output_untouched(dtype, shape):
+    p = gi.make_problem(*shape, dtype)
+    flat = run(p)
+    assert np.all(np.isnan(flat))
+
+
+# --- leading dimensions beyond the minimum, aligned and not -----------------------------
+@pytest.mark.parametrize("dtype,algo", CASES, ids=CASE_IDS)
+@pytest.mark.parametrize("pad", [1, 3, 8])
+def test_padded_leading_dimensions(dtype, algo, pad):
+    for orders in [(ROW_MAJOR, ROW_MAJOR, ROW_MAJOR), (ROW_MAJOR, COL_MAJOR, COL_MAJOR),
+                   (COL_MAJOR, ROW_MAJOR, ROW_MAJOR)]:
+        p = gi.make_problem(200, 264, 136, dtype, *orders, wid=43, pad_a=pad, pad_b=2 * pad,
+                            pad_c=pad)
+        check(p, algo)
+
+
+# --- determinism: no atomics, so repeated runs agree bit for bit ------------------------
+@pytest.mark.parametrize("dtype,algo", [("f32", g.Algo.REGBLOCK), ("f32", g.Algo.MFMA),
+                                        ("bf16", g.Algo.MFMA_256x256), ("bf16", g.Algo.MFMA_128x128)],
+                         ids=lambda x: str(x))
+def test_repeated_runs_identical(dtype, algo):
+    p = gi.make_problem(777, 1025, 513, dtype, ROW_MAJOR, COL_MAJOR, wid=44)
+    A, B = to_device(p.A), to_device(p.B)
+    first = run(p, algo, A, B)
+    for _ in range(9):
+        assert np.array_equal(run(p, algo, A, B), first, equal_nan=True)
+
+
+# --- the torch-facing helper -------------------------------------------------------------
+def test_matmul_helper_on_tensors_and_views():
+    import torch
+    rng = np.random.default_rng(5)
+    a = torch.from_numpy(rng.uniform(-1, 1, (300, 200)).astype(np.float32)).cuda()
+    b = torch.from_numpy(rng.uniform(-1, 1, (200, 100)).astype(np.float32)).cuda()
+    ref = (a.double() @ b.double()).cpu().numpy()
+    D = (a.abs().double() @ b.abs().double()).cpu().numpy()
+    for x, y in [(a, b), (a.t().contiguous().t(), b), (a, b.t().contiguous().t())]:
+        out = g.matmul(x, y)
+        assert oracle.normalised_error(out.cpu().numpy(), ref, D) <= TOL["f32"]
+    out_cm = torch.empty(100, 300, device="cuda").t()           # column-major C
+    g.matmul(a, b, out=out_cm)
+    assert oracle.normalised_error(out_cm.cpu().numpy(), ref, D) <= TOL["f32"]
+    ab, bb = a.bfloat16(), b.bfloat16()
+    refb = (ab.double() @ bb.double()).cpu().numpy()
+    Db = (ab.abs().double() @ bb.abs().double()).cpu().numpy()
+    out = g.matmul(ab, bb.t().contiguous().t())
+    assert oracle.normalised_error(out.cpu().numpy(), refb, Db) <= TOL["bf16"]
+    assert g.gemm_last_kernel().startswith("bf16_mfma")

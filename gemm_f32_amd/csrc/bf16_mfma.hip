@@ -48,6 +48,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned short u16;
+typedef __attribute__((address_space(3))) void lds_void;
 
 template <int BM_, int BN_>
 struct Tile {
@@ -59,61 +60,64 @@ struct Tile {
     static constexpr int B_CHUNKS = BN * 8 / THREADS;
     static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
     static constexpr int STAGE = A_BYTES + B_BYTES;
+    // direct global->LDS copies: each wavefront fills BM/4 rows of A and BN/4 rows of B,
+    // 8 rows (1 KB, one 16-byte chunk per lane) per instruction
+    static constexpr int A_RPW = BM / 4, B_RPW = BN / 4;
+    static constexpr int A_DMA = A_RPW / 8, B_DMA = B_RPW / 8;
 };
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 // One operand as the loader sees it: `rows` (M for A, N for B) by K, stored with k
-// contiguous (KC) or with rows contiguous.
+// contiguous (KC) or with rows contiguous (RC).
 struct Operand {
     const u16* p;
     int64_t ld;
     int rows;
 };
 
-// Chunk q of a KC operand tile: tile row q / 8, chunk q % 8 (k = 8 * (q % 8) .. +7).
-template <int TR>
-__device__ __forceinline__ uint4 load_kc(const Operand& x, int row0, int k0, int K, int q,
-                                         bool fast) {
-    const int r = q >> 3, c = q & 7;
-    if (fast) {
-        const int row = min(row0 + r, x.rows - 1);
-        return *reinterpret_cast<const uint4*>(x.p + (int64_t)row * x.ld + k0 + c * 8);
-    }
-    u16 v[8];
-    const int row = row0 + r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int k = k0 + c * 8 + e;
-        v[e] = (row < x.rows && k < K) ? x.p[(int64_t)row * x.ld + k] : (u16)0;
-    }
+__device__ __forceinline__ uint4 pack8(const u16 (&v)[8]) {
     return make_uint4(v[0] | (unsigned)v[1] << 16, v[2] | (unsigned)v[3] << 16,
                       v[4] | (unsigned)v[5] << 16, v[6] | (unsigned)v[7] << 16);
 }
 
-template <int TR>
+// Chunk q of a KC tile: tile row q / 8, k = 8 * (q % 8) .. +7.  The fast form needs a
+// full k-tile and 16-byte alignment; rows past the edge are clamped to the last row.
+__device__ __forceinline__ uint4 load_kc_fast(const Operand& x, int row0, int k0, int q) {
+    const int row = min(row0 + (q >> 3), x.rows - 1);
+    return *reinterpret_cast<const uint4*>(x.p + (int64_t)row * x.ld + k0 + (q & 7) * 8);
+}
+__device__ __forceinline__ uint4 load_kc_checked(const Operand& x, int row0, int k0, int K, int q) {
+    const int row = row0 + (q >> 3), kb = k0 + (q & 7) * 8;
+    u16 v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        v[e] = (row < x.rows && kb + e < K) ? x.p[(int64_t)row * x.ld + kb + e] : (u16)0;
+    return pack8(v);
+}
 __device__ __forceinline__ void store_kc(unsigned char* s, int q, uint4 v) {
     const int r = q >> 3, c = q & 7;
     *reinterpret_cast<uint4*>(s + r * 128 + ((c ^ swz(r)) << 4)) = v;
 }
 
-// Chunk q of a row-contiguous operand tile: k = q / (TR / 8), rows 8 * (q % (TR / 8)) .. +7.
+// Chunk q of an RC tile: k = q / (TR / 8), tile rows 8 * (q % (TR / 8)) .. +7.  The fast
+// form needs the whole tile inside the matrix, a full k-tile and 16-byte alignment.
 template <int TR>
-__device__ __forceinline__ uint4 load_rc(const Operand& x, int row0, int k0, int K, int q,
-                                         bool fast) {
-    constexpr int CPK = TR / 8;   // chunks per k
-    const int k = q / CPK, r = (q % CPK) * 8;
-    if (fast) return *reinterpret_cast<const uint4*>(x.p + (int64_t)(k0 + k) * x.ld + row0 + r);
+__device__ __forceinline__ uint4 load_rc_fast(const Operand& x, int row0, int k0, int q) {
+    constexpr int CPK = TR / 8;
+    return *reinterpret_cast<const uint4*>(x.p + (int64_t)(k0 + q / CPK) * x.ld + row0 + (q % CPK) * 8);
+}
+template <int TR>
+__device__ __forceinline__ uint4 load_rc_checked(const Operand& x, int row0, int k0, int K, int q) {
+    constexpr int CPK = TR / 8;
+    const int k = k0 + q / CPK, r = row0 + (q % CPK) * 8;
     u16 v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int row = row0 + r + e;
-        v[e] = (row < x.rows && k0 + k < K) ? x.p[(int64_t)(k0 + k) * x.ld + row] : (u16)0;
-    }
-    return make_uint4(v[0] | (unsigned)v[1] << 16, v[2] | (unsigned)v[3] << 16,
-                      v[4] | (unsigned)v[5] << 16, v[6] | (unsigned)v[7] << 16);
+    for (int e = 0; e < 8; ++e)
+        v[e] = (r + e < x.rows && k < K) ? x.p[(int64_t)k * x.ld + r + e] : (u16)0;
+    return pack8(v);
 }
-
+// Scatter the 8 values of an RC chunk into the k-contiguous LDS layout.
 template <int TR>
 __device__ __forceinline__ void store_rc(unsigned char* s, int q, uint4 v) {
     constexpr int CPK = TR / 8;
@@ -131,55 +135,73 @@ template <int BM, int BN, bool A_KC, bool B_KC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, int vec_b) {
     using T = Tile<BM, BN>;
+    // the direct path issues its copies in the first 4 * FM * FN instruction slots
+    static_assert(4 * T::FM * T::FN >= T::A_DMA + T::B_DMA, "too few slots for the copies");
     __shared__ __align__(16) unsigned char smem[2 * T::STAGE];
 
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = (wave >> 1) * T::WM, wn = (wave & 1) * T::WN;
     const int K = p.K;
     const int nk = (K + T::BK - 1) / T::BK;
+    const int nfull = K / T::BK;
     const bool interior = (m0 + BM <= p.M) && (n0 + BN <= p.N);
 
     const Operand a{static_cast<const u16*>(p.A), p.lda, p.M};
     const Operand b{static_cast<const u16*>(p.B), p.ldb, p.N};
-    // 16-byte loads need aligned pointers/leading dimensions; a row-contiguous operand also
-    // needs its whole tile inside the matrix (no clamping across a chunk).
-    const bool fast_a = vec_a && (A_KC || m0 + BM <= p.M);
-    const bool fast_b = vec_b && (B_KC || n0 + BN <= p.N);
+    // 16-byte loads of a whole k-tile: aligned operands, and a row-contiguous operand only
+    // when its tile lies inside the matrix (a k-contiguous one clamps edge rows instead)
+    const bool vec_tiles = vec_a && vec_b && (A_KC || m0 + BM <= p.M) && (B_KC || n0 + BN <= p.N);
 
+    // ---- register-staged 16-byte loads (full k-tiles when the direct copy does not apply)
     uint4 ra[T::A_CHUNKS], rb[T::B_CHUNKS];
-    auto gload = [&](int k0) {
-        const bool full = k0 + T::BK <= K;
+    auto gload_fast = [&](int k0) {
 #pragma unroll
-        for (int s = 0; s < T::A_CHUNKS; ++s) {
-            const int q = t + s * T::THREADS;
-            ra[s] = A_KC ? load_kc<BM>(a, m0, k0, K, q, fast_a && full)
-                         : load_rc<BM>(a, m0, k0, K, q, fast_a && full);
-        }
+        for (int s = 0; s < T::A_CHUNKS; ++s)
+            ra[s] = A_KC ? load_kc_fast(a, m0, k0, t + s * T::THREADS)
+                         : load_rc_fast<BM>(a, m0, k0, t + s * T::THREADS);
 #pragma unroll
-        for (int s = 0; s < T::B_CHUNKS; ++s) {
-            const int q = t + s * T::THREADS;
-            rb[s] = B_KC ? load_kc<BN>(b, n0, k0, K, q, fast_b && full)
-                         : load_rc<BN>(b, n0, k0, K, q, fast_b && full);
-        }
+        for (int s = 0; s < T::B_CHUNKS; ++s)
+            rb[s] = B_KC ? load_kc_fast(b, n0, k0, t + s * T::THREADS)
+                         : load_rc_fast<BN>(b, n0, k0, t + s * T::THREADS);
     };
     auto lstore = [&](int stage) {
         unsigned char* sa = smem + stage * T::STAGE;
         unsigned char* sb = sa + T::A_BYTES;
 #pragma unroll
         for (int s = 0; s < T::A_CHUNKS; ++s) {
-            const int q = t + s * T::THREADS;
-            if (A_KC) store_kc<BM>(sa, q, ra[s]); else store_rc<BM>(sa, q, ra[s]);
+            if (A_KC) store_kc(sa, t + s * T::THREADS, ra[s]);
+            else store_rc<BM>(sa, t + s * T::THREADS, ra[s]);
         }
 #pragma unroll
         for (int s = 0; s < T::B_CHUNKS; ++s) {
+            if (B_KC) store_kc(sb, t + s * T::THREADS, rb[s]);
+            else store_rc<BN>(sb, t + s * T::THREADS, rb[s]);
+        }
+    };
+    // ---- element-wise loads with bounds checks and zero fill, one chunk at a time (the K
+    // tail, misaligned operands, edge tiles of a row-contiguous operand)
+    auto load_store_checked = [&](int k0, int stage) {
+        unsigned char* sa = smem + stage * T::STAGE;
+        unsigned char* sb = sa + T::A_BYTES;
+#pragma unroll 1
+        for (int s = 0; s < T::A_CHUNKS; ++s) {
             const int q = t + s * T::THREADS;
-            if (B_KC) store_kc<BN>(sb, q, rb[s]); else store_rc<BN>(sb, q, rb[s]);
+            if (A_KC) store_kc(sa, q, load_kc_checked(a, m0, k0, K, q));
+            else store_rc<BM>(sa, q, load_rc_checked<BM>(a, m0, k0, K, q));
+        }
+#pragma unroll 1
+        for (int s = 0; s < T::B_CHUNKS; ++s) {
+            const int q = t + s * T::THREADS;
+            if (B_KC) store_kc(sb, q, load_kc_checked(b, n0, k0, K, q));
+            else store_rc<BN>(sb, q, load_rc_checked<BN>(b, n0, k0, K, q));
         }
     };
 
+    // ---- fragments and matrix instructions on one LDS stage ----
     f32x16 acc[T::FM][T::FN];
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
@@ -188,37 +210,112 @@ void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, in
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
     const int lr = lane & 31, h = lane >> 5;
     const int sw = swz(lr);                    // == swz(wm + 32 i + lr): wm, 32 i are multiples of 32
     const int a_off = (wm + lr) * 128;
     const int b_off = T::A_BYTES + (wn + lr) * 128;
-
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) gload((kt + 1) * T::BK);
-        const unsigned char* st = smem + cur * T::STAGE;
+    auto read_frags = [&](const unsigned char* st, int s, bf16x8 (&fa)[T::FM], bf16x8 (&fb)[T::FN]) {
+        const int coff = ((2 * s + h) ^ sw) << 4;
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i)
+            fa[i] = *reinterpret_cast<const bf16x8*>(st + a_off + i * 32 * 128 + coff);
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j)
+            fb[j] = *reinterpret_cast<const bf16x8*>(st + b_off + j * 32 * 128 + coff);
+    };
+    // One k-tile: 4 sub-steps of 16 k.  Fragments are double-buffered in registers so that
+    // the LDS reads of sub-step s + 1 are in flight while the matrix instructions of
+    // sub-step s run.  `copy(n)` is called before the n-th matrix instruction (n < 64) to
+    // fold the next tile's global->LDS copies into the same instruction stream.  Source
+    // order is issue order (sched_barrier fences).
+    auto compute = [&](int stage, auto copy) {
+        const unsigned char* st = smem + stage * T::STAGE;
+        bf16x8 fa[2][T::FM], fb[2][T::FN];
+        read_frags(st, 0, fa[0], fb[0]);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const int coff = ((2 * s + h) ^ sw) << 4;
-            bf16x8 fa[T::FM], fb[T::FN];
+            const int coff = ((2 * (s + 1) + h) ^ sw) << 4;
+            // MF matrix instructions and RD fragment reads per sub-step; small tiles have
+            // fewer instructions than reads, so the loop runs over the larger count
+            constexpr int MF = T::FM * T::FN, RD = T::FM + T::FN;
 #pragma unroll
-            for (int i = 0; i < T::FM; ++i)
-                fa[i] = *reinterpret_cast<const bf16x8*>(st + a_off + i * 32 * 128 + coff);
-#pragma unroll
-            for (int j = 0; j < T::FN; ++j)
-                fb[j] = *reinterpret_cast<const bf16x8*>(st + b_off + j * 32 * 128 + coff);
-#pragma unroll
-            for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-                for (int j = 0; j < T::FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            for (int m = 0; m < (MF > RD ? MF : RD); ++m) {
+                if (m < MF) copy(s * MF + m);
+                if (s < 3 && m < T::FM)
+                    fa[(s + 1) & 1][m] = *reinterpret_cast<const bf16x8*>(st + a_off + m * 32 * 128 + coff);
+                else if (s < 3 && m < RD)
+                    fb[(s + 1) & 1][m - T::FM] =
+                        *reinterpret_cast<const bf16x8*>(st + b_off + (m - T::FM) * 32 * 128 + coff);
+                if (m < MF) {
+                    const int i = m / T::FN, j = m % T::FN;
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j],
+                                                                         acc[i][j], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        if (more) lstore(cur ^ 1);
+    };
+    auto no_copy = [](int) {};
+
+    int kt = 0;
+    if (A_KC && B_KC && vec_a && vec_b && interior && nfull > 0) {
+        // ---- direct path: full k-tiles copied global -> LDS without registers ----
+        // Copy j of a wavefront fills tile rows r = r0 + 8 j .. +7 (r0 = the wavefront's
+        // first row); lane l fetches the chunk that belongs at LDS position l of that 1 KB
+        // block: row r0 + 8 j + l / 8, logical chunk (l % 8) ^ s(row).  With r0 a multiple
+        // of 16, s(row) = (l / 8) ^ (j & 1), so a lane needs two byte offsets (even and odd
+        // j) on top of a wavefront-uniform row address.
+        const int arow0 = m0 + wave * T::A_RPW, brow0 = n0 + wave * T::B_RPW;
+        const char* abase = reinterpret_cast<const char*>(a.p + (int64_t)arow0 * a.ld);
+        const char* bbase = reinterpret_cast<const char*>(b.p + (int64_t)brow0 * b.ld);
+        const int lrow = lane >> 3, lchunk = (lane & 7) ^ (lane >> 3);
+        unsigned aoff[2], boff[2];
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+            aoff[par] = (unsigned)((lrow * a.ld + (lchunk ^ par) * 8) * 2);
+            boff[par] = (unsigned)((lrow * b.ld + (lchunk ^ par) * 8) * 2);
+        }
+        auto issue_one = [&](int j, int k0, int stage) {   // copy j of this wavefront
+            unsigned char* sa = smem + stage * T::STAGE + wave * T::A_RPW * 128;
+            unsigned char* sb = smem + stage * T::STAGE + T::A_BYTES + wave * T::B_RPW * 128;
+            if (j < T::A_DMA) {
+                const char* g = abase + ((int64_t)j * 8 * a.ld + k0) * 2;
+                __builtin_amdgcn_global_load_lds(g + aoff[j & 1], (lds_void*)(sa + j * 1024), 16, 0, 0);
+            } else {
+                const int jb = j - T::A_DMA;
+                const char* g = bbase + ((int64_t)jb * 8 * b.ld + k0) * 2;
+                __builtin_amdgcn_global_load_lds(g + boff[jb & 1], (lds_void*)(sb + jb * 1024), 16, 0, 0);
+            }
+        };
+        for (int j = 0; j < T::A_DMA + T::B_DMA; ++j) issue_one(j, 0, 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        for (; kt + 1 < nfull; ++kt) {
+            const int k0n = (kt + 1) * T::BK, stn = (kt + 1) & 1;
+            compute(kt & 1, [&](int n) {
+                if (n < T::A_DMA + T::B_DMA) issue_one(n, k0n, stn);
+            });
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+    } else if (vec_tiles && nfull > 0) {
+        gload_fast(0);
+        lstore(0);
+        __syncthreads();
+    } else {
+        load_store_checked(0, 0);
+        __syncthreads();
+    }
+    // ---- remaining k-tiles through registers: the last full tile of the direct path and
+    // the K tail, or every tile when the direct copy does not apply ----
+    for (; kt < nk; ++kt) {
+        const int k0n = (kt + 1) * T::BK, stn = (kt + 1) & 1;
+        const bool more = kt + 1 < nk;
+        const bool next_fast = more && vec_tiles && k0n + T::BK <= K;
+        if (next_fast) gload_fast(k0n);
+        compute(kt & 1, no_copy);
+        if (next_fast) lstore(stn);
+        else if (more) load_store_checked(k0n, stn);
         __syncthreads();
     }
 

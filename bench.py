@@ -46,7 +46,54 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target host time of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain 256 MiB device-to-device copy instead (the reference "
+                         "for scaling FETCH_SIZE / WRITE_SIZE counters to bytes)")
     return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    """Hash of the library's kernel sources; counter-derived traffic is only reported for
+    the sources it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gemm_f32_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from profiles/traffic.json (FETCH_SIZE + WRITE_SIZE, scaled by
+    the copy calibration), or None when absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(f"{kernel}@{workload}")
+    if not rec or rec.get("source_digest") != kernel_source_digest():
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def copy_calibration(args):
+    import torch
+    n = 256 * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "ms": round(ms, 4),
+                      "GB/s": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 class Leg:
@@ -121,6 +168,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args)
+        return
     import torch
     import gemm_f32_amd as g
     from gemm_f32_amd import roofline as rl
@@ -165,7 +215,7 @@ def main():
     achieved = dom.flops / (di["ms"] * 1e-3)
     roof = {"bound": "mfma", "kernel": di["kernel"], "achieved": round(achieved / 1e12, 2),
             "peak": round(peak / 1e12, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-            "traffic": None,
+            "traffic": measured_traffic(di["kernel"], dom.name),
             "per_launch": f"2*M*N*K = {dom.flops:.4e} FLOP per launch ({dom.name})"}
 
     value = step_flops / (ms_step * 1e-3) / 1e12

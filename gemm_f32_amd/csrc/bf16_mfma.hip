@@ -6,31 +6,34 @@
 // (GEMM)", "Matrix cores: MFMA and Tensor Cores").  Those kernels were written for other
 // hardware; this one is laid out for gfx950:
 //
-//  * Block tile BM x BN (256 x 256, 256 x 128, 128 x 128 or 64 x 64) swept in BK = 64
-//    slices, 4 wavefronts in a 2 x 2 grid.  A wavefront owns (BM/2) x (BN/2) of C as
+//  * Block tile BM x BN (256 x 256, 256 x 128, 128 x 128 or 64 x 64) swept in BK = 32 or
+//    64 slices, 4 wavefronts in a 2 x 2 grid.  A wavefront owns (BM/2) x (BN/2) of C as
 //    32 x 32 fragments; at 256 x 256 that is 4 x 4 fragments = 256 FP32 accumulators
 //    per lane, which the compiler keeps in the accumulation registers.  Large tiles are
 //    what a matrix-core GEMM needs to stay fed ("A06", three consequences of matrix
 //    cores: the ridge moves right).
-//  * Both operands live in LDS k-contiguous: a row of 64 bf16 = 128 bytes = eight
-//    16-byte chunks, tile rows are rows of A and columns of B.  One lane's operand for
-//    one instruction is one 16-byte chunk (8 consecutive k), read with ds_read_b128.
-//  * Chunk c of LDS row r is stored at position c ^ s(r), s(r) = (r mod 8) xor bit 3 of
-//    r.  The 32 lanes that read one fragment read 32 consecutive rows at the same
-//    logical chunk; the XOR spreads any 16 consecutive rows over 16 distinct 16-byte
-//    bank groups, so the reads are free of bank conflicts whether the LDS serves 8 or 16
-//    lanes of a 16-byte read per cycle.  (The pages pad rows by one word; the XOR does the
-//    same job for 16-byte accesses without wasting LDS.)
+//  * Both operands live in LDS k-contiguous: a row of BK bf16 = BK/8 16-byte chunks,
+//    tile rows are rows of A and columns of B.  One lane's operand for one instruction is
+//    one 16-byte chunk (8 consecutive k), read with ds_read_b128.
+//  * Chunk c of LDS row r is stored at position c ^ s(r).  The 32 lanes that read one
+//    fragment read 32 consecutive rows at the same logical chunk; s spreads any 16
+//    consecutive rows over 16 distinct 16-byte bank groups (8 chunks per row: s(r) =
+//    (r mod 8) xor bit 3 of r; 4 chunks: s(r) = (r/2 xor r/8) mod 4), so the reads are
+//    free of bank conflicts whether the LDS serves 8 or 16 lanes of a 16-byte read per
+//    cycle.  (The pages pad rows by one word; the XOR does the same job for 16-byte
+//    accesses without wasting LDS.)
 //  * Fragment k-assignment: for sub-step s of a k-tile, lanes 0-31 supply chunk 2s and
 //    lanes 32-63 chunk 2s+1, for A and B alike.  Any assignment that pairs the same k
 //    on both operands gives the same sum of products, so the instruction's own k-lane
 //    order never needs to match the memory order.
 //  * Accumulator layout of the 32 x 32 result: lane l, register r holds C[i][j] with
 //    j = l % 32 and i = 8 (r / 4) + 4 (l / 32) + r % 4.
-//  * Double-buffered LDS (2 stages, 128 KB at 256 x 256 of the 160 KB per CU): the next
-//    k-tile's global loads are issued into registers before the current tile's
-//    fragments are read and multiplied, then stored to the other stage; one barrier per
-//    k-tile ("GEMM Optimization", V3; "A06", "The next two rungs").
+//  * Multi-stage LDS pipeline ("GEMM Optimization", V3; "A06", "The next two rungs"):
+//    with S stages the copies of k-tile kt + S - 1 are in flight while tile kt is
+//    multiplied (256 x 256 uses BK = 32 and 4 stages = 128 KB of the 160 KB per CU), one
+//    barrier per k-tile.  Aligned, interior tiles with both operands k-contiguous copy
+//    global -> LDS directly (global_load_lds_dwordx4, no registers); other tiles stage
+//    through registers with 2 stages.
 //  * Loads: a k-contiguous operand (row-major A, column-major B) is fetched in 16-byte
 //    chunks along k; rows past the matrix edge are clamped to the last row (their
 //    products only feed outputs that are never stored).  An operand contiguous along
@@ -50,23 +53,34 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned short u16;
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int BM_, int BN_>
+template <int BM_, int BN_, int BK_, int S_>
 struct Tile {
-    static constexpr int BM = BM_, BN = BN_, BK = 64;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_;
+    static constexpr int CH = BK / 8;                   // 16-byte chunks per LDS row
+    static constexpr int ROW = BK * 2;                  // LDS row bytes
+    static constexpr int SUB = BK / 16;                 // matrix-instruction k-steps per tile
     static constexpr int WM = BM / 2, WN = BN / 2;      // 2 x 2 wavefronts
     static constexpr int THREADS = 256;
     static constexpr int FM = WM / 32, FN = WN / 32;    // 32 x 32 fragments per wavefront
-    static constexpr int A_CHUNKS = BM * 8 / THREADS;   // 16-byte chunks per thread per k-tile
-    static constexpr int B_CHUNKS = BN * 8 / THREADS;
-    static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+    static constexpr int A_CHUNKS = BM * CH / THREADS;  // 16-byte chunks per thread per k-tile
+    static constexpr int B_CHUNKS = BN * CH / THREADS;
+    static constexpr int A_BYTES = BM * ROW, B_BYTES = BN * ROW;
     static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int LDS = (S > 2 ? S : 2) * STAGE;
     // direct global->LDS copies: each wavefront fills BM/4 rows of A and BN/4 rows of B,
-    // 8 rows (1 KB, one 16-byte chunk per lane) per instruction
+    // RPI rows (1 KB, one 16-byte chunk per lane) per instruction
+    static constexpr int RPI = 1024 / ROW;
     static constexpr int A_RPW = BM / 4, B_RPW = BN / 4;
-    static constexpr int A_DMA = A_RPW / 8, B_DMA = B_RPW / 8;
+    static constexpr int A_DMA = A_RPW / RPI, B_DMA = B_RPW / RPI;
+    static_assert(A_CHUNKS >= 1 && B_CHUNKS >= 1 && A_DMA >= 1 && B_DMA >= 1, "tile too small");
+    static_assert(A_RPW % 16 == 0 && B_RPW % 16 == 0, "wavefront row blocks must be 16-aligned");
 };
 
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+template <int CH>
+__device__ __forceinline__ int swz(int row) {
+    if (CH == 8) return (row & 7) ^ ((row >> 3) & 1);
+    return ((row >> 1) ^ (row >> 3)) & 3;
+}
 
 // One operand as the loader sees it: `rows` (M for A, N for B) by K, stored with k
 // contiguous (KC) or with rows contiguous (RC).
@@ -81,23 +95,26 @@ __device__ __forceinline__ uint4 pack8(const u16 (&v)[8]) {
                       v[4] | (unsigned)v[5] << 16, v[6] | (unsigned)v[7] << 16);
 }
 
-// Chunk q of a KC tile: tile row q / 8, k = 8 * (q % 8) .. +7.  The fast form needs a
+// Chunk q of a KC tile: tile row q / CH, k = 8 * (q % CH) .. +7.  The fast form needs a
 // full k-tile and 16-byte alignment; rows past the edge are clamped to the last row.
+template <int CH>
 __device__ __forceinline__ uint4 load_kc_fast(const Operand& x, int row0, int k0, int q) {
-    const int row = min(row0 + (q >> 3), x.rows - 1);
-    return *reinterpret_cast<const uint4*>(x.p + (int64_t)row * x.ld + k0 + (q & 7) * 8);
+    const int row = min(row0 + q / CH, x.rows - 1);
+    return *reinterpret_cast<const uint4*>(x.p + (int64_t)row * x.ld + k0 + (q % CH) * 8);
 }
+template <int CH>
 __device__ __forceinline__ uint4 load_kc_checked(const Operand& x, int row0, int k0, int K, int q) {
-    const int row = row0 + (q >> 3), kb = k0 + (q & 7) * 8;
+    const int row = row0 + q / CH, kb = k0 + (q % CH) * 8;
     u16 v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
         v[e] = (row < x.rows && kb + e < K) ? x.p[(int64_t)row * x.ld + kb + e] : (u16)0;
     return pack8(v);
 }
+template <int CH>
 __device__ __forceinline__ void store_kc(unsigned char* s, int q, uint4 v) {
-    const int r = q >> 3, c = q & 7;
-    *reinterpret_cast<uint4*>(s + r * 128 + ((c ^ swz(r)) << 4)) = v;
+    const int r = q / CH, c = q % CH;
+    *reinterpret_cast<uint4*>(s + r * CH * 16 + ((c ^ swz<CH>(r)) << 4)) = v;
 }
 
 // Chunk q of an RC tile: k = q / (TR / 8), tile rows 8 * (q % (TR / 8)) .. +7.  The fast
@@ -118,7 +135,7 @@ __device__ __forceinline__ uint4 load_rc_checked(const Operand& x, int row0, int
     return pack8(v);
 }
 // Scatter the 8 values of an RC chunk into the k-contiguous LDS layout.
-template <int TR>
+template <int TR, int CH>
 __device__ __forceinline__ void store_rc(unsigned char* s, int q, uint4 v) {
     constexpr int CPK = TR / 8;
     const int k = q / CPK, r = (q % CPK) * 8;
@@ -126,18 +143,19 @@ __device__ __forceinline__ void store_rc(unsigned char* s, int q, uint4 v) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int row = r + e;
-        *reinterpret_cast<u16*>(s + row * 128 + (((k >> 3) ^ swz(row)) << 4) + (k & 7) * 2) =
+        *reinterpret_cast<u16*>(s + row * CH * 16 + (((k >> 3) ^ swz<CH>(row)) << 4) + (k & 7) * 2) =
             (u16)(w[e >> 1] >> (16 * (e & 1)));
     }
 }
 
-template <int BM, int BN, bool A_KC, bool B_KC>
+template <int BM, int BN, int BK, int S, bool A_KC, bool B_KC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, int vec_b) {
-    using T = Tile<BM, BN>;
-    // the direct path issues its copies in the first 4 * FM * FN instruction slots
-    static_assert(4 * T::FM * T::FN >= T::A_DMA + T::B_DMA, "too few slots for the copies");
-    __shared__ __align__(16) unsigned char smem[2 * T::STAGE];
+    using T = Tile<BM, BN, BK, S>;
+    constexpr int CH = T::CH;
+    // the direct path issues one tile's copies in the first SUB * FM * FN instruction slots
+    static_assert(T::SUB * T::FM * T::FN >= T::A_DMA + T::B_DMA, "too few slots for the copies");
+    __shared__ __align__(16) unsigned char smem[T::LDS];
 
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
@@ -146,8 +164,8 @@ void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, in
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = (wave >> 1) * T::WM, wn = (wave & 1) * T::WN;
     const int K = p.K;
-    const int nk = (K + T::BK - 1) / T::BK;
-    const int nfull = K / T::BK;
+    const int nk = (K + BK - 1) / BK;
+    const int nfull = K / BK;
     const bool interior = (m0 + BM <= p.M) && (n0 + BN <= p.N);
 
     const Operand a{static_cast<const u16*>(p.A), p.lda, p.M};
@@ -161,11 +179,11 @@ void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, in
     auto gload_fast = [&](int k0) {
 #pragma unroll
         for (int s = 0; s < T::A_CHUNKS; ++s)
-            ra[s] = A_KC ? load_kc_fast(a, m0, k0, t + s * T::THREADS)
+            ra[s] = A_KC ? load_kc_fast<CH>(a, m0, k0, t + s * T::THREADS)
                          : load_rc_fast<BM>(a, m0, k0, t + s * T::THREADS);
 #pragma unroll
         for (int s = 0; s < T::B_CHUNKS; ++s)
-            rb[s] = B_KC ? load_kc_fast(b, n0, k0, t + s * T::THREADS)
+            rb[s] = B_KC ? load_kc_fast<CH>(b, n0, k0, t + s * T::THREADS)
                          : load_rc_fast<BN>(b, n0, k0, t + s * T::THREADS);
     };
     auto lstore = [&](int stage) {
@@ -173,13 +191,13 @@ void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, in
         unsigned char* sb = sa + T::A_BYTES;
 #pragma unroll
         for (int s = 0; s < T::A_CHUNKS; ++s) {
-            if (A_KC) store_kc(sa, t + s * T::THREADS, ra[s]);
-            else store_rc<BM>(sa, t + s * T::THREADS, ra[s]);
+            if (A_KC) store_kc<CH>(sa, t + s * T::THREADS, ra[s]);
+            else store_rc<BM, CH>(sa, t + s * T::THREADS, ra[s]);
         }
 #pragma unroll
         for (int s = 0; s < T::B_CHUNKS; ++s) {
-            if (B_KC) store_kc(sb, t + s * T::THREADS, rb[s]);
-            else store_rc<BN>(sb, t + s * T::THREADS, rb[s]);
+            if (B_KC) store_kc<CH>(sb, t + s * T::THREADS, rb[s]);
+            else store_rc<BN, CH>(sb, t + s * T::THREADS, rb[s]);
         }
     };
     // ---- element-wise loads with bounds checks and zero fill, one chunk at a time (the K
@@ -190,14 +208,14 @@ void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, in
 #pragma unroll 1
         for (int s = 0; s < T::A_CHUNKS; ++s) {
             const int q = t + s * T::THREADS;
-            if (A_KC) store_kc(sa, q, load_kc_checked(a, m0, k0, K, q));
-            else store_rc<BM>(sa, q, load_rc_checked<BM>(a, m0, k0, K, q));
+            if (A_KC) store_kc<CH>(sa, q, load_kc_checked<CH>(a, m0, k0, K, q));
+            else store_rc<BM, CH>(sa, q, load_rc_checked<BM>(a, m0, k0, K, q));
         }
 #pragma unroll 1
         for (int s = 0; s < T::B_CHUNKS; ++s) {
             const int q = t + s * T::THREADS;
-            if (B_KC) store_kc(sb, q, load_kc_checked(b, n0, k0, K, q));
-            else store_rc<BN>(sb, q, load_rc_checked<BN>(b, n0, k0, K, q));
+            if (B_KC) store_kc<CH>(sb, q, load_kc_checked<CH>(b, n0, k0, K, q));
+            else store_rc<BN, CH>(sb, q, load_rc_checked<BN>(b, n0, k0, K, q));
         }
     };
 
@@ -211,41 +229,42 @@ void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, in
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int lr = lane & 31, h = lane >> 5;
-    const int sw = swz(lr);                    // == swz(wm + 32 i + lr): wm, 32 i are multiples of 32
-    const int a_off = (wm + lr) * 128;
-    const int b_off = T::A_BYTES + (wn + lr) * 128;
+    const int sw = swz<CH>(lr);     // == swz(wm + 32 i + lr): s depends on row bits 0-4 only
+    const int a_off = (wm + lr) * T::ROW;
+    const int b_off = T::A_BYTES + (wn + lr) * T::ROW;
     auto read_frags = [&](const unsigned char* st, int s, bf16x8 (&fa)[T::FM], bf16x8 (&fb)[T::FN]) {
         const int coff = ((2 * s + h) ^ sw) << 4;
 #pragma unroll
         for (int i = 0; i < T::FM; ++i)
-            fa[i] = *reinterpret_cast<const bf16x8*>(st + a_off + i * 32 * 128 + coff);
+            fa[i] = *reinterpret_cast<const bf16x8*>(st + a_off + i * 32 * T::ROW + coff);
 #pragma unroll
         for (int j = 0; j < T::FN; ++j)
-            fb[j] = *reinterpret_cast<const bf16x8*>(st + b_off + j * 32 * 128 + coff);
+            fb[j] = *reinterpret_cast<const bf16x8*>(st + b_off + j * 32 * T::ROW + coff);
     };
-    // One k-tile: 4 sub-steps of 16 k.  Fragments are double-buffered in registers so that
-    // the LDS reads of sub-step s + 1 are in flight while the matrix instructions of
-    // sub-step s run.  `copy(n)` is called before the n-th matrix instruction (n < 64) to
-    // fold the next tile's global->LDS copies into the same instruction stream.  Source
-    // order is issue order (sched_barrier fences).
+    // One k-tile: SUB sub-steps of 16 k.  Fragments are double-buffered in registers so
+    // that the LDS reads of sub-step s + 1 are in flight while the matrix instructions of
+    // sub-step s run.  `copy(n)` is called before the n-th matrix instruction to fold
+    // another tile's global->LDS copies into the same instruction stream.  Source order is
+    // issue order (sched_barrier fences).
     auto compute = [&](int stage, auto copy) {
         const unsigned char* st = smem + stage * T::STAGE;
         bf16x8 fa[2][T::FM], fb[2][T::FN];
         read_frags(st, 0, fa[0], fb[0]);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < T::SUB; ++s) {
             const int coff = ((2 * (s + 1) + h) ^ sw) << 4;
             // MF matrix instructions and RD fragment reads per sub-step; small tiles have
             // fewer instructions than reads, so the loop runs over the larger count
             constexpr int MF = T::FM * T::FN, RD = T::FM + T::FN;
+            const bool next = s + 1 < T::SUB;
 #pragma unroll
             for (int m = 0; m < (MF > RD ? MF : RD); ++m) {
                 if (m < MF) copy(s * MF + m);
-                if (s < 3 && m < T::FM)
-                    fa[(s + 1) & 1][m] = *reinterpret_cast<const bf16x8*>(st + a_off + m * 32 * 128 + coff);
-                else if (s < 3 && m < RD)
+                if (next && m < T::FM)
+                    fa[(s + 1) & 1][m] = *reinterpret_cast<const bf16x8*>(st + a_off + m * 32 * T::ROW + coff);
+                else if (next && m < RD)
                     fb[(s + 1) & 1][m - T::FM] =
-                        *reinterpret_cast<const bf16x8*>(st + b_off + (m - T::FM) * 32 * 128 + coff);
+                        *reinterpret_cast<const bf16x8*>(st + b_off + (m - T::FM) * 32 * T::ROW + coff);
                 if (m < MF) {
                     const int i = m / T::FN, j = m % T::FN;
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j],
@@ -259,64 +278,87 @@ void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, in
 
     int kt = 0;
     if (A_KC && B_KC && vec_a && vec_b && interior && nfull > 0) {
-        // ---- direct path: full k-tiles copied global -> LDS without registers ----
-        // Copy j of a wavefront fills tile rows r = r0 + 8 j .. +7 (r0 = the wavefront's
-        // first row); lane l fetches the chunk that belongs at LDS position l of that 1 KB
-        // block: row r0 + 8 j + l / 8, logical chunk (l % 8) ^ s(row).  With r0 a multiple
-        // of 16, s(row) = (l / 8) ^ (j & 1), so a lane needs two byte offsets (even and odd
-        // j) on top of a wavefront-uniform row address.
+        // ---- direct path: full k-tiles copied global -> LDS without registers, S stages ----
+        // Copy j of a wavefront fills tile rows r0 + RPI j .. +RPI-1 (r0 = the wavefront's
+        // first row, a multiple of 16); lane l fetches the chunk that belongs at LDS
+        // position l of that 1 KB block: row r0 + RPI j + l / CH, logical chunk
+        // (l % CH) ^ s(row).  s(row) depends on l and on the parity of r0 / RPI + j only,
+        // so a lane needs two byte offsets on top of a wavefront-uniform row address.
         const int arow0 = m0 + wave * T::A_RPW, brow0 = n0 + wave * T::B_RPW;
         const char* abase = reinterpret_cast<const char*>(a.p + (int64_t)arow0 * a.ld);
         const char* bbase = reinterpret_cast<const char*>(b.p + (int64_t)brow0 * b.ld);
-        const int lrow = lane >> 3, lchunk = (lane & 7) ^ (lane >> 3);
+        const int lrow = lane / CH, lc = lane % CH;
         unsigned aoff[2], boff[2];
 #pragma unroll
         for (int par = 0; par < 2; ++par) {
-            aoff[par] = (unsigned)((lrow * a.ld + (lchunk ^ par) * 8) * 2);
-            boff[par] = (unsigned)((lrow * b.ld + (lchunk ^ par) * 8) * 2);
+            const int c = lc ^ swz<CH>(lrow + par * T::RPI);
+            aoff[par] = (unsigned)((lrow * a.ld + c * 8) * 2);
+            boff[par] = (unsigned)((lrow * b.ld + c * 8) * 2);
         }
+        const int apar = (arow0 / T::RPI) & 1, bpar = (brow0 / T::RPI) & 1;
         auto issue_one = [&](int j, int k0, int stage) {   // copy j of this wavefront
-            unsigned char* sa = smem + stage * T::STAGE + wave * T::A_RPW * 128;
-            unsigned char* sb = smem + stage * T::STAGE + T::A_BYTES + wave * T::B_RPW * 128;
+            unsigned char* sa = smem + stage * T::STAGE + wave * T::A_RPW * T::ROW;
+            unsigned char* sb = smem + stage * T::STAGE + T::A_BYTES + wave * T::B_RPW * T::ROW;
             if (j < T::A_DMA) {
-                const char* g = abase + ((int64_t)j * 8 * a.ld + k0) * 2;
-                __builtin_amdgcn_global_load_lds(g + aoff[j & 1], (lds_void*)(sa + j * 1024), 16, 0, 0);
+                const char* g = abase + ((int64_t)j * T::RPI * a.ld + k0) * 2;
+                __builtin_amdgcn_global_load_lds(g + aoff[(apar + j) & 1], (lds_void*)(sa + j * 1024), 16, 0, 0);
             } else {
                 const int jb = j - T::A_DMA;
-                const char* g = bbase + ((int64_t)jb * 8 * b.ld + k0) * 2;
-                __builtin_amdgcn_global_load_lds(g + boff[jb & 1], (lds_void*)(sb + jb * 1024), 16, 0, 0);
+                const char* g = bbase + ((int64_t)jb * T::RPI * b.ld + k0) * 2;
+                __builtin_amdgcn_global_load_lds(g + boff[(bpar + jb) & 1], (lds_void*)(sb + jb * 1024), 16, 0, 0);
             }
         };
-        for (int j = 0; j < T::A_DMA + T::B_DMA; ++j) issue_one(j, 0, 0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        for (; kt + 1 < nfull; ++kt) {
-            const int k0n = (kt + 1) * T::BK, stn = (kt + 1) & 1;
-            compute(kt & 1, [&](int n) {
-                if (n < T::A_DMA + T::B_DMA) issue_one(n, k0n, stn);
+        constexpr int DMA = T::A_DMA + T::B_DMA;
+        constexpr int SPREAD = T::SUB * T::FM * T::FN >= 2 * DMA ? 2 : 1;
+        // prologue: tiles 0 .. S-2 in flight
+#pragma unroll
+        for (int st = 0; st + 1 < S; ++st)
+            if (st < nfull)
+                for (int j = 0; j < DMA; ++j) issue_one(j, st * BK, st);
+        for (; kt < nfull; ++kt) {
+            // tile kt has landed once at most the copies of tiles kt+1 .. kt+S-2 are pending
+            if (kt + S - 2 < nfull) {
+                if (S == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                else if (S == 3) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(DMA) : "memory");
+                else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * DMA) : "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            __syncthreads();   // tile kt visible to all; stage (kt-1) % S free for reuse
+            const int kn = kt + S - 1;
+            const bool copies = kn < nfull;          // wavefront-uniform
+            const int k0n = kn * BK, stn = kn % S;
+            // one copy every SPREAD instruction slots: the copies share the CU's 64-byte/clk
+            // vector-memory path, and bursts of them stall the in-order wavefront
+            compute(kt % S, [&](int n) {
+                if (n % SPREAD == 0 && n / SPREAD < DMA && copies) issue_one(n / SPREAD, k0n, stn);
             });
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        if (nk > nfull) {      // the K tail: bounds-checked loads into the next free stage
+            __syncthreads();
+            load_store_checked(nfull * BK, nfull % S);
+            __syncthreads();
+            compute(nfull % S, no_copy);
+        }
+    } else {
+        // ---- register-staged path, 2 stages ----
+        if (vec_tiles && nfull > 0) {
+            gload_fast(0);
+            lstore(0);
+        } else {
+            load_store_checked(0, 0);
+        }
+        __syncthreads();
+        for (; kt < nk; ++kt) {
+            const int k0n = (kt + 1) * BK, stn = (kt + 1) & 1;
+            const bool more = kt + 1 < nk;
+            const bool next_fast = more && vec_tiles && k0n + BK <= K;
+            if (next_fast) gload_fast(k0n);
+            compute(kt & 1, no_copy);
+            if (next_fast) lstore(stn);
+            else if (more) load_store_checked(k0n, stn);
             __syncthreads();
         }
-    } else if (vec_tiles && nfull > 0) {
-        gload_fast(0);
-        lstore(0);
-        __syncthreads();
-    } else {
-        load_store_checked(0, 0);
-        __syncthreads();
-    }
-    // ---- remaining k-tiles through registers: the last full tile of the direct path and
-    // the K tail, or every tile when the direct copy does not apply ----
-    for (; kt < nk; ++kt) {
-        const int k0n = (kt + 1) * T::BK, stn = (kt + 1) & 1;
-        const bool more = kt + 1 < nk;
-        const bool next_fast = more && vec_tiles && k0n + T::BK <= K;
-        if (next_fast) gload_fast(k0n);
-        compute(kt & 1, no_copy);
-        if (next_fast) lstore(stn);
-        else if (more) load_store_checked(k0n, stn);
-        __syncthreads();
     }
 
 #pragma unroll
@@ -333,30 +375,31 @@ void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, in
         }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int BK, int S>
 hipError_t launch_tile(const Problem& p, const Launch& l) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const dim3 grid((unsigned)tiles_m * tiles_n), block(256);
     const bool akc = p.oa == kRow, bkc = p.ob == kCol;
     const int va = l.vec_a, vb = l.vec_b, g = l.group_m;
     if (akc && bkc)
-        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, true, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb);
+        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, true, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb);
     else if (akc)
-        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, true, false>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb);
+        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, true, false>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb);
     else if (bkc)
-        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, false, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb);
+        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, false, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb);
     else
-        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, false, false>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb);
+        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, false, false>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb);
     return hipGetLastError();
 }
 
 }  // namespace
 
+// Tile configurations: block tile, k-tile depth and LDS stages.
 hipError_t launch_bf16_mfma(const Problem& p, const Launch& l, int bm, int bn) {
-    if (bm == 256 && bn == 256) return launch_tile<256, 256>(p, l);
-    if (bm == 256 && bn == 128) return launch_tile<256, 128>(p, l);
-    if (bm == 128 && bn == 128) return launch_tile<128, 128>(p, l);
-    if (bm == 64 && bn == 64) return launch_tile<64, 64>(p, l);
+    if (bm == 256 && bn == 256) return launch_tile<256, 256, 64, 2>(p, l);   // 128 KB LDS
+    if (bm == 256 && bn == 128) return launch_tile<256, 128, 64, 3>(p, l);   // 144 KB
+    if (bm == 128 && bn == 128) return launch_tile<128, 128, 64, 2>(p, l);   //  64 KB
+    if (bm == 64 && bn == 64) return launch_tile<64, 64, 64, 2>(p, l);       //  32 KB
     return hipErrorInvalidValue;
 }
 

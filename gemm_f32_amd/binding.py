@@ -29,6 +29,7 @@ class Algo(enum.IntEnum):
     MFMA_256x128 = 7
     MFMA_128x128 = 8
     MFMA_64x64 = 9
+    MFMA_PINGPONG = 10
 
 
 class Status(enum.IntEnum):

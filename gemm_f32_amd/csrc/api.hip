@@ -103,6 +103,7 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
             break;
         case GEMM_ALGO_MFMA_128x128: break;
         case GEMM_ALGO_MFMA_256x256: case GEMM_ALGO_MFMA_256x128: case GEMM_ALGO_MFMA_64x64:
+        case GEMM_ALGO_MFMA_PINGPONG:
             if (f32) return GEMM_ERR_INVALID_VALUE;
             break;
         default: return GEMM_ERR_INVALID_VALUE;
@@ -152,6 +153,11 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
                 err = launch_f32_mfma(p, l); name = "f32_mfma128x128"; break;
             }
         }
+    } else if (algo == GEMM_ALGO_MFMA_PINGPONG) {
+        if (!bf16_pingpong_applies(p, l)) return GEMM_ERR_INVALID_VALUE;
+        l.group_m = pick_group_m(p.M / 256, p.N / 256);
+        err = launch_bf16_pingpong(p, l);
+        name = "bf16_pingpong256x256";
     } else {
         int bm = 256, bn = 256;
         switch (algo) {

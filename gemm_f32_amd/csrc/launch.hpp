@@ -15,6 +15,10 @@ hipError_t launch_regblock(const Problem& p, const Launch& l);
 hipError_t launch_f32_mfma(const Problem& p, const Launch& l);
 // BF16 matrix-core kernel (bf16_mfma.hip); tile is one of 256x256, 256x128, 128x128, 64x64
 hipError_t launch_bf16_mfma(const Problem& p, const Launch& l, int bm, int bn);
+// BF16 256 x 256 eight-wavefront ping-pong kernel (bf16_pingpong.hip), for row-major A,
+// column-major B, aligned, M and N multiples of 256, K a multiple of 32
+bool bf16_pingpong_applies(const Problem& p, const Launch& l);
+hipError_t launch_bf16_pingpong(const Problem& p, const Launch& l);
 // C = 0 for K == 0 (fill.hip)
 hipError_t launch_zero_c(const Problem& p, const Launch& l);
 

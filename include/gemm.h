@@ -71,7 +71,12 @@ typedef enum {
  *                      ("A06 - Tiled Matrix Multiply (GEMM)", "Matrix cores: MFMA and
  *                      Tensor Cores"); tile shape picked from the problem;
  *   MFMA_256x256, MFMA_256x128, MFMA_128x128, MFMA_64x64
- *                      the MFMA kernel with that block tile forced.
+ *                      the MFMA kernel with that block tile forced;
+ *   MFMA_PINGPONG      BF16 only: the 256 x 256 kernel with eight wavefronts in two groups
+ *                      that alternate matrix-instruction and memory phases; needs row-major
+ *                      A and column-major B (C may have either order), 16-byte aligned
+ *                      pointers and leading dimensions, M and N multiples of 256 and K a
+ *                      multiple of 32, else GEMM_ERR_INVALID_VALUE.
  * The FP32 entry point accepts every algorithm; the BF16 entry point only AUTO and the
  * MFMA ones (others give GEMM_ERR_INVALID_VALUE).
  */
@@ -85,7 +90,8 @@ typedef enum {
     GEMM_ALGO_MFMA_256x256 = 6,
     GEMM_ALGO_MFMA_256x128 = 7,
     GEMM_ALGO_MFMA_128x128 = 8,
-    GEMM_ALGO_MFMA_64x64 = 9
+    GEMM_ALGO_MFMA_64x64 = 9,
+    GEMM_ALGO_MFMA_PINGPONG = 10
 } gemm_algo_t;
 
 /* FP32 inputs, FP32 arithmetic, FP32 C.  Same as gemm_f32_algo(GEMM_ALGO_AUTO, ...). */

@@ -153,3 +153,55 @@ def test_matmul_helper_on_tensors_and_views():
     out = g.matmul(ab, bb.t().contiguous().t())
     assert oracle.normalised_error(out.cpu().numpy(), refb, Db) <= TOL["bf16"]
     assert g.gemm_last_kernel().startswith("bf16_mfma")
+
+
+# --- the eight-wavefront ping-pong kernel (row-major A, column-major B, 256-multiples) ---
+PP_SHAPES = [(256, 256, 32), (256, 256, 64), (512, 768, 96), (256, 512, 4096), (768, 256, 160),
+             (1024, 1024, 1024)]
+
+
+@pytest.mark.parametrize("shape", PP_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_pingpong_random(shape):
+    M, N, K = shape
+    p = gi.make_problem(M, N, K, "bf16", ROW_MAJOR, COL_MAJOR, wid=45)
+    check(p, g.Algo.MFMA_PINGPONG)
+    assert g.gemm_last_kernel() == "bf16_pingpong256x256"
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 32), (512, 256, 224), (256, 768, 1024)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_pingpong_small_integer_exact(shape):
+    M, N, K = shape
+    rng = np.random.default_rng(K)
+    A = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    B = rng.integers(-4, 5, (K, N)).astype(np.float32)
+    check(gi.make_problem(M, N, K, "bf16", ROW_MAJOR, COL_MAJOR, A_logical=A, B_logical=B),
+          g.Algo.MFMA_PINGPONG, exact=True)
+
+
+def test_pingpong_closed_forms():
+    n = 256
+    ident = gi.make_problem(n, n, n, "bf16", ROW_MAJOR, COL_MAJOR, wid=46, A_logical=np.eye(n))
+    assert np.array_equal(logical_c(ident, run(ident, g.Algo.MFMA_PINGPONG)), ident.b_f32())
+    perm = np.random.default_rng(3).permutation(n)
+    P = np.zeros((n, n)); P[np.arange(n), perm] = 1.0
+    pb = gi.make_problem(n, n, n, "bf16", ROW_MAJOR, COL_MAJOR, wid=47, B_logical=P)
+    assert np.array_equal(logical_c(pb, run(pb, g.Algo.MFMA_PINGPONG)), pb.a_f32()[:, np.argsort(perm)])
+
+
+def test_pingpong_column_major_c():
+    # C^T = B^T A^T: with a column-major C the kernel sees B^T (row-major, from a column-major
+    # B) and A^T (column-major, from a row-major A): the same operand layout it needs
+    p = gi.make_problem(512, 256, 128, "bf16", ROW_MAJOR, COL_MAJOR, COL_MAJOR, wid=48)
+    check(p, g.Algo.MFMA_PINGPONG)
+
+
+@pytest.mark.parametrize("bad", [dict(M=300), dict(K=48), dict(order_b=ROW_MAJOR)],
+                         ids=lambda d: str(d))
+def test_pingpong_rejects_unsupported_shapes(bad):
+    kw = dict(M=256, N=256, K=64, dtype="bf16", order_a=ROW_MAJOR, order_b=COL_MAJOR)
+    kw.update(bad)
+    p = gi.make_problem(**kw)
+    with pytest.raises(g.GemmError) as e:
+        run(p, g.Algo.MFMA_PINGPONG)
+    assert e.value.status == g.Status.ERR_INVALID_VALUE

@@ -30,6 +30,7 @@ class Algo(enum.IntEnum):
     MFMA_128x128 = 8
     MFMA_64x64 = 9
     MFMA_PINGPONG = 10
+    SKINNY = 11
 
 
 class Status(enum.IntEnum):

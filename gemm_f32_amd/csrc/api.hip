@@ -101,7 +101,7 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
         case GEMM_ALGO_REGBLOCK:
             if (!f32) return GEMM_ERR_INVALID_VALUE;
             break;
-        case GEMM_ALGO_MFMA_128x128: break;
+        case GEMM_ALGO_MFMA_128x128: case GEMM_ALGO_SKINNY: break;
         case GEMM_ALGO_MFMA_256x256: case GEMM_ALGO_MFMA_256x128: case GEMM_ALGO_MFMA_64x64:
         case GEMM_ALGO_MFMA_PINGPONG:
             if (f32) return GEMM_ERR_INVALID_VALUE;
@@ -147,12 +147,22 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
                                          (p.N + kRegblockBN - 1) / kRegblockBN);
                 err = launch_regblock(p, l); name = "f32_regblock128x128"; break;
             }
+            case GEMM_ALGO_SKINNY:
+                if (!skinny_applies(p, false)) return GEMM_ERR_INVALID_VALUE;
+                err = launch_skinny(p, l, false); name = "f32_skinny16"; break;
             default: {
+                if (algo == GEMM_ALGO_AUTO && skinny_applies(p, false)) {
+                    err = launch_skinny(p, l, false); name = "f32_skinny16"; break;
+                }
                 l.group_m = pick_group_m((p.M + kF32MfmaBM - 1) / kF32MfmaBM,
                                          (p.N + kF32MfmaBN - 1) / kF32MfmaBN);
                 err = launch_f32_mfma(p, l); name = "f32_mfma128x128"; break;
             }
         }
+    } else if (algo == GEMM_ALGO_SKINNY || (algo == GEMM_ALGO_AUTO && skinny_applies(p, true))) {
+        if (!skinny_applies(p, true)) return GEMM_ERR_INVALID_VALUE;
+        err = launch_skinny(p, l, true);
+        name = "bf16_skinny16";
     } else if (algo == GEMM_ALGO_MFMA_PINGPONG) {
         if (!bf16_pingpong_applies(p, l)) return GEMM_ERR_INVALID_VALUE;
         l.group_m = pick_group_m(p.M / 256, p.N / 256);

@@ -19,6 +19,11 @@ hipError_t launch_bf16_mfma(const Problem& p, const Launch& l, int bm, int bn);
 // column-major B, aligned, M and N multiples of 256, K a multiple of 32
 bool bf16_pingpong_applies(const Problem& p, const Launch& l);
 hipError_t launch_bf16_pingpong(const Problem& p, const Launch& l);
+// Small-M kernel (skinny.hip): M <= kSkinnyMaxM, row-major A; B column-major for BF16,
+// either order for FP32
+constexpr int kSkinnyMaxM = 64;
+bool skinny_applies(const Problem& p, bool bf16);
+hipError_t launch_skinny(const Problem& p, const Launch& l, bool bf16);
 // C = 0 for K == 0 (fill.hip)
 hipError_t launch_zero_c(const Problem& p, const Launch& l);
 

@@ -1,0 +1,194 @@
+// Small-M GEMM (M <= 64 after the host's normalisation): the skinny, memory-bound regime.
+//
+// "How a Matrix Multiply Runs on a GPU", "Shapes that run slowly, and why": with few rows
+// the product is bound by reading B once from HBM however well it is tiled, and a large
+// block tile leaves most CUs idle.  "A06 - Tiled Matrix Multiply (GEMM)", "The next two
+// rungs" (split-K): divide K among workers and combine the partial sums in a second step.
+// Design for MI355X:
+//
+//  * block b owns the 16 columns n0 = 16 b .. n0+15 of C and all M (<= 16 FM) rows, so a
+//    4096-column problem spreads over 256 workgroups, one per CU;
+//  * its 4 wavefronts split K into 4 contiguous ranges (split-K inside the workgroup) and
+//    each streams its range of those 16 columns of B and of the FM 16-row strips of A (A is
+//    small and stays in L2) straight from global memory into registers -- no LDS staging in
+//    the main loop, each lane loads 16 bytes per operand per step, two steps' loads in
+//    flight ahead of the matrix instructions;
+//  * matrix instructions with a 16-row granularity: v_mfma_f32_16x16x32_bf16 (BF16) and
+//    v_mfma_f32_16x16x4_f32 (FP32).  Lane l supplies row / column l % 16; the k-assignment
+//    of lanes is free as long as A and B use the same one, so lane l takes the 16-byte run
+//    of k that starts at 8 (l / 16) (BF16) or 4 (l / 16) (FP32) within each k-step;
+//  * the 4 partial products are summed through LDS in a fixed order (wave 0 + 1 + 2 + 3):
+//    deterministic, no atomics, no workspace;
+//  * accumulator layout of a 16 x 16 result: lane l, register r holds row 4 (l / 16) + r,
+//    column l % 16.
+//
+// Requirements (checked by the host): A row-major (k-contiguous); B column-major for BF16,
+// either order for FP32.  Rows past M and columns past N are clamped to the last valid one
+// (their products are never stored); the K tail and misaligned operands use element-wise
+// loads with zero fill.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace gemm {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16;
+
+constexpr int THREADS = 256, WAVES = 4, BN = 16, CHUNK = 4;   // k-steps per load batch
+
+// ---- per-dtype pieces -------------------------------------------------------------------
+// One k-step: BF16 32 k (lane holds 8 consecutive k), FP32 16 k (lane holds 4).
+struct Bf16 {
+    using Elem = u16;
+    using Frag = uint4;
+    static constexpr int KSTEP = 32, KL = 8;        // k per step, k per lane
+    __device__ static Frag load(const u16* row, int k, int K, bool fast) {
+        if (fast) return *reinterpret_cast<const uint4*>(row + k);
+        u16 v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (k + e < K) ? row[k + e] : (u16)0;
+        return make_uint4(v[0] | (unsigned)v[1] << 16, v[2] | (unsigned)v[3] << 16,
+                          v[4] | (unsigned)v[5] << 16, v[6] | (unsigned)v[7] << 16);
+    }
+    // B row-major is not handled by this kernel for BF16 (the host routes it elsewhere)
+    __device__ static f32x4 mma(const Frag& a, const Frag& b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+
+struct F32 {
+    using Elem = float;
+    using Frag = float4;
+    static constexpr int KSTEP = 16, KL = 4;
+    __device__ static Frag load(const float* row, int k, int K, bool fast) {
+        if (fast) return *reinterpret_cast<const float4*>(row + k);
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (k + e < K) ? row[k + e] : 0.f;
+        return make_float4(v[0], v[1], v[2], v[3]);
+    }
+    // B row-major: the 4 k of a lane are 4 rows of B (one column)
+    __device__ static Frag load_strided(const float* col, int64_t ld, int k, int K) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (k + e < K) ? col[(int64_t)(k + e) * ld] : 0.f;
+        return make_float4(v[0], v[1], v[2], v[3]);
+    }
+    __device__ static f32x4 mma(const Frag& a, const Frag& b, f32x4 c) {
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, c, 0, 0, 0);
+        return c;
+    }
+};
+
+template <typename D, int FM, bool B_KC>
+__global__ __launch_bounds__(THREADS) void k_skinny(Problem p, int klen, int vec_a, int vec_b) {
+    using E = typename D::Elem;
+    using Frag = typename D::Frag;
+    __shared__ f32x4 red[WAVES - 1][FM][64];
+
+    const int n0 = blockIdx.x * BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int li = lane & 15, lq = lane >> 4;
+    const int K = p.K;
+    const int kbeg = wave * klen, kend = min(K, kbeg + klen);
+
+    // this lane's rows of A (one per 16-row strip) and its column of B, clamped into range
+    const E* arow[FM];
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+        arow[f] = static_cast<const E*>(p.A) + (int64_t)min(16 * f + li, p.M - 1) * p.lda;
+    const int n = min(n0 + li, p.N - 1);
+    const E* bcol = static_cast<const E*>(p.B) + (B_KC ? (int64_t)n * p.ldb : (int64_t)n);
+
+    f32x4 acc[FM];
+#pragma unroll
+    for (int f = 0; f < FM; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    constexpr int CK = CHUNK * D::KSTEP;
+    Frag fa[2][CHUNK][FM], fb[2][CHUNK];
+    // one batch of CHUNK k-steps; `full` (wavefront-uniform): the whole batch lies inside
+    // this wavefront's K range, so 16-byte loads need no bounds checks
+    auto load_chunk = [&](int buf, int kc) {
+        const bool full = kc + CK <= kend;
+        const bool fa_fast = full && vec_a, fb_fast = full && vec_b;
+#pragma unroll
+        for (int s = 0; s < CHUNK; ++s) {
+            const int k = kc + s * D::KSTEP + lq * D::KL;
+#pragma unroll
+            for (int f = 0; f < FM; ++f) fa[buf][s][f] = D::load(arow[f], k, kend, fa_fast);
+            if constexpr (B_KC) fb[buf][s] = D::load(bcol, k, kend, fb_fast);
+            else fb[buf][s] = F32::load_strided(reinterpret_cast<const float*>(bcol), p.ldb, k, kend);
+        }
+    };
+    auto compute_chunk = [&](int buf) {
+#pragma unroll
+        for (int s = 0; s < CHUNK; ++s)
+#pragma unroll
+            for (int f = 0; f < FM; ++f) acc[f] = D::mma(fa[buf][s][f], fb[buf][s], acc[f]);
+    };
+    // two batches per trip so that register buffers are indexed by constants
+    if (kbeg < kend) load_chunk(0, kbeg);
+    for (int kc = kbeg; kc < kend; kc += 2 * CK) {
+        const bool second = kc + CK < kend;
+        if (second) load_chunk(1, kc + CK);
+        compute_chunk(0);
+        if (kc + 2 * CK < kend) load_chunk(0, kc + 2 * CK);
+        if (second) compute_chunk(1);
+    }
+
+    // ---- fixed-order sum of the 4 wavefronts' partial products ----
+    if (wave > 0)
+#pragma unroll
+        for (int f = 0; f < FM; ++f) red[wave - 1][f][lane] = acc[f];
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int f = 0; f < FM; ++f) {
+            f32x4 s = acc[f];
+#pragma unroll
+            for (int w = 0; w < WAVES - 1; ++w) s += red[w][f][lane];
+            const int col = n0 + li;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * f + 4 * lq + r;
+                if (row < p.M && col < p.N) p.C[(int64_t)row * p.ldc + col] = s[r];
+            }
+        }
+    }
+}
+
+template <typename D, bool B_KC>
+hipError_t launch_d(const Problem& p, const Launch& l) {
+    // per-wavefront K range, a multiple of the load batch
+    constexpr int CK = CHUNK * D::KSTEP;
+    const int per = (p.K + WAVES - 1) / WAVES;
+    const int klen = ((per + CK - 1) / CK) * CK;
+    const dim3 grid((unsigned)((p.N + BN - 1) / BN)), block(THREADS);
+    const int va = l.vec_a, vb = l.vec_b;
+    const int fm = (p.M + 15) / 16;
+    if (fm == 1) hipLaunchKernelGGL((k_skinny<D, 1, B_KC>), grid, block, 0, l.stream, p, klen, va, vb);
+    else if (fm == 2) hipLaunchKernelGGL((k_skinny<D, 2, B_KC>), grid, block, 0, l.stream, p, klen, va, vb);
+    else if (fm == 3) hipLaunchKernelGGL((k_skinny<D, 3, B_KC>), grid, block, 0, l.stream, p, klen, va, vb);
+    else hipLaunchKernelGGL((k_skinny<D, 4, B_KC>), grid, block, 0, l.stream, p, klen, va, vb);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool skinny_applies(const Problem& p, bool bf16) {
+    return p.M <= kSkinnyMaxM && p.oa == kRow && (bf16 ? p.ob == kCol : true);
+}
+
+hipError_t launch_skinny(const Problem& p, const Launch& l, bool bf16) {
+    if (bf16) return launch_d<Bf16, true>(p, l);
+    if (p.ob == kCol) return launch_d<F32, true>(p, l);
+    return launch_d<F32, false>(p, l);
+}
+
+}  // namespace gemm

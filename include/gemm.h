@@ -77,8 +77,15 @@ typedef enum {
  *                      A and column-major B (C may have either order), 16-byte aligned
  *                      pointers and leading dimensions, M and N multiples of 256 and K a
  *                      multiple of 32, else GEMM_ERR_INVALID_VALUE.
- * The FP32 entry point accepts every algorithm; the BF16 entry point only AUTO and the
- * MFMA ones (others give GEMM_ERR_INVALID_VALUE).
+ *   SKINNY             the small-M kernel ("How a Matrix Multiply Runs on a GPU",
+ *                      "Shapes that run slowly, and why": few rows make the product bound
+ *                      by reading B): 16 columns of C per workgroup, K split over its four
+ *                      wavefronts, partial sums added in a fixed order; needs M <= 64 and
+ *                      row-major A, and for BF16 a column-major B (with a column-major C the
+ *                      roles of M/N and A/B swap, C^T = B^T A^T), else
+ *                      GEMM_ERR_INVALID_VALUE.  AUTO uses it whenever it applies.
+ * The FP32 entry point accepts every algorithm but MFMA_PINGPONG; the BF16 entry point only
+ * AUTO, the MFMA ones and SKINNY (others give GEMM_ERR_INVALID_VALUE).
  */
 typedef enum {
     GEMM_ALGO_AUTO = 0,
@@ -91,7 +98,8 @@ typedef enum {
     GEMM_ALGO_MFMA_256x128 = 7,
     GEMM_ALGO_MFMA_128x128 = 8,
     GEMM_ALGO_MFMA_64x64 = 9,
-    GEMM_ALGO_MFMA_PINGPONG = 10
+    GEMM_ALGO_MFMA_PINGPONG = 10,
+    GEMM_ALGO_SKINNY = 11
 } gemm_algo_t;
 
 /* FP32 inputs, FP32 arithmetic, FP32 C.  Same as gemm_f32_algo(GEMM_ALGO_AUTO, ...). */

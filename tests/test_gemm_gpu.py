@@ -152,7 +152,7 @@ def test_matmul_helper_on_tensors_and_views():
     Db = (ab.abs().double() @ bb.abs().double()).cpu().numpy()
     out = g.matmul(ab, bb.t().contiguous().t())
     assert oracle.normalised_error(out.cpu().numpy(), refb, Db) <= TOL["bf16"]
-    assert g.gemm_last_kernel().startswith("bf16_mfma")
+    assert g.gemm_last_kernel().startswith("bf16_")
 
 
 # --- the eight-wavefront ping-pong kernel (row-major A, column-major B, 256-multiples) ---
@@ -204,4 +204,54 @@ def test_pingpong_rejects_unsupported_shapes(bad):
     p = gi.make_problem(**kw)
     with pytest.raises(g.GemmError) as e:
         run(p, g.Algo.MFMA_PINGPONG)
+    assert e.value.status == g.Status.ERR_INVALID_VALUE
+
+
+# --- the small-M kernel (M <= 64 after normalisation; row-major A) -----------------------
+SK_SHAPES = [(1, 1, 1), (5, 15, 7), (16, 16, 16), (17, 300, 100), (33, 64, 1000), (64, 257, 129),
+             (16, 4096, 4096), (48, 33, 4095)]
+
+
+@pytest.mark.parametrize("dtype,ob", [("bf16", COL_MAJOR), ("f32", COL_MAJOR), ("f32", ROW_MAJOR)],
+                         ids=["bf16-RC", "f32-RC", "f32-RR"])
+@pytest.mark.parametrize("shape", SK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_skinny_random(dtype, ob, shape):
+    M, N, K = shape
+    p = gi.make_problem(M, N, K, dtype, ROW_MAJOR, ob, wid=50)
+    check(p, g.Algo.SKINNY)
+    assert g.gemm_last_kernel() == f"{dtype}_skinny16"
+
+
+@pytest.mark.parametrize("dtype,ob", [("bf16", COL_MAJOR), ("f32", ROW_MAJOR)], ids=["bf16", "f32"])
+@pytest.mark.parametrize("pad", [1, 3, 8])
+def test_skinny_padded_and_misaligned(dtype, ob, pad):
+    p = gi.make_problem(37, 130, 517, dtype, ROW_MAJOR, ob, wid=51, pad_a=pad, pad_b=pad, pad_c=pad)
+    check(p, g.Algo.SKINNY)
+
+
+@pytest.mark.parametrize("dtype,ob", [("bf16", COL_MAJOR), ("f32", ROW_MAJOR), ("f32", COL_MAJOR)],
+                         ids=["bf16", "f32-RR", "f32-RC"])
+def test_skinny_small_integer_exact(dtype, ob):
+    rng = np.random.default_rng(9)
+    M, N, K = 40, 200, 999
+    A = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    B = rng.integers(-4, 5, (K, N)).astype(np.float32)
+    check(gi.make_problem(M, N, K, dtype, ROW_MAJOR, ob, A_logical=A, B_logical=B),
+          g.Algo.SKINNY, exact=True)
+
+
+def test_skinny_column_major_c_uses_n_as_rows():
+    # C column-major: the kernel computes C^T (N x M) = B^T A^T, so N <= 64 qualifies when B
+    # is column-major (B^T row-major) and, for BF16, A row-major (A^T column-major)
+    p = gi.make_problem(300, 20, 257, "bf16", ROW_MAJOR, COL_MAJOR, COL_MAJOR, wid=52)
+    check(p, g.Algo.SKINNY)
+
+
+@pytest.mark.parametrize("bad", [dict(M=65), dict(order_a=COL_MAJOR), dict(dtype="bf16", order_b=ROW_MAJOR)],
+                         ids=lambda d: str(d))
+def test_skinny_rejects_unsupported(bad):
+    kw = dict(M=16, N=64, K=64, dtype="f32", order_a=ROW_MAJOR, order_b=COL_MAJOR)
+    kw.update(bad)
+    with pytest.raises(g.GemmError) as e:
+        run(gi.make_problem(**kw), g.Algo.SKINNY)
     assert e.value.status == g.Status.ERR_INVALID_VALUE

@@ -200,8 +200,21 @@ void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, in
             else store_rc<BN, CH>(sb, t + s * T::THREADS, rb[s]);
         }
     };
-    // ---- element-wise loads with bounds checks and zero fill, one chunk at a time (the K
-    // tail, misaligned operands, edge tiles of a row-contiguous operand)
+    // ---- element-wise loads with bounds checks and zero fill into the same staging
+    // registers (misaligned operands, edge tiles of a row-contiguous operand): issued before
+    // a k-tile's matrix instructions and stored after them, like the 16-byte loads
+    auto gload_checked = [&](int k0) {
+#pragma unroll
+        for (int s = 0; s < T::A_CHUNKS; ++s)
+            ra[s] = A_KC ? load_kc_checked<CH>(a, m0, k0, K, t + s * T::THREADS)
+                         : load_rc_checked<BM>(a, m0, k0, K, t + s * T::THREADS);
+#pragma unroll
+        for (int s = 0; s < T::B_CHUNKS; ++s)
+            rb[s] = B_KC ? load_kc_checked<CH>(b, n0, k0, K, t + s * T::THREADS)
+                         : load_rc_checked<BN>(b, n0, k0, K, t + s * T::THREADS);
+    };
+    // ---- the same, one chunk at a time (the K tail after the direct path, where the
+    // registers are taken by the direct path's addressing)
     auto load_store_checked = [&](int k0, int stage) {
         unsigned char* sa = smem + stage * T::STAGE;
         unsigned char* sb = sa + T::A_BYTES;
@@ -341,21 +354,22 @@ void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, in
             compute(nfull % S, no_copy);
         }
     } else {
-        // ---- register-staged path, 2 stages ----
-        if (vec_tiles && nfull > 0) {
-            gload_fast(0);
-            lstore(0);
-        } else {
-            load_store_checked(0, 0);
-        }
+        // ---- register-staged path, 2 stages.  Checked loads are staged in registers too
+        // where the registers allow it (all but the mixed-layout 256 x 256 tiles, which load
+        // and store them a chunk at a time) ----
+        constexpr bool STAGE_CHECKED = A_KC == B_KC || T::A_CHUNKS + T::B_CHUNKS <= 12;
+        if (vec_tiles && nfull > 0) { gload_fast(0); lstore(0); }
+        else if (STAGE_CHECKED) { gload_checked(0); lstore(0); }
+        else load_store_checked(0, 0);
         __syncthreads();
         for (; kt < nk; ++kt) {
             const int k0n = (kt + 1) * BK, stn = (kt + 1) & 1;
             const bool more = kt + 1 < nk;
             const bool next_fast = more && vec_tiles && k0n + BK <= K;
             if (next_fast) gload_fast(k0n);
+            else if (more && STAGE_CHECKED) gload_checked(k0n);
             compute(kt & 1, no_copy);
-            if (next_fast) lstore(stn);
+            if (next_fast || (more && STAGE_CHECKED)) lstore(stn);
             else if (more) load_store_checked(k0n, stn);
             __syncthreads();
         }

@@ -22,6 +22,10 @@ hipError_t launch_bf16_pingpong(const Problem& p, const Launch& l);
 // Small-M kernel (skinny.hip): M <= kSkinnyMaxM, row-major A; B column-major for BF16,
 // either order for FP32
 constexpr int kSkinnyMaxM = 64;
+#ifndef GEMM_SKINNY_WAVES
+#define GEMM_SKINNY_WAVES 8
+#endif
+constexpr int kSkinnyWaves = GEMM_SKINNY_WAVES;   // wavefronts splitting K in a workgroup
 bool skinny_applies(const Problem& p, bool bf16);
 hipError_t launch_skinny(const Problem& p, const Launch& l, bool bf16);
 // C = 0 for K == 0 (fill.hip)

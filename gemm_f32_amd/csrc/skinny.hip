@@ -36,7 +36,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
 
-constexpr int THREADS = 256, WAVES = 4, BN = 16, CHUNK = 4;   // k-steps per load batch
+constexpr int BN = 16, CHUNK = 4;   // columns per workgroup, k-steps per load batch
 
 // ---- per-dtype pieces -------------------------------------------------------------------
 // One k-step: BF16 32 k (lane holds 8 consecutive k), FP32 16 k (lane holds 4).
@@ -86,13 +86,17 @@ struct F32 {
     }
 };
 
-template <typename D, int FM, bool B_KC>
-__global__ __launch_bounds__(THREADS) void k_skinny(Problem p, int klen, int vec_a, int vec_b) {
+template <typename D, int FM, int WAVES, bool B_KC>
+__global__ __launch_bounds__(64 * WAVES) void k_skinny(Problem p, int klen, int vec_a, int vec_b) {
     using E = typename D::Elem;
     using Frag = typename D::Frag;
     __shared__ f32x4 red[WAVES - 1][FM][64];
 
-    const int n0 = blockIdx.x * BN;
+    // column slab: neighbouring slabs (which share 128-byte lines of a row-major B) are
+    // given to workgroups that the dispatcher places on the same XCD
+    int unused, slab;
+    tile_coords(blockIdx.x, 1, gridDim.x, 1, unused, slab);
+    const int n0 = slab * BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lq = lane >> 4;
     const int K = p.K;
@@ -163,19 +167,19 @@ __global__ __launch_bounds__(THREADS) void k_skinny(Problem p, int klen, int vec
     }
 }
 
-template <typename D, bool B_KC>
+template <typename D, int WAVES, bool B_KC>
 hipError_t launch_d(const Problem& p, const Launch& l) {
     // per-wavefront K range, a multiple of the load batch
     constexpr int CK = CHUNK * D::KSTEP;
     const int per = (p.K + WAVES - 1) / WAVES;
     const int klen = ((per + CK - 1) / CK) * CK;
-    const dim3 grid((unsigned)((p.N + BN - 1) / BN)), block(THREADS);
+    const dim3 grid((unsigned)((p.N + BN - 1) / BN)), block(64 * WAVES);
     const int va = l.vec_a, vb = l.vec_b;
     const int fm = (p.M + 15) / 16;
-    if (fm == 1) hipLaunchKernelGGL((k_skinny<D, 1, B_KC>), grid, block, 0, l.stream, p, klen, va, vb);
-    else if (fm == 2) hipLaunchKernelGGL((k_skinny<D, 2, B_KC>), grid, block, 0, l.stream, p, klen, va, vb);
-    else if (fm == 3) hipLaunchKernelGGL((k_skinny<D, 3, B_KC>), grid, block, 0, l.stream, p, klen, va, vb);
-    else hipLaunchKernelGGL((k_skinny<D, 4, B_KC>), grid, block, 0, l.stream, p, klen, va, vb);
+    if (fm == 1) hipLaunchKernelGGL((k_skinny<D, 1, WAVES, B_KC>), grid, block, 0, l.stream, p, klen, va, vb);
+    else if (fm == 2) hipLaunchKernelGGL((k_skinny<D, 2, WAVES, B_KC>), grid, block, 0, l.stream, p, klen, va, vb);
+    else if (fm == 3) hipLaunchKernelGGL((k_skinny<D, 3, WAVES, B_KC>), grid, block, 0, l.stream, p, klen, va, vb);
+    else hipLaunchKernelGGL((k_skinny<D, 4, WAVES, B_KC>), grid, block, 0, l.stream, p, klen, va, vb);
     return hipGetLastError();
 }
 
@@ -186,9 +190,10 @@ bool skinny_applies(const Problem& p, bool bf16) {
 }
 
 hipError_t launch_skinny(const Problem& p, const Launch& l, bool bf16) {
-    if (bf16) return launch_d<Bf16, true>(p, l);
-    if (p.ob == kCol) return launch_d<F32, true>(p, l);
-    return launch_d<F32, false>(p, l);
+    constexpr int W = kSkinnyWaves;
+    if (bf16) return launch_d<Bf16, W, true>(p, l);
+    if (p.ob == kCol) return launch_d<F32, W, true>(p, l);
+    return launch_d<F32, W, false>(p, l);
 }
 
 }  // namespace gemm

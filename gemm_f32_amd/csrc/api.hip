@@ -73,14 +73,23 @@ int pick_group_m(int tiles_m, int tiles_n) {
 
 int64_t tiles(int64_t M, int64_t N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
 
-// BF16 tile choice.  A block tile per CU and as few partial waves as possible: among the
+// AUTO takes the small-problem kernel for few rows, or when even 64 x 64 tiles would leave
+// more than half of the CUs idle (each such tile walks all of K alone).
+bool prefer_small(const Problem& p, int cus) {
+    return p.M <= kSkinnyMaxM || tiles(p.M, p.N, 64, 64) * 2 < (cus > 0 ? cus : 256);
+}
+
+// Block-tile choice.  A block tile per CU and as few partial waves as possible: among the
 // tiles, estimate time as (waves of tiles over the CUs) x (work per tile / relative
 // efficiency of the tile size), and take the cheapest.
-void pick_bf16_tile(int64_t M, int64_t N, int cus, int& bm, int& bn) {
-    struct Opt { int bm, bn; double eff; };
-    const Opt opts[] = {{256, 256, 1.0}, {256, 128, 0.85}, {128, 128, 0.65}, {64, 64, 0.3}};
+struct TileOpt { int bm, bn; double eff; };
+constexpr TileOpt kBf16Tiles[] = {{256, 256, 1.0}, {256, 128, 0.85}, {128, 128, 0.65}, {64, 64, 0.3}};
+constexpr TileOpt kF32Tiles[] = {{128, 128, 1.0}, {64, 64, 0.5}};
+
+template <size_t NOPT>
+void pick_tile(const TileOpt (&opts)[NOPT], int64_t M, int64_t N, int cus, int& bm, int& bn) {
     double best = 1e300;
-    for (const Opt& o : opts) {
+    for (const TileOpt& o : opts) {
         const double n = (double)tiles(M, N, o.bm, o.bn);
         const double waves = std::ceil(n / (cus > 0 ? cus : 256));
         const double cost = waves * o.bm * o.bn / o.eff;
@@ -101,9 +110,8 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
         case GEMM_ALGO_REGBLOCK:
             if (!f32) return GEMM_ERR_INVALID_VALUE;
             break;
-        case GEMM_ALGO_MFMA_128x128: case GEMM_ALGO_SKINNY: break;
-        case GEMM_ALGO_MFMA_256x256: case GEMM_ALGO_MFMA_256x128: case GEMM_ALGO_MFMA_64x64:
-        case GEMM_ALGO_MFMA_PINGPONG:
+        case GEMM_ALGO_MFMA_128x128: case GEMM_ALGO_MFMA_64x64: case GEMM_ALGO_SKINNY: break;
+        case GEMM_ALGO_MFMA_256x256: case GEMM_ALGO_MFMA_256x128: case GEMM_ALGO_MFMA_PINGPONG:
             if (f32) return GEMM_ERR_INVALID_VALUE;
             break;
         default: return GEMM_ERR_INVALID_VALUE;
@@ -151,15 +159,20 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
                 if (!skinny_applies(p, false)) return GEMM_ERR_INVALID_VALUE;
                 err = launch_skinny(p, l, false); name = "f32_skinny16"; break;
             default: {
-                if (algo == GEMM_ALGO_AUTO && skinny_applies(p, false)) {
+                if (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus) && skinny_applies(p, false)) {
                     err = launch_skinny(p, l, false); name = "f32_skinny16"; break;
                 }
-                l.group_m = pick_group_m((p.M + kF32MfmaBM - 1) / kF32MfmaBM,
-                                         (p.N + kF32MfmaBN - 1) / kF32MfmaBN);
-                err = launch_f32_mfma(p, l); name = "f32_mfma128x128"; break;
+                int bm = 128, bn = 128;
+                if (algo == GEMM_ALGO_MFMA_64x64) bm = bn = 64;
+                else if (algo != GEMM_ALGO_MFMA_128x128) pick_tile(kF32Tiles, p.M, p.N, dev.cus, bm, bn);
+                l.group_m = pick_group_m((p.M + bm - 1) / bm, (p.N + bn - 1) / bn);
+                err = launch_f32_mfma(p, l, bm);
+                name = bm == 64 ? "f32_mfma64x64" : "f32_mfma128x128";
+                break;
             }
         }
-    } else if (algo == GEMM_ALGO_SKINNY || (algo == GEMM_ALGO_AUTO && skinny_applies(p, true))) {
+    } else if (algo == GEMM_ALGO_SKINNY ||
+               (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus) && skinny_applies(p, true))) {
         if (!skinny_applies(p, true)) return GEMM_ERR_INVALID_VALUE;
         err = launch_skinny(p, l, true);
         name = "bf16_skinny16";
@@ -175,7 +188,7 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
             case GEMM_ALGO_MFMA_256x128: bm = 256; bn = 128; break;
             case GEMM_ALGO_MFMA_128x128: bm = 128; bn = 128; break;
             case GEMM_ALGO_MFMA_64x64: bm = 64; bn = 64; break;
-            default: pick_bf16_tile(p.M, p.N, dev.cus, bm, bn); break;
+            default: pick_tile(kBf16Tiles, p.M, p.N, dev.cus, bm, bn); break;
         }
         l.group_m = pick_group_m((p.M + bm - 1) / bm, (p.N + bn - 1) / bn);
         err = launch_bf16_mfma(p, l, bm, bn);

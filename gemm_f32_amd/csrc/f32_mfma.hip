@@ -216,8 +216,9 @@ hipError_t launch_cfg(const Problem& p, const Launch& l) {
 
 }  // namespace
 
-hipError_t launch_f32_mfma(const Problem& p, const Launch& l) {
-    return launch_cfg<kF32MfmaBM, kF32MfmaBN, 16, 2, 2, false>(p, l);
+hipError_t launch_f32_mfma(const Problem& p, const Launch& l, int bm) {
+    if (bm == 64) return launch_cfg<64, 64, 16, 2, 2, false>(p, l);
+    return launch_cfg<128, 128, 16, 2, 2, false>(p, l);
 }
 
 }  // namespace gemm

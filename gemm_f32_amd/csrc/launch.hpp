@@ -11,16 +11,17 @@ hipError_t launch_naive(const Problem& p, const Launch& l, bool coalesced);
 hipError_t launch_tiled(const Problem& p, const Launch& l);
 // FP32 register-blocked VALU kernel (f32_regblock.hip)
 hipError_t launch_regblock(const Problem& p, const Launch& l);
-// FP32 matrix-core kernel (f32_mfma.hip)
-hipError_t launch_f32_mfma(const Problem& p, const Launch& l);
+// FP32 matrix-core kernel (f32_mfma.hip); tile is 128x128 or 64x64 (bm == bn)
+hipError_t launch_f32_mfma(const Problem& p, const Launch& l, int bm);
 // BF16 matrix-core kernel (bf16_mfma.hip); tile is one of 256x256, 256x128, 128x128, 64x64
 hipError_t launch_bf16_mfma(const Problem& p, const Launch& l, int bm, int bn);
 // BF16 256 x 256 eight-wavefront ping-pong kernel (bf16_pingpong.hip), for row-major A,
 // column-major B, aligned, M and N multiples of 256, K a multiple of 32
 bool bf16_pingpong_applies(const Problem& p, const Launch& l);
 hipError_t launch_bf16_pingpong(const Problem& p, const Launch& l);
-// Small-M kernel (skinny.hip): M <= kSkinnyMaxM, row-major A; B column-major for BF16,
-// either order for FP32
+// Small-problem kernel (skinny.hip): 64 x 16 blocks of C with K split over the workgroup;
+// row-major A, B column-major for BF16 or either order for FP32.  AUTO uses it for
+// M <= kSkinnyMaxM or when 64 x 64 tiles would not fill half the chip.
 constexpr int kSkinnyMaxM = 64;
 #ifndef GEMM_SKINNY_WAVES
 #define GEMM_SKINNY_WAVES 8
@@ -33,6 +34,5 @@ hipError_t launch_zero_c(const Problem& p, const Launch& l);
 
 // Block-tile sizes, exported for the host's scheduler choices.
 constexpr int kRegblockBM = 128, kRegblockBN = 128;
-constexpr int kF32MfmaBM = 128, kF32MfmaBN = 128;
 
 }  // namespace gemm

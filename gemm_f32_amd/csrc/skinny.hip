@@ -1,4 +1,5 @@
-// Small-M GEMM (M <= 64 after the host's normalisation): the skinny, memory-bound regime.
+// Small-problem GEMM: few rows (M <= 64 after the host's normalisation: the skinny,
+// memory-bound regime) or too few 128 x 128 tiles to fill the chip.
 //
 // "How a Matrix Multiply Runs on a GPU", "Shapes that run slowly, and why": with few rows
 // the product is bound by reading B once from HBM however well it is tiled, and a large
@@ -6,8 +7,9 @@
 // rungs" (split-K): divide K among workers and combine the partial sums in a second step.
 // Design for MI355X:
 //
-//  * block b owns the 16 columns n0 = 16 b .. n0+15 of C and all M (<= 16 FM) rows, so a
-//    4096-column problem spreads over 256 workgroups, one per CU;
+//  * a workgroup owns 16 columns n0 .. n0+15 and 64 rows m0 .. m0+63 of C (fewer when M is
+//    smaller: 16 FM rows), so a 16 x 4096 problem spreads over 256 workgroups, one per CU,
+//    and a 1000 x 1000 one over 16 x 63;
 //  * its 4 wavefronts split K into 4 contiguous ranges (split-K inside the workgroup) and
 //    each streams its range of those 16 columns of B and of the FM 16-row strips of A (A is
 //    small and stays in L2) straight from global memory into registers -- no LDS staging in
@@ -23,7 +25,8 @@
 //    column l % 16.
 //
 // Requirements (checked by the host): A row-major (k-contiguous); B column-major for BF16,
-// either order for FP32.  Rows past M and columns past N are clamped to the last valid one
+// either order for FP32.  Any M, N, K; A strips are re-read once per column slab, which is
+// cheap only while the problem is small or M is.  Rows past M and columns past N are clamped to the last valid one
 // (their products are never stored); the K tail and misaligned operands use element-wise
 // loads with zero fill.
 #include "common.hpp"
@@ -92,11 +95,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(Problem p, int klen, int 
     using Frag = typename D::Frag;
     __shared__ f32x4 red[WAVES - 1][FM][64];
 
-    // column slab: neighbouring slabs (which share 128-byte lines of a row-major B) are
-    // given to workgroups that the dispatcher places on the same XCD
-    int unused, slab;
-    tile_coords(blockIdx.x, 1, gridDim.x, 1, unused, slab);
-    const int n0 = slab * BN;
+    // (row block, column slab): the workgroups one XCD receives cover all row blocks of a
+    // run of neighbouring slabs (which share 128-byte lines of a row-major B)
+    const int slabs = (p.N + BN - 1) / BN, rblocks = (p.M + 63) / 64;
+    int rb, slab;
+    tile_coords(blockIdx.x, rblocks, slabs, rblocks, rb, slab);
+    const int n0 = slab * BN, m0 = rb * 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lq = lane >> 4;
     const int K = p.K;
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(Problem p, int klen, int 
     const E* arow[FM];
 #pragma unroll
     for (int f = 0; f < FM; ++f)
-        arow[f] = static_cast<const E*>(p.A) + (int64_t)min(16 * f + li, p.M - 1) * p.lda;
+        arow[f] = static_cast<const E*>(p.A) + (int64_t)min(m0 + 16 * f + li, p.M - 1) * p.lda;
     const int n = min(n0 + li, p.N - 1);
     const E* bcol = static_cast<const E*>(p.B) + (B_KC ? (int64_t)n * p.ldb : (int64_t)n);
 
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(Problem p, int klen, int 
             const int col = n0 + li;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = 16 * f + 4 * lq + r;
+                const int row = m0 + 16 * f + 4 * lq + r;
                 if (row < p.M && col < p.N) p.C[(int64_t)row * p.ldc + col] = s[r];
             }
         }
@@ -173,9 +177,10 @@ hipError_t launch_d(const Problem& p, const Launch& l) {
     constexpr int CK = CHUNK * D::KSTEP;
     const int per = (p.K + WAVES - 1) / WAVES;
     const int klen = ((per + CK - 1) / CK) * CK;
-    const dim3 grid((unsigned)((p.N + BN - 1) / BN)), block(64 * WAVES);
+    const int slabs = (p.N + BN - 1) / BN, rblocks = (p.M + 63) / 64;
+    const dim3 grid((unsigned)(slabs * rblocks)), block(64 * WAVES);
     const int va = l.vec_a, vb = l.vec_b;
-    const int fm = (p.M + 15) / 16;
+    const int fm = p.M >= 64 ? 4 : (p.M + 15) / 16;
     if (fm == 1) hipLaunchKernelGGL((k_skinny<D, 1, WAVES, B_KC>), grid, block, 0, l.stream, p, klen, va, vb);
     else if (fm == 2) hipLaunchKernelGGL((k_skinny<D, 2, WAVES, B_KC>), grid, block, 0, l.stream, p, klen, va, vb);
     else if (fm == 3) hipLaunchKernelGGL((k_skinny<D, 3, WAVES, B_KC>), grid, block, 0, l.stream, p, klen, va, vb);
@@ -186,7 +191,7 @@ hipError_t launch_d(const Problem& p, const Launch& l) {
 }  // namespace
 
 bool skinny_applies(const Problem& p, bool bf16) {
-    return p.M <= kSkinnyMaxM && p.oa == kRow && (bf16 ? p.ob == kCol : true);
+    return p.oa == kRow && (bf16 ? p.ob == kCol : true);
 }
 
 hipError_t launch_skinny(const Problem& p, const Launch& l, bool bf16) {

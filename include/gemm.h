@@ -71,21 +71,24 @@ typedef enum {
  *                      ("A06 - Tiled Matrix Multiply (GEMM)", "Matrix cores: MFMA and
  *                      Tensor Cores"); tile shape picked from the problem;
  *   MFMA_256x256, MFMA_256x128, MFMA_128x128, MFMA_64x64
- *                      the MFMA kernel with that block tile forced;
+ *                      the MFMA kernel with that block tile forced (FP32: 128x128 and
+ *                      64x64 only);
  *   MFMA_PINGPONG      BF16 only: the 256 x 256 kernel with eight wavefronts in two groups
  *                      that alternate matrix-instruction and memory phases; needs row-major
  *                      A and column-major B (C may have either order), 16-byte aligned
  *                      pointers and leading dimensions, M and N multiples of 256 and K a
  *                      multiple of 32, else GEMM_ERR_INVALID_VALUE.
- *   SKINNY             the small-M kernel ("How a Matrix Multiply Runs on a GPU",
+ *   SKINNY             the small-problem kernel ("How a Matrix Multiply Runs on a GPU",
  *                      "Shapes that run slowly, and why": few rows make the product bound
- *                      by reading B): 16 columns of C per workgroup, K split over its four
- *                      wavefronts, partial sums added in a fixed order; needs M <= 64 and
- *                      row-major A, and for BF16 a column-major B (with a column-major C the
- *                      roles of M/N and A/B swap, C^T = B^T A^T), else
- *                      GEMM_ERR_INVALID_VALUE.  AUTO uses it whenever it applies.
- * The FP32 entry point accepts every algorithm but MFMA_PINGPONG; the BF16 entry point only
- * AUTO, the MFMA ones and SKINNY (others give GEMM_ERR_INVALID_VALUE).
+ *                      by reading B; few tiles leave the chip idle): 64 x 16 blocks of C per
+ *                      workgroup, K split over its wavefronts, partial sums added in a fixed
+ *                      order; needs row-major A, and for BF16 a column-major B (with a
+ *                      column-major C the roles of M/N and A/B swap, C^T = B^T A^T), else
+ *                      GEMM_ERR_INVALID_VALUE.  AUTO uses it when it applies and M <= 64 or
+ *                      64 x 64 tiles would fill less than half of the CUs.
+ * The FP32 entry point accepts every algorithm but MFMA_256x256, MFMA_256x128 and
+ * MFMA_PINGPONG; the BF16 entry point only AUTO, the MFMA ones and SKINNY (others give
+ * GEMM_ERR_INVALID_VALUE).
  */
 typedef enum {
     GEMM_ALGO_AUTO = 0,

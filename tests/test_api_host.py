@@ -81,7 +81,7 @@ def test_bf16_rejects_vector_alu_ladder(algo):
     assert _status(BF16, algo, *args()) == INVALID
 
 
-@pytest.mark.parametrize("algo", [6, 7, 9, 10, 12, -1])
+@pytest.mark.parametrize("algo", [6, 7, 10, 12, -1])
 def test_f32_rejects_unknown_tiles(algo):
     assert _status(F32, algo, *args()) == INVALID
 

@@ -16,7 +16,7 @@ from gpu_util import TOL, check, logical_c, padding_untouched, run, to_device
 pytestmark = pytest.mark.gpu
 
 F32_ALGOS = [g.Algo.NAIVE_UNCOALESCED, g.Algo.NAIVE, g.Algo.TILED, g.Algo.REGBLOCK,
-             g.Algo.MFMA, g.Algo.AUTO]
+             g.Algo.MFMA_128x128, g.Algo.MFMA_64x64, g.Algo.AUTO]
 BF16_ALGOS = [g.Algo.MFMA_256x256, g.Algo.MFMA_256x128, g.Algo.MFMA_128x128,
               g.Algo.MFMA_64x64, g.Algo.AUTO]
 CASES = [("f32", a) for a in F32_ALGOS] + [("bf16", a) for a in BF16_ALGOS]
@@ -207,9 +207,10 @@ def test_pingpong_rejects_unsupported_shapes(bad):
     assert e.value.status == g.Status.ERR_INVALID_VALUE
 
 
-# --- the small-M kernel (M <= 64 after normalisation; row-major A) -----------------------
+# --- the small-problem kernel (row-major A; B column-major for BF16) ---------------------
 SK_SHAPES = [(1, 1, 1), (5, 15, 7), (16, 16, 16), (17, 300, 100), (33, 64, 1000), (64, 257, 129),
-             (16, 4096, 4096), (48, 33, 4095)]
+             (16, 4096, 4096), (48, 33, 4095), (65, 40, 70), (256, 256, 256), (1000, 700, 1000),
+             (129, 1025, 333)]
 
 
 @pytest.mark.parametrize("dtype,ob", [("bf16", COL_MAJOR), ("f32", COL_MAJOR), ("f32", ROW_MAJOR)],
@@ -247,7 +248,7 @@ def test_skinny_column_major_c_uses_n_as_rows():
     check(p, g.Algo.SKINNY)
 
 
-@pytest.mark.parametrize("bad", [dict(M=65), dict(order_a=COL_MAJOR), dict(dtype="bf16", order_b=ROW_MAJOR)],
+@pytest.mark.parametrize("bad", [dict(order_a=COL_MAJOR), dict(dtype="bf16", order_b=ROW_MAJOR)],
                          ids=lambda d: str(d))
 def test_skinny_rejects_unsupported(bad):
     kw = dict(M=16, N=64, K=64, dtype="f32", order_a=ROW_MAJOR, order_b=COL_MAJOR)
@@ -255,3 +256,16 @@ def test_skinny_rejects_unsupported(bad):
     with pytest.raises(g.GemmError) as e:
         run(gi.make_problem(**kw), g.Algo.SKINNY)
     assert e.value.status == g.Status.ERR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("dtype,shape,kernel", [
+    ("f32", (16, 4096, 4096), "f32_skinny16"), ("bf16", (16, 4096, 4096), "bf16_skinny16"),
+    ("f32", (256, 256, 256), "f32_skinny16"), ("f32", (1000, 1000, 1000), "f32_mfma64x64"),
+    ("bf16", (1000, 1000, 1000), "bf16_mfma64x64"), ("f32", (4096, 4096, 64), "f32_mfma128x128"),
+    ("bf16", (4096, 4096, 64), "bf16_mfma256x256")], ids=lambda v: str(v))
+def test_auto_kernel_choice(dtype, shape, kernel):
+    """AUTO: few rows or too few 64 x 64 tiles -> small-problem kernel, else block tiles."""
+    M, N, K = shape
+    p = gi.make_problem(M, N, K, dtype, ROW_MAJOR, COL_MAJOR if dtype == "bf16" else ROW_MAJOR, wid=52)
+    check(p, g.Algo.AUTO)
+    assert g.gemm_last_kernel() == kernel

@@ -31,6 +31,7 @@ class Algo(enum.IntEnum):
     MFMA_64x64 = 9
     MFMA_PINGPONG = 10
     SKINNY = 11
+    MFMA_DMA = 12
 
 
 class Status(enum.IntEnum):

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgemm.so")
 
-SOURCES = ["api.hip", "fill.hip", "f32_ladder.hip", "f32_regblock.hip", "f32_mfma.hip",
+SOURCES = ["api.hip", "fill.hip", "f32_ladder.hip", "f32_regblock.hip", "f32_mfma.hip", "f32_dma.hip",
            "bf16_mfma.hip", "bf16_pingpong.hip", "skinny.hip"]
 ARCH = "gfx950"
 
@@ -36,6 +36,12 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags.  f32_dma.hip keeps its matrix accumulators in ordinary vector
+# registers: with the accumulation-register form the compiler rotated the accumulators
+# through register copies on every k-tile (visible in the kernel's assembly).
+EXTRA_FLAGS = {"f32_dma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -45,7 +51,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> tuple[str, str]:
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [hipcc(), *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c",
+    cmd = [hipcc(), *FLAGS, *EXTRA_FLAGS.get(src, []), "-Rpass-analysis=kernel-resource-usage", "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -84,7 +84,10 @@ bool prefer_small(const Problem& p, int cus) {
 // efficiency of the tile size), and take the cheapest.
 struct TileOpt { int bm, bn; double eff; };
 constexpr TileOpt kBf16Tiles[] = {{256, 256, 1.0}, {256, 128, 0.85}, {128, 128, 0.65}, {64, 64, 0.3}};
+// FP32: the register-staged kernel (128 x 128, 64 x 64) and, where its requirements hold,
+// the direct-copy kernel (256 x 256, 128 x 128); relative speeds as measured at 4096^3
 constexpr TileOpt kF32Tiles[] = {{128, 128, 1.0}, {64, 64, 0.5}};
+constexpr TileOpt kF32DmaTiles[] = {{256, 256, 1.0}, {128, 128, 0.8}, {64, 64, 0.4}};
 
 template <size_t NOPT>
 void pick_tile(const TileOpt (&opts)[NOPT], int64_t M, int64_t N, int cus, int& bm, int& bn) {
@@ -95,6 +98,44 @@ void pick_tile(const TileOpt (&opts)[NOPT], int64_t M, int64_t N, int cus, int& 
         const double cost = waves * o.bm * o.bn / o.eff;
         if (cost < best) { best = cost; bm = o.bm; bn = o.bn; }
     }
+}
+
+// FP32 direct-copy kernel on the whole bt x bt tiles of C, the register-staged kernel on
+// the partial strips along the bottom and right edges (same stream, disjoint parts of C).
+hipError_t launch_f32_dma_split(const Problem& p, const Launch& l, int bt, int cus) {
+    const int mf = p.M / bt * bt, nf = p.N / bt * bt;
+    Problem core = p;
+    core.M = mf;
+    core.N = nf;
+    Launch lc = l;
+    lc.group_m = pick_group_m(mf / bt, nf / bt);
+    hipError_t err = launch_f32_dma(core, lc, bt, bt);
+    auto strip = [&](Problem s) {
+        if (err != hipSuccess) return;
+        int bm = 128, bn = 128;
+        pick_tile(kF32Tiles, s.M, s.N, cus, bm, bn);
+        Launch ls = l;
+        ls.group_m = pick_group_m((s.M + bm - 1) / bm, (s.N + bn - 1) / bn);
+        err = launch_f32_mfma(s, ls, bm);
+    };
+    const float* A = static_cast<const float*>(p.A);
+    const float* B = static_cast<const float*>(p.B);
+    if (mf < p.M) {          // rows mf .. M-1, all columns
+        Problem s = p;
+        s.M = p.M - mf;
+        s.A = A + (p.oa == kRow ? (int64_t)mf * p.lda : (int64_t)mf);
+        s.C = p.C + (int64_t)mf * p.ldc;
+        strip(s);
+    }
+    if (nf < p.N) {          // rows 0 .. mf-1, columns nf .. N-1
+        Problem s = p;
+        s.M = mf;
+        s.N = p.N - nf;
+        s.B = B + (p.ob == kCol ? (int64_t)nf * p.ldb : (int64_t)nf);
+        s.C = p.C + nf;
+        strip(s);
+    }
+    return err;
 }
 
 template <typename Elem>
@@ -111,7 +152,11 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
             if (!f32) return GEMM_ERR_INVALID_VALUE;
             break;
         case GEMM_ALGO_MFMA_128x128: case GEMM_ALGO_MFMA_64x64: case GEMM_ALGO_SKINNY: break;
-        case GEMM_ALGO_MFMA_256x256: case GEMM_ALGO_MFMA_256x128: case GEMM_ALGO_MFMA_PINGPONG:
+        case GEMM_ALGO_MFMA_DMA:
+            if (!f32) return GEMM_ERR_INVALID_VALUE;
+            break;
+        case GEMM_ALGO_MFMA_256x256: break;
+        case GEMM_ALGO_MFMA_256x128: case GEMM_ALGO_MFMA_PINGPONG:
             if (f32) return GEMM_ERR_INVALID_VALUE;
             break;
         default: return GEMM_ERR_INVALID_VALUE;
@@ -162,9 +207,37 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
                 if (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus) && skinny_applies(p, false)) {
                     err = launch_skinny(p, l, false); name = "f32_skinny16"; break;
                 }
+                // direct-copy kernel (tiles 256 or 128) where it applies, else register-staged
+                const bool dma256 = f32_dma_applies(p, l, 256, 256);
+                const bool dma128 = f32_dma_applies(p, l, 128, 128);
                 int bm = 128, bn = 128;
-                if (algo == GEMM_ALGO_MFMA_64x64) bm = bn = 64;
-                else if (algo != GEMM_ALGO_MFMA_128x128) pick_tile(kF32Tiles, p.M, p.N, dev.cus, bm, bn);
+                bool dma = false;
+                if (algo == GEMM_ALGO_MFMA_64x64) {
+                    bm = bn = 64;
+                } else if (algo == GEMM_ALGO_MFMA_128x128) {
+                    bm = bn = 128;
+                } else if (algo == GEMM_ALGO_MFMA_256x256) {
+                    if (!dma256) return GEMM_ERR_INVALID_VALUE;
+                    bm = bn = 256;
+                    dma = true;
+                } else if (algo == GEMM_ALGO_MFMA_DMA) {
+                    if (!dma128) return GEMM_ERR_INVALID_VALUE;
+                    bm = bn = 128;
+                    if (dma256) pick_tile(kF32DmaTiles, p.M, p.N, dev.cus, bm, bn);
+                    if (bm == 64) bm = bn = 128;
+                    dma = true;
+                } else if (dma128) {
+                    pick_tile(kF32DmaTiles, p.M, p.N, dev.cus, bm, bn);
+                    if (bm == 256 && !dma256) bm = bn = 128;
+                    dma = bm >= 128;
+                } else {
+                    pick_tile(kF32Tiles, p.M, p.N, dev.cus, bm, bn);
+                }
+                if (dma) {
+                    err = launch_f32_dma_split(p, l, bm, dev.cus);
+                    name = bm == 256 ? "f32_dma256x256" : "f32_dma128x128";
+                    break;
+                }
                 l.group_m = pick_group_m((p.M + bm - 1) / bm, (p.N + bn - 1) / bn);
                 err = launch_f32_mfma(p, l, bm);
                 name = bm == 64 ? "f32_mfma64x64" : "f32_mfma128x128";

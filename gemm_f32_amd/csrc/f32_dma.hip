@@ -1,0 +1,320 @@
+// FP32 GEMM on the matrix cores with direct global->LDS copies: v_mfma_f32_16x16x4_f32.
+//
+// Same operation as f32_mfma.hip (FP32 inputs, FP32 products and sums on the matrix cores,
+// "A06 - Tiled Matrix Multiply (GEMM)", "Matrix cores: MFMA and Tensor Cores"), arranged
+// so that the operands never pass through registers on their way to LDS and one 16-byte
+// LDS read feeds four matrix instructions:
+//
+//  * Block tile BM x BN, k-tiles BK = 32 deep, 4 wavefronts in a 2 x 2 grid; a wavefront
+//    owns (BM/2) x (BN/2) of C as 16 x 16 blocks (4 x 4 blocks = 64 accumulators per lane
+//    at 128 x 128).
+//  * Instruction: v_mfma_f32_16x16x4_f32.  Lane l supplies A[i = l % 16][slot l / 16] and
+//    B[slot l / 16][j = l % 16]; the result of one block sits in lane l, register v at row
+//    4 (l / 16) + v, column l % 16.  The four k-slots may be bound to any four k as long as
+//    A and B agree: in k-group t (16 k) at step e (0..3), slot g stands for
+//    k = 16 t + 4 g + e, so a lane's four consecutive k are one 16-byte run.
+//  * LDS layout of an operand follows its layout in memory, so that the copy is a plain
+//    copy ("GEMM Optimization", V3: stage tiles in shared memory, prefetch the next one):
+//      - k-contiguous operand (row-major A, column-major B): one LDS row of BK floats
+//        (128 bytes, 8 chunks of 16 bytes) per row of the tile, chunk c of row r stored at
+//        c ^ s(r) (s(r) = (r mod 8) xor bit 3 of r): the 16 rows read at one logical chunk
+//        land on 16 distinct 16-byte bank groups.  A lane's 16-byte read at chunk 4 t + g
+//        holds its k-run for steps e = 0..3 of one block;
+//      - row-contiguous operand (row-major B, column-major A): one LDS row of BN (BM)
+//        floats per k, unpadded (16 lanes read 256 contiguous bytes).  A lane's 16-byte
+//        read at k = 16 t + 4 g + e holds 4 consecutive columns n0 + 4 c .. +3 (c = l % 16);
+//        element q of it goes to block q, so block q's column c is column n0 + 4 c + q of
+//        C.  The epilogue undoes the interleave, and for a row-major B each lane stores 4
+//        consecutive columns of C at once.
+//  * Copies: global_load_lds_dwordx4, 1 KB per instruction (16 bytes per lane at LDS
+//    position 16 l); a lane fetches the global chunk that belongs at its LDS position.
+//    S stages, the copies of k-tile kt + S - 1 issued among the matrix instructions of
+//    k-tile kt, one barrier per k-tile.
+//  * Tile order from the XCD-aware, group-M scheduler in common.hpp.
+//
+// Requirements (checked by the host): 16-byte aligned A and B with leading dimensions that
+// are multiples of 4 floats, K a multiple of BK, M and N multiples of the block tile.  The
+// host runs the whole-tile part of a ragged problem here and the edge strips with
+// f32_mfma.hip.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace gemm {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int BK = 32;                      // k per k-tile (two k-groups of 16)
+constexpr int KC_ROW = BK * 4;              // bytes per LDS row of a k-contiguous tile
+
+__device__ __forceinline__ int swz8(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+template <int BM_, int BN_, int WGM_, int WGN_, int S_, bool A_KC_, bool B_KC_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, S = S_, WGM = WGM_, WGN = WGN_;
+    static constexpr bool A_KC = A_KC_, B_KC = B_KC_;
+    static constexpr int NW = WGM * WGN, THREADS = 64 * NW;  // wavefronts, threads
+    static constexpr int WM = BM / WGM, WN = BN / WGN;
+    static constexpr int FM = WM / 16, FN = WN / 16;        // 16 x 16 blocks per wavefront
+    static constexpr int A_BYTES = BM * BK * 4, B_BYTES = BN * BK * 4;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int A_DMA = A_BYTES / 1024 / NW;       // copies per wavefront per k-tile
+    static constexpr int B_DMA = B_BYTES / 1024 / NW;
+    static constexpr int DMA = A_DMA + B_DMA;
+    // 16-byte fragment reads per k-group: one per block for a k-contiguous operand, one per
+    // step and 64 columns for a row-contiguous one
+    static constexpr int A_RD = A_KC ? FM : 4 * (FM / 4);
+    static constexpr int B_RD = B_KC ? FN : 4 * (FN / 4);
+    static constexpr int MFMA_PER_GROUP = 4 * FM * FN;
+    static_assert(FM % 4 == 0 && FN % 4 == 0, "wavefront tile must be a multiple of 64");
+    static_assert(A_DMA >= 1 && B_DMA >= 1, "tile too small");
+    // copy ranges per wavefront: k-contiguous, a multiple of 16 rows (the swizzle of copy j
+    // then depends on the parity of j only); row-contiguous, whole copies of 256 / X k-rows
+    static_assert(A_KC ? (BM / NW) % 16 == 0 : (BK / NW) % (BM >= 256 ? 1 : 256 / BM) == 0, "A copies");
+    static_assert(B_KC ? (BN / NW) % 16 == 0 : (BK / NW) % (BN >= 256 ? 1 : 256 / BN) == 0, "B copies");
+};
+
+// One operand's copy plan for one wavefront: a wavefront-uniform base address plus a lane
+// offset per copy parity.
+//   k-contiguous (rows R = BM or BN, 8 rows per copy, NW wavefronts): wavefront w copies
+//     rows w R/NW .. +R/NW-1; copy j covers rows +8 j .. +7, lane l row l / 8, LDS chunk
+//     l % 8, logical chunk (l % 8) ^ s(row); s(row) depends on l and on the parity of j
+//     only (R / NW is a multiple of 16).
+//   row-contiguous (X = R floats per k, 1024 / (4 X) k-rows per copy): wavefront w copies
+//     k-rows w BK/NW .. +BK/NW-1; lane l covers k-row l / (X / 4), floats 4 (l % (X / 4)).
+template <bool KC, int R, int NW>
+struct CopyPlan {
+    const char* base;      // the wavefront's first row (k-contiguous) or k-row, at k = 0
+    unsigned off[2];       // lane byte offset for even / odd copies
+    int64_t step;          // bytes between consecutive copies in global memory
+    int64_t kstep;         // bytes per k-tile in global memory
+
+    __device__ void init(const float* p, int64_t ld, int x0, int wave, int lane) {
+        if (KC) {
+            base = reinterpret_cast<const char*>(p + (int64_t)(x0 + wave * (R / NW)) * ld);
+            const int lr = lane / 8;
+#pragma unroll
+            for (int par = 0; par < 2; ++par) {
+                const int c = (lane % 8) ^ swz8(lr + 8 * par);
+                off[par] = (unsigned)((lr * ld + c * 4) * 4);
+            }
+            step = (int64_t)8 * ld * 4;
+            kstep = BK * 4;
+        } else {
+            constexpr int LPR = R / 4;                  // lanes per k-row
+            constexpr int RPC = 64 / LPR;               // k-rows per copy
+            base = reinterpret_cast<const char*>(p + (int64_t)(wave * (BK / NW)) * ld + x0);
+            off[0] = off[1] = (unsigned)(((lane / LPR) * ld + 4 * (lane % LPR)) * 4);
+            step = (int64_t)RPC * ld * 4;
+            kstep = (int64_t)BK * ld * 4;
+        }
+    }
+};
+
+template <typename C>
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void k_f32_dma(Problem p, int tiles_m, int tiles_n, int group_m) {
+    constexpr int BM = C::BM, BN = C::BN, S = C::S, FM = C::FM, FN = C::FN;
+    constexpr bool A_KC = C::A_KC, B_KC = C::B_KC;
+    __shared__ __align__(16) unsigned char smem[S * C::STAGE];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = (wave / C::WGN) * C::WM, wn = (wave % C::WGN) * C::WN;
+    const int nk = p.K / BK;
+    const float* A = static_cast<const float*>(p.A);
+    const float* B = static_cast<const float*>(p.B);
+
+    // ---- copies (whole tiles only: the host keeps partial tiles away from this kernel)
+    CopyPlan<A_KC, BM, C::NW> ca;
+    CopyPlan<B_KC, BN, C::NW> cb;
+    ca.init(A, p.lda, m0, wave, lane);
+    cb.init(B, p.ldb, n0, wave, lane);
+    // LDS: stage st = [A tile | B tile]; wavefront w's copies fill 1 KB blocks
+    // w * X_DMA .. +X_DMA-1 of each tile
+    auto issue_one = [&](int j, int kt, int st) {
+        unsigned char* s = smem + st * C::STAGE;
+        if (j < C::A_DMA) {
+            const char* src = ca.base + kt * ca.kstep + j * ca.step + ca.off[j & 1];
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(s + (wave * C::A_DMA + j) * 1024), 16, 0, 0);
+        } else {
+            const int jb = j - C::A_DMA;
+            const char* src = cb.base + kt * cb.kstep + jb * cb.step + cb.off[jb & 1];
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(s + C::A_BYTES + (wave * C::B_DMA + jb) * 1024),
+                                             16, 0, 0);
+        }
+    };
+
+    // ---- fragments of one k-group and the matrix instructions on them ----
+    const int li = lane & 15, g = lane >> 4;
+    // k-contiguous: block i's row wm + 16 i + li; swizzle depends on li only
+    const int a_kc_off = (wm + li) * KC_ROW, b_kc_off = C::A_BYTES + (wn + li) * KC_ROW;
+    const int sw = swz8(li);
+    // row-contiguous: k-row 16 t + 4 g + e, columns x0 + 64 q + 4 li
+    const int a_rc_off = (4 * g * BM + wm + 4 * li) * 4;
+    const int b_rc_off = C::A_BYTES + (4 * g * BN + wn + 4 * li) * 4;
+
+    struct Frags { f32x4 a[C::A_RD]; f32x4 b[C::B_RD]; };
+    auto read_group = [&](const unsigned char* st, int t, Frags& f) {
+        if (A_KC) {
+            const int coff = ((4 * t + g) ^ sw) << 4;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                f.a[i] = *reinterpret_cast<const f32x4*>(st + a_kc_off + i * 16 * KC_ROW + coff);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int q = 0; q < FM / 4; ++q)
+                    f.a[e * (FM / 4) + q] =
+                        *reinterpret_cast<const f32x4*>(st + a_rc_off + ((16 * t + e) * BM + 64 * q) * 4);
+        }
+        if (B_KC) {
+            const int coff = ((4 * t + g) ^ sw) << 4;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                f.b[j] = *reinterpret_cast<const f32x4*>(st + b_kc_off + j * 16 * KC_ROW + coff);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int q = 0; q < FN / 4; ++q)
+                    f.b[e * (FN / 4) + q] =
+                        *reinterpret_cast<const f32x4*>(st + b_rc_off + ((16 * t + e) * BN + 64 * q) * 4);
+        }
+    };
+    // operand of block i (j) at step e
+    auto a_val = [&](const Frags& f, int i, int e) -> float {
+        return A_KC ? f.a[i][e] : f.a[e * (FM / 4) + i / 4][i % 4];
+    };
+    auto b_val = [&](const Frags& f, int j, int e) -> float {
+        return B_KC ? f.b[j][e] : f.b[e * (FN / 4) + j / 4][j % 4];
+    };
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // One k-tile = 2 k-groups.  The fragments of group 1 are read while group 0 is
+    // multiplied; copy(n) is called before the n-th matrix instruction of the k-tile.
+    auto compute = [&](int st_idx, auto copy) {
+        const unsigned char* st = smem + st_idx * C::STAGE;
+        Frags f[2];
+        read_group(st, 0, f[0]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const int n = t * C::MFMA_PER_GROUP + (e * FM + i) * FN + j;
+                        copy(n);
+                        if (t == 0 && e == 0 && i == 0 && j == 0) read_group(st, 1, f[1]);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_val(f[t], i, e), b_val(f[t], j, e),
+                                                                         acc[i][j], 0, 0, 0);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+        }
+    };
+
+    // ---- S-stage pipeline: tiles 0 .. S-2 in flight before the loop (clamped like the
+    // copies in the loop when K has fewer k-tiles) ----
+#pragma unroll
+    for (int st = 0; st + 1 < S; ++st)
+#pragma unroll
+        for (int j = 0; j < C::DMA; ++j) issue_one(j, min(st, nk - 1), st);
+    constexpr int SLOTS = 2 * C::MFMA_PER_GROUP;
+    constexpr int SPREAD = SLOTS / C::DMA >= 4 ? 4 : SLOTS / C::DMA;
+    // Every k-tile issues the copies of tile min(kt + S - 1, nk - 1) into stage
+    // (kt + S - 1) % S, which the barrier has just freed: past the end of K the last tile is
+    // copied again into a stage nobody reads, so that the loop body has no branch (a branch
+    // among the matrix instructions costs more than the extra copy of one k-tile).
+    for (int kt = 0; kt < nk; ++kt) {
+        // tile kt has landed once at most the copies of tiles kt+1 .. kt+S-2 are pending
+        if (S == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else if (S == 3) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(C::DMA) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * C::DMA) : "memory");
+        __syncthreads();   // tile kt visible to all; stage (kt-1) % S free for reuse
+        const int kn = min(kt + S - 1, nk - 1), stn = (kt + S - 1) % S;
+        compute(kt % S, [&](int n) {
+            if (n % SPREAD == 0 && n / SPREAD < C::DMA) issue_one(n / SPREAD, kn, stn);
+        });
+    }
+    // the surplus copies must land before the workgroup's LDS is released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // ---- epilogue: block (i, j), lane l, register v: block row 4 (l / 16) + v, block
+    // column l % 16, mapped back through the operand layouts ----
+    const bool vec_c = (p.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int br = 4 * g + v;
+            const int row = m0 + wm + (A_KC ? 16 * i + br : 4 * br + i % 4 + 64 * (i / 4));
+            float* crow = p.C + (int64_t)row * p.ldc;
+            if (B_KC) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int col = n0 + wn + 16 * j + li;
+                    crow[col] = acc[i][j][v];
+                }
+            } else {
+                // columns n0 + wn + 64 q + 4 li + (j % 4): 4 consecutive floats per lane
+#pragma unroll
+                for (int q = 0; q < FN / 4; ++q) {
+                    const int col = n0 + wn + 64 * q + 4 * li;
+                    const f32x4 val = {acc[i][4 * q][v], acc[i][4 * q + 1][v], acc[i][4 * q + 2][v],
+                                       acc[i][4 * q + 3][v]};
+                    if (vec_c) {
+                        *reinterpret_cast<f32x4*>(crow + col) = val;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) crow[col + e] = val[e];
+                    }
+                }
+            }
+        }
+}
+
+template <int BM, int BN, int WGM, int WGN, int S>
+hipError_t launch_cfg(const Problem& p, const Launch& l) {
+    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+    const dim3 grid((unsigned)tiles_m * tiles_n), block(64 * WGM * WGN);
+    const bool akc = p.oa == kRow, bkc = p.ob == kCol;
+    const int g = l.group_m;
+    if (akc && bkc)
+        hipLaunchKernelGGL((k_f32_dma<Cfg<BM, BN, WGM, WGN, S, true, true>>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
+    else if (akc)
+        hipLaunchKernelGGL((k_f32_dma<Cfg<BM, BN, WGM, WGN, S, true, false>>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
+    else if (bkc)
+        hipLaunchKernelGGL((k_f32_dma<Cfg<BM, BN, WGM, WGN, S, false, true>>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
+    else
+        hipLaunchKernelGGL((k_f32_dma<Cfg<BM, BN, WGM, WGN, S, false, false>>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool f32_dma_applies(const Problem& p, const Launch& l, int bm, int bn) {
+    // the whole-tile part must be non-empty; the host sends partial tiles elsewhere
+    return l.vec_a && l.vec_b && p.K >= BK && p.K % BK == 0 && p.M >= bm && p.N >= bn;
+}
+
+// Configurations: 256 x 256 with 8 wavefronts of 64 x 128 (2 per SIMD, 128 KB of LDS),
+// 128 x 128 with 4 wavefronts of 64 x 64 (two workgroups per CU).
+hipError_t launch_f32_dma(const Problem& p, const Launch& l, int bm, int bn) {
+    if (bm == 256 && bn == 256) return launch_cfg<256, 256, 4, 2, 2>(p, l);
+    if (bm == 128 && bn == 128) return launch_cfg<128, 128, 2, 2, 2>(p, l);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gemm

@@ -13,6 +13,12 @@ hipError_t launch_tiled(const Problem& p, const Launch& l);
 hipError_t launch_regblock(const Problem& p, const Launch& l);
 // FP32 matrix-core kernel (f32_mfma.hip); tile is 128x128 or 64x64 (bm == bn)
 hipError_t launch_f32_mfma(const Problem& p, const Launch& l, int bm);
+// FP32 matrix-core kernel with direct global->LDS copies (f32_dma.hip); tile 256x256 or
+// 128x128.
+// Needs aligned operands, K a multiple of 32 and whole tiles (M, N multiples of the tile);
+// f32_dma_applies says whether the whole-tile part of a problem may run there.
+bool f32_dma_applies(const Problem& p, const Launch& l, int bm, int bn);
+hipError_t launch_f32_dma(const Problem& p, const Launch& l, int bm, int bn);
 // BF16 matrix-core kernel (bf16_mfma.hip); tile is one of 256x256, 256x128, 128x128, 64x64
 hipError_t launch_bf16_mfma(const Problem& p, const Launch& l, int bm, int bn);
 // BF16 256 x 256 eight-wavefront ping-pong kernel (bf16_pingpong.hip), for row-major A,

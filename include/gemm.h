@@ -71,8 +71,10 @@ typedef enum {
  *                      ("A06 - Tiled Matrix Multiply (GEMM)", "Matrix cores: MFMA and
  *                      Tensor Cores"); tile shape picked from the problem;
  *   MFMA_256x256, MFMA_256x128, MFMA_128x128, MFMA_64x64
- *                      the MFMA kernel with that block tile forced (FP32: 128x128 and
- *                      64x64 only);
+ *                      the MFMA kernel with that block tile forced.  FP32: 128x128 and
+ *                      64x64 select the register-staged v_mfma_f32_32x32x2_f32 kernel,
+ *                      256x256 the direct-copy kernel below (same requirements, with
+ *                      M, N >= 256); 256x128 is BF16 only;
  *   MFMA_PINGPONG      BF16 only: the 256 x 256 kernel with eight wavefronts in two groups
  *                      that alternate matrix-instruction and memory phases; needs row-major
  *                      A and column-major B (C may have either order), 16-byte aligned
@@ -86,8 +88,17 @@ typedef enum {
  *                      column-major C the roles of M/N and A/B swap, C^T = B^T A^T), else
  *                      GEMM_ERR_INVALID_VALUE.  AUTO uses it when it applies and M <= 64 or
  *                      64 x 64 tiles would fill less than half of the CUs.
- * The FP32 entry point accepts every algorithm but MFMA_256x256, MFMA_256x128 and
- * MFMA_PINGPONG; the BF16 entry point only AUTO, the MFMA ones and SKINNY (others give
+ *   MFMA_DMA           FP32 only: the direct-copy kernel, v_mfma_f32_16x16x4_f32 with both
+ *                      operands copied global -> LDS as laid out in memory (no register
+ *                      staging, no transposing stores; "GEMM Optimization", V3 staging),
+ *                      256 x 256 tiles (eight wavefronts) or 128 x 128 tiles (four), picked
+ *                      from the shape; needs 16-byte aligned A and B with leading
+ *                      dimensions that are multiples of 4, K a multiple of 32 and M, N >= 128
+ *                      (after the column-major-C swap), else GEMM_ERR_INVALID_VALUE.  Partial
+ *                      tiles along the bottom and right edges run on the register-staged
+ *                      kernel in the same call.  AUTO uses it whenever it applies and the
+ *                      cost model picks tiles of 128 or more.
+ * The FP32 entry point accepts every algorithm but MFMA_256x128 and MFMA_PINGPONG; the BF16 entry point only AUTO, the MFMA ones and SKINNY (others give
  * GEMM_ERR_INVALID_VALUE).
  */
 typedef enum {
@@ -102,7 +113,8 @@ typedef enum {
     GEMM_ALGO_MFMA_128x128 = 8,
     GEMM_ALGO_MFMA_64x64 = 9,
     GEMM_ALGO_MFMA_PINGPONG = 10,
-    GEMM_ALGO_SKINNY = 11
+    GEMM_ALGO_SKINNY = 11,
+    GEMM_ALGO_MFMA_DMA = 12
 } gemm_algo_t;
 
 /* FP32 inputs, FP32 arithmetic, FP32 C.  Same as gemm_f32_algo(GEMM_ALGO_AUTO, ...). */

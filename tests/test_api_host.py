@@ -81,13 +81,14 @@ def test_bf16_rejects_vector_alu_ladder(algo):
     assert _status(BF16, algo, *args()) == INVALID
 
 
-@pytest.mark.parametrize("algo", [6, 7, 10, 12, -1])
+@pytest.mark.parametrize("algo", [7, 10, 13, -1])
 def test_f32_rejects_unknown_tiles(algo):
     assert _status(F32, algo, *args()) == INVALID
 
 
-def test_bf16_rejects_unknown_algo():
-    assert _status(BF16, 12, *args()) == INVALID
+@pytest.mark.parametrize("algo", [12, 13])
+def test_bf16_rejects_unknown_algo(algo):
+    assert _status(BF16, algo, *args()) == INVALID
 
 
 @pytest.mark.parametrize("shape", [(0, 8, 8), (8, 0, 8), (0, 0, 0)])

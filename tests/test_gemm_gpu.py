@@ -261,7 +261,8 @@ def test_skinny_rejects_unsupported(bad):
 @pytest.mark.parametrize("dtype,shape,kernel", [
     ("f32", (16, 4096, 4096), "f32_skinny16"), ("bf16", (16, 4096, 4096), "bf16_skinny16"),
     ("f32", (256, 256, 256), "f32_skinny16"), ("f32", (1000, 1000, 1000), "f32_mfma64x64"),
-    ("bf16", (1000, 1000, 1000), "bf16_mfma64x64"), ("f32", (4096, 4096, 64), "f32_mfma128x128"),
+    ("f32", (2048, 2048, 256), "f32_dma128x128"), ("f32", (2047, 2049, 255), "f32_mfma128x128"),
+    ("bf16", (1000, 1000, 1000), "bf16_mfma64x64"), ("f32", (4096, 4096, 64), "f32_dma256x256"),
     ("bf16", (4096, 4096, 64), "bf16_mfma256x256")], ids=lambda v: str(v))
 def test_auto_kernel_choice(dtype, shape, kernel):
     """AUTO: few rows or too few 64 x 64 tiles -> small-problem kernel, else block tiles."""
@@ -269,3 +270,79 @@ def test_auto_kernel_choice(dtype, shape, kernel):
     p = gi.make_problem(M, N, K, dtype, ROW_MAJOR, COL_MAJOR if dtype == "bf16" else ROW_MAJOR, wid=52)
     check(p, g.Algo.AUTO)
     assert g.gemm_last_kernel() == kernel
+
+
+# --- FP32 direct-copy kernel (16x16x4 matrix instructions, operands copied into LDS as laid
+# out in memory) --------------------------------------------------------------------------
+# leading dimensions must be multiples of 4 floats; the ragged shapes leave partial tiles
+DMA_SHAPES = [(128, 128, 32), (256, 384, 64), (200, 256, 96), (128, 132, 32), (132, 644, 1024),
+              (384, 128, 4096), (252, 388, 160)]
+
+
+@pytest.mark.parametrize("orders", ORDERS3, ids=lambda o: "".join("RC"[x] for x in o))
+@pytest.mark.parametrize("shape", DMA_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f32_dma_random(orders, shape):
+    M, N, K = shape
+    oa, ob, oc = orders
+    p = gi.make_problem(M, N, K, "f32", oa, ob, oc, wid=53)
+    check(p, g.Algo.MFMA_DMA, key=("dma", orders, shape))
+    assert g.gemm_last_kernel().startswith("f32_dma")
+
+
+DMA256_SHAPES = [(256, 256, 32), (512, 768, 96), (300, 516, 64), (256, 1028, 224), (772, 260, 32)]
+
+
+@pytest.mark.parametrize("orders", ORDERS3, ids=lambda o: "".join("RC"[x] for x in o))
+@pytest.mark.parametrize("shape", DMA256_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f32_dma256_random(orders, shape):
+    """256 x 256 tiles of eight wavefronts; ragged shapes leave strips for the other kernel."""
+    M, N, K = shape
+    oa, ob, oc = orders
+    p = gi.make_problem(M, N, K, "f32", oa, ob, oc, wid=54)
+    check(p, g.Algo.MFMA_256x256, key=("dma256", orders, shape))
+    assert g.gemm_last_kernel() == "f32_dma256x256"
+
+
+def test_f32_dma256_small_integer_exact():
+    rng = np.random.default_rng(12)
+    M, N, K = 520, 516, 640
+    A = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    B = rng.integers(-4, 5, (K, N)).astype(np.float32)
+    check(gi.make_problem(M, N, K, "f32", ROW_MAJOR, ROW_MAJOR, A_logical=A, B_logical=B),
+          g.Algo.MFMA_256x256, exact=True)
+
+
+@pytest.mark.parametrize("ob", [ROW_MAJOR, COL_MAJOR], ids=["RR", "RC"])
+def test_f32_dma_small_integer_exact(ob):
+    rng = np.random.default_rng(11)
+    M, N, K = 300, 256, 640
+    A = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    B = rng.integers(-4, 5, (K, N)).astype(np.float32)
+    check(gi.make_problem(M, N, K, "f32", ROW_MAJOR, ob, A_logical=A, B_logical=B), g.Algo.MFMA_DMA,
+          exact=True)
+
+
+def test_f32_dma_closed_forms():
+    n = 256
+    ones = gi.make_problem(n, n, n, "f32", ROW_MAJOR, ROW_MAJOR, A_logical=np.ones((n, n), np.float32),
+                           B_logical=np.ones((n, n), np.float32))
+    C = logical_c(ones, run(ones, g.Algo.MFMA_DMA))
+    assert np.all(C == n)
+    perm = np.random.default_rng(3).permutation(n)
+    P = np.eye(n, dtype=np.float32)[perm]
+    B = np.random.default_rng(4).uniform(-1, 1, (n, n)).astype(np.float32)
+    pb = gi.make_problem(n, n, n, "f32", ROW_MAJOR, ROW_MAJOR, A_logical=P, B_logical=B)
+    assert np.array_equal(logical_c(pb, run(pb, g.Algo.MFMA_DMA)), B[perm])
+    pa = gi.make_problem(n, n, n, "f32", ROW_MAJOR, ROW_MAJOR, A_logical=B, B_logical=P.T.copy())
+    assert np.array_equal(logical_c(pa, run(pa, g.Algo.MFMA_DMA)), B[:, perm])
+
+
+@pytest.mark.parametrize("bad", [dict(K=48), dict(N=100), dict(M=127), dict(pad_a=1), dict(pad_b=2),
+                                 dict(order_a=COL_MAJOR, K=16)], ids=lambda d: str(d))
+def test_f32_dma_rejects_unsupported(bad):
+    kw = dict(M=256, N=256, K=64, dtype="f32", order_a=ROW_MAJOR, order_b=ROW_MAJOR)
+    kw.update(bad)
+    p = gi.make_problem(**kw)
+    with pytest.raises(g.GemmError) as e:
+        run(p, g.Algo.MFMA_DMA)
+    assert e.value.status == g.Status.ERR_INVALID_VALUE

@@ -12,8 +12,10 @@ kernel against MI355X's published matrix-core peak for its dtype.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--algo NAME]
 
 `--workload` picks another single workload from gemm_inputs.WORKLOADS (then one step is
-that one GEMM); `--algo` forces a kernel (gemm_f32_amd.Algo name).  Inputs rotate over
-`--sets` copies so that the 256 MB last-level cache cannot hold them across steps.
+that one GEMM); `--algo` forces a kernel (gemm_f32_amd.Algo name).  Each GEMM's inputs
+rotate over enough independently drawn copies (`--sets`, default: at least 2 and more
+than 512 MB of A and B together) that the 256 MB last-level cache cannot hold them across
+steps.
 The CPU baseline times the fp64 oracle on the host on a bounded sample of the same
 problems (the first rows of C) and scales it to TFLOP/s.
 """
@@ -42,7 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT)
     ap.add_argument("--algo", default="AUTO")
-    ap.add_argument("--sets", type=int, default=2)
+    ap.add_argument("--sets", type=int, default=0,
+                    help="input copies per GEMM (0: enough for > 512 MB, at least 2)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target host time of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -108,6 +111,11 @@ class Leg:
         self.algo = g.Algo[algo]
         self.problems = []
         self.A, self.B = [], []
+        if sets <= 0:
+            e = 4 if self.w.dtype == "f32" else 2
+            per_set = e * (self.w.M * self.w.K + self.w.K * self.w.N)
+            sets = min(64, max(2, (512 * 2**20) // per_set + 1))
+        self.sets = sets
         for s in range(sets):
             w = self.w
             p = gi.make_problem(w.M, w.N, w.K, w.dtype, w.order_a, w.order_b, w.order_c, w.dist,
@@ -208,7 +216,8 @@ def main():
         tf = leg.flops / (ms * 1e-3) / 1e12
         leg_info[leg.name] = {"kernel": leg.kernel, "ms": round(ms, 5), "tflops": round(tf, 2),
                               "pct_peak": round(100 * tf * 1e12 / peak, 2),
-                              "M": leg.w.M, "N": leg.w.N, "K": leg.w.K, "dtype_in": leg.w.dtype}
+                              "M": leg.w.M, "N": leg.w.N, "K": leg.w.K, "dtype_in": leg.w.dtype,
+                              "input_sets": leg.sets}
     dom = max(legs, key=lambda l: leg_info[l.name]["ms"])
     di = leg_info[dom.name]
     peak = rl.mi355x_peak(dom.w.dtype)
@@ -227,7 +236,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload if args.workload != DEFAULT else
                    "4096^3 FP32 GEMM + 4096^3 BF16->FP32 GEMM per step",
-                   "legs": leg_info, "algo": args.algo, "input_sets": args.sets,
+                   "legs": leg_info, "algo": args.algo,
                    "wall_s": round(wall, 3)},
         "roofline": roof,
     }

@@ -23,7 +23,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgemm.so")
 
 SOURCES = ["api.hip", "fill.hip", "f32_ladder.hip", "f32_regblock.hip", "f32_mfma.hip", "f32_dma.hip",
-           "bf16_mfma.hip", "bf16_pingpong.hip", "skinny.hip"]
+           "bf16_mfma.hip", "bf16_dma.hip", "bf16_pingpong.hip", "skinny.hip"]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -36,10 +36,11 @@ FLAGS = [
 ]
 
 
-# Per-source extra flags.  f32_dma.hip keeps its matrix accumulators in ordinary vector
-# registers: with the accumulation-register form the compiler rotated the accumulators
-# through register copies on every k-tile (visible in the kernel's assembly).
-EXTRA_FLAGS = {"f32_dma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source extra flags.  The FP32 direct-copy kernel keeps its matrix accumulators in
+# ordinary vector registers: with the accumulation-register form the compiler rotated the
+# accumulators through register copies on every k-tile (visible in the kernel's assembly).
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+EXTRA_FLAGS = {"f32_dma.hip": _VGPR_FORM}
 
 
 def hipcc() -> str:

@@ -88,9 +88,10 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     NaN stays NaN (quiet); finite values that round past the largest bf16 become inf,
     as IEEE rounding prescribes.
     """
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     lsb = (u >> 16) & 1
-    rounded = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    # uint32 arithmetic: only NaN patterns (>= 0xFFFF8000) can wrap, and they are replaced below
+    rounded = ((u + np.uint32(0x7FFF) + lsb) >> 16).astype(np.uint16)
     nan = np.isnan(np.asarray(x, dtype=np.float32))
     if nan.any():
         rounded = rounded.copy()

@@ -88,16 +88,20 @@ typedef enum {
  *                      column-major C the roles of M/N and A/B swap, C^T = B^T A^T), else
  *                      GEMM_ERR_INVALID_VALUE.  AUTO uses it when it applies and M <= 64 or
  *                      64 x 64 tiles would fill less than half of the CUs.
- *   MFMA_DMA           FP32 only: the direct-copy kernel, v_mfma_f32_16x16x4_f32 with both
- *                      operands copied global -> LDS as laid out in memory (no register
- *                      staging, no transposing stores; "GEMM Optimization", V3 staging),
- *                      256 x 256 tiles (eight wavefronts) or 128 x 128 tiles (four), picked
- *                      from the shape; needs 16-byte aligned A and B with leading
- *                      dimensions that are multiples of 4, K a multiple of 32 and M, N >= 128
- *                      (after the column-major-C swap), else GEMM_ERR_INVALID_VALUE.  Partial
- *                      tiles along the bottom and right edges run on the register-staged
- *                      kernel in the same call.  AUTO uses it whenever it applies and the
- *                      cost model picks tiles of 128 or more.
+ *   MFMA_DMA           the direct-copy kernels: operands copied global -> LDS as laid out in
+ *                      memory, no register staging ("GEMM Optimization", V3 staging), tile
+ *                      picked from the shape.  FP32: v_mfma_f32_16x16x4_f32, 256 x 256 tiles
+ *                      (eight wavefronts) or 128 x 128 (four); needs 16-byte aligned A and B
+ *                      with leading dimensions that are multiples of 4, K a multiple of 32
+ *                      and M, N >= 128.  BF16: v_mfma_f32_32x32x16_bf16, 256 x 256 or
+ *                      256 x 128 tiles of four wavefronts; needs row-major A and column-major
+ *                      B, 16-byte aligned with leading dimensions that are multiples of 8, K
+ *                      a multiple of 64, M >= 256 and N >= 128.  Conditions apply after the
+ *                      column-major-C swap; otherwise GEMM_ERR_INVALID_VALUE.  Partial tiles
+ *                      along the bottom and right edges run on the register-staged kernels
+ *                      in the same call.  AUTO uses the FP32 one whenever it applies and
+ *                      the cost model picks its tile sizes; for BF16 AUTO keeps the MFMA
+ *                      kernel above (measured as fast or faster on the BF16 workloads).
  * The FP32 entry point accepts every algorithm but MFMA_256x128 and MFMA_PINGPONG; the BF16 entry point only AUTO, the MFMA ones and SKINNY (others give
  * GEMM_ERR_INVALID_VALUE).
  */

@@ -263,7 +263,8 @@ def test_skinny_rejects_unsupported(bad):
     ("f32", (256, 256, 256), "f32_skinny16"), ("f32", (1000, 1000, 1000), "f32_mfma64x64"),
     ("f32", (2048, 2048, 256), "f32_dma128x128"), ("f32", (2047, 2049, 255), "f32_mfma128x128"),
     ("bf16", (1000, 1000, 1000), "bf16_mfma64x64"), ("f32", (4096, 4096, 64), "f32_dma256x256"),
-    ("bf16", (4096, 4096, 64), "bf16_mfma256x256")], ids=lambda v: str(v))
+    ("bf16", (4096, 4096, 64), "bf16_mfma256x256"),
+    ("bf16", (2048, 4096, 128), "bf16_mfma256x128")], ids=lambda v: str(v))
 def test_auto_kernel_choice(dtype, shape, kernel):
     """AUTO: few rows or too few 64 x 64 tiles -> small-problem kernel, else block tiles."""
     M, N, K = shape
@@ -341,6 +342,53 @@ def test_f32_dma_closed_forms():
                                  dict(order_a=COL_MAJOR, K=16)], ids=lambda d: str(d))
 def test_f32_dma_rejects_unsupported(bad):
     kw = dict(M=256, N=256, K=64, dtype="f32", order_a=ROW_MAJOR, order_b=ROW_MAJOR)
+    kw.update(bad)
+    p = gi.make_problem(**kw)
+    with pytest.raises(g.GemmError) as e:
+        run(p, g.Algo.MFMA_DMA)
+    assert e.value.status == g.Status.ERR_INVALID_VALUE
+
+
+# --- BF16 direct-copy kernel (eight wavefronts, row-major A and column-major B) ----------
+BDMA_SHAPES = [(256, 256, 64), (512, 384, 128), (300, 264, 192), (256, 128, 64), (776, 392, 64),
+               (1024, 1024, 1024)]
+
+
+@pytest.mark.parametrize("oc", [ROW_MAJOR, COL_MAJOR], ids=["RCR", "RCC"])
+@pytest.mark.parametrize("shape", BDMA_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_bf16_dma_random(oc, shape):
+    M, N, K = shape
+    if oc == COL_MAJOR and (N < 256 or M < 128):
+        pytest.skip("after the column-major-C swap the shape is below the smallest tile")
+    p = gi.make_problem(M, N, K, "bf16", ROW_MAJOR, COL_MAJOR, oc, wid=55)
+    check(p, g.Algo.MFMA_DMA, key=("bdma", oc, shape))
+    assert g.gemm_last_kernel().startswith("bf16_dma")
+
+
+def test_bf16_dma_small_integer_exact():
+    rng = np.random.default_rng(13)
+    M, N, K = 520, 392, 640
+    A = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    B = rng.integers(-4, 5, (K, N)).astype(np.float32)
+    check(gi.make_problem(M, N, K, "bf16", ROW_MAJOR, COL_MAJOR, A_logical=A, B_logical=B),
+          g.Algo.MFMA_DMA, exact=True)
+
+
+def test_bf16_dma_closed_forms():
+    n = 256
+    perm = np.random.default_rng(5).permutation(n)
+    P = np.eye(n, dtype=np.float32)[perm]
+    B = gi.bf16_bits_to_f32(gi.f32_to_bf16_bits(np.random.default_rng(6).uniform(-1, 1, (n, n)).astype(np.float32)))
+    pb = gi.make_problem(n, n, n, "bf16", ROW_MAJOR, COL_MAJOR, A_logical=P, B_logical=B)
+    assert np.array_equal(logical_c(pb, run(pb, g.Algo.MFMA_DMA)), B[perm])
+    pa = gi.make_problem(n, n, n, "bf16", ROW_MAJOR, COL_MAJOR, A_logical=B, B_logical=P.T.copy())
+    assert np.array_equal(logical_c(pa, run(pa, g.Algo.MFMA_DMA)), B[:, perm])
+
+
+@pytest.mark.parametrize("bad", [dict(K=96), dict(order_b=ROW_MAJOR), dict(pad_a=1), dict(M=200),
+                                 dict(N=64), dict(order_a=COL_MAJOR)], ids=lambda d: str(d))
+def test_bf16_dma_rejects_unsupported(bad):
+    kw = dict(M=256, N=256, K=128, dtype="bf16", order_a=ROW_MAJOR, order_b=COL_MAJOR)
     kw.update(bad)
     p = gi.make_problem(**kw)
     with pytest.raises(g.GemmError) as e:

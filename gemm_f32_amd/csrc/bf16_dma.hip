@@ -202,7 +202,7 @@ hipError_t launch_cfg(const Problem& p, const Launch& l) {
 }  // namespace
 
 bool bf16_dma_applies(const Problem& p, const Launch& l, int bm, int bn) {
-    return p.oa == kRow && p.ob == kCol && l.vec_a && l.vec_b && p.K >= 64 && p.K % 64 == 0 &&
+    return p.oa == kRow && p.ob == kCol && l.al_a && l.al_b && p.K >= 64 && p.K % 64 == 0 &&
            p.M >= bm && p.N >= bn;
 }
 

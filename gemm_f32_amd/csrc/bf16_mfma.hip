@@ -38,9 +38,10 @@
 //    chunks along k; rows past the matrix edge are clamped to the last row (their
 //    products only feed outputs that are never stored).  An operand contiguous along
 //    M or N is fetched in 16-byte chunks along that dimension and scattered into the
-//    k-contiguous LDS layout.  The K tail, misaligned pointers or leading dimensions,
-//    and edge tiles of an M/N-contiguous operand take an element-wise path with bounds
-//    checks and zero fill ("A06", "Pitfall 1 - The boundary guard that fails silently").
+//    k-contiguous LDS layout.  16-byte loads need element alignment only (gfx950 serves
+//    unaligned vector loads); the direct copies need 16-byte aligned rows.  The K tail and
+//    edge tiles of an M/N-contiguous operand take an element-wise path with bounds checks
+//    and zero fill ("A06", "Pitfall 1 - The boundary guard that fails silently").
 //  * Tile order from the XCD-aware, group-M scheduler in common.hpp.
 #include "common.hpp"
 #include "launch.hpp"
@@ -96,11 +97,11 @@ __device__ __forceinline__ uint4 pack8(const u16 (&v)[8]) {
 }
 
 // Chunk q of a KC tile: tile row q / CH, k = 8 * (q % CH) .. +7.  The fast form needs a
-// full k-tile and 16-byte alignment; rows past the edge are clamped to the last row.
+// full k-tile; rows past the edge are clamped to the last row.
 template <int CH>
 __device__ __forceinline__ uint4 load_kc_fast(const Operand& x, int row0, int k0, int q) {
     const int row = min(row0 + q / CH, x.rows - 1);
-    return *reinterpret_cast<const uint4*>(x.p + (int64_t)row * x.ld + k0 + (q % CH) * 8);
+    return load16(x.p + (int64_t)row * x.ld + k0 + (q % CH) * 8);
 }
 template <int CH>
 __device__ __forceinline__ uint4 load_kc_checked(const Operand& x, int row0, int k0, int K, int q) {
@@ -118,11 +119,11 @@ __device__ __forceinline__ void store_kc(unsigned char* s, int q, uint4 v) {
 }
 
 // Chunk q of an RC tile: k = q / (TR / 8), tile rows 8 * (q % (TR / 8)) .. +7.  The fast
-// form needs the whole tile inside the matrix, a full k-tile and 16-byte alignment.
+// form needs the whole tile inside the matrix and a full k-tile.
 template <int TR>
 __device__ __forceinline__ uint4 load_rc_fast(const Operand& x, int row0, int k0, int q) {
     constexpr int CPK = TR / 8;
-    return *reinterpret_cast<const uint4*>(x.p + (int64_t)(k0 + q / CPK) * x.ld + row0 + (q % CPK) * 8);
+    return load16(x.p + (int64_t)(k0 + q / CPK) * x.ld + row0 + (q % CPK) * 8);
 }
 template <int TR>
 __device__ __forceinline__ uint4 load_rc_checked(const Operand& x, int row0, int k0, int K, int q) {
@@ -150,7 +151,7 @@ __device__ __forceinline__ void store_rc(unsigned char* s, int q, uint4 v) {
 
 template <int BM, int BN, int BK, int S, bool A_KC, bool B_KC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
-void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, int vec_b) {
+void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, int vec_b, int al_ab) {
     using T = Tile<BM, BN, BK, S>;
     constexpr int CH = T::CH;
     // the direct path issues one tile's copies in the first SUB * FM * FN instruction slots
@@ -201,7 +202,7 @@ void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, in
         }
     };
     // ---- element-wise loads with bounds checks and zero fill into the same staging
-    // registers (misaligned operands, edge tiles of a row-contiguous operand): issued before
+    // registers (K tail, edge tiles of a row-contiguous operand): issued before
     // a k-tile's matrix instructions and stored after them, like the 16-byte loads
     auto gload_checked = [&](int k0) {
 #pragma unroll
@@ -290,7 +291,7 @@ void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, in
     auto no_copy = [](int) {};
 
     int kt = 0;
-    if (A_KC && B_KC && vec_a && vec_b && interior && nfull > 0) {
+    if (A_KC && B_KC && al_ab && interior && nfull > 0) {
         // ---- direct path: full k-tiles copied global -> LDS without registers, S stages ----
         // Copy j of a wavefront fills tile rows r0 + RPI j .. +RPI-1 (r0 = the wavefront's
         // first row, a multiple of 16); lane l fetches the chunk that belongs at LDS
@@ -394,15 +395,15 @@ hipError_t launch_tile(const Problem& p, const Launch& l) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const dim3 grid((unsigned)tiles_m * tiles_n), block(256);
     const bool akc = p.oa == kRow, bkc = p.ob == kCol;
-    const int va = l.vec_a, vb = l.vec_b, g = l.group_m;
+    const int va = l.vec_a, vb = l.vec_b, g = l.group_m, al = l.al_a && l.al_b;
     if (akc && bkc)
-        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, true, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb);
+        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, true, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
     else if (akc)
-        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, true, false>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb);
+        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, true, false>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
     else if (bkc)
-        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, false, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb);
+        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, false, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
     else
-        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, false, false>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb);
+        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, false, false>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
     return hipGetLastError();
 }
 

@@ -181,7 +181,7 @@ void k_bf16_pingpong(Problem p, int tiles_m, int tiles_n, int group_m) {
 }  // namespace
 
 bool bf16_pingpong_applies(const Problem& p, const Launch& l) {
-    return p.oa == kRow && p.ob == kCol && l.vec_a && l.vec_b && p.M % BM == 0 &&
+    return p.oa == kRow && p.ob == kCol && l.al_a && l.al_b && p.M % BM == 0 &&
            p.N % BN == 0 && p.K % BK == 0 && p.K >= BK;
 }
 

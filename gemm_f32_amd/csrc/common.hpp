@@ -66,8 +66,24 @@ __host__ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int ti
 struct Launch {
     hipStream_t stream;
     int group_m;        // tile-scheduler band height (>= 1)
-    bool vec_a, vec_b;  // operand pointer and leading dimension allow 16-byte loads
+    bool vec_a, vec_b;  // 16-byte loads of the operand are allowed (load16 / load16f)
+    bool al_a, al_b;    // operand pointer and leading dimension are 16-byte aligned: needed
+                        // by the direct global->LDS copies
     bool vec_c;         // C pointer and ldc allow 16-byte stores
 };
+
+// 16-byte global loads from addresses aligned to the element only.  gfx950 serves unaligned
+// vector loads from global memory (the parity tests with padded and odd leading dimensions
+// cover it), so operands whose rows are not 16-byte aligned still move 16 bytes per lane.
+typedef unsigned int u32x4_ua __attribute__((ext_vector_type(4), aligned(2)));
+typedef float f32x4_ua __attribute__((ext_vector_type(4), aligned(4)));
+__device__ __forceinline__ uint4 load16(const void* p) {
+    const u32x4_ua v = *reinterpret_cast<const u32x4_ua*>(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 load16f(const float* p) {
+    const f32x4_ua v = *reinterpret_cast<const f32x4_ua*>(p);
+    return make_float4(v.x, v.y, v.z, v.w);
+}
 
 }  // namespace gemm

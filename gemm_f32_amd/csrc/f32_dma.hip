@@ -306,7 +306,7 @@ hipError_t launch_cfg(const Problem& p, const Launch& l) {
 
 bool f32_dma_applies(const Problem& p, const Launch& l, int bm, int bn) {
     // the whole-tile part must be non-empty; the host sends partial tiles elsewhere
-    return l.vec_a && l.vec_b && p.K >= BK && p.K % BK == 0 && p.M >= bm && p.N >= bn;
+    return l.al_a && l.al_b && p.K >= BK && p.K % BK == 0 && p.M >= bm && p.N >= bn;
 }
 
 // Configurations: 256 x 256 with 8 wavefronts of 64 x 128 (2 per SIMD, 128 KB of LDS),

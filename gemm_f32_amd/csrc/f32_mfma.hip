@@ -26,7 +26,8 @@
 //  * operand fragment for one instruction: lane l supplies A[i = l % 32][k = l / 32] and
 //    B[k = l / 32][j = l % 32]; accumulator layout: lane l, register r holds C[i][j] with
 //    j = l % 32 and i = 8 (r / 4) + 4 (l / 32) + r % 4;
-//  * loads along each operand's contiguous dimension, 16 bytes per lane when aligned;
+//  * loads along each operand's contiguous dimension, 16 bytes per lane (element alignment
+//    suffices on gfx950);
 //    edge tiles and the K tail load element by element with bounds checks and zero fill,
 //    stores are guarded ("A06", "Pitfall 1 - The boundary guard that fails silently").
 #include "common.hpp"
@@ -65,7 +66,7 @@ __device__ __forceinline__ float4 load4(const Operand& o, int x0, int k0, int K,
     const int x = KC ? idx / (BK / 4) : (idx % (X / 4)) * 4;
     const int k = KC ? (idx % (BK / 4)) * 4 : idx / (X / 4);
     if (fast)
-        return *reinterpret_cast<const float4*>(o.p + (KC ? (int64_t)(x0 + x) * o.ld + k0 + k
+        return load16f(o.p + (KC ? (int64_t)(x0 + x) * o.ld + k0 + k
                                                            : (int64_t)(k0 + k) * o.ld + x0 + x));
     float v[4];
 #pragma unroll

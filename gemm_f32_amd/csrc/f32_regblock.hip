@@ -42,7 +42,7 @@ __device__ __forceinline__ float4 load_a(const Problem& p, int m0, int k0, int t
     const float* A = static_cast<const float*>(p.A);
     const int m = OA == kRow ? t >> 1 : (t & 31) * 4;
     const int k = OA == kRow ? (t & 1) * 4 : t >> 5;
-    if (fast) return *reinterpret_cast<const float4*>(A + elem_offset(m0 + m, k0 + k, p.lda, OA));
+    if (fast) return load16f(A + elem_offset(m0 + m, k0 + k, p.lda, OA));
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -73,7 +73,7 @@ __device__ __forceinline__ float4 load_b(const Problem& p, int n0, int k0, int t
     const float* B = static_cast<const float*>(p.B);
     const int n = OB == kRow ? (t & 31) * 4 : t >> 1;
     const int k = OB == kRow ? t >> 5 : (t & 1) * 4;
-    if (fast) return *reinterpret_cast<const float4*>(B + elem_offset(k0 + k, n0 + n, p.ldb, OB));
+    if (fast) return load16f(B + elem_offset(k0 + k, n0 + n, p.ldb, OB));
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {

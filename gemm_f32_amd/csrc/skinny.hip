@@ -26,9 +26,9 @@
 //
 // Requirements (checked by the host): A row-major (k-contiguous); B column-major for BF16,
 // either order for FP32.  Any M, N, K; A strips are re-read once per column slab, which is
-// cheap only while the problem is small or M is.  Rows past M and columns past N are clamped to the last valid one
-// (their products are never stored); the K tail and misaligned operands use element-wise
-// loads with zero fill.
+// cheap only while the problem is small or M is.  Rows past M and columns past N are
+// clamped to the last valid one (their products are never stored); the K tail uses
+// element-wise loads with zero fill.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -48,7 +48,7 @@ struct Bf16 {
     using Frag = uint4;
     static constexpr int KSTEP = 32, KL = 8;        // k per step, k per lane
     __device__ static Frag load(const u16* row, int k, int K, bool fast) {
-        if (fast) return *reinterpret_cast<const uint4*>(row + k);
+        if (fast) return load16(row + k);
         u16 v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = (k + e < K) ? row[k + e] : (u16)0;
@@ -67,7 +67,7 @@ struct F32 {
     using Frag = float4;
     static constexpr int KSTEP = 16, KL = 4;
     __device__ static Frag load(const float* row, int k, int K, bool fast) {
-        if (fast) return *reinterpret_cast<const float4*>(row + k);
+        if (fast) return load16f(row + k);
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (k + e < K) ? row[k + e] : 0.f;

@@ -22,8 +22,8 @@
  *
  * Ownership.  All matrix pointers are device pointers owned by the caller; A and B are
  * only read, C is only written, and C must not overlap A or B.  Pointers need only their
- * element's natural alignment (4 bytes for float, 2 for bf16); wider alignment of the
- * pointers and leading dimensions lets the library pick wider loads.  The library
+ * element's natural alignment (4 bytes for float, 2 for bf16); 16-byte aligned pointers
+ * and leading dimensions let the library use its direct global->LDS kernels.  The library
  * allocates no device memory and keeps no state beyond a per-device property cache.
  *
  * Streams and errors.  Work is enqueued on `stream` (0 = the null stream) of the

@@ -79,26 +79,28 @@ bool prefer_small(const Problem& p, int cus) {
     return p.M <= kSkinnyMaxM || tiles(p.M, p.N, 64, 64) * 2 < (cus > 0 ? cus : 256);
 }
 
-// Block-tile choice.  A block tile per CU and as few partial waves as possible: among the
-// tiles, estimate time as (waves of tiles over the CUs) x (work per tile / relative
-// efficiency of the tile size), and take the cheapest.
-struct TileOpt { int bm, bn; double eff; };
-constexpr TileOpt kBf16Tiles[] = {{256, 256, 1.0}, {256, 128, 0.85}, {128, 128, 0.65}, {64, 64, 0.3}};
-// BF16 with the direct-copy kernel available (256 x 256, 256 x 128) and the
-// register-staged one for smaller tiles
-constexpr TileOpt kBf16DmaTiles[] = {{256, 256, 1.0}, {256, 128, 0.8}, {128, 128, 0.45}, {64, 64, 0.2}};
+// Block-tile choice.  The grid runs in rounds of cus x per_cu resident blocks (per_cu: how
+// many blocks of that kernel share a CU); a CU's round costs (blocks it holds) x (work per
+// tile / relative throughput of the tile size), so estimate time as the sum over rounds and
+// take the cheapest.  Relative throughputs are the kernels' measured rates at 4096^3 with full
+// rounds.
+struct TileOpt { int bm, bn; double eff; int per_cu; };
+constexpr TileOpt kBf16Tiles[] = {{256, 256, 1.0, 1}, {256, 128, 0.78, 1}, {128, 128, 0.82, 2},
+                                  {64, 64, 0.36, 4}};
+// BF16 direct-copy kernel (256 x 256, 256 x 128)
+constexpr TileOpt kBf16DmaTiles[] = {{256, 256, 1.0, 1}, {256, 128, 0.8, 1}};
 // FP32: the register-staged kernel (128 x 128, 64 x 64) and, where its requirements hold,
-// the direct-copy kernel (256 x 256, 128 x 128); relative speeds as measured at 4096^3
-constexpr TileOpt kF32Tiles[] = {{128, 128, 1.0}, {64, 64, 0.5}};
-constexpr TileOpt kF32DmaTiles[] = {{256, 256, 1.0}, {128, 128, 0.8}, {64, 64, 0.4}};
+// the direct-copy kernel (256 x 256, 128 x 128) with the register-staged 64 x 64
+constexpr TileOpt kF32Tiles[] = {{128, 128, 1.0, 4}, {64, 64, 0.92, 4}};
+constexpr TileOpt kF32DmaTiles[] = {{256, 256, 1.0, 1}, {128, 128, 0.85, 2}, {64, 64, 0.76, 4}};
 
 template <size_t NOPT>
 void pick_tile(const TileOpt (&opts)[NOPT], int64_t M, int64_t N, int cus, int& bm, int& bn) {
     double best = 1e300;
     for (const TileOpt& o : opts) {
-        const double n = (double)tiles(M, N, o.bm, o.bn);
-        const double waves = std::ceil(n / (cus > 0 ? cus : 256));
-        const double cost = waves * o.bm * o.bn / o.eff;
+        const double c = cus > 0 ? cus : 256, n = (double)tiles(M, N, o.bm, o.bn);
+        const double full = std::floor(n / (c * o.per_cu)), rest = n - full * c * o.per_cu;
+        const double cost = (full * o.per_cu + std::ceil(rest / c)) * o.bm * o.bn / o.eff;
         if (cost < best) { best = cost; bm = o.bm; bn = o.bn; }
     }
 }
@@ -266,7 +268,7 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
                     if (!dma128) return GEMM_ERR_INVALID_VALUE;
                     bm = bn = 128;
                     if (dma256) pick_tile(kF32DmaTiles, p.M, p.N, dev.cus, bm, bn);
-                    if (bm == 64) bm = bn = 128;
+                    if (bm != 256) bm = bn = 128;
                     dma = true;
                 } else if (dma128) {
                     pick_tile(kF32DmaTiles, p.M, p.N, dev.cus, bm, bn);

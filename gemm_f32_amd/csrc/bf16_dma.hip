@@ -16,11 +16,10 @@
 //    what matters, not its order).
 //  * Accumulator layout of a 32 x 32 fragment: lane l, register r holds row
 //    8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
-//  * Copies: global_load_lds_dwordx4, 1 KB (8 tile rows) per instruction, a lane fetching
-//    the chunk that belongs at its LDS position; S stages ("GEMM Optimization", V3), the
-//    copies of k-tile kt + S - 1 issued among the matrix instructions of k-tile kt, one
-//    barrier per k-tile.  The loop body has no branch: past the end of K the last k-tile
-//    is copied again into a stage nobody reads.
+//  * Copies: global_load_lds_dwordx4, 1 KB per instruction, a lane fetching the chunk that
+//    belongs at its LDS position; two stages ("GEMM Optimization", V3), software-pipelined
+//    across k-tiles (see the main loop), one barrier per k-tile.  The loop body has no
+//    branch: past the end of K the last k-tile is copied again into a stage nobody reads.
 //  * Tile order from the XCD-aware, group-M scheduler in common.hpp.
 //
 // Requirements (checked by the host): row-major A and column-major B after the
@@ -133,46 +132,54 @@ void k_bf16_dma(Problem p, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) f.b[j] = *reinterpret_cast<const bf16x8*>(st + b_off + j * 32 * ROW + coff);
     };
-    // One k-tile: SUB k-steps; the fragments of step s + 1 are read while step s is
-    // multiplied; copy(n) runs before the n-th matrix instruction of the k-tile.
-    auto compute = [&](int st_idx, auto copy) {
-        const unsigned char* st = smem + st_idx * C::STAGE;
-        Frags f[2];
-        read_step(st, 0, f[0]);
+    // ---- software pipeline over k-tiles, two LDS stages.  Iteration kt multiplies tile kt
+    // (stage kt % 2).  Its last k-step is preceded by the barrier that publishes tile kt+1
+    // (every wavefront has waited for its own copies of it) and frees stage kt % 2 (every
+    // wavefront's reads of it have completed).  During that last k-step each wavefront
+    // reads the first fragments of tile kt+1 and issues the copies of tile kt+2 into the
+    // freed stage, so neither the barrier nor the first LDS reads of a tile leave the matrix
+    // pipe waiting.  Past the end of K the copies repeat the last tile into a stage nobody
+    // reads and the reads of a tile nk are never used, which keeps the loop free of branches.
+    static_assert(S == 2, "two-stage pipeline");
+    // copies of the next tile spread over the last k-step: CPS per matrix instruction
+    constexpr int CPS = (C::DMA + C::MF - 1) / C::MF;
+#pragma unroll
+    for (int j = 0; j < C::DMA; ++j) issue_one(j, 0, 0);
+#pragma unroll
+    for (int j = 0; j < C::DMA; ++j) issue_one(j, min(1, nk - 1), 1);
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(C::DMA) : "memory");   // own copies of tile 0
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    Frags f[2];
+    read_step(smem, 0, f[0]);
+    for (int kt = 0; kt < nk; ++kt) {
+        const unsigned char* cur = smem + (kt & 1) * C::STAGE;
+        const unsigned char* nxt = smem + ((kt + 1) & 1) * C::STAGE;
+        const int kc = min(kt + 2, nk - 1);
 #pragma unroll
         for (int s = 0; s < SUB; ++s) {
+            if (s == SUB - 1) {
+                // own copies of tile kt+1 landed and own reads of tile kt complete; a plain
+                // barrier (the compiler's workgroup fence would also drain later copies)
+                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+            }
 #pragma unroll
             for (int m = 0; m < C::MF; ++m) {
                 const int i = m / FN, j = m % FN;
-                copy(s * C::MF + m);
-                if (m == 0 && s + 1 < SUB) read_step(st, s + 1, f[(s + 1) & 1]);
+                // after the first instruction of the step, so that the wait for this step's
+                // fragments does not also cover the reads of the next one
+                if (m == 1) read_step(s + 1 < SUB ? cur : nxt, (s + 1) % SUB, f[(s + 1) & 1]);
+                if (s == SUB - 1)
+#pragma unroll
+                    for (int c = m * CPS; c < (m + 1) * CPS; ++c)
+                        if (c < C::DMA) issue_one(c, kc, kt & 1);
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[s & 1].a[i], f[s & 1].b[j], acc[i][j], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-    };
-
-    // prologue: tiles 0 .. S-2 in flight (clamped to the last tile when K is short)
-#pragma unroll
-    for (int st = 0; st + 1 < S; ++st)
-#pragma unroll
-        for (int j = 0; j < C::DMA; ++j) issue_one(j, min(st, nk - 1), st);
-    constexpr int SLOTS = SUB * C::MF;
-    constexpr int SPREAD = SLOTS / C::DMA >= 4 ? 4 : SLOTS / C::DMA;
-    for (int kt = 0; kt < nk; ++kt) {
-        // tile kt has landed once at most the copies of tiles kt+1 .. kt+S-2 are pending
-        if (S == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        else if (S == 3) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(C::DMA) : "memory");
-        else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * C::DMA) : "memory");
-        // tile kt visible to all; stage (kt-1) % S free for reuse.  A plain barrier: the
-        // compiler's workgroup fence would also wait for the copies still in flight.
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        const int kn = min(kt + S - 1, nk - 1), stn = (kt + S - 1) % S;
-        compute(kt % S, [&](int n) {
-            if (n % SPREAD == 0 && n / SPREAD < C::DMA) issue_one(n / SPREAD, kn, stn);
-        });
     }
     // the surplus copies must land before the workgroup's LDS is released
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

@@ -33,9 +33,9 @@
 //  * Tile order from the XCD-aware, group-M scheduler in common.hpp.
 //
 // Requirements (checked by the host): 16-byte aligned A and B with leading dimensions that
-// are multiples of 4 floats, K a multiple of BK, M and N multiples of the block tile.  The
-// host runs the whole-tile part of a ragged problem here and the edge strips with
-// f32_mfma.hip.
+// are multiples of 4 floats, K >= BK, M and N multiples of the block tile.  A K tail takes
+// one more k-tile loaded with bounds checks.  The host runs the whole-tile part of a ragged
+// problem here and the edge strips with f32_mfma.hip.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -251,6 +251,45 @@ void k_f32_dma(Problem p, int tiles_m, int tiles_n, int group_m) {
     // the surplus copies must land before the workgroup's LDS is released
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+    // ---- K tail (K not a multiple of BK): one more k-tile, staged through registers with
+    // bounds checks and zero fill into the same LDS positions the copies would fill ----
+    if (p.K % BK != 0) {                       // uniform
+        __syncthreads();                       // every wavefront is done reading LDS
+        const int k0 = nk * BK;
+#pragma unroll
+        for (int j = 0; j < C::DMA; ++j) {
+            const bool is_a = j < C::A_DMA;
+            const int jj = is_a ? j : j - C::A_DMA;
+            const bool kc = is_a ? A_KC : B_KC;
+            const float* src = is_a ? A : B;
+            const int64_t ld = is_a ? p.lda : p.ldb;
+            const int x0 = is_a ? m0 : n0, R = is_a ? BM : BN;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (kc) {
+                // tile row r, logical chunk (lane % 8) ^ s(r): k = k0 + 4 c .. +3
+                const int r = wave * (R / C::NW) + 8 * jj + lane / 8;
+                const int k = k0 + 4 * ((lane % 8) ^ swz8(r));
+                const float* q = src + (int64_t)(x0 + r) * ld + k;
+                if (k + 3 < p.K) v = load16f(q);
+                else {
+                    if (k < p.K) v.x = q[0];
+                    if (k + 1 < p.K) v.y = q[1];
+                    if (k + 2 < p.K) v.z = q[2];
+                }
+            } else {
+                // k-row k0 + w BK/NW + RPC jj + lane / LPR, columns x0 + 4 (lane % LPR) .. +3
+                const int lpr = R / 4, rpc = 64 / lpr;
+                const int kr = k0 + wave * (BK / C::NW) + rpc * jj + lane / lpr;
+                if (kr < p.K) v = load16f(src + (int64_t)kr * ld + x0 + 4 * (lane % lpr));
+            }
+            unsigned char* dst = smem + (is_a ? (wave * C::A_DMA + jj) * 1024
+                                              : C::A_BYTES + (wave * C::B_DMA + jj) * 1024) + 16 * lane;
+            *reinterpret_cast<float4*>(dst) = v;
+        }
+        __syncthreads();
+        compute(0, [](int) {});
+    }
+
     // ---- epilogue: block (i, j), lane l, register v: block row 4 (l / 16) + v, block
     // column l % 16, mapped back through the operand layouts ----
     const bool vec_c = (p.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0;
@@ -306,7 +345,7 @@ hipError_t launch_cfg(const Problem& p, const Launch& l) {
 
 bool f32_dma_applies(const Problem& p, const Launch& l, int bm, int bn) {
     // the whole-tile part must be non-empty; the host sends partial tiles elsewhere
-    return l.al_a && l.al_b && p.K >= BK && p.K % BK == 0 && p.M >= bm && p.N >= bn;
+    return l.al_a && l.al_b && p.K >= BK && p.M >= bm && p.N >= bn;
 }
 
 // Configurations: 256 x 256 with 8 wavefronts of 64 x 128 (2 per SIMD, 128 KB of LDS),

@@ -92,8 +92,8 @@ typedef enum {
  *                      memory, no register staging ("GEMM Optimization", V3 staging), tile
  *                      picked from the shape.  FP32: v_mfma_f32_16x16x4_f32, 256 x 256 tiles
  *                      (eight wavefronts) or 128 x 128 (four); needs 16-byte aligned A and B
- *                      with leading dimensions that are multiples of 4, K a multiple of 32
- *                      and M, N >= 128.  BF16: v_mfma_f32_32x32x16_bf16, 256 x 256 or
+ *                      with leading dimensions that are multiples of 4, K >= 32 and
+ *                      M, N >= 128.  BF16: v_mfma_f32_32x32x16_bf16, 256 x 256 or
  *                      256 x 128 tiles of four wavefronts; needs row-major A and column-major
  *                      B, 16-byte aligned with leading dimensions that are multiples of 8, K
  *                      a multiple of 64, M >= 256 and N >= 128.  Conditions apply after the

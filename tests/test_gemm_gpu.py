@@ -277,7 +277,7 @@ def test_auto_kernel_choice(dtype, shape, kernel):
 # out in memory) --------------------------------------------------------------------------
 # leading dimensions must be multiples of 4 floats; the ragged shapes leave partial tiles
 DMA_SHAPES = [(128, 128, 32), (256, 384, 64), (200, 256, 96), (128, 132, 32), (132, 644, 1024),
-              (384, 128, 4096), (252, 388, 160)]
+              (384, 128, 4096), (252, 388, 160), (128, 128, 36), (260, 132, 1000), (256, 256, 60)]
 
 
 @pytest.mark.parametrize("orders", ORDERS3, ids=lambda o: "".join("RC"[x] for x in o))
@@ -290,7 +290,8 @@ def test_f32_dma_random(orders, shape):
     assert g.gemm_last_kernel().startswith("f32_dma")
 
 
-DMA256_SHAPES = [(256, 256, 32), (512, 768, 96), (300, 516, 64), (256, 1028, 224), (772, 260, 32)]
+DMA256_SHAPES = [(256, 256, 32), (512, 768, 96), (300, 516, 64), (256, 1028, 224), (772, 260, 32),
+                 (256, 256, 44), (516, 260, 1000)]
 
 
 @pytest.mark.parametrize("orders", ORDERS3, ids=lambda o: "".join("RC"[x] for x in o))
@@ -338,7 +339,7 @@ def test_f32_dma_closed_forms():
     assert np.array_equal(logical_c(pa, run(pa, g.Algo.MFMA_DMA)), B[:, perm])
 
 
-@pytest.mark.parametrize("bad", [dict(K=48), dict(N=100), dict(M=127), dict(pad_a=1), dict(pad_b=2),
+@pytest.mark.parametrize("bad", [dict(K=28), dict(N=100), dict(M=127), dict(pad_a=1), dict(pad_b=2),
                                  dict(order_a=COL_MAJOR, K=16)], ids=lambda d: str(d))
 def test_f32_dma_rejects_unsupported(bad):
     kw = dict(M=256, N=256, K=64, dtype="f32", order_a=ROW_MAJOR, order_b=ROW_MAJOR)

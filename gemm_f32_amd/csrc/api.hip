@@ -216,14 +216,10 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
     } else {
         p = Problem{(int)N, (int)M, (int)K, B, ldb, 1 - (int)ob, A, lda, 1 - (int)oa, C, ldc};
     }
-    const unsigned vw = f32 ? 4 : 8;   // elements per 16-byte load
     Launch l{};
     l.stream = stream;
-    // 16-byte loads need only element alignment (load16); the direct global->LDS copies
-    // need 16-byte aligned rows
+    // 16-byte loads and global->LDS copies need only element alignment on gfx950
     l.vec_a = l.vec_b = true;
-    l.al_a = (p.lda % vw == 0) && aligned(p.A, 16);
-    l.al_b = (p.ldb % vw == 0) && aligned(p.B, 16);
     l.vec_c = (p.ldc % 4 == 0) && aligned(p.C, 16);
 
     hipError_t err = hipSuccess;

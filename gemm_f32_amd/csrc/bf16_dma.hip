@@ -23,8 +23,8 @@
 //  * Tile order from the XCD-aware, group-M scheduler in common.hpp.
 //
 // Requirements (checked by the host): row-major A and column-major B after the
-// column-major-C swap, 16-byte aligned with leading dimensions that are multiples of 8,
-// K a multiple of BK, M and N multiples of the block tile (the host runs the whole-tile
+// column-major-C swap (element alignment suffices: gfx950's global->LDS copies accept
+// unaligned sources), K a multiple of BK, M and N multiples of the block tile (the host runs the whole-tile
 // part of a ragged problem here and the edge strips with bf16_mfma.hip).
 #include "common.hpp"
 #include "launch.hpp"
@@ -209,7 +209,7 @@ hipError_t launch_cfg(const Problem& p, const Launch& l) {
 }  // namespace
 
 bool bf16_dma_applies(const Problem& p, const Launch& l, int bm, int bn) {
-    return p.oa == kRow && p.ob == kCol && l.al_a && l.al_b && p.K >= 64 && p.K % 64 == 0 &&
+    return p.oa == kRow && p.ob == kCol && l.vec_a && l.vec_b && p.K >= 64 && p.K % 64 == 0 &&
            p.M >= bm && p.N >= bn;
 }
 

@@ -39,7 +39,7 @@
 //    products only feed outputs that are never stored).  An operand contiguous along
 //    M or N is fetched in 16-byte chunks along that dimension and scattered into the
 //    k-contiguous LDS layout.  16-byte loads need element alignment only (gfx950 serves
-//    unaligned vector loads); the direct copies need 16-byte aligned rows.  The K tail and
+//    unaligned vector loads and global->LDS copies).  The K tail and
 //    edge tiles of an M/N-contiguous operand take an element-wise path with bounds checks
 //    and zero fill ("A06", "Pitfall 1 - The boundary guard that fails silently").
 //  * Tile order from the XCD-aware, group-M scheduler in common.hpp.
@@ -151,7 +151,7 @@ __device__ __forceinline__ void store_rc(unsigned char* s, int q, uint4 v) {
 
 template <int BM, int BN, int BK, int S, bool A_KC, bool B_KC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
-void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, int vec_b, int al_ab) {
+void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, int vec_b, int direct) {
     using T = Tile<BM, BN, BK, S>;
     constexpr int CH = T::CH;
     // the direct path issues one tile's copies in the first SUB * FM * FN instruction slots
@@ -291,7 +291,7 @@ void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, in
     auto no_copy = [](int) {};
 
     int kt = 0;
-    if (A_KC && B_KC && al_ab && interior && nfull > 0) {
+    if (A_KC && B_KC && direct && interior && nfull > 0) {
         // ---- direct path: full k-tiles copied global -> LDS without registers, S stages ----
         // Copy j of a wavefront fills tile rows r0 + RPI j .. +RPI-1 (r0 = the wavefront's
         // first row, a multiple of 16); lane l fetches the chunk that belongs at LDS
@@ -395,7 +395,7 @@ hipError_t launch_tile(const Problem& p, const Launch& l) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const dim3 grid((unsigned)tiles_m * tiles_n), block(256);
     const bool akc = p.oa == kRow, bkc = p.ob == kCol;
-    const int va = l.vec_a, vb = l.vec_b, g = l.group_m, al = l.al_a && l.al_b;
+    const int va = l.vec_a, vb = l.vec_b, g = l.group_m, al = l.vec_a && l.vec_b;   // direct copies allowed
     if (akc && bkc)
         hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, true, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
     else if (akc)

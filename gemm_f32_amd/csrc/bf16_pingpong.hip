@@ -33,7 +33,7 @@
 // phase 2(k+S)-2, with the copies of the S-2 later tiles still allowed in flight.
 //
 // Requirements (checked by the host): row-major A and column-major B (both k-contiguous),
-// 16-byte aligned pointers and leading dimensions, M and N multiples of 256, K a multiple
+// M and N multiples of 256, K a multiple
 // of 32.  Other problems use bf16_mfma.hip.
 #include "common.hpp"
 #include "launch.hpp"
@@ -181,7 +181,7 @@ void k_bf16_pingpong(Problem p, int tiles_m, int tiles_n, int group_m) {
 }  // namespace
 
 bool bf16_pingpong_applies(const Problem& p, const Launch& l) {
-    return p.oa == kRow && p.ob == kCol && l.al_a && l.al_b && p.M % BM == 0 &&
+    return p.oa == kRow && p.ob == kCol && l.vec_a && l.vec_b && p.M % BM == 0 &&
            p.N % BN == 0 && p.K % BK == 0 && p.K >= BK;
 }
 

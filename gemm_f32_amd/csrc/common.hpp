@@ -67,14 +67,13 @@ struct Launch {
     hipStream_t stream;
     int group_m;        // tile-scheduler band height (>= 1)
     bool vec_a, vec_b;  // 16-byte loads of the operand are allowed (load16 / load16f)
-    bool al_a, al_b;    // operand pointer and leading dimension are 16-byte aligned: needed
-                        // by the direct global->LDS copies
     bool vec_c;         // C pointer and ldc allow 16-byte stores
 };
 
 // 16-byte global loads from addresses aligned to the element only.  gfx950 serves unaligned
-// vector loads from global memory (the parity tests with padded and odd leading dimensions
-// cover it), so operands whose rows are not 16-byte aligned still move 16 bytes per lane.
+// vector loads from global memory, and its 16-byte global->LDS copies too (the parity tests
+// with padded and odd leading dimensions cover both), so operands whose rows are not
+// 16-byte aligned still move 16 bytes per lane.
 typedef unsigned int u32x4_ua __attribute__((ext_vector_type(4), aligned(2)));
 typedef float f32x4_ua __attribute__((ext_vector_type(4), aligned(4)));
 __device__ __forceinline__ uint4 load16(const void* p) {

@@ -32,8 +32,8 @@
 //    k-tile kt, one barrier per k-tile.
 //  * Tile order from the XCD-aware, group-M scheduler in common.hpp.
 //
-// Requirements (checked by the host): 16-byte aligned A and B with leading dimensions that
-// are multiples of 4 floats, K >= BK, M and N multiples of the block tile.  A K tail takes
+// Requirements (checked by the host): K >= BK, M and N multiples of the block tile.  Rows
+// need element alignment only: gfx950's global->LDS copies accept unaligned sources.  A K tail takes
 // one more k-tile loaded with bounds checks.  The host runs the whole-tile part of a ragged
 // problem here and the edge strips with f32_mfma.hip.
 #include "common.hpp"
@@ -345,7 +345,7 @@ hipError_t launch_cfg(const Problem& p, const Launch& l) {
 
 bool f32_dma_applies(const Problem& p, const Launch& l, int bm, int bn) {
     // the whole-tile part must be non-empty; the host sends partial tiles elsewhere
-    return l.al_a && l.al_b && p.K >= BK && p.M >= bm && p.N >= bn;
+    return l.vec_a && l.vec_b && p.K >= BK && p.M >= bm && p.N >= bn;
 }
 
 // Configurations: 256 x 256 with 8 wavefronts of 64 x 128 (2 per SIMD, 128 KB of LDS),

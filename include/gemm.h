@@ -22,8 +22,7 @@
  *
  * Ownership.  All matrix pointers are device pointers owned by the caller; A and B are
  * only read, C is only written, and C must not overlap A or B.  Pointers need only their
- * element's natural alignment (4 bytes for float, 2 for bf16); 16-byte aligned pointers
- * and leading dimensions let the library use its direct global->LDS kernels.  The library
+ * element's natural alignment (4 bytes for float, 2 for bf16); no kernel needs more.  The library
  * allocates no device memory and keeps no state beyond a per-device property cache.
  *
  * Streams and errors.  Work is enqueued on `stream` (0 = the null stream) of the
@@ -77,9 +76,8 @@ typedef enum {
  *                      M, N >= 256); 256x128 is BF16 only;
  *   MFMA_PINGPONG      BF16 only: the 256 x 256 kernel with eight wavefronts in two groups
  *                      that alternate matrix-instruction and memory phases; needs row-major
- *                      A and column-major B (C may have either order), 16-byte aligned
- *                      pointers and leading dimensions, M and N multiples of 256 and K a
- *                      multiple of 32, else GEMM_ERR_INVALID_VALUE.
+ *                      A and column-major B (C may have either order), M and N multiples
+ *                      of 256 and K a multiple of 32, else GEMM_ERR_INVALID_VALUE.
  *   SKINNY             the small-problem kernel ("How a Matrix Multiply Runs on a GPU",
  *                      "Shapes that run slowly, and why": few rows make the product bound
  *                      by reading B; few tiles leave the chip idle): 64 x 16 blocks of C per
@@ -91,19 +89,17 @@ typedef enum {
  *   MFMA_DMA           the direct-copy kernels: operands copied global -> LDS as laid out in
  *                      memory, no register staging ("GEMM Optimization", V3 staging), tile
  *                      picked from the shape.  FP32: v_mfma_f32_16x16x4_f32, 256 x 256 tiles
- *                      (eight wavefronts) or 128 x 128 (four); needs 16-byte aligned A and B
- *                      with leading dimensions that are multiples of 4, K >= 32 and
+ *                      (eight wavefronts) or 128 x 128 (four); needs K >= 32 and
  *                      M, N >= 128.  BF16: v_mfma_f32_32x32x16_bf16, 256 x 256 or
  *                      256 x 128 tiles of four wavefronts; needs row-major A and column-major
- *                      B, 16-byte aligned with leading dimensions that are multiples of 8, K
- *                      a multiple of 64, M >= 256 and N >= 128.  Conditions apply after the
+ *                      B, K a multiple of 64, M >= 256 and N >= 128.  Conditions apply after the
  *                      column-major-C swap; otherwise GEMM_ERR_INVALID_VALUE.  Partial tiles
  *                      along the bottom and right edges run on the register-staged kernels
  *                      in the same call.  AUTO uses the FP32 one whenever it applies and
  *                      the cost model picks its tile sizes; for BF16 AUTO keeps the MFMA
  *                      kernel above (measured as fast or faster on the BF16 workloads).
- * The FP32 entry point accepts every algorithm but MFMA_256x128 and MFMA_PINGPONG; the BF16 entry point only AUTO, the MFMA ones and SKINNY (others give
- * GEMM_ERR_INVALID_VALUE).
+ * The FP32 entry point accepts every algorithm but MFMA_256x128 and MFMA_PINGPONG; the
+ * BF16 entry point only AUTO, the MFMA ones and SKINNY (others give GEMM_ERR_INVALID_VALUE).
  */
 typedef enum {
     GEMM_ALGO_AUTO = 0,

@@ -339,8 +339,8 @@ def test_f32_dma_closed_forms():
     assert np.array_equal(logical_c(pa, run(pa, g.Algo.MFMA_DMA)), B[:, perm])
 
 
-@pytest.mark.parametrize("bad", [dict(K=28), dict(N=100), dict(M=127), dict(pad_a=1), dict(pad_b=2),
-                                 dict(order_a=COL_MAJOR, K=16)], ids=lambda d: str(d))
+@pytest.mark.parametrize("bad", [dict(K=28), dict(N=100), dict(M=127), dict(order_a=COL_MAJOR, K=16)],
+                         ids=lambda d: str(d))
 def test_f32_dma_rejects_unsupported(bad):
     kw = dict(M=256, N=256, K=64, dtype="f32", order_a=ROW_MAJOR, order_b=ROW_MAJOR)
     kw.update(bad)
@@ -386,8 +386,8 @@ def test_bf16_dma_closed_forms():
     assert np.array_equal(logical_c(pa, run(pa, g.Algo.MFMA_DMA)), B[:, perm])
 
 
-@pytest.mark.parametrize("bad", [dict(K=96), dict(order_b=ROW_MAJOR), dict(pad_a=1), dict(M=200),
-                                 dict(N=64), dict(order_a=COL_MAJOR)], ids=lambda d: str(d))
+@pytest.mark.parametrize("bad", [dict(K=96), dict(order_b=ROW_MAJOR), dict(M=200), dict(N=64),
+                                 dict(order_a=COL_MAJOR)], ids=lambda d: str(d))
 def test_bf16_dma_rejects_unsupported(bad):
     kw = dict(M=256, N=256, K=128, dtype="bf16", order_a=ROW_MAJOR, order_b=COL_MAJOR)
     kw.update(bad)
@@ -395,3 +395,25 @@ def test_bf16_dma_rejects_unsupported(bad):
     with pytest.raises(g.GemmError) as e:
         run(p, g.Algo.MFMA_DMA)
     assert e.value.status == g.Status.ERR_INVALID_VALUE
+
+
+# --- direct copies from rows that are not 16-byte aligned (element alignment only) --------
+@pytest.mark.parametrize("orders", ORDERS3, ids=lambda o: "".join("RC"[x] for x in o))
+@pytest.mark.parametrize("pad", [1, 2, 3])
+def test_f32_dma_unaligned_rows(orders, pad):
+    oa, ob, oc = orders
+    p = gi.make_problem(260, 388, 100, "f32", oa, ob, oc, wid=56, pad_a=pad, pad_b=pad, pad_c=pad)
+    check(p, g.Algo.MFMA_DMA)
+    assert g.gemm_last_kernel().startswith("f32_dma")
+    p = gi.make_problem(512, 256, 64, "f32", oa, ob, oc, wid=57, pad_a=pad, pad_b=pad)
+    check(p, g.Algo.MFMA_256x256)
+
+
+@pytest.mark.parametrize("oc", [ROW_MAJOR, COL_MAJOR], ids=["RCR", "RCC"])
+@pytest.mark.parametrize("pad", [1, 3, 7])
+def test_bf16_direct_unaligned_rows(oc, pad):
+    p = gi.make_problem(512, 384, 192, "bf16", ROW_MAJOR, COL_MAJOR, oc, wid=58, pad_a=pad, pad_b=pad, pad_c=pad)
+    check(p, g.Algo.MFMA_DMA)
+    assert g.gemm_last_kernel().startswith("bf16_dma")
+    check(p, g.Algo.MFMA_256x256)      # bf16_mfma.hip's direct path
+    assert g.gemm_last_kernel() == "bf16_mfma256x256"

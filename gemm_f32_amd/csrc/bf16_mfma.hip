@@ -330,15 +330,16 @@ void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, in
             if (st < nfull)
                 for (int j = 0; j < DMA; ++j) issue_one(j, st * BK, st);
         for (; kt < nfull; ++kt) {
-            // tile kt has landed once at most the copies of tiles kt+1 .. kt+S-2 are pending
-            if (kt + S - 2 < nfull) {
-                if (S == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                else if (S == 3) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(DMA) : "memory");
-                else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * DMA) : "memory");
-            } else {
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            }
-            __syncthreads();   // tile kt visible to all; stage (kt-1) % S free for reuse
+            // Tile kt has landed once at most the copies of tiles kt+1 .. kt+S-2 are pending,
+            // and stage (kt-1) % S is free once this wavefront's reads of it have returned.
+            // Then a plain barrier: __syncthreads() would also wait for the later tiles'
+            // copies (the compiler's workgroup fence covers the global->LDS copies), which
+            // would cut the pipeline back to two stages.
+            static_assert((S - 2) * DMA < 64, "vmcnt range");
+            if (kt + S - 2 < nfull) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"((S - 2) * DMA) : "memory");
+            else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();   // tile kt visible to all; stage (kt-1) % S free
+            asm volatile("" ::: "memory");
             const int kn = kt + S - 1;
             const bool copies = kn < nfull;          // wavefront-uniform
             const int k0n = kn * BK, stn = kn % S;

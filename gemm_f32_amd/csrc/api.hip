@@ -312,9 +312,10 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
                 pick_tile(kBf16Tiles, p.M, p.N, dev.cus, bm, bn);
                 break;
         }
-        // AUTO keeps the register-staged/direct kernel of bf16_mfma.hip: the direct-copy
-        // kernel measured no faster at 4096^3 and slower on the 2048-row shapes
-        const bool use_dma = algo == GEMM_ALGO_MFMA_DMA;
+        // AUTO runs the whole 256-row tiles on the direct-copy kernel where it applies (the
+        // edge strips on bf16_mfma.hip); an explicitly chosen tile runs on bf16_mfma.hip
+        const bool use_dma = algo == GEMM_ALGO_MFMA_DMA ||
+                             (algo == GEMM_ALGO_AUTO && bm == 256 && bf16_dma_applies(p, l, bm, bn));
         if (use_dma) {
             err = launch_bf16_dma_split(p, l, bm, bn, dev.cus);
             name = bn == 256 ? "bf16_dma256x256" : "bf16_dma256x128";

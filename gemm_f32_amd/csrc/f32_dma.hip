@@ -28,8 +28,8 @@
 //        consecutive columns of C at once.
 //  * Copies: global_load_lds_dwordx4, 1 KB per instruction (16 bytes per lane at LDS
 //    position 16 l); a lane fetches the global chunk that belongs at its LDS position.
-//    S stages, the copies of k-tile kt + S - 1 issued among the matrix instructions of
-//    k-tile kt, one barrier per k-tile.
+//    Two stages; the copies of k-tile kt + 2 are spread over the second k-group of tile kt
+//    and the first of tile kt + 1, one barrier per k-tile (see the main loop).
 //  * Tile order from the XCD-aware, group-M scheduler in common.hpp.
 //
 // Requirements (checked by the host): K >= BK, M and N multiples of the block tile.  Rows
@@ -201,55 +201,70 @@ void k_f32_dma(Problem p, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // One k-tile = 2 k-groups.  The fragments of group 1 are read while group 0 is
-    // multiplied; copy(n) is called before the n-th matrix instruction of the k-tile.
-    auto compute = [&](int st_idx, auto copy) {
-        const unsigned char* st = smem + st_idx * C::STAGE;
-        Frags f[2];
-        read_group(st, 0, f[0]);
+    // One k-group: 4 steps x FM x FN matrix instructions on the fragments in f; `slot(n)` is
+    // called before the n-th instruction so that the caller can place copies and the reads
+    // of the next fragments among them.  Source order is issue order (sched_barrier).
+    auto group = [&](const Frags& f, auto slot) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < FN; ++j) {
-                        const int n = t * C::MFMA_PER_GROUP + (e * FM + i) * FN + j;
-                        copy(n);
-                        if (t == 0 && e == 0 && i == 0 && j == 0) read_group(st, 1, f[1]);
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_val(f[t], i, e), b_val(f[t], j, e),
-                                                                         acc[i][j], 0, 0, 0);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-        }
+                for (int j = 0; j < FN; ++j) {
+                    slot((e * FM + i) * FN + j);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_val(f, i, e), b_val(f, j, e), acc[i][j], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
     };
 
-    // ---- S-stage pipeline: tiles 0 .. S-2 in flight before the loop (clamped like the
-    // copies in the loop when K has fewer k-tiles) ----
+    // ---- software pipeline over k-tiles, two LDS stages.  Iteration kt multiplies tile kt
+    // (stage kt % 2) as two k-groups; group 1's fragments are read under group 0's matrix
+    // instructions.  The barrier before group 1 publishes tile kt+1 (every wavefront has
+    // waited for its own copies of it) and frees stage kt % 2 (every wavefront's reads of
+    // it have completed): during group 1 each wavefront reads group 0 of tile kt+1 and
+    // starts the copies of tile kt+2 into the freed stage; they continue through group 0
+    // of iteration kt+1 and have until its barrier to land.  So neither the barrier nor the
+    // first LDS reads of a tile leave the matrix pipe without work.  Past the end of K the
+    // copies repeat the last tile into a stage nobody reads and the fragments read for a
+    // tile nk are never used: the loop body has no branch (a branch among the matrix
+    // instructions costs more than the extra copies of one k-tile).
+    static_assert(S == 2, "two-stage pipeline");
+    constexpr int G = C::MFMA_PER_GROUP, W = 2 * G;    // copy window: two k-groups
+    constexpr int SP = W / C::DMA;                      // one copy every SP instructions
+    static_assert(W % C::DMA == 0, "copies evenly spread over the window");
+    // the copy that falls on slot `n` of the window, if any
+    auto copies_at = [&](int n, int kt, int st) {
+        if (n % SP == 0) issue_one(n / SP, kt, st);
+    };
+    const int last = nk - 1;
+    Frags f[2];
 #pragma unroll
-    for (int st = 0; st + 1 < S; ++st)
+    for (int j = 0; j < C::DMA; ++j) issue_one(j, 0, 0);
 #pragma unroll
-        for (int j = 0; j < C::DMA; ++j) issue_one(j, min(st, nk - 1), st);
-    constexpr int SLOTS = 2 * C::MFMA_PER_GROUP;
-    constexpr int SPREAD = SLOTS / C::DMA >= 4 ? 4 : SLOTS / C::DMA;
-    // Every k-tile issues the copies of tile min(kt + S - 1, nk - 1) into stage
-    // (kt + S - 1) % S, which the barrier has just freed: past the end of K the last tile is
-    // copied again into a stage nobody reads, so that the loop body has no branch (a branch
-    // among the matrix instructions costs more than the extra copy of one k-tile).
+    for (int n = 0; n < G; ++n) copies_at(n, min(1, last), 1);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    read_group(smem, 0, f[0]);
     for (int kt = 0; kt < nk; ++kt) {
-        // tile kt has landed once at most the copies of tiles kt+1 .. kt+S-2 are pending
-        if (S == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        else if (S == 3) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(C::DMA) : "memory");
-        else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * C::DMA) : "memory");
-        __syncthreads();   // tile kt visible to all; stage (kt-1) % S free for reuse
-        const int kn = min(kt + S - 1, nk - 1), stn = (kt + S - 1) % S;
-        compute(kt % S, [&](int n) {
-            if (n % SPREAD == 0 && n / SPREAD < C::DMA) issue_one(n / SPREAD, kn, stn);
+        const int st = kt & 1;
+        const int k1 = min(kt + 1, last), k2 = min(kt + 2, last);
+        group(f[0], [&](int n) {
+            copies_at(G + n, k1, st ^ 1);
+            if (n == 0) read_group(smem + st * C::STAGE, 1, f[1]);
+        });
+        // own copies of tile kt+1 landed, own reads of stage st complete; a plain barrier
+        // (__syncthreads() would also wait for the copies still in flight)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        group(f[1], [&](int n) {
+            copies_at(n, k2, st);
+            if (n == 0) read_group(smem + (st ^ 1) * C::STAGE, 0, f[0]);
         });
     }
-    // the surplus copies must land before the workgroup's LDS is released
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // the surplus copies must land before the workgroup's LDS is reused or released
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 
     // ---- K tail (K not a multiple of BK): one more k-tile, staged through registers with
     // bounds checks and zero fill into the same LDS positions the copies would fill ----
@@ -287,7 +302,11 @@ void k_f32_dma(Problem p, int tiles_m, int tiles_n, int group_m) {
             *reinterpret_cast<float4*>(dst) = v;
         }
         __syncthreads();
-        compute(0, [](int) {});
+        read_group(smem, 0, f[0]);
+        group(f[0], [&](int n) {
+            if (n == 0) read_group(smem, 1, f[1]);
+        });
+        group(f[1], [](int) {});
     }
 
     // ---- epilogue: block (i, j), lane l, register v: block row 4 (l / 16) + v, block

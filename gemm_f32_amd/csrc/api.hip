@@ -88,7 +88,7 @@ struct TileOpt { int bm, bn; double eff; int per_cu; };
 constexpr TileOpt kBf16Tiles[] = {{256, 256, 1.0, 1}, {256, 128, 0.78, 1}, {128, 128, 0.82, 2},
                                   {64, 64, 0.36, 4}};
 // BF16 direct-copy kernel (256 x 256, 256 x 128)
-constexpr TileOpt kBf16DmaTiles[] = {{256, 256, 1.0, 1}, {256, 128, 0.8, 1}};
+constexpr TileOpt kBf16DmaTiles[] = {{256, 256, 1.0, 1}, {256, 128, 0.86, 1}};
 // FP32: the register-staged kernel (128 x 128, 64 x 64) and, where its requirements hold,
 // the direct-copy kernel (256 x 256, 128 x 128) with the register-staged 64 x 64
 constexpr TileOpt kF32Tiles[] = {{128, 128, 1.0, 4}, {64, 64, 0.92, 4}};
@@ -309,13 +309,18 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
                 if (bm != 256) { bm = 256; bn = 128; }
                 break;
             default:
-                pick_tile(kBf16Tiles, p.M, p.N, dev.cus, bm, bn);
+                // the direct-copy kernel where it applies (its whole tiles; the edge strips run
+                // on bf16_mfma.hip), else the register-staged / direct kernel of bf16_mfma.hip
+                if (dma_any) {
+                    bm = 256; bn = 128;
+                    if (bf16_dma_applies(p, l, 256, 256)) pick_tile(kBf16DmaTiles, p.M, p.N, dev.cus, bm, bn);
+                } else {
+                    pick_tile(kBf16Tiles, p.M, p.N, dev.cus, bm, bn);
+                }
                 break;
         }
-        // AUTO runs the whole 256-row tiles on the direct-copy kernel where it applies (the
-        // edge strips on bf16_mfma.hip); an explicitly chosen tile runs on bf16_mfma.hip
-        const bool use_dma = algo == GEMM_ALGO_MFMA_DMA ||
-                             (algo == GEMM_ALGO_AUTO && bm == 256 && bf16_dma_applies(p, l, bm, bn));
+        // an explicitly chosen tile runs on bf16_mfma.hip
+        const bool use_dma = algo == GEMM_ALGO_MFMA_DMA || (algo == GEMM_ALGO_AUTO && dma_any);
         if (use_dma) {
             err = launch_bf16_dma_split(p, l, bm, bn, dev.cus);
             name = bn == 256 ? "bf16_dma256x256" : "bf16_dma256x128";

@@ -87,8 +87,11 @@ bool prefer_small(const Problem& p, int cus) {
 struct TileOpt { int bm, bn; double eff; int per_cu; };
 constexpr TileOpt kBf16Tiles[] = {{256, 256, 1.0, 1}, {256, 128, 0.78, 1}, {128, 128, 0.82, 2},
                                   {64, 64, 0.36, 4}};
-// BF16 direct-copy kernel (256 x 256, 256 x 128)
+// BF16 direct-copy kernel (256 x 256, 256 x 128) alone, and together with the
+// register-staged kernel's smaller tiles (bm == 256 marks the direct-copy kernel)
 constexpr TileOpt kBf16DmaTiles[] = {{256, 256, 1.0, 1}, {256, 128, 0.86, 1}};
+constexpr TileOpt kBf16AnyTiles[] = {{256, 256, 1.0, 1}, {256, 128, 0.86, 1}, {128, 128, 0.80, 2},
+                                     {64, 64, 0.35, 4}};
 // FP32: the register-staged kernel (128 x 128, 64 x 64) and, where its requirements hold,
 // the direct-copy kernel (256 x 256, 128 x 128) with the register-staged 64 x 64
 constexpr TileOpt kF32Tiles[] = {{128, 128, 1.0, 4}, {64, 64, 0.92, 4}};
@@ -103,44 +106,6 @@ void pick_tile(const TileOpt (&opts)[NOPT], int64_t M, int64_t N, int cus, int& 
         const double cost = (full * o.per_cu + std::ceil(rest / c)) * o.bm * o.bn / o.eff;
         if (cost < best) { best = cost; bm = o.bm; bn = o.bn; }
     }
-}
-
-// BF16 direct-copy kernel on the whole bm x bn tiles of C, the register-staged kernel on
-// the partial strips (same stream, disjoint parts of C).
-hipError_t launch_bf16_dma_split(const Problem& p, const Launch& l, int bm, int bn, int cus) {
-    const int mf = p.M / bm * bm, nf = p.N / bn * bn;
-    Problem core = p;
-    core.M = mf;
-    core.N = nf;
-    Launch lc = l;
-    lc.group_m = pick_group_m(mf / bm, nf / bn);
-    hipError_t err = launch_bf16_dma(core, lc, bm, bn);
-    auto strip = [&](Problem s) {
-        if (err != hipSuccess) return;
-        int sm = 128, sn = 128;
-        pick_tile(kBf16Tiles, s.M, s.N, cus, sm, sn);
-        Launch ls = l;
-        ls.group_m = pick_group_m((s.M + sm - 1) / sm, (s.N + sn - 1) / sn);
-        err = launch_bf16_mfma(s, ls, sm, sn);
-    };
-    const uint16_t* A = static_cast<const uint16_t*>(p.A);
-    const uint16_t* B = static_cast<const uint16_t*>(p.B);
-    if (mf < p.M) {          // rows mf .. M-1, all columns (A is row-major here)
-        Problem s = p;
-        s.M = p.M - mf;
-        s.A = A + (int64_t)mf * p.lda;
-        s.C = p.C + (int64_t)mf * p.ldc;
-        strip(s);
-    }
-    if (nf < p.N) {          // rows 0 .. mf-1, columns nf .. N-1 (B is column-major here)
-        Problem s = p;
-        s.M = mf;
-        s.N = p.N - nf;
-        s.B = B + (int64_t)nf * p.ldb;
-        s.C = p.C + nf;
-        strip(s);
-    }
-    return err;
 }
 
 // FP32 direct-copy kernel on the whole bt x bt tiles of C, the register-staged kernel on
@@ -296,36 +261,31 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
         name = "bf16_pingpong256x256";
     } else {
         int bm = 256, bn = 256;
-        const bool dma_any = bf16_dma_applies(p, l, 256, 128);
+        const bool dma = bf16_dma_applies(p, l, bm, bn);
         switch (algo) {
             case GEMM_ALGO_MFMA_256x256: bm = 256; bn = 256; break;
             case GEMM_ALGO_MFMA_256x128: bm = 256; bn = 128; break;
             case GEMM_ALGO_MFMA_128x128: bm = 128; bn = 128; break;
             case GEMM_ALGO_MFMA_64x64: bm = 64; bn = 64; break;
             case GEMM_ALGO_MFMA_DMA:
-                if (!dma_any) return GEMM_ERR_INVALID_VALUE;
-                bm = 256; bn = 128;
-                if (bf16_dma_applies(p, l, 256, 256)) pick_tile(kBf16DmaTiles, p.M, p.N, dev.cus, bm, bn);
-                if (bm != 256) { bm = 256; bn = 128; }
+                if (!dma) return GEMM_ERR_INVALID_VALUE;
+                pick_tile(kBf16DmaTiles, p.M, p.N, dev.cus, bm, bn);
                 break;
             default:
-                // the direct-copy kernel where it applies (its whole tiles; the edge strips run
-                // on bf16_mfma.hip), else the register-staged / direct kernel of bf16_mfma.hip
-                if (dma_any) {
-                    bm = 256; bn = 128;
-                    if (bf16_dma_applies(p, l, 256, 256)) pick_tile(kBf16DmaTiles, p.M, p.N, dev.cus, bm, bn);
-                } else {
-                    pick_tile(kBf16Tiles, p.M, p.N, dev.cus, bm, bn);
-                }
+                // the direct-copy kernel's tiles where it applies, else the register-staged
+                // / direct kernel of bf16_mfma.hip
+                if (dma) pick_tile(kBf16AnyTiles, p.M, p.N, dev.cus, bm, bn);
+                else pick_tile(kBf16Tiles, p.M, p.N, dev.cus, bm, bn);
                 break;
         }
         // an explicitly chosen tile runs on bf16_mfma.hip
-        const bool use_dma = algo == GEMM_ALGO_MFMA_DMA || (algo == GEMM_ALGO_AUTO && dma_any);
+        const bool use_dma = algo == GEMM_ALGO_MFMA_DMA || ((algo == GEMM_ALGO_AUTO || algo == GEMM_ALGO_MFMA) &&
+                                                            dma && bm == 256);
+        l.group_m = pick_group_m((p.M + bm - 1) / bm, (p.N + bn - 1) / bn);
         if (use_dma) {
-            err = launch_bf16_dma_split(p, l, bm, bn, dev.cus);
+            err = launch_bf16_dma(p, l, bm, bn);
             name = bn == 256 ? "bf16_dma256x256" : "bf16_dma256x128";
         } else {
-            l.group_m = pick_group_m((p.M + bm - 1) / bm, (p.N + bn - 1) / bn);
             err = launch_bf16_mfma(p, l, bm, bn);
             static const char* names[] = {"bf16_mfma256x256", "bf16_mfma256x128", "bf16_mfma128x128",
                                           "bf16_mfma64x64"};

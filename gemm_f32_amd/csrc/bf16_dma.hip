@@ -19,21 +19,26 @@
 //    what matters, not its order).
 //  * Accumulator layout of a 32 x 32 fragment: lane l, register r holds row
 //    8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
-//  * Copies: 1 KB per instruction, a lane fetching the chunk that belongs at its LDS
-//    position.  With 16-byte aligned operands they are buffer loads (a per-lane 32-bit
-//    offset, the k-tile and the row block as one scalar offset); otherwise global loads
-//    with 64-bit addresses (gfx950 serves those from element-aligned rows too).
+//  * Copies: buffer loads of 1 KB per instruction straight into LDS, a lane fetching the
+//    chunk that belongs at its LDS position; the per-lane offset is fixed, the k-tile and
+//    the copy's row block are a scalar offset.  Each wavefront's buffer covers exactly the
+//    rows of its copy block that exist, so rows past M (N) read as zero: edge tiles need no
+//    separate code in the k-loop.  (Buffer loads, like global ones, accept the 2-byte
+//    aligned rows of odd leading dimensions on gfx950.)
 //  * Two LDS stages ("GEMM Optimization", V3), software-pipelined across k-tiles (see the
 //    main loop); one barrier per k-tile.
+//  * K tail: a last k-tile staged through registers with bounds checks and zero fill into
+//    the same LDS positions ("A06 - Tiled Matrix Multiply (GEMM)", "Pitfall 1 - The
+//    boundary guard that fails silently": a ragged K needs the zero fill).
 //  * Epilogue: each wavefront passes its accumulators through LDS one 32-row band at a time
 //    and stores whole rows with 16-byte stores (straight from the accumulators, C rows are
 //    written 4 bytes per lane, 128 bytes per 32 lanes, which takes four times as many
-//    store instructions for the same 64 MB at 4096^2).
+//    store instructions for the same 64 MB at 4096^2); stores past M or N are skipped.
 //  * Tile order from the XCD-aware, group-M scheduler in common.hpp.
 //
 // Requirements (checked by the host): row-major A and column-major B after the
-// column-major-C swap, K a multiple of BK, M and N multiples of the block tile (the host
-// runs the whole-tile part of a ragged problem here and the edge strips with bf16_mfma.hip).
+// column-major-C swap (both k-contiguous), K >= 64, and byte offsets of a wavefront's row
+// block below 2^31.  Any M, N.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -85,7 +90,7 @@ struct Cfg {
     static_assert(NW % 4 == 0, "whole wavefronts per SIMD");
 };
 
-template <typename C, bool BUF, bool VEC_C>
+template <typename C, bool VEC_C>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::NW / 4, C::NW / 4)))
 void k_bf16_dma(Problem p, int tiles_m, int tiles_n, int group_m) {
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, FM = C::FM, FN = C::FN, SUB = C::SUB;
@@ -95,18 +100,19 @@ void k_bf16_dma(Problem p, int tiles_m, int tiles_n, int group_m) {
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    const bool interior = m0 + BM <= p.M && n0 + BN <= p.N;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = (wave / C::WGN) * C::WM, wn = (wave % C::WGN) * C::WN;
-    const int nk = p.K / BK;
+    const int nk = p.K / BK;                  // whole k-tiles; a K tail follows the loop
+    const u16* A = static_cast<const u16*>(p.A);
+    const u16* B = static_cast<const u16*>(p.B);
 
     // ---- copy plan: wavefront w fills rows w A_RPW .. +A_RPW-1 of the A tile (and the same
     // for B), RPC rows per copy; lane l fetches row l / 8 of the copy at logical chunk
     // (l % 8) ^ s(row), where s(row) depends on l and on the parity of the copy only
     // (copy blocks start at multiples of 16 rows).
     const int lr = lane / 8;
-    const u16* arow = static_cast<const u16*>(p.A) + (int64_t)(m0 + wave * C::A_RPW) * p.lda;
-    const u16* brow = static_cast<const u16*>(p.B) + (int64_t)(n0 + wave * C::B_RPW) * p.ldb;
     unsigned aoff[2], boff[2];
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
@@ -114,32 +120,31 @@ void k_bf16_dma(Problem p, int tiles_m, int tiles_n, int group_m) {
         aoff[par] = (unsigned)((lr * p.lda + c * 8) * 2);
         boff[par] = (unsigned)((lr * p.ldb + c * 8) * 2);
     }
-    // buffer resources over this wavefront's row blocks (the host checks that the byte
-    // offsets fit in 31 bits)
+    // buffer resources over the rows of this wavefront's copy blocks that exist: the
+    // hardware returns zero for the rest (the host checks that offsets fit in 31 bits)
+    const int arow0 = m0 + wave * C::A_RPW, brow0 = n0 + wave * C::B_RPW;
+    // (wavefront-uniform values; readfirstlane tells the compiler so, which keeps the buffer
+    // resources in scalar registers)
+    const int avalid = __builtin_amdgcn_readfirstlane(max(0, min(C::A_RPW, p.M - arow0)));
+    const int bvalid = __builtin_amdgcn_readfirstlane(max(0, min(C::B_RPW, p.N - brow0)));
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)arow, (short)0, (int)(C::A_RPW * p.lda * 2), kBufWord3);
+        (void*)(avalid > 0 ? A + (int64_t)arow0 * p.lda : A), (short)0, (int)(avalid * p.lda * 2), kBufWord3);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)brow, (short)0, (int)(C::B_RPW * p.ldb * 2), kBufWord3);
+        (void*)(bvalid > 0 ? B + (int64_t)brow0 * p.ldb : B), (short)0, (int)(bvalid * p.ldb * 2), kBufWord3);
     // byte distance between consecutive copies of a wavefront
-    const int64_t astep = (int64_t)C::RPC * p.lda * 2, bstep = (int64_t)C::RPC * p.ldb * 2;
-    // copy j (of DMA) of k-tile kt (source) into stage st
+    const int astep = C::RPC * (int)p.lda * 2, bstep = C::RPC * (int)p.ldb * 2;
+    // copy j (of DMA) of k-tile kt (source) into stage st.  (The LDS pointer is a named
+    // variable: cast inline in the builtin's argument list, the host pass of this compiler
+    // silently drops the kernel's launch stub.)
     auto issue_one = [&](int j, int kt, int st) {
         unsigned char* s = smem + st * C::STAGE;
         if (j < C::A_DMA) {
             lds_void* dst = (lds_void*)(s + (wave * C::A_DMA + j) * 1024);
-            if (BUF)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, aoff[j & 1], j * (int)astep + kt * (BK * 2), 0, 0);
-            else
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(arow) + j * astep +
-                                                 kt * (BK * 2) + aoff[j & 1], dst, 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, aoff[j & 1], j * astep + kt * (BK * 2), 0, 0);
         } else {
             const int jb = j - C::A_DMA;
             lds_void* dst = (lds_void*)(s + C::A_BYTES + (wave * C::B_DMA + jb) * 1024);
-            if (BUF)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, boff[jb & 1], jb * (int)bstep + kt * (BK * 2), 0, 0);
-            else
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(brow) + jb * bstep +
-                                                 kt * (BK * 2) + boff[jb & 1], dst, 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, boff[jb & 1], jb * bstep + kt * (BK * 2), 0, 0);
         }
     };
     // the copies that fall on slot `slot` of the window (copy q sits at slot q W / DMA)
@@ -184,46 +189,111 @@ void k_bf16_dma(Problem p, int tiles_m, int tiles_n, int group_m) {
     // stall the wavefront that issues them, and with it its matrix instructions.  Past the
     // end of K the copies repeat the last tile into a stage nobody reads, and the fragments
     // read for a tile nk are never used, so the loop body has no branch.
-    const int last = nk - 1;
+    if (nk > 0) {                             // uniform
+        const int last = nk - 1;
 #pragma unroll
-    for (int j = 0; j < C::DMA; ++j) issue_one(j, 0, 0);
+        for (int j = 0; j < C::DMA; ++j) issue_one(j, 0, 0);
 #pragma unroll
-    for (int slot = 0; slot < MF; ++slot) copies_at(slot, min(1, last), 1);
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int m = 0; m < C::RD; ++m) read_slot(0, 0, m, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-        const int st = kt & 1;
-        const int k1 = min(kt + 1, last), k2 = min(kt + 2, last);
-#pragma unroll
-        for (int s = 0; s < SUB - 1; ++s) {
-#pragma unroll
-            for (int m = 0; m < MF; ++m) {
-                if (s < C::CSPAN - 1) copies_at(MF + s * MF + m, k1, st ^ 1);
-                read_slot(st, s + 1, m, (s + 1) & 1);
-                mfma(m, s & 1);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        // own copies of tile kt+1 landed, own reads of stage st complete; a plain barrier
-        // (the compiler's workgroup fence would also wait for copies still in flight)
+        for (int slot = 0; slot < MF; ++slot) copies_at(slot, min(1, last), 1);
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
 #pragma unroll
-        for (int m = 0; m < MF; ++m) {
-            copies_at(m, k2, st);
-            read_slot(st ^ 1, 0, m, 0);
-            mfma(m, (SUB - 1) & 1);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int m = 0; m < C::RD; ++m) read_slot(0, 0, m, 0);
+        for (int kt = 0; kt < nk; ++kt) {
+            const int st = kt & 1;
+            const int k1 = min(kt + 1, last), k2 = min(kt + 2, last);
+#pragma unroll
+            for (int s = 0; s < SUB - 1; ++s) {
+#pragma unroll
+                for (int m = 0; m < MF; ++m) {
+                    if (s < C::CSPAN - 1) copies_at(MF + s * MF + m, k1, st ^ 1);
+                    read_slot(st, s + 1, m, (s + 1) & 1);
+                    mfma(m, s & 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            // own copies of tile kt+1 landed, own reads of stage st complete; a plain
+            // barrier (the compiler's workgroup fence would also wait for copies still in
+            // flight)
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int m = 0; m < MF; ++m) {
+                copies_at(m, k2, st);
+                read_slot(st ^ 1, 0, m, 0);
+                mfma(m, (SUB - 1) & 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
+        // the surplus copies land before LDS is reused or released
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     }
-    // the surplus copies land before LDS is reused or released
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 
-    // ---- epilogue ----
+    // ---- K tail: one more k-tile staged through registers with bounds checks and zero fill
+    // into the LDS positions the copies would have filled (stage 0).  Branch-free, so that
+    // all loads are in flight together: every lane loads 16 in-bounds bytes -- its chunk
+    // when the chunk lies inside K, else the last 8 elements of the row -- and keeps what
+    // belongs to its chunk (shifted into place for the chunk that straddles K), zero for the
+    // rest and for rows past M or N.  K >= 64 (host check), so a row holds 8 elements. ----
+    if (p.K % BK != 0) {                      // uniform
+        const int k0 = nk * BK;
+        uint4 v[C::DMA];
+        // the chunk of copy j that this lane stages: tile row, first k, row in range
+        auto chunk = [&](int j, const u16*& src, int& k, bool& keep) {
+            const bool is_a = j < C::A_DMA;
+            const int jj = is_a ? j : j - C::A_DMA;
+            const int tr = wave * (is_a ? C::A_RPW : C::B_RPW) + jj * C::RPC + lr;
+            const int grow = (is_a ? m0 : n0) + tr, rows = is_a ? p.M : p.N;
+            src = (is_a ? A : B) + (int64_t)min(grow, rows - 1) * (is_a ? p.lda : p.ldb);
+            k = k0 + 8 * ((lane % 8) ^ swz(lr + C::RPC * (jj & 1)));
+            keep = grow < rows && k < p.K;
+        };
+#pragma unroll
+        for (int j = 0; j < C::DMA; ++j) {    // all loads first
+            const u16* src; int k; bool keep;
+            chunk(j, src, k, keep);
+            v[j] = load16(src + (k + 8 <= p.K ? k : p.K - 8));
+        }
+#pragma unroll
+        for (int j = 0; j < C::DMA; ++j) {    // then keep, shift or clear, as arithmetic
+            const u16* src; int k; bool keep;
+            chunk(j, src, k, keep);
+            // straddling chunk: its r valid elements are the top r of the last 8 of the row
+            const int r = min(max(p.K - k, 1), 7);
+            const unsigned sh = 16 * (8 - r);                 // bits to drop, 16 .. 112
+            const uint64_t lo = v[j].x | (uint64_t)v[j].y << 32, hi = v[j].z | (uint64_t)v[j].w << 32;
+            const uint64_t slo = sh < 64 ? (lo >> sh) | (hi << (64 - sh)) : hi >> (sh - 64);
+            const uint64_t shi = sh < 64 ? hi >> sh : 0;
+            const uint64_t full = k + 8 <= p.K ? ~0ull : 0ull, kept = keep ? ~0ull : 0ull;
+            const uint64_t olo = ((lo & full) | (slo & ~full)) & kept, ohi = ((hi & full) | (shi & ~full)) & kept;
+            v[j] = make_uint4((unsigned)olo, (unsigned)(olo >> 32), (unsigned)ohi, (unsigned)(ohi >> 32));
+        }
+        __syncthreads();                      // every wavefront is done with the stages
+#pragma unroll
+        for (int j = 0; j < C::DMA; ++j) {
+            const bool is_a = j < C::A_DMA;
+            const int jj = is_a ? j : j - C::A_DMA;
+            unsigned char* dst = smem + (is_a ? (wave * C::A_DMA + jj) * 1024
+                                              : C::A_BYTES + (wave * C::B_DMA + jj) * 1024) + 16 * lane;
+            *reinterpret_cast<uint4*>(dst) = v[j];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < C::RD; ++m) read_slot(0, 0, m, 0);
+#pragma unroll
+        for (int s = 0; s < SUB; ++s) {
+#pragma unroll
+            for (int m = 0; m < MF; ++m) {
+                if (s + 1 < SUB) read_slot(0, s + 1, m, (s + 1) & 1);
+                mfma(m, s & 1);
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+
+    // ---- epilogue: stores past M or N are skipped ----
     if (VEC_C) {
         __builtin_amdgcn_s_barrier();      // every wavefront is done with the stages
         asm volatile("" ::: "memory");
@@ -240,7 +310,15 @@ void k_bf16_dma(Problem p, int tiles_m, int tiles_n, int group_m) {
             for (int q = 0; q < 32 / RPI; ++q) {
                 const int rr = q * RPI + lane / LPR, cc = 4 * (lane % LPR);
                 const f32x4 v = *reinterpret_cast<const f32x4*>(band + rr * C::EP + cc);
-                *reinterpret_cast<f32x4*>(p.C + (int64_t)(m0 + wm + 32 * i + rr) * p.ldc + n0 + wn + cc) = v;
+                const int row = m0 + wm + 32 * i + rr, col = n0 + wn + cc;
+                float* dst = p.C + (int64_t)row * p.ldc + col;
+                if (interior || (row < p.M && col + 3 < p.N)) {
+                    *reinterpret_cast<f32x4*>(dst) = v;
+                } else if (row < p.M) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (col + e < p.N) dst[e] = v[e];
+                }
             }
         }
     } else {
@@ -252,41 +330,30 @@ void k_bf16_dma(Problem p, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                    p.C[(int64_t)row * p.ldc + col] = acc[i][j][r];
+                    if (interior || (row < p.M && col < p.N)) p.C[(int64_t)row * p.ldc + col] = acc[i][j][r];
                 }
             }
     }
 }
 
 template <typename C>
-bool buffer_offsets_fit(const Problem& p) {
-    const int64_t lim = (int64_t)1 << 31;
-    return (int64_t)C::A_RPW * p.lda * 2 < lim && (int64_t)C::B_RPW * p.ldb * 2 < lim;
-}
-
-template <typename C>
 hipError_t launch_cfg(const Problem& p, const Launch& l) {
-    const int tiles_m = p.M / C::BM, tiles_n = p.N / C::BN;
+    const int tiles_m = (p.M + C::BM - 1) / C::BM, tiles_n = (p.N + C::BN - 1) / C::BN;
     const dim3 grid((unsigned)tiles_m * tiles_n), block(C::THREADS);
-    // buffer copies for 16-byte aligned operands whose row blocks are addressable with
-    // 32-bit offsets; global copies otherwise
-    const bool buf = p.lda % 8 == 0 && p.ldb % 8 == 0 && reinterpret_cast<uintptr_t>(p.A) % 16 == 0 &&
-                     reinterpret_cast<uintptr_t>(p.B) % 16 == 0 && buffer_offsets_fit<C>(p);
-    if (buf && l.vec_c)
-        hipLaunchKernelGGL((k_bf16_dma<C, true, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
-    else if (buf)
-        hipLaunchKernelGGL((k_bf16_dma<C, true, false>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
-    else if (l.vec_c)
-        hipLaunchKernelGGL((k_bf16_dma<C, false, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
+    if (l.vec_c)
+        hipLaunchKernelGGL((k_bf16_dma<C, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
     else
-        hipLaunchKernelGGL((k_bf16_dma<C, false, false>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
+        hipLaunchKernelGGL((k_bf16_dma<C, false>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
     return hipGetLastError();
 }
 
 }  // namespace
 
-bool bf16_dma_applies(const Problem& p, const Launch&, int bm, int bn) {
-    return p.oa == kRow && p.ob == kCol && p.K >= 64 && p.K % 64 == 0 && p.M >= bm && p.N >= bn;
+bool bf16_dma_applies(const Problem& p, const Launch&, int, int) {
+    // one bound for both configurations: 64 rows per wavefront copy block at most
+    const int64_t lim = (int64_t)1 << 31;
+    return p.oa == kRow && p.ob == kCol && p.K >= 64 && (int64_t)64 * p.lda * 2 < lim &&
+           (int64_t)64 * p.ldb * 2 < lim;
 }
 
 // Configurations: 256 x 256 with eight wavefronts of 128 x 64 (two per SIMD, 128 KB of

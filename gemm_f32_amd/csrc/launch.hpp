@@ -19,9 +19,8 @@ hipError_t launch_f32_mfma(const Problem& p, const Launch& l, int bm);
 // f32_dma_applies says whether the whole-tile part of a problem may run there.
 bool f32_dma_applies(const Problem& p, const Launch& l, int bm, int bn);
 hipError_t launch_f32_dma(const Problem& p, const Launch& l, int bm, int bn);
-// BF16 direct-copy kernel (bf16_dma.hip): row-major A, column-major B, aligned, K a
-// multiple of 64, whole 256x256 or 256x128 tiles; bf16_dma_applies says whether the
-// whole-tile part of a problem may run there.
+// BF16 direct-copy kernel (bf16_dma.hip): row-major A, column-major B, any M, N, K >= 64,
+// 256x256 or 256x128 tiles; bf16_dma_applies checks the layouts and offset ranges.
 bool bf16_dma_applies(const Problem& p, const Launch& l, int bm, int bn);
 hipError_t launch_bf16_dma(const Problem& p, const Launch& l, int bm, int bn);
 // BF16 matrix-core kernel (bf16_mfma.hip); tile is one of 256x256, 256x128, 128x128, 64x64

@@ -386,8 +386,9 @@ def test_bf16_dma_closed_forms():
     assert np.array_equal(logical_c(pa, run(pa, g.Algo.MFMA_DMA)), B[:, perm])
 
 
-@pytest.mark.parametrize("bad", [dict(K=96), dict(order_b=ROW_MAJOR), dict(M=200), dict(N=64),
-                                 dict(order_a=COL_MAJOR)], ids=lambda d: str(d))
+@pytest.mark.parametrize("bad", [dict(order_b=ROW_MAJOR), dict(order_a=COL_MAJOR),
+                                 dict(order_a=COL_MAJOR, order_b=ROW_MAJOR), dict(K=63)],
+                         ids=lambda d: str(d))
 def test_bf16_dma_rejects_unsupported(bad):
     kw = dict(M=256, N=256, K=128, dtype="bf16", order_a=ROW_MAJOR, order_b=COL_MAJOR)
     kw.update(bad)
@@ -395,6 +396,55 @@ def test_bf16_dma_rejects_unsupported(bad):
     with pytest.raises(g.GemmError) as e:
         run(p, g.Algo.MFMA_DMA)
     assert e.value.status == g.Status.ERR_INVALID_VALUE
+
+
+# --- BF16 direct-copy kernel on ragged shapes: partial edge tiles (rows past M or N read as
+# zero through the buffer range, stores guarded), a K tail staged with bounds checks, K
+# below one k-tile ---------------------------------------------------------------------------
+BDMA_RAGGED = [(1, 1, 64), (255, 129, 71), (257, 385, 65), (300, 200, 1000), (513, 127, 100),
+               (1000, 260, 1023), (260, 1001, 130), (4000, 4000, 100), (33, 300, 127)]
+
+
+@pytest.mark.parametrize("oc", [ROW_MAJOR, COL_MAJOR], ids=["RCR", "RCC"])
+@pytest.mark.parametrize("shape", BDMA_RAGGED, ids=lambda s: "x".join(map(str, s)))
+def test_bf16_dma_ragged(oc, shape):
+    M, N, K = shape
+    p = gi.make_problem(M, N, K, "bf16", ROW_MAJOR, COL_MAJOR, oc, wid=59)
+    check(p, g.Algo.MFMA_DMA, key=("bdma_ragged", oc, shape))
+    assert g.gemm_last_kernel().startswith("bf16_dma")
+
+
+@pytest.mark.parametrize("shape", [(300, 257, 129), (257, 300, 1000), (4000, 4000, 100)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_bf16_dma_ragged_small_integer_exact(shape):
+    M, N, K = shape
+    rng = np.random.default_rng(M + 3 * N + K)
+    A = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    B = rng.integers(-4, 5, (K, N)).astype(np.float32)
+    check(gi.make_problem(M, N, K, "bf16", ROW_MAJOR, COL_MAJOR, A_logical=A, B_logical=B),
+          g.Algo.MFMA_DMA, exact=True)
+    assert g.gemm_last_kernel().startswith("bf16_dma")
+
+
+@pytest.mark.parametrize("oc", [ROW_MAJOR, COL_MAJOR], ids=["RCR", "RCC"])
+@pytest.mark.parametrize("pad", [1, 3, 8])
+def test_bf16_dma_ragged_padded(oc, pad):
+    """Odd and padded leading dimensions with partial tiles and a K tail; C padding intact."""
+    p = gi.make_problem(300, 260, 100, "bf16", ROW_MAJOR, COL_MAJOR, oc, wid=60, pad_a=pad, pad_b=pad,
+                        pad_c=pad)
+    check(p, g.Algo.MFMA_DMA)
+    assert g.gemm_last_kernel().startswith("bf16_dma")
+
+
+def test_bf16_dma_ragged_closed_forms():
+    M, N, K = 300, 260, 100
+    P = np.eye(M, dtype=np.float32)[np.random.default_rng(8).permutation(M)]
+    B = np.random.default_rng(9).uniform(-1, 1, (M, N)).astype(np.float32)
+    pb = gi.make_problem(M, N, M, "bf16", ROW_MAJOR, COL_MAJOR, A_logical=P, B_logical=B)
+    assert np.array_equal(logical_c(pb, run(pb, g.Algo.MFMA_DMA)), P @ pb.b_f32())
+    ones = gi.make_problem(M, N, K, "bf16", ROW_MAJOR, COL_MAJOR, A_logical=np.ones((M, K)),
+                           B_logical=np.ones((K, N)))
+    assert np.all(logical_c(ones, run(ones, g.Algo.MFMA_DMA)) == K)
 
 
 # --- direct copies from rows that are not 16-byte aligned (element alignment only) --------

@@ -10,16 +10,17 @@
 //  * a workgroup owns 16 columns n0 .. n0+15 and 64 rows m0 .. m0+63 of C (fewer when M is
 //    smaller: 16 FM rows), so a 16 x 4096 problem spreads over 256 workgroups, one per CU,
 //    and a 1000 x 1000 one over 16 x 63;
-//  * its 4 wavefronts split K into 4 contiguous ranges (split-K inside the workgroup) and
+//  * its 8 wavefronts split K into 8 contiguous ranges (split-K inside the workgroup) and
 //    each streams its range of those 16 columns of B and of the FM 16-row strips of A (A is
 //    small and stays in L2) straight from global memory into registers -- no LDS staging in
-//    the main loop, each lane loads 16 bytes per operand per step, two steps' loads in
-//    flight ahead of the matrix instructions;
+//    the main loop, each lane loads 16 bytes per operand per step (4-byte loads from 4 rows
+//    for a row-major FP32 B), a ring of load batches in flight ahead of the matrix
+//    instructions (see Depth);
 //  * matrix instructions with a 16-row granularity: v_mfma_f32_16x16x32_bf16 (BF16) and
 //    v_mfma_f32_16x16x4_f32 (FP32).  Lane l supplies row / column l % 16; the k-assignment
 //    of lanes is free as long as A and B use the same one, so lane l takes the 16-byte run
 //    of k that starts at 8 (l / 16) (BF16) or 4 (l / 16) (FP32) within each k-step;
-//  * the 4 partial products are summed through LDS in a fixed order (wave 0 + 1 + 2 + 3):
+//  * the 8 partial products are summed through LDS in a fixed order (wave 0 + 1 + ... + 7):
 //    deterministic, no atomics, no workspace;
 //  * accumulator layout of a 16 x 16 result: lane l, register r holds row 4 (l / 16) + r,
 //    column l % 16.
@@ -39,7 +40,17 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
 
-constexpr int BN = 16, CHUNK = 4;   // columns per workgroup, k-steps per load batch
+constexpr int BN = 16;              // columns per workgroup
+
+// Loads in flight: a wavefront keeps RING batches of CHUNK k-steps in registers, the loads
+// of a batch issued RING - 1 batches before its matrix instructions.  Each wavefront has
+// few k-steps, so the kernel waits on memory latency unless many loads are in flight:
+// 16 k-steps with one 16-row strip of A (25% faster than 8 at 16 x 4096 x 4096; 24
+// measured no faster), 8 with more strips (the registers of two wavefronts per SIMD).
+template <int FM> struct Depth { static constexpr int RING = 2, CHUNK = 8; };
+template <> struct Depth<2> { static constexpr int RING = 2, CHUNK = 4; };
+template <> struct Depth<3> { static constexpr int RING = 2, CHUNK = 4; };
+template <> struct Depth<4> { static constexpr int RING = 2, CHUNK = 4; };
 
 // ---- per-dtype pieces -------------------------------------------------------------------
 // One k-step: BF16 32 k (lane holds 8 consecutive k), FP32 16 k (lane holds 4).
@@ -118,8 +129,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(Problem p, int klen, int 
 #pragma unroll
     for (int f = 0; f < FM; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    constexpr int CK = CHUNK * D::KSTEP;
-    Frag fa[2][CHUNK][FM], fb[2][CHUNK];
+    constexpr int CHUNK = Depth<FM>::CHUNK, RING = Depth<FM>::RING, CK = CHUNK * D::KSTEP;
+    Frag fa[RING][CHUNK][FM], fb[RING][CHUNK];
     // one batch of CHUNK k-steps; `full` (wavefront-uniform): the whole batch lies inside
     // this wavefront's K range, so 16-byte loads need no bounds checks
     auto load_chunk = [&](int buf, int kc) {
@@ -140,17 +151,21 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(Problem p, int klen, int 
 #pragma unroll
             for (int f = 0; f < FM; ++f) acc[f] = D::mma(fa[buf][s][f], fb[buf][s], acc[f]);
     };
-    // two batches per trip so that register buffers are indexed by constants
-    if (kbeg < kend) load_chunk(0, kbeg);
-    for (int kc = kbeg; kc < kend; kc += 2 * CK) {
-        const bool second = kc + CK < kend;
-        if (second) load_chunk(1, kc + CK);
-        compute_chunk(0);
-        if (kc + 2 * CK < kend) load_chunk(0, kc + 2 * CK);
-        if (second) compute_chunk(1);
+    // ring of RING register buffers, unrolled by RING so that buffers are indexed by
+    // constants: batch b lives in buffer b % RING
+#pragma unroll
+    for (int r = 0; r + 1 < RING; ++r)
+        if (kbeg + r * CK < kend) load_chunk(r, kbeg + r * CK);
+    for (int kc = kbeg; kc < kend; kc += RING * CK) {
+#pragma unroll
+        for (int r = 0; r < RING; ++r) {
+            const int kl = kc + (r + RING - 1) * CK;       // the batch RING - 1 ahead
+            if (kl < kend) load_chunk((r + RING - 1) % RING, kl);
+            if (kc + r * CK < kend) compute_chunk(r);
+        }
     }
 
-    // ---- fixed-order sum of the 4 wavefronts' partial products ----
+    // ---- fixed-order sum of the wavefronts' partial products ----
     if (wave > 0)
 #pragma unroll
         for (int f = 0; f < FM; ++f) red[wave - 1][f][lane] = acc[f];
@@ -173,8 +188,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(Problem p, int klen, int 
 
 template <typename D, int WAVES, bool B_KC>
 hipError_t launch_d(const Problem& p, const Launch& l) {
-    // per-wavefront K range, a multiple of the load batch
-    constexpr int CK = CHUNK * D::KSTEP;
+    // per-wavefront K range, a multiple of the smallest load batch (4 k-steps)
+    constexpr int CK = 4 * D::KSTEP;
     const int per = (p.K + WAVES - 1) / WAVES;
     const int klen = ((per + CK - 1) / CK) * CK;
     const int slabs = (p.N + BN - 1) / BN, rblocks = (p.M + 63) / 64;

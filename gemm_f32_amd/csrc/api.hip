@@ -74,9 +74,19 @@ int pick_group_m(int tiles_m, int tiles_n) {
 int64_t tiles(int64_t M, int64_t N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
 
 // AUTO takes the small-problem kernel for few rows, or when even 64 x 64 tiles would leave
-// more than half of the CUs idle (each such tile walks all of K alone).
-bool prefer_small(const Problem& p, int cus) {
-    return p.M <= kSkinnyMaxM || tiles(p.M, p.N, 64, 64) * 2 < (cus > 0 ? cus : 256);
+// more than half of the CUs idle (each such tile walks all of K alone).  For FP32 also when
+// 128 x 128 tiles cannot give every CU one: its K split over eight wavefronts then beats
+// the tile kernels, whose few tiles each wait on memory latency (1000^3: 58 -> 30 us).
+bool prefer_small(const Problem& p, int cus, bool f32) {
+    const int64_t c = cus > 0 ? cus : 256;
+    return p.M <= kSkinnyMaxM || tiles(p.M, p.N, 64, 64) * 2 < c || (f32 && tiles(p.M, p.N, 128, 128) < c);
+}
+
+// The small-problem kernel, with 1 or 4 column blocks of 16 per workgroup.
+hipError_t run_skinny(const Problem& p, const Launch& l, bool bf16, int cus, const char*& name) {
+    const int fn = skinny_blocks(p, cus);
+    name = bf16 ? (fn == 4 ? "bf16_skinny64" : "bf16_skinny16") : (fn == 4 ? "f32_skinny64" : "f32_skinny16");
+    return launch_skinny(p, l, bf16, fn);
 }
 
 // Block-tile choice.  The grid runs in rounds of cus x per_cu resident blocks (per_cu: how
@@ -207,10 +217,10 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
             }
             case GEMM_ALGO_SKINNY:
                 if (!skinny_applies(p, false)) return GEMM_ERR_INVALID_VALUE;
-                err = launch_skinny(p, l, false); name = "f32_skinny16"; break;
+                err = run_skinny(p, l, false, dev.cus, name); break;
             default: {
-                if (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus) && skinny_applies(p, false)) {
-                    err = launch_skinny(p, l, false); name = "f32_skinny16"; break;
+                if (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus, true) && skinny_applies(p, false)) {
+                    err = run_skinny(p, l, false, dev.cus, name); break;
                 }
                 // direct-copy kernel (tiles 256 or 128) where it applies, else register-staged
                 const bool dma256 = f32_dma_applies(p, l, 256, 256);
@@ -250,10 +260,9 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
             }
         }
     } else if (algo == GEMM_ALGO_SKINNY ||
-               (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus) && skinny_applies(p, true))) {
+               (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus, false) && skinny_applies(p, true))) {
         if (!skinny_applies(p, true)) return GEMM_ERR_INVALID_VALUE;
-        err = launch_skinny(p, l, true);
-        name = "bf16_skinny16";
+        err = run_skinny(p, l, true, dev.cus, name);
     } else if (algo == GEMM_ALGO_MFMA_PINGPONG) {
         if (!bf16_pingpong_applies(p, l)) return GEMM_ERR_INVALID_VALUE;
         l.group_m = pick_group_m(p.M / 256, p.N / 256);

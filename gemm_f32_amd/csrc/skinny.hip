@@ -7,9 +7,9 @@
 // rungs" (split-K): divide K among workers and combine the partial sums in a second step.
 // Design for MI355X:
 //
-//  * a workgroup owns 16 columns n0 .. n0+15 and 64 rows m0 .. m0+63 of C (fewer when M is
-//    smaller: 16 FM rows), so a 16 x 4096 problem spreads over 256 workgroups, one per CU,
-//    and a 1000 x 1000 one over 16 x 63;
+//  * a workgroup owns 16 FN columns n0 .. and 64 rows m0 .. m0+63 of C (fewer when M is
+//    smaller: 16 FM rows); FN = 4 (64 x 64) when that still gives every CU a workgroup
+//    (1000 x 1000: 16 x 16), else FN = 1 (16 x 4096: 256 workgroups of 16 x 16);
 //  * its 8 wavefronts split K into 8 contiguous ranges (split-K inside the workgroup) and
 //    each streams its range of those 16 columns of B and of the FM 16-row strips of A (A is
 //    small and stays in L2) straight from global memory into registers -- no LDS staging in
@@ -40,17 +40,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
 
-constexpr int BN = 16;              // columns per workgroup
 
 // Loads in flight: a wavefront keeps RING batches of CHUNK k-steps in registers, the loads
-// of a batch issued RING - 1 batches before its matrix instructions.  Each wavefront has
-// few k-steps, so the kernel waits on memory latency unless many loads are in flight:
-// 16 k-steps with one 16-row strip of A (25% faster than 8 at 16 x 4096 x 4096; 24
-// measured no faster), 8 with more strips (the registers of two wavefronts per SIMD).
-template <int FM> struct Depth { static constexpr int RING = 2, CHUNK = 8; };
-template <> struct Depth<2> { static constexpr int RING = 2, CHUNK = 4; };
-template <> struct Depth<3> { static constexpr int RING = 2, CHUNK = 4; };
-template <> struct Depth<4> { static constexpr int RING = 2, CHUNK = 4; };
+// of a batch issued RING - 1 batches before its matrix instructions: 16 k-steps with one
+// 16-row strip of A and one column block, fewer with more strips and blocks (the
+// registers of two wavefronts per SIMD).  (At 16 x 4096 x 4096, 8, 16 and 24 k-steps in
+// flight measured the same kernel time; at 1000^3 with four blocks, 2 batches of one
+// k-step beat 2 of two by 9%.)
+template <int FM, int FN> struct Depth {
+    static constexpr int RING = 2, CHUNK = FN > 1 ? 1 : (FM > 1 ? 4 : 8);
+};
 
 // ---- per-dtype pieces -------------------------------------------------------------------
 // One k-step: BF16 32 k (lane holds 8 consecutive k), FP32 16 k (lane holds 4).
@@ -91,6 +90,14 @@ struct F32 {
         for (int e = 0; e < 4; ++e) v[e] = (k + e < K) ? col[(int64_t)(k + e) * ld] : 0.f;
         return make_float4(v[0], v[1], v[2], v[3]);
     }
+    // B row-major, four column blocks: 4 consecutive columns col .. col+3 of row `row`
+    __device__ static Frag load_row4(const float* B, int64_t ld, int row, int K, int col, int N, bool fast) {
+        if (fast) return load16f(B + (int64_t)row * ld + col);
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = (row < K && col + q < N) ? B[(int64_t)row * ld + col + q] : 0.f;
+        return make_float4(v[0], v[1], v[2], v[3]);
+    }
     __device__ static f32x4 mma(const Frag& a, const Frag& b, f32x4 c) {
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, c, 0, 0, 0);
@@ -100,37 +107,54 @@ struct F32 {
     }
 };
 
-template <typename D, int FM, int WAVES, bool B_KC>
-__global__ __launch_bounds__(64 * WAVES) void k_skinny(Problem p, int klen, int vec_a, int vec_b) {
+// FN column blocks of 16 per workgroup (1 or 4).  With FN = 4 and a row-major FP32 B, a
+// lane's 16-byte load along N holds one k of 4 consecutive columns 4 c .. 4 c + 3, i.e. the
+// B operand of 4 matrix instructions: block q's column c is column n0 + 4 c + q of C, and
+// the epilogue writes the 4 columns of a lane with one 16-byte store.
+template <typename D, int FM, int FN, int WAVES, bool B_KC>
+__global__ __launch_bounds__(64 * WAVES) void k_skinny(Problem p, int klen, int vec_a, int vec_b, int vec_c) {
     using E = typename D::Elem;
     using Frag = typename D::Frag;
-    __shared__ f32x4 red[WAVES - 1][FM][64];
+    constexpr bool RC4 = !B_KC && FN == 4;     // row-major FP32 B read 16 bytes along N
+    constexpr int BNW = 16 * FN;               // columns per workgroup
+    constexpr int NB = RC4 ? 4 : FN;           // B fragments per k-step
+    static_assert(FN == 1 || FN == 4, "one or four column blocks");
+    static_assert(!RC4 || D::KL == 4, "four column blocks of a row-major B: FP32 only");
+    __shared__ f32x4 red[WAVES - 1][FM][FN][64];
 
     // (row block, column slab): the workgroups one XCD receives cover all row blocks of a
     // run of neighbouring slabs (which share 128-byte lines of a row-major B)
-    const int slabs = (p.N + BN - 1) / BN, rblocks = (p.M + 63) / 64;
+    const int slabs = (p.N + BNW - 1) / BNW, rblocks = (p.M + 63) / 64;
     int rb, slab;
     tile_coords(blockIdx.x, rblocks, slabs, rblocks, rb, slab);
-    const int n0 = slab * BN, m0 = rb * 64;
+    const int n0 = slab * BNW, m0 = rb * 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lq = lane >> 4;
     const int K = p.K;
     const int kbeg = wave * klen, kend = min(K, kbeg + klen);
+    const bool n_inside = n0 + BNW <= p.N;      // wavefront-uniform
 
-    // this lane's rows of A (one per 16-row strip) and its column of B, clamped into range
+    // this lane's rows of A (one per 16-row strip) and columns of B, clamped into range
     const E* arow[FM];
 #pragma unroll
     for (int f = 0; f < FM; ++f)
         arow[f] = static_cast<const E*>(p.A) + (int64_t)min(m0 + 16 * f + li, p.M - 1) * p.lda;
-    const int n = min(n0 + li, p.N - 1);
-    const E* bcol = static_cast<const E*>(p.B) + (B_KC ? (int64_t)n * p.ldb : (int64_t)n);
-
-    f32x4 acc[FM];
+    const E* bcol[FN];
 #pragma unroll
-    for (int f = 0; f < FM; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < FN; ++q) {
+        const int n = min(n0 + 16 * q + li, p.N - 1);
+        bcol[q] = static_cast<const E*>(p.B) + (B_KC ? (int64_t)n * p.ldb : (int64_t)n);
+    }
+    const float* Bf = reinterpret_cast<const float*>(p.B);
 
-    constexpr int CHUNK = Depth<FM>::CHUNK, RING = Depth<FM>::RING, CK = CHUNK * D::KSTEP;
-    Frag fa[RING][CHUNK][FM], fb[RING][CHUNK];
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+        for (int q = 0; q < FN; ++q) acc[f][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    constexpr int CHUNK = Depth<FM, FN>::CHUNK, RING = Depth<FM, FN>::RING, CK = CHUNK * D::KSTEP;
+    Frag fa[RING][CHUNK][FM], fb[RING][CHUNK][NB];
     // one batch of CHUNK k-steps; `full` (wavefront-uniform): the whole batch lies inside
     // this wavefront's K range, so 16-byte loads need no bounds checks
     auto load_chunk = [&](int buf, int kc) {
@@ -141,15 +165,38 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(Problem p, int klen, int 
             const int k = kc + s * D::KSTEP + lq * D::KL;
 #pragma unroll
             for (int f = 0; f < FM; ++f) fa[buf][s][f] = D::load(arow[f], k, kend, fa_fast);
-            if constexpr (B_KC) fb[buf][s] = D::load(bcol, k, kend, fb_fast);
-            else fb[buf][s] = F32::load_strided(reinterpret_cast<const float*>(bcol), p.ldb, k, kend);
+            if constexpr (B_KC) {
+#pragma unroll
+                for (int q = 0; q < FN; ++q) fb[buf][s][q] = D::load(bcol[q], k, kend, fb_fast);
+            } else if constexpr (RC4) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    fb[buf][s][e] = F32::load_row4(Bf, p.ldb, k + e, kend, n0 + 4 * li, p.N, full && n_inside);
+            } else {
+                fb[buf][s][0] = F32::load_strided(reinterpret_cast<const float*>(bcol[0]), p.ldb, k, kend);
+            }
         }
     };
     auto compute_chunk = [&](int buf) {
 #pragma unroll
-        for (int s = 0; s < CHUNK; ++s)
+        for (int s = 0; s < CHUNK; ++s) {
+            if constexpr (RC4) {
+                // step e: lane (g, c) holds A[row][k + e] and B[k + e][n0 + 4 c .. +3]
 #pragma unroll
-            for (int f = 0; f < FM; ++f) acc[f] = D::mma(fa[buf][s][f], fb[buf][s], acc[f]);
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int f = 0; f < FM; ++f)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            acc[f][q] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[buf][s][f][e], fb[buf][s][e][q],
+                                                                             acc[f][q], 0, 0, 0);
+            } else {
+#pragma unroll
+                for (int f = 0; f < FM; ++f)
+#pragma unroll
+                    for (int q = 0; q < FN; ++q) acc[f][q] = D::mma(fa[buf][s][f], fb[buf][s][q], acc[f][q]);
+            }
+        }
     };
     // ring of RING register buffers, unrolled by RING so that buffers are indexed by
     // constants: batch b lives in buffer b % RING
@@ -168,38 +215,61 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(Problem p, int klen, int 
     // ---- fixed-order sum of the wavefronts' partial products ----
     if (wave > 0)
 #pragma unroll
-        for (int f = 0; f < FM; ++f) red[wave - 1][f][lane] = acc[f];
+        for (int f = 0; f < FM; ++f)
+#pragma unroll
+            for (int q = 0; q < FN; ++q) red[wave - 1][f][q][lane] = acc[f][q];
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
         for (int f = 0; f < FM; ++f) {
-            f32x4 s = acc[f];
+            f32x4 sum[FN];
 #pragma unroll
-            for (int w = 0; w < WAVES - 1; ++w) s += red[w][f][lane];
-            const int col = n0 + li;
+            for (int q = 0; q < FN; ++q) {
+                sum[q] = acc[f][q];
+#pragma unroll
+                for (int w = 0; w < WAVES - 1; ++w) sum[q] += red[w][f][q][lane];
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = m0 + 16 * f + 4 * lq + r;
-                if (row < p.M && col < p.N) p.C[(int64_t)row * p.ldc + col] = s[r];
+                if (row >= p.M) continue;
+                float* crow = p.C + (int64_t)row * p.ldc;
+                if constexpr (RC4) {
+                    // block q's column li is column n0 + 4 li + q
+                    const int col = n0 + 4 * li;
+                    if (vec_c && n_inside) {
+                        *reinterpret_cast<f32x4*>(crow + col) = f32x4{sum[0][r], sum[1][r], sum[2][r], sum[3][r]};
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (col + q < p.N) crow[col + q] = sum[q][r];
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < FN; ++q) {
+                        const int col = n0 + 16 * q + li;
+                        if (col < p.N) crow[col] = sum[q][r];
+                    }
+                }
             }
         }
     }
 }
 
-template <typename D, int WAVES, bool B_KC>
+template <typename D, int FN, int WAVES, bool B_KC>
 hipError_t launch_d(const Problem& p, const Launch& l) {
-    // per-wavefront K range, a multiple of the smallest load batch (4 k-steps)
+    // per-wavefront K range, a multiple of 4 k-steps
     constexpr int CK = 4 * D::KSTEP;
     const int per = (p.K + WAVES - 1) / WAVES;
     const int klen = ((per + CK - 1) / CK) * CK;
-    const int slabs = (p.N + BN - 1) / BN, rblocks = (p.M + 63) / 64;
+    const int slabs = (p.N + 16 * FN - 1) / (16 * FN), rblocks = (p.M + 63) / 64;
     const dim3 grid((unsigned)(slabs * rblocks)), block(64 * WAVES);
-    const int va = l.vec_a, vb = l.vec_b;
+    const int va = l.vec_a, vb = l.vec_b, vc = l.vec_c;
     const int fm = p.M >= 64 ? 4 : (p.M + 15) / 16;
-    if (fm == 1) hipLaunchKernelGGL((k_skinny<D, 1, WAVES, B_KC>), grid, block, 0, l.stream, p, klen, va, vb);
-    else if (fm == 2) hipLaunchKernelGGL((k_skinny<D, 2, WAVES, B_KC>), grid, block, 0, l.stream, p, klen, va, vb);
-    else if (fm == 3) hipLaunchKernelGGL((k_skinny<D, 3, WAVES, B_KC>), grid, block, 0, l.stream, p, klen, va, vb);
-    else hipLaunchKernelGGL((k_skinny<D, 4, WAVES, B_KC>), grid, block, 0, l.stream, p, klen, va, vb);
+    if (fm == 1) hipLaunchKernelGGL((k_skinny<D, 1, FN, WAVES, B_KC>), grid, block, 0, l.stream, p, klen, va, vb, vc);
+    else if (fm == 2) hipLaunchKernelGGL((k_skinny<D, 2, FN, WAVES, B_KC>), grid, block, 0, l.stream, p, klen, va, vb, vc);
+    else if (fm == 3) hipLaunchKernelGGL((k_skinny<D, 3, FN, WAVES, B_KC>), grid, block, 0, l.stream, p, klen, va, vb, vc);
+    else hipLaunchKernelGGL((k_skinny<D, 4, FN, WAVES, B_KC>), grid, block, 0, l.stream, p, klen, va, vb, vc);
     return hipGetLastError();
 }
 
@@ -209,11 +279,22 @@ bool skinny_applies(const Problem& p, bool bf16) {
     return p.oa == kRow && (bf16 ? p.ob == kCol : true);
 }
 
-hipError_t launch_skinny(const Problem& p, const Launch& l, bool bf16) {
+int skinny_blocks(const Problem& p, int cus) {
+    // four column blocks per workgroup when that still gives every CU a workgroup
+    const int64_t wgs4 = (int64_t)((p.M + 63) / 64) * ((p.N + 63) / 64);
+    return wgs4 >= (cus > 0 ? cus : 256) ? 4 : 1;
+}
+
+hipError_t launch_skinny(const Problem& p, const Launch& l, bool bf16, int fn) {
     constexpr int W = kSkinnyWaves;
-    if (bf16) return launch_d<Bf16, W, true>(p, l);
-    if (p.ob == kCol) return launch_d<F32, W, true>(p, l);
-    return launch_d<F32, W, false>(p, l);
+    if (fn == 4) {
+        if (bf16) return launch_d<Bf16, 4, W, true>(p, l);
+        if (p.ob == kCol) return launch_d<F32, 4, W, true>(p, l);
+        return launch_d<F32, 4, W, false>(p, l);
+    }
+    if (bf16) return launch_d<Bf16, 1, W, true>(p, l);
+    if (p.ob == kCol) return launch_d<F32, 1, W, true>(p, l);
+    return launch_d<F32, 1, W, false>(p, l);
 }
 
 }  // namespace gemm

@@ -248,6 +248,54 @@ def test_skinny_column_major_c_uses_n_as_rows():
     check(p, g.Algo.SKINNY)
 
 
+# --- the small-problem kernel with four column blocks per workgroup (64 x 64 of C, K split
+# over eight wavefronts): chosen when that still gives every CU a workgroup -------------------
+SKINNY64_SHAPES = [(1000, 1000, 1000), (1030, 1000, 77), (1024, 1025, 1), (1001, 1023, 333), (1024, 1024, 4097)]
+
+
+@pytest.mark.parametrize("dtype,ob", [("f32", ROW_MAJOR), ("f32", COL_MAJOR), ("bf16", COL_MAJOR)],
+                         ids=["f32-RR", "f32-RC", "bf16"])
+@pytest.mark.parametrize("shape", SKINNY64_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_skinny64_random(dtype, ob, shape):
+    M, N, K = shape
+    p = gi.make_problem(M, N, K, dtype, ROW_MAJOR, ob, wid=53)
+    check(p, g.Algo.SKINNY, key=("skinny64", dtype, ob, shape))
+    assert g.gemm_last_kernel() == f"{dtype}_skinny64"
+
+
+@pytest.mark.parametrize("dtype,ob", [("f32", ROW_MAJOR), ("f32", COL_MAJOR), ("bf16", COL_MAJOR)],
+                         ids=["f32-RR", "f32-RC", "bf16"])
+def test_skinny64_small_integer_exact(dtype, ob):
+    rng = np.random.default_rng(19)
+    M, N, K = 1003, 1021, 301
+    A = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    B = rng.integers(-4, 5, (K, N)).astype(np.float32)
+    check(gi.make_problem(M, N, K, dtype, ROW_MAJOR, ob, A_logical=A, B_logical=B), g.Algo.SKINNY, exact=True)
+    assert g.gemm_last_kernel() == f"{dtype}_skinny64"
+
+
+@pytest.mark.parametrize("oc", [ROW_MAJOR, COL_MAJOR], ids=["C-row", "C-col"])
+@pytest.mark.parametrize("pad", [1, 4])
+def test_skinny64_padded_and_c_orders(oc, pad):
+    # column-major C swaps the operands: B^T (column-major when B is row-major) becomes A
+    ob = ROW_MAJOR if oc == ROW_MAJOR else COL_MAJOR
+    p = gi.make_problem(1000, 1030, 260, "f32", ROW_MAJOR, ob, oc, wid=54, pad_a=pad, pad_b=pad, pad_c=pad)
+    check(p, g.Algo.SKINNY)
+    assert g.gemm_last_kernel() == "f32_skinny64"
+
+
+def test_skinny64_closed_forms():
+    n = 1024
+    perm = np.random.default_rng(11).permutation(n)
+    P = np.eye(n, dtype=np.float32)[perm]
+    B = np.random.default_rng(12).uniform(-1, 1, (n, n)).astype(np.float32)
+    pb = gi.make_problem(n, n, n, "f32", ROW_MAJOR, ROW_MAJOR, A_logical=P, B_logical=B)
+    assert np.array_equal(logical_c(pb, run(pb, g.Algo.SKINNY)), B[perm])
+    pa = gi.make_problem(n, n, n, "f32", ROW_MAJOR, ROW_MAJOR, A_logical=B, B_logical=P.T.copy())
+    assert np.array_equal(logical_c(pa, run(pa, g.Algo.SKINNY)), B[:, perm])
+    assert g.gemm_last_kernel() == "f32_skinny64"
+
+
 @pytest.mark.parametrize("bad", [dict(order_a=COL_MAJOR), dict(dtype="bf16", order_b=ROW_MAJOR)],
                          ids=lambda d: str(d))
 def test_skinny_rejects_unsupported(bad):
@@ -260,7 +308,7 @@ def test_skinny_rejects_unsupported(bad):
 
 @pytest.mark.parametrize("dtype,shape,kernel", [
     ("f32", (16, 4096, 4096), "f32_skinny16"), ("bf16", (16, 4096, 4096), "bf16_skinny16"),
-    ("f32", (256, 256, 256), "f32_skinny16"), ("f32", (1000, 1000, 1000), "f32_mfma64x64"),
+    ("f32", (256, 256, 256), "f32_skinny16"), ("f32", (1000, 1000, 1000), "f32_skinny64"),
     ("f32", (2048, 2048, 256), "f32_dma128x128"), ("f32", (2047, 2049, 255), "f32_mfma64x64"),
     ("bf16", (1000, 1000, 1000), "bf16_mfma64x64"), ("f32", (4096, 4096, 64), "f32_dma256x256"),
     ("bf16", (4096, 4096, 64), "bf16_dma256x256"),

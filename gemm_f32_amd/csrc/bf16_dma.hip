@@ -10,7 +10,7 @@
 //    accumulators per lane), two per SIMD: while one of them waits on the issue of a copy
 //    or on the barrier, the other one keeps the SIMD's matrix pipe busy (measured 7% faster
 //    at 4096^3 than four wavefronts of 128 x 128, despite 1.5 times the LDS reads).  At
-//    256 x 128, four wavefronts of 128 x 64, one per SIMD.
+//    256 x 128, eight wavefronts of 64 x 64.
 //  * LDS: one row of BK bf16 (128 bytes, 8 chunks of 16 bytes) per row of each tile, chunk
 //    c of row r stored at c ^ s(r), s(r) = (r mod 8) xor bit 3 of r, so that the 32 rows
 //    read at one logical chunk fall on distinct 16-byte bank groups.  A lane's 16-byte read
@@ -25,8 +25,9 @@
 //    rows of its copy block that exist, so rows past M (N) read as zero: edge tiles need no
 //    separate code in the k-loop.  (Buffer loads, like global ones, accept the 2-byte
 //    aligned rows of odd leading dimensions on gfx950.)
-//  * Two LDS stages ("GEMM Optimization", V3), software-pipelined across k-tiles (see the
-//    main loop); one barrier per k-tile.
+//  * Two or three LDS stages ("GEMM Optimization", V3: stage the next tile while the current
+//    one is multiplied), software-pipelined across k-tiles (see the main loop); one barrier
+//    per k-tile.
 //  * K tail: a last k-tile staged through registers with bounds checks and zero fill into
 //    the same LDS positions ("A06 - Tiled Matrix Multiply (GEMM)", "Pitfall 1 - The
 //    boundary guard that fails silently": a ragged K needs the zero fill).
@@ -58,9 +59,9 @@ constexpr int kBufWord3 = 0x00020000;
 // logical chunk hit 16 distinct 16-byte bank groups
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-template <int BM_, int BN_, int WGM_, int WGN_, int CSPAN_>
+template <int BM_, int BN_, int WGM_, int WGN_, int CSPAN_, int S_>
 struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, BK = 64, WGM = WGM_, WGN = WGN_, S = 2;
+    static constexpr int BM = BM_, BN = BN_, BK = 64, WGM = WGM_, WGN = WGN_, S = S_;
     static constexpr int ROW = BK * 2;                       // LDS row bytes (8 chunks)
     static constexpr int RPC = 1024 / ROW;                   // tile rows per 1 KB copy
     static constexpr int NW = WGM * WGN, THREADS = 64 * NW;
@@ -73,14 +74,18 @@ struct Cfg {
     static constexpr int SUB = BK / 16;                      // k-steps per k-tile
     static constexpr int MF = FM * FN;                       // matrix instructions per k-step
     static constexpr int RD = FM + FN;                       // fragment reads per k-step
-    // the copies of a k-tile are spread over CSPAN k-steps (the last one of the k-tile
-    // before it and the first CSPAN - 1 of the k-tile before that), one every W / DMA
-    // instruction slots
+    // the copies of k-tile t are spread over CSPAN k-steps (the last one of k-tile t - S
+    // and the first CSPAN - 1 of k-tile t - S + 1), one every W / DMA instruction slots;
+    // HEAD of them fall on the first of those k-steps
     static constexpr int CSPAN = CSPAN_, W = CSPAN * MF;
+    static constexpr int HEAD = (MF * DMA + W - 1) / W;
     static_assert(FM >= 1 && FN >= 1 && A_DMA >= 1 && B_DMA >= 1, "tile too small");
     static_assert(A_RPW % 16 == 0 && B_RPW % 16 == 0, "copy blocks start at even swizzle parity");
     static_assert(RD <= MF, "one fragment read per instruction slot");
-    static_assert(CSPAN >= 1 && CSPAN < SUB, "copies must land before the k-tile's barrier");
+    static_assert(S == 2 || S == 3, "LDS stages");
+    // with two stages the copies of tile kt+1 are issued and land within iteration kt; with
+    // three they have until the barrier of iteration kt+1
+    static_assert(CSPAN >= 1 && (S == 2 ? CSPAN < SUB : CSPAN <= SUB), "copies land before their barrier");
     static_assert(W >= DMA, "at most one copy per instruction slot");
     static constexpr int LDS = S * STAGE;
     // epilogue: a 32 x WN band per wavefront, rows padded by 8 floats (the two half-waves
@@ -177,52 +182,57 @@ void k_bf16_dma(Problem p, int tiles_m, int tiles_n, int group_m) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[b][i], fb[b][j], acc[i][j], 0, 0, 0);
     };
 
-    // ---- software pipeline over k-tiles, two LDS stages.  Iteration kt multiplies tile kt
-    // (stage kt % 2), k-step by k-step, with the fragments of the next k-step read under
-    // the current one's matrix instructions.  Its last k-step is preceded by the barrier
-    // that publishes tile kt+1 (every wavefront has waited for its own copies of it) and
-    // frees stage kt % 2 (every wavefront's reads of it have completed): during that k-step
-    // each wavefront reads the first fragments of tile kt+1 and starts the copies of tile
-    // kt+2 into the freed stage, which continue through the first CSPAN - 1 k-steps of
-    // iteration kt+1 and have the k-steps up to its barrier to land.  The copies are spread
-    // out because the CU moves about one 1 KB copy per 16 cycles: bunched together they
-    // stall the wavefront that issues them, and with it its matrix instructions.  Past the
-    // end of K the copies repeat the last tile into a stage nobody reads, and the fragments
-    // read for a tile nk are never used, so the loop body has no branch.
+    // ---- software pipeline over k-tiles, S LDS stages (tile t in stage t % S).  Iteration
+    // kt multiplies tile kt k-step by k-step, with the fragments of the next k-step read
+    // under the current one's matrix instructions.  Its last k-step is preceded by the
+    // barrier that publishes tile kt+1 (every wavefront has waited for its own copies of
+    // it) and frees stage kt % S (every wavefront's reads of it have completed): during that
+    // k-step each wavefront reads the first fragments of tile kt+1 and starts the copies of
+    // tile kt+S into the freed stage, which continue through the first CSPAN - 1 k-steps of
+    // iteration kt+1 and have until the barrier of iteration kt+S-1 to land.  The copies
+    // are spread out because the CU moves about one 1 KB copy per 16 cycles: bunched
+    // together they stall the wavefront that issues them, and with it its matrix
+    // instructions.  Past the end of K the copies repeat the last tile into a stage nobody
+    // reads, and the fragments read for a tile nk are never used, so the loop body has no
+    // branch.
     if (nk > 0) {                             // uniform
+        constexpr int S = C::S;
         const int last = nk - 1;
 #pragma unroll
-        for (int j = 0; j < C::DMA; ++j) issue_one(j, 0, 0);
+        for (int t = 0; t + 1 < S; ++t)
 #pragma unroll
-        for (int slot = 0; slot < MF; ++slot) copies_at(slot, min(1, last), 1);
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            for (int j = 0; j < C::DMA; ++j) issue_one(j, min(t, last), t);
+#pragma unroll
+        for (int slot = 0; slot < MF; ++slot) copies_at(slot, min(S - 1, last), S - 1);
+        // tile 0 landed: at most tiles 1 .. S-2 and the first copies of tile S-1 pending
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"((S - 2) * C::DMA + C::HEAD) : "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
 #pragma unroll
         for (int m = 0; m < C::RD; ++m) read_slot(0, 0, m, 0);
         for (int kt = 0; kt < nk; ++kt) {
-            const int st = kt & 1;
-            const int k1 = min(kt + 1, last), k2 = min(kt + 2, last);
+            const int st = kt % S, st1 = (kt + 1) % S, stt = (kt + S - 1) % S;
+            const int kh = min(kt + S, last), kq = min(kt + S - 1, last);   // head / tail tiles
 #pragma unroll
             for (int s = 0; s < SUB - 1; ++s) {
 #pragma unroll
                 for (int m = 0; m < MF; ++m) {
-                    if (s < C::CSPAN - 1) copies_at(MF + s * MF + m, k1, st ^ 1);
+                    if (s < C::CSPAN - 1) copies_at(MF + s * MF + m, kq, stt);
                     read_slot(st, s + 1, m, (s + 1) & 1);
                     mfma(m, s & 1);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            // own copies of tile kt+1 landed, own reads of stage st complete; a plain
-            // barrier (the compiler's workgroup fence would also wait for copies still in
-            // flight)
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            // own copies of tile kt+1 landed (those of tiles kt+2 .. kt+S-1 may not have),
+            // own reads of stage st complete; a plain barrier (the compiler's workgroup fence
+            // would also wait for the copies still in flight)
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"((S - 2) * C::DMA) : "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
 #pragma unroll
             for (int m = 0; m < MF; ++m) {
-                copies_at(m, k2, st);
-                read_slot(st ^ 1, 0, m, 0);
+                copies_at(m, kh, st);
+                read_slot(st1, 0, m, 0);
                 mfma(m, (SUB - 1) & 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -356,11 +366,15 @@ bool bf16_dma_applies(const Problem& p, const Launch&, int, int) {
            (int64_t)64 * p.ldb * 2 < lim;
 }
 
-// Configurations: 256 x 256 with eight wavefronts of 128 x 64 (two per SIMD, 128 KB of
-// LDS), 256 x 128 with four wavefronts of 128 x 64 (eight of 64 x 64 measured no faster).
+// Configurations: 256 x 256 with eight wavefronts of 128 x 64 (two per SIMD), two stages
+// (128 KB of LDS), the copies of a tile spread over two k-steps; 256 x 128 with eight
+// wavefronts of 64 x 64 and three stages (144 KB), the copies spread over four k-steps.
+// Measured per 64-deep k-tile at 4096^3 (in-kernel clock): 256 x 256 2270 cycles against
+// 2048 of matrix work; 256 x 128 1350 against 1024 (four wavefronts of 128 x 64: 1425 with
+// three stages, 1540-1630 with two).
 hipError_t launch_bf16_dma(const Problem& p, const Launch& l, int bm, int bn) {
-    if (bm == 256 && bn == 256) return launch_cfg<Cfg<256, 256, 2, 4, 2>>(p, l);
-    if (bm == 256 && bn == 128) return launch_cfg<Cfg<256, 128, 2, 2, 2>>(p, l);
+    if (bm == 256 && bn == 256) return launch_cfg<Cfg<256, 256, 2, 4, 2, 2>>(p, l);
+    if (bm == 256 && bn == 128) return launch_cfg<Cfg<256, 128, 4, 2, 4, 3>>(p, l);
     return hipErrorInvalidValue;
 }
 

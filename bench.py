@@ -55,13 +55,26 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_digest() -> str:
-    """Hash of the library's kernel sources; counter-derived traffic is only reported for
-    the sources it was measured on."""
+# sources that define each dominant kernel: its own file plus the shared headers (tile
+# scheduler, buffer helpers) and the launch declarations
+KERNEL_SOURCES = {
+    "f32_dma": ("f32_dma.hip",),
+    "bf16_dma": ("bf16_dma.hip",),
+}
+SHARED_SOURCES = ("common.hpp", "launch.hpp")
+
+
+def kernel_source_digest(kernel: str) -> str:
+    """Hash of the sources a kernel is built from (the library's name for it, e.g.
+    f32_dma256x256); counter-derived traffic is only reported for the sources it was
+    measured on."""
     import hashlib
+    family = next((k for k in KERNEL_SOURCES if kernel.startswith(k)), None)
+    if family is None:
+        return ""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gemm_f32_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(KERNEL_SOURCES[family] + SHARED_SOURCES):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -75,7 +88,8 @@ def measured_traffic(kernel: str, workload: str):
         return None
     with open(path) as f:
         rec = json.load(f).get(f"{kernel}@{workload}")
-    if not rec or rec.get("source_digest") != kernel_source_digest():
+    digest = kernel_source_digest(kernel)
+    if not rec or not digest or rec.get("source_digest") != digest:
         return None
     return rec["hbm_bytes_per_launch"]
 

@@ -86,74 +86,219 @@ bool prefer_small(const Problem& p, int cus, bool f32) {
 hipError_t run_skinny(const Problem& p, const Launch& l, bool bf16, int cus, const char*& name) {
     const int fn = skinny_blocks(p, cus);
     name = bf16 ? (fn == 4 ? "bf16_skinny64" : "bf16_skinny16") : (fn == 4 ? "f32_skinny64" : "f32_skinny16");
-    return launch_skinny(p, l, bf16, fn);
+    return launch_skinny(p, l, bf16, fn, skinny_strips(p, fn, cus));
 }
 
 // Block-tile choice.  The grid runs in rounds of cus x per_cu resident blocks (per_cu: how
 // many blocks of that kernel share a CU); a CU's round costs (blocks it holds) x (work per
-// tile / relative throughput of the tile size), so estimate time as the sum over rounds and
-// take the cheapest.  Relative throughputs are the kernels' measured rates at 4096^3 with full
-// rounds.
-struct TileOpt { int bm, bn; double eff; int per_cu; };
-constexpr TileOpt kBf16Tiles[] = {{256, 256, 1.0, 1}, {256, 128, 0.78, 1}, {128, 128, 0.82, 2},
-                                  {64, 64, 0.36, 4}};
-// BF16 direct-copy kernel (256 x 256, 256 x 128) alone, and together with the
-// register-staged kernel's smaller tiles (bm == 256 marks the direct-copy kernel)
-constexpr TileOpt kBf16DmaTiles[] = {{256, 256, 1.0, 1}, {256, 128, 0.86, 1}};
-constexpr TileOpt kBf16AnyTiles[] = {{256, 256, 1.0, 1}, {256, 128, 0.86, 1}, {128, 128, 0.80, 2},
-                                     {64, 64, 0.35, 4}};
-// FP32: the register-staged kernel (128 x 128, 64 x 64) and, where its requirements hold,
-// the direct-copy kernel (256 x 256, 128 x 128) with the register-staged 64 x 64
-constexpr TileOpt kF32Tiles[] = {{128, 128, 1.0, 4}, {64, 64, 0.92, 4}};
-constexpr TileOpt kF32DmaTiles[] = {{256, 256, 1.0, 1}, {128, 128, 0.85, 2}, {64, 64, 0.76, 4}};
+// tile / relative throughput of the kernel and tile), so estimate time as the sum over rounds
+// and take the cheapest.  Relative throughputs are the kernels' measured rates at 4096^3 with
+// full rounds, against the fastest kernel of the dtype.
+struct TileOpt {
+    int bm, bn;
+    double eff;
+    int per_cu;
+    bool dma;       // the direct-copy kernel (else the register-staged one)
+};
+// FP32: direct-copy 256^2 and 128^2, register-staged 128^2 and 64^2 (f32_mfma.hip)
+constexpr TileOpt kF32DmaOpts[] = {{256, 256, 1.0, 1, true}, {128, 128, 0.85, 2, true}};
+constexpr TileOpt kF32MfmaOpts[] = {{128, 128, 0.85, 4, false}, {64, 64, 0.75, 4, false}};
+// BF16: direct-copy 256^2 and 256x128, register-staged tiles of bf16_mfma.hip
+constexpr TileOpt kBf16DmaOpts[] = {{256, 256, 1.0, 1, true}, {256, 128, 0.86, 1, true}};
+constexpr TileOpt kBf16MfmaOpts[] = {{256, 256, 1.0, 1, false}, {256, 128, 0.78, 1, false},
+                                     {128, 128, 0.74, 2, false}, {64, 64, 0.35, 4, false}};
+// relative throughput of the small tiles that run an edge strip
+constexpr double kF32StripEff = 0.75, kBf16StripEff = 0.35;
 
-template <size_t NOPT>
-void pick_tile(const TileOpt (&opts)[NOPT], int64_t M, int64_t N, int cus, int& bm, int& bn) {
-    double best = 1e300;
-    for (const TileOpt& o : opts) {
-        const double c = cus > 0 ? cus : 256, n = (double)tiles(M, N, o.bm, o.bn);
-        const double full = std::floor(n / (c * o.per_cu)), rest = n - full * c * o.per_cu;
-        const double cost = (full * o.per_cu + std::ceil(rest / c)) * o.bm * o.bn / o.eff;
-        if (cost < best) { best = cost; bm = o.bm; bn = o.bn; }
-    }
+double round_cost(int64_t n, int bm, int bn, double eff, int per_cu, int cus) {
+    const double c = cus > 0 ? cus : 256;
+    const double full = std::floor((double)n / (c * per_cu)), rest = (double)n - full * c * per_cu;
+    return (full * per_cu + std::ceil(rest / c)) * bm * bn / eff;
 }
 
-// FP32 direct-copy kernel on the whole bt x bt tiles of C, the register-staged kernel on
-// the partial strips along the bottom and right edges (same stream, disjoint parts of C).
-hipError_t launch_f32_dma_split(const Problem& p, const Launch& l, int bt, int cus) {
-    const int mf = p.M / bt * bt, nf = p.N / bt * bt;
-    Problem core = p;
-    core.M = mf;
-    core.N = nf;
-    Launch lc = l;
-    lc.group_m = pick_group_m(mf / bt, nf / bt);
-    hipError_t err = launch_f32_dma(core, lc, bt, bt);
-    auto strip = [&](Problem s) {
-        if (err != hipSuccess) return;
-        int bm = 128, bn = 128;
-        pick_tile(kF32Tiles, s.M, s.N, cus, bm, bn);
-        Launch ls = l;
-        ls.group_m = pick_group_m((s.M + bm - 1) / bm, (s.N + bn - 1) / bn);
-        err = launch_f32_mfma(s, ls, bm);
-    };
-    const float* A = static_cast<const float*>(p.A);
-    const float* B = static_cast<const float*>(p.B);
-    if (mf < p.M) {          // rows mf .. M-1, all columns
-        Problem s = p;
-        s.M = p.M - mf;
-        s.A = A + (p.oa == kRow ? (int64_t)mf * p.lda : (int64_t)mf);
-        s.C = p.C + (int64_t)mf * p.ldc;
-        strip(s);
+// A kernel's launch over a core of C (rows 0 .. mc-1, columns 0 .. nc-1) plus the strips
+// that complete it.  Along an edge the kernel may overhang (part_m / part_n) its last tiles
+// either overhang or the core stops at the last whole tile and the rest runs as a strip
+// (a separate GEMM, priced as 64 x 64 tiles); along any other edge the core stops at the
+// last whole tile.  4095 x 4097 on 256^2 tiles: 16 x 16 tiles (one round) and a one-column
+// strip, against 16 x 17 tiles (two rounds).
+struct Plan {
+    TileOpt opt{};
+    int mc = 0, nc = 0;
+    double cost = 1e300;
+};
+
+Plan plan_core(const Problem& p, const TileOpt& o, bool part_m, bool part_n, int cus, double strip_eff) {
+    Plan best;
+    best.opt = o;
+    for (int cm = 0; cm < 2; ++cm) {
+        if (cm == 0 && !part_m) continue;
+        const int mc = cm == 0 ? p.M : p.M / o.bm * o.bm;
+        for (int cn = 0; cn < 2; ++cn) {
+            if (cn == 0 && !part_n) continue;
+            const int nc = cn == 0 ? p.N : p.N / o.bn * o.bn;
+            if (mc == 0 || nc == 0) continue;
+            double c = round_cost(tiles(mc, nc, o.bm, o.bn), o.bm, o.bn, o.eff, o.per_cu, cus);
+            if (mc < p.M) c += round_cost(tiles(p.M - mc, p.N, 64, 64), 64, 64, strip_eff, 4, cus);
+            if (nc < p.N) c += round_cost(tiles(mc, p.N - nc, 64, 64), 64, 64, strip_eff, 4, cus);
+            if (c < best.cost) { best.cost = c; best.mc = mc; best.nc = nc; }
+        }
     }
-    if (nf < p.N) {          // rows 0 .. mf-1, columns nf .. N-1
-        Problem s = p;
-        s.M = mf;
-        s.N = p.N - nf;
-        s.B = B + (p.ob == kCol ? (int64_t)nf * p.ldb : (int64_t)nf);
-        s.C = p.C + nf;
-        strip(s);
-    }
+    return best;
+}
+
+// A kernel that takes any shape: the whole of C is its core.
+Plan plan_whole(const Problem& p, const TileOpt& o, int cus) {
+    Plan pl;
+    pl.opt = o;
+    pl.mc = p.M;
+    pl.nc = p.N;
+    pl.cost = round_cost(tiles(p.M, p.N, o.bm, o.bn), o.bm, o.bn, o.eff, o.per_cu, cus);
+    return pl;
+}
+
+// Options for a (sub-)problem whose C starts at p.C: 16-byte stores need an aligned C and
+// ldc; 16-byte loads and global->LDS copies need only element alignment on gfx950.
+Launch launch_for(const Problem& p, hipStream_t stream) {
+    Launch o{};
+    o.stream = stream;
+    o.vec_a = o.vec_b = true;
+    o.vec_c = (p.ldc % 4 == 0) && aligned(p.C, 16);
+    return o;
+}
+
+// Sub-problem: rows r0 .. r0+m-1 and columns c0 .. c0+n-1 of C (row-major C).
+Problem sub_problem(const Problem& p, int r0, int m, int c0, int n, int elem) {
+    Problem s = p;
+    s.M = m;
+    s.N = n;
+    const char* A = static_cast<const char*>(p.A);
+    const char* B = static_cast<const char*>(p.B);
+    s.A = A + (p.oa == kRow ? (int64_t)r0 * p.lda : (int64_t)r0) * elem;
+    s.B = B + (p.ob == kCol ? (int64_t)c0 * p.ldb : (int64_t)c0) * elem;
+    s.C = p.C + (int64_t)r0 * p.ldc + c0;
+    return s;
+}
+
+hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, bool f32, const DeviceInfo& dev,
+                    const char*& name, gemm_status_t& st);
+
+// Run a plan's core with `core` and its strips through the default choice, on one stream.
+template <typename CoreFn>
+hipError_t run_plan(const Problem& p, hipStream_t stream, const Plan& pl, bool f32, const DeviceInfo& dev,
+                    CoreFn core) {
+    const int e = f32 ? 4 : 2;
+    const Problem c = sub_problem(p, 0, pl.mc, 0, pl.nc, e);
+    Launch lc = launch_for(c, stream);
+    lc.group_m = pick_group_m((c.M + pl.opt.bm - 1) / pl.opt.bm, (c.N + pl.opt.bn - 1) / pl.opt.bn);
+    hipError_t err = core(c, lc);
+    const char* ignored = nullptr;
+    gemm_status_t st = GEMM_OK;
+    if (err == hipSuccess && pl.mc < p.M)        // rows mc .. M-1, all columns
+        err = dispatch(sub_problem(p, pl.mc, p.M - pl.mc, 0, p.N, e), stream, GEMM_ALGO_AUTO, f32, dev, ignored, st);
+    if (err == hipSuccess && pl.nc < p.N)        // rows 0 .. mc-1, columns nc .. N-1
+        err = dispatch(sub_problem(p, 0, pl.mc, pl.nc, p.N - pl.nc, e), stream, GEMM_ALGO_AUTO, f32, dev, ignored, st);
     return err;
+}
+
+const char* f32_name(const TileOpt& o) {
+    if (o.dma) return o.bm == 256 ? "f32_dma256x256" : "f32_dma128x128";
+    return o.bm == 64 ? "f32_mfma64x64" : "f32_mfma128x128";
+}
+const char* bf16_name(const TileOpt& o) {
+    if (o.dma) return o.bn == 256 ? "bf16_dma256x256" : "bf16_dma256x128";
+    static const char* names[] = {"bf16_mfma256x256", "bf16_mfma256x128", "bf16_mfma128x128", "bf16_mfma64x64"};
+    return names[o.bm == 256 ? (o.bn == 256 ? 0 : 1) : (o.bm == 128 ? 2 : 3)];
+}
+
+// The FP32 matrix-core kernels: the cheapest plan over the allowed options.
+hipError_t run_f32_tiles(const Problem& p, hipStream_t stream, gemm_algo_t algo, const DeviceInfo& dev,
+                         const char*& name, gemm_status_t& st) {
+    const Launch l = launch_for(p, stream);
+    const bool part_m = p.oa == kRow, part_n = p.ob == kCol;   // k-contiguous operands
+    Plan best;
+    auto consider = [&](const Plan& pl) { if (pl.cost < best.cost) best = pl; };
+    const bool any = algo == GEMM_ALGO_AUTO || algo == GEMM_ALGO_MFMA;
+    for (const TileOpt& o : kF32DmaOpts) {
+        const bool want = any || algo == GEMM_ALGO_MFMA_DMA || (algo == GEMM_ALGO_MFMA_256x256 && o.bm == 256);
+        if (want && f32_dma_applies(p, l, o.bm, o.bn))
+            consider(plan_core(p, o, part_m, part_n, dev.cus, kF32StripEff));
+    }
+    for (const TileOpt& o : kF32MfmaOpts) {
+        const bool want = any || (algo == GEMM_ALGO_MFMA_128x128 && o.bm == 128) ||
+                          (algo == GEMM_ALGO_MFMA_64x64 && o.bm == 64);
+        if (want) consider(plan_whole(p, o, dev.cus));
+    }
+    if (best.cost >= 1e300) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
+    name = f32_name(best.opt);
+    const TileOpt o = best.opt;
+    return run_plan(p, stream, best, true, dev, [&](const Problem& c, const Launch& lc) {
+        return o.dma ? launch_f32_dma(c, lc, o.bm, o.bn) : launch_f32_mfma(c, lc, o.bm);
+    });
+}
+
+// The BF16 tile kernels: the direct-copy kernel where it applies (any M, N: its tiles may
+// overhang both edges), else, or for an explicitly chosen tile, the register-staged kernels.
+hipError_t run_bf16_tiles(const Problem& p, hipStream_t stream, gemm_algo_t algo, const DeviceInfo& dev,
+                          const char*& name, gemm_status_t& st) {
+    const Launch l = launch_for(p, stream);
+    const bool dma = bf16_dma_applies(p, l, 256, 256);
+    Plan best;
+    auto consider = [&](const Plan& pl) { if (pl.cost < best.cost) best = pl; };
+    const bool any = algo == GEMM_ALGO_AUTO || algo == GEMM_ALGO_MFMA;
+    if (dma && (any || algo == GEMM_ALGO_MFMA_DMA))
+        for (const TileOpt& o : kBf16DmaOpts) consider(plan_core(p, o, true, true, dev.cus, kBf16StripEff));
+    for (const TileOpt& o : kBf16MfmaOpts) {
+        // with the direct-copy kernel available, the default choice leaves the 256-row tiles to it
+        const bool want = (any && !(dma && o.bm == 256)) ||
+                          (algo == GEMM_ALGO_MFMA_256x256 && o.bm == 256 && o.bn == 256) ||
+                          (algo == GEMM_ALGO_MFMA_256x128 && o.bm == 256 && o.bn == 128) ||
+                          (algo == GEMM_ALGO_MFMA_128x128 && o.bm == 128) || (algo == GEMM_ALGO_MFMA_64x64 && o.bm == 64);
+        if (want) consider(plan_whole(p, o, dev.cus));
+    }
+    if (best.cost >= 1e300) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
+    name = bf16_name(best.opt);
+    const TileOpt o = best.opt;
+    return run_plan(p, stream, best, false, dev, [&](const Problem& c, const Launch& lc) {
+        return o.dma ? launch_bf16_dma(c, lc, o.bm, o.bn) : launch_bf16_mfma(c, lc, o.bm, o.bn);
+    });
+}
+
+// Kernel choice and launch for a normalised problem (row-major C, K > 0).  A status other
+// than GEMM_OK in `st` means the request is invalid (nothing launched).
+hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, bool f32, const DeviceInfo& dev,
+                    const char*& name, gemm_status_t& st) {
+    Launch l = launch_for(p, stream);
+    if (f32) {
+        switch (algo) {
+            case GEMM_ALGO_NAIVE_UNCOALESCED: name = "f32_naive_uncoalesced"; return launch_naive(p, l, false);
+            case GEMM_ALGO_NAIVE: name = "f32_naive"; return launch_naive(p, l, true);
+            case GEMM_ALGO_TILED: name = "f32_tiled32"; return launch_tiled(p, l);
+            case GEMM_ALGO_REGBLOCK:
+                l.group_m = pick_group_m((p.M + kRegblockBM - 1) / kRegblockBM, (p.N + kRegblockBN - 1) / kRegblockBN);
+                name = "f32_regblock128x128";
+                return launch_regblock(p, l);
+            case GEMM_ALGO_SKINNY:
+                if (!skinny_applies(p, false)) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
+                return run_skinny(p, l, false, dev.cus, name);
+            default:
+                if (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus, true) && skinny_applies(p, false))
+                    return run_skinny(p, l, false, dev.cus, name);
+                return run_f32_tiles(p, stream, algo, dev, name, st);
+        }
+    }
+    if (algo == GEMM_ALGO_SKINNY ||
+        (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus, false) && skinny_applies(p, true))) {
+        if (!skinny_applies(p, true)) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
+        return run_skinny(p, l, true, dev.cus, name);
+    }
+    if (algo == GEMM_ALGO_MFMA_PINGPONG) {
+        if (!bf16_pingpong_applies(p, l)) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
+        l.group_m = pick_group_m(p.M / 256, p.N / 256);
+        name = "bf16_pingpong256x256";
+        return launch_bf16_pingpong(p, l);
+    }
+    return run_bf16_tiles(p, stream, algo, dev, name, st);
 }
 
 template <typename Elem>
@@ -191,115 +336,15 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
     } else {
         p = Problem{(int)N, (int)M, (int)K, B, ldb, 1 - (int)ob, A, lda, 1 - (int)oa, C, ldc};
     }
-    Launch l{};
-    l.stream = stream;
-    // 16-byte loads and global->LDS copies need only element alignment on gfx950
-    l.vec_a = l.vec_b = true;
-    l.vec_c = (p.ldc % 4 == 0) && aligned(p.C, 16);
-
     hipError_t err = hipSuccess;
     const char* name = "none";
     if (K == 0) {
-        err = launch_zero_c(p, l);
+        err = launch_zero_c(p, launch_for(p, stream));
         name = "zero_c";
-    } else if (f32) {
-        switch (algo) {
-            case GEMM_ALGO_NAIVE_UNCOALESCED:
-                err = launch_naive(p, l, false); name = "f32_naive_uncoalesced"; break;
-            case GEMM_ALGO_NAIVE:
-                err = launch_naive(p, l, true); name = "f32_naive"; break;
-            case GEMM_ALGO_TILED:
-                err = launch_tiled(p, l); name = "f32_tiled32"; break;
-            case GEMM_ALGO_REGBLOCK: {
-                l.group_m = pick_group_m((p.M + kRegblockBM - 1) / kRegblockBM,
-                                         (p.N + kRegblockBN - 1) / kRegblockBN);
-                err = launch_regblock(p, l); name = "f32_regblock128x128"; break;
-            }
-            case GEMM_ALGO_SKINNY:
-                if (!skinny_applies(p, false)) return GEMM_ERR_INVALID_VALUE;
-                err = run_skinny(p, l, false, dev.cus, name); break;
-            default: {
-                if (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus, true) && skinny_applies(p, false)) {
-                    err = run_skinny(p, l, false, dev.cus, name); break;
-                }
-                // direct-copy kernel (tiles 256 or 128) where it applies, else register-staged
-                const bool dma256 = f32_dma_applies(p, l, 256, 256);
-                const bool dma128 = f32_dma_applies(p, l, 128, 128);
-                int bm = 128, bn = 128;
-                bool dma = false;
-                if (algo == GEMM_ALGO_MFMA_64x64) {
-                    bm = bn = 64;
-                } else if (algo == GEMM_ALGO_MFMA_128x128) {
-                    bm = bn = 128;
-                } else if (algo == GEMM_ALGO_MFMA_256x256) {
-                    if (!dma256) return GEMM_ERR_INVALID_VALUE;
-                    bm = bn = 256;
-                    dma = true;
-                } else if (algo == GEMM_ALGO_MFMA_DMA) {
-                    if (!dma128) return GEMM_ERR_INVALID_VALUE;
-                    bm = bn = 128;
-                    if (dma256) pick_tile(kF32DmaTiles, p.M, p.N, dev.cus, bm, bn);
-                    if (bm != 256) bm = bn = 128;
-                    dma = true;
-                } else if (dma128) {
-                    pick_tile(kF32DmaTiles, p.M, p.N, dev.cus, bm, bn);
-                    if (bm == 256 && !dma256) bm = bn = 128;
-                    dma = bm >= 128;
-                } else {
-                    pick_tile(kF32Tiles, p.M, p.N, dev.cus, bm, bn);
-                }
-                if (dma) {
-                    err = launch_f32_dma_split(p, l, bm, dev.cus);
-                    name = bm == 256 ? "f32_dma256x256" : "f32_dma128x128";
-                    break;
-                }
-                l.group_m = pick_group_m((p.M + bm - 1) / bm, (p.N + bn - 1) / bn);
-                err = launch_f32_mfma(p, l, bm);
-                name = bm == 64 ? "f32_mfma64x64" : "f32_mfma128x128";
-                break;
-            }
-        }
-    } else if (algo == GEMM_ALGO_SKINNY ||
-               (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus, false) && skinny_applies(p, true))) {
-        if (!skinny_applies(p, true)) return GEMM_ERR_INVALID_VALUE;
-        err = run_skinny(p, l, true, dev.cus, name);
-    } else if (algo == GEMM_ALGO_MFMA_PINGPONG) {
-        if (!bf16_pingpong_applies(p, l)) return GEMM_ERR_INVALID_VALUE;
-        l.group_m = pick_group_m(p.M / 256, p.N / 256);
-        err = launch_bf16_pingpong(p, l);
-        name = "bf16_pingpong256x256";
     } else {
-        int bm = 256, bn = 256;
-        const bool dma = bf16_dma_applies(p, l, bm, bn);
-        switch (algo) {
-            case GEMM_ALGO_MFMA_256x256: bm = 256; bn = 256; break;
-            case GEMM_ALGO_MFMA_256x128: bm = 256; bn = 128; break;
-            case GEMM_ALGO_MFMA_128x128: bm = 128; bn = 128; break;
-            case GEMM_ALGO_MFMA_64x64: bm = 64; bn = 64; break;
-            case GEMM_ALGO_MFMA_DMA:
-                if (!dma) return GEMM_ERR_INVALID_VALUE;
-                pick_tile(kBf16DmaTiles, p.M, p.N, dev.cus, bm, bn);
-                break;
-            default:
-                // the direct-copy kernel's tiles where it applies, else the register-staged
-                // / direct kernel of bf16_mfma.hip
-                if (dma) pick_tile(kBf16AnyTiles, p.M, p.N, dev.cus, bm, bn);
-                else pick_tile(kBf16Tiles, p.M, p.N, dev.cus, bm, bn);
-                break;
-        }
-        // an explicitly chosen tile runs on bf16_mfma.hip
-        const bool use_dma = algo == GEMM_ALGO_MFMA_DMA || ((algo == GEMM_ALGO_AUTO || algo == GEMM_ALGO_MFMA) &&
-                                                            dma && bm == 256);
-        l.group_m = pick_group_m((p.M + bm - 1) / bm, (p.N + bn - 1) / bn);
-        if (use_dma) {
-            err = launch_bf16_dma(p, l, bm, bn);
-            name = bn == 256 ? "bf16_dma256x256" : "bf16_dma256x128";
-        } else {
-            err = launch_bf16_mfma(p, l, bm, bn);
-            static const char* names[] = {"bf16_mfma256x256", "bf16_mfma256x128", "bf16_mfma128x128",
-                                          "bf16_mfma64x64"};
-            name = names[bm == 256 ? (bn == 256 ? 0 : 1) : (bm == 128 ? 2 : 3)];
-        }
+        gemm_status_t bad = GEMM_OK;
+        err = dispatch(p, stream, algo, f32, dev, name, bad);
+        if (bad != GEMM_OK) return bad;
     }
     if (err != hipSuccess) {
         t_last_hip_error = (int)err;

@@ -141,15 +141,18 @@ void k_bf16_dma(Problem p, int tiles_m, int tiles_n, int group_m) {
     // copy j (of DMA) of k-tile kt (source) into stage st.  (The LDS pointer is a named
     // variable: cast inline in the builtin's argument list, the host pass of this compiler
     // silently drops the kernel's launch stub.)
+    // The copy's row block is part of the lane offset, the k-tile the scalar offset: rows past
+    // the buffer's range then read as zero whether or not the range check counts the scalar
+    // offset (a k offset stays inside its row).
     auto issue_one = [&](int j, int kt, int st) {
         unsigned char* s = smem + st * C::STAGE;
         if (j < C::A_DMA) {
             lds_void* dst = (lds_void*)(s + (wave * C::A_DMA + j) * 1024);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, aoff[j & 1], j * astep + kt * (BK * 2), 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, aoff[j & 1] + j * astep, kt * (BK * 2), 0, 0);
         } else {
             const int jb = j - C::A_DMA;
             lds_void* dst = (lds_void*)(s + C::A_BYTES + (wave * C::B_DMA + jb) * 1024);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, boff[jb & 1], jb * bstep + kt * (BK * 2), 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, boff[jb & 1] + jb * bstep, kt * (BK * 2), 0, 0);
         }
     };
     // the copies that fall on slot `slot` of the window (copy q sits at slot q W / DMA)

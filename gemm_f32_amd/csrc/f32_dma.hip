@@ -31,11 +31,23 @@
 //    Two stages; the copies of k-tile kt + 2 are spread over the second k-group of tile kt
 //    and the first of tile kt + 1, one barrier per k-tile (see the main loop).
 //  * Tile order from the XCD-aware, group-M scheduler in common.hpp.
+//  * Edges: k_f32_dma_edge, the same kernel except at three points, lets tiles overhang M
+//    where A is row-major and N where B is column-major (the k-contiguous operands): a
+//    copy row past the edge is fetched from the last row that exists (it only reaches rows
+//    or columns of C that are not stored), the K tail zero-fills such rows, and stores past
+//    M or N are skipped.  Problems of whole tiles run k_f32_dma, whose source is kept as it
+//    was measured: the same changes made inside it (as a template flag, or unconditionally)
+//    cost 4% at 4096^3 through the compiler's register assignment and scheduling of the
+//    k-loop, with the loop's instructions unchanged.
 //
-// Requirements (checked by the host): K >= BK, M and N multiples of the block tile.  Rows
-// need element alignment only: gfx950's global->LDS copies accept unaligned sources.  A K tail takes
-// one more k-tile loaded with bounds checks.  The host runs the whole-tile part of a ragged
-// problem here and the edge strips with f32_mfma.hip.
+// Requirements (checked by the host): K >= BK; M a multiple of the block tile unless A is
+// row-major, N unless B is column-major (k_f32_dma: both multiples); a k-contiguous
+// operand's copy block (32 rows) below 2^31 bytes.  Rows need element alignment only:
+// gfx950's global->LDS copies accept unaligned sources.  A K tail takes one more k-tile
+// loaded with bounds checks.  The host runs the rest of a ragged problem (strips along the
+// other edges) as separate GEMMs.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -343,12 +355,297 @@ void k_f32_dma(Problem p, int tiles_m, int tiles_n, int group_m) {
         }
 }
 
+// k_f32_dma_edge's plan for one operand: a k-contiguous operand gets one lane offset per
+// copy, so that a row past `limit` (M or N) can be replaced by the last row that exists; a
+// row-contiguous one is planned as in CopyPlan (its edge is never overhung).
+template <bool KC, int R, int NW>
+struct EdgeCopyPlan {
+    static constexpr int NJ = KC ? R / NW / 8 : 1;
+    CopyPlan<KC, R, NW> rc;     // row-contiguous operand
+    const char* base;
+    unsigned off[NJ];
+
+    __device__ void init(const float* p, int64_t ld, int x0, int limit, int wave, int lane) {
+        if (KC) {
+            const int row0 = x0 + wave * (R / NW);
+            const int first = min(row0, limit - 1);       // a row that exists
+            base = reinterpret_cast<const char*>(p + (int64_t)first * ld);
+            const int lr = lane / 8;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int c = (lane % 8) ^ swz8(lr + 8 * (j & 1));
+                const int row = min(row0 + 8 * j + lr, limit - 1);
+                off[j] = (unsigned)(((row - first) * ld + c * 4) * 4);
+            }
+        } else {
+            rc.init(p, ld, x0, wave, lane);
+        }
+    }
+    // source of copy j of k-tile kt
+    __device__ const char* src(int j, int kt) const {
+        if (KC) return base + kt * (BK * 4) + off[j];
+        return rc.base + kt * rc.kstep + j * rc.step + rc.off[0];
+    }
+};
+
+template <typename C>
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void k_f32_dma_edge(Problem p, int tiles_m, int tiles_n, int group_m) {
+    constexpr int BM = C::BM, BN = C::BN, S = C::S, FM = C::FM, FN = C::FN;
+    constexpr bool A_KC = C::A_KC, B_KC = C::B_KC;
+    __shared__ __align__(16) unsigned char smem[S * C::STAGE];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = (wave / C::WGN) * C::WM, wn = (wave % C::WGN) * C::WN;
+    const int nk = p.K / BK;
+    const float* A = static_cast<const float*>(p.A);
+    const float* B = static_cast<const float*>(p.B);
+
+    // ---- copies: rows of a k-contiguous operand past M (N) come from its last row
+    EdgeCopyPlan<A_KC, BM, C::NW> ca;
+    EdgeCopyPlan<B_KC, BN, C::NW> cb;
+    ca.init(A, p.lda, m0, p.M, wave, lane);
+    cb.init(B, p.ldb, n0, p.N, wave, lane);
+    // LDS: stage st = [A tile | B tile]; wavefront w's copies fill 1 KB blocks
+    // w * X_DMA .. +X_DMA-1 of each tile
+    auto issue_one = [&](int j, int kt, int st) {
+        unsigned char* s = smem + st * C::STAGE;
+        if (j < C::A_DMA) {
+            const char* src = ca.src(j, kt);
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(s + (wave * C::A_DMA + j) * 1024), 16, 0, 0);
+        } else {
+            const int jb = j - C::A_DMA;
+            const char* src = cb.src(jb, kt);
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(s + C::A_BYTES + (wave * C::B_DMA + jb) * 1024),
+                                             16, 0, 0);
+        }
+    };
+
+    // ---- fragments of one k-group and the matrix instructions on them ----
+    const int li = lane & 15, g = lane >> 4;
+    // k-contiguous: block i's row wm + 16 i + li; swizzle depends on li only
+    const int a_kc_off = (wm + li) * KC_ROW, b_kc_off = C::A_BYTES + (wn + li) * KC_ROW;
+    const int sw = swz8(li);
+    // row-contiguous: k-row 16 t + 4 g + e, columns x0 + 64 q + 4 li
+    const int a_rc_off = (4 * g * BM + wm + 4 * li) * 4;
+    const int b_rc_off = C::A_BYTES + (4 * g * BN + wn + 4 * li) * 4;
+
+    struct Frags { f32x4 a[C::A_RD]; f32x4 b[C::B_RD]; };
+    auto read_group = [&](const unsigned char* st, int t, Frags& f) {
+        if (A_KC) {
+            const int coff = ((4 * t + g) ^ sw) << 4;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                f.a[i] = *reinterpret_cast<const f32x4*>(st + a_kc_off + i * 16 * KC_ROW + coff);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int q = 0; q < FM / 4; ++q)
+                    f.a[e * (FM / 4) + q] =
+                        *reinterpret_cast<const f32x4*>(st + a_rc_off + ((16 * t + e) * BM + 64 * q) * 4);
+        }
+        if (B_KC) {
+            const int coff = ((4 * t + g) ^ sw) << 4;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                f.b[j] = *reinterpret_cast<const f32x4*>(st + b_kc_off + j * 16 * KC_ROW + coff);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int q = 0; q < FN / 4; ++q)
+                    f.b[e * (FN / 4) + q] =
+                        *reinterpret_cast<const f32x4*>(st + b_rc_off + ((16 * t + e) * BN + 64 * q) * 4);
+        }
+    };
+    // operand of block i (j) at step e
+    auto a_val = [&](const Frags& f, int i, int e) -> float {
+        return A_KC ? f.a[i][e] : f.a[e * (FM / 4) + i / 4][i % 4];
+    };
+    auto b_val = [&](const Frags& f, int j, int e) -> float {
+        return B_KC ? f.b[j][e] : f.b[e * (FN / 4) + j / 4][j % 4];
+    };
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // One k-group: 4 steps x FM x FN matrix instructions on the fragments in f; `slot(n)` is
+    // called before the n-th instruction so that the caller can place copies and the reads
+    // of the next fragments among them.  Source order is issue order (sched_barrier).
+    auto group = [&](const Frags& f, auto slot) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    slot((e * FM + i) * FN + j);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_val(f, i, e), b_val(f, j, e), acc[i][j], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+    };
+
+    // ---- software pipeline over k-tiles, two LDS stages.  Iteration kt multiplies tile kt
+    // (stage kt % 2) as two k-groups; group 1's fragments are read under group 0's matrix
+    // instructions.  The barrier before group 1 publishes tile kt+1 (every wavefront has
+    // waited for its own copies of it) and frees stage kt % 2 (every wavefront's reads of
+    // it have completed): during group 1 each wavefront reads group 0 of tile kt+1 and
+    // starts the copies of tile kt+2 into the freed stage; they continue through group 0
+    // of iteration kt+1 and have until its barrier to land.  So neither the barrier nor the
+    // first LDS reads of a tile leave the matrix pipe without work.  Past the end of K the
+    // copies repeat the last tile into a stage nobody reads and the fragments read for a
+    // tile nk are never used: the loop body has no branch (a branch among the matrix
+    // instructions costs more than the extra copies of one k-tile).
+    static_assert(S == 2, "two-stage pipeline");
+    constexpr int G = C::MFMA_PER_GROUP, W = 2 * G;    // copy window: two k-groups
+    constexpr int SP = W / C::DMA;                      // one copy every SP instructions
+    static_assert(W % C::DMA == 0, "copies evenly spread over the window");
+    // the copy that falls on slot `n` of the window, if any
+    auto copies_at = [&](int n, int kt, int st) {
+        if (n % SP == 0) issue_one(n / SP, kt, st);
+    };
+    const int last = nk - 1;
+    Frags f[2];
+#pragma unroll
+    for (int j = 0; j < C::DMA; ++j) issue_one(j, 0, 0);
+#pragma unroll
+    for (int n = 0; n < G; ++n) copies_at(n, min(1, last), 1);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    read_group(smem, 0, f[0]);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int st = kt & 1;
+        const int k1 = min(kt + 1, last), k2 = min(kt + 2, last);
+        group(f[0], [&](int n) {
+            copies_at(G + n, k1, st ^ 1);
+            if (n == 0) read_group(smem + st * C::STAGE, 1, f[1]);
+        });
+        // own copies of tile kt+1 landed, own reads of stage st complete; a plain barrier
+        // (__syncthreads() would also wait for the copies still in flight)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        group(f[1], [&](int n) {
+            copies_at(n, k2, st);
+            if (n == 0) read_group(smem + (st ^ 1) * C::STAGE, 0, f[0]);
+        });
+    }
+    // the surplus copies must land before the workgroup's LDS is reused or released
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+
+    // ---- K tail (K not a multiple of BK): one more k-tile, staged through registers with
+    // bounds checks and zero fill into the same LDS positions the copies would fill ----
+    if (p.K % BK != 0) {                       // uniform
+        __syncthreads();                       // every wavefront is done reading LDS
+        const int k0 = nk * BK;
+#pragma unroll
+        for (int j = 0; j < C::DMA; ++j) {
+            const bool is_a = j < C::A_DMA;
+            const int jj = is_a ? j : j - C::A_DMA;
+            const bool kc = is_a ? A_KC : B_KC;
+            const float* src = is_a ? A : B;
+            const int64_t ld = is_a ? p.lda : p.ldb;
+            const int x0 = is_a ? m0 : n0, R = is_a ? BM : BN, limit = is_a ? p.M : p.N;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (kc) {
+                // tile row r, logical chunk (lane % 8) ^ s(r): k = k0 + 4 c .. +3; rows past
+                // the edge stay zero
+                const int r = wave * (R / C::NW) + 8 * jj + lane / 8;
+                const int k = k0 + 4 * ((lane % 8) ^ swz8(r));
+                const float* q = src + (int64_t)min(x0 + r, limit - 1) * ld + k;
+                if (x0 + r >= limit) {
+                } else if (k + 3 < p.K) v = load16f(q);
+                else {
+                    if (k < p.K) v.x = q[0];
+                    if (k + 1 < p.K) v.y = q[1];
+                    if (k + 2 < p.K) v.z = q[2];
+                }
+            } else {
+                // k-row k0 + w BK/NW + RPC jj + lane / LPR, columns x0 + 4 (lane % LPR) .. +3
+                const int lpr = R / 4, rpc = 64 / lpr;
+                const int kr = k0 + wave * (BK / C::NW) + rpc * jj + lane / lpr;
+                if (kr < p.K) v = load16f(src + (int64_t)kr * ld + x0 + 4 * (lane % lpr));
+            }
+            unsigned char* dst = smem + (is_a ? (wave * C::A_DMA + jj) * 1024
+                                              : C::A_BYTES + (wave * C::B_DMA + jj) * 1024) + 16 * lane;
+            *reinterpret_cast<float4*>(dst) = v;
+        }
+        __syncthreads();
+        read_group(smem, 0, f[0]);
+        group(f[0], [&](int n) {
+            if (n == 0) read_group(smem, 1, f[1]);
+        });
+        group(f[1], [](int) {});
+    }
+
+    // ---- epilogue: block (i, j), lane l, register v: block row 4 (l / 16) + v, block
+    // column l % 16, mapped back through the operand layouts; on a tile that overhangs an
+    // edge, rows and columns past it are not stored (interior tiles skip the checks) ----
+    const bool vec_c = (p.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0;
+    auto store = [&](auto guard) {
+        constexpr bool G = decltype(guard)::value;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int br = 4 * g + v;
+                const int row = m0 + wm + (A_KC ? 16 * i + br : 4 * br + i % 4 + 64 * (i / 4));
+                if (G && row >= p.M) continue;
+                float* crow = p.C + (int64_t)row * p.ldc;
+                if (B_KC) {
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const int col = n0 + wn + 16 * j + li;
+                        if (!G || col < p.N) crow[col] = acc[i][j][v];
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < FN / 4; ++q) {
+                        const int col = n0 + wn + 64 * q + 4 * li;
+                        const f32x4 val = {acc[i][4 * q][v], acc[i][4 * q + 1][v], acc[i][4 * q + 2][v],
+                                           acc[i][4 * q + 3][v]};
+                        if (vec_c && (!G || col + 3 < p.N)) {
+                            *reinterpret_cast<f32x4*>(crow + col) = val;
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (!G || col + e < p.N) crow[col + e] = val[e];
+                        }
+                    }
+                }
+            }
+    };
+    if (m0 + BM <= p.M && n0 + BN <= p.N) store(std::false_type{});    // uniform
+    else store(std::true_type{});
+}
+
 template <int BM, int BN, int WGM, int WGN, int S>
 hipError_t launch_cfg(const Problem& p, const Launch& l) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const dim3 grid((unsigned)tiles_m * tiles_n), block(64 * WGM * WGN);
     const bool akc = p.oa == kRow, bkc = p.ob == kCol;
     const int g = l.group_m;
+    // tiles may overhang only the k-contiguous operands' edges
+    const bool over_m = p.M % BM != 0, over_n = p.N % BN != 0;
+    if ((over_m && !akc) || (over_n && !bkc)) return hipErrorInvalidValue;
+    if (over_m || over_n) {
+        if (akc && bkc)
+            hipLaunchKernelGGL((k_f32_dma_edge<Cfg<BM, BN, WGM, WGN, S, true, true>>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
+        else if (akc)
+            hipLaunchKernelGGL((k_f32_dma_edge<Cfg<BM, BN, WGM, WGN, S, true, false>>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
+        else
+            hipLaunchKernelGGL((k_f32_dma_edge<Cfg<BM, BN, WGM, WGN, S, false, true>>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
+        return hipGetLastError();
+    }
     if (akc && bkc)
         hipLaunchKernelGGL((k_f32_dma<Cfg<BM, BN, WGM, WGN, S, true, true>>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
     else if (akc)
@@ -363,7 +660,11 @@ hipError_t launch_cfg(const Problem& p, const Launch& l) {
 }  // namespace
 
 bool f32_dma_applies(const Problem& p, const Launch& l, int bm, int bn) {
-    // the whole-tile part must be non-empty; the host sends partial tiles elsewhere
+    // a k-contiguous operand's copy block (32 rows at both tile sizes) within 32-bit lane
+    // offsets
+    const int64_t rows = 32, lim = (int64_t)1 << 31;
+    if ((p.oa == kRow && rows * p.lda * 4 >= lim) || (p.ob == kCol && rows * p.ldb * 4 >= lim)) return false;
+    // at least one whole tile along each edge (the host plans overhangs and strips)
     return l.vec_a && l.vec_b && p.K >= BK && p.M >= bm && p.N >= bn;
 }
 

@@ -38,9 +38,11 @@ constexpr int kSkinnyMaxM = 64;
 #endif
 constexpr int kSkinnyWaves = GEMM_SKINNY_WAVES;   // wavefronts splitting K in a workgroup
 bool skinny_applies(const Problem& p, bool bf16);
-// column blocks of 16 per workgroup (1 or 4) for a problem on `cus` CUs
+// column blocks of 16 per workgroup (1 or 4) and row strips of 16 per workgroup (1 .. 4)
+// for a problem on `cus` CUs
 int skinny_blocks(const Problem& p, int cus);
-hipError_t launch_skinny(const Problem& p, const Launch& l, bool bf16, int fn);
+int skinny_strips(const Problem& p, int fn, int cus);
+hipError_t launch_skinny(const Problem& p, const Launch& l, bool bf16, int fn, int fm);
 // C = 0 for K == 0 (fill.hip)
 hipError_t launch_zero_c(const Problem& p, const Launch& l);
 

@@ -7,9 +7,11 @@
 // rungs" (split-K): divide K among workers and combine the partial sums in a second step.
 // Design for MI355X:
 //
-//  * a workgroup owns 16 FN columns n0 .. and 64 rows m0 .. m0+63 of C (fewer when M is
-//    smaller: 16 FM rows); FN = 4 (64 x 64) when that still gives every CU a workgroup
-//    (1000 x 1000: 16 x 16), else FN = 1 (16 x 4096: 256 workgroups of 16 x 16);
+//  * a workgroup owns 16 FN columns n0 .. and 16 FM rows m0 .. of C: FN = 4 (64 columns)
+//    when that still gives every CU a workgroup (1000 x 1000: 16 x 16), else FN = 1
+//    (16 x 4096: 256 workgroups of 16 x 16); FM = 4 (64 rows), or fewer when M is smaller
+//    or when fewer rows per block are needed to give every CU one (a 4095 x 1 column:
+//    256 blocks of 16 rows);
 //  * its 8 wavefronts split K among themselves (split-K inside the workgroup: batches of
 //    k-steps dealt in turn) and each streams its batches of those columns of B and of the
 //    FM 16-row strips of A (A stays in L2) straight from global memory into registers -- no LDS staging in
@@ -132,10 +134,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(Problem p, int vec_a, int
 
     // (row block, column slab): the workgroups one XCD receives cover all row blocks of a
     // run of neighbouring slabs (which share 128-byte lines of a row-major B)
-    const int slabs = (p.N + BNW - 1) / BNW, rblocks = (p.M + 63) / 64;
+    const int slabs = (p.N + BNW - 1) / BNW, rblocks = (p.M + 16 * FM - 1) / (16 * FM);
     int rb, slab;
     tile_coords(blockIdx.x, rblocks, slabs, rblocks, rb, slab);
-    const int n0 = slab * BNW, m0 = rb * 64;
+    const int n0 = slab * BNW, m0 = rb * 16 * FM;
     // the wavefront index is the same in every lane: as a scalar it keeps the K loop bounds
     // and the batch offsets scalar too (uniform branches, no exec-mask loop)
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -287,14 +289,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(Problem p, int vec_a, int
 }
 
 template <typename D, int FN, int WAVES, bool B_KC>
-hipError_t launch_d(const Problem& p, const Launch& l) {
-    const int slabs = (p.N + 16 * FN - 1) / (16 * FN), rblocks = (p.M + 63) / 64;
+hipError_t launch_d(const Problem& p, const Launch& l, int fm) {
+    const int slabs = (p.N + 16 * FN - 1) / (16 * FN), rblocks = (p.M + 16 * fm - 1) / (16 * fm);
     const dim3 grid((unsigned)(slabs * rblocks)), block(64 * WAVES);
     const int va = l.vec_a, vb = l.vec_b, vc = l.vec_c;
     // buffer offsets of a row-major B (rows up to K, plus 3 rows of one k-step's lane
     // spread) must fit in 31 bits
     const int bb = !B_KC && (int64_t)(p.K + 4) * p.ldb * 4 + (int64_t)p.N * 4 < ((int64_t)1 << 31);
-    const int fm = p.M >= 64 ? 4 : (p.M + 15) / 16;
     if (fm == 1) hipLaunchKernelGGL((k_skinny<D, 1, FN, WAVES, B_KC>), grid, block, 0, l.stream, p, va, vb, vc, bb);
     else if (fm == 2) hipLaunchKernelGGL((k_skinny<D, 2, FN, WAVES, B_KC>), grid, block, 0, l.stream, p, va, vb, vc, bb);
     else if (fm == 3) hipLaunchKernelGGL((k_skinny<D, 3, FN, WAVES, B_KC>), grid, block, 0, l.stream, p, va, vb, vc, bb);
@@ -314,16 +315,28 @@ int skinny_blocks(const Problem& p, int cus) {
     return wgs4 >= (cus > 0 ? cus : 256) ? 4 : 1;
 }
 
-hipError_t launch_skinny(const Problem& p, const Launch& l, bool bf16, int fn) {
+int skinny_strips(const Problem& p, int fn, int cus) {
+    // 16-row strips of A per workgroup: as many as M has up to four (64 rows), fewer when
+    // 64-row blocks would leave CUs without a workgroup (a 4095 x 1 column: 256 workgroups
+    // of 16 rows instead of 64 of 64; B is re-read per block, which is cheap when it is)
+    if (p.M < 64) return (p.M + 15) / 16;
+    const int64_t slabs = (p.N + 16 * fn - 1) / (16 * fn), c = cus > 0 ? cus : 256;
+    for (int fm = 4; fm > 1; fm /= 2)
+        if (slabs * ((p.M + 16 * fm - 1) / (16 * fm)) >= c) return fm;
+    return 1;
+}
+
+hipError_t launch_skinny(const Problem& p, const Launch& l, bool bf16, int fn, int fm) {
     constexpr int W = kSkinnyWaves;
+    if (fm < 1 || fm > 4) return hipErrorInvalidValue;
     if (fn == 4) {
-        if (bf16) return launch_d<Bf16, 4, W, true>(p, l);
-        if (p.ob == kCol) return launch_d<F32, 4, W, true>(p, l);
-        return launch_d<F32, 4, W, false>(p, l);
+        if (bf16) return launch_d<Bf16, 4, W, true>(p, l, fm);
+        if (p.ob == kCol) return launch_d<F32, 4, W, true>(p, l, fm);
+        return launch_d<F32, 4, W, false>(p, l, fm);
     }
-    if (bf16) return launch_d<Bf16, 1, W, true>(p, l);
-    if (p.ob == kCol) return launch_d<F32, 1, W, true>(p, l);
-    return launch_d<F32, 1, W, false>(p, l);
+    if (bf16) return launch_d<Bf16, 1, W, true>(p, l, fm);
+    if (p.ob == kCol) return launch_d<F32, 1, W, true>(p, l, fm);
+    return launch_d<F32, 1, W, false>(p, l, fm);
 }
 
 }  // namespace gemm

@@ -73,13 +73,17 @@ int pick_group_m(int tiles_m, int tiles_n) {
 
 int64_t tiles(int64_t M, int64_t N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
 
-// AUTO takes the small-problem kernel for few rows, or when even 64 x 64 tiles would leave
-// more than half of the CUs idle (each such tile walks all of K alone).  For FP32 also when
-// 128 x 128 tiles cannot give every CU one: its K split over eight wavefronts then beats
-// the tile kernels, whose few tiles each wait on memory latency (1000^3: 58 -> 30 us).
-bool prefer_small(const Problem& p, int cus, bool f32) {
+// AUTO takes the small-problem kernel for few rows, when even 64 x 64 tiles would leave more
+// than half of the CUs idle (each such tile walks all of K alone), or when 128 x 128 tiles
+// cannot give every CU one while the small-problem kernel's 64 x 64 blocks still fit in one
+// round: its K split over eight wavefronts then beats the tile kernels, whose few tiles each
+// wait on memory latency (rocprofv3: 1000^3 FP32 58 -> 40 us, BF16 16.2 -> 13.9 us;
+// 1024 x 1024 x 4096 BF16 46.6 -> 36.6 us).  With more blocks than CUs it loses
+// (1500 x 1500 x 512: FP32 58 against 49 us, BF16 29 against 13 us).
+bool prefer_small(const Problem& p, int cus) {
     const int64_t c = cus > 0 ? cus : 256;
-    return p.M <= kSkinnyMaxM || tiles(p.M, p.N, 64, 64) * 2 < c || (f32 && tiles(p.M, p.N, 128, 128) < c);
+    const int64_t t64 = tiles(p.M, p.N, 64, 64);
+    return p.M <= kSkinnyMaxM || t64 * 2 < c || (tiles(p.M, p.N, 128, 128) < c && t64 <= c);
 }
 
 // The small-problem kernel, with 1 or 4 column blocks of 16 per workgroup.
@@ -282,13 +286,13 @@ hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, bool
                 if (!skinny_applies(p, false)) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
                 return run_skinny(p, l, false, dev.cus, name);
             default:
-                if (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus, true) && skinny_applies(p, false))
+                if (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus) && skinny_applies(p, false))
                     return run_skinny(p, l, false, dev.cus, name);
                 return run_f32_tiles(p, stream, algo, dev, name, st);
         }
     }
     if (algo == GEMM_ALGO_SKINNY ||
-        (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus, false) && skinny_applies(p, true))) {
+        (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus) && skinny_applies(p, true))) {
         if (!skinny_applies(p, true)) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
         return run_skinny(p, l, true, dev.cus, name);
     }

@@ -311,7 +311,7 @@ def test_skinny_rejects_unsupported(bad):
     ("f32", (256, 256, 256), "f32_skinny16"), ("f32", (1000, 1000, 1000), "f32_skinny64"),
     ("f32", (2048, 2048, 256), "f32_dma128x128"), ("f32", (2047, 2049, 255), "f32_dma128x128"),
     ("f32", (4095, 4097, 1023), "f32_dma256x256"), ("bf16", (4095, 4097, 1023), "bf16_dma256x256"),
-    ("bf16", (1000, 1000, 1000), "bf16_mfma64x64"), ("f32", (4096, 4096, 64), "f32_dma256x256"),
+    ("bf16", (1000, 1000, 1000), "bf16_skinny64"), ("f32", (1500, 1500, 512), "f32_mfma64x64"), ("f32", (4096, 4096, 64), "f32_dma256x256"),
     ("bf16", (4096, 4096, 64), "bf16_dma256x256"),
     ("bf16", (2048, 4096, 128), "bf16_dma256x128")], ids=lambda v: str(v))
 def test_auto_kernel_choice(dtype, shape, kernel):

@@ -84,11 +84,15 @@ def _load():
     lib.gemm_last_hip_error.argtypes, lib.gemm_last_hip_error.restype = [], ci
     lib.gemm_last_kernel.argtypes, lib.gemm_last_kernel.restype = [], ctypes.c_char_p
     lib.gemm_version.argtypes, lib.gemm_version.restype = [], ctypes.c_char_p
+    lib.gemm_plan.argtypes = [ci, i64, i64, i64, ci, ci, ci, ci, ctypes.POINTER(ctypes.c_char_p),
+                              ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.gemm_plan.restype = ci
     return lib
 
 
 EXPORTED = ("gemm_f32", "gemm_bf16_f32acc", "gemm_f32_algo", "gemm_bf16_f32acc_algo",
-            "gemm_status_string", "gemm_last_hip_error", "gemm_last_kernel", "gemm_version")
+            "gemm_status_string", "gemm_last_hip_error", "gemm_last_kernel", "gemm_version",
+            "gemm_plan")
 
 
 def library_path() -> str:
@@ -137,6 +141,15 @@ def gemm_last_kernel() -> str:
 
 def gemm_version() -> str:
     return lib_handle().gemm_version().decode()
+
+
+def gemm_plan(dtype, M, N, K, order_a, order_b, order_c, cus=256):
+    """(kernel, core_rows, core_cols) the default choice would run; no device needed."""
+    kernel, rows, cols = ctypes.c_char_p(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib_handle().gemm_plan(1 if dtype == "bf16" else 0, M, N, K, order_a, order_b, order_c, cus,
+                                  ctypes.byref(kernel), ctypes.byref(rows), ctypes.byref(cols)),
+           "gemm_plan")
+    return kernel.value.decode(), rows.value, cols.value
 
 
 # --- torch tensors -> (pointer, leading dimension, order) ------------------------------

@@ -1,5 +1,6 @@
 // libgemm's C ABI: argument validation, normalisation of a column-major C, kernel choice
 // and launch.  The operation and its contract are documented in include/gemm.h.
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -86,10 +87,14 @@ bool prefer_small(const Problem& p, int cus) {
     return p.M <= kSkinnyMaxM || t64 * 2 < c || (tiles(p.M, p.N, 128, 128) < c && t64 <= c);
 }
 
+const char* skinny_name(bool bf16, int fn) {
+    return bf16 ? (fn == 4 ? "bf16_skinny64" : "bf16_skinny16") : (fn == 4 ? "f32_skinny64" : "f32_skinny16");
+}
+
 // The small-problem kernel, with 1 or 4 column blocks of 16 per workgroup.
 hipError_t run_skinny(const Problem& p, const Launch& l, bool bf16, int cus, const char*& name) {
     const int fn = skinny_blocks(p, cus);
-    name = bf16 ? (fn == 4 ? "bf16_skinny64" : "bf16_skinny16") : (fn == 4 ? "f32_skinny64" : "f32_skinny16");
+    name = skinny_name(bf16, fn);
     return launch_skinny(p, l, bf16, fn, skinny_strips(p, fn, cus));
 }
 
@@ -111,8 +116,6 @@ constexpr TileOpt kF32MfmaOpts[] = {{128, 128, 0.85, 4, false}, {64, 64, 0.75, 4
 constexpr TileOpt kBf16DmaOpts[] = {{256, 256, 1.0, 1, true}, {256, 128, 0.86, 1, true}};
 constexpr TileOpt kBf16MfmaOpts[] = {{256, 256, 1.0, 1, false}, {256, 128, 0.78, 1, false},
                                      {128, 128, 0.74, 2, false}, {64, 64, 0.35, 4, false}};
-// relative throughput of the small tiles that run an edge strip
-constexpr double kF32StripEff = 0.75, kBf16StripEff = 0.35;
 
 double round_cost(int64_t n, int bm, int bn, double eff, int per_cu, int cus) {
     const double c = cus > 0 ? cus : 256;
@@ -121,32 +124,64 @@ double round_cost(int64_t n, int bm, int bn, double eff, int per_cu, int cus) {
 }
 
 // A kernel's launch over a core of C (rows 0 .. mc-1, columns 0 .. nc-1) plus the strips
-// that complete it.  Along an edge the kernel may overhang (part_m / part_n) its last tiles
-// either overhang or the core stops at the last whole tile and the rest runs as a strip
-// (a separate GEMM, priced as 64 x 64 tiles); along any other edge the core stops at the
-// last whole tile.  4095 x 4097 on 256^2 tiles: 16 x 16 tiles (one round) and a one-column
-// strip, against 16 x 17 tiles (two rounds).
+// that complete it, each a separate GEMM through the same choice on the same stream, run after
+// the core.  Per edge the core either ends with tiles that overhang it (where the kernel allows:
+// part_m / part_n), or stops at the last whole tile, or stops after the tiles that fill exactly
+// one round of the CUs (the rest of the edge becomes a strip for smaller tiles).  4095 x 4097 on
+// 256^2 tiles: 16 x 16 tiles (one round) and a one-column strip, against 16 x 17 tiles (two
+// rounds); 2048 x 11008 BF16: 8 x 32 tiles of 256^2 (one round) and a 2048 x 2816 strip on
+// 256 x 128 tiles (one round), against 688 tiles of 256 x 128 (2.7 rounds).
 struct Plan {
     TileOpt opt{};
     int mc = 0, nc = 0;
     double cost = 1e300;
 };
 
-Plan plan_core(const Problem& p, const TileOpt& o, bool part_m, bool part_n, int cus, double strip_eff) {
+// A strip's price: its cheapest option among the given tile kernels, in rounds.
+struct StripPricer {
+    const TileOpt* a;
+    int na;
+    const TileOpt* b;
+    int nb;
+    int cus;
+    double operator()(int64_t m, int64_t n) const {
+        double best = 1e300;
+        for (int i = 0; i < na + nb; ++i) {
+            const TileOpt& o = i < na ? a[i] : b[i - na];
+            best = std::min(best, round_cost(tiles(m, n, o.bm, o.bn), o.bm, o.bn, o.eff, o.per_cu, cus));
+        }
+        return best;
+    }
+};
+
+Plan plan_core(const Problem& p, const TileOpt& o, bool part_m, bool part_n, int cus, const StripPricer& strip) {
     Plan best;
     best.opt = o;
-    for (int cm = 0; cm < 2; ++cm) {
-        if (cm == 0 && !part_m) continue;
-        const int mc = cm == 0 ? p.M : p.M / o.bm * o.bm;
-        for (int cn = 0; cn < 2; ++cn) {
-            if (cn == 0 && !part_n) continue;
-            const int nc = cn == 0 ? p.N : p.N / o.bn * o.bn;
-            if (mc == 0 || nc == 0) continue;
-            double c = round_cost(tiles(mc, nc, o.bm, o.bn), o.bm, o.bn, o.eff, o.per_cu, cus);
-            if (mc < p.M) c += round_cost(tiles(p.M - mc, p.N, 64, 64), 64, 64, strip_eff, 4, cus);
-            if (nc < p.N) c += round_cost(tiles(mc, p.N - nc, 64, 64), 64, 64, strip_eff, 4, cus);
-            if (c < best.cost) { best.cost = c; best.mc = mc; best.nc = nc; }
-        }
+    const int64_t slots = (int64_t)(cus > 0 ? cus : 256) * o.per_cu;    // blocks in one round
+    auto consider = [&](int mc, int nc) {
+        if (mc <= 0 || nc <= 0 || mc > p.M || nc > p.N) return;
+        // a core ends on a tile boundary, except where its last tiles may overhang C's edge
+        if ((mc % o.bm && (mc < p.M || !part_m)) || (nc % o.bn && (nc < p.N || !part_n))) return;
+        double c = round_cost(tiles(mc, nc, o.bm, o.bn), o.bm, o.bn, o.eff, o.per_cu, cus);
+        if (mc < p.M) c += strip(p.M - mc, p.N);
+        if (nc < p.N) c += strip(mc, p.N - nc);
+        if (c < best.cost) { best.cost = c; best.mc = mc; best.nc = nc; }
+    };
+    int ms[2], ns[2], nm = 0, nn = 0;
+    if (part_m) ms[nm++] = p.M;
+    ms[nm++] = p.M / o.bm * o.bm;
+    if (part_n) ns[nn++] = p.N;
+    ns[nn++] = p.N / o.bn * o.bn;
+    for (int i = 0; i < nm; ++i)
+        for (int j = 0; j < nn; ++j) consider(ms[i], ns[j]);
+    // one round exactly: as many tiles along one edge as fill the CUs with the other edge's
+    for (int i = 0; i < nm; ++i) {
+        const int64_t tm = (ms[i] + o.bm - 1) / o.bm;
+        if (tm > 0) consider(ms[i], (int)std::min<int64_t>(p.N, slots / tm * o.bn));
+    }
+    for (int j = 0; j < nn; ++j) {
+        const int64_t tn = (ns[j] + o.bn - 1) / o.bn;
+        if (tn > 0) consider((int)std::min<int64_t>(p.M, slots / tn * o.bm), ns[j]);
     }
     return best;
 }
@@ -216,23 +251,29 @@ const char* bf16_name(const TileOpt& o) {
 }
 
 // The FP32 matrix-core kernels: the cheapest plan over the allowed options.
-hipError_t run_f32_tiles(const Problem& p, hipStream_t stream, gemm_algo_t algo, const DeviceInfo& dev,
-                         const char*& name, gemm_status_t& st) {
-    const Launch l = launch_for(p, stream);
+Plan choose_f32_tiles(const Problem& p, gemm_algo_t algo, int cus) {
+    const Launch l = launch_for(p, nullptr);
     const bool part_m = p.oa == kRow, part_n = p.ob == kCol;   // k-contiguous operands
+    const StripPricer f32_strips{kF32DmaOpts, 2, kF32MfmaOpts, 2, cus};
     Plan best;
     auto consider = [&](const Plan& pl) { if (pl.cost < best.cost) best = pl; };
     const bool any = algo == GEMM_ALGO_AUTO || algo == GEMM_ALGO_MFMA;
     for (const TileOpt& o : kF32DmaOpts) {
         const bool want = any || algo == GEMM_ALGO_MFMA_DMA || (algo == GEMM_ALGO_MFMA_256x256 && o.bm == 256);
         if (want && f32_dma_applies(p, l, o.bm, o.bn))
-            consider(plan_core(p, o, part_m, part_n, dev.cus, kF32StripEff));
+            consider(plan_core(p, o, part_m, part_n, cus, f32_strips));
     }
     for (const TileOpt& o : kF32MfmaOpts) {
         const bool want = any || (algo == GEMM_ALGO_MFMA_128x128 && o.bm == 128) ||
                           (algo == GEMM_ALGO_MFMA_64x64 && o.bm == 64);
-        if (want) consider(plan_whole(p, o, dev.cus));
+        if (want) consider(plan_whole(p, o, cus));
     }
+    return best;
+}
+
+hipError_t run_f32_tiles(const Problem& p, hipStream_t stream, gemm_algo_t algo, const DeviceInfo& dev,
+                         const char*& name, gemm_status_t& st) {
+    const Plan best = choose_f32_tiles(p, algo, dev.cus);
     if (best.cost >= 1e300) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
     name = f32_name(best.opt);
     const TileOpt o = best.opt;
@@ -243,23 +284,29 @@ hipError_t run_f32_tiles(const Problem& p, hipStream_t stream, gemm_algo_t algo,
 
 // The BF16 tile kernels: the direct-copy kernel where it applies (any M, N: its tiles may
 // overhang both edges), else, or for an explicitly chosen tile, the register-staged kernels.
-hipError_t run_bf16_tiles(const Problem& p, hipStream_t stream, gemm_algo_t algo, const DeviceInfo& dev,
-                          const char*& name, gemm_status_t& st) {
-    const Launch l = launch_for(p, stream);
+Plan choose_bf16_tiles(const Problem& p, gemm_algo_t algo, int cus) {
+    const Launch l = launch_for(p, nullptr);
     const bool dma = bf16_dma_applies(p, l, 256, 256);
+    const StripPricer bf16_strips{kBf16DmaOpts, 2, kBf16MfmaOpts, 4, cus};
     Plan best;
     auto consider = [&](const Plan& pl) { if (pl.cost < best.cost) best = pl; };
     const bool any = algo == GEMM_ALGO_AUTO || algo == GEMM_ALGO_MFMA;
     if (dma && (any || algo == GEMM_ALGO_MFMA_DMA))
-        for (const TileOpt& o : kBf16DmaOpts) consider(plan_core(p, o, true, true, dev.cus, kBf16StripEff));
+        for (const TileOpt& o : kBf16DmaOpts) consider(plan_core(p, o, true, true, cus, bf16_strips));
     for (const TileOpt& o : kBf16MfmaOpts) {
         // with the direct-copy kernel available, the default choice leaves the 256-row tiles to it
         const bool want = (any && !(dma && o.bm == 256)) ||
                           (algo == GEMM_ALGO_MFMA_256x256 && o.bm == 256 && o.bn == 256) ||
                           (algo == GEMM_ALGO_MFMA_256x128 && o.bm == 256 && o.bn == 128) ||
                           (algo == GEMM_ALGO_MFMA_128x128 && o.bm == 128) || (algo == GEMM_ALGO_MFMA_64x64 && o.bm == 64);
-        if (want) consider(plan_whole(p, o, dev.cus));
+        if (want) consider(plan_whole(p, o, cus));
     }
+    return best;
+}
+
+hipError_t run_bf16_tiles(const Problem& p, hipStream_t stream, gemm_algo_t algo, const DeviceInfo& dev,
+                          const char*& name, gemm_status_t& st) {
+    const Plan best = choose_bf16_tiles(p, algo, dev.cus);
     if (best.cost >= 1e300) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
     name = bf16_name(best.opt);
     const TileOpt o = best.opt;
@@ -303,6 +350,18 @@ hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, bool
         return launch_bf16_pingpong(p, l);
     }
     return run_bf16_tiles(p, stream, algo, dev, name, st);
+}
+
+// What the default choice runs for a normalised problem with K > 0, without launching: the
+// kernel's name and the rows and columns of C its own launch covers (the rest are strips).
+const char* plan_auto(const Problem& p, bool f32, int cus, int& mc, int& nc) {
+    mc = p.M;
+    nc = p.N;
+    if (prefer_small(p, cus) && skinny_applies(p, !f32)) return skinny_name(!f32, skinny_blocks(p, cus));
+    const Plan pl = f32 ? choose_f32_tiles(p, GEMM_ALGO_AUTO, cus) : choose_bf16_tiles(p, GEMM_ALGO_AUTO, cus);
+    mc = pl.mc;
+    nc = pl.nc;
+    return f32 ? f32_name(pl.opt) : bf16_name(pl.opt);
 }
 
 template <typename Elem>
@@ -393,6 +452,37 @@ gemm_status_t gemm_bf16_f32acc_algo(gemm_algo_t algo, int64_t M, int64_t N, int6
                                     hipStream_t stream) {
     return gemm::run(gemm::In::BF16, algo, M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc,
                      order_c, stream);
+}
+
+gemm_status_t gemm_plan(int bf16, int64_t M, int64_t N, int64_t K, gemm_order_t order_a,
+                        gemm_order_t order_b, gemm_order_t order_c, int cus, const char** kernel,
+                        int64_t* core_rows, int64_t* core_cols) {
+    if (kernel == nullptr || core_rows == nullptr || core_cols == nullptr || cus <= 0) return GEMM_ERR_INVALID_VALUE;
+    if (M < 0 || N < 0 || K < 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return GEMM_ERR_INVALID_VALUE;
+    for (int o : {(int)order_a, (int)order_b, (int)order_c})
+        if (o != GEMM_ROW_MAJOR && o != GEMM_COL_MAJOR) return GEMM_ERR_INVALID_VALUE;
+    *kernel = "none";
+    *core_rows = *core_cols = 0;
+    if (M == 0 || N == 0) return GEMM_OK;
+    // the normalised problem with tight leading dimensions (no memory is touched)
+    const int64_t lda = order_a == GEMM_ROW_MAJOR ? std::max<int64_t>(K, 1) : M;
+    const int64_t ldb = order_b == GEMM_ROW_MAJOR ? N : std::max<int64_t>(K, 1);
+    gemm::Problem p{};
+    if (order_c == GEMM_ROW_MAJOR)
+        p = gemm::Problem{(int)M, (int)N, (int)K, nullptr, lda, (int)order_a, nullptr, ldb, (int)order_b, nullptr, N};
+    else
+        p = gemm::Problem{(int)N, (int)M, (int)K, nullptr, ldb, 1 - (int)order_b, nullptr, lda, 1 - (int)order_a, nullptr, M};
+    if (K == 0) {
+        *kernel = "zero_c";
+        *core_rows = p.M;
+        *core_cols = p.N;
+        return GEMM_OK;
+    }
+    int mc = 0, nc = 0;
+    *kernel = gemm::plan_auto(p, bf16 == 0, cus, mc, nc);
+    *core_rows = mc;
+    *core_cols = nc;
+    return GEMM_OK;
 }
 
 const char* gemm_status_string(gemm_status_t status) {

@@ -159,6 +159,21 @@ const char *gemm_last_kernel(void);
 /* Library version, e.g. "0.1.0". */
 const char *gemm_version(void);
 
+/* What gemm_f32 (bf16 == 0) or gemm_bf16_f32acc (bf16 != 0) would run for a problem of these
+ * extents and orders, with tight leading dimensions, on a device of `cus` compute units,
+ * without touching a device or launching anything; for tests of the kernel choice.
+ *   *kernel     static name, as gemm_last_kernel() would report it ("none" for M == 0 or
+ *               N == 0, "zero_c" for K == 0);
+ *   *core_rows, *core_cols   the part of C the named kernel's own launch covers, in the
+ *               orientation the library computes in: C itself when order_c is row-major,
+ *               C^T (N x M) when it is column-major.  The rest of C runs as edge strips,
+ *               separate GEMMs on the same stream chosen the same way.
+ * Errors: GEMM_ERR_INVALID_VALUE for a null output pointer, cus <= 0, negative or too large
+ * extents (> INT_MAX) or an invalid order; outputs untouched then. */
+gemm_status_t gemm_plan(int bf16, int64_t M, int64_t N, int64_t K, gemm_order_t order_a,
+                        gemm_order_t order_b, gemm_order_t order_c, int cus, const char **kernel,
+                        int64_t *core_rows, int64_t *core_cols);
+
 #ifdef __cplusplus
 }
 #endif

@@ -166,3 +166,74 @@ def test_tile_scheduler_is_a_bijection_with_xcd_blocks():
                        check=True, capture_output=True)
         r = subprocess.run([exe], capture_output=True, text=True)
         assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout
+
+
+# --- the default kernel choice, without a device (gemm_plan) -----------------------------
+KNOWN_KERNELS = {"f32_dma256x256", "f32_dma128x128", "f32_mfma128x128", "f32_mfma64x64",
+                 "f32_skinny16", "f32_skinny64", "bf16_dma256x256", "bf16_dma256x128",
+                 "bf16_mfma256x256", "bf16_mfma256x128", "bf16_mfma128x128", "bf16_mfma64x64",
+                 "bf16_skinny16", "bf16_skinny64", "zero_c", "none"}
+
+
+@pytest.mark.parametrize("dtype,shape,orders,expected", [
+    ("f32", (4096, 4096, 4096), (R, R, R), ("f32_dma256x256", 4096, 4096)),
+    ("bf16", (4096, 4096, 4096), (R, C_, R), ("bf16_dma256x256", 4096, 4096)),
+    # one round of 256^2 tiles, the last row of tiles overhanging M; column 4096 as a strip
+    ("f32", (4095, 4097, 1023), (R, R, R), ("f32_dma256x256", 4095, 4096)),
+    ("bf16", (4095, 4097, 1023), (R, C_, R), ("bf16_dma256x256", 4095, 4096)),
+    # 8 x 32 tiles of 256^2 fill one round; columns 8192 .. 11007 as a strip
+    ("bf16", (2048, 11008, 4096), (R, C_, R), ("bf16_dma256x256", 2048, 8192)),
+    ("bf16", (2048, 4096, 4096), (R, C_, R), ("bf16_dma256x128", 2048, 4096)),
+    ("bf16", (2048, 4096, 11008), (R, C_, R), ("bf16_dma256x128", 2048, 4096)),
+    ("f32", (16, 4096, 4096), (R, R, R), ("f32_skinny16", 16, 4096)),
+    ("bf16", (1000, 1000, 1000), (R, C_, R), ("bf16_skinny64", 1000, 1000)),
+    # column-major A: no overhang along M, so the core stops at the last whole row of tiles
+    # (a planner bug once let a one-round candidate overhang there; the launch refused it)
+    ("f32", (1055, 4096, 512), (C_, R, R), ("f32_dma128x128", 1024, 4096)),
+    ("f32", (2054, 2048, 512), (C_, R, R), ("f32_dma128x128", 2048, 2048)),
+    # column-major C: the library computes C^T (N x M)
+    ("bf16", (4097, 4095, 1023), (R, C_, C_), ("bf16_dma256x256", 4095, 4096)),
+    ("f32", (64, 64, 0), (R, R, R), ("zero_c", 64, 64)),
+    ("f32", (0, 64, 8), (R, R, R), ("none", 0, 0)),
+], ids=lambda v: str(v))
+def test_plan_of_known_shapes(dtype, shape, orders, expected):
+    assert g.gemm_plan(dtype, *shape, *orders) == expected
+
+
+def test_plan_rejects_invalid_arguments():
+    for kw in (dict(cus=0), dict(M=-1), dict(K=2**31)):
+        a = dict(dtype="f32", M=8, N=8, K=8, order_a=R, order_b=R, order_c=R, cus=256)
+        a.update(kw)
+        with pytest.raises(g.GemmError) as e:
+            g.gemm_plan(**a)
+        assert e.value.status == INVALID
+    with pytest.raises(g.GemmError):
+        g.gemm_plan("f32", 8, 8, 8, 2, R, R)
+
+
+def test_plan_invariants_on_random_shapes():
+    """Over random shapes and orders: the core lies inside C; kernels that take any shape
+    cover all of it; the FP32 direct-copy core ends on whole tiles except along the edge of a
+    k-contiguous operand (row-major A: M; column-major B: N), where its tiles may overhang."""
+    import numpy as np
+    rng = np.random.default_rng(2024)
+    for _ in range(400):
+        dtype = "bf16" if rng.random() < 0.5 else "f32"
+        M, N = (int(x) for x in rng.integers(1, 9000, 2))
+        K = int(rng.integers(1, 5000))
+        oa, ob, oc = (int(x) for x in rng.integers(0, 2, 3))
+        if dtype == "bf16" and rng.random() < 0.7:
+            oa, ob = R, C_                      # mostly the direct-copy kernel's layout
+        kernel, rows, cols = g.gemm_plan(dtype, M, N, K, oa, ob, oc)
+        assert kernel in KNOWN_KERNELS, kernel
+        # the orientation the library computes in
+        Mn, Nn, an, bn = (M, N, oa, ob) if oc == R else (N, M, 1 - ob, 1 - oa)
+        assert 0 < rows <= Mn and 0 < cols <= Nn, (kernel, M, N, rows, cols)
+        if "skinny" in kernel or "mfma" in kernel:
+            assert (rows, cols) == (Mn, Nn), (kernel, M, N, oc, rows, cols)
+        if kernel.startswith("f32_dma"):
+            t = 256 if kernel == "f32_dma256x256" else 128
+            assert rows % t == 0 or (an == R and rows == Mn), (kernel, M, N, oa, ob, oc, rows)
+            assert cols % t == 0 or (bn == C_ and cols == Nn), (kernel, M, N, oa, ob, oc, cols)
+        if kernel.startswith("bf16_dma"):
+            assert an == R and bn == C_

@@ -313,7 +313,8 @@ def test_skinny_rejects_unsupported(bad):
     ("f32", (4095, 4097, 1023), "f32_dma256x256"), ("bf16", (4095, 4097, 1023), "bf16_dma256x256"),
     ("bf16", (1000, 1000, 1000), "bf16_skinny64"), ("f32", (1500, 1500, 512), "f32_mfma64x64"), ("f32", (4096, 4096, 64), "f32_dma256x256"),
     ("bf16", (4096, 4096, 64), "bf16_dma256x256"),
-    ("bf16", (2048, 4096, 128), "bf16_dma256x128")], ids=lambda v: str(v))
+    ("bf16", (2048, 4096, 128), "bf16_dma256x128"), ("bf16", (2048, 11008, 128), "bf16_dma256x256")],
+    ids=lambda v: str(v))
 def test_auto_kernel_choice(dtype, shape, kernel):
     """AUTO: few rows or too few 64 x 64 tiles -> small-problem kernel, else block tiles; a
     tile kernel whose last tiles along an edge would start a second round stops at the last
@@ -328,6 +329,18 @@ def test_auto_kernel_choice(dtype, shape, kernel):
     else:
         check(p, g.Algo.AUTO)
     assert g.gemm_last_kernel() == kernel
+
+
+# --- plans of several launches: a core of tiles and strips for the rest of C (one-round cut:
+# 2048 x 11008 BF16 runs 8 x 32 tiles of 256^2 and a 2048 x 2816 strip; 3000^2 FP32 an
+# overhanging 128^2 core and strips; 6144^2 BF16 a 256 x 128 core and a 256^2 strip) -------
+@pytest.mark.parametrize("dtype,shape", [("bf16", (2048, 11008, 64)), ("f32", (3000, 3000, 96)),
+                                         ("bf16", (6144, 6144, 64)), ("f32", (4095, 4097, 40)),
+                                         ("bf16", (4095, 4097, 72))], ids=lambda v: str(v))
+def test_auto_core_and_strips(dtype, shape):
+    M, N, K = shape
+    p = gi.make_problem(M, N, K, dtype, ROW_MAJOR, COL_MAJOR if dtype == "bf16" else ROW_MAJOR, wid=56)
+    check(p, g.Algo.AUTO)
 
 
 # --- FP32 direct-copy kernel (16x16x4 matrix instructions, operands copied into LDS as laid

@@ -12,7 +12,10 @@ kernel against MI355X's published matrix-core peak for its dtype.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--algo NAME]
 
 `--workload` picks another single workload from gemm_inputs.WORKLOADS (then one step is
-that one GEMM); `--algo` forces a kernel (gemm_f32_amd.Algo name).  Each GEMM's inputs
+that one GEMM); `--algo` forces a kernel (gemm_f32_amd.Algo name); `--workspace` calls the
+workspace entry points (gemm_f32_ws / gemm_bf16_f32acc_ws, split-K across workgroups where
+the problem is too small to fill the device) with a workspace of the size the library asks
+for, allocated before the timed region.  Each GEMM's inputs
 rotate over enough independently drawn copies (`--sets`, default: at least 2 and more
 than 512 MB of A and B together) that the 256 MB last-level cache cannot hold them across
 steps.
@@ -44,6 +47,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT)
     ap.add_argument("--algo", default="AUTO")
+    ap.add_argument("--workspace", action="store_true",
+                    help="use the workspace (split-K) entry points; AUTO only")
     ap.add_argument("--sets", type=int, default=0,
                     help="input copies per GEMM (0: enough for > 512 MB, at least 2)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -116,7 +121,7 @@ def copy_calibration(args):
 class Leg:
     """One GEMM of the step with its resident device buffers."""
 
-    def __init__(self, name, algo, sets):
+    def __init__(self, name, algo, sets, workspace=False):
         import torch
         import gemm_f32_amd as g
         import gemm_inputs as gi
@@ -144,9 +149,23 @@ class Leg:
         self.fn = g.gemm_f32_algo if w.dtype == "f32" else g.gemm_bf16_f32acc_algo
         self.flops = 2 * w.M * w.N * w.K
         self.kernel = None
+        self.ws, self.ws_bytes = None, 0
+        if workspace:
+            if algo != "AUTO":
+                raise SystemExit("--workspace runs the default kernel choice (--algo AUTO)")
+            p0 = self.problems[0]
+            self.ws_bytes = g.gemm_workspace_size(w.dtype, p0.M, p0.N, p0.K, p0.order_a, p0.order_b,
+                                                  p0.order_c)
+            self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device="cuda")
+            self.fn_ws = g.gemm_f32_ws if w.dtype == "f32" else g.gemm_bf16_f32acc_ws
 
     def launch(self, s, stream):
         p = self.problems[s % len(self.problems)]
+        if self.ws is not None:
+            self.fn_ws(p.M, p.N, p.K, self.A[s % len(self.A)].data_ptr(), p.lda, p.order_a,
+                       self.B[s % len(self.B)].data_ptr(), p.ldb, p.order_b, self.C.data_ptr(), p.ldc,
+                       p.order_c, self.ws.data_ptr(), self.ws_bytes, stream)
+            return
         self.fn(self.algo, p.M, p.N, p.K, self.A[s % len(self.A)].data_ptr(), p.lda, p.order_a,
                 self.B[s % len(self.B)].data_ptr(), p.ldb, p.order_b, self.C.data_ptr(), p.ldc,
                 p.order_c, stream)
@@ -198,7 +217,7 @@ def main():
     from gemm_f32_amd import roofline as rl
 
     names = DEFAULT_LEGS if args.workload == DEFAULT else [args.workload]
-    legs = [Leg(n, args.algo, args.sets) for n in names]
+    legs = [Leg(n, args.algo, args.sets, args.workspace) for n in names]
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
@@ -232,6 +251,8 @@ def main():
                               "pct_peak": round(100 * tf * 1e12 / peak, 2),
                               "M": leg.w.M, "N": leg.w.N, "K": leg.w.K, "dtype_in": leg.w.dtype,
                               "input_sets": leg.sets}
+        if leg.ws is not None:
+            leg_info[leg.name]["workspace_bytes"] = leg.ws_bytes
     dom = max(legs, key=lambda l: leg_info[l.name]["ms"])
     di = leg_info[dom.name]
     peak = rl.mi355x_peak(dom.w.dtype)

@@ -85,14 +85,19 @@ def _load():
     lib.gemm_last_kernel.argtypes, lib.gemm_last_kernel.restype = [], ctypes.c_char_p
     lib.gemm_version.argtypes, lib.gemm_version.restype = [], ctypes.c_char_p
     lib.gemm_plan.argtypes = [ci, i64, i64, i64, ci, ci, ci, ci, ctypes.POINTER(ctypes.c_char_p),
-                              ctypes.POINTER(i64), ctypes.POINTER(i64)]
+                              ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_size_t)]
     lib.gemm_plan.restype = ci
+    lib.gemm_workspace_size.argtypes = [ci, i64, i64, i64, ci, ci, ci]
+    lib.gemm_workspace_size.restype = ctypes.c_size_t
+    for name in ("gemm_f32_ws", "gemm_bf16_f32acc_ws"):
+        f = getattr(lib, name)
+        f.argtypes, f.restype = args[:-1] + [vp, ctypes.c_size_t, vp], ci
     return lib
 
 
 EXPORTED = ("gemm_f32", "gemm_bf16_f32acc", "gemm_f32_algo", "gemm_bf16_f32acc_algo",
             "gemm_status_string", "gemm_last_hip_error", "gemm_last_kernel", "gemm_version",
-            "gemm_plan")
+            "gemm_plan", "gemm_workspace_size", "gemm_f32_ws", "gemm_bf16_f32acc_ws")
 
 
 def library_path() -> str:
@@ -143,13 +148,35 @@ def gemm_version() -> str:
     return lib_handle().gemm_version().decode()
 
 
-def gemm_plan(dtype, M, N, K, order_a, order_b, order_c, cus=256):
-    """(kernel, core_rows, core_cols) the default choice would run; no device needed."""
-    kernel, rows, cols = ctypes.c_char_p(), ctypes.c_int64(), ctypes.c_int64()
+def gemm_plan(dtype, M, N, K, order_a, order_b, order_c, cus=256, with_workspace=False):
+    """(kernel, core_rows, core_cols) the default choice would run, plus the split-K workspace
+    bytes when with_workspace; no device needed."""
+    kernel, rows, cols, ws = ctypes.c_char_p(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
     _check(lib_handle().gemm_plan(1 if dtype == "bf16" else 0, M, N, K, order_a, order_b, order_c, cus,
-                                  ctypes.byref(kernel), ctypes.byref(rows), ctypes.byref(cols)),
-           "gemm_plan")
-    return kernel.value.decode(), rows.value, cols.value
+                                  ctypes.byref(kernel), ctypes.byref(rows), ctypes.byref(cols),
+                                  ctypes.byref(ws)), "gemm_plan")
+    out = (kernel.value.decode(), rows.value, cols.value)
+    return out + (ws.value,) if with_workspace else out
+
+
+def gemm_workspace_size(dtype, M, N, K, order_a, order_b, order_c) -> int:
+    """Workspace bytes with which the _ws calls split K on the current device (0: no split)."""
+    return lib_handle().gemm_workspace_size(1 if dtype == "bf16" else 0, M, N, K, order_a, order_b,
+                                            order_c)
+
+
+def gemm_f32_ws(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, workspace, workspace_bytes,
+                stream=0):
+    """gemm_f32 with a caller's workspace (device pointer, bytes) for split-K."""
+    _check(lib_handle().gemm_f32_ws(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, workspace,
+                                    workspace_bytes, stream), "gemm_f32_ws")
+
+
+def gemm_bf16_f32acc_ws(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, workspace,
+                        workspace_bytes, stream=0):
+    """gemm_bf16_f32acc with a caller's workspace (device pointer, bytes) for split-K."""
+    _check(lib_handle().gemm_bf16_f32acc_ws(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c,
+                                            workspace, workspace_bytes, stream), "gemm_bf16_f32acc_ws")
 
 
 # --- torch tensors -> (pointer, leading dimension, order) ------------------------------

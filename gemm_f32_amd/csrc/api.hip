@@ -91,8 +91,27 @@ const char* skinny_name(bool bf16, int fn) {
     return bf16 ? (fn == 4 ? "bf16_skinny64" : "bf16_skinny16") : (fn == 4 ? "f32_skinny64" : "f32_skinny16");
 }
 
+// A caller's workspace (gemm_*_ws); empty for the plain entry points.
+struct Workspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+
+// The split the small-problem kernel takes with this workspace (slices == 1: none).
+SkinnySplit split_with(const Problem& p, bool bf16, int cus, const Workspace& ws) {
+    if (ws.ptr == nullptr || !aligned(ws.ptr, 16)) return SkinnySplit{};
+    const SkinnySplit sp = skinny_split(p, bf16, cus);
+    return sp.slices > 1 && sp.bytes <= ws.bytes ? sp : SkinnySplit{};
+}
+
 // The small-problem kernel, with 1 or 4 column blocks of 16 per workgroup.
-hipError_t run_skinny(const Problem& p, const Launch& l, bool bf16, int cus, const char*& name) {
+hipError_t run_skinny(const Problem& p, const Launch& l, bool bf16, int cus, const char*& name,
+                      const Workspace& ws = Workspace{}) {
+    const SkinnySplit sp = split_with(p, bf16, cus, ws);
+    if (sp.slices > 1) {       // K split across workgroups too: partial products in the workspace
+        name = bf16 ? "bf16_skinny64_splitk" : "f32_skinny64_splitk";
+        return launch_skinny(p, l, bf16, sp.fn, sp.fm, &sp, static_cast<float*>(ws.ptr));
+    }
     const int fn = skinny_blocks(p, cus);
     name = skinny_name(bf16, fn);
     return launch_skinny(p, l, bf16, fn, skinny_strips(p, fn, cus));
@@ -220,7 +239,7 @@ Problem sub_problem(const Problem& p, int r0, int m, int c0, int n, int elem) {
 }
 
 hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, bool f32, const DeviceInfo& dev,
-                    const char*& name, gemm_status_t& st);
+                    const char*& name, gemm_status_t& st, const Workspace& ws = Workspace{});
 
 // Run a plan's core with `core` and its strips through the default choice, on one stream.
 template <typename CoreFn>
@@ -318,7 +337,7 @@ hipError_t run_bf16_tiles(const Problem& p, hipStream_t stream, gemm_algo_t algo
 // Kernel choice and launch for a normalised problem (row-major C, K > 0).  A status other
 // than GEMM_OK in `st` means the request is invalid (nothing launched).
 hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, bool f32, const DeviceInfo& dev,
-                    const char*& name, gemm_status_t& st) {
+                    const char*& name, gemm_status_t& st, const Workspace& ws) {
     Launch l = launch_for(p, stream);
     if (f32) {
         switch (algo) {
@@ -334,14 +353,14 @@ hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, bool
                 return run_skinny(p, l, false, dev.cus, name);
             default:
                 if (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus) && skinny_applies(p, false))
-                    return run_skinny(p, l, false, dev.cus, name);
+                    return run_skinny(p, l, false, dev.cus, name, ws);
                 return run_f32_tiles(p, stream, algo, dev, name, st);
         }
     }
     if (algo == GEMM_ALGO_SKINNY ||
         (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus) && skinny_applies(p, true))) {
         if (!skinny_applies(p, true)) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
-        return run_skinny(p, l, true, dev.cus, name);
+        return run_skinny(p, l, true, dev.cus, name, algo == GEMM_ALGO_AUTO ? ws : Workspace{});
     }
     if (algo == GEMM_ALGO_MFMA_PINGPONG) {
         if (!bf16_pingpong_applies(p, l)) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
@@ -350,6 +369,23 @@ hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, bool
         return launch_bf16_pingpong(p, l);
     }
     return run_bf16_tiles(p, stream, algo, dev, name, st);
+}
+
+// The problem the library computes for extents and orders with tight leading dimensions and
+// no memory (a column-major C becomes C^T = B^T A^T), for queries that launch nothing.
+Problem query_problem(int64_t M, int64_t N, int64_t K, int oa, int ob, int oc) {
+    const int64_t lda = oa == GEMM_ROW_MAJOR ? std::max<int64_t>(K, 1) : M;
+    const int64_t ldb = ob == GEMM_ROW_MAJOR ? N : std::max<int64_t>(K, 1);
+    if (oc == GEMM_ROW_MAJOR) return Problem{(int)M, (int)N, (int)K, nullptr, lda, oa, nullptr, ldb, ob, nullptr, N};
+    return Problem{(int)N, (int)M, (int)K, nullptr, ldb, 1 - ob, nullptr, lda, 1 - oa, nullptr, M};
+}
+
+// Workspace bytes with which the _ws entry points split K (0: they never do for this problem).
+size_t split_bytes(const Problem& p, bool f32, int cus) {
+    if (p.M == 0 || p.N == 0 || p.K == 0) return 0;
+    if (!(prefer_small(p, cus) && skinny_applies(p, !f32))) return 0;
+    const SkinnySplit sp = skinny_split(p, !f32, cus);
+    return sp.slices > 1 ? sp.bytes : 0;
 }
 
 // What the default choice runs for a normalised problem with K > 0, without launching: the
@@ -367,9 +403,11 @@ const char* plan_auto(const Problem& p, bool f32, int cus, int& mc, int& nc) {
 template <typename Elem>
 gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, const Elem* A,
                   int64_t lda, gemm_order_t oa, const Elem* B, int64_t ldb, gemm_order_t ob,
-                  float* C, int64_t ldc, gemm_order_t oc, hipStream_t stream) {
+                  float* C, int64_t ldc, gemm_order_t oc, hipStream_t stream,
+                  const Workspace& ws = Workspace{}) {
     gemm_status_t st = validate(in, M, N, K, A, lda, oa, B, ldb, ob, C, ldc, oc);
     if (st != GEMM_OK) return st;
+    if (ws.ptr != nullptr && !aligned(ws.ptr, 16)) return GEMM_ERR_INVALID_VALUE;
     const bool f32 = in == In::F32;
     switch (algo) {
         case GEMM_ALGO_AUTO: case GEMM_ALGO_MFMA: break;
@@ -406,7 +444,7 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
         name = "zero_c";
     } else {
         gemm_status_t bad = GEMM_OK;
-        err = dispatch(p, stream, algo, f32, dev, name, bad);
+        err = dispatch(p, stream, algo, f32, dev, name, bad, ws);
         if (bad != GEMM_OK) return bad;
     }
     if (err != hipSuccess) {
@@ -456,22 +494,18 @@ gemm_status_t gemm_bf16_f32acc_algo(gemm_algo_t algo, int64_t M, int64_t N, int6
 
 gemm_status_t gemm_plan(int bf16, int64_t M, int64_t N, int64_t K, gemm_order_t order_a,
                         gemm_order_t order_b, gemm_order_t order_c, int cus, const char** kernel,
-                        int64_t* core_rows, int64_t* core_cols) {
-    if (kernel == nullptr || core_rows == nullptr || core_cols == nullptr || cus <= 0) return GEMM_ERR_INVALID_VALUE;
+                        int64_t* core_rows, int64_t* core_cols, size_t* workspace_bytes) {
+    if (kernel == nullptr || core_rows == nullptr || core_cols == nullptr || workspace_bytes == nullptr ||
+        cus <= 0)
+        return GEMM_ERR_INVALID_VALUE;
     if (M < 0 || N < 0 || K < 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return GEMM_ERR_INVALID_VALUE;
     for (int o : {(int)order_a, (int)order_b, (int)order_c})
         if (o != GEMM_ROW_MAJOR && o != GEMM_COL_MAJOR) return GEMM_ERR_INVALID_VALUE;
     *kernel = "none";
     *core_rows = *core_cols = 0;
+    *workspace_bytes = 0;
     if (M == 0 || N == 0) return GEMM_OK;
-    // the normalised problem with tight leading dimensions (no memory is touched)
-    const int64_t lda = order_a == GEMM_ROW_MAJOR ? std::max<int64_t>(K, 1) : M;
-    const int64_t ldb = order_b == GEMM_ROW_MAJOR ? N : std::max<int64_t>(K, 1);
-    gemm::Problem p{};
-    if (order_c == GEMM_ROW_MAJOR)
-        p = gemm::Problem{(int)M, (int)N, (int)K, nullptr, lda, (int)order_a, nullptr, ldb, (int)order_b, nullptr, N};
-    else
-        p = gemm::Problem{(int)N, (int)M, (int)K, nullptr, ldb, 1 - (int)order_b, nullptr, lda, 1 - (int)order_a, nullptr, M};
+    const gemm::Problem p = gemm::query_problem(M, N, K, order_a, order_b, order_c);
     if (K == 0) {
         *kernel = "zero_c";
         *core_rows = p.M;
@@ -482,7 +516,34 @@ gemm_status_t gemm_plan(int bf16, int64_t M, int64_t N, int64_t K, gemm_order_t 
     *kernel = gemm::plan_auto(p, bf16 == 0, cus, mc, nc);
     *core_rows = mc;
     *core_cols = nc;
+    *workspace_bytes = gemm::split_bytes(p, bf16 == 0, cus);
     return GEMM_OK;
+}
+
+size_t gemm_workspace_size(int bf16, int64_t M, int64_t N, int64_t K, gemm_order_t order_a,
+                           gemm_order_t order_b, gemm_order_t order_c) {
+    if (M <= 0 || N <= 0 || K <= 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return 0;
+    for (int o : {(int)order_a, (int)order_b, (int)order_c})
+        if (o != GEMM_ROW_MAJOR && o != GEMM_COL_MAJOR) return 0;
+    gemm::DeviceInfo dev;
+    if (!gemm::device_info(dev) || !dev.supported) return 0;
+    return gemm::split_bytes(gemm::query_problem(M, N, K, order_a, order_b, order_c), bf16 == 0, dev.cus);
+}
+
+gemm_status_t gemm_f32_ws(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                          gemm_order_t order_a, const float* B, int64_t ldb, gemm_order_t order_b,
+                          float* C, int64_t ldc, gemm_order_t order_c, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    return gemm::run(gemm::In::F32, GEMM_ALGO_AUTO, M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc,
+                     order_c, stream, gemm::Workspace{workspace, workspace_bytes});
+}
+
+gemm_status_t gemm_bf16_f32acc_ws(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                                  gemm_order_t order_a, const uint16_t* B, int64_t ldb,
+                                  gemm_order_t order_b, float* C, int64_t ldc, gemm_order_t order_c,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return gemm::run(gemm::In::BF16, GEMM_ALGO_AUTO, M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc,
+                     order_c, stream, gemm::Workspace{workspace, workspace_bytes});
 }
 
 const char* gemm_status_string(gemm_status_t status) {

@@ -42,7 +42,18 @@ bool skinny_applies(const Problem& p, bool bf16);
 // for a problem on `cus` CUs
 int skinny_blocks(const Problem& p, int cus);
 int skinny_strips(const Problem& p, int fn, int cus);
-hipError_t launch_skinny(const Problem& p, const Launch& l, bool bf16, int fn, int fm);
+// Split-K across workgroups for the small-problem kernel: `slices` K ranges of `kslice`,
+// partial products in a workspace of `bytes` (slices dense M x N FP32 slices), summed in
+// slice order by a second kernel.  slices == 1: no split (the problem fills the CUs, or K is
+// too short).
+struct SkinnySplit {
+    int fn = 1, fm = 1, kslice = 0, slices = 1;
+    size_t bytes = 0;
+};
+SkinnySplit skinny_split(const Problem& p, bool bf16, int cus);
+// `sp` and `part` (16-byte aligned, sp->bytes) select the split; nullptr: one pass into C
+hipError_t launch_skinny(const Problem& p, const Launch& l, bool bf16, int fn, int fm,
+                         const SkinnySplit* sp = nullptr, float* part = nullptr);
 // C = 0 for K == 0 (fill.hip)
 hipError_t launch_zero_c(const Problem& p, const Launch& l);
 

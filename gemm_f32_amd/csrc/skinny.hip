@@ -32,6 +32,8 @@
 // cheap only while the problem is small or M is.  Rows past M and columns past N are
 // clamped to the last valid one (their products are never stored); the K tail uses
 // element-wise loads with zero fill.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -50,7 +52,7 @@ typedef unsigned short u16;
 // flight measured the same kernel time; at 1000^3 with four blocks, 2 batches of one
 // k-step beat 2 of two by 9%.)
 template <int FM, int FN> struct Depth {
-    static constexpr int RING = 2, CHUNK = FN > 1 ? 1 : (FM > 1 ? 4 : 8);
+    static constexpr int RING = 2, CHUNK = FN > 1 ? (FM > 1 ? 1 : 4) : (FM > 1 ? 4 : 8);
 };
 
 // ---- per-dtype pieces -------------------------------------------------------------------
@@ -122,7 +124,8 @@ struct F32 {
 // B operand of 4 matrix instructions: block q's column c is column n0 + 4 c + q of C, and
 // the epilogue writes the 4 columns of a lane with one 16-byte store.
 template <typename D, int FM, int FN, int WAVES, bool B_KC>
-__global__ __launch_bounds__(64 * WAVES) void k_skinny(Problem p, int vec_a, int vec_b, int vec_c, int bbuf) {
+__global__ __launch_bounds__(64 * WAVES)
+void k_skinny(Problem p, int vec_a, int vec_b, int vec_c, int bbuf, int kslice, float* part) {
     using E = typename D::Elem;
     using Frag = typename D::Frag;
     constexpr bool RC4 = !B_KC && FN == 4;     // row-major FP32 B read 16 bytes along N
@@ -180,7 +183,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(Problem p, int vec_a, int
     // that the workgroup walks K as one front: at 16 x 4096 x 4096 this beat 8 contiguous
     // K ranges by 7% with one column block and by 2.3x with four (each workgroup's reads of
     // B stay within one contiguous band of rows)
-    const int kbeg = wave * CK, kend = K;
+    // split-K across workgroups (gridDim.y slices of `kslice`): this workgroup's slice is
+    // k in [kz0, kend); its partial product goes to slice z of the workspace `part`
+    const int z = blockIdx.y, kz0 = z * kslice, kend = min(K, kz0 + kslice);
+    const int kbeg = kz0 + wave * CK;
     constexpr int SC = WAVES * CK;              // K distance between a wavefront's batches
     Frag fa[RING][CHUNK][FM], fb[RING][CHUNK][NB];
     // one batch of CHUNK k-steps; `full` (wavefront-uniform): the whole batch lies inside
@@ -265,11 +271,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(Problem p, int vec_a, int
             for (int r = 0; r < 4; ++r) {
                 const int row = m0 + 16 * f + 4 * lq + r;
                 if (row >= p.M) continue;
-                float* crow = p.C + (int64_t)row * p.ldc;
+                float* crow = part ? part + ((int64_t)z * p.M + row) * p.N : p.C + (int64_t)row * p.ldc;
                 if constexpr (RC4) {
                     // block q's column li is column n0 + 4 li + q
                     const int col = n0 + 4 * li;
-                    if (vec_c && n_inside) {
+                    if ((part ? (p.N & 3) == 0 : vec_c) && n_inside) {
                         *reinterpret_cast<f32x4*>(crow + col) = f32x4{sum[0][r], sum[1][r], sum[2][r], sum[3][r]};
                     } else {
 #pragma unroll
@@ -288,19 +294,58 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(Problem p, int vec_a, int
     }
 }
 
+// K per batch of k-steps of the kernel instance (FM, FN) of dtype D
+template <typename D> int batch_k(int fm, int fn) {
+    const int chunk = fn > 1 ? (fm > 1 ? 1 : 4) : (fm > 1 ? 4 : 8);
+    return chunk * D::KSTEP;
+}
+
 template <typename D, int FN, int WAVES, bool B_KC>
-hipError_t launch_d(const Problem& p, const Launch& l, int fm) {
+hipError_t launch_d(const Problem& p, const Launch& l, int fm, int kslice, int slices, float* part) {
     const int slabs = (p.N + 16 * FN - 1) / (16 * FN), rblocks = (p.M + 16 * fm - 1) / (16 * fm);
-    const dim3 grid((unsigned)(slabs * rblocks)), block(64 * WAVES);
+    const dim3 grid((unsigned)(slabs * rblocks), (unsigned)slices), block(64 * WAVES);
     const int va = l.vec_a, vb = l.vec_b, vc = l.vec_c;
     // buffer offsets of a row-major B (rows up to K, plus 3 rows of one k-step's lane
     // spread) must fit in 31 bits
     const int bb = !B_KC && (int64_t)(p.K + 4) * p.ldb * 4 + (int64_t)p.N * 4 < ((int64_t)1 << 31);
-    if (fm == 1) hipLaunchKernelGGL((k_skinny<D, 1, FN, WAVES, B_KC>), grid, block, 0, l.stream, p, va, vb, vc, bb);
-    else if (fm == 2) hipLaunchKernelGGL((k_skinny<D, 2, FN, WAVES, B_KC>), grid, block, 0, l.stream, p, va, vb, vc, bb);
-    else if (fm == 3) hipLaunchKernelGGL((k_skinny<D, 3, FN, WAVES, B_KC>), grid, block, 0, l.stream, p, va, vb, vc, bb);
-    else hipLaunchKernelGGL((k_skinny<D, 4, FN, WAVES, B_KC>), grid, block, 0, l.stream, p, va, vb, vc, bb);
+    if (fm == 1) hipLaunchKernelGGL((k_skinny<D, 1, FN, WAVES, B_KC>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part);
+    else if (fm == 2) hipLaunchKernelGGL((k_skinny<D, 2, FN, WAVES, B_KC>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part);
+    else if (fm == 3) hipLaunchKernelGGL((k_skinny<D, 3, FN, WAVES, B_KC>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part);
+    else hipLaunchKernelGGL((k_skinny<D, 4, FN, WAVES, B_KC>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part);
     return hipGetLastError();
+}
+
+// Second pass of split-K: C = part[0] + part[1] + ... + part[S-1], in slice order (the same
+// sum for every call), four columns per thread.  part holds S dense M x N slices.
+__global__ __launch_bounds__(256) void k_sum_slices(const float* part, int S, int M, int N, float* C,
+                                                    int64_t ldc, int vec) {
+    const int cq = (N + 3) / 4;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)M * cq) return;
+    const int row = (int)(i / cq), col = 4 * (int)(i % cq);
+    const int64_t slice = (int64_t)M * N, off = (int64_t)row * N + col;
+    float* crow = C + (int64_t)row * ldc;
+    if (vec && col + 3 < N) {
+        // loads in batches of 8 in flight, added in slice order
+        constexpr int G = 8;
+        f32x4 acc = *reinterpret_cast<const f32x4*>(part + off);
+        int z = 1;
+        for (; z + G <= S; z += G) {
+            f32x4 v[G];
+#pragma unroll
+            for (int u = 0; u < G; ++u) v[u] = *reinterpret_cast<const f32x4*>(part + (z + u) * slice + off);
+#pragma unroll
+            for (int u = 0; u < G; ++u) acc += v[u];
+        }
+        for (; z < S; ++z) acc += *reinterpret_cast<const f32x4*>(part + z * slice + off);
+        *reinterpret_cast<f32x4*>(crow + col) = acc;
+    } else {
+        for (int e = 0; e < 4 && col + e < N; ++e) {
+            float acc = part[off + e];
+            for (int z = 1; z < S; ++z) acc += part[z * slice + off + e];
+            crow[col + e] = acc;
+        }
+    }
 }
 
 }  // namespace
@@ -326,17 +371,55 @@ int skinny_strips(const Problem& p, int fn, int cus) {
     return 1;
 }
 
-hipError_t launch_skinny(const Problem& p, const Launch& l, bool bf16, int fn, int fm) {
+SkinnySplit skinny_split(const Problem& p, bool bf16, int cus) {
+    SkinnySplit sp;
+    // 64 columns per workgroup (four times fewer reads of A per column of C than 16) and as
+    // many K slices as it takes to give every CU a workgroup, each slice at least one batch
+    // of k-steps per wavefront
+    const int64_t c = cus > 0 ? cus : 256;
+    // only where the kernel's own blocks leave CUs without a workgroup (at 16 x 4096 x 4096
+    // its 256 blocks of 16 columns fill the chip, and a split measured slower there)
+    const int fn0 = skinny_blocks(p, cus), fm0 = skinny_strips(p, fn0, cus);
+    if ((int64_t)((p.M + 16 * fm0 - 1) / (16 * fm0)) * ((p.N + 16 * fn0 - 1) / (16 * fn0)) >= c) return sp;
+    const int fn = 4, fm = skinny_strips(p, fn, cus);
+    const int64_t wgs = (int64_t)((p.M + 16 * fm - 1) / (16 * fm)) * ((p.N + 63) / 64);
+    if (wgs >= c) return sp;
+    const int bk = (bf16 ? batch_k<Bf16>(fm, fn) : batch_k<F32>(fm, fn)) * kSkinnyWaves;
+    const int64_t want = (c + wgs - 1) / wgs, most = p.K / bk;
+    const int s = (int)std::min<int64_t>(want, most);
+    if (s < 2) return sp;
+    const int kslice = ((p.K + s - 1) / s + bk - 1) / bk * bk;
+    sp.fn = fn;
+    sp.fm = fm;
+    sp.kslice = kslice;
+    sp.slices = (p.K + kslice - 1) / kslice;
+    sp.bytes = (size_t)sp.slices * p.M * p.N * sizeof(float);
+    return sp;
+}
+
+hipError_t launch_skinny(const Problem& p, const Launch& l, bool bf16, int fn, int fm, const SkinnySplit* sp,
+                         float* part) {
     constexpr int W = kSkinnyWaves;
     if (fm < 1 || fm > 4) return hipErrorInvalidValue;
+    const bool split = sp != nullptr && sp->slices > 1 && part != nullptr;
+    const int kslice = split ? sp->kslice : p.K, slices = split ? sp->slices : 1;
+    float* out = split ? part : nullptr;
+    hipError_t err;
     if (fn == 4) {
-        if (bf16) return launch_d<Bf16, 4, W, true>(p, l, fm);
-        if (p.ob == kCol) return launch_d<F32, 4, W, true>(p, l, fm);
-        return launch_d<F32, 4, W, false>(p, l, fm);
+        if (bf16) err = launch_d<Bf16, 4, W, true>(p, l, fm, kslice, slices, out);
+        else if (p.ob == kCol) err = launch_d<F32, 4, W, true>(p, l, fm, kslice, slices, out);
+        else err = launch_d<F32, 4, W, false>(p, l, fm, kslice, slices, out);
+    } else {
+        if (bf16) err = launch_d<Bf16, 1, W, true>(p, l, fm, kslice, slices, out);
+        else if (p.ob == kCol) err = launch_d<F32, 1, W, true>(p, l, fm, kslice, slices, out);
+        else err = launch_d<F32, 1, W, false>(p, l, fm, kslice, slices, out);
     }
-    if (bf16) return launch_d<Bf16, 1, W, true>(p, l, fm);
-    if (p.ob == kCol) return launch_d<F32, 1, W, true>(p, l, fm);
-    return launch_d<F32, 1, W, false>(p, l, fm);
+    if (err != hipSuccess || !split) return err;
+    const int64_t threads = (int64_t)p.M * ((p.N + 3) / 4);
+    const int vec = l.vec_c && (p.N & 3) == 0;
+    hipLaunchKernelGGL(k_sum_slices, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, l.stream, part,
+                       slices, p.M, p.N, p.C, p.ldc, vec);
+    return hipGetLastError();
 }
 
 }  // namespace gemm

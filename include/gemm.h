@@ -38,6 +38,7 @@
 #ifndef LIBGEMM_GEMM_H
 #define LIBGEMM_GEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -167,12 +168,49 @@ const char *gemm_version(void);
  *   *core_rows, *core_cols   the part of C the named kernel's own launch covers, in the
  *               orientation the library computes in: C itself when order_c is row-major,
  *               C^T (N x M) when it is column-major.  The rest of C runs as edge strips,
- *               separate GEMMs on the same stream chosen the same way.
+ *               separate GEMMs on the same stream chosen the same way;
+ *   *workspace_bytes   the workspace with which gemm_f32_ws / gemm_bf16_f32acc_ws split K
+ *               across workgroups for this problem (0: they never do).
  * Errors: GEMM_ERR_INVALID_VALUE for a null output pointer, cus <= 0, negative or too large
  * extents (> INT_MAX) or an invalid order; outputs untouched then. */
 gemm_status_t gemm_plan(int bf16, int64_t M, int64_t N, int64_t K, gemm_order_t order_a,
                         gemm_order_t order_b, gemm_order_t order_c, int cus, const char **kernel,
-                        int64_t *core_rows, int64_t *core_cols);
+                        int64_t *core_rows, int64_t *core_cols, size_t *workspace_bytes);
+
+/* ---- With a caller's workspace: split-K across workgroups ---------------------------------
+ * "A06 - Tiled Matrix Multiply (GEMM)", "The next two rungs" (split-K: workers take parts of
+ * K and a second step combines their partial sums): for problems whose output gives too few
+ * workgroups to occupy the device (few rows, or few columns after the column-major-C swap),
+ * the small-problem kernel also divides K among workgroups; each writes its partial product
+ * to the workspace and a second kernel sums the slices in slice order, so results are
+ * deterministic (identical from call to call; they may differ in the last bits from
+ * gemm_f32 / gemm_bf16_f32acc, which sum in another order).  The library still allocates
+ * nothing.
+ *
+ * gemm_workspace_size: bytes of workspace with which the _ws calls split K for this problem
+ * on the current device (the same extents and orders as the call; leading dimensions do not
+ * matter); 0 if they would not split, for invalid arguments, or without a gfx950 device.
+ *
+ * gemm_f32_ws / gemm_bf16_f32acc_ws: as gemm_f32 / gemm_bf16_f32acc.  workspace: device
+ * memory, 16-byte aligned, not overlapping A, B or C, of workspace_bytes bytes; it is used
+ * only if workspace_bytes >= gemm_workspace_size(...) and the call would split; otherwise,
+ * or with workspace == NULL, the call runs exactly as the plain one.  Its contents are
+ * scratch: overwritten by the call and meaningless afterwards.  Calls that share one
+ * workspace must not run concurrently (use one stream, or one workspace per stream).
+ * Errors: as the plain calls, plus GEMM_ERR_INVALID_VALUE for a workspace that is not
+ * 16-byte aligned. */
+size_t gemm_workspace_size(int bf16, int64_t M, int64_t N, int64_t K, gemm_order_t order_a,
+                           gemm_order_t order_b, gemm_order_t order_c);
+gemm_status_t gemm_f32_ws(int64_t M, int64_t N, int64_t K,
+                          const float *A, int64_t lda, gemm_order_t order_a,
+                          const float *B, int64_t ldb, gemm_order_t order_b,
+                          float *C, int64_t ldc, gemm_order_t order_c,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+gemm_status_t gemm_bf16_f32acc_ws(int64_t M, int64_t N, int64_t K,
+                                  const uint16_t *A, int64_t lda, gemm_order_t order_a,
+                                  const uint16_t *B, int64_t ldb, gemm_order_t order_b,
+                                  float *C, int64_t ldc, gemm_order_t order_c,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

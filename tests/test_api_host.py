@@ -237,3 +237,19 @@ def test_plan_invariants_on_random_shapes():
             assert cols % t == 0 or (bn == C_ and cols == Nn), (kernel, M, N, oa, ob, oc, cols)
         if kernel.startswith("bf16_dma"):
             assert an == R and bn == C_
+
+
+@pytest.mark.parametrize("dtype,shape,orders,expected", [
+    # 64 blocks of 16 x 16 leave most of 256 CUs idle: 16 slabs of 64 columns x 16 K slices
+    ("f32", (16, 1024, 16384), (R, R, R), 16 * 16 * 1024 * 4),
+    ("bf16", (16, 1024, 16384), (R, C_, R), 16 * 16 * 1024 * 4),
+    # its own 256 blocks fill the chip: no split
+    ("f32", (16, 4096, 4096), (R, R, R), 0),
+    ("f32", (4096, 4096, 4096), (R, R, R), 0),
+    # K too short for even two slices of one batch per wavefront
+    ("f32", (16, 1024, 500), (R, R, R), 0),
+    # column-major C: C^T has the few rows
+    ("f32", (1024, 16, 16384), (C_, C_, C_), 16 * 16 * 1024 * 4),
+], ids=lambda v: str(v))
+def test_split_k_workspace_of_known_shapes(dtype, shape, orders, expected):
+    assert g.gemm_plan(dtype, *shape, *orders, with_workspace=True)[3] == expected

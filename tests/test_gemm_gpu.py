@@ -541,3 +541,86 @@ def test_bf16_direct_unaligned_rows(oc, pad):
     assert g.gemm_last_kernel().startswith("bf16_dma")
     check(p, g.Algo.MFMA_256x256)      # bf16_mfma.hip's direct path
     assert g.gemm_last_kernel() == "bf16_mfma256x256"
+
+
+# --- split-K across workgroups with a caller's workspace (gemm_*_ws) ----------------------
+def run_ws(p, ws_bytes=None, misalign=0):
+    """C (flat) after one gemm_*_ws call with a fresh workspace; (C, bytes needed, kernel)."""
+    import torch
+    A, B = to_device(p.A), to_device(p.B)
+    C = torch.full((gi.c_buffer_size(p.M, p.N, p.ldc, p.order_c),), float("nan"), dtype=torch.float32,
+                   device="cuda")
+    need = g.gemm_workspace_size(p.dtype, p.M, p.N, p.K, p.order_a, p.order_b, p.order_c)
+    nbytes = need if ws_bytes is None else ws_bytes
+    ws = torch.full((nbytes // 4 + 64,), float("nan"), dtype=torch.float32, device="cuda")
+    fn = g.gemm_f32_ws if p.dtype == "f32" else g.gemm_bf16_f32acc_ws
+    print(f"[gpu] ws {p.dtype} M={p.M} N={p.N} K={p.K} orders=({p.order_a},{p.order_b},{p.order_c}) "
+          f"ws={nbytes}/{need}", flush=True)
+    fn(p.M, p.N, p.K, A.data_ptr(), p.lda, p.order_a, B.data_ptr(), p.ldb, p.order_b, C.data_ptr(), p.ldc,
+       p.order_c, ws.data_ptr() + misalign, nbytes, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return C.cpu().numpy(), need, g.gemm_last_kernel()
+
+
+# shapes whose own blocks leave CUs idle (few columns of C, long K), ragged in M, N and K
+WS_CASES = [("f32", ROW_MAJOR, (16, 1024, 16384)), ("f32", COL_MAJOR, (16, 1024, 16384)),
+            ("bf16", COL_MAJOR, (16, 1024, 16384)), ("f32", ROW_MAJOR, (5, 1000, 3001)),
+            ("bf16", COL_MAJOR, (33, 1030, 5000)), ("f32", ROW_MAJOR, (64, 512, 8193)),
+            ("f32", COL_MAJOR, (1, 250, 20000)), ("bf16", COL_MAJOR, (48, 70, 20000)),
+            ("f32", ROW_MAJOR, (16, 256, 65536))]
+
+
+@pytest.mark.parametrize("dtype,ob,shape", WS_CASES, ids=lambda v: str(v))
+@pytest.mark.parametrize("oc", [ROW_MAJOR, COL_MAJOR], ids=["C-R", "C-C"])
+def test_split_k_with_workspace(dtype, ob, shape, oc):
+    """K split across workgroups: parity with the oracle, a workspace actually used, and the
+    same bits on a second call (the slices are summed in a fixed order)."""
+    M, N, K = shape
+    if oc == COL_MAJOR:
+        # the library computes C^T = B^T A^T (N x M): the few rows are C's few columns, its A
+        # is B^T (row-major when B is column-major) and its B is A^T (order flipped)
+        M, N = N, M
+        p = gi.make_problem(M, N, K, dtype, 1 - ob, COL_MAJOR, oc, wid=57)
+    else:
+        p = gi.make_problem(M, N, K, dtype, ROW_MAJOR, ob, oc, wid=57)
+    flat, need, kernel = run_ws(p)
+    assert need > 0 and kernel.endswith("_splitk"), (need, kernel)
+    assert padding_untouched(p, flat)
+    ref, D = oracle.gemm(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b)
+    err = oracle.normalised_error(logical_c(p, flat), ref, D)
+    assert err <= TOL[dtype], err
+    again, _, _ = run_ws(p)
+    assert np.array_equal(flat.view(np.uint32), again.view(np.uint32)), "not deterministic"
+
+
+def test_split_k_small_integer_exact():
+    rng = np.random.default_rng(21)
+    M, N, K = 16, 1024, 6000
+    A = rng.integers(-3, 4, (M, K)).astype(np.float32)
+    B = rng.integers(-3, 4, (K, N)).astype(np.float32)
+    for dtype, ob in (("f32", ROW_MAJOR), ("bf16", COL_MAJOR)):
+        p = gi.make_problem(M, N, K, dtype, ROW_MAJOR, ob, A_logical=A, B_logical=B)
+        flat, need, kernel = run_ws(p)
+        assert need > 0 and kernel.endswith("_splitk")
+        ref, _ = oracle.gemm(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b)
+        assert np.array_equal(logical_c(p, flat).astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("dtype,ob", [("f32", ROW_MAJOR), ("bf16", COL_MAJOR)], ids=["f32", "bf16"])
+def test_workspace_too_small_or_absent_runs_the_plain_path(dtype, ob):
+    p = gi.make_problem(16, 1024, 16384, dtype, ROW_MAJOR, ob, wid=58)
+    plain = run(p)
+    plain_kernel = g.gemm_last_kernel()
+    need = g.gemm_workspace_size(dtype, p.M, p.N, p.K, p.order_a, p.order_b, p.order_c)
+    assert need > 0
+    for nbytes in (0, need - 4):
+        flat, _, kernel = run_ws(p, ws_bytes=nbytes)
+        assert kernel == plain_kernel
+        assert np.array_equal(flat.view(np.uint32), plain.view(np.uint32))
+
+
+def test_workspace_must_be_16_byte_aligned():
+    p = gi.make_problem(16, 4096, 4096, "f32", ROW_MAJOR, ROW_MAJOR, wid=59)
+    with pytest.raises(g.GemmError) as e:
+        run_ws(p, misalign=4)
+    assert e.value.status == g.Status.ERR_INVALID_VALUE

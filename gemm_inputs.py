@@ -59,6 +59,9 @@ WORKLOADS = {
         Workload("llm_attn_proj_2048x4096x4096", 5, 2048, 4096, 4096, "bf16", ROW_MAJOR, COL_MAJOR, ROW_MAJOR, "llm"),
         Workload("llm_ffn_up_2048x11008x4096", 5, 2048, 11008, 4096, "bf16", ROW_MAJOR, COL_MAJOR, ROW_MAJOR, "llm"),
         Workload("llm_ffn_down_2048x4096x11008", 5, 2048, 4096, 11008, "bf16", ROW_MAJOR, COL_MAJOR, ROW_MAJOR, "llm"),
+        # few columns of C and a long K: too few output blocks for the CUs (split-K's case)
+        Workload("fewcols16x1024x16384_f32", 6, 16, 1024, 16384, "f32"),
+        Workload("fewcols16x1024x16384_bf16", 6, 16, 1024, 16384, "bf16", ROW_MAJOR, COL_MAJOR),
     ]
 }
 

@@ -34,3 +34,33 @@ def test_workload_full_size_sampled(name):
     err = oracle.normalised_error(C[rows, cols], ref, D)
     print(f"{name}: normalised error {err:.3e} over {rows.size} sampled outputs")
     assert err <= TOL[p.dtype]
+
+
+@pytest.mark.parametrize("name", [n for n, w in gi.WORKLOADS.items() if n.startswith("fewcols")])
+def test_workload_full_size_sampled_with_workspace(name):
+    """The workspace entry point (split-K across workgroups) at the workload's full size."""
+    import torch
+    import gemm_f32_amd as g
+    from gpu_util import to_device
+    p = gi.workload_problem(name)
+    need = g.gemm_workspace_size(p.dtype, p.M, p.N, p.K, p.order_a, p.order_b, p.order_c)
+    assert need > 0
+    A, B = to_device(p.A), to_device(p.B)
+    C = torch.full((gi.c_buffer_size(p.M, p.N, p.ldc, p.order_c),), float("nan"), dtype=torch.float32,
+                   device="cuda")
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    fn = g.gemm_f32_ws if p.dtype == "f32" else g.gemm_bf16_f32acc_ws
+    print(f"[gpu] ws workload {name}", flush=True)
+    fn(p.M, p.N, p.K, A.data_ptr(), p.lda, p.order_a, B.data_ptr(), p.ldb, p.order_b, C.data_ptr(), p.ldc,
+       p.order_c, ws.data_ptr(), need, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert g.gemm_last_kernel().endswith("_splitk")
+    flat = C.cpu().numpy()
+    assert padding_untouched(p, flat)
+    Cl = logical_c(p, flat)
+    assert np.all(np.isfinite(Cl))
+    rows, cols = sample_indices(p.M, p.N, gi.WORKLOADS[name].wid)
+    ref, D = oracle.gemm_sampled(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b, rows, cols)
+    err = oracle.normalised_error(Cl[rows, cols], ref, D)
+    print(f"{name} (workspace): normalised error {err:.3e} over {rows.size} sampled outputs")
+    assert err <= TOL[p.dtype]

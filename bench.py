@@ -140,13 +140,13 @@ class Leg:
             p = gi.make_problem(w.M, w.N, w.K, w.dtype, w.order_a, w.order_b, w.order_c, w.dist,
                                 w.wid + 1000 * s)
             self.problems.append(p)
-            conv = (lambda b: b.view(np.int16)) if w.dtype == "bf16" else (lambda b: b)
+            conv = (lambda b: b.view(np.int16)) if w.dtype in ("bf16", "f16") else (lambda b: b)
             self.A.append(torch.from_numpy(conv(p.A)).to("cuda"))
             self.B.append(torch.from_numpy(conv(p.B)).to("cuda"))
         p = self.problems[0]
         self.C = torch.empty(gi.c_buffer_size(p.M, p.N, p.ldc, p.order_c), dtype=torch.float32,
                              device="cuda")
-        self.fn = g.gemm_f32_algo if w.dtype == "f32" else g.gemm_bf16_f32acc_algo
+        self.fn = {"f32": g.gemm_f32_algo, "bf16": g.gemm_bf16_f32acc_algo, "f16": g.gemm_f16_f32acc_algo}[w.dtype]
         self.flops = 2 * w.M * w.N * w.K
         self.kernel = None
         self.ws, self.ws_bytes = None, 0
@@ -157,7 +157,7 @@ class Leg:
             self.ws_bytes = g.gemm_workspace_size(w.dtype, p0.M, p0.N, p0.K, p0.order_a, p0.order_b,
                                                   p0.order_c)
             self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device="cuda")
-            self.fn_ws = g.gemm_f32_ws if w.dtype == "f32" else g.gemm_bf16_f32acc_ws
+            self.fn_ws = {"f32": g.gemm_f32_ws, "bf16": g.gemm_bf16_f32acc_ws, "f16": g.gemm_f16_f32acc_ws}[w.dtype]
 
     def launch(self, s, stream):
         p = self.problems[s % len(self.problems)]

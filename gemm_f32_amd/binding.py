@@ -89,15 +89,21 @@ def _load():
     lib.gemm_plan.restype = ci
     lib.gemm_workspace_size.argtypes = [ci, i64, i64, i64, ci, ci, ci]
     lib.gemm_workspace_size.restype = ctypes.c_size_t
-    for name in ("gemm_f32_ws", "gemm_bf16_f32acc_ws"):
+    for name in ("gemm_f32_ws", "gemm_bf16_f32acc_ws", "gemm_f16_f32acc_ws"):
         f = getattr(lib, name)
         f.argtypes, f.restype = args[:-1] + [vp, ctypes.c_size_t, vp], ci
+    lib.gemm_f16_f32acc.argtypes, lib.gemm_f16_f32acc.restype = args, ci
+    lib.gemm_f16_f32acc_algo.argtypes, lib.gemm_f16_f32acc_algo.restype = [ci] + args, ci
     return lib
 
 
 EXPORTED = ("gemm_f32", "gemm_bf16_f32acc", "gemm_f32_algo", "gemm_bf16_f32acc_algo",
             "gemm_status_string", "gemm_last_hip_error", "gemm_last_kernel", "gemm_version",
-            "gemm_plan", "gemm_workspace_size", "gemm_f32_ws", "gemm_bf16_f32acc_ws")
+            "gemm_plan", "gemm_workspace_size", "gemm_f32_ws", "gemm_bf16_f32acc_ws",
+            "gemm_f16_f32acc", "gemm_f16_f32acc_algo", "gemm_f16_f32acc_ws")
+
+# dtype codes of gemm_plan / gemm_workspace_size
+DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2}
 
 
 def library_path() -> str:
@@ -152,7 +158,7 @@ def gemm_plan(dtype, M, N, K, order_a, order_b, order_c, cus=256, with_workspace
     """(kernel, core_rows, core_cols) the default choice would run, plus the split-K workspace
     bytes when with_workspace; no device needed."""
     kernel, rows, cols, ws = ctypes.c_char_p(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
-    _check(lib_handle().gemm_plan(1 if dtype == "bf16" else 0, M, N, K, order_a, order_b, order_c, cus,
+    _check(lib_handle().gemm_plan(DTYPE_CODE[dtype], M, N, K, order_a, order_b, order_c, cus,
                                   ctypes.byref(kernel), ctypes.byref(rows), ctypes.byref(cols),
                                   ctypes.byref(ws)), "gemm_plan")
     out = (kernel.value.decode(), rows.value, cols.value)
@@ -161,8 +167,7 @@ def gemm_plan(dtype, M, N, K, order_a, order_b, order_c, cus=256, with_workspace
 
 def gemm_workspace_size(dtype, M, N, K, order_a, order_b, order_c) -> int:
     """Workspace bytes with which the _ws calls split K on the current device (0: no split)."""
-    return lib_handle().gemm_workspace_size(1 if dtype == "bf16" else 0, M, N, K, order_a, order_b,
-                                            order_c)
+    return lib_handle().gemm_workspace_size(DTYPE_CODE[dtype], M, N, K, order_a, order_b, order_c)
 
 
 def gemm_f32_ws(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, workspace, workspace_bytes,
@@ -170,6 +175,24 @@ def gemm_f32_ws(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, work
     """gemm_f32 with a caller's workspace (device pointer, bytes) for split-K."""
     _check(lib_handle().gemm_f32_ws(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, workspace,
                                     workspace_bytes, stream), "gemm_f32_ws")
+
+
+def gemm_f16_f32acc(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, stream=0):
+    """C = A.B with IEEE fp16 A and B (bit patterns), FP32 accumulate and FP32 C."""
+    _check(lib_handle().gemm_f16_f32acc(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, stream),
+           "gemm_f16_f32acc")
+
+
+def gemm_f16_f32acc_algo(algo, M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, stream=0):
+    _check(lib_handle().gemm_f16_f32acc_algo(int(algo), M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc,
+                                             order_c, stream), "gemm_f16_f32acc_algo")
+
+
+def gemm_f16_f32acc_ws(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, workspace,
+                       workspace_bytes, stream=0):
+    """gemm_f16_f32acc with a caller's workspace (device pointer, bytes) for split-K."""
+    _check(lib_handle().gemm_f16_f32acc_ws(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c,
+                                           workspace, workspace_bytes, stream), "gemm_f16_f32acc_ws")
 
 
 def gemm_bf16_f32acc_ws(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, workspace,

@@ -17,7 +17,9 @@ namespace {
 thread_local int t_last_hip_error = 0;
 thread_local const char* t_last_kernel = "none";
 
-enum class In { F32, BF16 };
+enum class In { F32, BF16, F16 };
+
+int elem_of(In in) { return in == In::F32 ? kElemF32 : in == In::BF16 ? kElemBf16 : kElemF16; }
 
 struct DeviceInfo {
     bool supported = false;
@@ -87,8 +89,11 @@ bool prefer_small(const Problem& p, int cus) {
     return p.M <= kSkinnyMaxM || t64 * 2 < c || (tiles(p.M, p.N, 128, 128) < c && t64 <= c);
 }
 
-const char* skinny_name(bool bf16, int fn) {
-    return bf16 ? (fn == 4 ? "bf16_skinny64" : "bf16_skinny16") : (fn == 4 ? "f32_skinny64" : "f32_skinny16");
+// Kernel names as gemm_last_kernel() reports them: the input type, then the kernel.
+const char* skinny_name(int et, int fn) {
+    static const char* names[3][2] = {{"f32_skinny16", "f32_skinny64"}, {"bf16_skinny16", "bf16_skinny64"},
+                                      {"f16_skinny16", "f16_skinny64"}};
+    return names[et][fn == 4 ? 1 : 0];
 }
 
 // A caller's workspace (gemm_*_ws); empty for the plain entry points.
@@ -98,23 +103,24 @@ struct Workspace {
 };
 
 // The split the small-problem kernel takes with this workspace (slices == 1: none).
-SkinnySplit split_with(const Problem& p, bool bf16, int cus, const Workspace& ws) {
+SkinnySplit split_with(const Problem& p, int et, int cus, const Workspace& ws) {
     if (ws.ptr == nullptr || !aligned(ws.ptr, 16)) return SkinnySplit{};
-    const SkinnySplit sp = skinny_split(p, bf16, cus);
+    const SkinnySplit sp = skinny_split(p, et != kElemF32, cus);
     return sp.slices > 1 && sp.bytes <= ws.bytes ? sp : SkinnySplit{};
 }
 
 // The small-problem kernel, with 1 or 4 column blocks of 16 per workgroup.
-hipError_t run_skinny(const Problem& p, const Launch& l, bool bf16, int cus, const char*& name,
+hipError_t run_skinny(const Problem& p, const Launch& l, int et, int cus, const char*& name,
                       const Workspace& ws = Workspace{}) {
-    const SkinnySplit sp = split_with(p, bf16, cus, ws);
+    const SkinnySplit sp = split_with(p, et, cus, ws);
     if (sp.slices > 1) {       // K split across workgroups too: partial products in the workspace
-        name = bf16 ? "bf16_skinny64_splitk" : "f32_skinny64_splitk";
-        return launch_skinny(p, l, bf16, sp.fn, sp.fm, &sp, static_cast<float*>(ws.ptr));
+        static const char* names[3] = {"f32_skinny64_splitk", "bf16_skinny64_splitk", "f16_skinny64_splitk"};
+        name = names[et];
+        return launch_skinny(p, l, et, sp.fn, sp.fm, &sp, static_cast<float*>(ws.ptr));
     }
     const int fn = skinny_blocks(p, cus);
-    name = skinny_name(bf16, fn);
-    return launch_skinny(p, l, bf16, fn, skinny_strips(p, fn, cus));
+    name = skinny_name(et, fn);
+    return launch_skinny(p, l, et, fn, skinny_strips(p, fn, cus));
 }
 
 // Block-tile choice.  The grid runs in rounds of cus x per_cu resident blocks (per_cu: how
@@ -238,14 +244,14 @@ Problem sub_problem(const Problem& p, int r0, int m, int c0, int n, int elem) {
     return s;
 }
 
-hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, bool f32, const DeviceInfo& dev,
+hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, int et, const DeviceInfo& dev,
                     const char*& name, gemm_status_t& st, const Workspace& ws = Workspace{});
 
 // Run a plan's core with `core` and its strips through the default choice, on one stream.
 template <typename CoreFn>
-hipError_t run_plan(const Problem& p, hipStream_t stream, const Plan& pl, bool f32, const DeviceInfo& dev,
+hipError_t run_plan(const Problem& p, hipStream_t stream, const Plan& pl, int et, const DeviceInfo& dev,
                     CoreFn core) {
-    const int e = f32 ? 4 : 2;
+    const int e = et == kElemF32 ? 4 : 2;
     const Problem c = sub_problem(p, 0, pl.mc, 0, pl.nc, e);
     Launch lc = launch_for(c, stream);
     lc.group_m = pick_group_m((c.M + pl.opt.bm - 1) / pl.opt.bm, (c.N + pl.opt.bn - 1) / pl.opt.bn);
@@ -253,9 +259,9 @@ hipError_t run_plan(const Problem& p, hipStream_t stream, const Plan& pl, bool f
     const char* ignored = nullptr;
     gemm_status_t st = GEMM_OK;
     if (err == hipSuccess && pl.mc < p.M)        // rows mc .. M-1, all columns
-        err = dispatch(sub_problem(p, pl.mc, p.M - pl.mc, 0, p.N, e), stream, GEMM_ALGO_AUTO, f32, dev, ignored, st);
+        err = dispatch(sub_problem(p, pl.mc, p.M - pl.mc, 0, p.N, e), stream, GEMM_ALGO_AUTO, et, dev, ignored, st);
     if (err == hipSuccess && pl.nc < p.N)        // rows 0 .. mc-1, columns nc .. N-1
-        err = dispatch(sub_problem(p, 0, pl.mc, pl.nc, p.N - pl.nc, e), stream, GEMM_ALGO_AUTO, f32, dev, ignored, st);
+        err = dispatch(sub_problem(p, 0, pl.mc, pl.nc, p.N - pl.nc, e), stream, GEMM_ALGO_AUTO, et, dev, ignored, st);
     return err;
 }
 
@@ -263,10 +269,12 @@ const char* f32_name(const TileOpt& o) {
     if (o.dma) return o.bm == 256 ? "f32_dma256x256" : "f32_dma128x128";
     return o.bm == 64 ? "f32_mfma64x64" : "f32_mfma128x128";
 }
-const char* bf16_name(const TileOpt& o) {
-    if (o.dma) return o.bn == 256 ? "bf16_dma256x256" : "bf16_dma256x128";
-    static const char* names[] = {"bf16_mfma256x256", "bf16_mfma256x128", "bf16_mfma128x128", "bf16_mfma64x64"};
-    return names[o.bm == 256 ? (o.bn == 256 ? 0 : 1) : (o.bm == 128 ? 2 : 3)];
+const char* b16_name(const TileOpt& o, int et) {
+    static const char* names[2][6] = {
+        {"bf16_dma256x256", "bf16_dma256x128", "bf16_mfma256x256", "bf16_mfma256x128", "bf16_mfma128x128", "bf16_mfma64x64"},
+        {"f16_dma256x256", "f16_dma256x128", "f16_mfma256x256", "f16_mfma256x128", "f16_mfma128x128", "f16_mfma64x64"}};
+    const int i = o.dma ? (o.bn == 256 ? 0 : 1) : (o.bm == 256 ? (o.bn == 256 ? 2 : 3) : (o.bm == 128 ? 4 : 5));
+    return names[et == kElemF16 ? 1 : 0][i];
 }
 
 // The FP32 matrix-core kernels: the cheapest plan over the allowed options.
@@ -296,7 +304,7 @@ hipError_t run_f32_tiles(const Problem& p, hipStream_t stream, gemm_algo_t algo,
     if (best.cost >= 1e300) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
     name = f32_name(best.opt);
     const TileOpt o = best.opt;
-    return run_plan(p, stream, best, true, dev, [&](const Problem& c, const Launch& lc) {
+    return run_plan(p, stream, best, kElemF32, dev, [&](const Problem& c, const Launch& lc) {
         return o.dma ? launch_f32_dma(c, lc, o.bm, o.bn) : launch_f32_mfma(c, lc, o.bm);
     });
 }
@@ -323,23 +331,24 @@ Plan choose_bf16_tiles(const Problem& p, gemm_algo_t algo, int cus) {
     return best;
 }
 
-hipError_t run_bf16_tiles(const Problem& p, hipStream_t stream, gemm_algo_t algo, const DeviceInfo& dev,
-                          const char*& name, gemm_status_t& st) {
+hipError_t run_b16_tiles(const Problem& p, hipStream_t stream, gemm_algo_t algo, int et, const DeviceInfo& dev,
+                         const char*& name, gemm_status_t& st) {
     const Plan best = choose_bf16_tiles(p, algo, dev.cus);
     if (best.cost >= 1e300) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
-    name = bf16_name(best.opt);
+    name = b16_name(best.opt, et);
     const TileOpt o = best.opt;
-    return run_plan(p, stream, best, false, dev, [&](const Problem& c, const Launch& lc) {
-        return o.dma ? launch_bf16_dma(c, lc, o.bm, o.bn) : launch_bf16_mfma(c, lc, o.bm, o.bn);
+    const bool f16 = et == kElemF16;
+    return run_plan(p, stream, best, et, dev, [&](const Problem& c, const Launch& lc) {
+        return o.dma ? launch_bf16_dma(c, lc, o.bm, o.bn, f16) : launch_bf16_mfma(c, lc, o.bm, o.bn, f16);
     });
 }
 
 // Kernel choice and launch for a normalised problem (row-major C, K > 0).  A status other
 // than GEMM_OK in `st` means the request is invalid (nothing launched).
-hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, bool f32, const DeviceInfo& dev,
+hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, int et, const DeviceInfo& dev,
                     const char*& name, gemm_status_t& st, const Workspace& ws) {
     Launch l = launch_for(p, stream);
-    if (f32) {
+    if (et == kElemF32) {
         switch (algo) {
             case GEMM_ALGO_NAIVE_UNCOALESCED: name = "f32_naive_uncoalesced"; return launch_naive(p, l, false);
             case GEMM_ALGO_NAIVE: name = "f32_naive"; return launch_naive(p, l, true);
@@ -350,25 +359,26 @@ hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, bool
                 return launch_regblock(p, l);
             case GEMM_ALGO_SKINNY:
                 if (!skinny_applies(p, false)) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
-                return run_skinny(p, l, false, dev.cus, name);
+                return run_skinny(p, l, kElemF32, dev.cus, name);
             default:
                 if (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus) && skinny_applies(p, false))
-                    return run_skinny(p, l, false, dev.cus, name, ws);
+                    return run_skinny(p, l, kElemF32, dev.cus, name, ws);
                 return run_f32_tiles(p, stream, algo, dev, name, st);
         }
     }
     if (algo == GEMM_ALGO_SKINNY ||
         (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus) && skinny_applies(p, true))) {
         if (!skinny_applies(p, true)) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
-        return run_skinny(p, l, true, dev.cus, name, algo == GEMM_ALGO_AUTO ? ws : Workspace{});
+        return run_skinny(p, l, et, dev.cus, name, algo == GEMM_ALGO_AUTO ? ws : Workspace{});
     }
     if (algo == GEMM_ALGO_MFMA_PINGPONG) {
-        if (!bf16_pingpong_applies(p, l)) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
+        // the ping-pong kernel is a BF16-only rung of the ladder
+        if (et != kElemBf16 || !bf16_pingpong_applies(p, l)) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
         l.group_m = pick_group_m(p.M / 256, p.N / 256);
         name = "bf16_pingpong256x256";
         return launch_bf16_pingpong(p, l);
     }
-    return run_bf16_tiles(p, stream, algo, dev, name, st);
+    return run_b16_tiles(p, stream, algo, et, dev, name, st);
 }
 
 // The problem the library computes for extents and orders with tight leading dimensions and
@@ -381,23 +391,24 @@ Problem query_problem(int64_t M, int64_t N, int64_t K, int oa, int ob, int oc) {
 }
 
 // Workspace bytes with which the _ws entry points split K (0: they never do for this problem).
-size_t split_bytes(const Problem& p, bool f32, int cus) {
+size_t split_bytes(const Problem& p, int et, int cus) {
     if (p.M == 0 || p.N == 0 || p.K == 0) return 0;
-    if (!(prefer_small(p, cus) && skinny_applies(p, !f32))) return 0;
-    const SkinnySplit sp = skinny_split(p, !f32, cus);
+    if (!(prefer_small(p, cus) && skinny_applies(p, et != kElemF32))) return 0;
+    const SkinnySplit sp = skinny_split(p, et != kElemF32, cus);
     return sp.slices > 1 ? sp.bytes : 0;
 }
 
 // What the default choice runs for a normalised problem with K > 0, without launching: the
 // kernel's name and the rows and columns of C its own launch covers (the rest are strips).
-const char* plan_auto(const Problem& p, bool f32, int cus, int& mc, int& nc) {
+const char* plan_auto(const Problem& p, int et, int cus, int& mc, int& nc) {
+    const bool f32 = et == kElemF32;
     mc = p.M;
     nc = p.N;
-    if (prefer_small(p, cus) && skinny_applies(p, !f32)) return skinny_name(!f32, skinny_blocks(p, cus));
+    if (prefer_small(p, cus) && skinny_applies(p, !f32)) return skinny_name(et, skinny_blocks(p, cus));
     const Plan pl = f32 ? choose_f32_tiles(p, GEMM_ALGO_AUTO, cus) : choose_bf16_tiles(p, GEMM_ALGO_AUTO, cus);
     mc = pl.mc;
     nc = pl.nc;
-    return f32 ? f32_name(pl.opt) : bf16_name(pl.opt);
+    return f32 ? f32_name(pl.opt) : b16_name(pl.opt, et);
 }
 
 template <typename Elem>
@@ -444,7 +455,7 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
         name = "zero_c";
     } else {
         gemm_status_t bad = GEMM_OK;
-        err = dispatch(p, stream, algo, f32, dev, name, bad, ws);
+        err = dispatch(p, stream, algo, elem_of(in), dev, name, bad, ws);
         if (bad != GEMM_OK) return bad;
     }
     if (err != hipSuccess) {
@@ -492,11 +503,11 @@ gemm_status_t gemm_bf16_f32acc_algo(gemm_algo_t algo, int64_t M, int64_t N, int6
                      order_c, stream);
 }
 
-gemm_status_t gemm_plan(int bf16, int64_t M, int64_t N, int64_t K, gemm_order_t order_a,
+gemm_status_t gemm_plan(int dtype, int64_t M, int64_t N, int64_t K, gemm_order_t order_a,
                         gemm_order_t order_b, gemm_order_t order_c, int cus, const char** kernel,
                         int64_t* core_rows, int64_t* core_cols, size_t* workspace_bytes) {
     if (kernel == nullptr || core_rows == nullptr || core_cols == nullptr || workspace_bytes == nullptr ||
-        cus <= 0)
+        cus <= 0 || dtype < 0 || dtype > 2)
         return GEMM_ERR_INVALID_VALUE;
     if (M < 0 || N < 0 || K < 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return GEMM_ERR_INVALID_VALUE;
     for (int o : {(int)order_a, (int)order_b, (int)order_c})
@@ -513,21 +524,21 @@ gemm_status_t gemm_plan(int bf16, int64_t M, int64_t N, int64_t K, gemm_order_t 
         return GEMM_OK;
     }
     int mc = 0, nc = 0;
-    *kernel = gemm::plan_auto(p, bf16 == 0, cus, mc, nc);
+    *kernel = gemm::plan_auto(p, dtype, cus, mc, nc);
     *core_rows = mc;
     *core_cols = nc;
-    *workspace_bytes = gemm::split_bytes(p, bf16 == 0, cus);
+    *workspace_bytes = gemm::split_bytes(p, dtype, cus);
     return GEMM_OK;
 }
 
-size_t gemm_workspace_size(int bf16, int64_t M, int64_t N, int64_t K, gemm_order_t order_a,
+size_t gemm_workspace_size(int dtype, int64_t M, int64_t N, int64_t K, gemm_order_t order_a,
                            gemm_order_t order_b, gemm_order_t order_c) {
-    if (M <= 0 || N <= 0 || K <= 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return 0;
+    if (M <= 0 || N <= 0 || K <= 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX || dtype < 0 || dtype > 2) return 0;
     for (int o : {(int)order_a, (int)order_b, (int)order_c})
         if (o != GEMM_ROW_MAJOR && o != GEMM_COL_MAJOR) return 0;
     gemm::DeviceInfo dev;
     if (!gemm::device_info(dev) || !dev.supported) return 0;
-    return gemm::split_bytes(gemm::query_problem(M, N, K, order_a, order_b, order_c), bf16 == 0, dev.cus);
+    return gemm::split_bytes(gemm::query_problem(M, N, K, order_a, order_b, order_c), dtype, dev.cus);
 }
 
 gemm_status_t gemm_f32_ws(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
@@ -543,6 +554,28 @@ gemm_status_t gemm_bf16_f32acc_ws(int64_t M, int64_t N, int64_t K, const uint16_
                                   gemm_order_t order_b, float* C, int64_t ldc, gemm_order_t order_c,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return gemm::run(gemm::In::BF16, GEMM_ALGO_AUTO, M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc,
+                     order_c, stream, gemm::Workspace{workspace, workspace_bytes});
+}
+
+gemm_status_t gemm_f16_f32acc(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                              gemm_order_t order_a, const uint16_t* B, int64_t ldb, gemm_order_t order_b,
+                              float* C, int64_t ldc, gemm_order_t order_c, hipStream_t stream) {
+    return gemm::run(gemm::In::F16, GEMM_ALGO_AUTO, M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc,
+                     order_c, stream);
+}
+
+gemm_status_t gemm_f16_f32acc_algo(gemm_algo_t algo, int64_t M, int64_t N, int64_t K, const uint16_t* A,
+                                   int64_t lda, gemm_order_t order_a, const uint16_t* B, int64_t ldb,
+                                   gemm_order_t order_b, float* C, int64_t ldc, gemm_order_t order_c,
+                                   hipStream_t stream) {
+    return gemm::run(gemm::In::F16, algo, M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, stream);
+}
+
+gemm_status_t gemm_f16_f32acc_ws(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                                 gemm_order_t order_a, const uint16_t* B, int64_t ldb, gemm_order_t order_b,
+                                 float* C, int64_t ldc, gemm_order_t order_c, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    return gemm::run(gemm::In::F16, GEMM_ALGO_AUTO, M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc,
                      order_c, stream, gemm::Workspace{workspace, workspace_bytes});
 }
 

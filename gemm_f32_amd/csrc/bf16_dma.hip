@@ -42,6 +42,7 @@
 // block below 2^31.  Any M, N.
 #include "common.hpp"
 #include "launch.hpp"
+#include "mma16.hpp"
 
 namespace gemm {
 namespace {
@@ -95,7 +96,7 @@ struct Cfg {
     static_assert(NW % 4 == 0, "whole wavefronts per SIMD");
 };
 
-template <typename C, bool VEC_C>
+template <typename C, bool VEC_C, bool F16 = false>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::NW / 4, C::NW / 4)))
 void k_bf16_dma(Problem p, int tiles_m, int tiles_n, int group_m) {
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, FM = C::FM, FN = C::FN, SUB = C::SUB;
@@ -182,7 +183,7 @@ void k_bf16_dma(Problem p, int tiles_m, int tiles_n, int group_m) {
     };
     auto mfma = [&](int m, int b) {
         const int i = m / FN, j = m % FN;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[b][i], fb[b][j], acc[i][j], 0, 0, 0);
+        acc[i][j] = mma_32x32x16<F16>(fa[b][i], fb[b][j], acc[i][j]);
     };
 
     // ---- software pipeline over k-tiles, S LDS stages (tile t in stage t % S).  Iteration
@@ -350,10 +351,14 @@ void k_bf16_dma(Problem p, int tiles_m, int tiles_n, int group_m) {
 }
 
 template <typename C>
-hipError_t launch_cfg(const Problem& p, const Launch& l) {
+hipError_t launch_cfg(const Problem& p, const Launch& l, bool f16) {
     const int tiles_m = (p.M + C::BM - 1) / C::BM, tiles_n = (p.N + C::BN - 1) / C::BN;
     const dim3 grid((unsigned)tiles_m * tiles_n), block(C::THREADS);
-    if (l.vec_c)
+    if (f16 && l.vec_c)
+        hipLaunchKernelGGL((k_bf16_dma<C, true, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
+    else if (f16)
+        hipLaunchKernelGGL((k_bf16_dma<C, false, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
+    else if (l.vec_c)
         hipLaunchKernelGGL((k_bf16_dma<C, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
     else
         hipLaunchKernelGGL((k_bf16_dma<C, false>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
@@ -375,9 +380,9 @@ bool bf16_dma_applies(const Problem& p, const Launch&, int, int) {
 // Measured per 64-deep k-tile at 4096^3 (in-kernel clock): 256 x 256 2270 cycles against
 // 2048 of matrix work; 256 x 128 1350 against 1024 (four wavefronts of 128 x 64: 1425 with
 // three stages, 1540-1630 with two).
-hipError_t launch_bf16_dma(const Problem& p, const Launch& l, int bm, int bn) {
-    if (bm == 256 && bn == 256) return launch_cfg<Cfg<256, 256, 2, 4, 2, 2>>(p, l);
-    if (bm == 256 && bn == 128) return launch_cfg<Cfg<256, 128, 4, 2, 4, 3>>(p, l);
+hipError_t launch_bf16_dma(const Problem& p, const Launch& l, int bm, int bn, bool f16) {
+    if (bm == 256 && bn == 256) return launch_cfg<Cfg<256, 256, 2, 4, 2, 2>>(p, l, f16);
+    if (bm == 256 && bn == 128) return launch_cfg<Cfg<256, 128, 4, 2, 4, 3>>(p, l, f16);
     return hipErrorInvalidValue;
 }
 

@@ -45,6 +45,7 @@
 //  * Tile order from the XCD-aware, group-M scheduler in common.hpp.
 #include "common.hpp"
 #include "launch.hpp"
+#include "mma16.hpp"
 
 namespace gemm {
 namespace {
@@ -149,7 +150,7 @@ __device__ __forceinline__ void store_rc(unsigned char* s, int q, uint4 v) {
     }
 }
 
-template <int BM, int BN, int BK, int S, bool A_KC, bool B_KC>
+template <int BM, int BN, int BK, int S, bool A_KC, bool B_KC, bool F16 = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, int vec_b, int direct) {
     using T = Tile<BM, BN, BK, S>;
@@ -281,8 +282,7 @@ void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, in
                         *reinterpret_cast<const bf16x8*>(st + b_off + (m - T::FM) * 32 * T::ROW + coff);
                 if (m < MF) {
                     const int i = m / T::FN, j = m % T::FN;
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j],
-                                                                         acc[i][j], 0, 0, 0);
+                    acc[i][j] = mma_32x32x16<F16>(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -391,31 +391,36 @@ void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, in
         }
 }
 
-template <int BM, int BN, int BK, int S>
-hipError_t launch_tile(const Problem& p, const Launch& l) {
+template <int BM, int BN, int BK, int S, bool F16>
+hipError_t launch_tile_t(const Problem& p, const Launch& l) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const dim3 grid((unsigned)tiles_m * tiles_n), block(256);
     const bool akc = p.oa == kRow, bkc = p.ob == kCol;
     const int va = l.vec_a, vb = l.vec_b, g = l.group_m, al = l.vec_a && l.vec_b;   // direct copies allowed
     if (akc && bkc)
-        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, true, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
+        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, true, true, F16>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
     else if (akc)
-        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, true, false>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
+        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, true, false, F16>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
     else if (bkc)
-        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, false, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
+        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, false, true, F16>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
     else
-        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, false, false>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
+        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, false, false, F16>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
     return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int S>
+hipError_t launch_tile(const Problem& p, const Launch& l, bool f16) {
+    return f16 ? launch_tile_t<BM, BN, BK, S, true>(p, l) : launch_tile_t<BM, BN, BK, S, false>(p, l);
 }
 
 }  // namespace
 
 // Tile configurations: block tile, k-tile depth and LDS stages.
-hipError_t launch_bf16_mfma(const Problem& p, const Launch& l, int bm, int bn) {
-    if (bm == 256 && bn == 256) return launch_tile<256, 256, 64, 2>(p, l);   // 128 KB LDS
-    if (bm == 256 && bn == 128) return launch_tile<256, 128, 64, 3>(p, l);   // 144 KB
-    if (bm == 128 && bn == 128) return launch_tile<128, 128, 64, 2>(p, l);   //  64 KB
-    if (bm == 64 && bn == 64) return launch_tile<64, 64, 64, 2>(p, l);       //  32 KB
+hipError_t launch_bf16_mfma(const Problem& p, const Launch& l, int bm, int bn, bool f16) {
+    if (bm == 256 && bn == 256) return launch_tile<256, 256, 64, 2>(p, l, f16);   // 128 KB LDS
+    if (bm == 256 && bn == 128) return launch_tile<256, 128, 64, 3>(p, l, f16);   // 144 KB
+    if (bm == 128 && bn == 128) return launch_tile<128, 128, 64, 2>(p, l, f16);   //  64 KB
+    if (bm == 64 && bn == 64) return launch_tile<64, 64, 64, 2>(p, l, f16);       //  32 KB
     return hipErrorInvalidValue;
 }
 

@@ -19,12 +19,16 @@ hipError_t launch_f32_mfma(const Problem& p, const Launch& l, int bm);
 // f32_dma_applies says whether the whole-tile part of a problem may run there.
 bool f32_dma_applies(const Problem& p, const Launch& l, int bm, int bn);
 hipError_t launch_f32_dma(const Problem& p, const Launch& l, int bm, int bn);
+// Input element types of the kernels that take more than one
+constexpr int kElemF32 = 0, kElemBf16 = 1, kElemF16 = 2;
 // BF16 direct-copy kernel (bf16_dma.hip): row-major A, column-major B, any M, N, K >= 64,
-// 256x256 or 256x128 tiles; bf16_dma_applies checks the layouts and offset ranges.
+// 256x256 or 256x128 tiles; bf16_dma_applies checks the layouts and offset ranges.  With
+// f16 the same kernel on IEEE fp16 inputs.
 bool bf16_dma_applies(const Problem& p, const Launch& l, int bm, int bn);
-hipError_t launch_bf16_dma(const Problem& p, const Launch& l, int bm, int bn);
-// BF16 matrix-core kernel (bf16_mfma.hip); tile is one of 256x256, 256x128, 128x128, 64x64
-hipError_t launch_bf16_mfma(const Problem& p, const Launch& l, int bm, int bn);
+hipError_t launch_bf16_dma(const Problem& p, const Launch& l, int bm, int bn, bool f16 = false);
+// BF16 matrix-core kernel (bf16_mfma.hip); tile is one of 256x256, 256x128, 128x128, 64x64;
+// f16: fp16 inputs
+hipError_t launch_bf16_mfma(const Problem& p, const Launch& l, int bm, int bn, bool f16 = false);
 // BF16 256 x 256 eight-wavefront ping-pong kernel (bf16_pingpong.hip), for row-major A,
 // column-major B, aligned, M and N multiples of 256, K a multiple of 32
 bool bf16_pingpong_applies(const Problem& p, const Launch& l);
@@ -51,8 +55,9 @@ struct SkinnySplit {
     size_t bytes = 0;
 };
 SkinnySplit skinny_split(const Problem& p, bool bf16, int cus);
-// `sp` and `part` (16-byte aligned, sp->bytes) select the split; nullptr: one pass into C
-hipError_t launch_skinny(const Problem& p, const Launch& l, bool bf16, int fn, int fm,
+// `et`: kElemF32, kElemBf16 or kElemF16.  `sp` and `part` (16-byte aligned, sp->bytes) select
+// the split; nullptr: one pass into C
+hipError_t launch_skinny(const Problem& p, const Launch& l, int et, int fn, int fm,
                          const SkinnySplit* sp = nullptr, float* part = nullptr);
 // C = 0 for K == 0 (fill.hip)
 hipError_t launch_zero_c(const Problem& p, const Launch& l);

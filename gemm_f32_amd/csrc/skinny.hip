@@ -36,6 +36,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "mma16.hpp"
 
 namespace gemm {
 namespace {
@@ -57,7 +58,9 @@ template <int FM, int FN> struct Depth {
 
 // ---- per-dtype pieces -------------------------------------------------------------------
 // One k-step: BF16 32 k (lane holds 8 consecutive k), FP32 16 k (lane holds 4).
-struct Bf16 {
+// 16-bit inputs: BF16, or IEEE fp16 with F16 (same loads, another matrix instruction)
+template <bool F16>
+struct In16 {
     using Elem = u16;
     using Frag = uint4;
     static constexpr int KSTEP = 32, KL = 8;        // k per step, k per lane
@@ -69,12 +72,13 @@ struct Bf16 {
         return make_uint4(v[0] | (unsigned)v[1] << 16, v[2] | (unsigned)v[3] << 16,
                           v[4] | (unsigned)v[5] << 16, v[6] | (unsigned)v[7] << 16);
     }
-    // B row-major is not handled by this kernel for BF16 (the host routes it elsewhere)
+    // B row-major is not handled by this kernel for 16-bit inputs (the host routes it elsewhere)
     __device__ static f32x4 mma(const Frag& a, const Frag& b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+        return mma_16x16x32<F16>(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c);
     }
 };
+using Bf16 = In16<false>;
+using F16 = In16<true>;
 
 struct F32 {
     using Elem = float;
@@ -397,7 +401,7 @@ SkinnySplit skinny_split(const Problem& p, bool bf16, int cus) {
     return sp;
 }
 
-hipError_t launch_skinny(const Problem& p, const Launch& l, bool bf16, int fn, int fm, const SkinnySplit* sp,
+hipError_t launch_skinny(const Problem& p, const Launch& l, int et, int fn, int fm, const SkinnySplit* sp,
                          float* part) {
     constexpr int W = kSkinnyWaves;
     if (fm < 1 || fm > 4) return hipErrorInvalidValue;
@@ -405,12 +409,15 @@ hipError_t launch_skinny(const Problem& p, const Launch& l, bool bf16, int fn, i
     const int kslice = split ? sp->kslice : p.K, slices = split ? sp->slices : 1;
     float* out = split ? part : nullptr;
     hipError_t err;
+    if (et != kElemF32 && et != kElemBf16 && et != kElemF16) return hipErrorInvalidValue;
     if (fn == 4) {
-        if (bf16) err = launch_d<Bf16, 4, W, true>(p, l, fm, kslice, slices, out);
+        if (et == kElemBf16) err = launch_d<Bf16, 4, W, true>(p, l, fm, kslice, slices, out);
+        else if (et == kElemF16) err = launch_d<F16, 4, W, true>(p, l, fm, kslice, slices, out);
         else if (p.ob == kCol) err = launch_d<F32, 4, W, true>(p, l, fm, kslice, slices, out);
         else err = launch_d<F32, 4, W, false>(p, l, fm, kslice, slices, out);
     } else {
-        if (bf16) err = launch_d<Bf16, 1, W, true>(p, l, fm, kslice, slices, out);
+        if (et == kElemBf16) err = launch_d<Bf16, 1, W, true>(p, l, fm, kslice, slices, out);
+        else if (et == kElemF16) err = launch_d<F16, 1, W, true>(p, l, fm, kslice, slices, out);
         else if (p.ob == kCol) err = launch_d<F32, 1, W, true>(p, l, fm, kslice, slices, out);
         else err = launch_d<F32, 1, W, false>(p, l, fm, kslice, slices, out);
     }

@@ -92,4 +92,5 @@ def kernel_model(M: int, N: int, K: int, bm: int, bn: int, bk: int, tm: int = 1,
 
 
 def mi355x_peak(dtype: str) -> float:
-    return {"bf16": MI355X_BF16_DENSE_FLOPS, "f32": MI355X_FP32_FLOPS}[dtype]
+    # fp16 inputs: the same dense matrix-core peak as bf16 (2.5 PFLOP/s, published figures)
+    return {"bf16": MI355X_BF16_DENSE_FLOPS, "f16": MI355X_BF16_DENSE_FLOPS, "f32": MI355X_FP32_FLOPS}[dtype]

@@ -32,7 +32,7 @@ class Workload:
     M: int
     N: int
     K: int
-    dtype: str               # "f32" or "bf16" (inputs); C is always fp32
+    dtype: str               # "f32", "bf16" or "f16" (inputs); C is always fp32
     order_a: int = ROW_MAJOR
     order_b: int = ROW_MAJOR
     order_c: int = ROW_MAJOR
@@ -50,6 +50,7 @@ WORKLOADS = {
         Workload("probe16_f32", 1, 16, 16, 16, "f32"),
         Workload("square4096_f32", 2, 4096, 4096, 4096, "f32"),
         Workload("square4096_bf16", 3, 4096, 4096, 4096, "bf16", ROW_MAJOR, COL_MAJOR),
+        Workload("square4096_f16", 3, 4096, 4096, 4096, "f16", ROW_MAJOR, COL_MAJOR),
         Workload("ragged1000_f32", 4, 1000, 1000, 1000, "f32"),
         Workload("ragged1000_bf16", 4, 1000, 1000, 1000, "bf16", ROW_MAJOR, COL_MAJOR),
         Workload("ragged4095x4097x1023_f32", 4, 4095, 4097, 1023, "f32"),
@@ -135,6 +136,8 @@ def lay_out(logical: np.ndarray, order: int, ld: int | None = None) -> tuple[np.
 def _sentinel(dtype) -> object:
     if dtype == np.uint16:
         return np.uint16(0x7FC1)     # a bf16 NaN
+    if dtype == np.float16:
+        return np.float16(np.nan)
     return np.float32(np.nan)
 
 
@@ -148,7 +151,7 @@ class Problem:
     order_a: int
     order_b: int
     order_c: int
-    A_logical: np.ndarray    # fp32 (M, K) or uint16 bf16 bits (M, K)
+    A_logical: np.ndarray    # fp32 (M, K), uint16 bf16 bits (M, K) or float16 (M, K)
     B_logical: np.ndarray
     A: np.ndarray            # flat buffer
     lda: int
@@ -157,10 +160,16 @@ class Problem:
     ldc: int
 
     def a_f32(self) -> np.ndarray:
-        return bf16_bits_to_f32(self.A_logical) if self.dtype == "bf16" else self.A_logical
+        return _to_f32(self.A_logical, self.dtype)
 
     def b_f32(self) -> np.ndarray:
-        return bf16_bits_to_f32(self.B_logical) if self.dtype == "bf16" else self.B_logical
+        return _to_f32(self.B_logical, self.dtype)
+
+
+def _to_f32(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return bf16_bits_to_f32(x)
+    return x.astype(np.float32) if dtype == "f16" else x
 
 
 def make_problem(M: int, N: int, K: int, dtype: str = "f32", order_a: int = ROW_MAJOR,
@@ -171,7 +180,8 @@ def make_problem(M: int, N: int, K: int, dtype: str = "f32", order_a: int = ROW_
 
     pad_* adds that many slots to the minimum leading dimension.
     A_logical / B_logical, if given, are fp32 matrices used instead of random draws
-    (rounded to bf16 when dtype == "bf16").
+    (rounded to bf16 when dtype == "bf16", to fp16 when "f16": numpy's round to nearest
+    even, values beyond the fp16 range becoming inf).
     """
     if A_logical is None:
         A_logical = draw(rng_for(wid, M, N, K, 0), M, K, dist, 0)
@@ -182,6 +192,9 @@ def make_problem(M: int, N: int, K: int, dtype: str = "f32", order_a: int = ROW_
     if dtype == "bf16":
         A_logical = f32_to_bf16_bits(A_logical)
         B_logical = f32_to_bf16_bits(B_logical)
+    elif dtype == "f16":
+        A_logical = A_logical.astype(np.float16)
+        B_logical = B_logical.astype(np.float16)
     elif dtype != "f32":
         raise ValueError(dtype)
     lda0 = K if order_a == ROW_MAJOR else M

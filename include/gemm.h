@@ -133,6 +133,18 @@ gemm_status_t gemm_bf16_f32acc(int64_t M, int64_t N, int64_t K,
                                float *C, int64_t ldc, gemm_order_t order_c,
                                hipStream_t stream);
 
+/* FP16-input, FP32-accumulate GEMM: as gemm_bf16_f32acc, with A and B holding IEEE
+ * binary16 bit patterns (1 sign, 5 exponent, 10 fraction bits).  The survey's other
+ * matrix-core input type: the same kernels with the fp16 matrix instructions
+ * (v_mfma_f32_32x32x16_f16, v_mfma_f32_16x16x32_f16); every product of two fp16 values is
+ * exact in FP32, sums are FP32.  Layouts, kernel choice and errors as for BF16 (the BF16-only
+ * ping-pong kernel is not offered). */
+gemm_status_t gemm_f16_f32acc(int64_t M, int64_t N, int64_t K,
+                              const uint16_t *A, int64_t lda, gemm_order_t order_a,
+                              const uint16_t *B, int64_t ldb, gemm_order_t order_b,
+                              float *C, int64_t ldc, gemm_order_t order_c,
+                              hipStream_t stream);
+
 /* As gemm_f32, with the kernel forced (see gemm_algo_t). */
 gemm_status_t gemm_f32_algo(gemm_algo_t algo, int64_t M, int64_t N, int64_t K,
                             const float *A, int64_t lda, gemm_order_t order_a,
@@ -147,6 +159,14 @@ gemm_status_t gemm_bf16_f32acc_algo(gemm_algo_t algo, int64_t M, int64_t N, int6
                                     float *C, int64_t ldc, gemm_order_t order_c,
                                     hipStream_t stream);
 
+/* As gemm_f16_f32acc, with the kernel forced (AUTO or one of the MFMA values except
+ * GEMM_ALGO_MFMA_PINGPONG). */
+gemm_status_t gemm_f16_f32acc_algo(gemm_algo_t algo, int64_t M, int64_t N, int64_t K,
+                                   const uint16_t *A, int64_t lda, gemm_order_t order_a,
+                                   const uint16_t *B, int64_t ldb, gemm_order_t order_b,
+                                   float *C, int64_t ldc, gemm_order_t order_c,
+                                   hipStream_t stream);
+
 /* Static, never-null description of a status code. */
 const char *gemm_status_string(gemm_status_t status);
 
@@ -160,8 +180,8 @@ const char *gemm_last_kernel(void);
 /* Library version, e.g. "0.1.0". */
 const char *gemm_version(void);
 
-/* What gemm_f32 (bf16 == 0) or gemm_bf16_f32acc (bf16 != 0) would run for a problem of these
- * extents and orders, with tight leading dimensions, on a device of `cus` compute units,
+/* What gemm_f32 (dtype 0), gemm_bf16_f32acc (dtype 1) or gemm_f16_f32acc (dtype 2) would run
+ * for a problem of these extents and orders, with tight leading dimensions, on a device of `cus` compute units,
  * without touching a device or launching anything; for tests of the kernel choice.
  *   *kernel     static name, as gemm_last_kernel() would report it ("none" for M == 0 or
  *               N == 0, "zero_c" for K == 0);
@@ -171,9 +191,10 @@ const char *gemm_version(void);
  *               separate GEMMs on the same stream chosen the same way;
  *   *workspace_bytes   the workspace with which gemm_f32_ws / gemm_bf16_f32acc_ws split K
  *               across workgroups for this problem (0: they never do).
- * Errors: GEMM_ERR_INVALID_VALUE for a null output pointer, cus <= 0, negative or too large
- * extents (> INT_MAX) or an invalid order; outputs untouched then. */
-gemm_status_t gemm_plan(int bf16, int64_t M, int64_t N, int64_t K, gemm_order_t order_a,
+ * Errors: GEMM_ERR_INVALID_VALUE for a null output pointer, cus <= 0, a dtype other than
+ * 0, 1, 2, negative or too large extents (> INT_MAX) or an invalid order; outputs untouched
+ * then. */
+gemm_status_t gemm_plan(int dtype, int64_t M, int64_t N, int64_t K, gemm_order_t order_a,
                         gemm_order_t order_b, gemm_order_t order_c, int cus, const char **kernel,
                         int64_t *core_rows, int64_t *core_cols, size_t *workspace_bytes);
 
@@ -188,10 +209,11 @@ gemm_status_t gemm_plan(int bf16, int64_t M, int64_t N, int64_t K, gemm_order_t 
  * nothing.
  *
  * gemm_workspace_size: bytes of workspace with which the _ws calls split K for this problem
- * on the current device (the same extents and orders as the call; leading dimensions do not
- * matter); 0 if they would not split, for invalid arguments, or without a gfx950 device.
+ * (dtype as for gemm_plan) on the current device (the same extents and orders as the call;
+ * leading dimensions do not matter); 0 if they would not split, for invalid arguments, or
+ * without a gfx950 device.
  *
- * gemm_f32_ws / gemm_bf16_f32acc_ws: as gemm_f32 / gemm_bf16_f32acc.  workspace: device
+ * gemm_f32_ws / gemm_bf16_f32acc_ws / gemm_f16_f32acc_ws: as the plain calls.  workspace: device
  * memory, 16-byte aligned, not overlapping A, B or C, of workspace_bytes bytes; it is used
  * only if workspace_bytes >= gemm_workspace_size(...) and the call would split; otherwise,
  * or with workspace == NULL, the call runs exactly as the plain one.  Its contents are
@@ -199,7 +221,7 @@ gemm_status_t gemm_plan(int bf16, int64_t M, int64_t N, int64_t K, gemm_order_t 
  * workspace must not run concurrently (use one stream, or one workspace per stream).
  * Errors: as the plain calls, plus GEMM_ERR_INVALID_VALUE for a workspace that is not
  * 16-byte aligned. */
-size_t gemm_workspace_size(int bf16, int64_t M, int64_t N, int64_t K, gemm_order_t order_a,
+size_t gemm_workspace_size(int dtype, int64_t M, int64_t N, int64_t K, gemm_order_t order_a,
                            gemm_order_t order_b, gemm_order_t order_c);
 gemm_status_t gemm_f32_ws(int64_t M, int64_t N, int64_t K,
                           const float *A, int64_t lda, gemm_order_t order_a,
@@ -211,6 +233,11 @@ gemm_status_t gemm_bf16_f32acc_ws(int64_t M, int64_t N, int64_t K,
                                   const uint16_t *B, int64_t ldb, gemm_order_t order_b,
                                   float *C, int64_t ldc, gemm_order_t order_c,
                                   void *workspace, size_t workspace_bytes, hipStream_t stream);
+gemm_status_t gemm_f16_f32acc_ws(int64_t M, int64_t N, int64_t K,
+                                 const uint16_t *A, int64_t lda, gemm_order_t order_a,
+                                 const uint16_t *B, int64_t ldb, gemm_order_t order_b,
+                                 float *C, int64_t ldc, gemm_order_t order_c,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

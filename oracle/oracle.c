@@ -10,10 +10,13 @@
  * ("GEMM", Part 4 of How to make your models fast, opening formulas;
  *  "GEMM Optimization", section "The Problem").
  *
- * Precision.  Operands are fp32 values or bf16 bit patterns.  Each is widened
- * exactly to double; the product of two such values is exact in double (at most
- * 24 + 24 significant bits), and products are summed in double over k in
- * ascending order.  The teaching module's lab does the same: its checker is a CPU
+ * Precision.  Operands are fp32 values, bf16 bit patterns or IEEE binary16 (fp16)
+ * bit patterns.  Each is widened exactly to double; the product of two such values
+ * is exact in double (at most 24 + 24 significant bits), and products are summed in
+ * double over k in ascending order.  fp16 is decoded from its fields as IEEE 754
+ * defines binary16 (1 sign, 5 exponent bits with bias 15, 10 fraction bits; exponent
+ * 0 holds zero and the subnormals fraction * 2^-24, exponent 31 infinity and NaN);
+ * the pages name fp16 only as another input type of the matrix cores.  The teaching module's lab does the same: its checker is a CPU
  * reference that accumulates in double ("A06 - Tiled Matrix Multiply (GEMM)",
  * section "Lab 1 - The optimization ladder", note on the tolerance).
  *
@@ -39,7 +42,21 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F16 = 2 };
+
+/* IEEE binary16 bit pattern -> its value */
+static double f16_value(uint16_t h)
+{
+    const int sign = h >> 15, exp = (h >> 10) & 0x1f, frac = h & 0x3ff;
+    double v;
+    if (exp == 0)
+        v = ldexp((double)frac, -24);              /* zero and subnormals */
+    else if (exp == 31)
+        v = frac == 0 ? INFINITY : NAN;
+    else
+        v = ldexp((double)(1024 + frac), exp - 25); /* (1 + frac/1024) * 2^(exp-15) */
+    return sign ? -v : v;
+}
 
 /* one operand element, widened exactly to double */
 static double element(const void *base, int dtype, int64_t r, int64_t c, int64_t ld, int order)
@@ -47,6 +64,8 @@ static double element(const void *base, int dtype, int64_t r, int64_t c, int64_t
     int64_t at = (order == 0) ? r * ld + c : r + c * ld;
     if (dtype == ORACLE_F32) {
         return (double)((const float *)base)[at];
+    } else if (dtype == ORACLE_F16) {
+        return f16_value(((const uint16_t *)base)[at]);
     } else {
         uint32_t bits = (uint32_t)((const uint16_t *)base)[at] << 16;
         float f;
@@ -65,7 +84,7 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K, int dtype,
                 const void *B, int64_t ldb, int order_b,
                 double *C, double *D, int64_t *macs)
 {
-    if (M < 0 || N < 0 || K < 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
+    if (M < 0 || N < 0 || K < 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F16))
         return -1;
     int64_t count = 0;
 #pragma omp parallel reduction(+ : count)
@@ -111,7 +130,8 @@ int oracle_gemm_sampled(int64_t M, int64_t N, int64_t K, int dtype,
                         const int64_t *rows, const int64_t *cols, int64_t nsamp,
                         double *C, double *D)
 {
-    if (M < 0 || N < 0 || K < 0 || nsamp < 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
+    if (M < 0 || N < 0 || K < 0 || nsamp < 0 ||
+        (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F16))
         return -1;
     for (int64_t t = 0; t < nsamp; ++t)
         if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N)

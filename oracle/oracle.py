@@ -1,7 +1,7 @@
 """ctypes front end of the C oracle (oracle.c) -- TEST INFRASTRUCTURE ONLY.
 
 The oracle computes C[i][j] = sum_k A[i][k] * B[k][j] in double, k ascending, on the
-exact fp32 or bf16 input values, and D[i][j] = sum_k |A[i][k] * B[k][j]|, the scale the
+exact fp32, bf16 or fp16 input values, and D[i][j] = sum_k |A[i][k] * B[k][j]|, the scale the
 parity tolerance is normalised by.  See oracle.c for the cited definition.
 """
 from __future__ import annotations
@@ -21,6 +21,7 @@ _lib = None
 
 F32 = 0
 BF16 = 1
+F16 = 2
 
 
 def library_path() -> str:
@@ -67,7 +68,9 @@ def _dtype_code(buf: np.ndarray) -> int:
         return F32
     if buf.dtype == np.uint16:
         return BF16
-    raise TypeError(f"oracle operands are fp32 or bf16 bits (uint16), got {buf.dtype}")
+    if buf.dtype == np.float16:
+        return F16
+    raise TypeError(f"oracle operands are fp32, bf16 bits (uint16) or fp16, got {buf.dtype}")
 
 
 def gemm(M, N, K, A, lda, order_a, B, ldb, order_b, lib=None, return_macs=False):

@@ -10,12 +10,13 @@ import gemm_f32_amd as g
 import gemm_inputs as gi
 import oracle
 
-TOL = {"f32": 1e-5, "bf16": 1e-4}   # max |C - C_ref| / sum_k |A_ik B_kj|
+# max |C - C_ref| / sum_k |A_ik B_kj|; fp16 inputs, like bf16, give exact products in FP32
+TOL = {"f32": 1e-5, "bf16": 1e-4, "f16": 1e-4}
 
 
 def to_device(buf: np.ndarray):
     import torch
-    if buf.dtype == np.uint16:
+    if buf.dtype in (np.uint16, np.float16):
         buf = buf.view(np.int16)
     return torch.from_numpy(np.ascontiguousarray(buf)).to("cuda")
 
@@ -27,7 +28,7 @@ def run(p: gi.Problem, algo=g.Algo.AUTO, A=None, B=None):
     B = to_device(p.B) if B is None else B
     n = gi.c_buffer_size(p.M, p.N, p.ldc, p.order_c)
     C = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
-    fn = g.gemm_f32_algo if p.dtype == "f32" else g.gemm_bf16_f32acc_algo
+    fn = {"f32": g.gemm_f32_algo, "bf16": g.gemm_bf16_f32acc_algo, "f16": g.gemm_f16_f32acc_algo}[p.dtype]
     print(f"[gpu] {p.dtype} algo={int(algo)} M={p.M} N={p.N} K={p.K} orders=({p.order_a},"
           f"{p.order_b},{p.order_c}) ld=({p.lda},{p.ldb},{p.ldc})", flush=True)
     fn(algo, p.M, p.N, p.K, A.data_ptr(), p.lda, p.order_a, B.data_ptr(), p.ldb, p.order_b,

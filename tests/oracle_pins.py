@@ -29,6 +29,7 @@ import oracle
 from gemm_inputs import COL_MAJOR, ROW_MAJOR
 
 ORDERS = [(oa, ob) for oa in (ROW_MAJOR, COL_MAJOR) for ob in (ROW_MAJOR, COL_MAJOR)]
+DTYPES = ("f32", "bf16", "f16")
 
 
 def _run(lib, p: gi.Problem, macs=False):
@@ -44,7 +45,7 @@ def _int_matrix(rng, r, c, lo=-4, hi=4):
 def pin_fraction_bruteforce(lib):
     """Exact rational sums on tiny shapes: |C - exact| <= (K-1) * 2^-53 * D."""
     shapes = [(1, 1, 1), (2, 3, 4), (3, 1, 5), (4, 4, 4), (5, 7, 3), (8, 8, 8), (1, 6, 8)]
-    for dtype in ("f32", "bf16"):
+    for dtype in DTYPES:
         for (M, N, K) in shapes:
             for oa, ob in ORDERS:
                 p = gi.make_problem(M, N, K, dtype, oa, ob, wid=101, pad_a=1, pad_b=2)
@@ -64,7 +65,7 @@ def pin_fraction_bruteforce(lib):
 
 def pin_numpy_crosscheck(lib):
     """numpy float64 matmul of the logical operands agrees to 1e-12 of D."""
-    for dtype in ("f32", "bf16"):
+    for dtype in DTYPES:
         for (M, N, K) in [(37, 53, 129), (64, 32, 16), (3, 100, 257)]:
             for oa, ob in ORDERS:
                 p = gi.make_problem(M, N, K, dtype, oa, ob, wid=102, pad_a=3, pad_b=1)
@@ -80,7 +81,7 @@ def pin_numpy_crosscheck(lib):
 def pin_ones(lib):
     """A = ones, B = ones  =>  C == K exactly (16^3 is the pages' worked size)."""
     for (M, N, K) in [(16, 16, 16), (32, 32, 32), (64, 64, 64), (37, 45, 67)]:
-        for dtype in ("f32", "bf16"):
+        for dtype in DTYPES:
             for oa, ob in ORDERS:
                 p = gi.make_problem(M, N, K, dtype, oa, ob, A_logical=np.ones((M, K)),
                                     B_logical=np.ones((K, N)))
@@ -103,7 +104,7 @@ def pin_ones_column_sums(lib):
 def pin_identity(lib):
     """A = I  =>  C == B bit for bit; B = I  =>  C == A bit for bit."""
     for n, other in [(16, 16), (32, 19), (7, 40)]:
-        for dtype in ("f32", "bf16"):
+        for dtype in DTYPES:
             for oa, ob in ORDERS:
                 p = gi.make_problem(n, other, n, dtype, oa, ob, wid=103, A_logical=np.eye(n))
                 C, _ = _run(lib, p)
@@ -120,7 +121,7 @@ def pin_permutation(lib):
         perm = rng.permutation(n)
         P = np.zeros((n, n))
         P[np.arange(n), perm] = 1.0           # (P.X)[i] = X[perm[i]]
-        for dtype in ("f32", "bf16"):
+        for dtype in DTYPES:
             for oa, ob in ORDERS:
                 p = gi.make_problem(n, other, n, dtype, oa, ob, wid=105, A_logical=P)
                 C, _ = _run(lib, p)
@@ -138,7 +139,7 @@ def pin_small_integers(lib):
         Al, Bl = _int_matrix(rng, M, K), _int_matrix(rng, K, N)
         exact = (Al.astype(np.int64) @ Bl.astype(np.int64)).astype(np.float64)
         dexact = (np.abs(Al).astype(np.int64) @ np.abs(Bl).astype(np.int64)).astype(np.float64)
-        for dtype in ("f32", "bf16"):
+        for dtype in DTYPES:
             for oa, ob in ORDERS:
                 p = gi.make_problem(M, N, K, dtype, oa, ob, A_logical=Al, B_logical=Bl, pad_a=2)
                 C, D = _run(lib, p)
@@ -148,7 +149,7 @@ def pin_small_integers(lib):
 
 def pin_transpose(lib):
     """(A.B)^T computed as B^T.A^T from the same buffers (order flags flipped) agrees bitwise."""
-    for dtype in ("f32", "bf16"):
+    for dtype in DTYPES:
         for oa, ob in ORDERS:
             p = gi.make_problem(23, 31, 41, dtype, oa, ob, wid=107, pad_b=5)
             C, D = _run(lib, p)
@@ -197,7 +198,7 @@ def pin_degenerate(lib):
 
 def pin_nonnegative_scale(lib):
     """With nonnegative entries, D (sum of |products|) equals C bit for bit."""
-    for dtype in ("f32", "bf16"):
+    for dtype in DTYPES:
         p = gi.make_problem(19, 21, 300, dtype, dist="unit", wid=109)
         C, D = _run(lib, p)
         assert np.array_equal(C, D)
@@ -213,9 +214,28 @@ def pin_bf16_widening(lib):
     assert D[0, 0] == 2.5 + 3.0 * 2.0 ** -126
 
 
+def pin_f16_widening(lib):
+    """Every IEEE binary16 bit pattern is read as the value it encodes, checked against
+    numpy's own float16 -> float64 conversion (a library routine the oracle does not call)
+    for all 65536 patterns: a 65536 x 1 times 1 x 1 product with B = 1 returns them."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    A = bits.view(np.float16)                          # 65536 x 1, row-major
+    B = np.array([1.0], dtype=np.float16)
+    C, D = oracle.gemm(65536, 1, 1, A, 1, ROW_MAJOR, B, 1, ROW_MAJOR, lib=lib)
+    want = A.astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(C[:, 0]), nan)
+    assert np.array_equal(C[~nan, 0], want[~nan])
+    # spot values fixed by the format: 1.0 = 0x3C00, -2 = 0xC000, 65504 (largest) = 0x7BFF,
+    # 2^-24 (smallest subnormal) = 0x0001, 2^-14 (smallest normal) = 0x0400, inf = 0x7C00
+    for pattern, value in ((0x3C00, 1.0), (0xC000, -2.0), (0x7BFF, 65504.0), (0x0001, 2.0 ** -24),
+                           (0x0400, 2.0 ** -14), (0x7C00, np.inf), (0x8000, -0.0)):
+        assert C[pattern, 0] == value
+
+
 def pin_sampled_matches_full(lib):
     """The sampled entry point returns the full product's elements bit for bit."""
-    for dtype in ("f32", "bf16"):
+    for dtype in DTYPES:
         for oa, ob in ORDERS:
             p = gi.make_problem(29, 33, 77, dtype, oa, ob, wid=110, pad_a=1)
             C, D = _run(lib, p)
@@ -231,5 +251,5 @@ ALL_PINS = [
     pin_fraction_bruteforce, pin_numpy_crosscheck, pin_ones, pin_ones_column_sums,
     pin_identity, pin_permutation, pin_small_integers, pin_transpose, pin_k_split,
     pin_mac_count, pin_degenerate, pin_nonnegative_scale, pin_bf16_widening,
-    pin_sampled_matches_full,
+    pin_f16_widening, pin_sampled_matches_full,
 ]

@@ -253,3 +253,15 @@ def test_plan_invariants_on_random_shapes():
 ], ids=lambda v: str(v))
 def test_split_k_workspace_of_known_shapes(dtype, shape, orders, expected):
     assert g.gemm_plan(dtype, *shape, *orders, with_workspace=True)[3] == expected
+
+
+@pytest.mark.parametrize("shape,expected", [
+    ((4096, 4096, 4096), ("f16_dma256x256", 4096, 4096)),
+    ((2048, 11008, 4096), ("f16_dma256x256", 2048, 8192)),
+    ((16, 4096, 4096), ("f16_skinny16", 16, 4096)),
+], ids=str)
+def test_f16_plans_follow_bf16(shape, expected):
+    """fp16 inputs take the same kernels and plans as bf16, under their own names."""
+    assert g.gemm_plan("f16", *shape, R, C_, R) == expected
+    bf = g.gemm_plan("bf16", *shape, R, C_, R)
+    assert bf[1:] == expected[1:] and bf[0] == expected[0].replace("f16_", "bf16_")

@@ -553,7 +553,7 @@ def run_ws(p, ws_bytes=None, misalign=0):
     need = g.gemm_workspace_size(p.dtype, p.M, p.N, p.K, p.order_a, p.order_b, p.order_c)
     nbytes = need if ws_bytes is None else ws_bytes
     ws = torch.full((nbytes // 4 + 64,), float("nan"), dtype=torch.float32, device="cuda")
-    fn = g.gemm_f32_ws if p.dtype == "f32" else g.gemm_bf16_f32acc_ws
+    fn = {"f32": g.gemm_f32_ws, "bf16": g.gemm_bf16_f32acc_ws, "f16": g.gemm_f16_f32acc_ws}[p.dtype]
     print(f"[gpu] ws {p.dtype} M={p.M} N={p.N} K={p.K} orders=({p.order_a},{p.order_b},{p.order_c}) "
           f"ws={nbytes}/{need}", flush=True)
     fn(p.M, p.N, p.K, A.data_ptr(), p.lda, p.order_a, B.data_ptr(), p.ldb, p.order_b, C.data_ptr(), p.ldc,
@@ -624,3 +624,90 @@ def test_workspace_must_be_16_byte_aligned():
     with pytest.raises(g.GemmError) as e:
         run_ws(p, misalign=4)
     assert e.value.status == g.Status.ERR_INVALID_VALUE
+
+
+# --- FP16 inputs (the same 16-bit kernels with the fp16 matrix instructions) --------------
+F16_AUTO = [((4096, 4096, 256), "f16_dma256x256"), ((2048, 4096, 128), "f16_dma256x128"),
+            ((1000, 1000, 1000), "f16_skinny64"), ((16, 4096, 4096), "f16_skinny16"),
+            ((4095, 4097, 72), "f16_dma256x256"), ((300, 264, 192), None), ((33, 300, 127), None)]
+
+
+@pytest.mark.parametrize("shape,kernel", F16_AUTO, ids=lambda v: str(v))
+@pytest.mark.parametrize("oc", [ROW_MAJOR, COL_MAJOR], ids=["RCR", "RCC"])
+def test_f16_auto(shape, kernel, oc):
+    M, N, K = shape
+    if oc == COL_MAJOR:
+        kernel = None                      # C^T is another problem; parity only
+    p = gi.make_problem(M, N, K, "f16", ROW_MAJOR, COL_MAJOR, oc, wid=60)
+    check(p, g.Algo.AUTO, key=("f16auto", shape, oc))
+    if kernel:
+        assert g.gemm_last_kernel() == kernel
+
+
+F16_FORCED = [(g.Algo.MFMA_DMA, (257, 385, 65)), (g.Algo.MFMA_DMA, (512, 384, 200)),
+              (g.Algo.MFMA_256x256, (300, 516, 96)), (g.Algo.MFMA_256x128, (260, 200, 70)),
+              (g.Algo.MFMA_128x128, (129, 257, 33)), (g.Algo.MFMA_64x64, (65, 100, 130)),
+              (g.Algo.SKINNY, (40, 700, 999))]
+
+
+@pytest.mark.parametrize("algo,shape", F16_FORCED, ids=lambda v: str(v))
+def test_f16_forced_kernels(algo, shape):
+    M, N, K = shape
+    p = gi.make_problem(M, N, K, "f16", ROW_MAJOR, COL_MAJOR, wid=61)
+    check(p, algo)
+    assert g.gemm_last_kernel().startswith("f16_")
+
+
+@pytest.mark.parametrize("orders", [(ROW_MAJOR, ROW_MAJOR), (COL_MAJOR, COL_MAJOR), (COL_MAJOR, ROW_MAJOR)],
+                         ids=["RR", "CC", "CR"])
+def test_f16_other_layouts(orders):
+    """Operands that are not both k-contiguous take the register-staged 16-bit kernel."""
+    oa, ob = orders
+    p = gi.make_problem(200, 300, 150, "f16", oa, ob, wid=62, pad_a=3, pad_b=1)
+    check(p, g.Algo.AUTO)
+    assert g.gemm_last_kernel().startswith("f16_mfma")
+
+
+def test_f16_small_integer_exact():
+    rng = np.random.default_rng(31)
+    M, N, K = 520, 392, 640
+    A = rng.integers(-8, 9, (M, K)).astype(np.float32)
+    B = rng.integers(-8, 9, (K, N)).astype(np.float32)
+    check(gi.make_problem(M, N, K, "f16", ROW_MAJOR, COL_MAJOR, A_logical=A, B_logical=B), g.Algo.AUTO,
+          exact=True)
+
+
+@pytest.mark.parametrize("algo,shape", [(g.Algo.AUTO, (256, 256, 1024)), (g.Algo.AUTO, (16, 512, 2048)),
+                                        (g.Algo.AUTO, (2048, 2048, 256)), (g.Algo.MFMA_DMA, (512, 512, 256)),
+                                        (g.Algo.MFMA_256x256, (256, 256, 128))], ids=str)
+def test_f16_values_bf16_cannot_hold(algo, shape):
+    """1 + 2^-10 is exact in fp16 and not in bf16 (7 fraction bits): a kernel that read the
+    fp16 patterns as bf16 would be far off.  Also a subnormal (2^-20) and a value near the
+    top of the fp16 range (61440 = 15 * 2^12), products exact in FP32."""
+    M, N, K = shape
+    A = np.full((M, K), 1.0 + 2.0 ** -10, np.float32)
+    A[:, 1] = 2.0 ** -20
+    A[:, 2] = 61440.0
+    B = np.ones((K, N), np.float32)
+    p = gi.make_problem(M, N, K, "f16", ROW_MAJOR, COL_MAJOR, A_logical=A, B_logical=B)
+    C = logical_c(p, run(p, algo))
+    want = (K - 2) * (1.0 + 2.0 ** -10) + 2.0 ** -20 + 61440.0
+    ref, D = oracle.gemm(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b)
+    assert ref[0, 0] == want
+    assert oracle.normalised_error(C, ref, D) <= TOL["f16"]
+
+
+def test_f16_rejects_pingpong_and_vector_ladder():
+    p = gi.make_problem(256, 256, 64, "f16", ROW_MAJOR, COL_MAJOR)
+    for algo in (g.Algo.MFMA_PINGPONG, g.Algo.NAIVE, g.Algo.REGBLOCK):
+        with pytest.raises(g.GemmError) as e:
+            run(p, algo)
+        assert e.value.status == g.Status.ERR_INVALID_VALUE
+
+
+def test_f16_split_k_with_workspace():
+    p = gi.make_problem(16, 1024, 16384, "f16", ROW_MAJOR, COL_MAJOR, wid=63)
+    flat, need, kernel = run_ws(p)
+    assert need > 0 and kernel == "f16_skinny64_splitk"
+    ref, D = oracle.gemm(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b)
+    assert oracle.normalised_error(logical_c(p, flat), ref, D) <= TOL["f16"]

@@ -28,6 +28,9 @@ MUTANTS = {
     "col_major_as_row": ("r * ld + c : r + c * ld", "r * ld + c : r * ld + c"),
     "row_major_as_col": ("r * ld + c : r + c * ld", "r + c * ld : r + c * ld"),
     "bf16_shift": ("<< 16;", "<< 15;"),
+    "f16_exponent_bias": ("exp - 25", "exp - 24"),
+    "f16_subnormals_as_zero": ("v = ldexp((double)frac, -24);", "v = 0.0;"),
+    "f16_fraction_width": ("(double)(1024 + frac)", "(double)(512 + frac)"),
     "scale_without_abs": ("d[j] += fabs(p);", "d[j] += p;"),
     "no_row_reset": ("s[j] = 0.0;\n                d[j] = 0.0;", "d[j] = 0.0;"),
     "fp32_accumulator": ("double p = a * element(B, dtype, k, j, ldb, order_b);\n                    s[j] += p;",

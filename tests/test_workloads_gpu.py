@@ -49,7 +49,7 @@ def test_workload_full_size_sampled_with_workspace(name):
     C = torch.full((gi.c_buffer_size(p.M, p.N, p.ldc, p.order_c),), float("nan"), dtype=torch.float32,
                    device="cuda")
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-    fn = g.gemm_f32_ws if p.dtype == "f32" else g.gemm_bf16_f32acc_ws
+    fn = {"f32": g.gemm_f32_ws, "bf16": g.gemm_bf16_f32acc_ws, "f16": g.gemm_f16_f32acc_ws}[p.dtype]
     print(f"[gpu] ws workload {name}", flush=True)
     fn(p.M, p.N, p.K, A.data_ptr(), p.lda, p.order_a, B.data_ptr(), p.ldb, p.order_b, C.data_ptr(), p.ldc,
        p.order_c, ws.data_ptr(), need, torch.cuda.current_stream().cuda_stream)

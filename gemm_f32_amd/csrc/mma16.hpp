@@ -1,7 +1,7 @@
 // Matrix instructions on 16-bit inputs.  The BF16 kernels carry their operand fragments as
-// eight 16-bit patterns (bf16x8); the same kernels serve IEEE fp16 inputs (the survey's
-// other MFMA input type: same layouts, same copies, another instruction) by choosing the
-// instruction here: F16 reads the patterns as fp16 (v_mfma_f32_32x32x16_f16,
+// eight 16-bit patterns (bf16x8); the same kernels serve IEEE fp16 inputs, the other
+// 16-bit input type of the matrix cores ("Matrix cores: MFMA and Tensor Cores"; same
+// layouts, same copies, another instruction), by choosing the instruction here: F16 reads the patterns as fp16 (v_mfma_f32_32x32x16_f16,
 // v_mfma_f32_16x16x32_f16), otherwise as bf16.  Products and sums are FP32 either way.
 #pragma once
 

@@ -134,8 +134,9 @@ gemm_status_t gemm_bf16_f32acc(int64_t M, int64_t N, int64_t K,
                                hipStream_t stream);
 
 /* FP16-input, FP32-accumulate GEMM: as gemm_bf16_f32acc, with A and B holding IEEE
- * binary16 bit patterns (1 sign, 5 exponent, 10 fraction bits).  The survey's other
- * matrix-core input type: the same kernels with the fp16 matrix instructions
+ * binary16 bit patterns (1 sign, 5 exponent, 10 fraction bits), the other 16-bit input
+ * type of the matrix cores ("A06 - Tiled Matrix Multiply (GEMM)", "Matrix cores: MFMA and
+ * Tensor Cores"): the same kernels with the fp16 matrix instructions
  * (v_mfma_f32_32x32x16_f16, v_mfma_f32_16x16x32_f16); every product of two fp16 values is
  * exact in FP32, sums are FP32.  Layouts, kernel choice and errors as for BF16 (the BF16-only
  * ping-pong kernel is not offered). */

@@ -64,7 +64,7 @@ def parse():
 # scheduler, buffer helpers) and the launch declarations
 KERNEL_SOURCES = {
     "f32_dma": ("f32_dma.hip",),
-    "bf16_dma": ("bf16_dma.hip",),
+    "bf16_dma": ("bf16_dma.hip", "mma16.hpp"),
 }
 SHARED_SOURCES = ("common.hpp", "launch.hpp")
 

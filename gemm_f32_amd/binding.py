@@ -223,12 +223,13 @@ def operand_layout(t) -> tuple[int, int]:
 def matmul(a, b, out=None, algo: Algo = Algo.AUTO, stream=None):
     """out = a @ b for torch device tensors, through libgemm on the current stream.
 
-    a: (M, K), b: (K, N), both float32 (FP32 path) or both bfloat16 (BF16 inputs, FP32
-    accumulate).  out: float32 (M, N), row- or column-major; allocated row-major if None.
+    a: (M, K), b: (K, N), both float32 (FP32 path), both bfloat16 or both float16 (16-bit
+    inputs, FP32 accumulate).  out: float32 (M, N), row- or column-major; allocated row-major
+    if None.
     """
     import torch
-    if a.dtype != b.dtype or a.dtype not in (torch.float32, torch.bfloat16):
-        raise TypeError("a and b must both be float32 or both bfloat16")
+    if a.dtype != b.dtype or a.dtype not in (torch.float32, torch.bfloat16, torch.float16):
+        raise TypeError("a and b must both be float32, both bfloat16 or both float16")
     M, K = a.shape
     K2, N = b.shape
     if K != K2:
@@ -244,6 +245,8 @@ def matmul(a, b, out=None, algo: Algo = Algo.AUTO, stream=None):
     args = (M, N, K, a.data_ptr(), lda, oa, b.data_ptr(), ldb, ob, out.data_ptr(), ldc, oc, s)
     if a.dtype == torch.float32:
         gemm_f32_algo(algo, *args)
-    else:
+    elif a.dtype == torch.bfloat16:
         gemm_bf16_f32acc_algo(algo, *args)
+    else:
+        gemm_f16_f32acc_algo(algo, *args)
     return out

@@ -135,24 +135,34 @@ def test_repeated_runs_identical(dtype, algo):
 
 # --- the torch-facing helper -------------------------------------------------------------
 def test_matmul_helper_on_tensors_and_views():
+    """The torch helper maps strides to (ld, order) for row- and column-major operands and C;
+    references from the fp64 oracle on the same values."""
     import torch
     rng = np.random.default_rng(5)
-    a = torch.from_numpy(rng.uniform(-1, 1, (300, 200)).astype(np.float32)).cuda()
-    b = torch.from_numpy(rng.uniform(-1, 1, (200, 100)).astype(np.float32)).cuda()
-    ref = (a.double() @ b.double()).cpu().numpy()
-    D = (a.abs().double() @ b.abs().double()).cpu().numpy()
+    a32 = rng.uniform(-1, 1, (300, 200)).astype(np.float32)
+    b32 = rng.uniform(-1, 1, (200, 100)).astype(np.float32)
+    ref, D = oracle.gemm(300, 100, 200, a32.reshape(-1), 200, ROW_MAJOR, b32.reshape(-1), 100, ROW_MAJOR)
+    a, b = torch.from_numpy(a32).cuda(), torch.from_numpy(b32).cuda()
     for x, y in [(a, b), (a.t().contiguous().t(), b), (a, b.t().contiguous().t())]:
         out = g.matmul(x, y)
         assert oracle.normalised_error(out.cpu().numpy(), ref, D) <= TOL["f32"]
     out_cm = torch.empty(100, 300, device="cuda").t()           # column-major C
     g.matmul(a, b, out=out_cm)
     assert oracle.normalised_error(out_cm.cpu().numpy(), ref, D) <= TOL["f32"]
+    # 16-bit inputs: the oracle reads the same rounded values (bf16 bit patterns, fp16)
     ab, bb = a.bfloat16(), b.bfloat16()
-    refb = (ab.double() @ bb.double()).cpu().numpy()
-    Db = (ab.abs().double() @ bb.abs().double()).cpu().numpy()
+    abits = ab.cpu().view(torch.int16).numpy().view(np.uint16).reshape(-1)
+    bbits = bb.cpu().view(torch.int16).numpy().view(np.uint16).reshape(-1)
+    refb, Db = oracle.gemm(300, 100, 200, abits, 200, ROW_MAJOR, bbits, 100, ROW_MAJOR)
     out = g.matmul(ab, bb.t().contiguous().t())
     assert oracle.normalised_error(out.cpu().numpy(), refb, Db) <= TOL["bf16"]
     assert g.gemm_last_kernel().startswith("bf16_")
+    ah, bh = a.half(), b.half()
+    refh, Dh = oracle.gemm(300, 100, 200, ah.cpu().numpy().reshape(-1), 200, ROW_MAJOR,
+                           bh.cpu().numpy().reshape(-1), 100, ROW_MAJOR)
+    out = g.matmul(ah, bh.t().contiguous().t())
+    assert oracle.normalised_error(out.cpu().numpy(), refh, Dh) <= TOL["f16"]
+    assert g.gemm_last_kernel().startswith("f16_")
 
 
 # --- the eight-wavefront ping-pong kernel (row-major A, column-major B, 256-multiples) ---

@@ -12,7 +12,8 @@ kernel against MI355X's published matrix-core peak for its dtype.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--algo NAME]
 
 `--workload` picks another single workload from gemm_inputs.WORKLOADS (then one step is
-that one GEMM); `--algo` forces a kernel (gemm_f32_amd.Algo name); `--workspace` calls the
+that one GEMM, or one strided batched call for a batch workload such as attention's per-head
+products); `--algo` forces a kernel (gemm_f32_amd.Algo name); `--workspace` calls the
 workspace entry points (gemm_f32_ws / gemm_bf16_f32acc_ws, split-K across workgroups where
 the problem is too small to fill the device) with a workspace of the size the library asks
 for, allocated before the timed region.  Each GEMM's inputs
@@ -130,24 +131,30 @@ class Leg:
         self.algo = g.Algo[algo]
         self.problems = []
         self.A, self.B = [], []
+        self.batched = self.w.batch > 1
+        if self.batched and (algo != "AUTO" or workspace):
+            raise SystemExit("a strided batch runs the default kernel choice without a workspace")
+        e = 4 if self.w.dtype == "f32" else 2
         if sets <= 0:
-            e = 4 if self.w.dtype == "f32" else 2
-            per_set = e * (self.w.M * self.w.K + self.w.K * self.w.N)
+            per_set = e * self.w.batch * (self.w.M * self.w.K + self.w.K * self.w.N)
             sets = min(64, max(2, (512 * 2**20) // per_set + 1))
         self.sets = sets
         for s in range(sets):
             w = self.w
-            p = gi.make_problem(w.M, w.N, w.K, w.dtype, w.order_a, w.order_b, w.order_c, w.dist,
-                                w.wid + 1000 * s)
+            p = gi.workload_problem(name, 1000 * s)
             self.problems.append(p)
             conv = (lambda b: b.view(np.int16)) if w.dtype in ("bf16", "f16") else (lambda b: b)
             self.A.append(torch.from_numpy(conv(p.A)).to("cuda"))
             self.B.append(torch.from_numpy(conv(p.B)).to("cuda"))
         p = self.problems[0]
-        self.C = torch.empty(gi.c_buffer_size(p.M, p.N, p.ldc, p.order_c), dtype=torch.float32,
-                             device="cuda")
+        size = p.c_size() if self.batched else gi.c_buffer_size(p.M, p.N, p.ldc, p.order_c)
+        self.C = torch.empty(size, dtype=torch.float32, device="cuda")
         self.fn = {"f32": g.gemm_f32_algo, "bf16": g.gemm_bf16_f32acc_algo, "f16": g.gemm_f16_f32acc_algo}[w.dtype]
-        self.flops = 2 * w.M * w.N * w.K
+        self.fn_batched = {"f32": g.gemm_f32_strided_batched, "bf16": g.gemm_bf16_f32acc_strided_batched,
+                           "f16": g.gemm_f16_f32acc_strided_batched}[w.dtype]
+        self.flops = w.flops
+        # compulsory HBM bytes: every input element read once, every output element written once
+        self.bytes = w.batch * (e * (w.M * w.K + w.K * w.N) + 4 * w.M * w.N)
         self.kernel = None
         self.ws, self.ws_bytes = None, 0
         if workspace:
@@ -161,6 +168,11 @@ class Leg:
 
     def launch(self, s, stream):
         p = self.problems[s % len(self.problems)]
+        if self.batched:
+            self.fn_batched(p.batch, p.M, p.N, p.K, self.A[s % len(self.A)].data_ptr(), p.lda, p.sa, p.order_a,
+                            self.B[s % len(self.B)].data_ptr(), p.ldb, p.sb, p.order_b, self.C.data_ptr(), p.ldc,
+                            p.sc, p.order_c, stream)
+            return
         if self.ws is not None:
             self.fn_ws(p.M, p.N, p.K, self.A[s % len(self.A)].data_ptr(), p.lda, p.order_a,
                        self.B[s % len(self.B)].data_ptr(), p.ldb, p.order_b, self.C.data_ptr(), p.ldc,
@@ -199,7 +211,8 @@ def cpu_baseline(legs, target_s):
     flops = sum(2 * rows * l.w.N * l.w.K for l in legs)
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "seconds": round(t, 3),
-            "sample": f"first {rows} rows of C for each of {', '.join(l.name for l in legs)} "
+            "sample": f"first {rows} rows of C for each of "
+                      f"{', '.join(l.name + (' (entry 0)' if l.batched else '') for l in legs)} "
                       f"({flops / 2:.3e} multiply-adds, fp64 oracle, {threads} OpenMP threads)"}
 
 
@@ -249,18 +262,29 @@ def main():
         tf = leg.flops / (ms * 1e-3) / 1e12
         leg_info[leg.name] = {"kernel": leg.kernel, "ms": round(ms, 5), "tflops": round(tf, 2),
                               "pct_peak": round(100 * tf * 1e12 / peak, 2),
-                              "M": leg.w.M, "N": leg.w.N, "K": leg.w.K, "dtype_in": leg.w.dtype,
+                              "M": leg.w.M, "N": leg.w.N, "K": leg.w.K, "batch": leg.w.batch,
+                              "dtype_in": leg.w.dtype, "gb_per_s": round(leg.bytes / (ms * 1e-3) / 1e9, 1),
                               "input_sets": leg.sets}
         if leg.ws is not None:
             leg_info[leg.name]["workspace_bytes"] = leg.ws_bytes
     dom = max(legs, key=lambda l: leg_info[l.name]["ms"])
     di = leg_info[dom.name]
     peak = rl.mi355x_peak(dom.w.dtype)
-    achieved = dom.flops / (di["ms"] * 1e-3)
-    roof = {"bound": "mfma", "kernel": di["kernel"], "achieved": round(achieved / 1e12, 2),
-            "peak": round(peak / 1e12, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-            "traffic": measured_traffic(di["kernel"], dom.name),
-            "per_launch": f"2*M*N*K = {dom.flops:.4e} FLOP per launch ({dom.name})"}
+    per = f" x {dom.w.batch} entries" if dom.batched else ""
+    if dom.bytes / rl.MI355X_HBM_BYTES_PER_S > dom.flops / peak:
+        # the compulsory traffic takes longer at HBM's peak than the arithmetic at the matrix cores'
+        achieved = dom.bytes / (di["ms"] * 1e-3)
+        roof = {"bound": "hbm", "kernel": di["kernel"], "achieved": round(achieved / 1e9, 1),
+                "peak": rl.MI355X_HBM_BYTES_PER_S / 1e9, "unit": "GB/s",
+                "frac": round(achieved / rl.MI355X_HBM_BYTES_PER_S, 4),
+                "traffic": measured_traffic(di["kernel"], dom.name),
+                "per_launch": f"e*(M*K + K*N) + 4*M*N{per} = {dom.bytes:.4e} B per launch ({dom.name})"}
+    else:
+        achieved = dom.flops / (di["ms"] * 1e-3)
+        roof = {"bound": "mfma", "kernel": di["kernel"], "achieved": round(achieved / 1e12, 2),
+                "peak": round(peak / 1e12, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": measured_traffic(di["kernel"], dom.name),
+                "per_launch": f"2*M*N*K{per} = {dom.flops:.4e} FLOP per launch ({dom.name})"}
 
     value = step_flops / (ms_step * 1e-3) / 1e12
     dtype = "+".join(sorted({"f32" if l.w.dtype == "f32" else "bf16->f32" for l in legs}))

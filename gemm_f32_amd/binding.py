@@ -94,13 +94,20 @@ def _load():
         f.argtypes, f.restype = args[:-1] + [vp, ctypes.c_size_t, vp], ci
     lib.gemm_f16_f32acc.argtypes, lib.gemm_f16_f32acc.restype = args, ci
     lib.gemm_f16_f32acc_algo.argtypes, lib.gemm_f16_f32acc_algo.restype = [ci] + args, ci
+    batched = [i64, i64, i64, i64, vp, i64, i64, ci, vp, i64, i64, ci, vp, i64, i64, ci, vp]
+    for name in ("gemm_f32_strided_batched", "gemm_bf16_f32acc_strided_batched",
+                 "gemm_f16_f32acc_strided_batched"):
+        f = getattr(lib, name)
+        f.argtypes, f.restype = batched, ci
     return lib
 
 
 EXPORTED = ("gemm_f32", "gemm_bf16_f32acc", "gemm_f32_algo", "gemm_bf16_f32acc_algo",
             "gemm_status_string", "gemm_last_hip_error", "gemm_last_kernel", "gemm_version",
             "gemm_plan", "gemm_workspace_size", "gemm_f32_ws", "gemm_bf16_f32acc_ws",
-            "gemm_f16_f32acc", "gemm_f16_f32acc_algo", "gemm_f16_f32acc_ws")
+            "gemm_f16_f32acc", "gemm_f16_f32acc_algo", "gemm_f16_f32acc_ws",
+            "gemm_f32_strided_batched", "gemm_bf16_f32acc_strided_batched",
+            "gemm_f16_f32acc_strided_batched")
 
 # dtype codes of gemm_plan / gemm_workspace_size
 DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2}
@@ -203,6 +210,30 @@ def gemm_bf16_f32acc_ws(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order
 
 
 # --- torch tensors -> (pointer, leading dimension, order) ------------------------------
+def gemm_f32_strided_batched(batch, M, N, K, A, lda, stride_a, order_a, B, ldb, stride_b, order_b,
+                             C, ldc, stride_c, order_c, stream=0):
+    """C_z = A_z.B_z for z < batch, FP32; entry z at A + z*stride_a etc. (element strides)."""
+    _check(lib_handle().gemm_f32_strided_batched(batch, M, N, K, A, lda, stride_a, order_a, B, ldb, stride_b,
+                                                 order_b, C, ldc, stride_c, order_c, stream),
+           "gemm_f32_strided_batched")
+
+
+def gemm_bf16_f32acc_strided_batched(batch, M, N, K, A, lda, stride_a, order_a, B, ldb, stride_b, order_b,
+                                     C, ldc, stride_c, order_c, stream=0):
+    """Strided batch of bf16 products (bit patterns), FP32 accumulate and FP32 C."""
+    _check(lib_handle().gemm_bf16_f32acc_strided_batched(batch, M, N, K, A, lda, stride_a, order_a, B, ldb,
+                                                         stride_b, order_b, C, ldc, stride_c, order_c, stream),
+           "gemm_bf16_f32acc_strided_batched")
+
+
+def gemm_f16_f32acc_strided_batched(batch, M, N, K, A, lda, stride_a, order_a, B, ldb, stride_b, order_b,
+                                    C, ldc, stride_c, order_c, stream=0):
+    """Strided batch of IEEE fp16 products (bit patterns), FP32 accumulate and FP32 C."""
+    _check(lib_handle().gemm_f16_f32acc_strided_batched(batch, M, N, K, A, lda, stride_a, order_a, B, ldb,
+                                                        stride_b, order_b, C, ldc, stride_c, order_c, stream),
+           "gemm_f16_f32acc_strided_batched")
+
+
 def operand_layout(t) -> tuple[int, int]:
     """(ld, order) of a 2-D tensor whose memory is row- or column-major with padding."""
     if t.dim() != 2:

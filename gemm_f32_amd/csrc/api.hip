@@ -96,6 +96,11 @@ const char* skinny_name(int et, int fn) {
     return names[et][fn == 4 ? 1 : 0];
 }
 
+// A strided batch on the normalised problem (element strides; C's in floats); n == 1: one problem.
+struct Batch {
+    int64_t n = 1, sa = 0, sb = 0, sc = 0;
+};
+
 // A caller's workspace (gemm_*_ws); empty for the plain entry points.
 struct Workspace {
     void* ptr = nullptr;
@@ -223,11 +228,15 @@ Plan plan_whole(const Problem& p, const TileOpt& o, int cus) {
 
 // Options for a (sub-)problem whose C starts at p.C: 16-byte stores need an aligned C and
 // ldc; 16-byte loads and global->LDS copies need only element alignment on gfx950.
-Launch launch_for(const Problem& p, hipStream_t stream) {
+Launch launch_for(const Problem& p, hipStream_t stream, const Batch& b = Batch{}) {
     Launch o{};
     o.stream = stream;
     o.vec_a = o.vec_b = true;
-    o.vec_c = (p.ldc % 4 == 0) && aligned(p.C, 16);
+    o.vec_c = (p.ldc % 4 == 0) && aligned(p.C, 16) && (b.n == 1 || b.sc % 4 == 0);
+    o.batch = (int)b.n;
+    o.sa = b.sa;
+    o.sb = b.sb;
+    o.sc = b.sc;
     return o;
 }
 
@@ -245,23 +254,26 @@ Problem sub_problem(const Problem& p, int r0, int m, int c0, int n, int elem) {
 }
 
 hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, int et, const DeviceInfo& dev,
-                    const char*& name, gemm_status_t& st, const Workspace& ws = Workspace{});
+                    const char*& name, gemm_status_t& st, const Workspace& ws = Workspace{},
+                    const Batch& b = Batch{});
 
 // Run a plan's core with `core` and its strips through the default choice, on one stream.
 template <typename CoreFn>
 hipError_t run_plan(const Problem& p, hipStream_t stream, const Plan& pl, int et, const DeviceInfo& dev,
-                    CoreFn core) {
+                    const Batch& b, CoreFn core) {
     const int e = et == kElemF32 ? 4 : 2;
     const Problem c = sub_problem(p, 0, pl.mc, 0, pl.nc, e);
-    Launch lc = launch_for(c, stream);
+    Launch lc = launch_for(c, stream, b);
     lc.group_m = pick_group_m((c.M + pl.opt.bm - 1) / pl.opt.bm, (c.N + pl.opt.bn - 1) / pl.opt.bn);
     hipError_t err = core(c, lc);
     const char* ignored = nullptr;
     gemm_status_t st = GEMM_OK;
     if (err == hipSuccess && pl.mc < p.M)        // rows mc .. M-1, all columns
-        err = dispatch(sub_problem(p, pl.mc, p.M - pl.mc, 0, p.N, e), stream, GEMM_ALGO_AUTO, et, dev, ignored, st);
+        err = dispatch(sub_problem(p, pl.mc, p.M - pl.mc, 0, p.N, e), stream, GEMM_ALGO_AUTO, et, dev, ignored, st,
+                       Workspace{}, b);
     if (err == hipSuccess && pl.nc < p.N)        // rows 0 .. mc-1, columns nc .. N-1
-        err = dispatch(sub_problem(p, 0, pl.mc, pl.nc, p.N - pl.nc, e), stream, GEMM_ALGO_AUTO, et, dev, ignored, st);
+        err = dispatch(sub_problem(p, 0, pl.mc, pl.nc, p.N - pl.nc, e), stream, GEMM_ALGO_AUTO, et, dev, ignored, st,
+                       Workspace{}, b);
     return err;
 }
 
@@ -299,12 +311,12 @@ Plan choose_f32_tiles(const Problem& p, gemm_algo_t algo, int cus) {
 }
 
 hipError_t run_f32_tiles(const Problem& p, hipStream_t stream, gemm_algo_t algo, const DeviceInfo& dev,
-                         const char*& name, gemm_status_t& st) {
+                         const char*& name, gemm_status_t& st, const Batch& b) {
     const Plan best = choose_f32_tiles(p, algo, dev.cus);
     if (best.cost >= 1e300) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
     name = f32_name(best.opt);
     const TileOpt o = best.opt;
-    return run_plan(p, stream, best, kElemF32, dev, [&](const Problem& c, const Launch& lc) {
+    return run_plan(p, stream, best, kElemF32, dev, b, [&](const Problem& c, const Launch& lc) {
         return o.dma ? launch_f32_dma(c, lc, o.bm, o.bn) : launch_f32_mfma(c, lc, o.bm);
     });
 }
@@ -332,13 +344,13 @@ Plan choose_bf16_tiles(const Problem& p, gemm_algo_t algo, int cus) {
 }
 
 hipError_t run_b16_tiles(const Problem& p, hipStream_t stream, gemm_algo_t algo, int et, const DeviceInfo& dev,
-                         const char*& name, gemm_status_t& st) {
+                         const char*& name, gemm_status_t& st, const Batch& b) {
     const Plan best = choose_bf16_tiles(p, algo, dev.cus);
     if (best.cost >= 1e300) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
     name = b16_name(best.opt, et);
     const TileOpt o = best.opt;
     const bool f16 = et == kElemF16;
-    return run_plan(p, stream, best, et, dev, [&](const Problem& c, const Launch& lc) {
+    return run_plan(p, stream, best, et, dev, b, [&](const Problem& c, const Launch& lc) {
         return o.dma ? launch_bf16_dma(c, lc, o.bm, o.bn, f16) : launch_bf16_mfma(c, lc, o.bm, o.bn, f16);
     });
 }
@@ -346,8 +358,8 @@ hipError_t run_b16_tiles(const Problem& p, hipStream_t stream, gemm_algo_t algo,
 // Kernel choice and launch for a normalised problem (row-major C, K > 0).  A status other
 // than GEMM_OK in `st` means the request is invalid (nothing launched).
 hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, int et, const DeviceInfo& dev,
-                    const char*& name, gemm_status_t& st, const Workspace& ws) {
-    Launch l = launch_for(p, stream);
+                    const char*& name, gemm_status_t& st, const Workspace& ws, const Batch& b) {
+    Launch l = launch_for(p, stream, b);
     if (et == kElemF32) {
         switch (algo) {
             case GEMM_ALGO_NAIVE_UNCOALESCED: name = "f32_naive_uncoalesced"; return launch_naive(p, l, false);
@@ -363,7 +375,7 @@ hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, int 
             default:
                 if (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus) && skinny_applies(p, false))
                     return run_skinny(p, l, kElemF32, dev.cus, name, ws);
-                return run_f32_tiles(p, stream, algo, dev, name, st);
+                return run_f32_tiles(p, stream, algo, dev, name, st, b);
         }
     }
     if (algo == GEMM_ALGO_SKINNY ||
@@ -378,7 +390,7 @@ hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, int 
         name = "bf16_pingpong256x256";
         return launch_bf16_pingpong(p, l);
     }
-    return run_b16_tiles(p, stream, algo, et, dev, name, st);
+    return run_b16_tiles(p, stream, algo, et, dev, name, st, b);
 }
 
 // The problem the library computes for extents and orders with tight leading dimensions and
@@ -461,6 +473,78 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
     if (err != hipSuccess) {
         t_last_hip_error = (int)err;
         return GEMM_ERR_LAUNCH;
+    }
+    t_last_kernel = name;
+    return GEMM_OK;
+}
+
+// Entries of a strided batch that one launch covers (the grid's z extent).
+constexpr int64_t kMaxBatchLaunch = 65535;
+
+// Whether the entries of a batched C (normalised: row-major M x N, leading dimension ldc,
+// entry stride sc) are disjoint: stacked (each entry starts past the previous one's last
+// element) or side by side within each row (sc >= N and all n entries inside ldc).
+bool c_entries_disjoint(int64_t M, int64_t N, int64_t ldc, int64_t sc, int64_t n) {
+    if (n <= 1) return true;
+    if ((__int128)sc >= (__int128)(M - 1) * ldc + N) return true;
+    return sc >= N && (n - 1) <= (ldc - N) / sc;
+}
+
+template <typename Elem>
+gemm_status_t run_batched(In in, int64_t batch, int64_t M, int64_t N, int64_t K, const Elem* A, int64_t lda,
+                          int64_t sa, gemm_order_t oa, const Elem* B, int64_t ldb, int64_t sb, gemm_order_t ob,
+                          float* C, int64_t ldc, int64_t sc, gemm_order_t oc, hipStream_t stream) {
+    gemm_status_t st = validate(in, M, N, K, A, lda, oa, B, ldb, ob, C, ldc, oc);
+    if (st != GEMM_OK) return st;
+    if (batch < 0 || sa < 0 || sb < 0 || sc < 0) return GEMM_ERR_INVALID_VALUE;
+    const int64_t span = batch > 1 ? batch - 1 : 0;       // entry offsets, in bytes, fit in int64
+    for (int64_t s : {sa, sb, sc})
+        if (span > 0 && s > INT64_MAX / 4 / span) return GEMM_ERR_INVALID_VALUE;
+    const bool row = oc == GEMM_ROW_MAJOR;
+    if (M > 0 && N > 0 && !c_entries_disjoint(row ? M : N, row ? N : M, ldc, sc, batch))
+        return GEMM_ERR_INVALID_VALUE;
+    if (batch == 0 || M == 0 || N == 0) {
+        t_last_kernel = "none";
+        return GEMM_OK;
+    }
+    DeviceInfo dev;
+    if (!device_info(dev) || !dev.supported) return GEMM_ERR_UNSUPPORTED_DEVICE;
+
+    // Column-major C: every entry computes C^T = B^T A^T, so A and B swap strides too.
+    Problem p{};
+    Batch b{};
+    if (row) {
+        p = Problem{(int)M, (int)N, (int)K, A, lda, (int)oa, B, ldb, (int)ob, C, ldc};
+        b = Batch{batch, sa, sb, sc};
+    } else {
+        p = Problem{(int)N, (int)M, (int)K, B, ldb, 1 - (int)ob, A, lda, 1 - (int)oa, C, ldc};
+        b = Batch{batch, sb, sa, sc};
+    }
+    const int e = in == In::F32 ? 4 : 2;
+    const char* name = "none";
+    for (int64_t z0 = 0; z0 < batch; z0 += kMaxBatchLaunch) {
+        Batch bz = b;
+        bz.n = std::min(kMaxBatchLaunch, batch - z0);
+        Problem pz = p;
+        pz.A = static_cast<const char*>(p.A) + z0 * b.sa * e;
+        pz.B = static_cast<const char*>(p.B) + z0 * b.sb * e;
+        pz.C = p.C + z0 * b.sc;
+        hipError_t err = hipSuccess;
+        if (K == 0) {
+            err = launch_zero_c(pz, launch_for(pz, stream, bz));
+            name = "zero_c";
+        } else {
+            // the planner prices tiles against the CUs one entry gets
+            DeviceInfo de = dev;
+            de.cus = (int)std::max<int64_t>(1, dev.cus / bz.n);
+            gemm_status_t bad = GEMM_OK;
+            err = dispatch(pz, stream, GEMM_ALGO_AUTO, elem_of(in), de, name, bad, Workspace{}, bz);
+            if (bad != GEMM_OK) return bad;
+        }
+        if (err != hipSuccess) {
+            t_last_hip_error = (int)err;
+            return GEMM_ERR_LAUNCH;
+        }
     }
     t_last_kernel = name;
     return GEMM_OK;
@@ -577,6 +661,32 @@ gemm_status_t gemm_f16_f32acc_ws(int64_t M, int64_t N, int64_t K, const uint16_t
                                  size_t workspace_bytes, hipStream_t stream) {
     return gemm::run(gemm::In::F16, GEMM_ALGO_AUTO, M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc,
                      order_c, stream, gemm::Workspace{workspace, workspace_bytes});
+}
+
+gemm_status_t gemm_f32_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const float* A,
+                                       int64_t lda, int64_t stride_a, gemm_order_t order_a, const float* B,
+                                       int64_t ldb, int64_t stride_b, gemm_order_t order_b, float* C,
+                                       int64_t ldc, int64_t stride_c, gemm_order_t order_c, hipStream_t stream) {
+    return gemm::run_batched(gemm::In::F32, batch, M, N, K, A, lda, stride_a, order_a, B, ldb, stride_b, order_b,
+                             C, ldc, stride_c, order_c, stream);
+}
+
+gemm_status_t gemm_bf16_f32acc_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
+                                               const uint16_t* A, int64_t lda, int64_t stride_a,
+                                               gemm_order_t order_a, const uint16_t* B, int64_t ldb,
+                                               int64_t stride_b, gemm_order_t order_b, float* C, int64_t ldc,
+                                               int64_t stride_c, gemm_order_t order_c, hipStream_t stream) {
+    return gemm::run_batched(gemm::In::BF16, batch, M, N, K, A, lda, stride_a, order_a, B, ldb, stride_b, order_b,
+                             C, ldc, stride_c, order_c, stream);
+}
+
+gemm_status_t gemm_f16_f32acc_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
+                                              const uint16_t* A, int64_t lda, int64_t stride_a,
+                                              gemm_order_t order_a, const uint16_t* B, int64_t ldb,
+                                              int64_t stride_b, gemm_order_t order_b, float* C, int64_t ldc,
+                                              int64_t stride_c, gemm_order_t order_c, hipStream_t stream) {
+    return gemm::run_batched(gemm::In::F16, batch, M, N, K, A, lda, stride_a, order_a, B, ldb, stride_b, order_b,
+                             C, ldc, stride_c, order_c, stream);
 }
 
 const char* gemm_status_string(gemm_status_t status) {

@@ -96,12 +96,13 @@ struct Cfg {
     static_assert(NW % 4 == 0, "whole wavefronts per SIMD");
 };
 
-template <typename C, bool VEC_C, bool F16 = false>
+template <typename C, bool VEC_C, bool F16 = false, bool BATCH = false>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::NW / 4, C::NW / 4)))
-void k_bf16_dma(Problem p, int tiles_m, int tiles_n, int group_m) {
+void k_bf16_dma(KArg<BATCH> p, int tiles_m, int tiles_n, int group_m) {
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, FM = C::FM, FN = C::FN, SUB = C::SUB;
     constexpr int ROW = C::ROW, MF = C::MF;
     __shared__ __align__(16) unsigned char smem[C::LDS];
+    if constexpr (BATCH) p.select(blockIdx.z);
 
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
@@ -350,19 +351,25 @@ void k_bf16_dma(Problem p, int tiles_m, int tiles_n, int group_m) {
     }
 }
 
-template <typename C>
-hipError_t launch_cfg(const Problem& p, const Launch& l, bool f16) {
+template <typename C, bool BATCH>
+hipError_t launch_cfg(const KArg<BATCH>& p, const Launch& l, bool f16) {
     const int tiles_m = (p.M + C::BM - 1) / C::BM, tiles_n = (p.N + C::BN - 1) / C::BN;
-    const dim3 grid((unsigned)tiles_m * tiles_n), block(C::THREADS);
+    const dim3 grid((unsigned)tiles_m * tiles_n, 1, BATCH ? l.batch : 1), block(C::THREADS);
     if (f16 && l.vec_c)
-        hipLaunchKernelGGL((k_bf16_dma<C, true, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
+        hipLaunchKernelGGL((k_bf16_dma<C, true, true, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
     else if (f16)
-        hipLaunchKernelGGL((k_bf16_dma<C, false, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
+        hipLaunchKernelGGL((k_bf16_dma<C, false, true, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
     else if (l.vec_c)
-        hipLaunchKernelGGL((k_bf16_dma<C, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
+        hipLaunchKernelGGL((k_bf16_dma<C, true, false, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
     else
-        hipLaunchKernelGGL((k_bf16_dma<C, false>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
+        hipLaunchKernelGGL((k_bf16_dma<C, false, false, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
     return hipGetLastError();
+}
+
+template <typename C>
+hipError_t launch_any(const Problem& p, const Launch& l, bool f16) {
+    if (l.batch > 1) return launch_cfg<C, true>(batch_arg(p, l, 2), l, f16);
+    return launch_cfg<C, false>(p, l, f16);
 }
 
 }  // namespace
@@ -381,8 +388,8 @@ bool bf16_dma_applies(const Problem& p, const Launch&, int, int) {
 // 2048 of matrix work; 256 x 128 1350 against 1024 (four wavefronts of 128 x 64: 1425 with
 // three stages, 1540-1630 with two).
 hipError_t launch_bf16_dma(const Problem& p, const Launch& l, int bm, int bn, bool f16) {
-    if (bm == 256 && bn == 256) return launch_cfg<Cfg<256, 256, 2, 4, 2, 2>>(p, l, f16);
-    if (bm == 256 && bn == 128) return launch_cfg<Cfg<256, 128, 4, 2, 4, 3>>(p, l, f16);
+    if (bm == 256 && bn == 256) return launch_any<Cfg<256, 256, 2, 4, 2, 2>>(p, l, f16);
+    if (bm == 256 && bn == 128) return launch_any<Cfg<256, 128, 4, 2, 4, 3>>(p, l, f16);
     return hipErrorInvalidValue;
 }
 

@@ -150,14 +150,15 @@ __device__ __forceinline__ void store_rc(unsigned char* s, int q, uint4 v) {
     }
 }
 
-template <int BM, int BN, int BK, int S, bool A_KC, bool B_KC, bool F16 = false>
+template <int BM, int BN, int BK, int S, bool A_KC, bool B_KC, bool F16 = false, bool BATCH = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
-void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, int vec_b, int direct) {
+void k_bf16_mfma(KArg<BATCH> p, int tiles_m, int tiles_n, int group_m, int vec_a, int vec_b, int direct) {
     using T = Tile<BM, BN, BK, S>;
     constexpr int CH = T::CH;
     // the direct path issues one tile's copies in the first SUB * FM * FN instruction slots
     static_assert(T::SUB * T::FM * T::FN >= T::A_DMA + T::B_DMA, "too few slots for the copies");
     __shared__ __align__(16) unsigned char smem[T::LDS];
+    if constexpr (BATCH) p.select(blockIdx.z);
 
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
@@ -391,26 +392,30 @@ void k_bf16_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, in
         }
 }
 
-template <int BM, int BN, int BK, int S, bool F16>
-hipError_t launch_tile_t(const Problem& p, const Launch& l) {
+template <int BM, int BN, int BK, int S, bool F16, bool BATCH>
+hipError_t launch_tile_t(const KArg<BATCH>& p, const Launch& l) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-    const dim3 grid((unsigned)tiles_m * tiles_n), block(256);
+    const dim3 grid((unsigned)tiles_m * tiles_n, 1, BATCH ? l.batch : 1), block(256);
     const bool akc = p.oa == kRow, bkc = p.ob == kCol;
     const int va = l.vec_a, vb = l.vec_b, g = l.group_m, al = l.vec_a && l.vec_b;   // direct copies allowed
     if (akc && bkc)
-        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, true, true, F16>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
+        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, true, true, F16, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
     else if (akc)
-        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, true, false, F16>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
+        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, true, false, F16, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
     else if (bkc)
-        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, false, true, F16>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
+        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, false, true, F16, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
     else
-        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, false, false, F16>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
+        hipLaunchKernelGGL((k_bf16_mfma<BM, BN, BK, S, false, false, F16, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb, al);
     return hipGetLastError();
 }
 
 template <int BM, int BN, int BK, int S>
 hipError_t launch_tile(const Problem& p, const Launch& l, bool f16) {
-    return f16 ? launch_tile_t<BM, BN, BK, S, true>(p, l) : launch_tile_t<BM, BN, BK, S, false>(p, l);
+    if (l.batch > 1) {
+        const BatchProblem b = batch_arg(p, l, 2);
+        return f16 ? launch_tile_t<BM, BN, BK, S, true, true>(b, l) : launch_tile_t<BM, BN, BK, S, false, true>(b, l);
+    }
+    return f16 ? launch_tile_t<BM, BN, BK, S, true, false>(p, l) : launch_tile_t<BM, BN, BK, S, false, false>(p, l);
 }
 
 }  // namespace

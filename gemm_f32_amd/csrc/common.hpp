@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gemm {
 
 enum Order : int { kRow = 0, kCol = 1 };
@@ -24,6 +26,20 @@ struct Problem {
     float* C;
     int64_t ldc;
 };
+
+// A strided batch of problems of one shape: entry z reads A + z*sa and B + z*sb (bytes) and
+// writes C + z*sc (floats).  The batched instantiation of a kernel takes its entry from
+// blockIdx.z and moves the three pointers before anything else; the plain instantiation takes
+// a Problem and has no such step.
+struct BatchProblem : Problem {
+    int64_t sa, sb, sc;
+    __device__ __forceinline__ void select(int64_t z) {
+        A = static_cast<const char*>(A) + z * sa;
+        B = static_cast<const char*>(B) + z * sb;
+        C += z * sc;
+    }
+};
+template <bool BATCH> using KArg = std::conditional_t<BATCH, BatchProblem, Problem>;
 
 // Offset of logical element (r, c) in an operand with leading dimension ld and order o.
 __device__ __forceinline__ int64_t elem_offset(int64_t r, int64_t c, int64_t ld, int o) {
@@ -68,7 +84,19 @@ struct Launch {
     int group_m;        // tile-scheduler band height (>= 1)
     bool vec_a, vec_b;  // 16-byte loads of the operand are allowed (load16 / load16f)
     bool vec_c;         // C pointer and ldc allow 16-byte stores
+    int batch = 1;      // entries of a strided batch (gridDim.z); 1: one problem
+    int64_t sa = 0, sb = 0, sc = 0;   // element strides between entries (A, B; C in floats)
 };
+
+// The kernel argument of a batched launch: strides of A and B turned into bytes.
+inline BatchProblem batch_arg(const Problem& p, const Launch& l, int elem_bytes) {
+    BatchProblem b{};
+    static_cast<Problem&>(b) = p;
+    b.sa = l.sa * elem_bytes;
+    b.sb = l.sb * elem_bytes;
+    b.sc = l.sc;
+    return b;
+}
 
 // 16-byte global loads from addresses aligned to the element only.  gfx950 serves unaligned
 // vector loads from global memory, and its 16-byte global->LDS copies too (the parity tests

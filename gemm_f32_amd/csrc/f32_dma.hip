@@ -124,12 +124,13 @@ struct CopyPlan {
     }
 };
 
-template <typename C>
+template <typename C, bool BATCH = false>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
-void k_f32_dma(Problem p, int tiles_m, int tiles_n, int group_m) {
+void k_f32_dma(KArg<BATCH> p, int tiles_m, int tiles_n, int group_m) {
     constexpr int BM = C::BM, BN = C::BN, S = C::S, FM = C::FM, FN = C::FN;
     constexpr bool A_KC = C::A_KC, B_KC = C::B_KC;
     __shared__ __align__(16) unsigned char smem[S * C::STAGE];
+    if constexpr (BATCH) p.select(blockIdx.z);
 
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
@@ -388,12 +389,13 @@ struct EdgeCopyPlan {
     }
 };
 
-template <typename C>
+template <typename C, bool BATCH = false>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
-void k_f32_dma_edge(Problem p, int tiles_m, int tiles_n, int group_m) {
+void k_f32_dma_edge(KArg<BATCH> p, int tiles_m, int tiles_n, int group_m) {
     constexpr int BM = C::BM, BN = C::BN, S = C::S, FM = C::FM, FN = C::FN;
     constexpr bool A_KC = C::A_KC, B_KC = C::B_KC;
     __shared__ __align__(16) unsigned char smem[S * C::STAGE];
+    if constexpr (BATCH) p.select(blockIdx.z);
 
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
@@ -628,10 +630,10 @@ void k_f32_dma_edge(Problem p, int tiles_m, int tiles_n, int group_m) {
     else store(std::true_type{});
 }
 
-template <int BM, int BN, int WGM, int WGN, int S>
-hipError_t launch_cfg(const Problem& p, const Launch& l) {
+template <int BM, int BN, int WGM, int WGN, int S, bool BATCH>
+hipError_t launch_cfg(const KArg<BATCH>& p, const Launch& l) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-    const dim3 grid((unsigned)tiles_m * tiles_n), block(64 * WGM * WGN);
+    const dim3 grid((unsigned)tiles_m * tiles_n, 1, BATCH ? l.batch : 1), block(64 * WGM * WGN);
     const bool akc = p.oa == kRow, bkc = p.ob == kCol;
     const int g = l.group_m;
     // tiles may overhang only the k-contiguous operands' edges
@@ -639,22 +641,28 @@ hipError_t launch_cfg(const Problem& p, const Launch& l) {
     if ((over_m && !akc) || (over_n && !bkc)) return hipErrorInvalidValue;
     if (over_m || over_n) {
         if (akc && bkc)
-            hipLaunchKernelGGL((k_f32_dma_edge<Cfg<BM, BN, WGM, WGN, S, true, true>>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
+            hipLaunchKernelGGL((k_f32_dma_edge<Cfg<BM, BN, WGM, WGN, S, true, true>, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
         else if (akc)
-            hipLaunchKernelGGL((k_f32_dma_edge<Cfg<BM, BN, WGM, WGN, S, true, false>>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
+            hipLaunchKernelGGL((k_f32_dma_edge<Cfg<BM, BN, WGM, WGN, S, true, false>, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
         else
-            hipLaunchKernelGGL((k_f32_dma_edge<Cfg<BM, BN, WGM, WGN, S, false, true>>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
+            hipLaunchKernelGGL((k_f32_dma_edge<Cfg<BM, BN, WGM, WGN, S, false, true>, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
         return hipGetLastError();
     }
     if (akc && bkc)
-        hipLaunchKernelGGL((k_f32_dma<Cfg<BM, BN, WGM, WGN, S, true, true>>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
+        hipLaunchKernelGGL((k_f32_dma<Cfg<BM, BN, WGM, WGN, S, true, true>, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
     else if (akc)
-        hipLaunchKernelGGL((k_f32_dma<Cfg<BM, BN, WGM, WGN, S, true, false>>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
+        hipLaunchKernelGGL((k_f32_dma<Cfg<BM, BN, WGM, WGN, S, true, false>, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
     else if (bkc)
-        hipLaunchKernelGGL((k_f32_dma<Cfg<BM, BN, WGM, WGN, S, false, true>>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
+        hipLaunchKernelGGL((k_f32_dma<Cfg<BM, BN, WGM, WGN, S, false, true>, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
     else
-        hipLaunchKernelGGL((k_f32_dma<Cfg<BM, BN, WGM, WGN, S, false, false>>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
+        hipLaunchKernelGGL((k_f32_dma<Cfg<BM, BN, WGM, WGN, S, false, false>, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g);
     return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN, int S>
+hipError_t launch_any(const Problem& p, const Launch& l) {
+    if (l.batch > 1) return launch_cfg<BM, BN, WGM, WGN, S, true>(batch_arg(p, l, 4), l);
+    return launch_cfg<BM, BN, WGM, WGN, S, false>(p, l);
 }
 
 }  // namespace
@@ -671,8 +679,8 @@ bool f32_dma_applies(const Problem& p, const Launch& l, int bm, int bn) {
 // Configurations: 256 x 256 with 8 wavefronts of 64 x 128 (2 per SIMD, 128 KB of LDS),
 // 128 x 128 with 4 wavefronts of 64 x 64 (two workgroups per CU).
 hipError_t launch_f32_dma(const Problem& p, const Launch& l, int bm, int bn) {
-    if (bm == 256 && bn == 256) return launch_cfg<256, 256, 4, 2, 2>(p, l);
-    if (bm == 128 && bn == 128) return launch_cfg<128, 128, 2, 2, 2>(p, l);
+    if (bm == 256 && bn == 256) return launch_any<256, 256, 4, 2, 2>(p, l);
+    if (bm == 128 && bn == 128) return launch_any<128, 128, 2, 2, 2>(p, l);
     return hipErrorInvalidValue;
 }
 

@@ -91,12 +91,13 @@ __device__ __forceinline__ void store4(float* T, int idx, float4 v) {
     }
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, bool PF, int PAD, bool A_KC, bool B_KC>
+template <int BM, int BN, int BK, int WGM, int WGN, bool PF, int PAD, bool A_KC, bool B_KC, bool BATCH = false>
 __global__ __launch_bounds__(64 * WGM * WGN)
-void k_f32_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, int vec_b) {
+void k_f32_mfma(KArg<BATCH> p, int tiles_m, int tiles_n, int group_m, int vec_a, int vec_b) {
     using T = F32Tile<BM, BN, BK, WGM, WGN, PAD>;
     __shared__ __align__(16) float As[2][BK * T::PA];
     __shared__ __align__(16) float Bs[2][BK * T::PB];
+    if constexpr (BATCH) p.select(blockIdx.z);
 
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
@@ -198,28 +199,34 @@ void k_f32_mfma(Problem p, int tiles_m, int tiles_n, int group_m, int vec_a, int
         }
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, bool PF, int PAD = 28>
-hipError_t launch_cfg(const Problem& p, const Launch& l) {
+template <int BM, int BN, int BK, int WGM, int WGN, bool PF, int PAD, bool BATCH>
+hipError_t launch_cfg(const KArg<BATCH>& p, const Launch& l) {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-    const dim3 grid((unsigned)tiles_m * tiles_n), block(64 * WGM * WGN);
+    const dim3 grid((unsigned)tiles_m * tiles_n, 1, BATCH ? l.batch : 1), block(64 * WGM * WGN);
     const bool akc = p.oa == kRow, bkc = p.ob == kCol;
     const int va = l.vec_a, vb = l.vec_b, g = l.group_m;
     if (akc && bkc)
-        hipLaunchKernelGGL((k_f32_mfma<BM, BN, BK, WGM, WGN, PF, PAD, true, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb);
+        hipLaunchKernelGGL((k_f32_mfma<BM, BN, BK, WGM, WGN, PF, PAD, true, true, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb);
     else if (akc)
-        hipLaunchKernelGGL((k_f32_mfma<BM, BN, BK, WGM, WGN, PF, PAD, true, false>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb);
+        hipLaunchKernelGGL((k_f32_mfma<BM, BN, BK, WGM, WGN, PF, PAD, true, false, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb);
     else if (bkc)
-        hipLaunchKernelGGL((k_f32_mfma<BM, BN, BK, WGM, WGN, PF, PAD, false, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb);
+        hipLaunchKernelGGL((k_f32_mfma<BM, BN, BK, WGM, WGN, PF, PAD, false, true, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb);
     else
-        hipLaunchKernelGGL((k_f32_mfma<BM, BN, BK, WGM, WGN, PF, PAD, false, false>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb);
+        hipLaunchKernelGGL((k_f32_mfma<BM, BN, BK, WGM, WGN, PF, PAD, false, false, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, g, va, vb);
     return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, bool PF, int PAD = 28>
+hipError_t launch_any(const Problem& p, const Launch& l) {
+    if (l.batch > 1) return launch_cfg<BM, BN, BK, WGM, WGN, PF, PAD, true>(batch_arg(p, l, 4), l);
+    return launch_cfg<BM, BN, BK, WGM, WGN, PF, PAD, false>(p, l);
 }
 
 }  // namespace
 
 hipError_t launch_f32_mfma(const Problem& p, const Launch& l, int bm) {
-    if (bm == 64) return launch_cfg<64, 64, 16, 2, 2, false>(p, l);
-    return launch_cfg<128, 128, 16, 2, 2, false>(p, l);
+    if (bm == 64) return launch_any<64, 64, 16, 2, 2, false>(p, l);
+    return launch_any<128, 128, 16, 2, 2, false>(p, l);
 }
 
 }  // namespace gemm

@@ -7,7 +7,8 @@
 namespace gemm {
 namespace {
 
-__global__ __launch_bounds__(256) void k_zero_c(float* C, int M, int N, int64_t ldc) {
+__global__ __launch_bounds__(256) void k_zero_c(float* C, int M, int N, int64_t ldc, int64_t sc) {
+    C += blockIdx.y * sc;     // entry of a strided batch (0 for one problem)
     const int64_t total = (int64_t)M * N;
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
          e += (int64_t)gridDim.x * blockDim.x) {
@@ -22,7 +23,9 @@ hipError_t launch_zero_c(const Problem& p, const Launch& l) {
     const int64_t total = (int64_t)p.M * p.N;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(k_zero_c, dim3((unsigned)blocks), dim3(256), 0, l.stream, p.C, p.M, p.N, p.ldc);
+    if (l.batch > 1 && blocks > 64) blocks = 64;     // the batch fills the grid along y
+    hipLaunchKernelGGL(k_zero_c, dim3((unsigned)blocks, (unsigned)l.batch), dim3(256), 0, l.stream, p.C, p.M, p.N,
+                       p.ldc, l.batch > 1 ? l.sc : (int64_t)0);
     return hipGetLastError();
 }
 

@@ -127,9 +127,10 @@ struct F32 {
 // lane's 16-byte load along N holds one k of 4 consecutive columns 4 c .. 4 c + 3, i.e. the
 // B operand of 4 matrix instructions: block q's column c is column n0 + 4 c + q of C, and
 // the epilogue writes the 4 columns of a lane with one 16-byte store.
-template <typename D, int FM, int FN, int WAVES, bool B_KC>
+template <typename D, int FM, int FN, int WAVES, bool B_KC, bool BATCH = false>
 __global__ __launch_bounds__(64 * WAVES)
-void k_skinny(Problem p, int vec_a, int vec_b, int vec_c, int bbuf, int kslice, float* part) {
+void k_skinny(KArg<BATCH> p, int vec_a, int vec_b, int vec_c, int bbuf, int kslice, float* part) {
+    if constexpr (BATCH) p.select(blockIdx.z);
     using E = typename D::Elem;
     using Frag = typename D::Frag;
     constexpr bool RC4 = !B_KC && FN == 4;     // row-major FP32 B read 16 bytes along N
@@ -304,18 +305,18 @@ template <typename D> int batch_k(int fm, int fn) {
     return chunk * D::KSTEP;
 }
 
-template <typename D, int FN, int WAVES, bool B_KC>
-hipError_t launch_d(const Problem& p, const Launch& l, int fm, int kslice, int slices, float* part) {
+template <typename D, int FN, int WAVES, bool B_KC, bool BATCH>
+hipError_t launch_d(const KArg<BATCH>& p, const Launch& l, int fm, int kslice, int slices, float* part) {
     const int slabs = (p.N + 16 * FN - 1) / (16 * FN), rblocks = (p.M + 16 * fm - 1) / (16 * fm);
-    const dim3 grid((unsigned)(slabs * rblocks), (unsigned)slices), block(64 * WAVES);
+    const dim3 grid((unsigned)(slabs * rblocks), (unsigned)slices, BATCH ? l.batch : 1), block(64 * WAVES);
     const int va = l.vec_a, vb = l.vec_b, vc = l.vec_c;
     // buffer offsets of a row-major B (rows up to K, plus 3 rows of one k-step's lane
     // spread) must fit in 31 bits
     const int bb = !B_KC && (int64_t)(p.K + 4) * p.ldb * 4 + (int64_t)p.N * 4 < ((int64_t)1 << 31);
-    if (fm == 1) hipLaunchKernelGGL((k_skinny<D, 1, FN, WAVES, B_KC>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part);
-    else if (fm == 2) hipLaunchKernelGGL((k_skinny<D, 2, FN, WAVES, B_KC>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part);
-    else if (fm == 3) hipLaunchKernelGGL((k_skinny<D, 3, FN, WAVES, B_KC>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part);
-    else hipLaunchKernelGGL((k_skinny<D, 4, FN, WAVES, B_KC>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part);
+    if (fm == 1) hipLaunchKernelGGL((k_skinny<D, 1, FN, WAVES, B_KC, BATCH>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part);
+    else if (fm == 2) hipLaunchKernelGGL((k_skinny<D, 2, FN, WAVES, B_KC, BATCH>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part);
+    else if (fm == 3) hipLaunchKernelGGL((k_skinny<D, 3, FN, WAVES, B_KC, BATCH>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part);
+    else hipLaunchKernelGGL((k_skinny<D, 4, FN, WAVES, B_KC, BATCH>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part);
     return hipGetLastError();
 }
 
@@ -401,26 +402,36 @@ SkinnySplit skinny_split(const Problem& p, bool bf16, int cus) {
     return sp;
 }
 
+namespace {
+// The kernel instance for input type, column blocks and B's order.
+template <bool BATCH>
+hipError_t launch_e(const KArg<BATCH>& p, const Launch& l, int et, int fn, int fm, int kslice, int slices,
+                    float* out) {
+    constexpr int W = kSkinnyWaves;
+    if (fn == 4) {
+        if (et == kElemBf16) return launch_d<Bf16, 4, W, true, BATCH>(p, l, fm, kslice, slices, out);
+        if (et == kElemF16) return launch_d<F16, 4, W, true, BATCH>(p, l, fm, kslice, slices, out);
+        if (p.ob == kCol) return launch_d<F32, 4, W, true, BATCH>(p, l, fm, kslice, slices, out);
+        return launch_d<F32, 4, W, false, BATCH>(p, l, fm, kslice, slices, out);
+    }
+    if (et == kElemBf16) return launch_d<Bf16, 1, W, true, BATCH>(p, l, fm, kslice, slices, out);
+    if (et == kElemF16) return launch_d<F16, 1, W, true, BATCH>(p, l, fm, kslice, slices, out);
+    if (p.ob == kCol) return launch_d<F32, 1, W, true, BATCH>(p, l, fm, kslice, slices, out);
+    return launch_d<F32, 1, W, false, BATCH>(p, l, fm, kslice, slices, out);
+}
+}  // namespace
+
 hipError_t launch_skinny(const Problem& p, const Launch& l, int et, int fn, int fm, const SkinnySplit* sp,
                          float* part) {
-    constexpr int W = kSkinnyWaves;
     if (fm < 1 || fm > 4) return hipErrorInvalidValue;
     const bool split = sp != nullptr && sp->slices > 1 && part != nullptr;
     const int kslice = split ? sp->kslice : p.K, slices = split ? sp->slices : 1;
     float* out = split ? part : nullptr;
-    hipError_t err;
     if (et != kElemF32 && et != kElemBf16 && et != kElemF16) return hipErrorInvalidValue;
-    if (fn == 4) {
-        if (et == kElemBf16) err = launch_d<Bf16, 4, W, true>(p, l, fm, kslice, slices, out);
-        else if (et == kElemF16) err = launch_d<F16, 4, W, true>(p, l, fm, kslice, slices, out);
-        else if (p.ob == kCol) err = launch_d<F32, 4, W, true>(p, l, fm, kslice, slices, out);
-        else err = launch_d<F32, 4, W, false>(p, l, fm, kslice, slices, out);
-    } else {
-        if (et == kElemBf16) err = launch_d<Bf16, 1, W, true>(p, l, fm, kslice, slices, out);
-        else if (et == kElemF16) err = launch_d<F16, 1, W, true>(p, l, fm, kslice, slices, out);
-        else if (p.ob == kCol) err = launch_d<F32, 1, W, true>(p, l, fm, kslice, slices, out);
-        else err = launch_d<F32, 1, W, false>(p, l, fm, kslice, slices, out);
-    }
+    if (split && l.batch > 1) return hipErrorInvalidValue;     // one workspace holds one entry's slices
+    const hipError_t err = l.batch > 1
+        ? launch_e<true>(batch_arg(p, l, et == kElemF32 ? 4 : 2), l, et, fn, fm, kslice, slices, out)
+        : launch_e<false>(p, l, et, fn, fm, kslice, slices, out);
     if (err != hipSuccess || !split) return err;
     const int64_t threads = (int64_t)p.M * ((p.N + 3) / 4);
     const int vec = l.vec_c && (p.N & 3) == 0;

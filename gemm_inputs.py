@@ -36,11 +36,13 @@ class Workload:
     order_a: int = ROW_MAJOR
     order_b: int = ROW_MAJOR
     order_c: int = ROW_MAJOR
-    dist: str = "uniform"    # "uniform" -> U[-1,1]; "llm" -> A~N(0,1), B~N(0,0.02)
+    dist: str = "uniform"    # "uniform" -> U[-1,1]; "llm" -> A~N(0,1), B~N(0,0.02); see draw()
+    batch: int = 1           # entries of a strided batch (1: one problem)
+    layout: tuple = ()       # batched: (("lda", v), ("sa", v), ...) for make_batched_problem
 
     @property
     def flops(self) -> int:
-        return 2 * self.M * self.N * self.K
+        return 2 * self.M * self.N * self.K * self.batch
 
 
 # The workloads the pages' measurements are about (all synthetic).
@@ -63,6 +65,15 @@ WORKLOADS = {
         # few columns of C and a long K: too few output blocks for the CUs (split-K's case)
         Workload("fewcols16x1024x16384_f32", 6, 16, 1024, 16384, "f32"),
         Workload("fewcols16x1024x16384_bf16", 6, 16, 1024, 16384, "bf16", ROW_MAJOR, COL_MAJOR),
+        # LLaMA-2-7B attention at 2K tokens, per head (32 heads of 128): the scores Q.K^T and the
+        # scores times V as strided batches.  Q, K, V and the output are [tokens, heads, 128]
+        # (leading dimension 4096, stride 128 per head); the scores are [heads, 2048, 2048].
+        Workload("attn_scores_32x2048x2048x128_bf16", 7, 2048, 2048, 128, "bf16", ROW_MAJOR, COL_MAJOR,
+                 ROW_MAJOR, "act", 32, (("lda", 4096), ("sa", 128), ("ldb", 4096), ("sb", 128),
+                                        ("ldc", 2048), ("sc", 2048 * 2048))),
+        Workload("attn_pv_32x2048x128x2048_bf16", 7, 2048, 128, 2048, "bf16", ROW_MAJOR, ROW_MAJOR,
+                 ROW_MAJOR, "probs", 32, (("lda", 2048), ("sa", 2048 * 2048), ("ldb", 4096), ("sb", 128),
+                                         ("ldc", 4096), ("sc", 128))),
     ]
 }
 
@@ -81,6 +92,10 @@ def draw(rng: np.random.Generator, rows: int, cols: int, dist: str, operand: int
         x = rng.standard_normal((rows, cols)) * sigma
     elif dist == "unit":          # [0, 1): the teaching module's lab inputs
         x = rng.uniform(0.0, 1.0, (rows, cols))
+    elif dist == "act":           # activations on both sides (attention's Q and K): N(0, 1)
+        x = rng.standard_normal((rows, cols))
+    elif dist == "probs":         # A: attention probabilities, U[0, 2/cols) (rows sum to ~1); B ~ N(0, 1)
+        x = rng.uniform(0.0, 2.0 / cols, (rows, cols)) if operand == 0 else rng.standard_normal((rows, cols))
     else:
         raise ValueError(f"unknown distribution {dist!r}")
     return x.astype(np.float32)
@@ -206,9 +221,135 @@ def make_problem(M: int, N: int, K: int, dtype: str = "f32", order_a: int = ROW_
                    A, lda, B, ldb, max(1, ldc0) + pad_c)
 
 
-def workload_problem(name: str) -> Problem:
+@dataclass
+class BatchedProblem:
+    """A seeded strided batch: batch entries of one M x N x K shape in shared flat buffers.
+
+    Entry z's element (r, c) of an operand sits at z*stride + offset(r, c) (offset by the
+    operand's order and leading dimension).  A stride of 0 for A or B means one matrix for
+    every entry (its logical array repeats).  Slots no entry uses hold the sentinel.
+    """
+    batch: int
+    M: int
+    N: int
+    K: int
+    dtype: str
+    order_a: int
+    order_b: int
+    order_c: int
+    A_logical: np.ndarray    # (batch, M, K) in the input encoding
+    B_logical: np.ndarray    # (batch, K, N)
+    A: np.ndarray
+    lda: int
+    sa: int
+    B: np.ndarray
+    ldb: int
+    sb: int
+    ldc: int
+    sc: int
+
+    def c_size(self) -> int:
+        return self.sc * (self.batch - 1) + _whole(self.M, self.N, self.ldc, self.order_c) \
+            if self.batch and self.M and self.N else 1
+
+    def c_view(self, flat: np.ndarray) -> np.ndarray:
+        """(batch, M, N) strided view of the entries in a C buffer."""
+        return entry_view(flat, self.batch, self.M, self.N, self.ldc, self.sc, self.order_c)
+
+    def c_untouched(self, flat: np.ndarray) -> np.ndarray:
+        """Values of the C slots that belong to no entry."""
+        mask = np.ones(flat.size, dtype=bool)
+        entry_view(mask, self.batch, self.M, self.N, self.ldc, self.sc, self.order_c)[...] = False
+        return flat[mask]
+
+
+def _span(R: int, C: int, ld: int, order: int) -> int:
+    return (R - 1) * ld + C if order == ROW_MAJOR else (C - 1) * ld + R
+
+
+def _whole(R: int, C: int, ld: int, order: int) -> int:
+    """Elements of an R x C matrix stored in whole rows (columns) of ld, as lay_out stores one."""
+    return R * ld if order == ROW_MAJOR else C * ld
+
+
+def entries_disjoint(batch: int, R: int, C: int, ld: int, stride: int, order: int) -> bool:
+    """Entries one after another (stride >= span) or side by side within ld."""
+    if batch <= 1:
+        return True
+    inner = C if order == ROW_MAJOR else R
+    return stride >= _span(R, C, ld, order) or (stride >= inner and (batch - 1) * stride + inner <= ld)
+
+
+def entry_view(flat: np.ndarray, batch: int, R: int, C: int, ld: int, stride: int, order: int) -> np.ndarray:
+    """(batch, R, C) view of flat: entry z's element (r, c) at z*stride + offset(r, c)."""
+    if batch == 0 or R == 0 or C == 0:
+        return np.zeros((batch, R, C), dtype=flat.dtype)
+    assert flat.size >= stride * (batch - 1) + _span(R, C, ld, order)
+    e = flat.itemsize
+    strides = (stride * e, ld * e, e) if order == ROW_MAJOR else (stride * e, e, ld * e)
+    return np.lib.stride_tricks.as_strided(flat, shape=(batch, R, C), strides=strides)
+
+
+def _place(logical: np.ndarray, order: int, ld: int, stride: int) -> np.ndarray:
+    batch, R, C = logical.shape
+    if batch == 0 or R == 0 or C == 0:
+        return np.zeros(1, dtype=logical.dtype)
+    assert stride == 0 or entries_disjoint(batch, R, C, ld, stride, order), "entries of this layout overlap"
+    # the last entry ends with whole rows (columns) of ld, as a single laid-out matrix does
+    flat = np.full(stride * (batch - 1) + _whole(R, C, ld, order), _sentinel(logical.dtype), dtype=logical.dtype)
+    entry_view(flat, batch, R, C, ld, stride, order)[...] = logical
+    return flat
+
+
+def make_batched_problem(batch: int, M: int, N: int, K: int, dtype: str = "f32", order_a: int = ROW_MAJOR,
+                         order_b: int = ROW_MAJOR, order_c: int = ROW_MAJOR, lda: int | None = None,
+                         sa: int | None = None, ldb: int | None = None, sb: int | None = None,
+                         ldc: int | None = None, sc: int | None = None, dist: str = "uniform",
+                         wid: int = 0, A_logical: np.ndarray | None = None,
+                         B_logical: np.ndarray | None = None) -> BatchedProblem:
+    """Draw (or take, as fp32 (batch, rows, cols) arrays) every entry's operands and lay them out.
+
+    Leading dimensions default to tight, strides to one tight entry after another.  Entry z
+    draws from its own seeded stream; with stride 0 entry 0's matrix serves all.
+    """
+    lda = lda if lda is not None else max(1, K if order_a == ROW_MAJOR else M)
+    ldb = ldb if ldb is not None else max(1, N if order_b == ROW_MAJOR else K)
+    ldc = ldc if ldc is not None else max(1, N if order_c == ROW_MAJOR else M)
+    sa = sa if sa is not None else _span(M, K, lda, order_a) if M and K else 0
+    sb = sb if sb is not None else _span(K, N, ldb, order_b) if K and N else 0
+    sc = sc if sc is not None else _span(M, N, ldc, order_c) if M and N else 0
+
+    def operand(given, rows, cols, operand_id, stride):
+        if given is not None:
+            x = np.asarray(given, dtype=np.float32).reshape(batch, rows, cols)
+        else:
+            n = batch if stride else min(batch, 1)
+            x = np.stack([draw(rng_for(wid, M, N, K, operand_id, z + 1), rows, cols, dist, operand_id)
+                          for z in range(n)]) if n else np.zeros((0, rows, cols), np.float32)
+            if not stride and batch:
+                x = np.repeat(x, batch, axis=0)
+        if dtype == "bf16":
+            return f32_to_bf16_bits(x.reshape(-1)).reshape(x.shape)
+        if dtype == "f16":
+            return x.astype(np.float16)
+        if dtype != "f32":
+            raise ValueError(dtype)
+        return x
+
+    A_log = operand(A_logical, M, K, 0, sa)
+    B_log = operand(B_logical, K, N, 1, sb)
+    return BatchedProblem(batch, M, N, K, dtype, order_a, order_b, order_c, A_log, B_log,
+                          _place(A_log, order_a, lda, sa), lda, sa, _place(B_log, order_b, ldb, sb), ldb, sb,
+                          ldc, sc)
+
+
+def workload_problem(name: str, seed_offset: int = 0):
+    """The named workload's seeded inputs: a Problem, or a BatchedProblem for a batch."""
     w = WORKLOADS[name]
-    return make_problem(w.M, w.N, w.K, w.dtype, w.order_a, w.order_b, w.order_c, w.dist, w.wid)
+    if w.batch > 1:
+        return make_batched_problem(w.batch, w.M, w.N, w.K, w.dtype, w.order_a, w.order_b, w.order_c,
+                                    dist=w.dist, wid=w.wid + seed_offset, **dict(w.layout))
+    return make_problem(w.M, w.N, w.K, w.dtype, w.order_a, w.order_b, w.order_c, w.dist, w.wid + seed_offset)
 
 
 def unpack_c(flat: np.ndarray, M: int, N: int, ldc: int, order_c: int) -> np.ndarray:

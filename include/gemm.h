@@ -240,6 +240,44 @@ gemm_status_t gemm_f16_f32acc_ws(int64_t M, int64_t N, int64_t K,
                                  float *C, int64_t ldc, gemm_order_t order_c,
                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Strided batched GEMM: C_z = A_z . B_z for z = 0 .. batch-1, every entry M x N x K with the
+ * orders and leading dimensions of the plain calls.  Attention runs one such product per head:
+ * the scores Q.K^T and the scores times V ("A06 - Tiled Matrix Multiply (GEMM)", sections
+ * "2. First Principles" and "7. Real-World Use Cases").
+ *
+ * Entry z reads A + z*stride_a and B + z*stride_b and writes C + z*stride_c; strides count
+ * elements (of the input type for A and B, floats for C).  stride_a or stride_b 0 uses one
+ * operand for every entry.  Heads interleaved in one row, as in a [tokens, heads, head_dim]
+ * tensor, are leading dimension heads*head_dim with stride head_dim.  Each entry is computed as
+ * the plain call of the same type computes it (same kernels, same accuracy), all of them on
+ * `stream` in one launch per kernel (65535 entries at most per launch; more take several).
+ * No workspace is used and nothing is allocated.
+ *
+ * Errors: as the plain calls, plus GEMM_ERR_INVALID_VALUE for batch < 0, a negative stride,
+ * entry offsets beyond int64 bytes, or entries of C that may overlap: they must either follow
+ * one another (stride_c at least one entry's span, (rows-1)*ldc + columns in C's own order) or
+ * sit side by side within each row (stride_c >= the entry's row length, all batch entries
+ * inside ldc).  batch == 0, M == 0 or N == 0: nothing happens. */
+gemm_status_t gemm_f32_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
+                                       const float *A, int64_t lda, int64_t stride_a, gemm_order_t order_a,
+                                       const float *B, int64_t ldb, int64_t stride_b, gemm_order_t order_b,
+                                       float *C, int64_t ldc, int64_t stride_c, gemm_order_t order_c,
+                                       hipStream_t stream);
+gemm_status_t gemm_bf16_f32acc_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
+                                               const uint16_t *A, int64_t lda, int64_t stride_a,
+                                               gemm_order_t order_a,
+                                               const uint16_t *B, int64_t ldb, int64_t stride_b,
+                                               gemm_order_t order_b,
+                                               float *C, int64_t ldc, int64_t stride_c, gemm_order_t order_c,
+                                               hipStream_t stream);
+gemm_status_t gemm_f16_f32acc_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
+                                              const uint16_t *A, int64_t lda, int64_t stride_a,
+                                              gemm_order_t order_a,
+                                              const uint16_t *B, int64_t ldb, int64_t stride_b,
+                                              gemm_order_t order_b,
+                                              float *C, int64_t ldc, int64_t stride_c, gemm_order_t order_c,
+                                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

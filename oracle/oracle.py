@@ -111,6 +111,34 @@ def gemm_sampled(M, N, K, A, lda, order_a, B, ldb, order_b, rows, cols, lib=None
     return C, D
 
 
+def gemm_strided_batched(batch, M, N, K, A, lda, stride_a, order_a, B, ldb, stride_b, order_b, lib=None):
+    """A strided batch, entry by entry: (C, D) as batch x M x N float64 arrays.
+
+    Entry z is the full product (gemm above) of the M x K matrix whose element (0, 0) sits at
+    position z*stride_a of the flat buffer A and the K x N matrix at z*stride_b of B, each
+    with its own leading dimension and order.  This is what a strided batched GEMM means:
+    one independent product per entry ("A06 - Tiled Matrix Multiply (GEMM)", section "2.
+    First Principles", the per-head attention products).
+    """
+    A = np.ascontiguousarray(A).reshape(-1)
+    B = np.ascontiguousarray(B).reshape(-1)
+    C = np.zeros((batch, M, N), dtype=np.float64)
+    D = np.zeros((batch, M, N), dtype=np.float64)
+    for z in range(batch):
+        a = A[z * stride_a:]
+        b = B[z * stride_b:]
+        if M and N and K:
+            assert a.size >= _extent(M, K, lda, order_a) and b.size >= _extent(K, N, ldb, order_b), \
+                "a batch entry runs past the end of its buffer"
+        C[z], D[z] = gemm(M, N, K, a, lda, order_a, b, ldb, order_b, lib=lib)
+    return C, D
+
+
+def _extent(rows, cols, ld, order):
+    """Elements a rows x cols matrix spans from its first element."""
+    return (rows - 1) * ld + cols if order == 0 else (cols - 1) * ld + rows
+
+
 def normalised_error(C_test: np.ndarray, C_ref: np.ndarray, D: np.ndarray) -> float:
     """max over elements of |C_test - C_ref| / D.
 

@@ -78,3 +78,30 @@ def check(p: gi.Problem, algo=g.Algo.AUTO, key=None, exact=False):
     err = oracle.normalised_error(C, ref, D)
     assert err <= TOL[p.dtype], f"normalised error {err:.3e} > {TOL[p.dtype]:.0e}"
     return err
+
+
+def run_batched(p: gi.BatchedProblem):
+    """C buffer (flat float32 numpy, NaN-filled before the call) after one strided batched call."""
+    import torch
+    A, B = to_device(p.A), to_device(p.B)
+    C = torch.full((p.c_size(),), float("nan"), dtype=torch.float32, device="cuda")
+    fn = {"f32": g.gemm_f32_strided_batched, "bf16": g.gemm_bf16_f32acc_strided_batched,
+          "f16": g.gemm_f16_f32acc_strided_batched}[p.dtype]
+    print(f"[gpu] batched {p.dtype} batch={p.batch} M={p.M} N={p.N} K={p.K} orders=({p.order_a},{p.order_b},"
+          f"{p.order_c}) ld=({p.lda},{p.ldb},{p.ldc}) strides=({p.sa},{p.sb},{p.sc})", flush=True)
+    fn(p.batch, p.M, p.N, p.K, A.data_ptr(), p.lda, p.sa, p.order_a, B.data_ptr(), p.ldb, p.sb, p.order_b,
+       C.data_ptr(), p.ldc, p.sc, p.order_c, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return C.cpu().numpy()
+
+
+def check_batched(p: gi.BatchedProblem):
+    """Run a strided batch and compare every entry element by element with the oracle."""
+    flat = run_batched(p)
+    assert np.all(np.isnan(p.c_untouched(flat))), "C written outside the entries"
+    got = p.c_view(flat)
+    ref, D = oracle.gemm_strided_batched(p.batch, p.M, p.N, p.K, p.A, p.lda, p.sa, p.order_a, p.B, p.ldb, p.sb,
+                                         p.order_b)
+    err = oracle.normalised_error(got, ref, D)
+    assert err <= TOL[p.dtype], f"normalised error {err:.3e} > {TOL[p.dtype]:.0e}"
+    return err

@@ -247,9 +247,58 @@ def pin_sampled_matches_full(lib):
             assert np.array_equal(Cs, C[rows, cols]) and np.array_equal(Ds, D[rows, cols])
 
 
+def _batched(lib, p: gi.BatchedProblem):
+    return oracle.gemm_strided_batched(p.batch, p.M, p.N, p.K, p.A, p.lda, p.sa, p.order_a, p.B, p.ldb,
+                                       p.sb, p.order_b, lib=lib)
+
+
+# layouts of a strided batch: interleaved rows ([rows, entries, cols]), stacked with gaps,
+# and one operand shared by every entry (stride 0)
+BATCH_LAYOUTS = [
+    dict(lda=3 * 4, sa=4, ldb=5, sb=4 * 5 + 2),                  # A interleaved, B stacked + gap
+    dict(order_a=COL_MAJOR, lda=2, sa=2 * 4 + 1, order_b=COL_MAJOR, ldb=3 * 4, sb=4),
+    dict(sa=0, ldb=5 + 1),                                       # one A for every entry
+    dict(order_a=COL_MAJOR, sb=0, order_b=COL_MAJOR),            # one B for every entry
+]
+
+
+def pin_batched_bruteforce(lib):
+    """Each entry of a strided batch equals the exact rational product of that entry's own
+    logical matrices (the generator's arrays, independent of the layout), for interleaved,
+    stacked and shared operands."""
+    for dtype in DTYPES:
+        for lay in BATCH_LAYOUTS:
+            p = gi.make_batched_problem(3, 2, 5, 4, dtype, wid=111, **lay)
+            C, D = _batched(lib, p)
+            a = gi._to_f32(p.A_logical, dtype)
+            b = gi._to_f32(p.B_logical, dtype)
+            assert C.shape == (3, 2, 5)
+            for z in range(3):
+                for i in range(2):
+                    for j in range(5):
+                        exact = sum((Fraction(float(a[z, i, k])) * Fraction(float(b[z, k, j])) for k in range(4)),
+                                    Fraction(0))
+                        assert abs(Fraction(C[z, i, j]) - exact) <= Fraction(3, 2 ** 53) * Fraction(D[z, i, j])
+
+
+def pin_batched_scaled_identity(lib):
+    """A_z = (z + 1) I gives C_z = (z + 1) B_z exactly, entry by entry; an entry that read
+    another entry's A or B, or the wrong stride, shows up as a wrong scale or matrix."""
+    batch, n, N = 5, 6, 7
+    eye = np.stack([(z + 1) * np.eye(n, dtype=np.float32) for z in range(batch)])
+    rng = np.random.default_rng(23)
+    Bl = _int_matrix(rng, batch * n, N).reshape(batch, n, N)
+    for dtype in DTYPES:
+        for lay in (dict(), dict(lda=batch * n, sa=n, ldb=N + 3, sb=(N + 3) * n + 1)):
+            p = gi.make_batched_problem(batch, n, N, n, dtype, A_logical=eye, B_logical=Bl, **lay)
+            C, _ = _batched(lib, p)
+            for z in range(batch):
+                assert np.array_equal(C[z], (z + 1) * Bl[z].astype(np.float64))
+
+
 ALL_PINS = [
     pin_fraction_bruteforce, pin_numpy_crosscheck, pin_ones, pin_ones_column_sums,
     pin_identity, pin_permutation, pin_small_integers, pin_transpose, pin_k_split,
     pin_mac_count, pin_degenerate, pin_nonnegative_scale, pin_bf16_widening,
-    pin_f16_widening, pin_sampled_matches_full,
+    pin_f16_widening, pin_sampled_matches_full, pin_batched_bruteforce, pin_batched_scaled_identity,
 ]

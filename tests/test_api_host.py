@@ -265,3 +265,52 @@ def test_f16_plans_follow_bf16(shape, expected):
     assert g.gemm_plan("f16", *shape, R, C_, R) == expected
     bf = g.gemm_plan("bf16", *shape, R, C_, R)
     assert bf[1:] == expected[1:] and bf[0] == expected[0].replace("f16_", "bf16_")
+
+
+# --- strided batched calls: validation happens before any device call --------------------
+BATCHED = {"f32": g.gemm_f32_strided_batched, "bf16": g.gemm_bf16_f32acc_strided_batched,
+           "f16": g.gemm_f16_f32acc_strided_batched}
+
+
+def bargs(batch=3, M=8, N=8, K=8, A=FAKE, lda=8, sa=64, oa=R, B=FAKE, ldb=8, sb=64, ob=R, C=FAKE, ldc=8,
+          sc=64, oc=R):
+    return (batch, M, N, K, A, lda, sa, oa, B, ldb, sb, ob, C, ldc, sc, oc, 0)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(batch=-1), dict(sa=-1), dict(sb=-8), dict(sc=-64), dict(M=-1), dict(ldc=7), dict(A=0),
+    dict(C=FAKE + 2), dict(oc=3),
+    dict(sc=63),                                   # stacked entries one element too close
+    dict(sc=0),                                    # every entry on the same C
+    dict(ldc=24, sc=8),                            # side by side needs 3 x 8 <= 24 ... and 8 >= N
+    dict(ldc=23, sc=8, N=8),                       # third entry would run past ldc: overlaps row 1
+    dict(ldc=24, sc=7),                            # side by side closer than N
+    dict(oc=C_, M=4, N=8, ldc=4, sc=31),           # column-major C: entry span (8-1)*4 + 4 = 32
+    dict(batch=2**40, sa=2**40),                   # entry offsets beyond int64 bytes
+], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_batched_invalid_arguments(dtype, bad):
+    if bad == dict(ldc=24, sc=8):
+        pytest.skip("3 entries of 8 columns fill ldc 24 exactly: a valid layout")
+    assert _status(BATCHED[dtype], *bargs(**bad)) == INVALID
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("shape", [dict(batch=0), dict(M=0), dict(N=0)])
+def test_batched_empty_is_ok_without_launch(dtype, shape):
+    assert _status(BATCHED[dtype], *bargs(**shape)) == g.Status.OK
+    assert g.gemm_last_kernel() == "none"
+
+
+@pytest.mark.skipif(gpu_available(), reason="checks the no-GPU path")
+@pytest.mark.parametrize("layout", [
+    dict(sc=64),                          # stacked, dense
+    dict(sc=100),                         # stacked with a gap
+    dict(ldc=24, sc=8),                   # side by side: [rows, entries, cols]
+    dict(ldc=32, sc=10),                  # side by side with gaps
+    dict(sa=0, sb=0),                     # one A and one B for every entry
+    dict(oc=C_, M=4, N=8, ldc=4, sc=32),  # column-major C stacked
+    dict(batch=1, sc=0),                  # one entry: no stride matters
+], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_batched_valid_layouts_reach_the_device_check(layout):
+    assert _status(BATCHED["f32"], *bargs(**layout)) == g.Status.ERR_UNSUPPORTED_DEVICE

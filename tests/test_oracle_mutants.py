@@ -74,3 +74,32 @@ for pin in oracle_pins.ALL_PINS:
         failed.append(pin.__name__)
 print(json.dumps(failed))
 """
+
+
+# The strided batch is a loop over the pinned product in oracle.py; each plausible mistake in
+# that loop must fail one of the batched pins.
+ORACLE_PY = os.path.join(os.path.dirname(oracle.library_path()), "oracle.py")
+PY_MUTANTS = {
+    "a_takes_b_stride": ("a = A[z * stride_a:]", "a = A[z * stride_b:]"),
+    "b_takes_a_stride": ("b = B[z * stride_b:]", "b = B[z * stride_a:]"),
+    "every_entry_reads_entry_0": ("a = A[z * stride_a:]", "a = A[0:]"),
+    "entries_shifted": ("C[z], D[z] = gemm(", "C[(z + 1) % batch], D[(z + 1) % batch] = gemm("),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_batched_mutant_fails_a_pin(name, monkeypatch):
+    before, after = PY_MUTANTS[name]
+    src = open(ORACLE_PY).read()
+    assert src.count(before) == 1, f"mutation site for {name} not found"
+    ns = {"__name__": "oracle_mutant", "__file__": ORACLE_PY}
+    exec(compile(src.replace(before, after), "oracle_mutant.py", "exec"), ns)
+    lib = oracle.oracle.load()
+    monkeypatch.setattr(oracle, "gemm_strided_batched", ns["gemm_strided_batched"])
+    failed = []
+    for pin in (oracle_pins.pin_batched_bruteforce, oracle_pins.pin_batched_scaled_identity):
+        try:
+            pin(lib)
+        except Exception:
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every batched pin"

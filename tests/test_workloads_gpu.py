@@ -21,7 +21,7 @@ def sample_indices(M, N, seed):
     return np.concatenate(r), np.concatenate(c)
 
 
-@pytest.mark.parametrize("name", list(gi.WORKLOADS))
+@pytest.mark.parametrize("name", [n for n, w in gi.WORKLOADS.items() if w.batch == 1])
 def test_workload_full_size_sampled(name):
     p = gi.workload_problem(name)
     flat = run(p)
@@ -64,3 +64,22 @@ def test_workload_full_size_sampled_with_workspace(name):
     err = oracle.normalised_error(Cl[rows, cols], ref, D)
     print(f"{name} (workspace): normalised error {err:.3e} over {rows.size} sampled outputs")
     assert err <= TOL[p.dtype]
+
+
+@pytest.mark.parametrize("name", [n for n, w in gi.WORKLOADS.items() if w.batch > 1])
+def test_batched_workload_full_size_sampled(name):
+    """Strided batch at full size: sampled outputs of the first, second, a middle and the last
+    entry, each from the oracle on that entry's operands."""
+    from gpu_util import run_batched
+    p = gi.workload_problem(name)
+    flat = run_batched(p)
+    got = p.c_view(flat)
+    assert np.all(np.isfinite(got)), "every output written and finite"
+    assert np.all(np.isnan(p.c_untouched(flat)))
+    for z in sorted({0, 1, p.batch // 2, p.batch - 1}):
+        rows, cols = sample_indices(p.M, p.N, gi.WORKLOADS[name].wid + z)
+        ref, D = oracle.gemm_sampled(p.M, p.N, p.K, p.A[z * p.sa:], p.lda, p.order_a, p.B[z * p.sb:], p.ldb,
+                                     p.order_b, rows, cols)
+        err = oracle.normalised_error(got[z][rows, cols], ref, D)
+        print(f"{name} entry {z}: normalised error {err:.3e} over {rows.size} sampled outputs")
+        assert err <= TOL[p.dtype]

@@ -13,7 +13,8 @@ kernel against MI355X's published matrix-core peak for its dtype.
 
 `--workload` picks another single workload from gemm_inputs.WORKLOADS (then one step is
 that one GEMM, or one strided batched call for a batch workload such as attention's per-head
-products); `--algo` forces a kernel (gemm_f32_amd.Algo name); `--workspace` calls the
+products); `--algo` forces a kernel (gemm_f32_amd.Algo name); `--epilogue NAME` calls the fused-epilogue entry point (bias, activation, bf16 output) for a 16-bit
+workload; `--workspace` calls the
 workspace entry points (gemm_f32_ws / gemm_bf16_f32acc_ws, split-K across workgroups where
 the problem is too small to fill the device) with a workspace of the size the library asks
 for, allocated before the timed region.  Each GEMM's inputs
@@ -39,6 +40,9 @@ sys.path.insert(0, ROOT)
 METRIC = "GEMM TFLOP/s at 4096³ (FP32, BF16→FP32) and % of MI355X peak"
 DEFAULT = "square4096"
 DEFAULT_LEGS = ["square4096_f32", "square4096_bf16"]
+# fused epilogues for --epilogue: (alpha, beta, bias, activation, bf16 output)
+EPILOGUES = {"identity_f32": (1.0, 0.0, False, 0, False), "bias_gelu_bf16": (1.0, 0.0, True, 2, True),
+             "beta_bias_relu_f32": (1.0, 1.0, True, 1, False)}
 
 
 def parse():
@@ -55,6 +59,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target host time of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--epilogue", default=None, choices=sorted(EPILOGUES),
+                    help="run the fused-epilogue entry point (16-bit inputs, row-major A, column-major B)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 256 MiB device-to-device copy instead (the reference "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -122,7 +128,7 @@ def copy_calibration(args):
 class Leg:
     """One GEMM of the step with its resident device buffers."""
 
-    def __init__(self, name, algo, sets, workspace=False):
+    def __init__(self, name, algo, sets, workspace=False, epilogue=None):
         import torch
         import gemm_f32_amd as g
         import gemm_inputs as gi
@@ -157,6 +163,18 @@ class Leg:
         self.bytes = w.batch * (e * (w.M * w.K + w.K * w.N) + 4 * w.M * w.N)
         self.kernel = None
         self.ws, self.ws_bytes = None, 0
+        self.epi = None
+        if epilogue is not None:
+            if algo != "AUTO" or workspace or self.batched or w.dtype == "f32":
+                raise SystemExit("--epilogue runs the 16-bit fused entry point alone")
+            alpha, beta, has_bias, act, out16 = EPILOGUES[epilogue]
+            bias = torch.from_numpy(np.random.default_rng(1).uniform(-1, 1, w.N).astype(np.float32)).to("cuda")
+            self.epi = (alpha, beta, bias if has_bias else None, act, 1 if out16 else 0)
+            if out16:
+                self.C = torch.zeros(size, dtype=torch.int16, device="cuda")
+            else:
+                self.C.zero_()
+            self.fn_fused = {"bf16": g.gemm_bf16_f32acc_fused, "f16": g.gemm_f16_f32acc_fused}[w.dtype]
         if workspace:
             if algo != "AUTO":
                 raise SystemExit("--workspace runs the default kernel choice (--algo AUTO)")
@@ -172,6 +190,13 @@ class Leg:
             self.fn_batched(p.batch, p.M, p.N, p.K, self.A[s % len(self.A)].data_ptr(), p.lda, p.sa, p.order_a,
                             self.B[s % len(self.B)].data_ptr(), p.ldb, p.sb, p.order_b, self.C.data_ptr(), p.ldc,
                             p.sc, p.order_c, stream)
+            return
+        if self.epi is not None:
+            alpha, beta, bias, act, out = self.epi
+            self.fn_fused(p.M, p.N, p.K, self.A[s % len(self.A)].data_ptr(), p.lda, p.order_a,
+                          self.B[s % len(self.B)].data_ptr(), p.ldb, p.order_b, self.C.data_ptr(), p.ldc, p.order_c,
+                          alpha=alpha, beta=beta, bias=bias.data_ptr() if bias is not None else 0, activation=act,
+                          out_type=out, stream=stream)
             return
         if self.ws is not None:
             self.fn_ws(p.M, p.N, p.K, self.A[s % len(self.A)].data_ptr(), p.lda, p.order_a,
@@ -230,7 +255,7 @@ def main():
     from gemm_f32_amd import roofline as rl
 
     names = DEFAULT_LEGS if args.workload == DEFAULT else [args.workload]
-    legs = [Leg(n, args.algo, args.sets, args.workspace) for n in names]
+    legs = [Leg(n, args.algo, args.sets, args.workspace, args.epilogue) for n in names]
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
@@ -295,7 +320,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload if args.workload != DEFAULT else
                    "4096^3 FP32 GEMM + 4096^3 BF16->FP32 GEMM per step",
-                   "legs": leg_info, "algo": args.algo,
+                   "legs": leg_info, "algo": args.algo, "epilogue": args.epilogue,
                    "wall_s": round(wall, 3)},
         "roofline": roof,
     }

@@ -9,5 +9,6 @@ from .binding import (  # noqa: F401
     gemm_f32, gemm_f32_algo, gemm_last_hip_error, gemm_last_kernel, gemm_status_string,
     gemm_version, gemm_plan, gemm_workspace_size, gemm_f32_ws, gemm_bf16_f32acc_ws,
     gemm_f16_f32acc, gemm_f16_f32acc_algo, gemm_f16_f32acc_ws,
-    gemm_f32_strided_batched, gemm_bf16_f32acc_strided_batched, gemm_f16_f32acc_strided_batched, lib_handle, library_path, LibraryNotBuilt, matmul, operand_layout,
+    gemm_f32_strided_batched, gemm_bf16_f32acc_strided_batched, gemm_f16_f32acc_strided_batched,
+    gemm_bf16_f32acc_fused, gemm_f16_f32acc_fused, Act, Out, lib_handle, library_path, LibraryNotBuilt, matmul, operand_layout,
 )

@@ -99,7 +99,29 @@ def _load():
                  "gemm_f16_f32acc_strided_batched"):
         f = getattr(lib, name)
         f.argtypes, f.restype = batched, ci
+    for name in ("gemm_bf16_f32acc_fused", "gemm_f16_f32acc_fused"):
+        f = getattr(lib, name)
+        f.argtypes, f.restype = args[:-1] + [ctypes.POINTER(EpilogueStruct), vp], ci
     return lib
+
+
+class Act(enum.IntEnum):
+    """gemm_activation_t"""
+    NONE = 0
+    RELU = 1
+    GELU = 2
+
+
+class Out(enum.IntEnum):
+    """gemm_out_t"""
+    F32 = 0
+    BF16 = 1
+
+
+class EpilogueStruct(ctypes.Structure):
+    """gemm_epilogue_t"""
+    _fields_ = [("alpha", ctypes.c_float), ("beta", ctypes.c_float), ("bias", ctypes.c_void_p),
+                ("activation", ctypes.c_int), ("out_type", ctypes.c_int)]
 
 
 EXPORTED = ("gemm_f32", "gemm_bf16_f32acc", "gemm_f32_algo", "gemm_bf16_f32acc_algo",
@@ -107,7 +129,7 @@ EXPORTED = ("gemm_f32", "gemm_bf16_f32acc", "gemm_f32_algo", "gemm_bf16_f32acc_a
             "gemm_plan", "gemm_workspace_size", "gemm_f32_ws", "gemm_bf16_f32acc_ws",
             "gemm_f16_f32acc", "gemm_f16_f32acc_algo", "gemm_f16_f32acc_ws",
             "gemm_f32_strided_batched", "gemm_bf16_f32acc_strided_batched",
-            "gemm_f16_f32acc_strided_batched")
+            "gemm_f16_f32acc_strided_batched", "gemm_bf16_f32acc_fused", "gemm_f16_f32acc_fused")
 
 # dtype codes of gemm_plan / gemm_workspace_size
 DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2}
@@ -232,6 +254,28 @@ def gemm_f16_f32acc_strided_batched(batch, M, N, K, A, lda, stride_a, order_a, B
     _check(lib_handle().gemm_f16_f32acc_strided_batched(batch, M, N, K, A, lda, stride_a, order_a, B, ldb,
                                                         stride_b, order_b, C, ldc, stride_c, order_c, stream),
            "gemm_f16_f32acc_strided_batched")
+
+
+def _fused(name, M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, alpha, beta, bias, activation,
+           out_type, stream):
+    epi = EpilogueStruct(alpha, beta, bias or None, int(activation), int(out_type))
+    _check(getattr(lib_handle(), name)(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c,
+                                       ctypes.byref(epi), stream), name)
+
+
+def gemm_bf16_f32acc_fused(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, alpha=1.0, beta=0.0,
+                           bias=0, activation=Act.NONE, out_type=Out.F32, stream=0):
+    """C = act(alpha*A.B + beta*C + bias) with bf16 inputs; C float or bf16 bits per out_type;
+    bias a device pointer to N floats (0: none)."""
+    _fused("gemm_bf16_f32acc_fused", M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, alpha, beta,
+           bias, activation, out_type, stream)
+
+
+def gemm_f16_f32acc_fused(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, alpha=1.0, beta=0.0,
+                          bias=0, activation=Act.NONE, out_type=Out.F32, stream=0):
+    """gemm_bf16_f32acc_fused for IEEE fp16 inputs."""
+    _fused("gemm_f16_f32acc_fused", M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, alpha, beta,
+           bias, activation, out_type, stream)
 
 
 def operand_layout(t) -> tuple[int, int]:

@@ -49,7 +49,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 gemm_status_t validate(In in, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                        int oa, const void* B, int64_t ldb, int ob, const void* C, int64_t ldc,
-                       int oc) {
+                       int oc, uintptr_t c_align = 4) {
     if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_VALUE;
     if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return GEMM_ERR_INVALID_VALUE;
     for (int o : {oa, ob, oc})
@@ -61,7 +61,7 @@ gemm_status_t validate(In in, int64_t M, int64_t N, int64_t K, const void* A, in
     if (M > 0 && N > 0 && C == nullptr) return GEMM_ERR_INVALID_VALUE;
     if (M > 0 && N > 0 && K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_INVALID_VALUE;
     const uintptr_t e = in == In::F32 ? 4 : 2;
-    if (!aligned(A, e) || !aligned(B, e) || !aligned(C, 4)) return GEMM_ERR_INVALID_VALUE;
+    if (!aligned(A, e) || !aligned(B, e) || !aligned(C, c_align)) return GEMM_ERR_INVALID_VALUE;
     return GEMM_OK;
 }
 
@@ -550,10 +550,83 @@ gemm_status_t run_batched(In in, int64_t batch, int64_t M, int64_t N, int64_t K,
     return GEMM_OK;
 }
 
+// GEMM with the fused epilogue: 16-bit inputs on the direct-copy kernel, the whole of C in one
+// launch (tiles overhang both edges), or the epilogue of an empty sum for K == 0.
+gemm_status_t run_fused(In in, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, gemm_order_t oa,
+                        const uint16_t* B, int64_t ldb, gemm_order_t ob, void* C, int64_t ldc, gemm_order_t oc,
+                        const gemm_epilogue_t* epi, hipStream_t stream) {
+    if (epi == nullptr) return GEMM_ERR_INVALID_VALUE;
+    if (epi->activation != GEMM_ACT_NONE && epi->activation != GEMM_ACT_RELU && epi->activation != GEMM_ACT_GELU)
+        return GEMM_ERR_INVALID_VALUE;
+    if (epi->out_type != GEMM_OUT_F32 && epi->out_type != GEMM_OUT_BF16) return GEMM_ERR_INVALID_VALUE;
+    const bool out16 = epi->out_type == GEMM_OUT_BF16;
+    gemm_status_t st = validate(in, M, N, K, A, lda, oa, B, ldb, ob, C, ldc, oc, out16 ? 2 : 4);
+    if (st != GEMM_OK) return st;
+    if (epi->bias != nullptr && !aligned(epi->bias, 4)) return GEMM_ERR_INVALID_VALUE;
+    const bool row = oc == GEMM_ROW_MAJOR;
+    Problem p{};
+    if (row) p = Problem{(int)M, (int)N, (int)K, A, lda, (int)oa, B, ldb, (int)ob, static_cast<float*>(C), ldc};
+    else p = Problem{(int)N, (int)M, (int)K, B, ldb, 1 - (int)ob, A, lda, 1 - (int)oa, static_cast<float*>(C), ldc};
+    // the direct-copy kernel's layout: k-contiguous operands (after a column-major C's swap)
+    if (K > 0 && !bf16_dma_applies(p, Launch{}, 256, 256)) return GEMM_ERR_INVALID_VALUE;
+    if (M == 0 || N == 0) {
+        t_last_kernel = "none";
+        return GEMM_OK;
+    }
+    DeviceInfo dev;
+    if (!device_info(dev) || !dev.supported) return GEMM_ERR_UNSUPPORTED_DEVICE;
+
+    EpiProblem ep{};
+    static_cast<Problem&>(ep) = p;
+    // a column-major C's bias runs along its columns, the rows of the normalised C
+    ep.e = Epilogue{epi->alpha, epi->beta, epi->bias, row ? 0 : 1, (int)epi->activation, out16 ? 1 : 0};
+    Launch l = launch_for(p, stream);
+    l.vec_c = (p.ldc % 4 == 0) && aligned(C, out16 ? 8 : 16);
+    hipError_t err = hipSuccess;
+    const char* name = "epilogue_fill";
+    if (K == 0) {
+        err = launch_epi_fill(ep, l);
+    } else {
+        Plan best;
+        for (const TileOpt& o : kBf16DmaOpts) {
+            const Plan pl = plan_whole(p, o, dev.cus);
+            if (pl.cost < best.cost) best = pl;
+        }
+        const int bm = best.opt.bm, bn = best.opt.bn;
+        l.group_m = pick_group_m((p.M + bm - 1) / bm, (p.N + bn - 1) / bn);
+        static const char* names[2][2] = {{"bf16_dma256x256_fused", "bf16_dma256x128_fused"},
+                                          {"f16_dma256x256_fused", "f16_dma256x128_fused"}};
+        name = names[in == In::F16 ? 1 : 0][bn == 256 ? 0 : 1];
+        err = launch_bf16_dma_epi(ep, l, bm, bn, in == In::F16);
+    }
+    if (err != hipSuccess) {
+        t_last_hip_error = (int)err;
+        return GEMM_ERR_LAUNCH;
+    }
+    t_last_kernel = name;
+    return GEMM_OK;
+}
+
 }  // namespace
 }  // namespace gemm
 
 extern "C" {
+
+gemm_status_t gemm_bf16_f32acc_fused(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                                     gemm_order_t order_a, const uint16_t* B, int64_t ldb, gemm_order_t order_b,
+                                     void* C, int64_t ldc, gemm_order_t order_c, const gemm_epilogue_t* epilogue,
+                                     hipStream_t stream) {
+    return gemm::run_fused(gemm::In::BF16, M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, epilogue,
+                           stream);
+}
+
+gemm_status_t gemm_f16_f32acc_fused(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                                    gemm_order_t order_a, const uint16_t* B, int64_t ldb, gemm_order_t order_b,
+                                    void* C, int64_t ldc, gemm_order_t order_c, const gemm_epilogue_t* epilogue,
+                                    hipStream_t stream) {
+    return gemm::run_fused(gemm::In::F16, M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, epilogue,
+                           stream);
+}
 
 gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                        gemm_order_t order_a, const float* B, int64_t ldb, gemm_order_t order_b,

@@ -41,6 +41,7 @@
 // column-major-C swap (both k-contiguous), K >= 64, and byte offsets of a wavefront's row
 // block below 2^31.  Any M, N.
 #include "common.hpp"
+#include "epilogue.hpp"
 #include "launch.hpp"
 #include "mma16.hpp"
 
@@ -96,9 +97,11 @@ struct Cfg {
     static_assert(NW % 4 == 0, "whole wavefronts per SIMD");
 };
 
-template <typename C, bool VEC_C, bool F16 = false, bool BATCH = false>
+// EPI: the fused-epilogue instantiation (an EpiProblem; not batched).
+template <typename C, bool VEC_C, bool F16 = false, bool BATCH = false, bool EPI = false>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::NW / 4, C::NW / 4)))
-void k_bf16_dma(KArg<BATCH> p, int tiles_m, int tiles_n, int group_m) {
+void k_bf16_dma(std::conditional_t<EPI, EpiProblem, KArg<BATCH>> p, int tiles_m, int tiles_n, int group_m) {
+    static_assert(!(EPI && BATCH), "the epilogue instantiation takes one problem");
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, FM = C::FM, FN = C::FN, SUB = C::SUB;
     constexpr int ROW = C::ROW, MF = C::MF;
     __shared__ __align__(16) unsigned char smem[C::LDS];
@@ -309,6 +312,18 @@ void k_bf16_dma(KArg<BATCH> p, int tiles_m, int tiles_n, int group_m) {
     }
 
     // ---- epilogue: stores past M or N are skipped ----
+    if constexpr (EPI) {     // applied in place first: the store paths below only convert and store
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3), col = n0 + wn + 32 * j + l32;
+                    if (interior || (row < p.M && col < p.N))
+                        acc[i][j][r] = epi_value(p.e, acc[i][j][r], p.C, (int64_t)row * p.ldc + col, row, col);
+                }
+    }
     if (VEC_C) {
         __builtin_amdgcn_s_barrier();      // every wavefront is done with the stages
         asm volatile("" ::: "memory");
@@ -326,6 +341,18 @@ void k_bf16_dma(KArg<BATCH> p, int tiles_m, int tiles_n, int group_m) {
                 const int rr = q * RPI + lane / LPR, cc = 4 * (lane % LPR);
                 const f32x4 v = *reinterpret_cast<const f32x4*>(band + rr * C::EP + cc);
                 const int row = m0 + wm + 32 * i + rr, col = n0 + wn + cc;
+                if constexpr (EPI) {
+                    const int64_t off = (int64_t)row * p.ldc + col;
+                    if (interior || (row < p.M && col + 3 < p.N)) {
+                        const float y[4] = {v[0], v[1], v[2], v[3]};
+                        epi_store4(p.e, p.C, off, y);
+                    } else if (row < p.M) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (col + e < p.N) epi_store(p.e, p.C, off + e, v[e]);
+                    }
+                    continue;
+                }
                 float* dst = p.C + (int64_t)row * p.ldc + col;
                 if (interior || (row < p.M && col + 3 < p.N)) {
                     *reinterpret_cast<f32x4*>(dst) = v;
@@ -345,7 +372,10 @@ void k_bf16_dma(KArg<BATCH> p, int tiles_m, int tiles_n, int group_m) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                    if (interior || (row < p.M && col < p.N)) p.C[(int64_t)row * p.ldc + col] = acc[i][j][r];
+                    if constexpr (EPI) {
+                        const int64_t off = (int64_t)row * p.ldc + col;
+                        if (interior || (row < p.M && col < p.N)) epi_store(p.e, p.C, off, acc[i][j][r]);
+                    } else if (interior || (row < p.M && col < p.N)) p.C[(int64_t)row * p.ldc + col] = acc[i][j][r];
                 }
             }
     }
@@ -372,6 +402,21 @@ hipError_t launch_any(const Problem& p, const Launch& l, bool f16) {
     return launch_cfg<C, false>(p, l, f16);
 }
 
+template <typename C>
+hipError_t launch_epi(const EpiProblem& p, const Launch& l, bool f16) {
+    const int tiles_m = (p.M + C::BM - 1) / C::BM, tiles_n = (p.N + C::BN - 1) / C::BN;
+    const dim3 grid((unsigned)tiles_m * tiles_n), block(C::THREADS);
+    if (f16 && l.vec_c)
+        hipLaunchKernelGGL((k_bf16_dma<C, true, true, false, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
+    else if (f16)
+        hipLaunchKernelGGL((k_bf16_dma<C, false, true, false, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
+    else if (l.vec_c)
+        hipLaunchKernelGGL((k_bf16_dma<C, true, false, false, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
+    else
+        hipLaunchKernelGGL((k_bf16_dma<C, false, false, false, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool bf16_dma_applies(const Problem& p, const Launch&, int, int) {
@@ -390,6 +435,12 @@ bool bf16_dma_applies(const Problem& p, const Launch&, int, int) {
 hipError_t launch_bf16_dma(const Problem& p, const Launch& l, int bm, int bn, bool f16) {
     if (bm == 256 && bn == 256) return launch_any<Cfg<256, 256, 2, 4, 2, 2>>(p, l, f16);
     if (bm == 256 && bn == 128) return launch_any<Cfg<256, 128, 4, 2, 4, 3>>(p, l, f16);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bf16_dma_epi(const EpiProblem& p, const Launch& l, int bm, int bn, bool f16) {
+    if (bm == 256 && bn == 256) return launch_epi<Cfg<256, 256, 2, 4, 2, 2>>(p, l, f16);
+    if (bm == 256 && bn == 128) return launch_epi<Cfg<256, 128, 4, 2, 4, 3>>(p, l, f16);
     return hipErrorInvalidValue;
 }
 

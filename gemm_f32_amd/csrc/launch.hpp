@@ -3,6 +3,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "epilogue.hpp"
 
 namespace gemm {
 
@@ -61,6 +62,11 @@ hipError_t launch_skinny(const Problem& p, const Launch& l, int et, int fn, int 
                          const SkinnySplit* sp = nullptr, float* part = nullptr);
 // C = 0 for K == 0 (fill.hip)
 hipError_t launch_zero_c(const Problem& p, const Launch& l);
+// Fused epilogue (epilogue.hpp): the 16-bit direct-copy kernel with the epilogue in its stores
+// (same requirements as launch_bf16_dma; l.vec_c for 16-byte FP32 or 8-byte bf16 row groups),
+// and the epilogue of an empty sum for K == 0 (fill.hip)
+hipError_t launch_bf16_dma_epi(const EpiProblem& p, const Launch& l, int bm, int bn, bool f16);
+hipError_t launch_epi_fill(const EpiProblem& p, const Launch& l);
 
 // Block-tile sizes, exported for the host's scheduler choices.
 constexpr int kRegblockBM = 128, kRegblockBN = 128;

@@ -278,6 +278,49 @@ gemm_status_t gemm_f16_f32acc_strided_batched(int64_t batch, int64_t M, int64_t 
                                               float *C, int64_t ldc, int64_t stride_c, gemm_order_t order_c,
                                               hipStream_t stream);
 
+/* Fused epilogue: C = act(alpha * A.B + beta * C + bias), computed on each output while it is
+ * still in registers and stored as FP32 or bf16 ("How a Matrix Multiply Runs on a GPU", section
+ * "Level 2", the epilogue of the block-tile loop, and section "Operational guidance and
+ * trade-offs"; "A06 - Tiled Matrix Multiply (GEMM)", section "6. Challenges, Drawbacks &
+ * Tradeoffs").
+ *
+ *   alpha, beta   scale of the product and of C's previous contents; beta == 0 does not read C
+ *                 (it may hold anything, NaN included)
+ *   bias          device pointer to N floats, bias[j] added to every element of column j;
+ *                 NULL: none
+ *   activation    GEMM_ACT_NONE; GEMM_ACT_RELU max(x, 0); GEMM_ACT_GELU x * Phi(x), Phi the
+ *                 standard normal distribution function (the erf form), applied last
+ *   out_type      GEMM_OUT_F32: C is float; GEMM_OUT_BF16: C holds bf16 bit patterns
+ *                 (uint16_t), rounded to nearest even from the FP32 result, ldc in elements */
+typedef enum { GEMM_ACT_NONE = 0, GEMM_ACT_RELU = 1, GEMM_ACT_GELU = 2 } gemm_activation_t;
+typedef enum { GEMM_OUT_F32 = 0, GEMM_OUT_BF16 = 1 } gemm_out_t;
+typedef struct {
+    float alpha;
+    float beta;
+    const float *bias;
+    gemm_activation_t activation;
+    gemm_out_t out_type;
+} gemm_epilogue_t;
+
+/* gemm_bf16_f32acc_fused / gemm_f16_f32acc_fused: C = epilogue(A.B) for bf16 or fp16 inputs,
+ * FP32 products and sums.  C is `void *` (float or uint16_t per out_type); the rest as the plain
+ * calls.  The epilogue runs in the 16-bit direct-copy kernel, which takes k-contiguous operands:
+ * row-major A with column-major B (a PyTorch Linear: x . W^T), and K >= 64 (K == 0 gives
+ * act(beta * C + bias)).  One kernel launch; nothing is allocated.
+ * Errors: as the plain calls, plus GEMM_ERR_INVALID_VALUE for a NULL epilogue, an unknown
+ * activation or output type, a bias not 4-byte aligned, a C not aligned to its output element,
+ * or operands the direct-copy kernel does not take (other orders, 0 < K < 64). */
+gemm_status_t gemm_bf16_f32acc_fused(int64_t M, int64_t N, int64_t K,
+                                     const uint16_t *A, int64_t lda, gemm_order_t order_a,
+                                     const uint16_t *B, int64_t ldb, gemm_order_t order_b,
+                                     void *C, int64_t ldc, gemm_order_t order_c,
+                                     const gemm_epilogue_t *epilogue, hipStream_t stream);
+gemm_status_t gemm_f16_f32acc_fused(int64_t M, int64_t N, int64_t K,
+                                    const uint16_t *A, int64_t lda, gemm_order_t order_a,
+                                    const uint16_t *B, int64_t ldb, gemm_order_t order_b,
+                                    void *C, int64_t ldc, gemm_order_t order_c,
+                                    const gemm_epilogue_t *epilogue, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

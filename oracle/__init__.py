@@ -5,5 +5,5 @@ package.  The HIP path never imports, links or calls it, and it imports nothing
 from the HIP path.  See oracle.c for what is computed and why.
 """
 from .oracle import (  # noqa: F401
-    build, gemm, gemm_sampled, gemm_strided_batched, normalised_error, num_threads, library_path,
+    build, gemm, gemm_sampled, gemm_strided_batched, epilogue, ACT_NONE, ACT_RELU, ACT_GELU, normalised_error, num_threads, library_path,
 )

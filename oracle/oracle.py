@@ -134,6 +134,44 @@ def gemm_strided_batched(batch, M, N, K, A, lda, stride_a, order_a, B, ldb, stri
     return C, D
 
 
+ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
+
+
+def epilogue(C, D, alpha=1.0, beta=0.0, C_old=None, bias=None, activation=ACT_NONE):
+    """Fused epilogue on the exact product, in float64: (Y, S) with
+
+        Y = act(alpha * C + beta * C_old + bias[j])        (beta == 0: C_old is not read)
+
+    as the epilogue line of the block-tile loop writes it ("How a Matrix Multiply Runs on a
+    GPU", section "Level 2"), bias per column j, the activation applied last: ReLU max(x, 0), or
+    GELU x * Phi(x) with Phi the standard normal distribution function (erf form).  S is the
+    scale a parity tolerance is normalised by: the magnitudes that enter the activation's
+    argument (|alpha| D + |beta C_old| + |bias|), times 1.13, a bound on the slope of either
+    activation.
+    """
+    from scipy.special import erf
+    C = np.asarray(C, dtype=np.float64)
+    pre = alpha * C
+    S = abs(alpha) * np.asarray(D, dtype=np.float64)
+    if beta != 0.0:
+        old = np.asarray(C_old, dtype=np.float64)
+        pre = pre + beta * old
+        S = S + np.abs(beta * old)
+    if bias is not None:
+        b = np.asarray(bias, dtype=np.float64)[None, :]
+        pre = pre + b
+        S = S + np.abs(b)
+    if activation == ACT_RELU:
+        Y = np.maximum(pre, 0.0)
+    elif activation == ACT_GELU:
+        Y = pre * 0.5 * (1.0 + erf(pre / np.sqrt(2.0)))
+    elif activation == ACT_NONE:
+        Y = pre
+    else:
+        raise ValueError(f"unknown activation {activation}")
+    return Y, 1.13 * S
+
+
 def _extent(rows, cols, ld, order):
     """Elements a rows x cols matrix spans from its first element."""
     return (rows - 1) * ld + cols if order == 0 else (cols - 1) * ld + rows

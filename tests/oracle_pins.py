@@ -296,9 +296,46 @@ def pin_batched_scaled_identity(lib):
                 assert np.array_equal(C[z], (z + 1) * Bl[z].astype(np.float64))
 
 
+def pin_epilogue_closed_forms(lib):
+    """act(alpha*C + beta*C_old + bias) on small integers, exact in float64: identity with the
+    defaults, scaling, the old C term, a bias per column (distinct values on a non-square C),
+    ReLU, and beta == 0 never reading C_old (NaN there stays out)."""
+    rng = np.random.default_rng(29)
+    p = gi.make_problem(5, 7, 9, "f32", A_logical=_int_matrix(rng, 5, 9), B_logical=_int_matrix(rng, 9, 7))
+    C, D = _run(lib, p)
+    old = _int_matrix(rng, 5, 7)
+    bias = np.arange(7, dtype=np.float64) * 3 - 10
+    Y, _ = oracle.epilogue(C, D)
+    assert np.array_equal(Y, C)
+    Y, _ = oracle.epilogue(C, D, alpha=2.0, beta=-0.5, C_old=old, bias=bias)
+    for i in range(5):
+        for j in range(7):
+            assert Y[i, j] == 2 * C[i, j] - 0.5 * old[i, j] + (3 * j - 10)
+    Y, _ = oracle.epilogue(C, D, bias=bias, activation=oracle.ACT_RELU)
+    assert np.array_equal(Y, np.where(C + bias > 0, C + bias, 0.0))
+    Y, _ = oracle.epilogue(C, D, beta=0.0, C_old=np.full((5, 7), np.nan))
+    assert np.array_equal(Y, C)
+
+
+def pin_gelu_values(lib):
+    """GELU(x) = x Phi(x): Phi(1) = 0.8413447460685429 and Phi(-1) = 0.15865525393145707 (the
+    normal table), GELU(0) = 0, GELU(10) = 10 in float64, GELU(x) - GELU(-x) = x (Phi(x) +
+    Phi(-x) = 1), and GELU of a large negative value vanishes (-10 Phi(-10) is about -8e-23)."""
+    x = np.array([[1.0, -1.0, 0.0, 10.0, -10.0]])
+    Y, _ = oracle.epilogue(x, np.abs(x), activation=oracle.ACT_GELU)
+    assert abs(Y[0, 0] - 0.8413447460685429) < 1e-15
+    assert abs(Y[0, 1] + 0.15865525393145707) < 1e-15
+    assert Y[0, 2] == 0.0 and Y[0, 3] == 10.0 and abs(Y[0, 4]) < 1e-20
+    r = np.random.default_rng(31).uniform(-6, 6, (1, 200))
+    Yp, _ = oracle.epilogue(r, np.abs(r), activation=oracle.ACT_GELU)
+    Yn, _ = oracle.epilogue(-r, np.abs(r), activation=oracle.ACT_GELU)
+    assert np.allclose(Yp - Yn, r, rtol=0, atol=1e-14)
+
+
 ALL_PINS = [
     pin_fraction_bruteforce, pin_numpy_crosscheck, pin_ones, pin_ones_column_sums,
     pin_identity, pin_permutation, pin_small_integers, pin_transpose, pin_k_split,
     pin_mac_count, pin_degenerate, pin_nonnegative_scale, pin_bf16_widening,
     pin_f16_widening, pin_sampled_matches_full, pin_batched_bruteforce, pin_batched_scaled_identity,
+    pin_epilogue_closed_forms, pin_gelu_values,
 ]

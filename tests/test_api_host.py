@@ -46,9 +46,9 @@ def test_strings():
     assert "unknown" in g.gemm_status_string(99)
 
 
-def _status(fn, *args):
+def _status(fn, *args, **kw):
     try:
-        fn(*args)
+        fn(*args, **kw)
     except g.GemmError as e:
         return e.status
     return g.Status.OK
@@ -314,3 +314,38 @@ def test_batched_empty_is_ok_without_launch(dtype, shape):
 ], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
 def test_batched_valid_layouts_reach_the_device_check(layout):
     assert _status(BATCHED["f32"], *bargs(**layout)) == g.Status.ERR_UNSUPPORTED_DEVICE
+
+
+# --- fused epilogue: argument checks before any device call -------------------------------
+FUSED = {"bf16": g.gemm_bf16_f32acc_fused, "f16": g.gemm_f16_f32acc_fused}
+
+
+def fargs(M=8, N=8, K=64, A=FAKE, lda=64, oa=R, B=FAKE, ldb=64, ob=C_, C=FAKE, ldc=8, oc=R):
+    return (M, N, K, A, lda, oa, B, ldb, ob, C, ldc, oc)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(call=dict(ob=R, ldb=8)),                 # B not k-contiguous: the kernel takes R,C only
+    dict(call=dict(oa=C_, lda=8)),
+    dict(call=dict(K=32, lda=32, ldb=32)),        # 0 < K < 64
+    dict(call=dict(C=FAKE + 2)),                  # FP32 output needs 4-byte alignment
+    dict(call=dict(C=FAKE + 1), epi=dict(out_type=g.Out.BF16)),
+    dict(epi=dict(activation=3)), dict(epi=dict(out_type=2)), dict(epi=dict(bias=FAKE + 2)),
+    dict(call=dict(M=-1)), dict(call=dict(ldc=7)),
+], ids=lambda d: ",".join(f"{k}={v}" for k, v in {**d.get("call", {}), **d.get("epi", {})}.items()))
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_fused_invalid_arguments(dtype, bad):
+    assert _status(FUSED[dtype], *fargs(**bad.get("call", {})), **bad.get("epi", {})) == INVALID
+
+
+def test_fused_null_epilogue_rejected():
+    rc = g.lib_handle().gemm_bf16_f32acc_fused(*fargs(), None, None)
+    assert rc == INVALID
+
+
+@pytest.mark.skipif(gpu_available(), reason="checks the no-GPU path")
+@pytest.mark.parametrize("call", [dict(), dict(oc=C_), dict(K=0), dict(C=FAKE + 2, ldc=8)])
+def test_fused_valid_calls_reach_the_device_check(call):
+    out = g.Out.BF16 if call.get("C") == FAKE + 2 else g.Out.F32
+    assert _status(FUSED["bf16"], *fargs(**call), activation=g.Act.GELU, bias=FAKE,
+                   out_type=out) == g.Status.ERR_UNSUPPORTED_DEVICE

@@ -76,14 +76,21 @@ print(json.dumps(failed))
 """
 
 
-# The strided batch is a loop over the pinned product in oracle.py; each plausible mistake in
-# that loop must fail one of the batched pins.
+# The strided batch and the fused epilogue are written in oracle.py; each plausible mistake in
+# either must fail one of their pins.
 ORACLE_PY = os.path.join(os.path.dirname(oracle.library_path()), "oracle.py")
 PY_MUTANTS = {
     "a_takes_b_stride": ("a = A[z * stride_a:]", "a = A[z * stride_b:]"),
     "b_takes_a_stride": ("b = B[z * stride_b:]", "b = B[z * stride_a:]"),
     "every_entry_reads_entry_0": ("a = A[z * stride_a:]", "a = A[0:]"),
     "entries_shifted": ("C[z], D[z] = gemm(", "C[(z + 1) % batch], D[(z + 1) % batch] = gemm("),
+    "gelu_tanh_form": ("Y = pre * 0.5 * (1.0 + erf(pre / np.sqrt(2.0)))",
+                       "Y = pre * 0.5 * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (pre + 0.044715 * pre ** 3)))"),
+    "bias_per_row": ("b = np.asarray(bias, dtype=np.float64)[None, :]",
+                     "b = np.resize(np.asarray(bias, dtype=np.float64), pre.shape[0])[:, None]"),
+    "beta_scales_product": ("pre = pre + beta * old", "pre = pre + beta * C"),
+    "relu_as_abs": ("Y = np.maximum(pre, 0.0)", "Y = np.abs(pre)"),
+    "alpha_dropped": ("pre = alpha * C", "pre = C"),
 }
 
 
@@ -97,9 +104,11 @@ def test_batched_mutant_fails_a_pin(name, monkeypatch):
     lib = oracle.oracle.load()
     monkeypatch.setattr(oracle, "gemm_strided_batched", ns["gemm_strided_batched"])
     failed = []
-    for pin in (oracle_pins.pin_batched_bruteforce, oracle_pins.pin_batched_scaled_identity):
+    monkeypatch.setattr(oracle, "epilogue", ns["epilogue"])
+    for pin in (oracle_pins.pin_batched_bruteforce, oracle_pins.pin_batched_scaled_identity,
+                oracle_pins.pin_epilogue_closed_forms, oracle_pins.pin_gelu_values):
         try:
             pin(lib)
         except Exception:
             failed.append(pin.__name__)
-    assert failed, f"mutant {name} passed every batched pin"
+    assert failed, f"mutant {name} passed every pin of oracle.py"

@@ -355,7 +355,10 @@ void k_bf16_dma(std::conditional_t<EPI, EpiProblem, KArg<BATCH>> p, int tiles_m,
                 }
                 float* dst = p.C + (int64_t)row * p.ldc + col;
                 if (interior || (row < p.M && col + 3 < p.N)) {
-                    *reinterpret_cast<f32x4*>(dst) = v;
+                    // a batch streams C once (attention's scores): non-temporal stores keep it from
+                    // displacing the operands in the caches
+                    if constexpr (BATCH) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
+                    else *reinterpret_cast<f32x4*>(dst) = v;
                 } else if (row < p.M) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)

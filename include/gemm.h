@@ -248,9 +248,10 @@ gemm_status_t gemm_f16_f32acc_ws(int64_t M, int64_t N, int64_t K,
  * Entry z reads A + z*stride_a and B + z*stride_b and writes C + z*stride_c; strides count
  * elements (of the input type for A and B, floats for C).  stride_a or stride_b 0 uses one
  * operand for every entry.  Heads interleaved in one row, as in a [tokens, heads, head_dim]
- * tensor, are leading dimension heads*head_dim with stride head_dim.  Each entry is computed as
- * the plain call of the same type computes it (same kernels, same accuracy), all of them on
- * `stream` in one launch per kernel (65535 entries at most per launch; more take several).
+ * tensor, are leading dimension heads*head_dim with stride head_dim.  Entries run on the kernels
+ * the plain calls of the same type use (same arithmetic, same accuracy), the kernel and tile
+ * chosen for the batch as a whole, all of them on `stream` in one launch per kernel (65535
+ * entries at most per launch; more take several).
  * No workspace is used and nothing is allocated.
  *
  * Errors: as the plain calls, plus GEMM_ERR_INVALID_VALUE for batch < 0, a negative stride,

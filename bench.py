@@ -208,6 +208,18 @@ class Leg:
                 p.order_c, stream)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(legs, target_s):
     """The oracle (as is) on the first R rows of each leg's problem, R sized to ~target_s."""
     import oracle
@@ -235,10 +247,38 @@ def cpu_baseline(legs, target_s):
     t = run(rows)
     flops = sum(2 * rows * l.w.N * l.w.K for l in legs)
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "seconds": round(t, 3),
+            "nproc": os.cpu_count(), "cpu_model": cpu_model(), "seconds": round(t, 3),
             "sample": f"first {rows} rows of C for each of "
                       f"{', '.join(l.name + (' (entry 0)' if l.batched else '') for l in legs)} "
                       f"({flops / 2:.3e} multiply-adds, fp64 oracle, {threads} OpenMP threads)"}
+
+
+TIMING = ("mean launch time from HIP events recorded before and after each launch on the "
+          "launch stream, over the timed steps")
+
+
+def leg_roofline(leg, info):
+    """The roofline object of one leg's kernel: algorithmic work per launch (2MNK flops, or
+    the compulsory bytes where those take longer at HBM's peak) over its mean launch time,
+    against MI355X's published peak for the leg's dtype."""
+    from gemm_f32_amd import roofline as rl
+    peak = rl.mi355x_peak(leg.w.dtype)
+    per = f" x {leg.w.batch} entries" if leg.batched else ""
+    sec = info["ms"] * 1e-3
+    if leg.bytes / rl.MI355X_HBM_BYTES_PER_S > leg.flops / peak:
+        achieved = leg.bytes / sec
+        return {"bound": "hbm", "kernel": info["kernel"], "achieved": round(achieved / 1e9, 1),
+                "peak": rl.MI355X_HBM_BYTES_PER_S / 1e9, "unit": "GB/s",
+                "frac": round(achieved / rl.MI355X_HBM_BYTES_PER_S, 4),
+                "traffic": measured_traffic(info["kernel"], leg.name),
+                "per_launch": f"e*(M*K + K*N) + 4*M*N{per} = {leg.bytes:.4e} B per launch ({leg.name})",
+                "timing": TIMING}
+    achieved = leg.flops / sec
+    return {"bound": "mfma", "kernel": info["kernel"], "achieved": round(achieved / 1e12, 2),
+            "peak": round(peak / 1e12, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+            "traffic": measured_traffic(info["kernel"], leg.name),
+            "per_launch": f"2*M*N*K{per} = {leg.flops:.4e} FLOP per launch ({leg.name})",
+            "timing": TIMING}
 
 
 def main():
@@ -292,24 +332,9 @@ def main():
                               "input_sets": leg.sets}
         if leg.ws is not None:
             leg_info[leg.name]["workspace_bytes"] = leg.ws_bytes
+    roofs = {leg.name: leg_roofline(leg, leg_info[leg.name]) for leg in legs}
     dom = max(legs, key=lambda l: leg_info[l.name]["ms"])
-    di = leg_info[dom.name]
-    peak = rl.mi355x_peak(dom.w.dtype)
-    per = f" x {dom.w.batch} entries" if dom.batched else ""
-    if dom.bytes / rl.MI355X_HBM_BYTES_PER_S > dom.flops / peak:
-        # the compulsory traffic takes longer at HBM's peak than the arithmetic at the matrix cores'
-        achieved = dom.bytes / (di["ms"] * 1e-3)
-        roof = {"bound": "hbm", "kernel": di["kernel"], "achieved": round(achieved / 1e9, 1),
-                "peak": rl.MI355X_HBM_BYTES_PER_S / 1e9, "unit": "GB/s",
-                "frac": round(achieved / rl.MI355X_HBM_BYTES_PER_S, 4),
-                "traffic": measured_traffic(di["kernel"], dom.name),
-                "per_launch": f"e*(M*K + K*N) + 4*M*N{per} = {dom.bytes:.4e} B per launch ({dom.name})"}
-    else:
-        achieved = dom.flops / (di["ms"] * 1e-3)
-        roof = {"bound": "mfma", "kernel": di["kernel"], "achieved": round(achieved / 1e12, 2),
-                "peak": round(peak / 1e12, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": measured_traffic(di["kernel"], dom.name),
-                "per_launch": f"2*M*N*K{per} = {dom.flops:.4e} FLOP per launch ({dom.name})"}
+    roof = roofs[dom.name]
 
     value = step_flops / (ms_step * 1e-3) / 1e12
     dtype = "+".join(sorted({"f32" if l.w.dtype == "f32" else "bf16->f32" for l in legs}))
@@ -323,6 +348,7 @@ def main():
                    "legs": leg_info, "algo": args.algo, "epilogue": args.epilogue,
                    "wall_s": round(wall, 3)},
         "roofline": roof,
+        "roofline_legs": roofs,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(legs, args.cpu_seconds)

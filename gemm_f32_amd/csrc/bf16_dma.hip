@@ -5,12 +5,10 @@
 // usually has (row-major A, column-major B: both operands contiguous along k), arranged so
 // that the k-loop is one branch-free block:
 //
-//  * Block tile BM x BN, k-tiles BK = 64 deep, WGM x WGN wavefronts.  At 256 x 256 eight
-//    wavefronts in a 2 x 4 grid own 128 x 64 of C each (4 x 2 fragments of 32 x 32 = 128
-//    accumulators per lane), two per SIMD: while one of them waits on the issue of a copy
-//    or on the barrier, the other one keeps the SIMD's matrix pipe busy (measured 7% faster
-//    at 4096^3 than four wavefronts of 128 x 128, despite 1.5 times the LDS reads).  At
-//    256 x 128, eight wavefronts of 64 x 64.
+//  * Block tile BM x BN, k-tiles BK = 64 deep, WGM x WGN wavefronts.  At 256 x 256 four
+//    wavefronts in a 2 x 2 grid own 128 x 128 of C each (4 x 4 fragments of 32 x 32 = 256
+//    accumulators per lane), one per SIMD.  At 256 x 128, eight wavefronts of 64 x 64, two
+//    per SIMD.
 //  * LDS: one row of BK bf16 (128 bytes, 8 chunks of 16 bytes) per row of each tile, chunk
 //    c of row r stored at c ^ s(r), s(r) = (r mod 8) xor bit 3 of r, so that the 32 rows
 //    read at one logical chunk fall on distinct 16-byte bank groups.  A lane's 16-byte read
@@ -25,9 +23,11 @@
 //    rows of its copy block that exist, so rows past M (N) read as zero: edge tiles need no
 //    separate code in the k-loop.  (Buffer loads, like global ones, accept the 2-byte
 //    aligned rows of odd leading dimensions on gfx950.)
-//  * Two or three LDS stages ("GEMM Optimization", V3: stage the next tile while the current
-//    one is multiplied), software-pipelined across k-tiles (see the main loop); one barrier
-//    per k-tile.
+//  * Staging ahead ("GEMM Optimization", V3: stage the next tile while the current one is
+//    multiplied), software-pipelined across k-tiles, one barrier per k-tile: at 256 x 256 a
+//    ring of five half-stage buffers (an A or a B tile each, 160 KB) that lets each copy
+//    start one to two k-tiles before its tile is multiplied; at 256 x 128 three whole
+//    stages.
 //  * K tail: a last k-tile staged through registers with bounds checks and zero fill into
 //    the same LDS positions ("A06 - Tiled Matrix Multiply (GEMM)", "Pitfall 1 - The
 //    boundary guard that fails silently": a ragged K needs the zero fill).
@@ -61,9 +61,12 @@ constexpr int kBufWord3 = 0x00020000;
 // logical chunk hit 16 distinct 16-byte bank groups
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-template <int BM_, int BN_, int WGM_, int WGN_, int CSPAN_, int S_>
+// RING: the five-buffer half-stage pipeline of the main loop below (BM == BN) instead of S
+// whole stages
+template <int BM_, int BN_, int WGM_, int WGN_, int CSPAN_, int S_, bool RING_ = false>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = 64, WGM = WGM_, WGN = WGN_, S = S_;
+    static constexpr bool RING = RING_;
     static constexpr int ROW = BK * 2;                       // LDS row bytes (8 chunks)
     static constexpr int RPC = 1024 / ROW;                   // tile rows per 1 KB copy
     static constexpr int NW = WGM * WGN, THREADS = 64 * NW;
@@ -89,13 +92,16 @@ struct Cfg {
     // three they have until the barrier of iteration kt+1
     static_assert(CSPAN >= 1 && (S == 2 ? CSPAN < SUB : CSPAN <= SUB), "copies land before their barrier");
     static_assert(W >= DMA, "at most one copy per instruction slot");
-    static constexpr int LDS = S * STAGE;
+    static_assert(!RING || (BM == BN && B_DMA <= MF && A_DMA <= (SUB - 1) * MF), "ring layout");
+    static constexpr int LDS = RING ? 5 * A_BYTES : S * STAGE;
     // epilogue: a 32 x WN band per wavefront, rows padded by 8 floats (the two half-waves
     // of one accumulator register, 4 rows apart, land on different banks)
     static constexpr int EP = WN + 8;
     static_assert(NW * 32 * EP * 4 <= LDS, "epilogue staging fits in the stages");
     static_assert(NW % 4 == 0, "whole wavefronts per SIMD");
 };
+
+using Cfg256 = Cfg<256, 256, 2, 2, 2, 2, true>;
 
 // EPI: the fused-epilogue instantiation (an EpiProblem; not batched).
 template <typename C, bool VEC_C, bool F16 = false, bool BATCH = false, bool EPI = false>
@@ -203,7 +209,90 @@ void k_bf16_dma(std::conditional_t<EPI, EpiProblem, KArg<BATCH>> p, int tiles_m,
     // instructions.  Past the end of K the copies repeat the last tile into a stage nobody
     // reads, and the fragments read for a tile nk are never used, so the loop body has no
     // branch.
-    if (nk > 0) {                             // uniform
+    if constexpr (C::RING) {
+        // ---- ring of five half-stages (160 KB at 256 x 256): the A tile of k-tile t lives in
+        // buffer 2t mod 5, its B tile in buffer 2t+1 mod 5.  The barrier of iteration kt (before
+        // its last k-step) frees both buffers of tile kt.  The B tile of kt+2 is copied into the
+        // first during that last k-step and has until the next barrier to land; the A tile of
+        // kt+3 is copied into the second during the first SUB-1 k-steps of iteration kt+1 and
+        // has until the barrier after next.  Against two whole stages, every copy has one to two
+        // k-tiles to arrive instead of one to three k-steps, and a k-tile's copies are spread
+        // over all of its k-steps (measured at 4096^3: 2300 instead of 2750 cycles per k-tile,
+        // against 2048 of matrix work).
+        if (nk > 0) {                         // uniform
+            const int last = nk - 1;
+            const int rb_off = b_off - C::A_BYTES;
+            auto read_ring = [&](int abuf, int bbuf, int s, int m, int b) {
+                const int coff = ((2 * s + h) ^ sw) << 4;
+                if (m < FM)
+                    fa[b][m] = *reinterpret_cast<const bf16x8*>(smem + abuf * C::A_BYTES + a_off + m * 32 * ROW + coff);
+                else if (m < C::RD)
+                    fb[b][m - FM] = *reinterpret_cast<const bf16x8*>(smem + bbuf * C::A_BYTES + rb_off +
+                                                                     (m - FM) * 32 * ROW + coff);
+            };
+            auto issue_a = [&](int j, int kt, int buf) {
+                lds_void* dst = (lds_void*)(smem + buf * C::A_BYTES + (wave * C::A_DMA + j) * 1024);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, aoff[j & 1] + j * astep, kt * (BK * 2), 0, 0);
+            };
+            auto issue_b = [&](int j, int kt, int buf) {
+                lds_void* dst = (lds_void*)(smem + buf * C::A_BYTES + (wave * C::B_DMA + j) * 1024);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, boff[j & 1] + j * bstep, kt * (BK * 2), 0, 0);
+            };
+            // instruction slots between two copies: B over the last k-step, A over the others
+            constexpr int BSL = MF / C::B_DMA, ASL = (SUB - 1) * MF / C::A_DMA;
+#pragma unroll
+            for (int j = 0; j < C::A_DMA; ++j) issue_a(j, 0, 0);
+#pragma unroll
+            for (int j = 0; j < C::B_DMA; ++j) issue_b(j, 0, 1);
+#pragma unroll
+            for (int j = 0; j < C::A_DMA; ++j) issue_a(j, min(1, last), 2);
+#pragma unroll
+            for (int j = 0; j < C::B_DMA; ++j) issue_b(j, min(1, last), 3);
+            // tile 0 landed; tile 1 may be in flight
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"(C::A_DMA + C::B_DMA) : "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int m = 0; m < C::RD; ++m) read_ring(0, 1, 0, m, 0);
+            int ab = 0;                        // 2 kt mod 5: the A buffer of tile kt
+            for (int kt = 0; kt < nk; ++kt) {
+                const int bb = ab == 4 ? 0 : ab + 1;                  // B buffer of tile kt
+                const int a2 = ab >= 1 ? ab - 1 : 4;                  // 2 kt + 4 mod 5: A of tile kt+2
+                const int a1 = ab >= 3 ? ab - 3 : ab + 2;             // 2 kt + 2 mod 5: A of tile kt+1
+                const int b1 = a1 == 4 ? 0 : a1 + 1;                  // B of tile kt+1
+                const int k2 = min(kt + 2, last);
+#pragma unroll
+                for (int s = 0; s < SUB - 1; ++s) {
+#pragma unroll
+                    for (int m = 0; m < MF; ++m) {
+#pragma unroll
+                        for (int q = 0; q < C::A_DMA; ++q)
+                            if (q * ASL == s * MF + m) issue_a(q, k2, a2);
+                        read_ring(ab, bb, s + 1, m, (s + 1) & 1);
+                        mfma(m, s & 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                // tile kt+1 landed (the A copies of tile kt+2 issued above may be in flight);
+                // own reads of tile kt complete
+                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"(C::A_DMA) : "memory");
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int m = 0; m < MF; ++m) {
+#pragma unroll
+                    for (int q = 0; q < C::B_DMA; ++q)
+                        if (q * BSL == m) issue_b(q, k2, ab);         // B of tile kt+2: 2 kt + 5 mod 5
+                    read_ring(a1, b1, 0, m, 0);
+                    mfma(m, (SUB - 1) & 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                ab = a1;
+            }
+            // the surplus copies land before LDS is reused or released
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        }
+    } else if (nk > 0) {                      // uniform
         constexpr int S = C::S;
         const int last = nk - 1;
 #pragma unroll
@@ -324,63 +413,46 @@ void k_bf16_dma(std::conditional_t<EPI, EpiProblem, KArg<BATCH>> p, int tiles_m,
                         acc[i][j][r] = epi_value(p.e, acc[i][j][r], p.C, (int64_t)row * p.ldc + col, row, col);
                 }
     }
-    if (VEC_C) {
-        __builtin_amdgcn_s_barrier();      // every wavefront is done with the stages
-        asm volatile("" ::: "memory");
-        constexpr int LPR = C::WN / 4, RPI = 64 / LPR;   // lanes per C row, rows per store
-        float* band = reinterpret_cast<float*>(smem) + wave * 32 * C::EP;
+    // every path stages a 32-row band through LDS and stores whole rows, 16 bytes per lane
+    // where C allows (VEC_C) and the four columns lie inside, else element by element
+    __builtin_amdgcn_s_barrier();          // every wavefront is done with the stages
+    asm volatile("" ::: "memory");
+    constexpr int LPR = C::WN / 4, RPI = 64 / LPR;   // lanes per C row, rows per store
+    float* band = reinterpret_cast<float*>(smem) + wave * 32 * C::EP;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    band[(8 * (r >> 2) + 4 * h + (r & 3)) * C::EP + 32 * j + l32] = acc[i][j][r];
+            for (int r = 0; r < 16; ++r)
+                band[(8 * (r >> 2) + 4 * h + (r & 3)) * C::EP + 32 * j + l32] = acc[i][j][r];
 #pragma unroll
-            for (int q = 0; q < 32 / RPI; ++q) {
-                const int rr = q * RPI + lane / LPR, cc = 4 * (lane % LPR);
-                const f32x4 v = *reinterpret_cast<const f32x4*>(band + rr * C::EP + cc);
-                const int row = m0 + wm + 32 * i + rr, col = n0 + wn + cc;
-                if constexpr (EPI) {
-                    const int64_t off = (int64_t)row * p.ldc + col;
-                    if (interior || (row < p.M && col + 3 < p.N)) {
-                        const float y[4] = {v[0], v[1], v[2], v[3]};
-                        epi_store4(p.e, p.C, off, y);
-                    } else if (row < p.M) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (col + e < p.N) epi_store(p.e, p.C, off + e, v[e]);
-                    }
-                    continue;
-                }
-                float* dst = p.C + (int64_t)row * p.ldc + col;
-                if (interior || (row < p.M && col + 3 < p.N)) {
-                    // a batch streams C once (attention's scores): non-temporal stores keep it from
-                    // displacing the operands in the caches
-                    if constexpr (BATCH) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
-                    else *reinterpret_cast<f32x4*>(dst) = v;
+        for (int q = 0; q < 32 / RPI; ++q) {
+            const int rr = q * RPI + lane / LPR, cc = 4 * (lane % LPR);
+            const f32x4 v = *reinterpret_cast<const f32x4*>(band + rr * C::EP + cc);
+            const int row = m0 + wm + 32 * i + rr, col = n0 + wn + cc;
+            const int64_t off = (int64_t)row * p.ldc + col;
+            const bool whole = VEC_C && (interior || (row < p.M && col + 3 < p.N));
+            if constexpr (EPI) {
+                if (whole) {
+                    const float y[4] = {v[0], v[1], v[2], v[3]};
+                    epi_store4(p.e, p.C, off, y);
                 } else if (row < p.M) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (col + e < p.N) dst[e] = v[e];
+                        if (col + e < p.N) epi_store(p.e, p.C, off + e, v[e]);
                 }
+            } else if (whole) {
+                // a batch streams C once (attention's scores): non-temporal stores keep it from
+                // displacing the operands in the caches
+                if constexpr (BATCH) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p.C + off));
+                else *reinterpret_cast<f32x4*>(p.C + off) = v;
+            } else if (row < p.M) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (col + e < p.N) p.C[off + e] = v[e];
             }
         }
-    } else {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int col = n0 + wn + 32 * j + l32;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                    if constexpr (EPI) {
-                        const int64_t off = (int64_t)row * p.ldc + col;
-                        if (interior || (row < p.M && col < p.N)) epi_store(p.e, p.C, off, acc[i][j][r]);
-                    } else if (interior || (row < p.M && col < p.N)) p.C[(int64_t)row * p.ldc + col] = acc[i][j][r];
-                }
-            }
     }
 }
 
@@ -429,20 +501,23 @@ bool bf16_dma_applies(const Problem& p, const Launch&, int, int) {
            (int64_t)64 * p.ldb * 2 < lim;
 }
 
-// Configurations: 256 x 256 with eight wavefronts of 128 x 64 (two per SIMD), two stages
-// (128 KB of LDS), the copies of a tile spread over two k-steps; 256 x 128 with eight
-// wavefronts of 64 x 64 and three stages (144 KB), the copies spread over four k-steps.
-// Measured per 64-deep k-tile at 4096^3 (in-kernel clock): 256 x 256 2270 cycles against
-// 2048 of matrix work; 256 x 128 1350 against 1024 (four wavefronts of 128 x 64: 1425 with
-// three stages, 1540-1630 with two).
+// Configurations.  256 x 256: four wavefronts of 128 x 128 (one per SIMD, 256 accumulators
+// each in accumulation registers) on the five-buffer ring (160 KB of LDS).  Against eight
+// wavefronts of 128 x 64 on two whole stages (the previous layout) it reads a third less from LDS
+// per product, and the ring gives every copy one to two k-tiles to land: at 4096^3,
+// interleaved with the FP32 GEMM as the benchmark step runs them, 116 -> 108 us (2750 -> 2300
+// cycles per k-tile against 2048 of matrix work; the shader clock, set by the power limit, went
+// 1.79 -> 1.68 GHz).  256 x 128: eight wavefronts of 64 x 64 and three whole stages (144 KB),
+// the copies spread over four k-steps (1350 cycles per k-tile against 1024; four wavefronts of
+// 128 x 64: 1425 with three stages, 1540-1630 with two).
 hipError_t launch_bf16_dma(const Problem& p, const Launch& l, int bm, int bn, bool f16) {
-    if (bm == 256 && bn == 256) return launch_any<Cfg<256, 256, 2, 4, 2, 2>>(p, l, f16);
+    if (bm == 256 && bn == 256) return launch_any<Cfg256>(p, l, f16);
     if (bm == 256 && bn == 128) return launch_any<Cfg<256, 128, 4, 2, 4, 3>>(p, l, f16);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_bf16_dma_epi(const EpiProblem& p, const Launch& l, int bm, int bn, bool f16) {
-    if (bm == 256 && bn == 256) return launch_epi<Cfg<256, 256, 2, 4, 2, 2>>(p, l, f16);
+    if (bm == 256 && bn == 256) return launch_epi<Cfg256>(p, l, f16);
     if (bm == 256 && bn == 128) return launch_epi<Cfg<256, 128, 4, 2, 4, 3>>(p, l, f16);
     return hipErrorInvalidValue;
 }

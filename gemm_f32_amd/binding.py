@@ -39,6 +39,7 @@ class Status(enum.IntEnum):
     ERR_INVALID_VALUE = 1
     ERR_UNSUPPORTED_DEVICE = 2
     ERR_LAUNCH = 3
+    ERR_SCRATCH_TOO_SMALL = 4
 
 
 class LibraryNotBuilt(ImportError):
@@ -102,6 +103,7 @@ def _load():
     for name in ("gemm_bf16_f32acc_fused", "gemm_f16_f32acc_fused"):
         f = getattr(lib, name)
         f.argtypes, f.restype = args[:-1] + [ctypes.POINTER(EpilogueStruct), vp], ci
+    lib.gemm_bf16_f32acc_noalloc.argtypes, lib.gemm_bf16_f32acc_noalloc.restype = args, ci
     return lib
 
 
@@ -129,7 +131,11 @@ EXPORTED = ("gemm_f32", "gemm_bf16_f32acc", "gemm_f32_algo", "gemm_bf16_f32acc_a
             "gemm_plan", "gemm_workspace_size", "gemm_f32_ws", "gemm_bf16_f32acc_ws",
             "gemm_f16_f32acc", "gemm_f16_f32acc_algo", "gemm_f16_f32acc_ws",
             "gemm_f32_strided_batched", "gemm_bf16_f32acc_strided_batched",
-            "gemm_f16_f32acc_strided_batched", "gemm_bf16_f32acc_fused", "gemm_f16_f32acc_fused")
+            "gemm_f16_f32acc_strided_batched", "gemm_bf16_f32acc_fused", "gemm_f16_f32acc_fused",
+            "gemm_bf16_f32acc_noalloc")
+
+# bytes of the static scratch behind gemm_bf16_f32acc_noalloc (GEMM_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # dtype codes of gemm_plan / gemm_workspace_size
 DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2}
@@ -229,6 +235,12 @@ def gemm_bf16_f32acc_ws(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order
     """gemm_bf16_f32acc with a caller's workspace (device pointer, bytes) for split-K."""
     _check(lib_handle().gemm_bf16_f32acc_ws(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c,
                                             workspace, workspace_bytes, stream), "gemm_bf16_f32acc_ws")
+
+
+def gemm_bf16_f32acc_noalloc(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, stream=0):
+    """gemm_bf16_f32acc_ws with the library's static scratch as workspace: allocates nothing."""
+    _check(lib_handle().gemm_bf16_f32acc_noalloc(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c,
+                                                 stream), "gemm_bf16_f32acc_noalloc")
 
 
 # --- torch tensors -> (pointer, leading dimension, order) ------------------------------

@@ -11,6 +11,14 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+// Scratch memory of gemm_bf16_f32acc_noalloc: the split-K partial sums that the _ws calls keep
+// in a caller's workspace, here in a fixed array of device memory.  Every GPU the library runs
+// on holds its own copy until the process ends.  In host code this name only stands for the
+// array; the device address of the current device's copy comes from hipGetSymbolAddress
+// (scratch_address below), and only that address is passed to kernels.
+constexpr size_t kScratchBytes = GEMM_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace gemm {
 namespace {
 
@@ -43,6 +51,26 @@ bool device_info(DeviceInfo& out) {
     });
     out = g_dev[dev];
     return true;
+}
+
+// The device address of the current device's copy of `scratch`, looked up once per device
+// with that device current (the lookup's error is kept and returned on every later call).
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+hipError_t scratch_address(void*& ptr) {
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    ptr = g_scratch_ptr[dev];
+    return g_scratch_err[dev];
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -607,10 +635,39 @@ gemm_status_t run_fused(In in, int64_t M, int64_t N, int64_t K, const uint16_t* 
     return GEMM_OK;
 }
 
+// gemm_bf16_f32acc_noalloc: the _ws call with `scratch` as its workspace.  Nothing is
+// allocated; a problem whose split would need more than kScratchBytes is refused.
+gemm_status_t run_noalloc(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, gemm_order_t oa,
+                          const uint16_t* B, int64_t ldb, gemm_order_t ob, float* C, int64_t ldc, gemm_order_t oc,
+                          hipStream_t stream) {
+    const gemm_status_t st = validate(In::BF16, M, N, K, A, lda, oa, B, ldb, ob, C, ldc, oc);
+    if (st != GEMM_OK) return st;
+    if (M == 0 || N == 0) return run(In::BF16, GEMM_ALGO_AUTO, M, N, K, A, lda, oa, B, ldb, ob, C, ldc, oc, stream);
+    DeviceInfo dev;
+    if (!device_info(dev) || !dev.supported) return GEMM_ERR_UNSUPPORTED_DEVICE;
+    void* ptr = nullptr;
+    const hipError_t e = scratch_address(ptr);
+    if (e != hipSuccess) {
+        t_last_hip_error = (int)e;
+        return GEMM_ERR_LAUNCH;
+    }
+    const size_t need = K > 0 ? split_bytes(query_problem(M, N, K, oa, ob, oc), kElemBf16, dev.cus) : 0;
+    if (need > kScratchBytes) return GEMM_ERR_SCRATCH_TOO_SMALL;
+    // the planner uses the workspace only for a split that fits in the bytes it is given
+    return run(In::BF16, GEMM_ALGO_AUTO, M, N, K, A, lda, oa, B, ldb, ob, C, ldc, oc, stream,
+               Workspace{ptr, kScratchBytes});
+}
+
 }  // namespace
 }  // namespace gemm
 
 extern "C" {
+
+gemm_status_t gemm_bf16_f32acc_noalloc(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                                       gemm_order_t order_a, const uint16_t* B, int64_t ldb, gemm_order_t order_b,
+                                       float* C, int64_t ldc, gemm_order_t order_c, hipStream_t stream) {
+    return gemm::run_noalloc(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, stream);
+}
 
 gemm_status_t gemm_bf16_f32acc_fused(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                                      gemm_order_t order_a, const uint16_t* B, int64_t ldb, gemm_order_t order_b,
@@ -768,6 +825,9 @@ const char* gemm_status_string(gemm_status_t status) {
         case GEMM_ERR_INVALID_VALUE: return "GEMM_ERR_INVALID_VALUE: invalid argument";
         case GEMM_ERR_UNSUPPORTED_DEVICE: return "GEMM_ERR_UNSUPPORTED_DEVICE: current device is not gfx950";
         case GEMM_ERR_LAUNCH: return "GEMM_ERR_LAUNCH: kernel launch failed";
+        case GEMM_ERR_SCRATCH_TOO_SMALL:
+            return "GEMM_ERR_SCRATCH_TOO_SMALL: the problem's split-K partial sums need more than the library's "
+                   "static scratch (GEMM_NOALLOC_SCRATCH_BYTES); use gemm_bf16_f32acc_ws with a workspace";
     }
     return "unknown gemm_status_t";
 }

@@ -33,7 +33,9 @@
  *                                 operand, or a shape the chosen algorithm cannot run;
  *     GEMM_ERR_UNSUPPORTED_DEVICE the current device is not gfx950;
  *     GEMM_ERR_LAUNCH             the HIP runtime refused the launch (see
- *                                 gemm_last_hip_error).
+ *                                 gemm_last_hip_error);
+ *     GEMM_ERR_SCRATCH_TOO_SMALL  gemm_bf16_f32acc_noalloc only: the problem's split-K partial
+ *                                 sums would not fit in the library's static scratch.
  */
 #ifndef LIBGEMM_GEMM_H
 #define LIBGEMM_GEMM_H
@@ -52,7 +54,8 @@ typedef enum {
     GEMM_OK = 0,
     GEMM_ERR_INVALID_VALUE = 1,
     GEMM_ERR_UNSUPPORTED_DEVICE = 2,
-    GEMM_ERR_LAUNCH = 3
+    GEMM_ERR_LAUNCH = 3,
+    GEMM_ERR_SCRATCH_TOO_SMALL = 4
 } gemm_status_t;
 
 /*
@@ -321,6 +324,29 @@ gemm_status_t gemm_f16_f32acc_fused(int64_t M, int64_t N, int64_t K,
                                     const uint16_t *B, int64_t ldb, gemm_order_t order_b,
                                     void *C, int64_t ldc, gemm_order_t order_c,
                                     const gemm_epilogue_t *epilogue, hipStream_t stream);
+
+/* ---- Without any allocation: split-K partial sums in a static scratch array ---------------
+ * For callers that cannot allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * gemm_bf16_f32acc_noalloc: as gemm_bf16_f32acc_ws (same kernels, same split-K choice, same
+ * results bit for bit), with the workspace replaced by a fixed array of
+ * GEMM_NOALLOC_SCRATCH_BYTES bytes in device memory that the library holds on every GPU it
+ * runs on until the process ends.  The call allocates nothing (no hipMalloc, no library
+ * allocation); its first call on a device looks the array's address up once.  A problem whose
+ * partial sums would need more than GEMM_NOALLOC_SCRATCH_BYTES (gemm_workspace_size(1, ...))
+ * is refused with GEMM_ERR_SCRATCH_TOO_SMALL before anything is enqueued.  Every call on one
+ * GPU uses that GPU's one array, which keeps the last call's contents (every value a call reads
+ * from it is written earlier in the same call): calls that may overlap on one GPU -- on two
+ * streams, or from two threads -- race and must be serialised by the caller.
+ * Errors: as gemm_bf16_f32acc, plus GEMM_ERR_SCRATCH_TOO_SMALL, and GEMM_ERR_LAUNCH if the
+ * array's address cannot be obtained on the current device. */
+#define GEMM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+gemm_status_t gemm_bf16_f32acc_noalloc(int64_t M, int64_t N, int64_t K,
+                                       const uint16_t *A, int64_t lda, gemm_order_t order_a,
+                                       const uint16_t *B, int64_t ldb, gemm_order_t order_b,
+                                       float *C, int64_t ldc, gemm_order_t order_c,
+                                       hipStream_t stream);
 
 #ifdef __cplusplus
 }

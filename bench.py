@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--epilogue", default=None, choices=sorted(EPILOGUES),
                     help="run the fused-epilogue entry point (16-bit inputs, row-major A, column-major B)")
+    ap.add_argument("--tile-order", default="swizzled", choices=["swizzled", "rowmajor"],
+                    help="rowmajor: the tile scheduler's XCD and group-M remaps off (GEMM_TILE_ORDER), to "
+                         "measure what they buy")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 256 MiB device-to-device copy instead (the reference "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -71,7 +74,11 @@ def parse():
 # scheduler, buffer helpers) and the launch declarations
 KERNEL_SOURCES = {
     "f32_dma": ("f32_dma.hip",),
-    "bf16_dma": ("bf16_dma.hip", "mma16.hpp"),
+    "bf16_dma": ("bf16_dma.hip", "mma16.hpp", "epilogue.hpp"),
+    "f16_dma": ("bf16_dma.hip", "mma16.hpp", "epilogue.hpp"),
+    "bf16_mfma": ("bf16_mfma.hip", "mma16.hpp"),
+    "f32_skinny": ("skinny.hip", "mma16.hpp"),
+    "bf16_skinny": ("skinny.hip", "mma16.hpp"),
 }
 SHARED_SOURCES = ("common.hpp", "launch.hpp")
 
@@ -290,6 +297,8 @@ def main():
     if args.copy_calibration:
         copy_calibration(args)
         return
+    if args.tile_order == "rowmajor":
+        os.environ["GEMM_TILE_ORDER"] = "rowmajor"     # read once, before the first call
     import torch
     import gemm_f32_amd as g
     from gemm_f32_amd import roofline as rl
@@ -345,7 +354,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload if args.workload != DEFAULT else
                    "4096^3 FP32 GEMM + 4096^3 BF16->FP32 GEMM per step",
-                   "legs": leg_info, "algo": args.algo, "epilogue": args.epilogue,
+                   "legs": leg_info, "algo": args.algo, "epilogue": args.epilogue, "tile_order": args.tile_order,
                    "wall_s": round(wall, 3)},
         "roofline": roof,
         "roofline_legs": roofs,

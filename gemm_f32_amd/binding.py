@@ -29,7 +29,6 @@ class Algo(enum.IntEnum):
     MFMA_256x128 = 7
     MFMA_128x128 = 8
     MFMA_64x64 = 9
-    MFMA_PINGPONG = 10
     SKINNY = 11
     MFMA_DMA = 12
 

@@ -23,7 +23,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgemm.so")
 
 SOURCES = ["api.hip", "fill.hip", "f32_ladder.hip", "f32_regblock.hip", "f32_mfma.hip", "f32_dma.hip",
-           "bf16_mfma.hip", "bf16_dma.hip", "bf16_pingpong.hip", "skinny.hip"]
+           "bf16_mfma.hip", "bf16_dma.hip", "skinny.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -4,6 +4,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -93,7 +94,18 @@ gemm_status_t validate(In in, int64_t M, int64_t N, int64_t K, const void* A, in
     return GEMM_OK;
 }
 
+// GEMM_TILE_ORDER=rowmajor in the environment (read once) turns the tile scheduler's remaps
+// off, so that what they buy can be measured.
+bool plain_tile_order() {
+    static const bool plain = [] {
+        const char* v = std::getenv("GEMM_TILE_ORDER");
+        return v != nullptr && std::strcmp(v, "rowmajor") == 0;
+    }();
+    return plain;
+}
+
 int pick_group_m(int tiles_m, int tiles_n) {
+    if (plain_tile_order()) return 0;
     // Make the run of tiles that one XCD receives (total / 8 consecutive ids) cover a
     // near-square patch of C: group_m x (per_xcd / group_m) tiles.
     const int per_xcd = (tiles_m * tiles_n) / kNumXcds;
@@ -171,9 +183,9 @@ struct TileOpt {
 constexpr TileOpt kF32DmaOpts[] = {{256, 256, 1.0, 1, true}, {128, 128, 0.85, 2, true}};
 constexpr TileOpt kF32MfmaOpts[] = {{128, 128, 0.85, 4, false}, {64, 64, 0.75, 4, false}};
 // BF16: direct-copy 256^2 and 256x128, register-staged tiles of bf16_mfma.hip
-constexpr TileOpt kBf16DmaOpts[] = {{256, 256, 1.0, 1, true}, {256, 128, 0.86, 1, true}};
-constexpr TileOpt kBf16MfmaOpts[] = {{256, 256, 1.0, 1, false}, {256, 128, 0.78, 1, false},
-                                     {128, 128, 0.74, 2, false}, {64, 64, 0.35, 4, false}};
+constexpr TileOpt kBf16DmaOpts[] = {{256, 256, 1.0, 1, true}, {256, 128, 0.71, 1, true}};
+constexpr TileOpt kBf16MfmaOpts[] = {{256, 128, 0.72, 1, false}, {128, 128, 0.69, 2, false},
+                                     {64, 64, 0.33, 4, false}};
 
 double round_cost(int64_t n, int bm, int bn, double eff, int per_cu, int cus) {
     const double c = cus > 0 ? cus : 256;
@@ -310,10 +322,10 @@ const char* f32_name(const TileOpt& o) {
     return o.bm == 64 ? "f32_mfma64x64" : "f32_mfma128x128";
 }
 const char* b16_name(const TileOpt& o, int et) {
-    static const char* names[2][6] = {
-        {"bf16_dma256x256", "bf16_dma256x128", "bf16_mfma256x256", "bf16_mfma256x128", "bf16_mfma128x128", "bf16_mfma64x64"},
-        {"f16_dma256x256", "f16_dma256x128", "f16_mfma256x256", "f16_mfma256x128", "f16_mfma128x128", "f16_mfma64x64"}};
-    const int i = o.dma ? (o.bn == 256 ? 0 : 1) : (o.bm == 256 ? (o.bn == 256 ? 2 : 3) : (o.bm == 128 ? 4 : 5));
+    static const char* names[2][5] = {
+        {"bf16_dma256x256", "bf16_dma256x128", "bf16_mfma256x128", "bf16_mfma128x128", "bf16_mfma64x64"},
+        {"f16_dma256x256", "f16_dma256x128", "f16_mfma256x128", "f16_mfma128x128", "f16_mfma64x64"}};
+    const int i = o.dma ? (o.bn == 256 ? 0 : 1) : (o.bm == 256 ? 2 : (o.bm == 128 ? 3 : 4));
     return names[et == kElemF16 ? 1 : 0][i];
 }
 
@@ -354,27 +366,112 @@ hipError_t run_f32_tiles(const Problem& p, hipStream_t stream, gemm_algo_t algo,
 Plan choose_bf16_tiles(const Problem& p, gemm_algo_t algo, int cus) {
     const Launch l = launch_for(p, nullptr);
     const bool dma = bf16_dma_applies(p, l, 256, 256);
-    const StripPricer bf16_strips{kBf16DmaOpts, 2, kBf16MfmaOpts, 4, cus};
+    const StripPricer bf16_strips{kBf16DmaOpts, 2, kBf16MfmaOpts, 3, cus};
     Plan best;
     auto consider = [&](const Plan& pl) { if (pl.cost < best.cost) best = pl; };
     const bool any = algo == GEMM_ALGO_AUTO || algo == GEMM_ALGO_MFMA;
-    if (dma && (any || algo == GEMM_ALGO_MFMA_DMA))
-        for (const TileOpt& o : kBf16DmaOpts) consider(plan_core(p, o, true, true, cus, bf16_strips));
+    if (dma)
+        for (const TileOpt& o : kBf16DmaOpts) {
+            const bool want = any || algo == GEMM_ALGO_MFMA_DMA || (algo == GEMM_ALGO_MFMA_256x256 && o.bn == 256) ||
+                              (algo == GEMM_ALGO_MFMA_256x128 && o.bn == 128);
+            if (want) consider(plan_core(p, o, true, true, cus, bf16_strips));
+        }
     for (const TileOpt& o : kBf16MfmaOpts) {
         // with the direct-copy kernel available, the default choice leaves the 256-row tiles to it
-        const bool want = (any && !(dma && o.bm == 256)) ||
-                          (algo == GEMM_ALGO_MFMA_256x256 && o.bm == 256 && o.bn == 256) ||
-                          (algo == GEMM_ALGO_MFMA_256x128 && o.bm == 256 && o.bn == 128) ||
+        const bool want = (any && !(dma && o.bm == 256)) || (algo == GEMM_ALGO_MFMA_256x128 && o.bm == 256 && !dma) ||
                           (algo == GEMM_ALGO_MFMA_128x128 && o.bm == 128) || (algo == GEMM_ALGO_MFMA_64x64 && o.bm == 64);
         if (want) consider(plan_whole(p, o, cus));
     }
     return best;
 }
 
+// Split-K on the 16-bit direct-copy kernel's 256 x 256 tiles, for problems whose tiles leave
+// CUs idle: S slices of K per tile as a second grid dimension (one round: tiles x S <= CUs),
+// each slice at least kMinSliceK deep; the slabs of slices 1 .. S-1 need (S-1) M N floats of
+// workspace and a second pass adds them to C.  S and the choice against the unsplit kernels come
+// from a time model fitted to measurements (rocprofv3 and HIP events, interleaved with the FP32
+// 4096^3 GEMM as the benchmark runs): per 64-deep k-tile and round, 1.5 us at 256 x 256 and
+// 0.87 us at 256 x 128 with every CU busy, times 0.75 + 0.25 u when only a fraction u of the
+// CUs holds a tile (the clock the power limit allows rises); 2 us per launch; C (or the slabs)
+// written at 5 TB/s; the slab pass 3 us plus (S+1) M N floats at 6 TB/s.  Measured against that:
+// 4096 x 512 x 4096, 4 slices 40.1 us (8: 45.7, unsplit 55.3); 2048 x 2048 x 8192, 4 slices
+// 78.4 us (unsplit 105.6); 1024 x 1024 x 8192, 8 slices 40.6 us (unsplit 88.8); no split where the
+// tiles fill the chip or K is short (2048 x 4096 x 4096: 2 slices 79.8 us, unsplit 67.0).
+struct TileSplit {
+    int slices = 1, kslice = 0;
+    size_t bytes = 0;
+};
+constexpr int kMinSliceK = 512;
+constexpr double kTau256 = 1.5e-6, kTau128 = 0.87e-6, kLaunchSec = 2e-6, kWriteBps = 5e12, kSumSec = 3e-6,
+                 kSumBps = 6e12;
+
+double occupancy_factor(int64_t units, int cus) {
+    const double u = std::min(1.0, (double)units / (cus > 0 ? cus : 256));
+    return 0.75 + 0.25 * u;
+}
+
+// Seconds of the unsplit direct-copy kernel on tiles bm x bn.
+double dma_plain_seconds(const Problem& p, int bn, int cus) {
+    const int64_t c = cus > 0 ? cus : 256, n = tiles(p.M, p.N, 256, bn);
+    const int64_t rounds = (n + c - 1) / c, last = n - (rounds - 1) * c;
+    const double step = (p.K / 64.0) * (bn == 256 ? kTau256 : kTau128);
+    return (rounds - 1) * (kLaunchSec + step) + kLaunchSec + step * occupancy_factor(last, cus) +
+           4.0 * p.M * p.N / kWriteBps;
+}
+
+double split_seconds(const Problem& p, const TileSplit& t, int cus) {
+    const int64_t units = tiles(p.M, p.N, 256, 256) * t.slices;
+    return kLaunchSec + (t.kslice / 64.0) * kTau256 * occupancy_factor(units, cus) + units * 65536.0 * 4 / kWriteBps +
+           kSumSec + (t.slices + 1) * 4.0 * p.M * p.N / kSumBps;
+}
+
+// The best split by the model (slices == 1: none better than the unsplit direct-copy kernel by 5%).
+TileSplit tile_split(const Problem& p, int cus) {
+    TileSplit best;
+    if (!bf16_dma_applies(p, Launch{}, 256, 256)) return best;
+    const int64_t c = cus > 0 ? cus : 256, n = tiles(p.M, p.N, 256, 256);
+    const int64_t most = std::min<int64_t>(c / std::max<int64_t>(n, 1), p.K / kMinSliceK);
+    double best_t = 0.95 * std::min(dma_plain_seconds(p, 256, cus), dma_plain_seconds(p, 128, cus));
+    for (int s = 2; s <= most; ++s) {
+        TileSplit t;
+        t.kslice = (int)(((p.K + s - 1) / s + 63) / 64 * 64);
+        t.slices = (p.K + t.kslice - 1) / t.kslice;
+        if (t.slices != s || p.K - (int64_t)(s - 1) * t.kslice < 64) continue;
+        t.bytes = (size_t)(s - 1) * p.M * p.N * sizeof(float);
+        const double sec = split_seconds(p, t, cus);
+        if (sec < best_t) {
+            best_t = sec;
+            best = t;
+        }
+    }
+    return best;
+}
+
+// The split the default choice takes with this workspace (slices == 1: none).
+TileSplit tile_split_with(const Problem& p, int cus, const Workspace& ws) {
+    if (ws.ptr == nullptr || !aligned(ws.ptr, 16)) return TileSplit{};
+    const TileSplit t = tile_split(p, cus);
+    return t.slices > 1 && t.bytes <= ws.bytes ? t : TileSplit{};
+}
+
 hipError_t run_b16_tiles(const Problem& p, hipStream_t stream, gemm_algo_t algo, int et, const DeviceInfo& dev,
-                         const char*& name, gemm_status_t& st, const Batch& b) {
+                         const char*& name, gemm_status_t& st, const Batch& b, const Workspace& ws = Workspace{}) {
     const Plan best = choose_bf16_tiles(p, algo, dev.cus);
     if (best.cost >= 1e300) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
+    if (algo == GEMM_ALGO_AUTO && b.n == 1) {
+        const TileSplit t = tile_split_with(p, dev.cus, ws);
+        if (t.slices > 1) {
+            SplitProblem sp{};
+            static_cast<Problem&>(sp) = p;
+            sp.kslice = t.kslice;
+            sp.part = static_cast<float*>(ws.ptr);
+            Launch l = launch_for(p, stream);
+            l.vec_c = l.vec_c && p.N % 4 == 0;
+            l.group_m = pick_group_m((p.M + 255) / 256, (p.N + 255) / 256);
+            name = et == kElemF16 ? "f16_dma256x256_splitk" : "bf16_dma256x256_splitk";
+            return launch_bf16_dma_split(sp, t.slices, l, 256, 256, et == kElemF16);
+        }
+    }
     name = b16_name(best.opt, et);
     const TileOpt o = best.opt;
     const bool f16 = et == kElemF16;
@@ -411,14 +508,7 @@ hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, int 
         if (!skinny_applies(p, true)) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
         return run_skinny(p, l, et, dev.cus, name, algo == GEMM_ALGO_AUTO ? ws : Workspace{});
     }
-    if (algo == GEMM_ALGO_MFMA_PINGPONG) {
-        // the ping-pong kernel is a BF16-only rung of the ladder
-        if (et != kElemBf16 || !bf16_pingpong_applies(p, l)) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
-        l.group_m = pick_group_m(p.M / 256, p.N / 256);
-        name = "bf16_pingpong256x256";
-        return launch_bf16_pingpong(p, l);
-    }
-    return run_b16_tiles(p, stream, algo, et, dev, name, st, b);
+    return run_b16_tiles(p, stream, algo, et, dev, name, st, b, ws);
 }
 
 // The problem the library computes for extents and orders with tight leading dimensions and
@@ -433,9 +523,13 @@ Problem query_problem(int64_t M, int64_t N, int64_t K, int oa, int ob, int oc) {
 // Workspace bytes with which the _ws entry points split K (0: they never do for this problem).
 size_t split_bytes(const Problem& p, int et, int cus) {
     if (p.M == 0 || p.N == 0 || p.K == 0) return 0;
-    if (!(prefer_small(p, cus) && skinny_applies(p, et != kElemF32))) return 0;
-    const SkinnySplit sp = skinny_split(p, et != kElemF32, cus);
-    return sp.slices > 1 ? sp.bytes : 0;
+    if (prefer_small(p, cus) && skinny_applies(p, et != kElemF32)) {
+        const SkinnySplit sp = skinny_split(p, et != kElemF32, cus);
+        return sp.slices > 1 ? sp.bytes : 0;
+    }
+    if (et == kElemF32) return 0;
+    const TileSplit t = tile_split(p, cus);
+    return t.slices > 1 ? t.bytes : 0;
 }
 
 // What the default choice runs for a normalised problem with K > 0, without launching: the
@@ -469,7 +563,7 @@ gemm_status_t run(In in, gemm_algo_t algo, int64_t M, int64_t N, int64_t K, cons
         case GEMM_ALGO_MFMA_128x128: case GEMM_ALGO_MFMA_64x64: case GEMM_ALGO_SKINNY: break;
         case GEMM_ALGO_MFMA_DMA: break;
         case GEMM_ALGO_MFMA_256x256: break;
-        case GEMM_ALGO_MFMA_256x128: case GEMM_ALGO_MFMA_PINGPONG:
+        case GEMM_ALGO_MFMA_256x128:
             if (f32) return GEMM_ERR_INVALID_VALUE;
             break;
         default: return GEMM_ERR_INVALID_VALUE;

@@ -103,15 +103,17 @@ struct Cfg {
 
 using Cfg256 = Cfg<256, 256, 2, 2, 2, 2, true>;
 
-// EPI: the fused-epilogue instantiation (an EpiProblem; not batched).
-template <typename C, bool VEC_C, bool F16 = false, bool BATCH = false, bool EPI = false>
+// MODE: kPlain, kBatched (entry blockIdx.z of a strided batch), kEpilogue (the fused epilogue,
+// one problem) or kSplitK (K slice blockIdx.y of one problem).
+template <typename C, bool VEC_C, bool F16, int MODE>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::NW / 4, C::NW / 4)))
-void k_bf16_dma(std::conditional_t<EPI, EpiProblem, KArg<BATCH>> p, int tiles_m, int tiles_n, int group_m) {
-    static_assert(!(EPI && BATCH), "the epilogue instantiation takes one problem");
+void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int group_m) {
+    constexpr bool BATCH = MODE == kBatched, EPI = MODE == kEpilogue;
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, FM = C::FM, FN = C::FN, SUB = C::SUB;
     constexpr int ROW = C::ROW, MF = C::MF;
     __shared__ __align__(16) unsigned char smem[C::LDS];
     if constexpr (BATCH) p.select(blockIdx.z);
+    if constexpr (MODE == kSplitK) p.select(blockIdx.y, 2);
 
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
@@ -456,40 +458,26 @@ void k_bf16_dma(std::conditional_t<EPI, EpiProblem, KArg<BATCH>> p, int tiles_m,
     }
 }
 
-template <typename C, bool BATCH>
-hipError_t launch_cfg(const KArg<BATCH>& p, const Launch& l, bool f16) {
+// One launch of configuration C in mode MODE: tiles along x, grid_y K slices, grid_z batch entries.
+template <typename C, int MODE>
+hipError_t launch_cfg(const typename ModeArgT<MODE>::type& p, const Launch& l, bool f16, int grid_y = 1) {
     const int tiles_m = (p.M + C::BM - 1) / C::BM, tiles_n = (p.N + C::BN - 1) / C::BN;
-    const dim3 grid((unsigned)tiles_m * tiles_n, 1, BATCH ? l.batch : 1), block(C::THREADS);
+    const dim3 grid((unsigned)tiles_m * tiles_n, (unsigned)grid_y, MODE == kBatched ? l.batch : 1), block(C::THREADS);
     if (f16 && l.vec_c)
-        hipLaunchKernelGGL((k_bf16_dma<C, true, true, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
+        hipLaunchKernelGGL((k_bf16_dma<C, true, true, MODE>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
     else if (f16)
-        hipLaunchKernelGGL((k_bf16_dma<C, false, true, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
+        hipLaunchKernelGGL((k_bf16_dma<C, false, true, MODE>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
     else if (l.vec_c)
-        hipLaunchKernelGGL((k_bf16_dma<C, true, false, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
+        hipLaunchKernelGGL((k_bf16_dma<C, true, false, MODE>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
     else
-        hipLaunchKernelGGL((k_bf16_dma<C, false, false, BATCH>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
+        hipLaunchKernelGGL((k_bf16_dma<C, false, false, MODE>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
     return hipGetLastError();
 }
 
 template <typename C>
 hipError_t launch_any(const Problem& p, const Launch& l, bool f16) {
-    if (l.batch > 1) return launch_cfg<C, true>(batch_arg(p, l, 2), l, f16);
-    return launch_cfg<C, false>(p, l, f16);
-}
-
-template <typename C>
-hipError_t launch_epi(const EpiProblem& p, const Launch& l, bool f16) {
-    const int tiles_m = (p.M + C::BM - 1) / C::BM, tiles_n = (p.N + C::BN - 1) / C::BN;
-    const dim3 grid((unsigned)tiles_m * tiles_n), block(C::THREADS);
-    if (f16 && l.vec_c)
-        hipLaunchKernelGGL((k_bf16_dma<C, true, true, false, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
-    else if (f16)
-        hipLaunchKernelGGL((k_bf16_dma<C, false, true, false, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
-    else if (l.vec_c)
-        hipLaunchKernelGGL((k_bf16_dma<C, true, false, false, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
-    else
-        hipLaunchKernelGGL((k_bf16_dma<C, false, false, false, true>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
-    return hipGetLastError();
+    if (l.batch > 1) return launch_cfg<C, kBatched>(batch_arg(p, l, 2), l, f16);
+    return launch_cfg<C, kPlain>(p, l, f16);
 }
 
 }  // namespace
@@ -517,9 +505,19 @@ hipError_t launch_bf16_dma(const Problem& p, const Launch& l, int bm, int bn, bo
 }
 
 hipError_t launch_bf16_dma_epi(const EpiProblem& p, const Launch& l, int bm, int bn, bool f16) {
-    if (bm == 256 && bn == 256) return launch_epi<Cfg256>(p, l, f16);
-    if (bm == 256 && bn == 128) return launch_epi<Cfg<256, 128, 4, 2, 4, 3>>(p, l, f16);
+    if (bm == 256 && bn == 256) return launch_cfg<Cfg256, kEpilogue>(p, l, f16);
+    if (bm == 256 && bn == 128) return launch_cfg<Cfg<256, 128, 4, 2, 4, 3>, kEpilogue>(p, l, f16);
     return hipErrorInvalidValue;
+}
+
+// Split-K: s.part holds the slabs of slices 1 .. S-1 (16-byte aligned; l.vec_c also covers their
+// rows, N % 4 == 0), then the slabs are added to C in slice order.
+hipError_t launch_bf16_dma_split(const SplitProblem& s, int slices, const Launch& l, int bm, int bn, bool f16) {
+    hipError_t err = hipErrorInvalidValue;
+    if (bm == 256 && bn == 256) err = launch_cfg<Cfg256, kSplitK>(s, l, f16, slices);
+    else if (bm == 256 && bn == 128) err = launch_cfg<Cfg<256, 128, 4, 2, 4, 3>, kSplitK>(s, l, f16, slices);
+    if (err != hipSuccess) return err;
+    return launch_add_slabs(s.C, s.ldc, s.M, s.N, s.part, slices - 1, l);
 }
 
 }  // namespace gemm

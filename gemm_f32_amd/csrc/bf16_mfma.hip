@@ -6,7 +6,7 @@
 // (GEMM)", "Matrix cores: MFMA and Tensor Cores").  Those kernels were written for other
 // hardware; this one is laid out for gfx950:
 //
-//  * Block tile BM x BN (256 x 256, 256 x 128, 128 x 128 or 64 x 64) swept in BK = 32 or
+//  * Block tile BM x BN (256 x 128, 128 x 128 or 64 x 64) swept in BK = 32 or
 //    64 slices, 4 wavefronts in a 2 x 2 grid.  A wavefront owns (BM/2) x (BN/2) of C as
 //    32 x 32 fragments; at 256 x 256 that is 4 x 4 fragments = 256 FP32 accumulators
 //    per lane, which the compiler keeps in the accumulation registers.  Large tiles are
@@ -422,7 +422,6 @@ hipError_t launch_tile(const Problem& p, const Launch& l, bool f16) {
 
 // Tile configurations: block tile, k-tile depth and LDS stages.
 hipError_t launch_bf16_mfma(const Problem& p, const Launch& l, int bm, int bn, bool f16) {
-    if (bm == 256 && bn == 256) return launch_tile<256, 256, 64, 2>(p, l, f16);   // 128 KB LDS
     if (bm == 256 && bn == 128) return launch_tile<256, 128, 64, 3>(p, l, f16);   // 144 KB
     if (bm == 128 && bn == 128) return launch_tile<128, 128, 64, 2>(p, l, f16);   //  64 KB
     if (bm == 64 && bn == 64) return launch_tile<64, 64, 64, 2>(p, l, f16);       //  32 KB

@@ -41,6 +41,32 @@ struct BatchProblem : Problem {
 };
 template <bool BATCH> using KArg = std::conditional_t<BATCH, BatchProblem, Problem>;
 
+// One problem with K split across workgroups ("A06 - Tiled Matrix Multiply (GEMM)", "The next
+// two rungs": split-K, each worker sums part of K and a second step adds the partial sums).
+// Slice z (blockIdx.y) takes k in [z kslice, min(K, (z+1) kslice)); slice 0 writes C, slice
+// z >= 1 the dense M x N slab part + (z-1) M N (leading dimension N), which a second kernel adds
+// to C in slice order.
+struct SplitProblem : Problem {
+    int kslice;
+    float* part;
+    __device__ __forceinline__ void select(int z, int elem_bytes) {
+        const int64_t k0 = (int64_t)z * kslice;
+        A = static_cast<const char*>(A) + (oa == kRow ? k0 : k0 * lda) * elem_bytes;
+        B = static_cast<const char*>(B) + (ob == kCol ? k0 : k0 * ldb) * elem_bytes;
+        K = (int)(K - k0 < kslice ? K - k0 : kslice);
+        if (z > 0) {
+            C = part + (int64_t)(z - 1) * M * N;
+            ldc = N;
+        }
+    }
+};
+
+// Instantiation kinds of a tile kernel and the argument each takes.
+enum KernelMode : int { kPlain = 0, kBatched = 1, kEpilogue = 2, kSplitK = 3 };
+template <int MODE> struct ModeArgT { using type = Problem; };
+template <> struct ModeArgT<kBatched> { using type = BatchProblem; };
+template <> struct ModeArgT<kSplitK> { using type = SplitProblem; };
+
 // Offset of logical element (r, c) in an operand with leading dimension ld and order o.
 __device__ __forceinline__ int64_t elem_offset(int64_t r, int64_t c, int64_t ld, int o) {
     return o == kRow ? r * ld + c : r + c * ld;
@@ -64,8 +90,15 @@ __device__ __forceinline__ int64_t elem_offset(int64_t r, int64_t c, int64_t ld,
 // ---------------------------------------------------------------------------------------
 constexpr int kNumXcds = 8;
 
+// group_m <= 0 turns both remaps off (tiles in plain row-major order of workgroup ids), for
+// measuring what they are worth.
 __host__ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n,
                                                      int group_m, int& tile_m, int& tile_n) {
+    if (group_m <= 0) {
+        tile_m = wg / tiles_n;
+        tile_n = wg % tiles_n;
+        return;
+    }
     const int total = tiles_m * tiles_n;
     const int per_xcd = total / kNumXcds;
     int id = wg;

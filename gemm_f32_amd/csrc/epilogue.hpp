@@ -24,6 +24,7 @@ struct Epilogue {
 struct EpiProblem : Problem {
     Epilogue e;
 };
+template <> struct ModeArgT<kEpilogue> { using type = EpiProblem; };
 
 // C's previous value at element offset off, as FP32.
 __device__ __forceinline__ float epi_load(const Epilogue& e, const void* C, int64_t off) {

@@ -29,7 +29,47 @@ __global__ __launch_bounds__(256) void k_epi_fill(EpiProblem p) {
     }
 }
 
+// The second step of split-K: C += slab 0 + slab 1 + ... + slab S-1, added in that order (every
+// call sums the same way, so results are identical from call to call).  The slabs are dense
+// M x N; four columns per thread, 16-byte accesses when C's rows allow them (vec).
+__global__ __launch_bounds__(256) void k_add_slabs(float* C, int64_t ldc, int M, int N, const float* part, int S,
+                                                   int vec) {
+    const int64_t groups = (N + 3) / 4, total = (int64_t)M * groups, slab = (int64_t)M * N;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+        const int r = (int)(t / groups), c = 4 * (int)(t % groups);
+        const int64_t off = (int64_t)r * N + c;
+        float* dst = C + (int64_t)r * ldc + c;
+        if (vec && c + 3 < N) {
+            float4 acc = *reinterpret_cast<const float4*>(dst);
+            for (int z = 0; z < S; ++z) {
+                const float4 v = *reinterpret_cast<const float4*>(part + z * slab + off);
+                acc.x += v.x;
+                acc.y += v.y;
+                acc.z += v.z;
+                acc.w += v.w;
+            }
+            *reinterpret_cast<float4*>(dst) = acc;
+        } else {
+            for (int e = 0; e < 4 && c + e < N; ++e) {
+                float acc = dst[e];
+                for (int z = 0; z < S; ++z) acc += part[z * slab + off + e];
+                dst[e] = acc;
+            }
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_add_slabs(float* C, int64_t ldc, int M, int N, const float* part, int slabs, const Launch& l) {
+    if (slabs <= 0 || M == 0 || N == 0) return hipSuccess;
+    const int64_t total = (int64_t)M * ((N + 3) / 4);
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    const int vec = l.vec_c && (N % 4) == 0;
+    hipLaunchKernelGGL(k_add_slabs, dim3((unsigned)blocks), dim3(256), 0, l.stream, C, ldc, M, N, part, slabs, vec);
+    return hipGetLastError();
+}
 
 hipError_t launch_epi_fill(const EpiProblem& p, const Launch& l) {
     const int64_t total = (int64_t)p.M * p.N;

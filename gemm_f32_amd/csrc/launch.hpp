@@ -27,13 +27,9 @@ constexpr int kElemF32 = 0, kElemBf16 = 1, kElemF16 = 2;
 // f16 the same kernel on IEEE fp16 inputs.
 bool bf16_dma_applies(const Problem& p, const Launch& l, int bm, int bn);
 hipError_t launch_bf16_dma(const Problem& p, const Launch& l, int bm, int bn, bool f16 = false);
-// BF16 matrix-core kernel (bf16_mfma.hip); tile is one of 256x256, 256x128, 128x128, 64x64;
+// BF16 matrix-core kernel (bf16_mfma.hip); tile is one of 256x128, 128x128, 64x64;
 // f16: fp16 inputs
 hipError_t launch_bf16_mfma(const Problem& p, const Launch& l, int bm, int bn, bool f16 = false);
-// BF16 256 x 256 eight-wavefront ping-pong kernel (bf16_pingpong.hip), for row-major A,
-// column-major B, aligned, M and N multiples of 256, K a multiple of 32
-bool bf16_pingpong_applies(const Problem& p, const Launch& l);
-hipError_t launch_bf16_pingpong(const Problem& p, const Launch& l);
 // Small-problem kernel (skinny.hip): 64 x 16 blocks of C with K split over the workgroup;
 // row-major A, B column-major for BF16 or either order for FP32.  AUTO uses it for
 // M <= kSkinnyMaxM or when 64 x 64 tiles would not fill half the chip.
@@ -67,6 +63,11 @@ hipError_t launch_zero_c(const Problem& p, const Launch& l);
 // and the epilogue of an empty sum for K == 0 (fill.hip)
 hipError_t launch_bf16_dma_epi(const EpiProblem& p, const Launch& l, int bm, int bn, bool f16);
 hipError_t launch_epi_fill(const EpiProblem& p, const Launch& l);
+// Split-K on the 16-bit direct-copy kernel (same requirements as launch_bf16_dma, every slice
+// K >= 64): `slices` K slices of s.kslice as a second grid dimension, slices 1 .. S-1 into the
+// slabs at s.part, then launch_add_slabs (fill.hip) adds them to C in slice order.
+hipError_t launch_bf16_dma_split(const SplitProblem& s, int slices, const Launch& l, int bm, int bn, bool f16);
+hipError_t launch_add_slabs(float* C, int64_t ldc, int M, int N, const float* part, int slabs, const Launch& l);
 
 // Block-tile sizes, exported for the host's scheduler choices.
 constexpr int kRegblockBM = 128, kRegblockBN = 128;

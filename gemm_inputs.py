@@ -62,6 +62,10 @@ WORKLOADS = {
         Workload("llm_attn_proj_2048x4096x4096", 5, 2048, 4096, 4096, "bf16", ROW_MAJOR, COL_MAJOR, ROW_MAJOR, "llm"),
         Workload("llm_ffn_up_2048x11008x4096", 5, 2048, 11008, 4096, "bf16", ROW_MAJOR, COL_MAJOR, ROW_MAJOR, "llm"),
         Workload("llm_ffn_down_2048x4096x11008", 5, 2048, 4096, 11008, "bf16", ROW_MAJOR, COL_MAJOR, ROW_MAJOR, "llm"),
+        # one GPU's share of the 4096^3 GEMMs with B and C split by columns over eight GPUs
+        # (A replicated): 32 tiles of 256 x 256 for 256 CUs
+        Workload("shard4096x512x4096_f32", 8, 4096, 512, 4096, "f32"),
+        Workload("shard4096x512x4096_bf16", 8, 4096, 512, 4096, "bf16", ROW_MAJOR, COL_MAJOR),
         # few columns of C and a long K: too few output blocks for the CUs (split-K's case)
         Workload("fewcols16x1024x16384_f32", 6, 16, 1024, 16384, "f32"),
         Workload("fewcols16x1024x16384_bf16", 6, 16, 1024, 16384, "bf16", ROW_MAJOR, COL_MAJOR),

@@ -21,9 +21,12 @@
  * tiled kernel, and what each line is protecting").
  *
  * Ownership.  All matrix pointers are device pointers owned by the caller; A and B are
- * only read, C is only written, and C must not overlap A or B.  Pointers need only their
- * element's natural alignment (4 bytes for float, 2 for bf16); no kernel needs more.  The library
- * allocates no device memory and keeps no state beyond a per-device property cache.
+ * only read and must not overlap C.  C is only written, except by the fused-epilogue calls
+ * with beta != 0, which read C's previous contents first.  Pointers need only their element's
+ * natural alignment (4 bytes for float, 2 for bf16/fp16); no kernel needs more.  The plain
+ * calls allocate no device memory and keep no state beyond a per-device property cache; the
+ * _ws calls use the caller's workspace, and gemm_bf16_f32acc_noalloc a static array of the
+ * library's (both below).
  *
  * Streams and errors.  Work is enqueued on `stream` (0 = the null stream) of the
  * current device and the call returns without waiting for it.  Argument errors are
@@ -69,41 +72,45 @@ typedef enum {
  *   TILED              32 x 32 tiles staged in LDS, one output per thread ("Level 1");
  *   REGBLOCK           128 x 128 block tiles, 8 x 8 outputs per thread on the vector
  *                      ALUs, double-buffered LDS ("Level 2"; "GEMM Optimization", V2/V3);
- *   MFMA               matrix-core kernel: v_mfma_f32_32x32x2_f32 for FP32 inputs,
- *                      v_mfma_f32_32x32x16_bf16 for BF16 inputs, FP32 accumulate
- *                      ("A06 - Tiled Matrix Multiply (GEMM)", "Matrix cores: MFMA and
- *                      Tensor Cores"); tile shape picked from the problem;
+ *   MFMA               the matrix-core kernels only (AUTO without the small-problem kernel),
+ *                      tile and kernel picked by the same cost model as AUTO ("A06 - Tiled
+ *                      Matrix Multiply (GEMM)", "Matrix cores: MFMA and Tensor Cores").  FP32:
+ *                      the direct-copy kernel (v_mfma_f32_16x16x4_f32, MFMA_DMA below)
+ *                      wherever it applies, else the register-staged kernel
+ *                      (v_mfma_f32_32x32x2_f32, 128 x 128 or 64 x 64 tiles, any layout).  BF16 /
+ *                      FP16: the direct-copy kernel (v_mfma_f32_32x32x16_bf16 / _f16) for
+ *                      row-major A with column-major B and K >= 64, else the register-staged
+ *                      kernel (128 x 128, 64 x 64 or 256 x 128 tiles, any layout);
  *   MFMA_256x256, MFMA_256x128, MFMA_128x128, MFMA_64x64
- *                      the MFMA kernel with that block tile forced.  FP32: 128x128 and
- *                      64x64 select the register-staged v_mfma_f32_32x32x2_f32 kernel,
- *                      256x256 the direct-copy kernel below (same requirements, with
- *                      M, N >= 256); 256x128 is BF16 only;
- *   MFMA_PINGPONG      BF16 only: the 256 x 256 kernel with eight wavefronts in two groups
- *                      that alternate matrix-instruction and memory phases; needs row-major
- *                      A and column-major B (C may have either order), M and N multiples
- *                      of 256 and K a multiple of 32, else GEMM_ERR_INVALID_VALUE.
+ *                      a block tile forced.  256x256: the direct-copy kernel at 256 x 256 (its
+ *                      requirements below; GEMM_ERR_INVALID_VALUE otherwise).  256x128 (16-bit
+ *                      inputs only): the direct-copy kernel at 256 x 128 where it applies, else
+ *                      the register-staged kernel.  128x128, 64x64: the register-staged kernel;
  *   SKINNY             the small-problem kernel ("How a Matrix Multiply Runs on a GPU",
  *                      "Shapes that run slowly, and why": few rows make the product bound
- *                      by reading B; few tiles leave the chip idle): 64 x 16 blocks of C per
- *                      workgroup, K split over its wavefronts, partial sums added in a fixed
- *                      order; needs row-major A, and for BF16 a column-major B (with a
- *                      column-major C the roles of M/N and A/B swap, C^T = B^T A^T), else
- *                      GEMM_ERR_INVALID_VALUE.  AUTO uses it when it applies and M <= 64 or
- *                      64 x 64 tiles would fill less than half of the CUs.
+ *                      by reading B; few tiles leave the chip idle): 64 x 16 or 64 x 64 blocks
+ *                      of C per workgroup, K split over its eight wavefronts, partial sums added
+ *                      in a fixed order; needs row-major A, and for 16-bit inputs a column-major
+ *                      B (with a column-major C the roles of M/N and A/B swap, C^T = B^T A^T),
+ *                      else GEMM_ERR_INVALID_VALUE.  AUTO uses it when it applies and M <= 64
+ *                      or 64 x 64 tiles would fill less than half of the CUs;
  *   MFMA_DMA           the direct-copy kernels: operands copied global -> LDS as laid out in
- *                      memory, no register staging ("GEMM Optimization", V3 staging), tile
- *                      picked from the shape.  FP32: v_mfma_f32_16x16x4_f32, 256 x 256 tiles
- *                      (eight wavefronts) or 128 x 128 (four); needs K >= 32 and
- *                      M, N >= 128.  BF16: v_mfma_f32_32x32x16_bf16, 256 x 256 or
- *                      256 x 128 tiles of four wavefronts; needs row-major A and column-major
- *                      B, K a multiple of 64, M >= 256 and N >= 128.  Conditions apply after the
- *                      column-major-C swap; otherwise GEMM_ERR_INVALID_VALUE.  Partial tiles
- *                      along the bottom and right edges run on the register-staged kernels
- *                      in the same call.  AUTO uses the FP32 one whenever it applies and
- *                      the cost model picks its tile sizes; for BF16 AUTO keeps the MFMA
- *                      kernel above (measured as fast or faster on the BF16 workloads).
- * The FP32 entry point accepts every algorithm but MFMA_256x128 and MFMA_PINGPONG; the
- * BF16 entry point only AUTO, the MFMA ones and SKINNY (others give GEMM_ERR_INVALID_VALUE).
+ *                      memory by buffer loads straight into LDS, no register staging ("GEMM
+ *                      Optimization", V3 staging), tile picked by the cost model.  FP32:
+ *                      v_mfma_f32_16x16x4_f32, 256 x 256 tiles of eight wavefronts or 128 x 128
+ *                      of four; needs K >= 32 and M, N at least the tile; tiles may overhang
+ *                      the edge along a k-contiguous operand, other remainders run as strips on
+ *                      the register-staged kernel in the same call.  16-bit inputs:
+ *                      v_mfma_f32_32x32x16, 256 x 256 tiles of four wavefronts (128 x 128 each,
+ *                      a ring of five half-stage LDS buffers) or 256 x 128 of eight (64 x 64
+ *                      each, three stages); needs row-major A, column-major B and K >= 64, any
+ *                      M and N (tiles overhang both edges; rows past M or N read as zero).
+ *                      Conditions apply after the column-major-C swap; otherwise
+ *                      GEMM_ERR_INVALID_VALUE.  AUTO picks these kernels wherever they apply and
+ *                      the cost model prefers them (every workload of the benchmark suite).
+ * The FP32 entry point accepts every algorithm but MFMA_256x128; the 16-bit entry points only
+ * AUTO, the MFMA ones and SKINNY (others give GEMM_ERR_INVALID_VALUE).  The value 10 is unused
+ * (it named a ping-pong kernel that was slower than the direct-copy kernel and was removed).
  */
 typedef enum {
     GEMM_ALGO_AUTO = 0,
@@ -116,7 +123,6 @@ typedef enum {
     GEMM_ALGO_MFMA_256x128 = 7,
     GEMM_ALGO_MFMA_128x128 = 8,
     GEMM_ALGO_MFMA_64x64 = 9,
-    GEMM_ALGO_MFMA_PINGPONG = 10,
     GEMM_ALGO_SKINNY = 11,
     GEMM_ALGO_MFMA_DMA = 12
 } gemm_algo_t;
@@ -163,8 +169,7 @@ gemm_status_t gemm_bf16_f32acc_algo(gemm_algo_t algo, int64_t M, int64_t N, int6
                                     float *C, int64_t ldc, gemm_order_t order_c,
                                     hipStream_t stream);
 
-/* As gemm_f16_f32acc, with the kernel forced (AUTO or one of the MFMA values except
- * GEMM_ALGO_MFMA_PINGPONG). */
+/* As gemm_f16_f32acc, with the kernel forced (AUTO, one of the MFMA values or SKINNY). */
 gemm_status_t gemm_f16_f32acc_algo(gemm_algo_t algo, int64_t M, int64_t N, int64_t K,
                                    const uint16_t *A, int64_t lda, gemm_order_t order_a,
                                    const uint16_t *B, int64_t ldb, gemm_order_t order_b,

@@ -128,7 +128,7 @@ SCHED_CHECK = r"""
 // receives (w % 8 equal) cover tiles that share few row/column panels.
 int main() {
     const int shapes[][3] = {{16,16,4},{16,16,1},{1,1,1},{3,5,2},{8,43,4},{16,86,8},{33,17,4},
-                             {1,64,1},{7,9,8},{32,32,4},{2,344,2}};
+                             {1,64,1},{7,9,8},{32,32,4},{2,344,2},{16,16,0},{3,5,0}};
     for (auto& s : shapes) {
         const int tm_ = s[0], tn_ = s[1], gm = s[2];
         std::vector<int> seen(tm_ * tn_, 0);
@@ -149,6 +149,12 @@ int main() {
             cmin = b < cmin ? b : cmin; cmax = b > cmax ? b : cmax;
         }
         if (rmax - rmin != 3 || cmax - cmin != 7) { printf("xcd %d block %d x %d\n", x, rmax-rmin+1, cmax-cmin+1); return 1; }
+    }
+    // group_m 0: both remaps off, tiles in row-major order of the workgroup id
+    for (int w = 0; w < 15; ++w) {
+        int a, b;
+        gemm::tile_coords(w, 3, 5, 0, a, b);
+        if (a != w / 5 || b != w % 5) { printf("plain order %d\n", w); return 1; }
     }
     printf("ok\n");
     return 0;
@@ -171,7 +177,7 @@ def test_tile_scheduler_is_a_bijection_with_xcd_blocks():
 # --- the default kernel choice, without a device (gemm_plan) -----------------------------
 KNOWN_KERNELS = {"f32_dma256x256", "f32_dma128x128", "f32_mfma128x128", "f32_mfma64x64",
                  "f32_skinny16", "f32_skinny64", "bf16_dma256x256", "bf16_dma256x128",
-                 "bf16_mfma256x256", "bf16_mfma256x128", "bf16_mfma128x128", "bf16_mfma64x64",
+                 "bf16_mfma256x128", "bf16_mfma128x128", "bf16_mfma64x64",
                  "bf16_skinny16", "bf16_skinny64", "zero_c", "none"}
 
 
@@ -250,6 +256,15 @@ def test_plan_invariants_on_random_shapes():
     ("f32", (16, 1024, 500), (R, R, R), 0),
     # column-major C: C^T has the few rows
     ("f32", (1024, 16, 16384), (C_, C_, C_), 16 * 16 * 1024 * 4),
+    # 16-bit inputs on 256 x 256 tiles that leave CUs idle: one GPU's column shard of 4096^3 in
+    # 5 K slices, 2048^2 x 8192 in 4 (slices 1 .. S-1 as M x N FP32 slabs); none where the
+    # tiles fill the chip or where the unsplit 256 x 128 kernel is estimated as fast
+    ("bf16", (4096, 512, 4096), (R, C_, R), 4 * 4096 * 512 * 4),
+    ("bf16", (2048, 2048, 8192), (R, C_, R), 3 * 2048 * 2048 * 4),
+    ("bf16", (4096, 4096, 4096), (R, C_, R), 0),
+    ("bf16", (2048, 4096, 4096), (R, C_, R), 0),
+    ("bf16", (2048, 4096, 11008), (R, C_, R), 0),
+    ("f32", (4096, 512, 4096), (R, R, R), 0),
 ], ids=lambda v: str(v))
 def test_split_k_workspace_of_known_shapes(dtype, shape, orders, expected):
     assert g.gemm_plan(dtype, *shape, *orders, with_workspace=True)[3] == expected

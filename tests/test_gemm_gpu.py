@@ -11,14 +11,13 @@ import gemm_f32_amd as g
 import gemm_inputs as gi
 import oracle
 from gemm_inputs import COL_MAJOR, ROW_MAJOR
-from gpu_util import TOL, check, logical_c, padding_untouched, run, to_device
+from gpu_util import TOL, check, logical_c, padding_untouched, reference, run, to_device
 
 pytestmark = pytest.mark.gpu
 
 F32_ALGOS = [g.Algo.NAIVE_UNCOALESCED, g.Algo.NAIVE, g.Algo.TILED, g.Algo.REGBLOCK,
              g.Algo.MFMA_128x128, g.Algo.MFMA_64x64, g.Algo.AUTO]
-BF16_ALGOS = [g.Algo.MFMA_256x256, g.Algo.MFMA_256x128, g.Algo.MFMA_128x128,
-              g.Algo.MFMA_64x64, g.Algo.AUTO]
+BF16_ALGOS = [g.Algo.MFMA_256x128, g.Algo.MFMA_128x128, g.Algo.MFMA_64x64, g.Algo.AUTO]
 CASES = [("f32", a) for a in F32_ALGOS] + [("bf16", a) for a in BF16_ALGOS]
 CASE_IDS = [f"{d}-{a.name}" for d, a in CASES]
 ORDERS3 = [(a, b, c) for a in (ROW_MAJOR, COL_MAJOR) for b in (ROW_MAJOR, COL_MAJOR)
@@ -163,58 +162,6 @@ def test_matmul_helper_on_tensors_and_views():
     out = g.matmul(ah, bh.t().contiguous().t())
     assert oracle.normalised_error(out.cpu().numpy(), refh, Dh) <= TOL["f16"]
     assert g.gemm_last_kernel().startswith("f16_")
-
-
-# --- the eight-wavefront ping-pong kernel (row-major A, column-major B, 256-multiples) ---
-PP_SHAPES = [(256, 256, 32), (256, 256, 64), (512, 768, 96), (256, 512, 4096), (768, 256, 160),
-             (1024, 1024, 1024)]
-
-
-@pytest.mark.parametrize("shape", PP_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_pingpong_random(shape):
-    M, N, K = shape
-    p = gi.make_problem(M, N, K, "bf16", ROW_MAJOR, COL_MAJOR, wid=45)
-    check(p, g.Algo.MFMA_PINGPONG)
-    assert g.gemm_last_kernel() == "bf16_pingpong256x256"
-
-
-@pytest.mark.parametrize("shape", [(256, 256, 32), (512, 256, 224), (256, 768, 1024)],
-                         ids=lambda s: "x".join(map(str, s)))
-def test_pingpong_small_integer_exact(shape):
-    M, N, K = shape
-    rng = np.random.default_rng(K)
-    A = rng.integers(-4, 5, (M, K)).astype(np.float32)
-    B = rng.integers(-4, 5, (K, N)).astype(np.float32)
-    check(gi.make_problem(M, N, K, "bf16", ROW_MAJOR, COL_MAJOR, A_logical=A, B_logical=B),
-          g.Algo.MFMA_PINGPONG, exact=True)
-
-
-def test_pingpong_closed_forms():
-    n = 256
-    ident = gi.make_problem(n, n, n, "bf16", ROW_MAJOR, COL_MAJOR, wid=46, A_logical=np.eye(n))
-    assert np.array_equal(logical_c(ident, run(ident, g.Algo.MFMA_PINGPONG)), ident.b_f32())
-    perm = np.random.default_rng(3).permutation(n)
-    P = np.zeros((n, n)); P[np.arange(n), perm] = 1.0
-    pb = gi.make_problem(n, n, n, "bf16", ROW_MAJOR, COL_MAJOR, wid=47, B_logical=P)
-    assert np.array_equal(logical_c(pb, run(pb, g.Algo.MFMA_PINGPONG)), pb.a_f32()[:, np.argsort(perm)])
-
-
-def test_pingpong_column_major_c():
-    # C^T = B^T A^T: with a column-major C the kernel sees B^T (row-major, from a column-major
-    # B) and A^T (column-major, from a row-major A): the same operand layout it needs
-    p = gi.make_problem(512, 256, 128, "bf16", ROW_MAJOR, COL_MAJOR, COL_MAJOR, wid=48)
-    check(p, g.Algo.MFMA_PINGPONG)
-
-
-@pytest.mark.parametrize("bad", [dict(M=300), dict(K=48), dict(order_b=ROW_MAJOR)],
-                         ids=lambda d: str(d))
-def test_pingpong_rejects_unsupported_shapes(bad):
-    kw = dict(M=256, N=256, K=64, dtype="bf16", order_a=ROW_MAJOR, order_b=COL_MAJOR)
-    kw.update(bad)
-    p = gi.make_problem(**kw)
-    with pytest.raises(g.GemmError) as e:
-        run(p, g.Algo.MFMA_PINGPONG)
-    assert e.value.status == g.Status.ERR_INVALID_VALUE
 
 
 # --- the small-problem kernel (row-major A; B column-major for BF16) ---------------------
@@ -549,8 +496,8 @@ def test_bf16_direct_unaligned_rows(oc, pad):
     p = gi.make_problem(512, 384, 192, "bf16", ROW_MAJOR, COL_MAJOR, oc, wid=58, pad_a=pad, pad_b=pad, pad_c=pad)
     check(p, g.Algo.MFMA_DMA)
     assert g.gemm_last_kernel().startswith("bf16_dma")
-    check(p, g.Algo.MFMA_256x256)      # bf16_mfma.hip's direct path
-    assert g.gemm_last_kernel() == "bf16_mfma256x256"
+    check(p, g.Algo.MFMA_256x256)      # the direct-copy kernel's 256 x 256 ring
+    assert g.gemm_last_kernel() == "bf16_dma256x256"
 
 
 # --- split-K across workgroups with a caller's workspace (gemm_*_ws) ----------------------
@@ -601,6 +548,53 @@ def test_split_k_with_workspace(dtype, ob, shape, oc):
     assert err <= TOL[dtype], err
     again, _, _ = run_ws(p)
     assert np.array_equal(flat.view(np.uint32), again.view(np.uint32)), "not deterministic"
+
+
+# --- split-K on the 16-bit direct-copy kernel's 256 x 256 tiles (few tiles, long K) --------
+# (M, N, K, order of C): the default choice with a workspace splits each of these (5 to 8
+# slices; K = 3000 and 4999 leave a ragged K tail in the last slice; ragged M and N overhang)
+TILE_SPLIT_CASES = [(1000, 1025, 3000, ROW_MAJOR), (1500, 700, 4999, COL_MAJOR), (2048, 1024, 4096, ROW_MAJOR),
+                    (4096, 512, 4096, ROW_MAJOR)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("case", TILE_SPLIT_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_tile_split_k_with_workspace(dtype, case):
+    M, N, K, oc = case
+    p = gi.make_problem(M, N, K, dtype, ROW_MAJOR, COL_MAJOR, oc, wid=64, pad_c=3)
+    flat, need, kernel = run_ws(p)
+    assert need > 0 and kernel == f"{dtype}_dma256x256_splitk", (need, kernel)
+    assert padding_untouched(p, flat)
+    ref, D = reference(p, key=("tilesplit", dtype, case))
+    err = oracle.normalised_error(logical_c(p, flat), ref, D)
+    assert err <= TOL[dtype], err
+    again, _, _ = run_ws(p)
+    assert np.array_equal(flat.view(np.uint32), again.view(np.uint32)), "not deterministic"
+
+
+def test_tile_split_k_small_integer_exact_and_closed_forms():
+    rng = np.random.default_rng(65)
+    M, N, K = 1000, 1025, 3000
+    A = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    B = rng.integers(-4, 5, (K, N)).astype(np.float32)
+    p = gi.make_problem(M, N, K, "bf16", ROW_MAJOR, COL_MAJOR, A_logical=A, B_logical=B)
+    flat, need, kernel = run_ws(p)
+    assert kernel == "bf16_dma256x256_splitk"
+    ref, _ = oracle.gemm(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b)
+    assert np.array_equal(logical_c(p, flat).astype(np.float64), ref)
+    ones = gi.make_problem(M, N, K, "bf16", ROW_MAJOR, COL_MAJOR, A_logical=np.ones((M, K)),
+                           B_logical=np.ones((K, N)))
+    flat, _, kernel = run_ws(ones)
+    assert kernel == "bf16_dma256x256_splitk" and np.all(logical_c(ones, flat) == K)
+
+
+def test_tile_split_k_workspace_too_small_runs_unsplit():
+    p = gi.make_problem(1000, 1025, 3000, "bf16", ROW_MAJOR, COL_MAJOR, wid=66)
+    need = g.gemm_workspace_size("bf16", p.M, p.N, p.K, p.order_a, p.order_b, p.order_c)
+    flat, _, kernel = run_ws(p, ws_bytes=need - 16)
+    assert not kernel.endswith("_splitk"), kernel
+    ref, D = reference(p, key=("tilesplit-small", 1))
+    assert oracle.normalised_error(logical_c(p, flat), ref, D) <= TOL["bf16"]
 
 
 def test_split_k_small_integer_exact():
@@ -707,9 +701,9 @@ def test_f16_values_bf16_cannot_hold(algo, shape):
     assert oracle.normalised_error(C, ref, D) <= TOL["f16"]
 
 
-def test_f16_rejects_pingpong_and_vector_ladder():
+def test_f16_rejects_the_vector_ladder():
     p = gi.make_problem(256, 256, 64, "f16", ROW_MAJOR, COL_MAJOR)
-    for algo in (g.Algo.MFMA_PINGPONG, g.Algo.NAIVE, g.Algo.REGBLOCK):
+    for algo in (g.Algo.NAIVE, g.Algo.REGBLOCK):
         with pytest.raises(g.GemmError) as e:
             run(p, algo)
         assert e.value.status == g.Status.ERR_INVALID_VALUE

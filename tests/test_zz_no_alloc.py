@@ -59,3 +59,18 @@ def test_noalloc_plain_shapes_and_empty_problems():
     p = gi.make_problem(0, 16, 16, "bf16", gi.ROW_MAJOR, gi.COL_MAJOR, wid=61)
     _call(g.gemm_bf16_f32acc_noalloc, p, to_device(p.A), to_device(p.B))
     assert g.gemm_last_kernel() == "none"
+
+
+def test_noalloc_refuses_a_split_beyond_its_scratch():
+    """2048 x 2048 x 8192 splits K into 4 slices: 3 slabs of 16 MiB exceed the 32 MiB scratch."""
+    M, N, K = 2048, 2048, 8192
+    need = g.gemm_workspace_size("bf16", M, N, K, gi.ROW_MAJOR, gi.COL_MAJOR, gi.ROW_MAJOR)
+    assert need > g.NOALLOC_SCRATCH_BYTES
+    import torch
+    A = torch.zeros(M * K, dtype=torch.int16, device="cuda")
+    B = torch.zeros(N * K, dtype=torch.int16, device="cuda")
+    C = torch.zeros(M * N, dtype=torch.float32, device="cuda")
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_bf16_f32acc_noalloc(M, N, K, A.data_ptr(), K, gi.ROW_MAJOR, B.data_ptr(), K, gi.COL_MAJOR,
+                                   C.data_ptr(), N, gi.ROW_MAJOR, torch.cuda.current_stream().cuda_stream)
+    assert e.value.status == g.Status.ERR_SCRATCH_TOO_SMALL

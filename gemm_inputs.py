@@ -12,7 +12,11 @@ Value recipes follow the pages' workloads:
     ~ N(0, 1) and weights ~ N(0, 0.02) (0.02 read as the standard deviation).
 No dataset or trained weights stand behind any of them: the values are synthetic.
 
-bf16 rounding is round-to-nearest-even of the fp32 value, done once here on the host.
+bf16 rounding is round-to-nearest-even of the fp32 value, done once here on the host; so is
+the rounding to the two OCP 8-bit formats (E4M3, E5M2) of the fp8 workloads ("A06 - Tiled Matrix
+Multiply (GEMM)", section "Matrix cores: MFMA and Tensor Cores", names fp8 as a matrix-core input
+type; its format is read as the OCP one gfx950's matrix instructions take).  A dtype of "e4m3" or
+"e5m2" gives both operands that format; "e4m3_e5m2" and "e5m2_e4m3" name A's and B's.
 """
 from __future__ import annotations
 
@@ -127,6 +131,64 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+# OCP 8-bit formats: (exponent bits, fraction bits, bias)
+FP8_FORMATS = {"e4m3": (4, 3, 7), "e5m2": (5, 2, 15)}
+FP8_DTYPES = {"e4m3": ("e4m3", "e4m3"), "e5m2": ("e5m2", "e5m2"), "e4m3_e5m2": ("e4m3", "e5m2"),
+              "e5m2_e4m3": ("e5m2", "e4m3")}
+
+
+def f32_to_fp8_bits(x: np.ndarray, fmt: str) -> np.ndarray:
+    """Round fp32 to an OCP 8-bit format (round to nearest, ties to even); uint8 bit patterns.
+
+    Values that round past the largest finite one become NaN in E4M3 (it has no infinities;
+    0x7F) and infinity in E5M2 (0x7C, sign kept); NaN becomes 0x7F in both.
+    """
+    ebits, mbits, bias = FP8_FORMATS[fmt]
+    x = np.asarray(x, dtype=np.float32)
+    a = np.abs(x).astype(np.float64)
+    finite = np.isfinite(a)
+    a = np.where(finite, a, 0.0)
+    emin = 1 - bias                                   # exponent of the smallest normal value
+    _, e = np.frexp(a)                                # a = m 2^e, m in [0.5, 1)
+    E = np.maximum(e - 1, emin)                       # subnormals share the smallest exponent
+    q = np.rint(a / np.exp2(E - mbits))               # significand in last-place units, ties to even
+    carry = q >= 2 ** (mbits + 1)
+    E = np.where(carry, E + 1, E)
+    q = np.where(carry, q / 2, q)
+    normal = q >= 2 ** mbits
+    expf = np.where(normal, E + bias, 0).astype(np.int64)
+    frac = np.where(normal, q - 2 ** mbits, q).astype(np.int64)
+    bits = (expf << mbits) | frac
+    if fmt == "e4m3":
+        over = (expf > 15) | ((expf == 15) & (frac == 7)) | np.isinf(x)
+        bits = np.where(over, 0x7F, bits)
+    else:
+        over = (expf >= 31) | np.isinf(x)
+        bits = np.where(over, 0x7C, bits)
+    sign = np.signbit(x).astype(np.int64) << 7
+    bits = np.where(np.isnan(x), 0x7F, bits | sign)
+    return bits.astype(np.uint8)
+
+
+def fp8_bits_to_f32(b: np.ndarray, fmt: str) -> np.ndarray:
+    """Exact widening of OCP 8-bit bit patterns to fp32 (every such value is an fp32 value)."""
+    ebits, mbits, bias = FP8_FORMATS[fmt]
+    table = np.empty(256, dtype=np.float64)
+    for v in range(256):
+        sign = -1.0 if v >> 7 else 1.0
+        expf, frac = (v >> mbits) & ((1 << ebits) - 1), v & ((1 << mbits) - 1)
+        top = (1 << ebits) - 1
+        if fmt == "e4m3" and expf == top and frac == (1 << mbits) - 1:
+            table[v] = np.nan
+        elif fmt == "e5m2" and expf == top:
+            table[v] = sign * np.inf if frac == 0 else np.nan
+        elif expf == 0:
+            table[v] = sign * frac * 2.0 ** (1 - bias - mbits)
+        else:
+            table[v] = sign * (1 + frac / 2 ** mbits) * 2.0 ** (expf - bias)
+    return table[np.asarray(b, dtype=np.uint8)].astype(np.float32)
+
+
 def lay_out(logical: np.ndarray, order: int, ld: int | None = None) -> tuple[np.ndarray, int]:
     """Place a logical R x C matrix in a flat buffer with the given order and leading dim.
 
@@ -153,6 +215,8 @@ def lay_out(logical: np.ndarray, order: int, ld: int | None = None) -> tuple[np.
 
 
 def _sentinel(dtype) -> object:
+    if dtype == np.uint8:
+        return np.uint8(0x7F)        # NaN in both 8-bit formats
     if dtype == np.uint16:
         return np.uint16(0x7FC1)     # a bf16 NaN
     if dtype == np.float16:
@@ -179,15 +243,31 @@ class Problem:
     ldc: int
 
     def a_f32(self) -> np.ndarray:
-        return _to_f32(self.A_logical, self.dtype)
+        return _to_f32(self.A_logical, self.dtype, 0)
 
     def b_f32(self) -> np.ndarray:
-        return _to_f32(self.B_logical, self.dtype)
+        return _to_f32(self.B_logical, self.dtype, 1)
+
+    @property
+    def fmt_a(self):
+        """A's 8-bit format ("e4m3" / "e5m2"), None for other input types."""
+        return FP8_DTYPES[self.dtype][0] if self.dtype in FP8_DTYPES else None
+
+    @property
+    def fmt_b(self):
+        return FP8_DTYPES[self.dtype][1] if self.dtype in FP8_DTYPES else None
 
 
-def _to_f32(x: np.ndarray, dtype: str) -> np.ndarray:
+def oracle_formats(p) -> dict:
+    """The fmt_a / fmt_b arguments the oracle needs for a problem's 8-bit operands ({} otherwise)."""
+    return {"fmt_a": p.fmt_a, "fmt_b": p.fmt_b} if p.dtype in FP8_DTYPES else {}
+
+
+def _to_f32(x: np.ndarray, dtype: str, operand: int = 0) -> np.ndarray:
     if dtype == "bf16":
         return bf16_bits_to_f32(x)
+    if dtype in FP8_DTYPES:
+        return fp8_bits_to_f32(x, FP8_DTYPES[dtype][operand])
     return x.astype(np.float32) if dtype == "f16" else x
 
 
@@ -214,6 +294,9 @@ def make_problem(M: int, N: int, K: int, dtype: str = "f32", order_a: int = ROW_
     elif dtype == "f16":
         A_logical = A_logical.astype(np.float16)
         B_logical = B_logical.astype(np.float16)
+    elif dtype in FP8_DTYPES:
+        A_logical = f32_to_fp8_bits(A_logical, FP8_DTYPES[dtype][0])
+        B_logical = f32_to_fp8_bits(B_logical, FP8_DTYPES[dtype][1])
     elif dtype != "f32":
         raise ValueError(dtype)
     lda0 = K if order_a == ROW_MAJOR else M

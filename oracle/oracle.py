@@ -1,8 +1,10 @@
 """ctypes front end of the C oracle (oracle.c) -- TEST INFRASTRUCTURE ONLY.
 
 The oracle computes C[i][j] = sum_k A[i][k] * B[k][j] in double, k ascending, on the
-exact fp32, bf16 or fp16 input values, and D[i][j] = sum_k |A[i][k] * B[k][j]|, the scale the
-parity tolerance is normalised by.  See oracle.c for the cited definition.
+exact fp32, bf16, fp16 or 8-bit (OCP E4M3 / E5M2) input values, and D[i][j] = sum_k
+|A[i][k] * B[k][j]|, the scale the parity tolerance is normalised by.  See oracle.c for the
+cited definition.  8-bit operands are uint8 bit patterns whose format is named by the fmt_a /
+fmt_b arguments ("e4m3" or "e5m2").
 """
 from __future__ import annotations
 
@@ -22,6 +24,9 @@ _lib = None
 F32 = 0
 BF16 = 1
 F16 = 2
+E4M3 = 3
+E5M2 = 4
+FP8_CODES = {"e4m3": E4M3, "e5m2": E5M2}
 
 
 def library_path() -> str:
@@ -59,53 +64,65 @@ def _bind(lib):
                                         vp, i64, ctypes.c_int, ctypes.POINTER(i64),
                                         ctypes.POINTER(i64), i64, dp, dp]
     lib.oracle_gemm_sampled.restype = ctypes.c_int
+    lib.oracle_gemm_ab.argtypes = [i64, i64, i64, ctypes.c_int, vp, i64, ctypes.c_int,
+                                   ctypes.c_int, vp, i64, ctypes.c_int, dp, dp, ctypes.POINTER(i64)]
+    lib.oracle_gemm_ab.restype = ctypes.c_int
+    lib.oracle_gemm_sampled_ab.argtypes = [i64, i64, i64, ctypes.c_int, vp, i64, ctypes.c_int,
+                                           ctypes.c_int, vp, i64, ctypes.c_int, ctypes.POINTER(i64),
+                                           ctypes.POINTER(i64), i64, dp, dp]
+    lib.oracle_gemm_sampled_ab.restype = ctypes.c_int
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
 
 
-def _dtype_code(buf: np.ndarray) -> int:
+def _dtype_code(buf: np.ndarray, fmt=None) -> int:
+    if buf.dtype == np.uint8:
+        if fmt not in FP8_CODES:
+            raise TypeError("8-bit operands need their format: fmt 'e4m3' or 'e5m2'")
+        return FP8_CODES[fmt]
     if buf.dtype == np.float32:
         return F32
     if buf.dtype == np.uint16:
         return BF16
     if buf.dtype == np.float16:
         return F16
-    raise TypeError(f"oracle operands are fp32, bf16 bits (uint16) or fp16, got {buf.dtype}")
+    raise TypeError(f"oracle operands are fp32, bf16 bits (uint16), fp16 or fp8 bits (uint8), got {buf.dtype}")
 
 
-def gemm(M, N, K, A, lda, order_a, B, ldb, order_b, lib=None, return_macs=False):
+def gemm(M, N, K, A, lda, order_a, B, ldb, order_b, lib=None, return_macs=False, fmt_a=None, fmt_b=None):
     """Full product: returns (C, D) as M x N float64 arrays (and the MAC count if asked)."""
     lib = lib or load()
     A = np.ascontiguousarray(A)
     B = np.ascontiguousarray(B)
-    dt = _dtype_code(A)
-    assert _dtype_code(B) == dt
+    da, db = _dtype_code(A, fmt_a), _dtype_code(B, fmt_b)
+    if da in (F32, BF16, F16) or db in (F32, BF16, F16):
+        assert da == db, "operands of different types are 8-bit formats only"
     C = np.zeros((M, N), dtype=np.float64)
     D = np.zeros((M, N), dtype=np.float64)
     macs = ctypes.c_int64(-1)
     dp = ctypes.POINTER(ctypes.c_double)
-    rc = lib.oracle_gemm(M, N, K, dt, A.ctypes.data, lda, order_a, B.ctypes.data, ldb, order_b,
-                         C.ctypes.data_as(dp), D.ctypes.data_as(dp), ctypes.byref(macs))
+    rc = lib.oracle_gemm_ab(M, N, K, da, A.ctypes.data, lda, order_a, db, B.ctypes.data, ldb, order_b,
+                            C.ctypes.data_as(dp), D.ctypes.data_as(dp), ctypes.byref(macs))
     if rc != 0:
         raise ValueError("oracle_gemm rejected its arguments")
     return (C, D, macs.value) if return_macs else (C, D)
 
 
-def gemm_sampled(M, N, K, A, lda, order_a, B, ldb, order_b, rows, cols, lib=None):
+def gemm_sampled(M, N, K, A, lda, order_a, B, ldb, order_b, rows, cols, lib=None, fmt_a=None, fmt_b=None):
     """C and D at the (rows[t], cols[t]) elements only."""
     lib = lib or load()
     A = np.ascontiguousarray(A)
     B = np.ascontiguousarray(B)
-    dt = _dtype_code(A)
+    da, db = _dtype_code(A, fmt_a), _dtype_code(B, fmt_b)
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     cols = np.ascontiguousarray(cols, dtype=np.int64)
     C = np.zeros(rows.size, dtype=np.float64)
     D = np.zeros(rows.size, dtype=np.float64)
     dp = ctypes.POINTER(ctypes.c_double)
     ip = ctypes.POINTER(ctypes.c_int64)
-    rc = lib.oracle_gemm_sampled(M, N, K, dt, A.ctypes.data, lda, order_a, B.ctypes.data, ldb,
-                                 order_b, rows.ctypes.data_as(ip), cols.ctypes.data_as(ip),
-                                 rows.size, C.ctypes.data_as(dp), D.ctypes.data_as(dp))
+    rc = lib.oracle_gemm_sampled_ab(M, N, K, da, A.ctypes.data, lda, order_a, db, B.ctypes.data, ldb,
+                                    order_b, rows.ctypes.data_as(ip), cols.ctypes.data_as(ip),
+                                    rows.size, C.ctypes.data_as(dp), D.ctypes.data_as(dp))
     if rc != 0:
         raise ValueError("oracle_gemm_sampled rejected its arguments")
     return C, D

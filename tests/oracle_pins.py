@@ -29,12 +29,14 @@ import oracle
 from gemm_inputs import COL_MAJOR, ROW_MAJOR
 
 ORDERS = [(oa, ob) for oa in (ROW_MAJOR, COL_MAJOR) for ob in (ROW_MAJOR, COL_MAJOR)]
-DTYPES = ("f32", "bf16", "f16")
+# every input type of the one-problem oracle: fp32, bf16, fp16 and the 8-bit formats (also mixed)
+DTYPES = ("f32", "bf16", "f16", "e4m3", "e5m2", "e4m3_e5m2")
+BATCH_DTYPES = ("f32", "bf16", "f16")
 
 
 def _run(lib, p: gi.Problem, macs=False):
     return oracle.gemm(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b,
-                       lib=lib, return_macs=macs)
+                       lib=lib, return_macs=macs, **gi.oracle_formats(p))
 
 
 def _int_matrix(rng, r, c, lo=-4, hi=4):
@@ -153,8 +155,9 @@ def pin_transpose(lib):
         for oa, ob in ORDERS:
             p = gi.make_problem(23, 31, 41, dtype, oa, ob, wid=107, pad_b=5)
             C, D = _run(lib, p)
+            fm = gi.oracle_formats(p)
             Ct, Dt = oracle.gemm(p.N, p.M, p.K, p.B, p.ldb, 1 - p.order_b, p.A, p.lda,
-                                 1 - p.order_a, lib=lib)
+                                 1 - p.order_a, lib=lib, fmt_a=fm.get("fmt_b"), fmt_b=fm.get("fmt_a"))
             assert np.array_equal(Ct, C.T) and np.array_equal(Dt, D.T), (dtype, oa, ob)
 
 
@@ -233,6 +236,40 @@ def pin_f16_widening(lib):
         assert C[pattern, 0] == value
 
 
+def pin_fp8_widening(lib):
+    """Every bit pattern of both OCP 8-bit formats is read as the value it encodes, checked
+    against torch's float8_e4m3fn / float8_e5m2 -> float32 conversion (a library routine the
+    oracle does not call) for all 256 patterns: a 256 x 1 times 1 x 1 product with B = 1 returns
+    them.  Also the formats' fixed points: the largest finite values (448 = 0x7E, 57344 = 0x7B),
+    the smallest subnormals (2^-9 = 0x01, 2^-16 = 0x01) and normals (2^-6 = 0x08, 2^-14 = 0x04),
+    1.0 (0x38, 0x3C), -0 (0x80), E4M3's only NaNs 0x7F / 0xFF and E5M2's infinities 0x7C / 0xFC."""
+    import torch
+    bits = np.arange(256, dtype=np.uint16).astype(np.uint8)
+    for fmt, tdt, one in (("e4m3", torch.float8_e4m3fn, 0x38), ("e5m2", torch.float8_e5m2, 0x3C)):
+        B = np.array([one], dtype=np.uint8)
+        C, D = oracle.gemm(256, 1, 1, bits, 1, ROW_MAJOR, B, 1, ROW_MAJOR, lib=lib, fmt_a=fmt, fmt_b=fmt)
+        want = torch.from_numpy(bits.copy()).view(tdt).float().numpy().astype(np.float64)
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(C[:, 0]), nan), fmt
+        assert np.array_equal(C[~nan, 0], want[~nan]), fmt
+    C4, _ = oracle.gemm(256, 1, 1, bits, 1, ROW_MAJOR, np.array([0x38], np.uint8), 1, ROW_MAJOR, lib=lib,
+                        fmt_a="e4m3", fmt_b="e4m3")
+    for pattern, value in ((0x7E, 448.0), (0x01, 2.0 ** -9), (0x08, 2.0 ** -6), (0x38, 1.0), (0xB8, -1.0),
+                           (0x80, -0.0), (0x77, 240.0)):
+        assert C4[pattern, 0] == value, (hex(pattern), C4[pattern, 0])
+    assert np.isnan(C4[0x7F, 0]) and np.isnan(C4[0xFF, 0]) and np.isfinite(C4[0x78, 0])
+    C5, _ = oracle.gemm(256, 1, 1, bits, 1, ROW_MAJOR, np.array([0x3C], np.uint8), 1, ROW_MAJOR, lib=lib,
+                        fmt_a="e5m2", fmt_b="e5m2")
+    for pattern, value in ((0x7B, 57344.0), (0x01, 2.0 ** -16), (0x04, 2.0 ** -14), (0x3C, 1.0),
+                           (0x7C, np.inf), (0xFC, -np.inf), (0x80, -0.0)):
+        assert C5[pattern, 0] == value, (hex(pattern), C5[pattern, 0])
+    assert np.isnan(C5[0x7D, 0]) and np.isnan(C5[0xFF, 0])
+    # mixed formats: an E4M3 A against an E5M2 B reads each in its own format
+    C, _ = oracle.gemm(1, 1, 1, np.array([0x7E], np.uint8), 1, ROW_MAJOR, np.array([0x7B], np.uint8), 1,
+                       ROW_MAJOR, lib=lib, fmt_a="e4m3", fmt_b="e5m2")
+    assert C[0, 0] == 448.0 * 57344.0
+
+
 def pin_sampled_matches_full(lib):
     """The sampled entry point returns the full product's elements bit for bit."""
     for dtype in DTYPES:
@@ -243,7 +280,7 @@ def pin_sampled_matches_full(lib):
             rows = rng.integers(0, p.M, 50)
             cols = rng.integers(0, p.N, 50)
             Cs, Ds = oracle.gemm_sampled(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb,
-                                         p.order_b, rows, cols, lib=lib)
+                                         p.order_b, rows, cols, lib=lib, **gi.oracle_formats(p))
             assert np.array_equal(Cs, C[rows, cols]) and np.array_equal(Ds, D[rows, cols])
 
 
@@ -266,7 +303,7 @@ def pin_batched_bruteforce(lib):
     """Each entry of a strided batch equals the exact rational product of that entry's own
     logical matrices (the generator's arrays, independent of the layout), for interleaved,
     stacked and shared operands."""
-    for dtype in DTYPES:
+    for dtype in BATCH_DTYPES:
         for lay in BATCH_LAYOUTS:
             p = gi.make_batched_problem(3, 2, 5, 4, dtype, wid=111, **lay)
             C, D = _batched(lib, p)
@@ -288,7 +325,7 @@ def pin_batched_scaled_identity(lib):
     eye = np.stack([(z + 1) * np.eye(n, dtype=np.float32) for z in range(batch)])
     rng = np.random.default_rng(23)
     Bl = _int_matrix(rng, batch * n, N).reshape(batch, n, N)
-    for dtype in DTYPES:
+    for dtype in BATCH_DTYPES:
         for lay in (dict(), dict(lda=batch * n, sa=n, ldb=N + 3, sb=(N + 3) * n + 1)):
             p = gi.make_batched_problem(batch, n, N, n, dtype, A_logical=eye, B_logical=Bl, **lay)
             C, _ = _batched(lib, p)
@@ -336,6 +373,6 @@ ALL_PINS = [
     pin_fraction_bruteforce, pin_numpy_crosscheck, pin_ones, pin_ones_column_sums,
     pin_identity, pin_permutation, pin_small_integers, pin_transpose, pin_k_split,
     pin_mac_count, pin_degenerate, pin_nonnegative_scale, pin_bf16_widening,
-    pin_f16_widening, pin_sampled_matches_full, pin_batched_bruteforce, pin_batched_scaled_identity,
+    pin_f16_widening, pin_fp8_widening, pin_sampled_matches_full, pin_batched_bruteforce, pin_batched_scaled_identity,
     pin_epilogue_closed_forms, pin_gelu_values,
 ]

@@ -49,6 +49,32 @@ def test_bf16_rounding_is_nearest_even():
     assert np.array_equal(gi.f32_to_bf16_bits(gi.bf16_bits_to_f32(r)), r)
 
 
+def test_fp8_rounding_is_nearest_even():
+    """fp32 -> OCP E4M3 / E5M2 rounding of the input generator: hand-worked ties and edges, and
+    agreement with torch's float8 conversions (a library routine) on 200 000 random values."""
+    import torch
+    # E4M3: 1 + 2^-4 ties between 1.0 (0x38) and 1.125 (0x39) -> even 0x38; 1 + 3*2^-4 ties
+    # between 0x39 and 0x3A -> even 0x3A; 464 ties between 448 (0x7E) and the NaN code -> 0x7E;
+    # 500 overflows to NaN; 2^-10 ties between 0 and the smallest subnormal 2^-9 -> 0
+    x = np.array([1.0, 1.0625, 1.1875, 464.0, 500.0, 2.0 ** -10, 3 * 2.0 ** -11, -0.0, -448.0], np.float32)
+    assert [int(b) for b in gi.f32_to_fp8_bits(x, "e4m3")] == [0x38, 0x38, 0x3A, 0x7E, 0x7F, 0x00, 0x01, 0x80, 0xFE]
+    # E5M2: 61440 ties between 57344 (0x7B) and 65536 (overflow) -> infinity 0x7C; 2^-17 -> 0
+    x = np.array([1.0, 1.125, 61440.0, -70000.0, 2.0 ** -17, 2.0 ** -16, np.inf], np.float32)
+    assert [int(b) for b in gi.f32_to_fp8_bits(x, "e5m2")] == [0x3C, 0x3C, 0x7C, 0xFC, 0x00, 0x01, 0x7C]
+    r = np.random.default_rng(1).standard_normal(200000).astype(np.float32) * np.float32(50.0)
+    for fmt, tdt in (("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)):
+        ours = gi.f32_to_fp8_bits(r, fmt)
+        theirs = torch.from_numpy(r).to(tdt).view(torch.uint8).numpy()
+        dec = gi.fp8_bits_to_f32(ours, fmt)
+        assert np.array_equal(ours[~np.isnan(dec)], theirs[~np.isnan(dec)])
+        assert np.all(np.isnan(torch.from_numpy(theirs[np.isnan(dec)]).view(tdt).float().numpy()))
+        # widening is exact: round-tripping every finite pattern is the identity
+        allb = np.arange(256, dtype=np.uint16).astype(np.uint8)
+        fin = np.isfinite(gi.fp8_bits_to_f32(allb, fmt))
+        back = gi.f32_to_fp8_bits(gi.fp8_bits_to_f32(allb[fin], fmt), fmt)
+        assert np.array_equal(back, allb[fin])
+
+
 def test_layout_places_elements():
     L = np.arange(12, dtype=np.float32).reshape(3, 4)
     flat, ld = gi.lay_out(L, gi.ROW_MAJOR, 6)

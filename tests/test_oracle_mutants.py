@@ -22,8 +22,8 @@ MUTANTS = {
                        "for (int64_t k = 0; k < K - 1; ++k) {\n                double a"),
     "skip_first_term": ("for (int64_t k = 0; k < K; ++k) {\n                double a",
                         "for (int64_t k = 1; k < K; ++k) {\n                double a"),
-    "transpose_b": ("a * element(B, dtype, k, j, ldb, order_b)",
-                    "a * element(B, dtype, j, k, ldb, order_b)"),
+    "transpose_b": ("a * element(B, dtype_b, k, j, ldb, order_b)",
+                    "a * element(B, dtype_b, j, k, ldb, order_b)"),
     "wrong_sign": ("s[j] += p;", "s[j] -= p;"),
     "col_major_as_row": ("r * ld + c : r + c * ld", "r * ld + c : r * ld + c"),
     "row_major_as_col": ("r * ld + c : r + c * ld", "r + c * ld : r + c * ld"),
@@ -33,10 +33,19 @@ MUTANTS = {
     "f16_fraction_width": ("(double)(1024 + frac)", "(double)(512 + frac)"),
     "scale_without_abs": ("d[j] += fabs(p);", "d[j] += p;"),
     "no_row_reset": ("s[j] = 0.0;\n                d[j] = 0.0;", "d[j] = 0.0;"),
-    "fp32_accumulator": ("double p = a * element(B, dtype, k, j, ldb, order_b);\n                    s[j] += p;",
-                         "double p = a * element(B, dtype, k, j, ldb, order_b);\n                    s[j] = (float)(s[j] + p);"),
-    "sampled_off_by_one": ("element(B, dtype, k, cols[t], ldb, order_b)",
-                           "element(B, dtype, k, cols[t] > 0 ? cols[t] - 1 : 0, ldb, order_b)"),
+    "fp32_accumulator": ("double p = a * element(B, dtype_b, k, j, ldb, order_b);\n                    s[j] += p;",
+                         "double p = a * element(B, dtype_b, k, j, ldb, order_b);\n                    s[j] = (float)(s[j] + p);"),
+    "sampled_off_by_one": ("element(B, dtype_b, k, cols[t], ldb, order_b)",
+                           "element(B, dtype_b, k, cols[t] > 0 ? cols[t] - 1 : 0, ldb, order_b)"),
+    "e4m3_exponent_bias": ("exp - 10);     /* (1 + frac/8)", "exp - 11);     /* (1 + frac/8)"),
+    "e4m3_fraction_width": ("ldexp((double)(8 + frac), exp - 10)", "ldexp((double)(4 + frac), exp - 10)"),
+    "e4m3_top_exponent_as_nan": ("if (exp == 15 && frac == 7)", "if (exp == 15)"),
+    "e4m3_subnormals_as_zero": ("v = ldexp((double)frac, -9);", "v = 0.0;"),
+    "e5m2_exponent_bias": ("exp - 17);     /* (1 + frac/4)", "exp - 16);     /* (1 + frac/4)"),
+    "e5m2_fraction_width": ("ldexp((double)(4 + frac), exp - 17)", "ldexp((double)(8 + frac), exp - 17)"),
+    "e5m2_fields_split_as_e4m3": ("exp = (b >> 2) & 0x1f, frac = b & 0x3;", "exp = (b >> 3) & 0x1f, frac = b & 0x7;"),
+    "b_read_with_a_format": ("a * element(B, dtype_b, k, j, ldb, order_b)",
+                             "a * element(B, dtype_a, k, j, ldb, order_b)"),
     "mac_undercount": ("count += N;", "count += N - (k == 0);"),
 }
 

@@ -76,6 +76,7 @@ KERNEL_SOURCES = {
     "f32_dma": ("f32_dma.hip",),
     "bf16_dma": ("bf16_dma.hip", "mma16.hpp", "epilogue.hpp"),
     "f16_dma": ("bf16_dma.hip", "mma16.hpp", "epilogue.hpp"),
+    "fp8_dma": ("bf16_dma.hip", "mma16.hpp", "epilogue.hpp"),
     "bf16_mfma": ("bf16_mfma.hip", "mma16.hpp"),
     "f32_skinny": ("skinny.hip", "mma16.hpp"),
     "bf16_skinny": ("skinny.hip", "mma16.hpp"),
@@ -147,7 +148,10 @@ class Leg:
         self.batched = self.w.batch > 1
         if self.batched and (algo != "AUTO" or workspace):
             raise SystemExit("a strided batch runs the default kernel choice without a workspace")
-        e = 4 if self.w.dtype == "f32" else 2
+        fp8 = self.w.dtype in gi.FP8_DTYPES
+        e = 4 if self.w.dtype == "f32" else 1 if fp8 else 2
+        if fp8 and (algo != "AUTO" or workspace or self.batched or epilogue is not None):
+            raise SystemExit("8-bit workloads run gemm_fp8_f32acc alone (one kernel family, no workspace)")
         if sets <= 0:
             per_set = e * self.w.batch * (self.w.M * self.w.K + self.w.K * self.w.N)
             sets = min(64, max(2, (512 * 2**20) // per_set + 1))
@@ -162,9 +166,16 @@ class Leg:
         p = self.problems[0]
         size = p.c_size() if self.batched else gi.c_buffer_size(p.M, p.N, p.ldc, p.order_c)
         self.C = torch.empty(size, dtype=torch.float32, device="cuda")
-        self.fn = {"f32": g.gemm_f32_algo, "bf16": g.gemm_bf16_f32acc_algo, "f16": g.gemm_f16_f32acc_algo}[w.dtype]
-        self.fn_batched = {"f32": g.gemm_f32_strided_batched, "bf16": g.gemm_bf16_f32acc_strided_batched,
-                           "f16": g.gemm_f16_f32acc_strided_batched}[w.dtype]
+        if fp8:
+            code = {"e4m3": g.Fp8.E4M3, "e5m2": g.Fp8.E5M2}
+            fa, fb = code[gi.FP8_DTYPES[w.dtype][0]], code[gi.FP8_DTYPES[w.dtype][1]]
+            self.fn = lambda algo, M, N, K, A, lda, oa, B, ldb, ob, C, ldc, oc, stream: g.gemm_fp8_f32acc(
+                M, N, K, A, lda, oa, fa, B, ldb, ob, fb, C, ldc, oc, stream)
+            self.fn_batched = None
+        else:
+            self.fn = {"f32": g.gemm_f32_algo, "bf16": g.gemm_bf16_f32acc_algo, "f16": g.gemm_f16_f32acc_algo}[w.dtype]
+            self.fn_batched = {"f32": g.gemm_f32_strided_batched, "bf16": g.gemm_bf16_f32acc_strided_batched,
+                               "f16": g.gemm_f16_f32acc_strided_batched}[w.dtype]
         self.flops = w.flops
         # compulsory HBM bytes: every input element read once, every output element written once
         self.bytes = w.batch * (e * (w.M * w.K + w.K * w.N) + 4 * w.M * w.N)
@@ -232,6 +243,8 @@ def cpu_baseline(legs, target_s):
     import oracle
     threads = oracle.num_threads()
 
+    import gemm_inputs as gi
+
     def run(rows):
         t0 = time.perf_counter()
         for leg in legs:
@@ -239,12 +252,11 @@ def cpu_baseline(legs, target_s):
             a = p.A if p.order_a == 0 else None
             if a is None:                      # a column-major A: take the sub-matrix's rows
                 sub = p.A_logical[:rows]
-                import gemm_inputs as gi
                 a, lda = gi.lay_out(sub, 1)
             else:
                 lda = p.lda
                 a = p.A[: rows * p.lda]
-            oracle.gemm(rows, p.N, p.K, a, lda, p.order_a, p.B, p.ldb, p.order_b)
+            oracle.gemm(rows, p.N, p.K, a, lda, p.order_a, p.B, p.ldb, p.order_b, **gi.oracle_formats(p))
         return time.perf_counter() - t0
 
     probe = max(1, threads)
@@ -346,7 +358,7 @@ def main():
     roof = roofs[dom.name]
 
     value = step_flops / (ms_step * 1e-3) / 1e12
-    dtype = "+".join(sorted({"f32" if l.w.dtype == "f32" else "bf16->f32" for l in legs}))
+    dtype = "+".join(sorted({"f32" if l.w.dtype == "f32" else l.w.dtype + "->f32" for l in legs}))
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),

@@ -41,6 +41,12 @@ class Status(enum.IntEnum):
     ERR_SCRATCH_TOO_SMALL = 4
 
 
+class Fp8(enum.IntEnum):
+    """gemm_fp8_t: the OCP 8-bit formats of gemm_fp8_f32acc's operands"""
+    E4M3 = 0
+    E5M2 = 1
+
+
 class LibraryNotBuilt(ImportError):
     pass
 
@@ -103,6 +109,8 @@ def _load():
         f = getattr(lib, name)
         f.argtypes, f.restype = args[:-1] + [ctypes.POINTER(EpilogueStruct), vp], ci
     lib.gemm_bf16_f32acc_noalloc.argtypes, lib.gemm_bf16_f32acc_noalloc.restype = args, ci
+    lib.gemm_fp8_f32acc.argtypes = [i64, i64, i64, vp, i64, ci, ci, vp, i64, ci, ci, vp, i64, ci, vp]
+    lib.gemm_fp8_f32acc.restype = ci
     return lib
 
 
@@ -131,13 +139,13 @@ EXPORTED = ("gemm_f32", "gemm_bf16_f32acc", "gemm_f32_algo", "gemm_bf16_f32acc_a
             "gemm_f16_f32acc", "gemm_f16_f32acc_algo", "gemm_f16_f32acc_ws",
             "gemm_f32_strided_batched", "gemm_bf16_f32acc_strided_batched",
             "gemm_f16_f32acc_strided_batched", "gemm_bf16_f32acc_fused", "gemm_f16_f32acc_fused",
-            "gemm_bf16_f32acc_noalloc")
+            "gemm_bf16_f32acc_noalloc", "gemm_fp8_f32acc")
 
 # bytes of the static scratch behind gemm_bf16_f32acc_noalloc (GEMM_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
-# dtype codes of gemm_plan / gemm_workspace_size
-DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2}
+# dtype codes of gemm_plan / gemm_workspace_size (every 8-bit format pairing is code 3)
+DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2, "fp8": 3, "e4m3": 3, "e5m2": 3, "e4m3_e5m2": 3, "e5m2_e4m3": 3}
 
 
 def library_path() -> str:
@@ -240,6 +248,13 @@ def gemm_bf16_f32acc_noalloc(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, 
     """gemm_bf16_f32acc_ws with the library's static scratch as workspace: allocates nothing."""
     _check(lib_handle().gemm_bf16_f32acc_noalloc(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c,
                                                  stream), "gemm_bf16_f32acc_noalloc")
+
+
+def gemm_fp8_f32acc(M, N, K, A, lda, order_a, format_a, B, ldb, order_b, format_b, C, ldc, order_c, stream=0):
+    """C = A.B with 8-bit A and B (bit patterns; format_* an Fp8), FP32 accumulate and FP32 C.
+    A row-major, B column-major."""
+    _check(lib_handle().gemm_fp8_f32acc(M, N, K, A, lda, order_a, int(format_a), B, ldb, order_b, int(format_b),
+                                        C, ldc, order_c, stream), "gemm_fp8_f32acc")
 
 
 # --- torch tensors -> (pointer, leading dimension, order) ------------------------------

@@ -113,7 +113,7 @@ def summarize(args) -> None:
         stem = tagged[:-2]
         workload, order = stem.split("@")
         w = gi.WORKLOADS[workload]
-        e = 4 if w.dtype == "f32" else 2
+        e = 4 if w.dtype == "f32" else 1 if w.dtype in gi.FP8_DTYPES else 2
         compulsory = w.batch * (e * (w.M * w.K + w.K * w.N) + 4 * w.M * w.N)
         parts = {t: _read(os.path.join(os.path.dirname(os.path.normpath(base)), f"{stem}_{t}")) for t in "ABC"}
         names = sorted({k for p in parts.values() for k in p if _library_kernel(k)})

@@ -26,9 +26,11 @@ namespace {
 thread_local int t_last_hip_error = 0;
 thread_local const char* t_last_kernel = "none";
 
-enum class In { F32, BF16, F16 };
+enum class In { F32, BF16, F16, FP8 };
 
-int elem_of(In in) { return in == In::F32 ? kElemF32 : in == In::BF16 ? kElemBf16 : kElemF16; }
+int elem_of(In in) {
+    return in == In::F32 ? kElemF32 : in == In::BF16 ? kElemBf16 : in == In::F16 ? kElemF16 : kElemFp8;
+}
 
 struct DeviceInfo {
     bool supported = false;
@@ -89,7 +91,7 @@ gemm_status_t validate(In in, int64_t M, int64_t N, int64_t K, const void* A, in
     if (ldc < at_least(oc == GEMM_ROW_MAJOR ? N : M)) return GEMM_ERR_INVALID_VALUE;
     if (M > 0 && N > 0 && C == nullptr) return GEMM_ERR_INVALID_VALUE;
     if (M > 0 && N > 0 && K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_INVALID_VALUE;
-    const uintptr_t e = in == In::F32 ? 4 : 2;
+    const uintptr_t e = in == In::F32 ? 4 : in == In::FP8 ? 1 : 2;
     if (!aligned(A, e) || !aligned(B, e) || !aligned(C, c_align)) return GEMM_ERR_INVALID_VALUE;
     return GEMM_OK;
 }
@@ -522,7 +524,7 @@ Problem query_problem(int64_t M, int64_t N, int64_t K, int oa, int ob, int oc) {
 
 // Workspace bytes with which the _ws entry points split K (0: they never do for this problem).
 size_t split_bytes(const Problem& p, int et, int cus) {
-    if (p.M == 0 || p.N == 0 || p.K == 0) return 0;
+    if (p.M == 0 || p.N == 0 || p.K == 0 || et == kElemFp8) return 0;
     if (prefer_small(p, cus) && skinny_applies(p, et != kElemF32)) {
         const SkinnySplit sp = skinny_split(p, et != kElemF32, cus);
         return sp.slices > 1 ? sp.bytes : 0;
@@ -534,10 +536,25 @@ size_t split_bytes(const Problem& p, int et, int cus) {
 
 // What the default choice runs for a normalised problem with K > 0, without launching: the
 // kernel's name and the rows and columns of C its own launch covers (the rest are strips).
+// The tile of the 8-bit kernel: the cheaper of its two configurations over the whole of C
+// (256 x 128, whose build has a byte-wise K tail, for K < 16).
+Plan plan_fp8(const Problem& p, int cus) {
+    if (p.K < 16) return plan_whole(p, kBf16DmaOpts[1], cus);
+    Plan best;
+    for (const TileOpt& o : kBf16DmaOpts) {
+        const Plan pl = plan_whole(p, o, cus);
+        if (pl.cost < best.cost) best = pl;
+    }
+    return best;
+}
+
+const char* fp8_name(const TileOpt& o) { return o.bn == 256 ? "fp8_dma256x256" : "fp8_dma256x128"; }
+
 const char* plan_auto(const Problem& p, int et, int cus, int& mc, int& nc) {
     const bool f32 = et == kElemF32;
     mc = p.M;
     nc = p.N;
+    if (et == kElemFp8) return fp8_name(plan_fp8(p, cus).opt);
     if (prefer_small(p, cus) && skinny_applies(p, !f32)) return skinny_name(et, skinny_blocks(p, cus));
     const Plan pl = f32 ? choose_f32_tiles(p, GEMM_ALGO_AUTO, cus) : choose_bf16_tiles(p, GEMM_ALGO_AUTO, cus);
     mc = pl.mc;
@@ -729,6 +746,53 @@ gemm_status_t run_fused(In in, int64_t M, int64_t N, int64_t K, const uint16_t* 
     return GEMM_OK;
 }
 
+// GEMM on 8-bit floating-point inputs: the direct-copy kernel with the 8-bit matrix
+// instruction over the whole of C (tiles overhang both edges), zero_c for K == 0.
+gemm_status_t run_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, gemm_order_t oa, int fa,
+                      const uint8_t* B, int64_t ldb, gemm_order_t ob, int fb, float* C, int64_t ldc, gemm_order_t oc,
+                      hipStream_t stream) {
+    for (int f : {fa, fb})
+        if (f != GEMM_FP8_E4M3 && f != GEMM_FP8_E5M2) return GEMM_ERR_INVALID_VALUE;
+    const gemm_status_t st = validate(In::FP8, M, N, K, A, lda, oa, B, ldb, ob, C, ldc, oc);
+    if (st != GEMM_OK) return st;
+    // both operands contiguous along k (the column-major-C swap keeps that)
+    if (oa != GEMM_ROW_MAJOR || ob != GEMM_COL_MAJOR) return GEMM_ERR_INVALID_VALUE;
+    const bool row = oc == GEMM_ROW_MAJOR;
+    Problem p{};
+    int f0 = fa, f1 = fb;
+    if (row) {
+        p = Problem{(int)M, (int)N, (int)K, A, lda, (int)oa, B, ldb, (int)ob, C, ldc};
+    } else {
+        p = Problem{(int)N, (int)M, (int)K, B, ldb, 1 - (int)ob, A, lda, 1 - (int)oa, C, ldc};
+        std::swap(f0, f1);
+    }
+    if (K > 0 && !fp8_dma_applies(p)) return GEMM_ERR_INVALID_VALUE;
+    if (M == 0 || N == 0) {
+        t_last_kernel = "none";
+        return GEMM_OK;
+    }
+    DeviceInfo dev;
+    if (!device_info(dev) || !dev.supported) return GEMM_ERR_UNSUPPORTED_DEVICE;
+    Launch l = launch_for(p, stream);
+    hipError_t err = hipSuccess;
+    const char* name = "zero_c";
+    if (K == 0) {
+        err = launch_zero_c(p, l);
+    } else {
+        const Plan best = plan_fp8(p, dev.cus);
+        const int bm = best.opt.bm, bn = best.opt.bn;
+        l.group_m = pick_group_m((p.M + bm - 1) / bm, (p.N + bn - 1) / bn);
+        name = fp8_name(best.opt);
+        err = launch_fp8_dma(p, l, bm, bn, f0, f1);
+    }
+    if (err != hipSuccess) {
+        t_last_hip_error = (int)err;
+        return GEMM_ERR_LAUNCH;
+    }
+    t_last_kernel = name;
+    return GEMM_OK;
+}
+
 // gemm_bf16_f32acc_noalloc: the _ws call with `scratch` as its workspace.  Nothing is
 // allocated; a problem whose split would need more than kScratchBytes is refused.
 gemm_status_t run_noalloc(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, gemm_order_t oa,
@@ -779,6 +843,13 @@ gemm_status_t gemm_f16_f32acc_fused(int64_t M, int64_t N, int64_t K, const uint1
                            stream);
 }
 
+gemm_status_t gemm_fp8_f32acc(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, gemm_order_t order_a,
+                              gemm_fp8_t format_a, const uint8_t* B, int64_t ldb, gemm_order_t order_b,
+                              gemm_fp8_t format_b, float* C, int64_t ldc, gemm_order_t order_c, hipStream_t stream) {
+    return gemm::run_fp8(M, N, K, A, lda, order_a, (int)format_a, B, ldb, order_b, (int)format_b, C, ldc, order_c,
+                         stream);
+}
+
 gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                        gemm_order_t order_a, const float* B, int64_t ldb, gemm_order_t order_b,
                        float* C, int64_t ldc, gemm_order_t order_c, hipStream_t stream) {
@@ -815,11 +886,13 @@ gemm_status_t gemm_plan(int dtype, int64_t M, int64_t N, int64_t K, gemm_order_t
                         gemm_order_t order_b, gemm_order_t order_c, int cus, const char** kernel,
                         int64_t* core_rows, int64_t* core_cols, size_t* workspace_bytes) {
     if (kernel == nullptr || core_rows == nullptr || core_cols == nullptr || workspace_bytes == nullptr ||
-        cus <= 0 || dtype < 0 || dtype > 2)
+        cus <= 0 || dtype < 0 || dtype > 3)
         return GEMM_ERR_INVALID_VALUE;
     if (M < 0 || N < 0 || K < 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return GEMM_ERR_INVALID_VALUE;
     for (int o : {(int)order_a, (int)order_b, (int)order_c})
         if (o != GEMM_ROW_MAJOR && o != GEMM_COL_MAJOR) return GEMM_ERR_INVALID_VALUE;
+    if (dtype == gemm::kElemFp8 && (order_a != GEMM_ROW_MAJOR || order_b != GEMM_COL_MAJOR))
+        return GEMM_ERR_INVALID_VALUE;
     *kernel = "none";
     *core_rows = *core_cols = 0;
     *workspace_bytes = 0;
@@ -841,7 +914,7 @@ gemm_status_t gemm_plan(int dtype, int64_t M, int64_t N, int64_t K, gemm_order_t
 
 size_t gemm_workspace_size(int dtype, int64_t M, int64_t N, int64_t K, gemm_order_t order_a,
                            gemm_order_t order_b, gemm_order_t order_c) {
-    if (M <= 0 || N <= 0 || K <= 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX || dtype < 0 || dtype > 2) return 0;
+    if (M <= 0 || N <= 0 || K <= 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX || dtype < 0 || dtype > 3) return 0;
     for (int o : {(int)order_a, (int)order_b, (int)order_c})
         if (o != GEMM_ROW_MAJOR && o != GEMM_COL_MAJOR) return 0;
     gemm::DeviceInfo dev;

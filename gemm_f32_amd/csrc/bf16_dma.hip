@@ -1,20 +1,24 @@
-// BF16-input, FP32-accumulate GEMM with direct global->LDS copies: v_mfma_f32_32x32x16_bf16.
+// 16-bit- and 8-bit-input, FP32-accumulate GEMM with direct global->LDS copies:
+// v_mfma_f32_32x32x16_bf16 / _f16, and for the OCP 8-bit formats (E4M3, E5M2)
+// v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales.
 //
 // Same operation as bf16_mfma.hip ("GEMM, step by step", Concept; "A06 - Tiled Matrix
 // Multiply (GEMM)", "Matrix cores: MFMA and Tensor Cores"), for the layout a BF16 GEMM
 // usually has (row-major A, column-major B: both operands contiguous along k), arranged so
 // that the k-loop is one branch-free block:
 //
-//  * Block tile BM x BN, k-tiles BK = 64 deep, WGM x WGN wavefronts.  At 256 x 256 four
+//  * Block tile BM x BN, k-tiles of 128 bytes per row (BK = 64 16-bit or 128 8-bit
+//    elements), WGM x WGN wavefronts.  At 256 x 256 four
 //    wavefronts in a 2 x 2 grid own 128 x 128 of C each (4 x 4 fragments of 32 x 32 = 256
 //    accumulators per lane), one per SIMD.  At 256 x 128, eight wavefronts of 64 x 64, two
 //    per SIMD.
-//  * LDS: one row of BK bf16 (128 bytes, 8 chunks of 16 bytes) per row of each tile, chunk
+//  * LDS: one row of BK elements (128 bytes, 8 chunks of 16 bytes) per row of each tile, chunk
 //    c of row r stored at c ^ s(r), s(r) = (r mod 8) xor bit 3 of r, so that the 32 rows
 //    read at one logical chunk fall on distinct 16-byte bank groups.  A lane's 16-byte read
 //    is one instruction's operand: at k-step s (16 k) lanes 0-31 read chunk 2 s, lanes
 //    32-63 chunk 2 s + 1, for A and B alike (the pairing of k between the two operands is
-//    what matters, not its order).
+//    what matters, not its order).  With 8-bit inputs an operand is 32 bytes: at k-step s
+//    (64 k) lanes 0-31 read chunks 4 s and 4 s + 1, lanes 32-63 chunks 4 s + 2 and 4 s + 3.
 //  * Accumulator layout of a 32 x 32 fragment: lane l, register r holds row
 //    8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
 //  * Copies: buffer loads of 1 KB per instruction straight into LDS, a lane fetching the
@@ -22,7 +26,8 @@
 //    the copy's row block are a scalar offset.  Each wavefront's buffer covers exactly the
 //    rows of its copy block that exist, so rows past M (N) read as zero: edge tiles need no
 //    separate code in the k-loop.  (Buffer loads, like global ones, accept the 2-byte
-//    aligned rows of odd leading dimensions on gfx950.)
+//    aligned rows of odd leading dimensions on gfx950, and the byte-aligned rows of 8-bit
+//    operands.)
 //  * Staging ahead ("GEMM Optimization", V3: stage the next tile while the current one is
 //    multiplied), software-pipelined across k-tiles, one barrier per k-tile: at 256 x 256 a
 //    ring of five half-stage buffers (an A or a B tile each, 160 KB) that lets each copy
@@ -38,8 +43,8 @@
 //  * Tile order from the XCD-aware, group-M scheduler in common.hpp.
 //
 // Requirements (checked by the host): row-major A and column-major B after the
-// column-major-C swap (both k-contiguous), K >= 64, and byte offsets of a wavefront's row
-// block below 2^31.  Any M, N.
+// column-major-C swap (both k-contiguous), K >= 64 for 16-bit inputs (any K >= 1 for 8-bit
+// ones), and byte offsets of a wavefront's row block below 2^31.  Any M, N.
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "launch.hpp"
@@ -49,10 +54,14 @@ namespace gemm {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16;
 typedef __attribute__((address_space(3))) void lds_void;
+
+// input element types of the kernel: 16-bit, or 8-bit as kInFp8 + 2 fmt_a + fmt_b
+enum InType { kInBf16 = 0, kInF16 = 1, kInFp8 = 2 };
 
 // gfx950 buffer resource, word 3: 32-bit unformatted data, no swizzle
 constexpr int kBufWord3 = 0x00020000;
@@ -62,12 +71,17 @@ constexpr int kBufWord3 = 0x00020000;
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 // RING: the five-buffer half-stage pipeline of the main loop below (BM == BN) instead of S
-// whole stages
-template <int BM_, int BN_, int WGM_, int WGN_, int CSPAN_, int S_, bool RING_ = false>
+// whole stages.  ES: bytes per input element, 2 (bf16, fp16) or 1 (the 8-bit formats); a
+// k-tile is one 128-byte row either way, 64 or 128 k deep.
+template <int BM_, int BN_, int WGM_, int WGN_, int CSPAN_, int S_, bool RING_ = false, int ES_ = 2>
 struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, BK = 64, WGM = WGM_, WGN = WGN_, S = S_;
+    static constexpr int ES = ES_;
+    static constexpr int BM = BM_, BN = BN_, BK = 128 / ES, WGM = WGM_, WGN = WGN_, S = S_;
     static constexpr bool RING = RING_;
-    static constexpr int ROW = BK * 2;                       // LDS row bytes (8 chunks)
+    static constexpr int ROW = BK * ES;                      // LDS row bytes (8 chunks)
+    // k of one matrix instruction (32x32x16 on 16-bit inputs, 32x32x64 on 8-bit ones) and the
+    // 16-byte chunks of a row each lane supplies to it
+    static constexpr int KSTEP = ES == 2 ? 16 : 64, FC = KSTEP * ES / 32;
     static constexpr int RPC = 1024 / ROW;                   // tile rows per 1 KB copy
     static constexpr int NW = WGM * WGN, THREADS = 64 * NW;
     static constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -76,7 +90,7 @@ struct Cfg {
     static constexpr int A_RPW = BM / NW, B_RPW = BN / NW;   // tile rows copied per wavefront
     static constexpr int A_DMA = A_RPW / RPC, B_DMA = B_RPW / RPC;
     static constexpr int DMA = A_DMA + B_DMA;                // copies per wavefront per k-tile
-    static constexpr int SUB = BK / 16;                      // k-steps per k-tile
+    static constexpr int SUB = BK / KSTEP;                   // k-steps per k-tile
     static constexpr int MF = FM * FN;                       // matrix instructions per k-step
     static constexpr int RD = FM + FN;                       // fragment reads per k-step
     // the copies of k-tile t are spread over CSPAN k-steps (the last one of k-tile t - S
@@ -84,6 +98,7 @@ struct Cfg {
     // HEAD of them fall on the first of those k-steps
     static constexpr int CSPAN = CSPAN_, W = CSPAN * MF;
     static constexpr int HEAD = (MF * DMA + W - 1) / W;
+    static_assert(ES == 1 || ES == 2, "element size");
     static_assert(FM >= 1 && FN >= 1 && A_DMA >= 1 && B_DMA >= 1, "tile too small");
     static_assert(A_RPW % 16 == 0 && B_RPW % 16 == 0, "copy blocks start at even swizzle parity");
     static_assert(RD <= MF, "one fragment read per instruction slot");
@@ -103,17 +118,30 @@ struct Cfg {
 
 using Cfg256 = Cfg<256, 256, 2, 2, 2, 2, true>;
 
+// 8-bit configurations: 256 x 256 on the ring, 256 x 128 with three stages (copies spread over
+// both k-steps of a 128-deep k-tile)
+using Cfg256F8 = Cfg<256, 256, 2, 2, 1, 2, true, 1>;
+using Cfg256x128F8 = Cfg<256, 128, 4, 2, 2, 3, false, 1>;
+
+// IT: input type, kInBf16, kInF16 or, for 8-bit inputs, kInFp8 + 2 fmt_a + fmt_b (format 0 E4M3,
+// 1 E5M2, the operand-format codes of the gfx950 8-bit matrix instruction).
 // MODE: kPlain, kBatched (entry blockIdx.z of a strided batch), kEpilogue (the fused epilogue,
 // one problem) or kSplitK (K slice blockIdx.y of one problem).
-template <typename C, bool VEC_C, bool F16, int MODE>
+// TK: K below one 16-byte chunk of 8-bit elements (K < 16): no k-loop, the K tail read byte by
+// byte.  (A separate kernel: with byte loads anywhere in the function, the compiler adds waits
+// for all copies in flight before every LDS read of the k-loop.)
+template <typename C, bool VEC_C, int IT, int MODE, bool TK = false>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::NW / 4, C::NW / 4)))
 void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int group_m) {
     constexpr bool BATCH = MODE == kBatched, EPI = MODE == kEpilogue;
+    static_assert((IT >= kInFp8) == (C::ES == 1), "8-bit inputs take the 8-bit configurations");
+    static_assert(!TK || C::ES == 1, "byte-wise K tail for 8-bit inputs only");
+    constexpr int ES = C::ES;
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, FM = C::FM, FN = C::FN, SUB = C::SUB;
     constexpr int ROW = C::ROW, MF = C::MF;
     __shared__ __align__(16) unsigned char smem[C::LDS];
     if constexpr (BATCH) p.select(blockIdx.z);
-    if constexpr (MODE == kSplitK) p.select(blockIdx.y, 2);
+    if constexpr (MODE == kSplitK) p.select(blockIdx.y, ES);
 
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
@@ -123,20 +151,20 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = (wave / C::WGN) * C::WM, wn = (wave % C::WGN) * C::WN;
     const int nk = p.K / BK;                  // whole k-tiles; a K tail follows the loop
-    const u16* A = static_cast<const u16*>(p.A);
-    const u16* B = static_cast<const u16*>(p.B);
+    const unsigned char* A = static_cast<const unsigned char*>(p.A);
+    const unsigned char* B = static_cast<const unsigned char*>(p.B);
 
     // ---- copy plan: wavefront w fills rows w A_RPW .. +A_RPW-1 of the A tile (and the same
     // for B), RPC rows per copy; lane l fetches row l / 8 of the copy at logical chunk
     // (l % 8) ^ s(row), where s(row) depends on l and on the parity of the copy only
-    // (copy blocks start at multiples of 16 rows).
+    // (copy blocks start at multiples of 16 rows).  Offsets are in bytes.
     const int lr = lane / 8;
     unsigned aoff[2], boff[2];
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
         const int c = (lane % 8) ^ swz(lr + C::RPC * par);
-        aoff[par] = (unsigned)((lr * p.lda + c * 8) * 2);
-        boff[par] = (unsigned)((lr * p.ldb + c * 8) * 2);
+        aoff[par] = (unsigned)(lr * p.lda * ES + c * 16);
+        boff[par] = (unsigned)(lr * p.ldb * ES + c * 16);
     }
     // buffer resources over the rows of this wavefront's copy blocks that exist: the
     // hardware returns zero for the rest (the host checks that offsets fit in 31 bits)
@@ -146,11 +174,11 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
     const int avalid = __builtin_amdgcn_readfirstlane(max(0, min(C::A_RPW, p.M - arow0)));
     const int bvalid = __builtin_amdgcn_readfirstlane(max(0, min(C::B_RPW, p.N - brow0)));
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(avalid > 0 ? A + (int64_t)arow0 * p.lda : A), (short)0, (int)(avalid * p.lda * 2), kBufWord3);
+        (void*)(avalid > 0 ? A + (int64_t)arow0 * p.lda * ES : A), (short)0, (int)(avalid * p.lda * ES), kBufWord3);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(bvalid > 0 ? B + (int64_t)brow0 * p.ldb : B), (short)0, (int)(bvalid * p.ldb * 2), kBufWord3);
+        (void*)(bvalid > 0 ? B + (int64_t)brow0 * p.ldb * ES : B), (short)0, (int)(bvalid * p.ldb * ES), kBufWord3);
     // byte distance between consecutive copies of a wavefront
-    const int astep = C::RPC * (int)p.lda * 2, bstep = C::RPC * (int)p.ldb * 2;
+    const int astep = C::RPC * (int)p.lda * ES, bstep = C::RPC * (int)p.ldb * ES;
     // copy j (of DMA) of k-tile kt (source) into stage st.  (The LDS pointer is a named
     // variable: cast inline in the builtin's argument list, the host pass of this compiler
     // silently drops the kernel's launch stub.)
@@ -161,11 +189,11 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
         unsigned char* s = smem + st * C::STAGE;
         if (j < C::A_DMA) {
             lds_void* dst = (lds_void*)(s + (wave * C::A_DMA + j) * 1024);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, aoff[j & 1] + j * astep, kt * (BK * 2), 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, aoff[j & 1] + j * astep, kt * ROW, 0, 0);
         } else {
             const int jb = j - C::A_DMA;
             lds_void* dst = (lds_void*)(s + C::A_BYTES + (wave * C::B_DMA + jb) * 1024);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, boff[jb & 1] + jb * bstep, kt * (BK * 2), 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, boff[jb & 1] + jb * bstep, kt * ROW, 0, 0);
         }
     };
     // the copies that fall on slot `slot` of the window (copy q sits at slot q W / DMA)
@@ -185,17 +213,37 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    bf16x8 fa[2][FM], fb[2][FN];
+    // a lane's operand of one matrix instruction: 8 bf16 / fp16 values, or 32 8-bit values (two
+    // chunks).  At k-step s lanes 0-31 take the FC chunks FC (2 s) .. and lanes 32-63 the FC
+    // chunks after them, for A and B alike (which k goes to which lane only has to agree
+    // between the two operands).
+    using Frag = std::conditional_t<ES == 2, bf16x8, i32x8>;
+    Frag fa[2][FM], fb[2][FN];
+    auto frag_at = [&](const unsigned char* row, int s) -> Frag {
+        if constexpr (C::FC == 1) {
+            return *reinterpret_cast<const bf16x8*>(row + (((2 * s + h) ^ sw) << 4));
+        } else {
+            // (read as 16-bit vectors: with that access type the compiler adds no wait for the
+            // copies in flight before these reads; the waits in the loop below order them)
+            const i32x4 lo = __builtin_bit_cast(i32x4, *reinterpret_cast<const bf16x8*>(row + (((4 * s + 2 * h) ^ sw) << 4)));
+            const i32x4 hi = __builtin_bit_cast(i32x4, *reinterpret_cast<const bf16x8*>(row + (((4 * s + 2 * h + 1) ^ sw) << 4)));
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
     // fragment read `m` (A fragments first, then B) of k-step s of stage st into buffer b
     auto read_slot = [&](int st, int s, int m, int b) {
         const unsigned char* base = smem + st * C::STAGE;
-        const int coff = ((2 * s + h) ^ sw) << 4;
-        if (m < FM) fa[b][m] = *reinterpret_cast<const bf16x8*>(base + a_off + m * 32 * ROW + coff);
-        else if (m < C::RD) fb[b][m - FM] = *reinterpret_cast<const bf16x8*>(base + b_off + (m - FM) * 32 * ROW + coff);
+        if (m < FM) fa[b][m] = frag_at(base + a_off + m * 32 * ROW, s);
+        else if (m < C::RD) fb[b][m - FM] = frag_at(base + b_off + (m - FM) * 32 * ROW, s);
     };
     auto mfma = [&](int m, int b) {
         const int i = m / FN, j = m % FN;
-        acc[i][j] = mma_32x32x16<F16>(fa[b][i], fb[b][j], acc[i][j]);
+        if constexpr (IT >= kInFp8)     // unit scales (E8M0 127 = 2^0): a plain 8-bit product
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[b][i], fb[b][j], acc[i][j],
+                                                                         (IT - kInFp8) >> 1, (IT - kInFp8) & 1,
+                                                                         0, 127, 0, 127);
+        else
+            acc[i][j] = mma_32x32x16<IT == kInF16>(fa[b][i], fb[b][j], acc[i][j]);
     };
 
     // ---- software pipeline over k-tiles, S LDS stages (tile t in stage t % S).  Iteration
@@ -211,7 +259,9 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
     // instructions.  Past the end of K the copies repeat the last tile into a stage nobody
     // reads, and the fragments read for a tile nk are never used, so the loop body has no
     // branch.
-    if constexpr (C::RING) {
+    if constexpr (TK) {
+        // K < 16: no whole k-tile
+    } else if constexpr (C::RING) {
         // ---- ring of five half-stages (160 KB at 256 x 256): the A tile of k-tile t lives in
         // buffer 2t mod 5, its B tile in buffer 2t+1 mod 5.  The barrier of iteration kt (before
         // its last k-step) frees both buffers of tile kt.  The B tile of kt+2 is copied into the
@@ -225,20 +275,16 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
             const int last = nk - 1;
             const int rb_off = b_off - C::A_BYTES;
             auto read_ring = [&](int abuf, int bbuf, int s, int m, int b) {
-                const int coff = ((2 * s + h) ^ sw) << 4;
-                if (m < FM)
-                    fa[b][m] = *reinterpret_cast<const bf16x8*>(smem + abuf * C::A_BYTES + a_off + m * 32 * ROW + coff);
-                else if (m < C::RD)
-                    fb[b][m - FM] = *reinterpret_cast<const bf16x8*>(smem + bbuf * C::A_BYTES + rb_off +
-                                                                     (m - FM) * 32 * ROW + coff);
+                if (m < FM) fa[b][m] = frag_at(smem + abuf * C::A_BYTES + a_off + m * 32 * ROW, s);
+                else if (m < C::RD) fb[b][m - FM] = frag_at(smem + bbuf * C::A_BYTES + rb_off + (m - FM) * 32 * ROW, s);
             };
             auto issue_a = [&](int j, int kt, int buf) {
                 lds_void* dst = (lds_void*)(smem + buf * C::A_BYTES + (wave * C::A_DMA + j) * 1024);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, aoff[j & 1] + j * astep, kt * (BK * 2), 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, aoff[j & 1] + j * astep, kt * ROW, 0, 0);
             };
             auto issue_b = [&](int j, int kt, int buf) {
                 lds_void* dst = (lds_void*)(smem + buf * C::A_BYTES + (wave * C::B_DMA + j) * 1024);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, boff[j & 1] + j * bstep, kt * (BK * 2), 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, boff[j & 1] + j * bstep, kt * ROW, 0, 0);
             };
             // instruction slots between two copies: B over the last k-step, A over the others
             constexpr int BSL = MF / C::B_DMA, ASL = (SUB - 1) * MF / C::A_DMA;
@@ -343,41 +389,56 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
     // ---- K tail: one more k-tile staged through registers with bounds checks and zero fill
     // into the LDS positions the copies would have filled (stage 0).  Branch-free, so that
     // all loads are in flight together: every lane loads 16 in-bounds bytes -- its chunk
-    // when the chunk lies inside K, else the last 8 elements of the row -- and keeps what
+    // when the chunk lies inside K, else the last CE elements of the row -- and keeps what
     // belongs to its chunk (shifted into place for the chunk that straddles K), zero for the
-    // rest and for rows past M or N.  K >= 64 (host check), so a row holds 8 elements. ----
+    // rest and for rows past M or N.  Rows shorter than one chunk (8-bit inputs with K < 16,
+    // the TK kernel; 16-bit inputs have K >= 64 by the host check) are read byte by byte. ----
     if (p.K % BK != 0) {                      // uniform
+        constexpr int CE = 16 / ES;           // elements per 16-byte chunk
         const int k0 = nk * BK;
         uint4 v[C::DMA];
-        // the chunk of copy j that this lane stages: tile row, first k, row in range
-        auto chunk = [&](int j, const u16*& src, int& k, bool& keep) {
+        // the chunk of copy j that this lane stages: its row, first k, row in range
+        auto chunk = [&](int j, const unsigned char*& src, int& k, bool& keep) {
             const bool is_a = j < C::A_DMA;
             const int jj = is_a ? j : j - C::A_DMA;
             const int tr = wave * (is_a ? C::A_RPW : C::B_RPW) + jj * C::RPC + lr;
             const int grow = (is_a ? m0 : n0) + tr, rows = is_a ? p.M : p.N;
-            src = (is_a ? A : B) + (int64_t)min(grow, rows - 1) * (is_a ? p.lda : p.ldb);
-            k = k0 + 8 * ((lane % 8) ^ swz(lr + C::RPC * (jj & 1)));
+            src = (is_a ? A : B) + (int64_t)min(grow, rows - 1) * (is_a ? p.lda : p.ldb) * ES;
+            k = k0 + CE * ((lane % 8) ^ swz(lr + C::RPC * (jj & 1)));
             keep = grow < rows && k < p.K;
         };
+        if constexpr (!TK) {                  // K >= CE (16-bit inputs: K >= 64)
 #pragma unroll
-        for (int j = 0; j < C::DMA; ++j) {    // all loads first
-            const u16* src; int k; bool keep;
-            chunk(j, src, k, keep);
-            v[j] = load16(src + (k + 8 <= p.K ? k : p.K - 8));
-        }
+            for (int j = 0; j < C::DMA; ++j) {    // all loads first
+                const unsigned char* src; int k; bool keep;
+                chunk(j, src, k, keep);
+                v[j] = load16(src + (int64_t)(k + CE <= p.K ? k : p.K - CE) * ES);
+            }
 #pragma unroll
-        for (int j = 0; j < C::DMA; ++j) {    // then keep, shift or clear, as arithmetic
-            const u16* src; int k; bool keep;
-            chunk(j, src, k, keep);
-            // straddling chunk: its r valid elements are the top r of the last 8 of the row
-            const int r = min(max(p.K - k, 1), 7);
-            const unsigned sh = 16 * (8 - r);                 // bits to drop, 16 .. 112
-            const uint64_t lo = v[j].x | (uint64_t)v[j].y << 32, hi = v[j].z | (uint64_t)v[j].w << 32;
-            const uint64_t slo = sh < 64 ? (lo >> sh) | (hi << (64 - sh)) : hi >> (sh - 64);
-            const uint64_t shi = sh < 64 ? hi >> sh : 0;
-            const uint64_t full = k + 8 <= p.K ? ~0ull : 0ull, kept = keep ? ~0ull : 0ull;
-            const uint64_t olo = ((lo & full) | (slo & ~full)) & kept, ohi = ((hi & full) | (shi & ~full)) & kept;
-            v[j] = make_uint4((unsigned)olo, (unsigned)(olo >> 32), (unsigned)ohi, (unsigned)(ohi >> 32));
+            for (int j = 0; j < C::DMA; ++j) {    // then keep, shift or clear, as arithmetic
+                const unsigned char* src; int k; bool keep;
+                chunk(j, src, k, keep);
+                // straddling chunk: its r valid elements are the top r of the last CE of the row
+                const int r = min(max(p.K - k, 1), CE - 1);
+                const unsigned sh = 8 * ES * (CE - r);            // bits to drop, 8 ES .. 128 - 8 ES
+                const uint64_t lo = v[j].x | (uint64_t)v[j].y << 32, hi = v[j].z | (uint64_t)v[j].w << 32;
+                const uint64_t slo = sh < 64 ? (lo >> sh) | (hi << (64 - sh)) : hi >> (sh - 64);
+                const uint64_t shi = sh < 64 ? hi >> sh : 0;
+                const uint64_t full = k + CE <= p.K ? ~0ull : 0ull, kept = keep ? ~0ull : 0ull;
+                const uint64_t olo = ((lo & full) | (slo & ~full)) & kept, ohi = ((hi & full) | (shi & ~full)) & kept;
+                v[j] = make_uint4((unsigned)olo, (unsigned)(olo >> 32), (unsigned)ohi, (unsigned)(ohi >> 32));
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < C::DMA; ++j) {
+                const unsigned char* src; int k; bool keep;
+                chunk(j, src, k, keep);
+                unsigned w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int b = 0; b < 16; ++b)
+                    if (keep && k + b < p.K) w[b / 4] |= (unsigned)src[k + b] << (8 * (b % 4));
+                v[j] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
         }
         __syncthreads();                      // every wavefront is done with the stages
 #pragma unroll
@@ -458,27 +519,43 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
     }
 }
 
-// One launch of configuration C in mode MODE: tiles along x, grid_y K slices, grid_z batch entries.
-template <typename C, int MODE>
-hipError_t launch_cfg(const typename ModeArgT<MODE>::type& p, const Launch& l, bool f16, int grid_y = 1) {
+// One launch of configuration C in mode MODE for input type `it`: tiles along x, grid_y K
+// slices, grid_z batch entries.
+template <typename C, int MODE, int IT, bool TK = false>
+hipError_t launch_it(const typename ModeArgT<MODE>::type& p, const Launch& l, int grid_y) {
     const int tiles_m = (p.M + C::BM - 1) / C::BM, tiles_n = (p.N + C::BN - 1) / C::BN;
     const dim3 grid((unsigned)tiles_m * tiles_n, (unsigned)grid_y, MODE == kBatched ? l.batch : 1), block(C::THREADS);
-    if (f16 && l.vec_c)
-        hipLaunchKernelGGL((k_bf16_dma<C, true, true, MODE>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
-    else if (f16)
-        hipLaunchKernelGGL((k_bf16_dma<C, false, true, MODE>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
-    else if (l.vec_c)
-        hipLaunchKernelGGL((k_bf16_dma<C, true, false, MODE>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
+    if (l.vec_c)
+        hipLaunchKernelGGL((k_bf16_dma<C, true, IT, MODE, TK>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
     else
-        hipLaunchKernelGGL((k_bf16_dma<C, false, false, MODE>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
+        hipLaunchKernelGGL((k_bf16_dma<C, false, IT, MODE, TK>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
     return hipGetLastError();
 }
 
-template <typename C>
-hipError_t launch_any(const Problem& p, const Launch& l, bool f16) {
-    if (l.batch > 1) return launch_cfg<C, kBatched>(batch_arg(p, l, 2), l, f16);
-    return launch_cfg<C, kPlain>(p, l, f16);
+template <typename C, int MODE, bool TK = false>
+hipError_t launch_cfg(const typename ModeArgT<MODE>::type& p, const Launch& l, int it, int grid_y = 1) {
+    if constexpr (C::ES == 2) {
+        if (it == kInBf16) return launch_it<C, MODE, kInBf16>(p, l, grid_y);
+        if (it == kInF16) return launch_it<C, MODE, kInF16>(p, l, grid_y);
+    } else {
+        switch (it) {
+            case kInFp8 + 0: return launch_it<C, MODE, kInFp8 + 0, TK>(p, l, grid_y);
+            case kInFp8 + 1: return launch_it<C, MODE, kInFp8 + 1, TK>(p, l, grid_y);
+            case kInFp8 + 2: return launch_it<C, MODE, kInFp8 + 2, TK>(p, l, grid_y);
+            case kInFp8 + 3: return launch_it<C, MODE, kInFp8 + 3, TK>(p, l, grid_y);
+            default: break;
+        }
+    }
+    return hipErrorInvalidValue;
 }
+
+template <typename C>
+hipError_t launch_any(const Problem& p, const Launch& l, int it) {
+    if (l.batch > 1) return launch_cfg<C, kBatched>(batch_arg(p, l, C::ES), l, it);
+    return launch_cfg<C, kPlain>(p, l, it);
+}
+
+int in16(bool f16) { return f16 ? kInF16 : kInBf16; }
 
 }  // namespace
 
@@ -487,6 +564,11 @@ bool bf16_dma_applies(const Problem& p, const Launch&, int, int) {
     const int64_t lim = (int64_t)1 << 31;
     return p.oa == kRow && p.ob == kCol && p.K >= 64 && (int64_t)64 * p.lda * 2 < lim &&
            (int64_t)64 * p.ldb * 2 < lim;
+}
+
+bool fp8_dma_applies(const Problem& p) {
+    const int64_t lim = (int64_t)1 << 31;
+    return p.oa == kRow && p.ob == kCol && p.K >= 1 && (int64_t)64 * p.lda < lim && (int64_t)64 * p.ldb < lim;
 }
 
 // Configurations.  256 x 256: four wavefronts of 128 x 128 (one per SIMD, 256 accumulators
@@ -499,14 +581,14 @@ bool bf16_dma_applies(const Problem& p, const Launch&, int, int) {
 // the copies spread over four k-steps (1350 cycles per k-tile against 1024; four wavefronts of
 // 128 x 64: 1425 with three stages, 1540-1630 with two).
 hipError_t launch_bf16_dma(const Problem& p, const Launch& l, int bm, int bn, bool f16) {
-    if (bm == 256 && bn == 256) return launch_any<Cfg256>(p, l, f16);
-    if (bm == 256 && bn == 128) return launch_any<Cfg<256, 128, 4, 2, 4, 3>>(p, l, f16);
+    if (bm == 256 && bn == 256) return launch_any<Cfg256>(p, l, in16(f16));
+    if (bm == 256 && bn == 128) return launch_any<Cfg<256, 128, 4, 2, 4, 3>>(p, l, in16(f16));
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_bf16_dma_epi(const EpiProblem& p, const Launch& l, int bm, int bn, bool f16) {
-    if (bm == 256 && bn == 256) return launch_cfg<Cfg256, kEpilogue>(p, l, f16);
-    if (bm == 256 && bn == 128) return launch_cfg<Cfg<256, 128, 4, 2, 4, 3>, kEpilogue>(p, l, f16);
+    if (bm == 256 && bn == 256) return launch_cfg<Cfg256, kEpilogue>(p, l, in16(f16));
+    if (bm == 256 && bn == 128) return launch_cfg<Cfg<256, 128, 4, 2, 4, 3>, kEpilogue>(p, l, in16(f16));
     return hipErrorInvalidValue;
 }
 
@@ -514,10 +596,21 @@ hipError_t launch_bf16_dma_epi(const EpiProblem& p, const Launch& l, int bm, int
 // rows, N % 4 == 0), then the slabs are added to C in slice order.
 hipError_t launch_bf16_dma_split(const SplitProblem& s, int slices, const Launch& l, int bm, int bn, bool f16) {
     hipError_t err = hipErrorInvalidValue;
-    if (bm == 256 && bn == 256) err = launch_cfg<Cfg256, kSplitK>(s, l, f16, slices);
-    else if (bm == 256 && bn == 128) err = launch_cfg<Cfg<256, 128, 4, 2, 4, 3>, kSplitK>(s, l, f16, slices);
+    if (bm == 256 && bn == 256) err = launch_cfg<Cfg256, kSplitK>(s, l, in16(f16), slices);
+    else if (bm == 256 && bn == 128) err = launch_cfg<Cfg<256, 128, 4, 2, 4, 3>, kSplitK>(s, l, in16(f16), slices);
     if (err != hipSuccess) return err;
     return launch_add_slabs(s.C, s.ldc, s.M, s.N, s.part, slices - 1, l);
+}
+
+// 8-bit inputs (format codes 0 E4M3, 1 E5M2) on the same skeleton: a k-tile is 128 deep, one
+// 32 x 32 x 64 matrix instruction per fragment pair and k-step, with unit block scales.
+hipError_t launch_fp8_dma(const Problem& p, const Launch& l, int bm, int bn, int fmt_a, int fmt_b) {
+    if ((fmt_a != 0 && fmt_a != 1) || (fmt_b != 0 && fmt_b != 1)) return hipErrorInvalidValue;
+    const int it = kInFp8 + 2 * fmt_a + fmt_b;
+    if (p.K < 16) return launch_cfg<Cfg256x128F8, kPlain, true>(p, l, it);     // either tile: no k-loop
+    if (bm == 256 && bn == 256) return launch_cfg<Cfg256F8, kPlain>(p, l, it);
+    if (bm == 256 && bn == 128) return launch_cfg<Cfg256x128F8, kPlain>(p, l, it);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace gemm

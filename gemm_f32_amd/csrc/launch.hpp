@@ -21,12 +21,17 @@ hipError_t launch_f32_mfma(const Problem& p, const Launch& l, int bm);
 bool f32_dma_applies(const Problem& p, const Launch& l, int bm, int bn);
 hipError_t launch_f32_dma(const Problem& p, const Launch& l, int bm, int bn);
 // Input element types of the kernels that take more than one
-constexpr int kElemF32 = 0, kElemBf16 = 1, kElemF16 = 2;
+constexpr int kElemF32 = 0, kElemBf16 = 1, kElemF16 = 2, kElemFp8 = 3;
 // BF16 direct-copy kernel (bf16_dma.hip): row-major A, column-major B, any M, N, K >= 64,
 // 256x256 or 256x128 tiles; bf16_dma_applies checks the layouts and offset ranges.  With
 // f16 the same kernel on IEEE fp16 inputs.
 bool bf16_dma_applies(const Problem& p, const Launch& l, int bm, int bn);
 hipError_t launch_bf16_dma(const Problem& p, const Launch& l, int bm, int bn, bool f16 = false);
+// The same kernel on 8-bit inputs (OCP formats, fmt 0 E4M3, 1 E5M2 per operand): row-major A,
+// column-major B, any M, N and K >= 1, 256x256 or 256x128 tiles; fp8_dma_applies checks the
+// layouts and offset ranges.
+bool fp8_dma_applies(const Problem& p);
+hipError_t launch_fp8_dma(const Problem& p, const Launch& l, int bm, int bn, int fmt_a, int fmt_b);
 // BF16 matrix-core kernel (bf16_mfma.hip); tile is one of 256x128, 128x128, 64x64;
 // f16: fp16 inputs
 hipError_t launch_bf16_mfma(const Problem& p, const Launch& l, int bm, int bn, bool f16 = false);

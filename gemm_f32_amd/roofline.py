@@ -28,6 +28,7 @@ MI355X_CUS = 256
 MI355X_CLOCK_HZ = 2.4e9
 MI355X_HBM_BYTES_PER_S = 8.0e12
 MI355X_BF16_DENSE_FLOPS = 2516.6e12        # 256 CU x 4096 flop/clk x 2.4 GHz
+MI355X_FP8_DENSE_FLOPS = 5033.2e12         # 256 CU x 8192 flop/clk x 2.4 GHz
 MI355X_FP32_FLOPS = 157.3e12               # 256 CU x 256 flop/clk x 2.4 GHz (packed FMA / MFMA)
 MI355X_FP32_VALU_UNPACKED_FLOPS = 78.6e12  # 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz
 
@@ -93,4 +94,7 @@ def kernel_model(M: int, N: int, K: int, bm: int, bn: int, bk: int, tm: int = 1,
 
 def mi355x_peak(dtype: str) -> float:
     # fp16 inputs: the same dense matrix-core peak as bf16 (2.5 PFLOP/s, published figures)
+    # 8-bit inputs (every E4M3 / E5M2 pairing): the dense fp8 peak (5.0 PFLOP/s, published figures)
+    if dtype in ("e4m3", "e5m2", "e4m3_e5m2", "e5m2_e4m3"):
+        return MI355X_FP8_DENSE_FLOPS
     return {"bf16": MI355X_BF16_DENSE_FLOPS, "f16": MI355X_BF16_DENSE_FLOPS, "f32": MI355X_FP32_FLOPS}[dtype]

@@ -36,7 +36,7 @@ class Workload:
     M: int
     N: int
     K: int
-    dtype: str               # "f32", "bf16" or "f16" (inputs); C is always fp32
+    dtype: str               # "f32", "bf16", "f16" or an 8-bit pairing of FP8_DTYPES (inputs); C is fp32
     order_a: int = ROW_MAJOR
     order_b: int = ROW_MAJOR
     order_c: int = ROW_MAJOR
@@ -57,6 +57,10 @@ WORKLOADS = {
         Workload("square4096_f32", 2, 4096, 4096, 4096, "f32"),
         Workload("square4096_bf16", 3, 4096, 4096, 4096, "bf16", ROW_MAJOR, COL_MAJOR),
         Workload("square4096_f16", 3, 4096, 4096, 4096, "f16", ROW_MAJOR, COL_MAJOR),
+        Workload("square4096_e4m3", 3, 4096, 4096, 4096, "e4m3", ROW_MAJOR, COL_MAJOR),
+        Workload("square4096_e5m2", 3, 4096, 4096, 4096, "e5m2", ROW_MAJOR, COL_MAJOR),
+        Workload("llm_ffn_up_2048x11008x4096_e4m3", 5, 2048, 11008, 4096, "e4m3", ROW_MAJOR, COL_MAJOR, ROW_MAJOR,
+                 "llm"),
         Workload("ragged1000_f32", 4, 1000, 1000, 1000, "f32"),
         Workload("ragged1000_bf16", 4, 1000, 1000, 1000, "bf16", ROW_MAJOR, COL_MAJOR),
         Workload("ragged4095x4097x1023_f32", 4, 4095, 4097, 1023, "f32"),

@@ -23,7 +23,7 @@
  * Ownership.  All matrix pointers are device pointers owned by the caller; A and B are
  * only read and must not overlap C.  C is only written, except by the fused-epilogue calls
  * with beta != 0, which read C's previous contents first.  Pointers need only their element's
- * natural alignment (4 bytes for float, 2 for bf16/fp16); no kernel needs more.  The plain
+ * natural alignment (4 bytes for float, 2 for bf16/fp16, 1 for fp8); no kernel needs more.  The plain
  * calls allocate no device memory and keep no state beyond a per-device property cache; the
  * _ws calls use the caller's workspace, and gemm_bf16_f32acc_noalloc a static array of the
  * library's (both below).
@@ -147,11 +147,36 @@ gemm_status_t gemm_bf16_f32acc(int64_t M, int64_t N, int64_t K,
  * type of the matrix cores ("A06 - Tiled Matrix Multiply (GEMM)", "Matrix cores: MFMA and
  * Tensor Cores"): the same kernels with the fp16 matrix instructions
  * (v_mfma_f32_32x32x16_f16, v_mfma_f32_16x16x32_f16); every product of two fp16 values is
- * exact in FP32, sums are FP32.  Layouts, kernel choice and errors as for BF16 (the BF16-only
- * ping-pong kernel is not offered). */
+ * exact in FP32, sums are FP32.  Layouts, kernel choice and errors as for BF16. */
 gemm_status_t gemm_f16_f32acc(int64_t M, int64_t N, int64_t K,
                               const uint16_t *A, int64_t lda, gemm_order_t order_a,
                               const uint16_t *B, int64_t ldb, gemm_order_t order_b,
+                              float *C, int64_t ldc, gemm_order_t order_c,
+                              hipStream_t stream);
+
+/* 8-bit floating-point inputs, FP32 products and sums, FP32 C.  The matrix cores take fp8 as
+ * well as 16-bit inputs with FP32 accumulation ("A06 - Tiled Matrix Multiply (GEMM)", "Matrix
+ * cores: MFMA and Tensor Cores", the table's inputs row), and quantized inference runs this same
+ * GEMM on a narrower operand type (same page, section 7, "Real-World Use Cases").  A and B hold
+ * one byte per element in one of the two OCP 8-bit formats, chosen per operand:
+ *   GEMM_FP8_E4M3  sign, 4 exponent bits (bias 7), 3 fraction bits; subnormals; no infinities;
+ *                  S.1111.111 is NaN; largest finite 448;
+ *   GEMM_FP8_E5M2  sign, 5 exponent bits (bias 15), 2 fraction bits; subnormals; IEEE infinities
+ *                  (S.11111.00) and NaNs (S.11111.xx, xx != 00); largest finite 57344.
+ * C[i][j] = sum over k of decode(A[i][k]) * decode(B[k][j]); every product is exact in FP32,
+ * sums are FP32 (v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales), so results agree with
+ * an exact sum to FP32 rounding of partial sums, as for BF16.  A NaN or infinite input gives a
+ * non-finite result in its row or column of C.
+ * Layout: A row-major and B column-major (both contiguous along k, one byte apart; the
+ * layout the 8-bit matrix instruction gathers its operands in); C either order; lda >= K and
+ * ldb >= K, any alignment.  Any M, N, K (K == 0: C = 0).  The library has no other kernel for
+ * these inputs and no split-K path for them.
+ * Errors: GEMM_ERR_INVALID_VALUE as for gemm_bf16_f32acc, and for a format other than the two
+ * below or A column-major or B row-major. */
+typedef enum { GEMM_FP8_E4M3 = 0, GEMM_FP8_E5M2 = 1 } gemm_fp8_t;
+gemm_status_t gemm_fp8_f32acc(int64_t M, int64_t N, int64_t K,
+                              const uint8_t *A, int64_t lda, gemm_order_t order_a, gemm_fp8_t format_a,
+                              const uint8_t *B, int64_t ldb, gemm_order_t order_b, gemm_fp8_t format_b,
                               float *C, int64_t ldc, gemm_order_t order_c,
                               hipStream_t stream);
 
@@ -189,7 +214,8 @@ const char *gemm_last_kernel(void);
 /* Library version, e.g. "0.1.0". */
 const char *gemm_version(void);
 
-/* What gemm_f32 (dtype 0), gemm_bf16_f32acc (dtype 1) or gemm_f16_f32acc (dtype 2) would run
+/* What gemm_f32 (dtype 0), gemm_bf16_f32acc (dtype 1), gemm_f16_f32acc (dtype 2) or
+ * gemm_fp8_f32acc (dtype 3; either format: the choice does not depend on it) would run
  * for a problem of these extents and orders, with tight leading dimensions, on a device of `cus` compute units,
  * without touching a device or launching anything; for tests of the kernel choice.
  *   *kernel     static name, as gemm_last_kernel() would report it ("none" for M == 0 or
@@ -201,8 +227,8 @@ const char *gemm_version(void);
  *   *workspace_bytes   the workspace with which gemm_f32_ws / gemm_bf16_f32acc_ws split K
  *               across workgroups for this problem (0: they never do).
  * Errors: GEMM_ERR_INVALID_VALUE for a null output pointer, cus <= 0, a dtype other than
- * 0, 1, 2, negative or too large extents (> INT_MAX) or an invalid order; outputs untouched
- * then. */
+ * 0 .. 3, negative or too large extents (> INT_MAX), an invalid order, or for dtype 3 orders
+ * gemm_fp8_f32acc refuses; outputs untouched then. */
 gemm_status_t gemm_plan(int dtype, int64_t M, int64_t N, int64_t K, gemm_order_t order_a,
                         gemm_order_t order_b, gemm_order_t order_c, int cus, const char **kernel,
                         int64_t *core_rows, int64_t *core_cols, size_t *workspace_bytes);

@@ -10,8 +10,10 @@ import gemm_f32_amd as g
 import gemm_inputs as gi
 import oracle
 
-# max |C - C_ref| / sum_k |A_ik B_kj|; fp16 inputs, like bf16, give exact products in FP32
-TOL = {"f32": 1e-5, "bf16": 1e-4, "f16": 1e-4}
+# max |C - C_ref| / sum_k |A_ik B_kj|; fp16 and 8-bit inputs, like bf16, give exact products in
+# FP32, so only the FP32 sums round
+TOL = {"f32": 1e-5, "bf16": 1e-4, "f16": 1e-4, **{d: 1e-4 for d in gi.FP8_DTYPES}}
+FP8_CODE = {"e4m3": g.Fp8.E4M3, "e5m2": g.Fp8.E5M2}
 
 
 def to_device(buf: np.ndarray):
@@ -28,11 +30,16 @@ def run(p: gi.Problem, algo=g.Algo.AUTO, A=None, B=None):
     B = to_device(p.B) if B is None else B
     n = gi.c_buffer_size(p.M, p.N, p.ldc, p.order_c)
     C = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
-    fn = {"f32": g.gemm_f32_algo, "bf16": g.gemm_bf16_f32acc_algo, "f16": g.gemm_f16_f32acc_algo}[p.dtype]
     print(f"[gpu] {p.dtype} algo={int(algo)} M={p.M} N={p.N} K={p.K} orders=({p.order_a},"
           f"{p.order_b},{p.order_c}) ld=({p.lda},{p.ldb},{p.ldc})", flush=True)
-    fn(algo, p.M, p.N, p.K, A.data_ptr(), p.lda, p.order_a, B.data_ptr(), p.ldb, p.order_b,
-       C.data_ptr(), p.ldc, p.order_c, torch.cuda.current_stream().cuda_stream)
+    stream = torch.cuda.current_stream().cuda_stream
+    if p.dtype in gi.FP8_DTYPES:           # one kernel family: no algorithm argument
+        g.gemm_fp8_f32acc(p.M, p.N, p.K, A.data_ptr(), p.lda, p.order_a, FP8_CODE[p.fmt_a], B.data_ptr(), p.ldb,
+                          p.order_b, FP8_CODE[p.fmt_b], C.data_ptr(), p.ldc, p.order_c, stream)
+    else:
+        fn = {"f32": g.gemm_f32_algo, "bf16": g.gemm_bf16_f32acc_algo, "f16": g.gemm_f16_f32acc_algo}[p.dtype]
+        fn(algo, p.M, p.N, p.K, A.data_ptr(), p.lda, p.order_a, B.data_ptr(), p.ldb, p.order_b,
+           C.data_ptr(), p.ldc, p.order_c, stream)
     torch.cuda.synchronize()
     return C.cpu().numpy()
 
@@ -52,7 +59,7 @@ def padding_untouched(p: gi.Problem, flat: np.ndarray) -> bool:
 @functools.lru_cache(maxsize=64)
 def _oracle_cached(key):
     p = _PROBLEMS[key]
-    return oracle.gemm(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b)
+    return oracle.gemm(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b, **gi.oracle_formats(p))
 
 
 _PROBLEMS: dict = {}
@@ -61,7 +68,7 @@ _PROBLEMS: dict = {}
 def reference(p: gi.Problem, key=None):
     """(C_ref, D) from the oracle; cached per key when one is given."""
     if key is None:
-        return oracle.gemm(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b)
+        return oracle.gemm(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b, **gi.oracle_formats(p))
     _PROBLEMS[key] = p
     return _oracle_cached(key)
 

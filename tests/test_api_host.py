@@ -71,6 +71,31 @@ def test_invalid_arguments_rejected_before_launch(fn, bad):
     assert _status(fn, g.Algo.AUTO, *args(**bad)) == INVALID
 
 
+def fp8_args(M=8, N=8, K=8, A=FAKE, lda=8, oa=R, fa=0, B=FAKE, ldb=8, ob=C_, fb=0, C=FAKE, ldc=8, oc=R):
+    return (M, N, K, A, lda, oa, fa, B, ldb, ob, fb, C, ldc, oc, 0)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(M=-1), dict(K=-1), dict(K=2**31), dict(lda=7), dict(ldb=7), dict(ldc=7), dict(oc=C_, ldc=7),
+    dict(oa=C_), dict(ob=R), dict(oa=C_, ob=R), dict(fa=2), dict(fb=-1), dict(A=0), dict(C=0),
+    dict(C=FAKE + 2),
+], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_fp8_invalid_arguments_rejected_before_launch(bad):
+    """8-bit operands: k-contiguous layouts only, two formats; any byte alignment of A and B."""
+    assert _status(g.gemm_fp8_f32acc, *fp8_args(**bad)) == INVALID
+
+
+def test_fp8_plan():
+    assert g.gemm_plan("e4m3", 4096, 4096, 4096, R, C_, R) == ("fp8_dma256x256", 4096, 4096)
+    assert g.gemm_plan("fp8", 256, 128, 384, R, C_, R)[0] == "fp8_dma256x128"
+    # a column-major C swaps the roles: 16 x 4096 becomes 4096 x 16
+    assert g.gemm_plan("fp8", 16, 4096, 4096, R, C_, C_) == ("fp8_dma256x128", 4096, 16)
+    assert g.gemm_plan("fp8", 8, 8, 0, R, C_, R)[0] == "zero_c"
+    assert g.gemm_plan("fp8", 64, 64, 64, R, C_, R, with_workspace=True)[3] == 0
+    with pytest.raises(g.GemmError):
+        g.gemm_plan("fp8", 64, 64, 64, C_, C_, R)
+
+
 def test_f32_needs_4_byte_alignment_bf16_needs_2():
     assert _status(F32, g.Algo.AUTO, *args(A=FAKE + 2)) == INVALID
     assert _status(BF16, g.Algo.AUTO, *args(A=FAKE + 1)) == INVALID

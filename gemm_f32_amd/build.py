@@ -1,6 +1,7 @@
 """Build libgemm.so (the HIP kernels and the C ABI) in-tree with hipcc for gfx950.
 
     python -m gemm_f32_amd.build          # or __graft_entry__.build()
+    python -m gemm_f32_amd.build --resource-table    # markdown table of the last build's report
 
 Each source compiles to an object under gemm_f32_amd/_build/ (in parallel), then they
 link into gemm_f32_amd/libgemm.so.  The compiler's per-kernel resource report (VGPRs,
@@ -89,5 +90,54 @@ def _resource_lines(log: str) -> str:
     return "\n".join(keep)
 
 
+def _first_template_arg(name: str) -> str:
+    """`k<Cfg<1, 2>, true, 3>(...)` -> `k<Cfg<1, 2>, ...>`: a kernel and its tile configuration."""
+    if "<" not in name:
+        return name.split("(")[0]
+    i = name.index("<") + 1
+    depth = 1
+    for j in range(i, len(name)):
+        c = name[j]
+        depth += c == "<"
+        depth -= c == ">"
+        if depth == 0 or (depth == 1 and c == ","):
+            return name[:j] + (", ...>" if c == "," else ">")
+    return name
+
+
+def resource_table(path: str = os.path.join(BUILD, "resource_usage.txt")) -> str:
+    """Markdown table of the compiler's resource report for the last build, one row per kernel
+    template and tile configuration (ranges over its instantiations): registers, LDS, scratch and
+    spills, occupancy."""
+    text = open(path).read()
+    blocks = re.split(r"^Function Name: ", text, flags=re.M)[1:]
+    rows = []
+    for b in blocks:
+        lines = b.splitlines()
+        fields = dict(re.match(r"\s*(.*?):\s*(.*)", ln).groups() for ln in lines[1:] if ":" in ln)
+        rows.append((lines[0].strip(), fields))
+    names = subprocess.run(["c++filt"], input="\n".join(n for n, _ in rows), capture_output=True,
+                           text=True).stdout.splitlines() if shutil.which("c++filt") else [n for n, _ in rows]
+    groups: dict = {}
+    for (_, f), name in zip(rows, names):
+        short = name.replace("void ", "").replace("gemm::(anonymous namespace)::", "").replace("gemm::", "")
+        groups.setdefault(_first_template_arg(short), []).append(f)
+
+    def rng(fs, key):
+        v = sorted({int(f.get(key, 0)) for f in fs})
+        return str(v[0]) if len(v) == 1 else f"{v[0]}-{v[-1]}"
+
+    out = ["| kernel (tile configuration) | instantiations | VGPRs | AGPRs | SGPRs | LDS bytes | scratch bytes/lane | "
+           "VGPR spills | SGPR spills | occupancy (waves/SIMD) |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for k, fs in groups.items():
+        out.append(f"| `{k}` | {len(fs)} | {rng(fs, 'VGPRs')} | {rng(fs, 'AGPRs')} | {rng(fs, 'TotalSGPRs')} | "
+                   f"{rng(fs, 'LDS Size [bytes/block]')} | {rng(fs, 'ScratchSize [bytes/lane]')} | "
+                   f"{rng(fs, 'VGPRs Spill')} | {rng(fs, 'SGPRs Spill')} | {rng(fs, 'Occupancy [waves/SIMD]')} |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--resource-table" in sys.argv:
+        print(resource_table())
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -715,28 +715,59 @@ gemm_status_t run_fused(In in, int64_t M, int64_t N, int64_t K, const uint16_t* 
     DeviceInfo dev;
     if (!device_info(dev) || !dev.supported) return GEMM_ERR_UNSUPPORTED_DEVICE;
 
-    EpiProblem ep{};
-    static_cast<Problem&>(ep) = p;
     // a column-major C's bias runs along its columns, the rows of the normalised C
-    ep.e = Epilogue{epi->alpha, epi->beta, epi->bias, row ? 0 : 1, (int)epi->activation, out16 ? 1 : 0};
-    Launch l = launch_for(p, stream);
-    l.vec_c = (p.ldc % 4 == 0) && aligned(C, out16 ? 8 : 16);
+    const Epilogue e{epi->alpha, epi->beta, epi->bias, row ? 0 : 1, (int)epi->activation, out16 ? 1 : 0};
+    // nothing to apply: the plain kernel on the same plan
+    const bool identity = e.alpha == 1.f && e.beta == 0.f && e.bias == nullptr && e.act == kActNone && !out16;
     hipError_t err = hipSuccess;
     const char* name = "epilogue_fill";
     if (K == 0) {
+        EpiProblem ep{};
+        static_cast<Problem&>(ep) = p;
+        ep.e = e;
+        Launch l = launch_for(p, stream);
+        l.vec_c = (p.ldc % 4 == 0) && aligned(C, out16 ? 8 : 16);
         err = launch_epi_fill(ep, l);
     } else {
+        // a core on one direct-copy tile and the strips that complete it, every part on the
+        // direct-copy kernels (the only ones that carry the epilogue), each strip on its own
+        // cheapest tile: 2048 x 11008 is 8 x 32 tiles of 256 x 256 (one round) and a 2048 x 2816
+        // strip of 256 x 128 tiles (one round), against 2.7 rounds of 256 x 128 tiles
+        const StripPricer dma_strips{kBf16DmaOpts, 2, kBf16DmaOpts, 0, dev.cus};
         Plan best;
         for (const TileOpt& o : kBf16DmaOpts) {
-            const Plan pl = plan_whole(p, o, dev.cus);
+            const Plan pl = plan_core(p, o, true, true, dev.cus, dma_strips);
             if (pl.cost < best.cost) best = pl;
         }
-        const int bm = best.opt.bm, bn = best.opt.bn;
-        l.group_m = pick_group_m((p.M + bm - 1) / bm, (p.N + bn - 1) / bn);
-        static const char* names[2][2] = {{"bf16_dma256x256_fused", "bf16_dma256x128_fused"},
-                                          {"f16_dma256x256_fused", "f16_dma256x128_fused"}};
-        name = names[in == In::F16 ? 1 : 0][bn == 256 ? 0 : 1];
-        err = launch_bf16_dma_epi(ep, l, bm, bn, in == In::F16);
+        const int eb = out16 ? 2 : 4;
+        auto part = [&](int r0, int m, int c0, int n, const TileOpt* force) {
+            EpiProblem ep{};
+            static_cast<Problem&>(ep) = sub_problem(p, r0, m, c0, n, 2);
+            ep.C = reinterpret_cast<float*>(static_cast<char*>(C) + ((int64_t)r0 * p.ldc + c0) * eb);
+            ep.e = e;
+            if (e.bias != nullptr) ep.e.bias = e.bias + (e.bias_rows ? r0 : c0);
+            TileOpt o = force != nullptr ? *force : kBf16DmaOpts[0];
+            if (force == nullptr) {
+                double c = 1e300;
+                for (const TileOpt& t : kBf16DmaOpts) {
+                    const double pc = plan_whole(ep, t, dev.cus).cost;
+                    if (pc < c) { c = pc; o = t; }
+                }
+            }
+            Launch l = launch_for(ep, stream);
+            l.vec_c = (p.ldc % 4 == 0) && aligned(ep.C, out16 ? 8 : 16);
+            l.group_m = pick_group_m((m + o.bm - 1) / o.bm, (n + o.bn - 1) / o.bn);
+            return identity ? launch_bf16_dma(ep, l, o.bm, o.bn, in == In::F16)
+                            : launch_bf16_dma_epi(ep, l, o.bm, o.bn, in == In::F16);
+        };
+        err = part(0, best.mc, 0, best.nc, &best.opt);
+        if (err == hipSuccess && best.mc < p.M) err = part(best.mc, p.M - best.mc, 0, p.N, nullptr);
+        if (err == hipSuccess && best.nc < p.N) err = part(0, best.mc, best.nc, p.N - best.nc, nullptr);
+        static const char* names[2][2][2] = {{{"bf16_dma256x256_fused", "bf16_dma256x128_fused"},
+                                              {"f16_dma256x256_fused", "f16_dma256x128_fused"}},
+                                             {{"bf16_dma256x256", "bf16_dma256x128"},
+                                              {"f16_dma256x256", "f16_dma256x128"}}};
+        name = names[identity ? 1 : 0][in == In::F16 ? 1 : 0][best.opt.bn == 256 ? 0 : 1];
     }
     if (err != hipSuccess) {
         t_last_hip_error = (int)err;

@@ -464,24 +464,23 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
     }
 
     // ---- epilogue: stores past M or N are skipped ----
-    if constexpr (EPI) {     // applied in place first: the store paths below only convert and store
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3), col = n0 + wn + 32 * j + l32;
-                    if (interior || (row < p.M && col < p.N))
-                        acc[i][j][r] = epi_value(p.e, acc[i][j][r], p.C, (int64_t)row * p.ldc + col, row, col);
-                }
-    }
     // every path stages a 32-row band through LDS and stores whole rows, 16 bytes per lane
     // where C allows (VEC_C) and the four columns lie inside, else element by element
     __builtin_amdgcn_s_barrier();          // every wavefront is done with the stages
     asm volatile("" ::: "memory");
     constexpr int LPR = C::WN / 4, RPI = 64 / LPR;   // lanes per C row, rows per store
+    constexpr int Q = 32 / RPI;                       // stores per 32-row band
     float* band = reinterpret_cast<float*>(smem) + wave * 32 * C::EP;
+    const int cc = 4 * (lane % LPR), col = n0 + wn + cc;    // this lane's four columns, every store
+    // fused epilogue: a column bias is the same for every store of the lane, loaded once
+    float bcol[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (EPI) {
+        if (p.e.bias != nullptr && !p.e.bias_rows) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (col + e < p.N) bcol[e] = p.e.bias[col + e];
+        }
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -489,31 +488,99 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 band[(8 * (r >> 2) + 4 * h + (r & 3)) * C::EP + 32 * j + l32] = acc[i][j][r];
+        const int row0 = m0 + wm + 32 * i + lane / LPR;     // row of store q: row0 + q RPI
+        if constexpr (EPI) {
+            // The fused epilogue on the staged values, four columns of a row per store.  C's previous
+            // values (beta != 0) and a row bias are loaded one store ahead, so that their latency
+            // overlaps the previous store's arithmetic.  The loop stays rolled: unrolled, its code
+            // grows enough that the loop over i is left rolled too and the accumulators go to
+            // scratch memory.
+            auto load_ahead = [&](int q, float (&old)[4], float& brow) {
+                const int row = row0 + q * RPI;
+                const int64_t off = (int64_t)row * p.ldc + col;
+                brow = 0.f;
 #pragma unroll
-        for (int q = 0; q < 32 / RPI; ++q) {
-            const int rr = q * RPI + lane / LPR, cc = 4 * (lane % LPR);
-            const f32x4 v = *reinterpret_cast<const f32x4*>(band + rr * C::EP + cc);
-            const int row = m0 + wm + 32 * i + rr, col = n0 + wn + cc;
-            const int64_t off = (int64_t)row * p.ldc + col;
-            const bool whole = VEC_C && (interior || (row < p.M && col + 3 < p.N));
-            if constexpr (EPI) {
-                if (whole) {
-                    const float y[4] = {v[0], v[1], v[2], v[3]};
+                for (int e = 0; e < 4; ++e) old[e] = 0.f;
+                if (row < p.M) {
+                    if (p.e.bias != nullptr && p.e.bias_rows) brow = p.e.bias[row];
+                    if (p.e.beta != 0.f) {
+                        if (VEC_C && (interior || col + 3 < p.N)) {
+                            epi_load4(p.e, p.C, off, old);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (col + e < p.N) old[e] = epi_load(p.e, p.C, off + e);
+                        }
+                    }
+                }
+            };
+            float old_n[4], brow_n;
+            if (VEC_C && interior) {      // uniform: every store whole, no bounds to check
+                auto load_whole = [&](int q, float (&old)[4], float& brow) {
+                    const int row = row0 + q * RPI;
+                    brow = p.e.bias != nullptr && p.e.bias_rows ? p.e.bias[row] : 0.f;
+                    if (p.e.beta != 0.f) epi_load4(p.e, p.C, (int64_t)row * p.ldc + col, old);
+                    else old[0] = old[1] = old[2] = old[3] = 0.f;
+                };
+                load_whole(0, old_n, brow_n);
+#pragma unroll 1
+                for (int q = 0; q < Q; ++q) {
+                    const float old[4] = {old_n[0], old_n[1], old_n[2], old_n[3]};
+                    const float brow = brow_n;
+                    if (q + 1 < Q) load_whole(q + 1, old_n, brow_n);
+                    const int rr = q * RPI + lane / LPR, row = row0 + q * RPI;
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(band + rr * C::EP + cc);
+                    float y[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        y[e] = fmaf(p.e.alpha, v[e], fmaf(p.e.beta, old[e], p.e.bias_rows ? brow : bcol[e]));
+                    if (p.e.act == kActRelu) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) y[e] = fmaxf(y[e], 0.f);
+                    } else if (p.e.act == kActGelu) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) y[e] = gelu(y[e]);
+                    }
+                    epi_store4(p.e, p.C, (int64_t)row * p.ldc + col, y);
+                }
+                continue;
+            }
+            load_ahead(0, old_n, brow_n);
+#pragma unroll 1
+            for (int q = 0; q < Q; ++q) {
+                const float old[4] = {old_n[0], old_n[1], old_n[2], old_n[3]};
+                const float brow = brow_n;
+                if (q + 1 < Q) load_ahead(q + 1, old_n, brow_n);
+                const int rr = q * RPI + lane / LPR, row = row0 + q * RPI;
+                const f32x4 v = *reinterpret_cast<const f32x4*>(band + rr * C::EP + cc);
+                const int64_t off = (int64_t)row * p.ldc + col;
+                float y[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = epi_apply(p.e, v[e], old[e], p.e.bias_rows ? brow : bcol[e]);
+                if (VEC_C && (interior || (row < p.M && col + 3 < p.N))) {
                     epi_store4(p.e, p.C, off, y);
                 } else if (row < p.M) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (col + e < p.N) epi_store(p.e, p.C, off + e, v[e]);
+                        if (col + e < p.N) epi_store(p.e, p.C, off + e, y[e]);
                 }
-            } else if (whole) {
-                // a batch streams C once (attention's scores): non-temporal stores keep it from
-                // displacing the operands in the caches
-                if constexpr (BATCH) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p.C + off));
-                else *reinterpret_cast<f32x4*>(p.C + off) = v;
-            } else if (row < p.M) {
+            }
+        } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (col + e < p.N) p.C[off + e] = v[e];
+            for (int q = 0; q < Q; ++q) {
+                const int rr = q * RPI + lane / LPR, row = row0 + q * RPI;
+                const f32x4 v = *reinterpret_cast<const f32x4*>(band + rr * C::EP + cc);
+                const int64_t off = (int64_t)row * p.ldc + col;
+                if (VEC_C && (interior || (row < p.M && col + 3 < p.N))) {
+                    // a batch streams C once (attention's scores): non-temporal stores keep it from
+                    // displacing the operands in the caches
+                    if constexpr (BATCH) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p.C + off));
+                    else *reinterpret_cast<f32x4*>(p.C + off) = v;
+                } else if (row < p.M) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (col + e < p.N) p.C[off + e] = v[e];
+                }
             }
         }
     }

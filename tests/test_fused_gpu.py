@@ -78,7 +78,9 @@ def test_fused_matches_oracle(dtype, oc, shape, epi):
     p = gi.make_problem(M, N, K, dtype, R, C_, oc, wid=81, pad_c=3)
     got, Y, S, pad_ok = run_fused(p, EPILOGUES[epi], seed=M + N)
     assert pad_ok, "C written outside the logical matrix"
-    assert g.gemm_last_kernel().endswith("_fused")
+    # the identity epilogue runs the plain direct-copy kernel on the same plan
+    assert g.gemm_last_kernel().endswith("_fused") != (epi == "plain")
+    assert "_dma256x" in g.gemm_last_kernel()
     assert_close(got, Y, S, dtype, EPILOGUES[epi][4])
 
 
@@ -127,3 +129,69 @@ def test_fused_ffn_up_full_size_sampled():
     ref, D = oracle.gemm_sampled(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b, rows, cols)
     Y, S = oracle.epilogue(ref[None, :], D[None, :], bias=bias[cols], activation=oracle.ACT_GELU)
     assert_close(got[rows, cols][None, :], Y, S, "bf16", g.Out.BF16)
+
+
+@pytest.mark.parametrize("oc", [R, C_], ids=["rowC", "colC"])
+def test_fused_ffn_up_core_and_strip(oc):
+    """2048 x 11008 x 4096 runs as a 256 x 256 core and a 256 x 128 strip (along N for a row-major
+    C, along the normalised M for a column-major one): beta, bias and ReLU, sampled outputs on both
+    sides of the seam against the oracle."""
+    import torch
+    from test_workloads_gpu import sample_indices
+    p = gi.workload_problem("llm_ffn_up_2048x11008x4096")
+    if oc == C_:
+        p = gi.make_problem(p.M, p.N, p.K, "bf16", R, C_, C_, A_logical=gi.bf16_bits_to_f32(p.A_logical),
+                            B_logical=gi.bf16_bits_to_f32(p.B_logical))
+    rng = np.random.default_rng(23)
+    bias = rng.uniform(-1, 1, p.N).astype(np.float32)
+    old = rng.uniform(-1, 1, (p.M, p.N)).astype(np.float32)
+    flat, _ = gi.lay_out(old, p.order_c, p.ldc)
+    A, B, C, bias_d = to_device(p.A), to_device(p.B), to_device(flat), to_device(bias)
+    print(f"[gpu] fused ffn-up core and strip oc={oc}", flush=True)
+    g.gemm_bf16_f32acc_fused(p.M, p.N, p.K, A.data_ptr(), p.lda, R, B.data_ptr(), p.ldb, C_, C.data_ptr(), p.ldc,
+                             p.order_c, alpha=0.5, beta=1.0, bias=bias_d.data_ptr(), activation=g.Act.RELU)
+    torch.cuda.synchronize()
+    assert g.gemm_last_kernel() == "bf16_dma256x256_fused"
+    got = gi.unpack_c(C.cpu().numpy(), p.M, p.N, p.ldc, p.order_c).astype(np.float64)
+    rows, cols = sample_indices(p.M, p.N, 5)
+    seam = 8192       # the strip's first column of C (a row of the normalised C when C is column-major)
+    extra_c = np.arange(seam - 64, seam + 64)
+    extra_r = rng.integers(0, p.M, extra_c.size)
+    rows, cols = np.concatenate([rows, extra_r]), np.concatenate([cols, extra_c])
+    ref, D = oracle.gemm_sampled(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b, rows, cols)
+    Y, S = oracle.epilogue(ref[None, :], D[None, :], alpha=0.5, beta=1.0, C_old=old[rows, cols][None, :],
+                           bias=bias[cols], activation=oracle.ACT_RELU)
+    assert_close(got[rows, cols][None, :], Y, S, "bf16", g.Out.F32)
+
+
+@pytest.mark.parametrize("out", [g.Out.F32, g.Out.BF16], ids=["f32", "bf16"])
+def test_fused_gelu_accuracy(out):
+    """GELU on exact pre-activations: small-integer operands make every sum exact, alpha = 2^-5 maps
+    them onto about [-8, 8].  FP32 output within 5e-7 |x| of x Phi(x) (the epilogue's erf is
+    Abramowitz and Stegun 7.1.26, |error| <= 1.5e-7, evaluated with the hardware's exp2 and
+    reciprocal; 3.0e-7 |x| at most in a float32 emulation with exact exp2 and reciprocal); a bf16
+    output is that value rounded to nearest even, so within 2^-8 |y| + 5e-7 |x|."""
+    import torch
+    from scipy.special import erf
+    rng = np.random.default_rng(31)
+    M, N, K = 256, 384, 64
+    Al = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    Bl = rng.integers(-4, 5, (K, N)).astype(np.float32)
+    p = gi.make_problem(M, N, K, "bf16", R, C_, R, A_logical=Al, B_logical=Bl)
+    alpha = 2.0 ** -5
+    A, B = to_device(p.A), to_device(p.B)
+    if out == g.Out.F32:
+        C = torch.full((M * N,), float("nan"), dtype=torch.float32, device="cuda")
+    else:
+        C = torch.full((M * N,), -1, dtype=torch.int16, device="cuda")
+    print(f"[gpu] fused gelu accuracy out={int(out)}", flush=True)
+    g.gemm_bf16_f32acc_fused(M, N, K, A.data_ptr(), p.lda, R, B.data_ptr(), p.ldb, C_, C.data_ptr(), N, R,
+                             alpha=alpha, activation=g.Act.GELU, out_type=out)
+    torch.cuda.synchronize()
+    res = C.cpu().numpy()
+    got = (gi.bf16_bits_to_f32(res.view(np.uint16)) if out == g.Out.BF16 else res).reshape(M, N).astype(np.float64)
+    x = alpha * (Al.astype(np.float64) @ Bl)
+    assert np.abs(x).max() > 4
+    ref = x * 0.5 * (1.0 + erf(x / np.sqrt(2.0)))
+    bound = 5e-7 * np.abs(x) + (2.0 ** -8 * np.abs(ref) if out == g.Out.BF16 else 0.0)
+    assert np.all(np.abs(got - ref) <= bound + 1e-30)

@@ -33,6 +33,7 @@
 // clamped to the last valid one (their products are never stored); the K tail uses
 // element-wise loads with zero fill.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -195,10 +196,12 @@ void k_skinny(KArg<BATCH> p, int vec_a, int vec_b, int vec_c, int bbuf, int ksli
     constexpr int SC = WAVES * CK;              // K distance between a wavefront's batches
     Frag fa[RING][CHUNK][FM], fb[RING][CHUNK][NB];
     // one batch of CHUNK k-steps; `full` (wavefront-uniform): the whole batch lies inside
-    // K, so 16-byte loads need no bounds checks
-    auto load_chunk = [&](int buf, int kc) {
-        const bool full = kc + CK <= kend;
-        const bool fa_fast = full && vec_a, fb_fast = full && vec_b;
+    // K, so 16-byte loads need no bounds checks.  FAST: the caller knows the batch is full and
+    // every operand takes its unchecked path (a branch-free batch, see the main loop)
+    auto load_chunk = [&](int buf, int kc, auto fast) {
+        constexpr bool FAST = decltype(fast)::value;
+        const bool full = FAST || kc + CK <= kend;
+        const bool fa_fast = FAST || (full && vec_a), fb_fast = FAST || (full && vec_b);
 #pragma unroll
         for (int s = 0; s < CHUNK; ++s) {
             const int k = kc + s * D::KSTEP + lq * D::KL;
@@ -210,8 +213,8 @@ void k_skinny(KArg<BATCH> p, int vec_a, int vec_b, int vec_c, int bbuf, int ksli
             } else if constexpr (RC4) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    fb[buf][s][e] = F32::load_row4(Bf, p.ldb, k + e, kend, n0 + 4 * li, p.N, full && n_inside);
-            } else if (bbuf && full) {
+                    fb[buf][s][e] = F32::load_row4(Bf, p.ldb, k + e, kend, n0 + 4 * li, p.N, FAST || (full && n_inside));
+            } else if (FAST || (bbuf && full)) {
                 // kc is the same in every lane; saying so keeps the offset scalar (no waterfall)
                 const int soff = __builtin_amdgcn_readfirstlane((int)((int64_t)(kc + s * D::KSTEP) * p.ldb * 4));
                 fb[buf][s][0] = F32::load_strided_buf(rbuf, bvoff, soff);
@@ -242,15 +245,31 @@ void k_skinny(KArg<BATCH> p, int vec_a, int vec_b, int vec_c, int bbuf, int ksli
         }
     };
     // ring of RING register buffers, unrolled by RING so that buffers are indexed by
-    // constants: batch b lives in buffer b % RING
+    // constants: batch b lives in buffer b % RING.  While every batch loaded in a round is
+    // full and takes the unchecked loads, the round has no branch, and the wait before a
+    // batch's matrix instructions leaves the loads of the batches after it in flight; with a
+    // branch between checked and unchecked loads the compiler waits for all of them, the batch
+    // ahead included, so each batch's memory latency was exposed in turn.  The rest of K (the
+    // last rounds, or operands that need checked loads) runs the general round.
+    const bool unchecked = vec_a && (B_KC ? vec_b : RC4 ? n_inside : bbuf != 0);   // uniform
 #pragma unroll
     for (int r = 0; r + 1 < RING; ++r)
-        if (kbeg + r * SC < kend) load_chunk(r, kbeg + r * SC);
-    for (int kc = kbeg; kc < kend; kc += RING * SC) {
+        if (kbeg + r * SC < kend) load_chunk(r, kbeg + r * SC, std::false_type{});
+    int kc = kbeg;
+    if (unchecked) {
+        for (; kc + (2 * RING - 2) * SC + CK <= kend; kc += RING * SC) {
+#pragma unroll
+            for (int r = 0; r < RING; ++r) {
+                load_chunk((r + RING - 1) % RING, kc + (r + RING - 1) * SC, std::true_type{});
+                compute_chunk(r);
+            }
+        }
+    }
+    for (; kc < kend; kc += RING * SC) {
 #pragma unroll
         for (int r = 0; r < RING; ++r) {
             const int kl = kc + (r + RING - 1) * SC;       // the batch RING - 1 ahead
-            if (kl < kend) load_chunk((r + RING - 1) % RING, kl);
+            if (kl < kend) load_chunk((r + RING - 1) % RING, kl, std::false_type{});
             if (kc + r * SC < kend) compute_chunk(r);
         }
     }

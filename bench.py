@@ -14,7 +14,8 @@ kernel against MI355X's published matrix-core peak for its dtype.
 `--workload` picks another single workload from gemm_inputs.WORKLOADS (then one step is
 that one GEMM, or one strided batched call for a batch workload such as attention's per-head
 products); `--algo` forces a kernel (gemm_f32_amd.Algo name); `--epilogue NAME` calls the fused-epilogue entry point (bias, activation, bf16 output) for a 16-bit
-workload; `--workspace` calls the
+workload; `--k K` replaces a single workload's K (a sweep over K separates a kernel's fixed
+cost -- launch, first loads, the C write -- from its cost per k-tile); `--workspace` calls the
 workspace entry points (gemm_f32_ws / gemm_bf16_f32acc_ws, split-K across workgroups where
 the problem is too small to fill the device) with a workspace of the size the library asks
 for, allocated before the timed region.  Each GEMM's inputs
@@ -52,6 +53,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT)
     ap.add_argument("--algo", default="AUTO")
+    ap.add_argument("--k", type=int, default=None,
+                    help="replace the workload's K (same shape and recipe otherwise), for sweeps over K")
     ap.add_argument("--workspace", action="store_true",
                     help="use the workspace (split-K) entry points; AUTO only")
     ap.add_argument("--sets", type=int, default=0,
@@ -136,11 +139,12 @@ def copy_calibration(args):
 class Leg:
     """One GEMM of the step with its resident device buffers."""
 
-    def __init__(self, name, algo, sets, workspace=False, epilogue=None):
+    def __init__(self, name, algo, sets, workspace=False, epilogue=None, k=None):
+        import dataclasses
         import torch
         import gemm_f32_amd as g
         import gemm_inputs as gi
-        self.w = gi.WORKLOADS[name]
+        self.w = gi.WORKLOADS[name] if k is None else dataclasses.replace(gi.WORKLOADS[name], K=k)
         self.name = name
         self.algo = g.Algo[algo]
         self.problems = []
@@ -158,7 +162,7 @@ class Leg:
         self.sets = sets
         for s in range(sets):
             w = self.w
-            p = gi.workload_problem(name, 1000 * s)
+            p = gi.workload_problem(name, 1000 * s, K=k)
             self.problems.append(p)
             conv = (lambda b: b.view(np.int16)) if w.dtype in ("bf16", "f16") else (lambda b: b)
             self.A.append(torch.from_numpy(conv(p.A)).to("cuda"))
@@ -316,7 +320,9 @@ def main():
     from gemm_f32_amd import roofline as rl
 
     names = DEFAULT_LEGS if args.workload == DEFAULT else [args.workload]
-    legs = [Leg(n, args.algo, args.sets, args.workspace, args.epilogue) for n in names]
+    if args.k is not None and args.workload == DEFAULT:
+        raise SystemExit("--k applies to a single --workload")
+    legs = [Leg(n, args.algo, args.sets, args.workspace, args.epilogue, args.k) for n in names]
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
@@ -367,6 +373,7 @@ def main():
         "config": {"workload": args.workload if args.workload != DEFAULT else
                    "4096^3 FP32 GEMM + 4096^3 BF16->FP32 GEMM per step",
                    "legs": leg_info, "algo": args.algo, "epilogue": args.epilogue, "tile_order": args.tile_order,
+                   "k_override": args.k,
                    "wall_s": round(wall, 3)},
         "roofline": roof,
         "roofline_legs": roofs,

@@ -45,6 +45,12 @@ SPECS = [
     ("square4096_f16", ["--workload", "square4096_f16"], 30),
     ("square4096_e4m3", ["--workload", "square4096_e4m3"], 30),
     ("square4096_e5m2", ["--workload", "square4096_e5m2"], 30),
+    # the same 4096 x 4096 outputs over K: fixed cost (launch, first loads, the 64 MB C write)
+    # against the cost per k-tile
+    ("square4096_bf16@K128", ["--workload", "square4096_bf16", "--k", "128"], 30),
+    ("square4096_bf16@K1024", ["--workload", "square4096_bf16", "--k", "1024"], 30),
+    ("square4096_e4m3@K128", ["--workload", "square4096_e4m3", "--k", "128"], 30),
+    ("square4096_e4m3@K1024", ["--workload", "square4096_e4m3", "--k", "1024"], 30),
     ("ragged1000_f32", ["--workload", "ragged1000_f32"], 30),
     ("ragged1000_bf16", ["--workload", "ragged1000_bf16"], 30),
     ("ragged4095x4097x1023_f32", ["--workload", "ragged4095x4097x1023_f32"], 30),
@@ -147,9 +153,10 @@ def table(args) -> None:
 
 def _row(tag, arg, leg, rows, us, w, rl) -> None:
     kern = "; ".join(f"`{_short(r['Name'])}` {r['Calls']} x {float(r['AverageNs']) / 1e3:.1f}" for r in rows)
-    tf = w.flops / (us * 1e-6) / 1e12
+    M, N, K, batch = leg["M"], leg["N"], leg["K"], leg["batch"]      # as run (K may be overridden)
+    tf = 2 * batch * M * N * K / (us * 1e-6) / 1e12
     e = 4 if w.dtype == "f32" else 1 if w.dtype in ("e4m3", "e5m2", "e4m3_e5m2", "e5m2_e4m3") else 2
-    gbs = w.batch * (e * (w.M * w.K + w.K * w.N) + 4 * w.M * w.N) / (us * 1e-6) / 1e9
+    gbs = batch * (e * (M * K + K * N) + 4 * M * N) / (us * 1e-6) / 1e9
     pct = 100 * tf * 1e12 / rl.mi355x_peak(w.dtype)
     print(f"| {tag} | `{arg}` | {leg['kernel']} | {kern} | {us:.1f} | {tf:.1f} | {pct:.1f} | {gbs:.0f} | "
           f"{leg['ms'] * 1e3:.1f} |")

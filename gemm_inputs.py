@@ -20,6 +20,7 @@ type; its format is read as the OCP one gfx950's matrix instructions take).  A d
 """
 from __future__ import annotations
 
+import dataclasses
 from dataclasses import dataclass
 
 import numpy as np
@@ -434,9 +435,10 @@ def make_batched_problem(batch: int, M: int, N: int, K: int, dtype: str = "f32",
                           ldc, sc)
 
 
-def workload_problem(name: str, seed_offset: int = 0):
-    """The named workload's seeded inputs: a Problem, or a BatchedProblem for a batch."""
-    w = WORKLOADS[name]
+def workload_problem(name: str, seed_offset: int = 0, K: int | None = None):
+    """The named workload's seeded inputs: a Problem, or a BatchedProblem for a batch.  K, if
+    given, replaces the workload's depth (same recipe otherwise)."""
+    w = WORKLOADS[name] if K is None else dataclasses.replace(WORKLOADS[name], K=K)
     if w.batch > 1:
         return make_batched_problem(w.batch, w.M, w.N, w.K, w.dtype, w.order_a, w.order_b, w.order_c,
                                     dist=w.dist, wid=w.wid + seed_offset, **dict(w.layout))

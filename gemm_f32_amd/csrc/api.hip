@@ -352,10 +352,32 @@ Plan choose_f32_tiles(const Problem& p, gemm_algo_t algo, int cus) {
     return best;
 }
 
+// A split of K over the tiles of the direct-copy kernels (slices == 1: none), the workspace it
+// needs and its slice depth; chosen by tile_split (16-bit) and f32_tile_split below.
+struct TileSplit {
+    int slices = 1, kslice = 0;
+    size_t bytes = 0;
+};
+TileSplit tile_split_with(const Problem& p, int cus, const Workspace& ws, bool f32);
+
 hipError_t run_f32_tiles(const Problem& p, hipStream_t stream, gemm_algo_t algo, const DeviceInfo& dev,
-                         const char*& name, gemm_status_t& st, const Batch& b) {
+                         const char*& name, gemm_status_t& st, const Batch& b, const Workspace& ws = Workspace{}) {
     const Plan best = choose_f32_tiles(p, algo, dev.cus);
     if (best.cost >= 1e300) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
+    if (algo == GEMM_ALGO_AUTO && b.n == 1) {
+        const TileSplit t = tile_split_with(p, dev.cus, ws, true);
+        if (t.slices > 1) {
+            SplitProblem sp{};
+            static_cast<Problem&>(sp) = p;
+            sp.kslice = t.kslice;
+            sp.part = static_cast<float*>(ws.ptr);
+            Launch l = launch_for(p, stream);
+            l.vec_c = l.vec_c && p.N % 4 == 0;
+            l.group_m = pick_group_m(p.M / 256, p.N / 256);
+            name = "f32_dma256x256_splitk";
+            return launch_f32_dma_split(sp, t.slices, l);
+        }
+    }
     name = f32_name(best.opt);
     const TileOpt o = best.opt;
     return run_plan(p, stream, best, kElemF32, dev, b, [&](const Problem& c, const Launch& lc) {
@@ -399,10 +421,6 @@ Plan choose_bf16_tiles(const Problem& p, gemm_algo_t algo, int cus) {
 // 4096 x 512 x 4096, 4 slices 40.1 us (8: 45.7, unsplit 55.3); 2048 x 2048 x 8192, 4 slices
 // 78.4 us (unsplit 105.6); 1024 x 1024 x 8192, 8 slices 40.6 us (unsplit 88.8); no split where the
 // tiles fill the chip or K is short (2048 x 4096 x 4096: 2 slices 79.8 us, unsplit 67.0).
-struct TileSplit {
-    int slices = 1, kslice = 0;
-    size_t bytes = 0;
-};
 constexpr int kMinSliceK = 512;
 constexpr double kTau256 = 1.5e-6, kTau128 = 0.87e-6, kLaunchSec = 2e-6, kWriteBps = 5e12, kSumSec = 3e-6,
                  kSumBps = 6e12;
@@ -449,10 +467,51 @@ TileSplit tile_split(const Problem& p, int cus) {
     return best;
 }
 
+// FP32: whole 256 x 256 tiles of the direct-copy kernel split into at most one round's worth of
+// slices, each at least kMinSliceK deep, when the same time model with the FP32 kernel's own
+// figure (7.7 us per 32-deep k-tile and round with every CU busy, from 4096^3) prices the split
+// below the default plan.  The default plan's kernels (register-staged 64^2 and 128^2 tiles,
+// the 128^2 direct-copy tile) are priced by their round cost: a 256^2 tile's round of
+// 65536 units costs K / 32 k-tiles of that figure (no margin: this pricing is optimistic for the
+// register-staged tiles, 164 against 194-209 us measured on the shard).  Measured (events,
+// interleaved runs):
+// 4096 x 512 x 4096 209 / 194 -> 160 / 150 us, 4096 x 512 x 8192 362 -> 264 us, 2048^2 x 4096
+// 280 -> 264 us; 4096 x 768 x 2048 is left unsplit (126 against 137 us split).
+constexpr double kTauF32 = 7.7e-6;
+
+double f32_split_seconds(const Problem& p, const TileSplit& t, int cus) {
+    const int64_t units = tiles(p.M, p.N, 256, 256) * t.slices;
+    return kLaunchSec + (t.kslice / 32.0) * kTauF32 * occupancy_factor(units, cus) +
+           (t.slices - 1) * 4.0 * p.M * p.N / kWriteBps + kSumSec + (t.slices + 1) * 4.0 * p.M * p.N / kSumBps;
+}
+
+TileSplit f32_tile_split(const Problem& p, int cus) {
+    TileSplit best;
+    const int64_t c = cus > 0 ? cus : 256;
+    if (p.M % 256 != 0 || p.N % 256 != 0 || !f32_dma_applies(p, launch_for(p, nullptr), 256, 256)) return best;
+    const int64_t n = tiles(p.M, p.N, 256, 256);
+    const int64_t most = std::min<int64_t>(c / std::max<int64_t>(n, 1), p.K / kMinSliceK);
+    const Plan plain = choose_f32_tiles(p, GEMM_ALGO_AUTO, cus);
+    double best_t = plain.cost / 65536.0 * (p.K / 32.0) * kTauF32;
+    for (int s = 2; s <= most; ++s) {
+        TileSplit t;
+        t.kslice = (int)(((p.K + s - 1) / s + 63) / 64 * 64);
+        t.slices = (p.K + t.kslice - 1) / t.kslice;
+        if (t.slices != s) continue;
+        t.bytes = (size_t)(s - 1) * p.M * p.N * sizeof(float);
+        const double sec = f32_split_seconds(p, t, cus);
+        if (sec < best_t) {
+            best_t = sec;
+            best = t;
+        }
+    }
+    return best;
+}
+
 // The split the default choice takes with this workspace (slices == 1: none).
-TileSplit tile_split_with(const Problem& p, int cus, const Workspace& ws) {
+TileSplit tile_split_with(const Problem& p, int cus, const Workspace& ws, bool f32) {
     if (ws.ptr == nullptr || !aligned(ws.ptr, 16)) return TileSplit{};
-    const TileSplit t = tile_split(p, cus);
+    const TileSplit t = f32 ? f32_tile_split(p, cus) : tile_split(p, cus);
     return t.slices > 1 && t.bytes <= ws.bytes ? t : TileSplit{};
 }
 
@@ -461,7 +520,7 @@ hipError_t run_b16_tiles(const Problem& p, hipStream_t stream, gemm_algo_t algo,
     const Plan best = choose_bf16_tiles(p, algo, dev.cus);
     if (best.cost >= 1e300) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
     if (algo == GEMM_ALGO_AUTO && b.n == 1) {
-        const TileSplit t = tile_split_with(p, dev.cus, ws);
+        const TileSplit t = tile_split_with(p, dev.cus, ws, false);
         if (t.slices > 1) {
             SplitProblem sp{};
             static_cast<Problem&>(sp) = p;
@@ -502,7 +561,7 @@ hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, int 
             default:
                 if (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus) && skinny_applies(p, false))
                     return run_skinny(p, l, kElemF32, dev.cus, name, ws);
-                return run_f32_tiles(p, stream, algo, dev, name, st, b);
+                return run_f32_tiles(p, stream, algo, dev, name, st, b, ws);
         }
     }
     if (algo == GEMM_ALGO_SKINNY ||
@@ -529,8 +588,7 @@ size_t split_bytes(const Problem& p, int et, int cus) {
         const SkinnySplit sp = skinny_split(p, et != kElemF32, cus);
         return sp.slices > 1 ? sp.bytes : 0;
     }
-    if (et == kElemF32) return 0;
-    const TileSplit t = tile_split(p, cus);
+    const TileSplit t = et == kElemF32 ? f32_tile_split(p, cus) : tile_split(p, cus);
     return t.slices > 1 ? t.bytes : 0;
 }
 

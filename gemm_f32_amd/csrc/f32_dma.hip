@@ -124,13 +124,16 @@ struct CopyPlan {
     }
 };
 
-template <typename C, bool BATCH = false>
+// SPLIT: K slice blockIdx.y of one problem (slice 0 into C, the others into their slabs)
+template <typename C, bool BATCH = false, bool SPLIT = false>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
-void k_f32_dma(KArg<BATCH> p, int tiles_m, int tiles_n, int group_m) {
+void k_f32_dma(std::conditional_t<SPLIT, SplitProblem, KArg<BATCH>> p, int tiles_m, int tiles_n, int group_m) {
     constexpr int BM = C::BM, BN = C::BN, S = C::S, FM = C::FM, FN = C::FN;
     constexpr bool A_KC = C::A_KC, B_KC = C::B_KC;
+    static_assert(!(BATCH && SPLIT), "a batch is not split");
     __shared__ __align__(16) unsigned char smem[S * C::STAGE];
     if constexpr (BATCH) p.select(blockIdx.z);
+    if constexpr (SPLIT) p.select(blockIdx.y, 4);
 
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
@@ -674,6 +677,28 @@ bool f32_dma_applies(const Problem& p, const Launch& l, int bm, int bn) {
     if ((p.oa == kRow && rows * p.lda * 4 >= lim) || (p.ob == kCol && rows * p.ldb * 4 >= lim)) return false;
     // at least one whole tile along each edge (the host plans overhangs and strips)
     return l.vec_a && l.vec_b && p.K >= BK && p.M >= bm && p.N >= bn;
+}
+
+// Split-K on whole 256 x 256 tiles (M and N multiples of 256): `slices` K slices of s.kslice as
+// the grid's second dimension, slices 1 .. S-1 into the slabs at s.part (16-byte aligned), then
+// launch_add_slabs adds them to C in slice order.
+hipError_t launch_f32_dma_split(const SplitProblem& s, int slices, const Launch& l) {
+    if (s.M % 256 != 0 || s.N % 256 != 0) return hipErrorInvalidValue;
+    const int tiles_m = s.M / 256, tiles_n = s.N / 256;
+    const dim3 grid((unsigned)tiles_m * tiles_n, (unsigned)slices, 1), block(64 * 4 * 2);
+    const bool akc = s.oa == kRow, bkc = s.ob == kCol;
+    const int g = l.group_m;
+    if (akc && bkc)
+        hipLaunchKernelGGL((k_f32_dma<Cfg<256, 256, 4, 2, 2, true, true>, false, true>), grid, block, 0, l.stream, s, tiles_m, tiles_n, g);
+    else if (akc)
+        hipLaunchKernelGGL((k_f32_dma<Cfg<256, 256, 4, 2, 2, true, false>, false, true>), grid, block, 0, l.stream, s, tiles_m, tiles_n, g);
+    else if (bkc)
+        hipLaunchKernelGGL((k_f32_dma<Cfg<256, 256, 4, 2, 2, false, true>, false, true>), grid, block, 0, l.stream, s, tiles_m, tiles_n, g);
+    else
+        hipLaunchKernelGGL((k_f32_dma<Cfg<256, 256, 4, 2, 2, false, false>, false, true>), grid, block, 0, l.stream, s, tiles_m, tiles_n, g);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return launch_add_slabs(s.C, s.ldc, s.M, s.N, s.part, slices - 1, l);
 }
 
 // Configurations: 256 x 256 with 8 wavefronts of 64 x 128 (2 per SIMD, 128 KB of LDS),

@@ -236,12 +236,16 @@ gemm_status_t gemm_plan(int dtype, int64_t M, int64_t N, int64_t K, gemm_order_t
 /* ---- With a caller's workspace: split-K across workgroups ---------------------------------
  * "A06 - Tiled Matrix Multiply (GEMM)", "The next two rungs" (split-K: workers take parts of
  * K and a second step combines their partial sums): for problems whose output gives too few
- * workgroups to occupy the device (few rows, or few columns after the column-major-C swap),
- * the small-problem kernel also divides K among workgroups; each writes its partial product
- * to the workspace and a second kernel sums the slices in slice order, so results are
- * deterministic (identical from call to call; they may differ in the last bits from
- * gemm_f32 / gemm_bf16_f32acc, which sum in another order).  The library still allocates
- * nothing.
+ * workgroups to occupy the device, K is also divided among workgroups -- by the small-problem
+ * kernel for few rows (or few columns after the column-major-C swap), and by the direct-copy
+ * kernels on 256 x 256 tiles when those leave CUs idle (FP32 inputs with M and N multiples of
+ * 256; 16-bit inputs in that kernel's layout, row-major A and column-major B), where a time
+ * model prices the split below the unsplit plan (one GPU's 4096 x 512 x 4096 column shard of a
+ * 4096^3 product, for one).  The slices' partial products go to the workspace (the tile kernels
+ * write the first slice straight to C) and a second kernel adds them in slice order, so results
+ * are deterministic
+ * (identical from call to call; they may differ in the last bits from the plain calls, which
+ * sum in another order).  The library still allocates nothing.
  *
  * gemm_workspace_size: bytes of workspace with which the _ws calls split K for this problem
  * (dtype as for gemm_plan) on the current device (the same extents and orders as the call;

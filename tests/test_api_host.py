@@ -289,7 +289,15 @@ def test_plan_invariants_on_random_shapes():
     ("bf16", (4096, 4096, 4096), (R, C_, R), 0),
     ("bf16", (2048, 4096, 4096), (R, C_, R), 0),
     ("bf16", (2048, 4096, 11008), (R, C_, R), 0),
-    ("f32", (4096, 512, 4096), (R, R, R), 0),
+    # FP32: whole 256 x 256 tiles split into one round's worth of slices of at least 512 where the
+    # time model prices that below the default plan: the shard's 32 tiles in 8 slices, 2048^2 in 4;
+    # not 4096 x 768 x 2048 (short slices), not ragged M, not tiles that fill the chip
+    ("f32", (4096, 512, 4096), (R, R, R), 7 * 4096 * 512 * 4),
+    ("f32", (4096, 512, 8000), (C_, C_, R), 7 * 4096 * 512 * 4),
+    ("f32", (2048, 2048, 4096), (R, R, R), 3 * 2048 * 2048 * 4),
+    ("f32", (4096, 768, 2048), (C_, R, R), 0),
+    ("f32", (4096, 4096, 4096), (R, C_, R), 0),
+    ("f32", (4100, 512, 4096), (R, R, R), 0),
 ], ids=lambda v: str(v))
 def test_split_k_workspace_of_known_shapes(dtype, shape, orders, expected):
     assert g.gemm_plan(dtype, *shape, *orders, with_workspace=True)[3] == expected

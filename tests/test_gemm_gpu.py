@@ -572,6 +572,41 @@ def test_tile_split_k_with_workspace(dtype, case):
     assert np.array_equal(flat.view(np.uint32), again.view(np.uint32)), "not deterministic"
 
 
+# FP32 split-K on whole 256 x 256 direct-copy tiles: (M, N, K, orders A, B, C); every
+# instantiation of the operand orders, a ragged last slice (K = 8000: 7 slices of 1024 and one of
+# 832), a column-major C
+F32_TILE_SPLIT_CASES = [(4096, 512, 4096, ROW_MAJOR, ROW_MAJOR, ROW_MAJOR),
+                        (4096, 512, 8000, COL_MAJOR, COL_MAJOR, ROW_MAJOR),
+                        (512, 4096, 4096, ROW_MAJOR, COL_MAJOR, COL_MAJOR),
+                        (2048, 2048, 4096, COL_MAJOR, ROW_MAJOR, ROW_MAJOR)]
+
+
+@pytest.mark.parametrize("case", F32_TILE_SPLIT_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_f32_tile_split_k_with_workspace(case):
+    M, N, K, oa, ob, oc = case
+    p = gi.make_problem(M, N, K, "f32", oa, ob, oc, wid=67, pad_c=4)
+    flat, need, kernel = run_ws(p)
+    assert need > 0 and kernel == "f32_dma256x256_splitk", (need, kernel)
+    assert padding_untouched(p, flat)
+    ref, D = reference(p, key=("f32tilesplit", case))
+    err = oracle.normalised_error(logical_c(p, flat), ref, D)
+    assert err <= TOL["f32"], err
+    again, _, _ = run_ws(p)
+    assert np.array_equal(flat.view(np.uint32), again.view(np.uint32)), "not deterministic"
+
+
+def test_f32_tile_split_k_small_integer_exact():
+    rng = np.random.default_rng(68)
+    M, N, K = 4096, 512, 8000
+    A = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    B = rng.integers(-4, 5, (K, N)).astype(np.float32)
+    p = gi.make_problem(M, N, K, "f32", ROW_MAJOR, ROW_MAJOR, A_logical=A, B_logical=B)
+    flat, need, kernel = run_ws(p)
+    assert kernel == "f32_dma256x256_splitk"
+    ref, _ = oracle.gemm(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b)
+    assert np.array_equal(logical_c(p, flat).astype(np.float64), ref)
+
+
 def test_tile_split_k_small_integer_exact_and_closed_forms():
     rng = np.random.default_rng(65)
     M, N, K = 1000, 1025, 3000

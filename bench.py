@@ -13,8 +13,8 @@ kernel against MI355X's published matrix-core peak for its dtype.
 
 `--workload` picks another single workload from gemm_inputs.WORKLOADS (then one step is
 that one GEMM, or one strided batched call for a batch workload such as attention's per-head
-products); `--algo` forces a kernel (gemm_f32_amd.Algo name); `--epilogue NAME` calls the fused-epilogue entry point (bias, activation, bf16 output) for a 16-bit
-workload; `--k K` replaces a single workload's K (a sweep over K separates a kernel's fixed
+products); `--algo` forces a kernel (gemm_f32_amd.Algo name); `--epilogue NAME` calls the fused-epilogue entry point (bias, activation, bf16 output) for a
+workload with row-major A and column-major B; `--k K` replaces a single workload's K (a sweep over K separates a kernel's fixed
 cost -- launch, first loads, the C write -- from its cost per k-tile); `--workspace` calls the
 workspace entry points (gemm_f32_ws / gemm_bf16_f32acc_ws, split-K across workgroups where
 the problem is too small to fill the device) with a workspace of the size the library asks
@@ -187,8 +187,8 @@ class Leg:
         self.ws, self.ws_bytes = None, 0
         self.epi = None
         if epilogue is not None:
-            if algo != "AUTO" or workspace or self.batched or w.dtype == "f32":
-                raise SystemExit("--epilogue runs the 16-bit fused entry point alone")
+            if algo != "AUTO" or workspace or self.batched:
+                raise SystemExit("--epilogue runs a fused entry point alone")
             alpha, beta, has_bias, act, out16 = EPILOGUES[epilogue]
             bias = torch.from_numpy(np.random.default_rng(1).uniform(-1, 1, w.N).astype(np.float32)).to("cuda")
             self.epi = (alpha, beta, bias if has_bias else None, act, 1 if out16 else 0)
@@ -196,7 +196,8 @@ class Leg:
                 self.C = torch.zeros(size, dtype=torch.int16, device="cuda")
             else:
                 self.C.zero_()
-            self.fn_fused = {"bf16": g.gemm_bf16_f32acc_fused, "f16": g.gemm_f16_f32acc_fused}[w.dtype]
+            self.fn_fused = {"bf16": g.gemm_bf16_f32acc_fused, "f16": g.gemm_f16_f32acc_fused,
+                             "f32": g.gemm_f32_fused}[w.dtype]
         if workspace:
             if algo != "AUTO":
                 raise SystemExit("--workspace runs the default kernel choice (--algo AUTO)")

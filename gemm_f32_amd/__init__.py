@@ -11,5 +11,5 @@ from .binding import (  # noqa: F401
     gemm_f16_f32acc, gemm_f16_f32acc_algo, gemm_f16_f32acc_ws,
     gemm_f32_strided_batched, gemm_bf16_f32acc_strided_batched, gemm_f16_f32acc_strided_batched,
     gemm_bf16_f32acc_fused, gemm_f16_f32acc_fused, gemm_bf16_f32acc_noalloc, NOALLOC_SCRATCH_BYTES,
-    gemm_fp8_f32acc, Fp8, Act, Out, lib_handle, library_path, LibraryNotBuilt, matmul, operand_layout,
+    gemm_fp8_f32acc, Fp8, gemm_f32_fused, Act, Out, lib_handle, library_path, LibraryNotBuilt, matmul, operand_layout,
 )

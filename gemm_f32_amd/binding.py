@@ -105,7 +105,7 @@ def _load():
                  "gemm_f16_f32acc_strided_batched"):
         f = getattr(lib, name)
         f.argtypes, f.restype = batched, ci
-    for name in ("gemm_bf16_f32acc_fused", "gemm_f16_f32acc_fused"):
+    for name in ("gemm_bf16_f32acc_fused", "gemm_f16_f32acc_fused", "gemm_f32_fused"):
         f = getattr(lib, name)
         f.argtypes, f.restype = args[:-1] + [ctypes.POINTER(EpilogueStruct), vp], ci
     lib.gemm_bf16_f32acc_noalloc.argtypes, lib.gemm_bf16_f32acc_noalloc.restype = args, ci
@@ -139,7 +139,7 @@ EXPORTED = ("gemm_f32", "gemm_bf16_f32acc", "gemm_f32_algo", "gemm_bf16_f32acc_a
             "gemm_f16_f32acc", "gemm_f16_f32acc_algo", "gemm_f16_f32acc_ws",
             "gemm_f32_strided_batched", "gemm_bf16_f32acc_strided_batched",
             "gemm_f16_f32acc_strided_batched", "gemm_bf16_f32acc_fused", "gemm_f16_f32acc_fused",
-            "gemm_bf16_f32acc_noalloc", "gemm_fp8_f32acc")
+            "gemm_bf16_f32acc_noalloc", "gemm_fp8_f32acc", "gemm_f32_fused")
 
 # bytes of the static scratch behind gemm_bf16_f32acc_noalloc (GEMM_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -301,6 +301,13 @@ def gemm_f16_f32acc_fused(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, ord
                           bias=0, activation=Act.NONE, out_type=Out.F32, stream=0):
     """gemm_bf16_f32acc_fused for IEEE fp16 inputs."""
     _fused("gemm_f16_f32acc_fused", M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, alpha, beta,
+           bias, activation, out_type, stream)
+
+
+def gemm_f32_fused(M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, alpha=1.0, beta=0.0,
+                   bias=0, activation=Act.NONE, out_type=Out.F32, stream=0):
+    """gemm_bf16_f32acc_fused for FP32 inputs (row-major A, column-major B, K >= 32)."""
+    _fused("gemm_f32_fused", M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, alpha, beta,
            bias, activation, out_type, stream)
 
 

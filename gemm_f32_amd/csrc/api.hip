@@ -749,8 +749,8 @@ gemm_status_t run_batched(In in, int64_t batch, int64_t M, int64_t N, int64_t K,
 
 // GEMM with the fused epilogue: 16-bit inputs on the direct-copy kernel, the whole of C in one
 // launch (tiles overhang both edges), or the epilogue of an empty sum for K == 0.
-gemm_status_t run_fused(In in, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, gemm_order_t oa,
-                        const uint16_t* B, int64_t ldb, gemm_order_t ob, void* C, int64_t ldc, gemm_order_t oc,
+gemm_status_t run_fused(In in, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, gemm_order_t oa,
+                        const void* B, int64_t ldb, gemm_order_t ob, void* C, int64_t ldc, gemm_order_t oc,
                         const gemm_epilogue_t* epi, hipStream_t stream) {
     if (epi == nullptr) return GEMM_ERR_INVALID_VALUE;
     if (epi->activation != GEMM_ACT_NONE && epi->activation != GEMM_ACT_RELU && epi->activation != GEMM_ACT_GELU)
@@ -764,8 +764,13 @@ gemm_status_t run_fused(In in, int64_t M, int64_t N, int64_t K, const uint16_t* 
     Problem p{};
     if (row) p = Problem{(int)M, (int)N, (int)K, A, lda, (int)oa, B, ldb, (int)ob, static_cast<float*>(C), ldc};
     else p = Problem{(int)N, (int)M, (int)K, B, ldb, 1 - (int)ob, A, lda, 1 - (int)oa, static_cast<float*>(C), ldc};
-    // the direct-copy kernel's layout: k-contiguous operands (after a column-major C's swap)
-    if (K > 0 && !bf16_dma_applies(p, Launch{}, 256, 256)) return GEMM_ERR_INVALID_VALUE;
+    // the direct-copy kernels' layout: k-contiguous operands (after a column-major C's swap); for
+    // FP32 inputs K >= 32 and 32-row copy blocks within 32-bit offsets
+    const bool f32 = in == In::F32;
+    const int64_t lim = (int64_t)1 << 31;
+    if (K > 0 && !f32 && !bf16_dma_applies(p, Launch{}, 256, 256)) return GEMM_ERR_INVALID_VALUE;
+    if (K > 0 && f32 && (p.oa != kRow || p.ob != kCol || K < 32 || 32 * p.lda * 4 >= lim || 32 * p.ldb * 4 >= lim))
+        return GEMM_ERR_INVALID_VALUE;
     if (M == 0 || N == 0) {
         t_last_kernel = "none";
         return GEMM_OK;
@@ -775,8 +780,11 @@ gemm_status_t run_fused(In in, int64_t M, int64_t N, int64_t K, const uint16_t* 
 
     // a column-major C's bias runs along its columns, the rows of the normalised C
     const Epilogue e{epi->alpha, epi->beta, epi->bias, row ? 0 : 1, (int)epi->activation, out16 ? 1 : 0};
-    // nothing to apply: the plain kernel on the same plan
+    // nothing to apply: the plain kernel on the same plan (FP32 inputs: the plain call)
     const bool identity = e.alpha == 1.f && e.beta == 0.f && e.bias == nullptr && e.act == kActNone && !out16;
+    if (identity && f32 && K > 0)
+        return run(In::F32, GEMM_ALGO_AUTO, M, N, K, static_cast<const float*>(A), lda, oa, static_cast<const float*>(B),
+                   ldb, ob, static_cast<float*>(C), ldc, oc, stream);
     hipError_t err = hipSuccess;
     const char* name = "epilogue_fill";
     if (K == 0) {
@@ -791,30 +799,32 @@ gemm_status_t run_fused(In in, int64_t M, int64_t N, int64_t K, const uint16_t* 
         // direct-copy kernels (the only ones that carry the epilogue), each strip on its own
         // cheapest tile: 2048 x 11008 is 8 x 32 tiles of 256 x 256 (one round) and a 2048 x 2816
         // strip of 256 x 128 tiles (one round), against 2.7 rounds of 256 x 128 tiles
-        const StripPricer dma_strips{kBf16DmaOpts, 2, kBf16DmaOpts, 0, dev.cus};
+        const TileOpt* opts = f32 ? kF32DmaOpts : kBf16DmaOpts;
+        const StripPricer dma_strips{opts, 2, opts, 0, dev.cus};
         Plan best;
-        for (const TileOpt& o : kBf16DmaOpts) {
-            const Plan pl = plan_core(p, o, true, true, dev.cus, dma_strips);
+        for (int i = 0; i < 2; ++i) {
+            const Plan pl = plan_core(p, opts[i], true, true, dev.cus, dma_strips);
             if (pl.cost < best.cost) best = pl;
         }
         const int eb = out16 ? 2 : 4;
         auto part = [&](int r0, int m, int c0, int n, const TileOpt* force) {
             EpiProblem ep{};
-            static_cast<Problem&>(ep) = sub_problem(p, r0, m, c0, n, 2);
+            static_cast<Problem&>(ep) = sub_problem(p, r0, m, c0, n, f32 ? 4 : 2);
             ep.C = reinterpret_cast<float*>(static_cast<char*>(C) + ((int64_t)r0 * p.ldc + c0) * eb);
             ep.e = e;
             if (e.bias != nullptr) ep.e.bias = e.bias + (e.bias_rows ? r0 : c0);
-            TileOpt o = force != nullptr ? *force : kBf16DmaOpts[0];
+            TileOpt o = force != nullptr ? *force : opts[0];
             if (force == nullptr) {
                 double c = 1e300;
-                for (const TileOpt& t : kBf16DmaOpts) {
-                    const double pc = plan_whole(ep, t, dev.cus).cost;
-                    if (pc < c) { c = pc; o = t; }
+                for (int i = 0; i < 2; ++i) {
+                    const double pc = plan_whole(ep, opts[i], dev.cus).cost;
+                    if (pc < c) { c = pc; o = opts[i]; }
                 }
             }
             Launch l = launch_for(ep, stream);
             l.vec_c = (p.ldc % 4 == 0) && aligned(ep.C, out16 ? 8 : 16);
             l.group_m = pick_group_m((m + o.bm - 1) / o.bm, (n + o.bn - 1) / o.bn);
+            if (f32) return launch_f32_dma_epi(ep, l, o.bm, o.bn);
             return identity ? launch_bf16_dma(ep, l, o.bm, o.bn, in == In::F16)
                             : launch_bf16_dma_epi(ep, l, o.bm, o.bn, in == In::F16);
         };
@@ -825,7 +835,8 @@ gemm_status_t run_fused(In in, int64_t M, int64_t N, int64_t K, const uint16_t* 
                                               {"f16_dma256x256_fused", "f16_dma256x128_fused"}},
                                              {{"bf16_dma256x256", "bf16_dma256x128"},
                                               {"f16_dma256x256", "f16_dma256x128"}}};
-        name = names[identity ? 1 : 0][in == In::F16 ? 1 : 0][best.opt.bn == 256 ? 0 : 1];
+        name = f32 ? (best.opt.bn == 256 ? "f32_dma256x256_fused" : "f32_dma128x128_fused")
+                   : names[identity ? 1 : 0][in == In::F16 ? 1 : 0][best.opt.bn == 256 ? 0 : 1];
     }
     if (err != hipSuccess) {
         t_last_hip_error = (int)err;
@@ -937,6 +948,13 @@ gemm_status_t gemm_fp8_f32acc(int64_t M, int64_t N, int64_t K, const uint8_t* A,
                               gemm_fp8_t format_b, float* C, int64_t ldc, gemm_order_t order_c, hipStream_t stream) {
     return gemm::run_fp8(M, N, K, A, lda, order_a, (int)format_a, B, ldb, order_b, (int)format_b, C, ldc, order_c,
                          stream);
+}
+
+gemm_status_t gemm_f32_fused(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, gemm_order_t order_a,
+                             const float* B, int64_t ldb, gemm_order_t order_b, void* C, int64_t ldc,
+                             gemm_order_t order_c, const gemm_epilogue_t* epilogue, hipStream_t stream) {
+    return gemm::run_fused(gemm::In::F32, M, N, K, A, lda, order_a, B, ldb, order_b, C, ldc, order_c, epilogue,
+                           stream);
 }
 
 gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,

@@ -49,6 +49,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "epilogue.hpp"
 #include "launch.hpp"
 
 namespace gemm {
@@ -392,11 +393,14 @@ struct EdgeCopyPlan {
     }
 };
 
-template <typename C, bool BATCH = false>
+// EPI: the fused epilogue (both operands k-contiguous), C = act(alpha acc + beta C + bias) stored
+// as FP32 or bf16 element by element from the accumulator layout.
+template <typename C, bool BATCH = false, bool EPI = false>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
-void k_f32_dma_edge(KArg<BATCH> p, int tiles_m, int tiles_n, int group_m) {
+void k_f32_dma_edge(std::conditional_t<EPI, EpiProblem, KArg<BATCH>> p, int tiles_m, int tiles_n, int group_m) {
     constexpr int BM = C::BM, BN = C::BN, S = C::S, FM = C::FM, FN = C::FN;
     constexpr bool A_KC = C::A_KC, B_KC = C::B_KC;
+    static_assert(!EPI || (A_KC && B_KC && !BATCH), "the fused epilogue takes k-contiguous operands");
     __shared__ __align__(16) unsigned char smem[S * C::STAGE];
     if constexpr (BATCH) p.select(blockIdx.z);
 
@@ -606,7 +610,19 @@ void k_f32_dma_edge(KArg<BATCH> p, int tiles_m, int tiles_n, int group_m) {
                 const int row = m0 + wm + (A_KC ? 16 * i + br : 4 * br + i % 4 + 64 * (i / 4));
                 if (G && row >= p.M) continue;
                 float* crow = p.C + (int64_t)row * p.ldc;
-                if (B_KC) {
+                if constexpr (EPI) {
+                    // 16 consecutive columns per 16 lanes: one 64-byte run of C per row and j
+                    const float brow = p.e.bias != nullptr && p.e.bias_rows ? p.e.bias[row] : 0.f;
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const int col = n0 + wn + 16 * j + li;
+                        if (G && col >= p.N) continue;
+                        const int64_t off = (int64_t)row * p.ldc + col;
+                        const float old = p.e.beta != 0.f ? epi_load(p.e, p.C, off) : 0.f;
+                        const float b = p.e.bias == nullptr ? 0.f : p.e.bias_rows ? brow : p.e.bias[col];
+                        epi_store(p.e, p.C, off, epi_apply(p.e, acc[i][j][v], old, b));
+                    }
+                } else if (B_KC) {
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
                         const int col = n0 + wn + 16 * j + li;
@@ -677,6 +693,25 @@ bool f32_dma_applies(const Problem& p, const Launch& l, int bm, int bn) {
     if ((p.oa == kRow && rows * p.lda * 4 >= lim) || (p.ob == kCol && rows * p.ldb * 4 >= lim)) return false;
     // at least one whole tile along each edge (the host plans overhangs and strips)
     return l.vec_a && l.vec_b && p.K >= BK && p.M >= bm && p.N >= bn;
+}
+
+// Fused epilogue on either tile, both operands k-contiguous, any M, N (tiles overhang both
+// edges) and K >= BK.
+hipError_t launch_f32_dma_epi(const EpiProblem& p, const Launch& l, int bm, int bn) {
+    if (p.oa != kRow || p.ob != kCol || p.K < BK) return hipErrorInvalidValue;
+    const int g = l.group_m;
+    if (bm == 256 && bn == 256) {
+        const int tm = (p.M + 255) / 256, tn = (p.N + 255) / 256;
+        hipLaunchKernelGGL((k_f32_dma_edge<Cfg<256, 256, 4, 2, 2, true, true>, false, true>), dim3(tm * tn),
+                           dim3(64 * 8), 0, l.stream, p, tm, tn, g);
+    } else if (bm == 128 && bn == 128) {
+        const int tm = (p.M + 127) / 128, tn = (p.N + 127) / 128;
+        hipLaunchKernelGGL((k_f32_dma_edge<Cfg<128, 128, 2, 2, 2, true, true>, false, true>), dim3(tm * tn),
+                           dim3(64 * 4), 0, l.stream, p, tm, tn, g);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 // Split-K on whole 256 x 256 tiles (M and N multiples of 256): `slices` K slices of s.kslice as

@@ -23,6 +23,9 @@ hipError_t launch_f32_dma(const Problem& p, const Launch& l, int bm, int bn);
 // Split-K on the FP32 direct-copy kernel's whole 256 x 256 tiles (M, N multiples of 256, the
 // f32_dma_applies conditions, every slice K >= 32 deep): as launch_bf16_dma_split.
 hipError_t launch_f32_dma_split(const SplitProblem& s, int slices, const Launch& l);
+// The FP32 direct-copy kernel with the fused epilogue (epilogue.hpp): row-major A, column-major
+// B, any M, N, K >= 32, tiles 256x256 or 128x128 overhanging both edges.
+hipError_t launch_f32_dma_epi(const EpiProblem& p, const Launch& l, int bm, int bn);
 // Input element types of the kernels that take more than one
 constexpr int kElemF32 = 0, kElemBf16 = 1, kElemF16 = 2, kElemFp8 = 3;
 // BF16 direct-copy kernel (bf16_dma.hip): row-major A, column-major B, any M, N, K >= 64,

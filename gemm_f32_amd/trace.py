@@ -39,6 +39,8 @@ SPECS = [
     ("square4096_f32@REGBLOCK", ["--workload", "square4096_f32", "--algo", "REGBLOCK"], 20),
     ("square4096_f32@TILED", ["--workload", "square4096_f32", "--algo", "TILED"], 3),
     ("square4096_f32@NAIVE", ["--workload", "square4096_f32", "--algo", "NAIVE"], 2),
+    ("square4096_f32_rc", ["--workload", "square4096_f32_rc"], 20),
+    ("square4096_f32_rc@bias_gelu_bf16", ["--workload", "square4096_f32_rc", "--epilogue", "bias_gelu_bf16"], 20),
     ("square4096_bf16", ["--workload", "square4096_bf16"], 30),
     ("square4096_bf16@MFMA_256x128", ["--workload", "square4096_bf16", "--algo", "MFMA_256x128"], 30),
     ("square4096_bf16@MFMA_128x128", ["--workload", "square4096_bf16", "--algo", "MFMA_128x128"], 30),

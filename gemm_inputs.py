@@ -56,6 +56,7 @@ WORKLOADS = {
         Workload("square256_f32", 1, 256, 256, 256, "f32"),
         Workload("probe16_f32", 1, 16, 16, 16, "f32"),
         Workload("square4096_f32", 2, 4096, 4096, 4096, "f32"),
+        Workload("square4096_f32_rc", 2, 4096, 4096, 4096, "f32", ROW_MAJOR, COL_MAJOR),
         Workload("square4096_bf16", 3, 4096, 4096, 4096, "bf16", ROW_MAJOR, COL_MAJOR),
         Workload("square4096_f16", 3, 4096, 4096, 4096, "f16", ROW_MAJOR, COL_MAJOR),
         Workload("square4096_e4m3", 3, 4096, 4096, 4096, "e4m3", ROW_MAJOR, COL_MAJOR),

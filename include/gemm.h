@@ -317,8 +317,8 @@ gemm_status_t gemm_f16_f32acc_strided_batched(int64_t batch, int64_t M, int64_t 
                                               float *C, int64_t ldc, int64_t stride_c, gemm_order_t order_c,
                                               hipStream_t stream);
 
-/* Fused epilogue: C = act(alpha * A.B + beta * C + bias), computed on each output while it is
- * still in registers and stored as FP32 or bf16 ("How a Matrix Multiply Runs on a GPU", section
+/* Fused epilogue: C = act(alpha * A.B + beta * C + bias), computed on each output inside the GEMM
+ * kernel, between its accumulators and its store, and stored as FP32 or bf16 ("How a Matrix Multiply Runs on a GPU", section
  * "Level 2", the epilogue of the block-tile loop, and section "Operational guidance and
  * trade-offs"; "A06 - Tiled Matrix Multiply (GEMM)", section "6. Challenges, Drawbacks &
  * Tradeoffs").
@@ -345,10 +345,15 @@ typedef struct {
  * FP32 products and sums.  C is `void *` (float or uint16_t per out_type); the rest as the plain
  * calls.  The epilogue runs in the 16-bit direct-copy kernel, which takes k-contiguous operands:
  * row-major A with column-major B (a PyTorch Linear: x . W^T), and K >= 64 (K == 0 gives
- * act(beta * C + bias)).  One kernel launch; nothing is allocated.
+ * act(beta * C + bias)).  A core launch plus at most two edge strips on the same stream, all on
+ * that kernel; nothing is allocated.  An identity epilogue (alpha 1, beta 0, no bias or
+ * activation, FP32 C) runs the plain kernel on the same plan.
+ * gemm_f32_fused: the same for FP32 inputs on the FP32 direct-copy kernel: row-major A with
+ * column-major B, K >= 32; an identity epilogue is gemm_f32.
  * Errors: as the plain calls, plus GEMM_ERR_INVALID_VALUE for a NULL epilogue, an unknown
  * activation or output type, a bias not 4-byte aligned, a C not aligned to its output element,
- * or operands the direct-copy kernel does not take (other orders, 0 < K < 64). */
+ * or operands the direct-copy kernels do not take (other orders, 0 < K < 64 for 16-bit inputs,
+ * 0 < K < 32 for FP32 ones). */
 gemm_status_t gemm_bf16_f32acc_fused(int64_t M, int64_t N, int64_t K,
                                      const uint16_t *A, int64_t lda, gemm_order_t order_a,
                                      const uint16_t *B, int64_t ldb, gemm_order_t order_b,
@@ -359,6 +364,11 @@ gemm_status_t gemm_f16_f32acc_fused(int64_t M, int64_t N, int64_t K,
                                     const uint16_t *B, int64_t ldb, gemm_order_t order_b,
                                     void *C, int64_t ldc, gemm_order_t order_c,
                                     const gemm_epilogue_t *epilogue, hipStream_t stream);
+gemm_status_t gemm_f32_fused(int64_t M, int64_t N, int64_t K,
+                             const float *A, int64_t lda, gemm_order_t order_a,
+                             const float *B, int64_t ldb, gemm_order_t order_b,
+                             void *C, int64_t ldc, gemm_order_t order_c,
+                             const gemm_epilogue_t *epilogue, hipStream_t stream);
 
 /* ---- Without any allocation: split-K partial sums in a static scratch array ---------------
  * For callers that cannot allocate device memory or pass a workspace: code under HIP graph

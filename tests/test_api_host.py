@@ -365,7 +365,7 @@ def test_batched_valid_layouts_reach_the_device_check(layout):
 
 
 # --- fused epilogue: argument checks before any device call -------------------------------
-FUSED = {"bf16": g.gemm_bf16_f32acc_fused, "f16": g.gemm_f16_f32acc_fused}
+FUSED = {"bf16": g.gemm_bf16_f32acc_fused, "f16": g.gemm_f16_f32acc_fused, "f32": g.gemm_f32_fused}
 
 
 def fargs(M=8, N=8, K=64, A=FAKE, lda=64, oa=R, B=FAKE, ldb=64, ob=C_, C=FAKE, ldc=8, oc=R):
@@ -381,9 +381,24 @@ def fargs(M=8, N=8, K=64, A=FAKE, lda=64, oa=R, B=FAKE, ldb=64, ob=C_, C=FAKE, l
     dict(epi=dict(activation=3)), dict(epi=dict(out_type=2)), dict(epi=dict(bias=FAKE + 2)),
     dict(call=dict(M=-1)), dict(call=dict(ldc=7)),
 ], ids=lambda d: ",".join(f"{k}={v}" for k, v in {**d.get("call", {}), **d.get("epi", {})}.items()))
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_fused_invalid_arguments(dtype, bad):
+    if dtype == "f32" and bad.get("call", {}).get("K") == 32:
+        pytest.skip("K = 32 is one whole FP32 k-tile: valid for FP32 inputs")
     assert _status(FUSED[dtype], *fargs(**bad.get("call", {})), **bad.get("epi", {})) == INVALID
+
+
+@pytest.mark.parametrize("call", [dict(K=31, lda=31, ldb=31), dict(K=16, lda=16, ldb=16), dict(A=FAKE + 2),
+                                  dict(oa=C_, lda=8)])
+def test_f32_fused_invalid_arguments(call):
+    """FP32 inputs: K >= 32 (one k-tile of the FP32 direct-copy kernel), 4-byte aligned operands."""
+    assert _status(FUSED["f32"], *fargs(**call)) == INVALID
+
+
+@pytest.mark.skipif(gpu_available(), reason="checks the no-GPU path")
+def test_f32_fused_valid_call_reaches_the_device_check():
+    assert _status(FUSED["f32"], *fargs(K=32, lda=32, ldb=32), activation=g.Act.RELU,
+                   bias=FAKE) == g.Status.ERR_UNSUPPORTED_DEVICE
 
 
 def test_fused_null_epilogue_rejected():

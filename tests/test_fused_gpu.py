@@ -40,7 +40,7 @@ def run_fused(p, epi, seed=0):
         flat = np.full_like(flat, BF16_NAN if out == g.Out.BF16 else np.nan)   # never read
     A, B, C = to_device(p.A), to_device(p.B), to_device(flat)
     bias_d = to_device(bias) if bias is not None else None
-    fn = {"bf16": g.gemm_bf16_f32acc_fused, "f16": g.gemm_f16_f32acc_fused}[p.dtype]
+    fn = {"bf16": g.gemm_bf16_f32acc_fused, "f16": g.gemm_f16_f32acc_fused, "f32": g.gemm_f32_fused}[p.dtype]
     print(f"[gpu] fused {p.dtype} M={p.M} N={p.N} K={p.K} oc={p.order_c} epi={epi}", flush=True)
     fn(p.M, p.N, p.K, A.data_ptr(), p.lda, p.order_a, B.data_ptr(), p.ldb, p.order_b, C.data_ptr(), p.ldc,
        p.order_c, alpha=alpha, beta=beta, bias=bias_d.data_ptr() if bias_d is not None else 0, activation=act,
@@ -72,15 +72,17 @@ def assert_close(got, Y, S, dtype, out):
 @pytest.mark.parametrize("epi", list(EPILOGUES))
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("oc", [R, C_], ids=["rowC", "colC"])
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_fused_matches_oracle(dtype, oc, shape, epi):
     M, N, K = shape
     p = gi.make_problem(M, N, K, dtype, R, C_, oc, wid=81, pad_c=3)
     got, Y, S, pad_ok = run_fused(p, EPILOGUES[epi], seed=M + N)
     assert pad_ok, "C written outside the logical matrix"
-    # the identity epilogue runs the plain direct-copy kernel on the same plan
-    assert g.gemm_last_kernel().endswith("_fused") != (epi == "plain")
-    assert "_dma256x" in g.gemm_last_kernel()
+    # the identity epilogue runs the plain kernel (16-bit inputs: on the same plan; FP32: gemm_f32)
+    kernel = g.gemm_last_kernel()
+    assert kernel.endswith("_fused") != (epi == "plain"), kernel
+    if dtype != "f32" or epi != "plain":
+        assert "_dma" in kernel, kernel
     assert_close(got, Y, S, dtype, EPILOGUES[epi][4])
 
 
@@ -195,3 +197,29 @@ def test_fused_gelu_accuracy(out):
     ref = x * 0.5 * (1.0 + erf(x / np.sqrt(2.0)))
     bound = 5e-7 * np.abs(x) + (2.0 ** -8 * np.abs(ref) if out == g.Out.BF16 else 0.0)
     assert np.all(np.abs(got - ref) <= bound + 1e-30)
+
+
+@pytest.mark.parametrize("oc", [R, C_], ids=["rowC", "colC"])
+def test_f32_fused_whole_tiles_and_edges(oc):
+    """FP32 inputs on 256 x 256 tiles overhanging both edges (4095 x 4097 x 512): beta, bias and
+    ReLU, sampled on whole rows and columns at tile boundaries against the oracle."""
+    import torch
+    from test_workloads_gpu import sample_indices
+    M, N, K = 4095, 4097, 512
+    p = gi.make_problem(M, N, K, "f32", R, C_, oc, wid=82)
+    rng = np.random.default_rng(29)
+    bias = rng.uniform(-1, 1, N).astype(np.float32)
+    old = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+    flat, _ = gi.lay_out(old, p.order_c, p.ldc)
+    A, B, C, bias_d = to_device(p.A), to_device(p.B), to_device(flat), to_device(bias)
+    print(f"[gpu] f32 fused 4095x4097x512 oc={oc}", flush=True)
+    g.gemm_f32_fused(M, N, K, A.data_ptr(), p.lda, R, B.data_ptr(), p.ldb, C_, C.data_ptr(), p.ldc, p.order_c,
+                     alpha=0.75, beta=0.5, bias=bias_d.data_ptr(), activation=g.Act.RELU)
+    torch.cuda.synchronize()
+    assert g.gemm_last_kernel() == "f32_dma256x256_fused"
+    got = gi.unpack_c(C.cpu().numpy(), M, N, p.ldc, p.order_c).astype(np.float64)
+    rows, cols = sample_indices(M, N, 7)
+    ref, D = oracle.gemm_sampled(M, N, K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b, rows, cols)
+    Y, S = oracle.epilogue(ref[None, :], D[None, :], alpha=0.75, beta=0.5, C_old=old[rows, cols][None, :],
+                           bias=bias[cols], activation=oracle.ACT_RELU)
+    assert_close(got[rows, cols][None, :], Y, S, "f32", g.Out.F32)

@@ -30,7 +30,7 @@ def test_workload_full_size_sampled(name):
     assert np.all(np.isfinite(C)), "every output written and finite"
     rows, cols = sample_indices(p.M, p.N, gi.WORKLOADS[name].wid)
     ref, D = oracle.gemm_sampled(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b,
-                                 rows, cols)
+                                 rows, cols, **gi.oracle_formats(p))
     err = oracle.normalised_error(C[rows, cols], ref, D)
     print(f"{name}: normalised error {err:.3e} over {rows.size} sampled outputs")
     assert err <= TOL[p.dtype]

@@ -59,12 +59,24 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // input element types of the kernel: 16-bit, or 8-bit as kInFp8 + 2 fmt_a + fmt_b
 enum InType { kInBf16 = 0, kInF16 = 1, kInFp8 = 2 };
 
 // gfx950 buffer resource, word 3: 32-bit unformatted data, no swizzle
 constexpr int kBufWord3 = 0x00020000;
+
+// gfx950's transposing LDS read of four 16-bit values per lane.  (Through a restrict-qualified
+// parameter: the inlined read then carries alias information, without which the compiler makes
+// it wait for every copy into LDS in flight, as it does not for the plain vector reads.)
+__device__ __forceinline__ s16x4 lds_read_tr16(lds_s16x4* __restrict__ p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+}
+
+// the lane's index within its wavefront
+__device__ __forceinline__ int lane_id() { return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
 // chunk c of LDS row r is stored at c ^ swz(r): any 16 consecutive rows read at one
 // logical chunk hit 16 distinct 16-byte bank groups
@@ -130,12 +142,17 @@ using Cfg256x128F8 = Cfg<256, 128, 4, 2, 2, 3, false, 1>;
 // TK: K below one 16-byte chunk of 8-bit elements (K < 16): no k-loop, the K tail read byte by
 // byte.  (A separate kernel: with byte loads anywhere in the function, the compiler adds waits
 // for all copies in flight before every LDS read of the k-loop.)
-template <typename C, bool VEC_C, int IT, int MODE, bool TK = false>
+// BRM: row-major B (n contiguous; 16-bit inputs).  The B tile is then held in LDS as it lies in
+// memory, BK k-rows of BN columns, and read with gfx950's transposing LDS read, which hands each
+// lane four consecutive k of one column (the layout of the B tile and its reads are described at
+// the copy plan below).
+template <typename C, bool VEC_C, int IT, int MODE, bool TK = false, bool BRM = false>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::NW / 4, C::NW / 4)))
 void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int group_m) {
     constexpr bool BATCH = MODE == kBatched, EPI = MODE == kEpilogue;
     static_assert((IT >= kInFp8) == (C::ES == 1), "8-bit inputs take the 8-bit configurations");
     static_assert(!TK || C::ES == 1, "byte-wise K tail for 8-bit inputs only");
+    static_assert(!BRM || C::ES == 2, "row-major B for 16-bit inputs only");
     constexpr int ES = C::ES;
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, FM = C::FM, FN = C::FN, SUB = C::SUB;
     constexpr int ROW = C::ROW, MF = C::MF;
@@ -179,6 +196,47 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
         (void*)(bvalid > 0 ? B + (int64_t)brow0 * p.ldb * ES : B), (short)0, (int)(bvalid * p.ldb * ES), kBufWord3);
     // byte distance between consecutive copies of a wavefront
     const int astep = C::RPC * (int)p.lda * ES, bstep = C::RPC * (int)p.ldb * ES;
+
+    // ---- row-major B (BRM).  The B tile of a k-tile is BK = 64 k-rows of BN columns, RP = 2 BN
+    // bytes each, in RP / 64 groups of 64 bytes (32 columns).  Group q of k-row kr is stored at
+    // q ^ bsw(kr), bsw taking bits 0, 1 and 3 of kr (as many as there are groups), so that the
+    // k-rows one transposing read takes together (four consecutive ones, and the four 8 rows on
+    // that the other half-wavefront takes) fall on distinct banks.  A copy fills 1024 / RP whole
+    // k-rows; the lane that stores position l of it fetches k-row l / (RP / 16), physical chunk
+    // c = l % (RP / 16), which holds logical chunk c ^ 4 bsw(kr) (8 columns).  Chunks past N (the
+    // last column tile) fetch the row's last 8 columns instead: they feed only columns of C that
+    // are never stored, and every fetch stays inside the operand (the host requires N % 8 == 0).
+    // bsw of a copy's k-row is the xor of bsw of its parts (the wavefront's first k-row, the
+    // copy's first row, the lane's row in the copy: disjoint bits), so a copy's lane offset
+    // depends on the copy only through one of at most RP / 64 group patterns.
+    constexpr int RP = BN * 2, RPC2 = 1024 / RP, KRW = BK / C::NW, GM = RP / 64 - 1;
+    auto bsw = [](int kr) { return ((kr & 3) | ((kr >> 1) & 4)) & GM; };
+    const int lr2 = lane / (RP / 16), cc2 = lane % (RP / 16);
+    const int bsw_w = __builtin_amdgcn_readfirstlane(bsw(wave * KRW));
+    // offset of this lane's 16 bytes from the wavefront's first k-row of the k-tile, for a copy
+    // whose k-rows have pattern f
+    auto brm_lane = [&](int f) -> unsigned {
+        const int col = min(n0 + 8 * (cc2 ^ (4 * (bsw(lr2) ^ f))), p.N - 8);
+        return (unsigned)(lr2 * (int)p.ldb * 2 + 2 * (col - n0));
+    };
+    // the resource starts at the wavefront's first k-row, column n0, and ends after element
+    // (K-1, N-1), which no fetch passes (the host requires K ldb 2 < 2^31)
+    const int brm_row0 = wave * KRW;
+    const __amdgpu_buffer_rsrc_t rbr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(B + ((int64_t)brm_row0 * p.ldb + n0) * 2), (short)0,
+        (int)(((int64_t)(p.K - 1 - brm_row0) * p.ldb + p.N - n0) * 2), kBufWord3);
+    const int brm_kt = BK * (int)p.ldb * 2, brm_step = RPC2 * (int)p.ldb * 2;   // per k-tile, per copy
+    // B copy jb of k-tile kt into the LDS block at dst
+    // (offsets as named values: with the lambda call inside the builtin's argument list the host
+    // pass of this compiler silently drops the kernel's launch stub)
+    auto copy_b = [&](int jb, int kt, lds_void* dst) {
+        if constexpr (BRM) {
+            const unsigned vo = brm_lane(bsw_w ^ bsw(jb * RPC2));
+            const int so = kt * brm_kt + jb * brm_step;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rbr, dst, 16, vo, so, 0, 0);
+        } else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, boff[jb & 1] + jb * bstep, kt * ROW, 0, 0);
+    };
     // copy j (of DMA) of k-tile kt (source) into stage st.  (The LDS pointer is a named
     // variable: cast inline in the builtin's argument list, the host pass of this compiler
     // silently drops the kernel's launch stub.)
@@ -193,7 +251,7 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
         } else {
             const int jb = j - C::A_DMA;
             lds_void* dst = (lds_void*)(s + C::A_BYTES + (wave * C::B_DMA + jb) * 1024);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, boff[jb & 1] + jb * bstep, kt * ROW, 0, 0);
+            copy_b(jb, kt, dst);
         }
     };
     // the copies that fall on slot `slot` of the window (copy q sits at slot q W / DMA)
@@ -205,7 +263,7 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
 
     // ---- fragments and matrix instructions ----
     const int l32 = lane & 31, h = lane >> 5, sw = swz(l32);
-    const int a_off = (wm + l32) * ROW, b_off = C::A_BYTES + (wn + l32) * ROW;
+    const int a_off = (wm + l32) * ROW;
     f32x16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -230,11 +288,36 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
             return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
     };
+    // BRM: lane L of 16-lane group g = L / 16 (l = L % 16) takes, for B fragment j at k-step s,
+    // column wn + 32 j + L % 32 at k = 16 s + 8 h + 0..7 (the k of A's lane L) from two
+    // transposing reads of four k-rows each.  In such a read the lanes of a group address k-rows
+    // kb + l / 4, the four columns from 4 (l % 4) of the group's 16, and lane l receives element
+    // l % 4 of the 8-byte chunks of lanes 4 e + l / 4, e = 0..3: column l of the 16 at k-rows
+    // kb .. kb + 3.  The lane's k-row 8 h + l / 4 (plus 16 s + 4 t) fixes its group pattern, and
+    // fragment j's group index (wn / 32 + j, wn / 32 a multiple of the fragment count) differs
+    // from fragment 0's in the low bits only: fragment j's offset is fragment 0's xor 64 j.
+    const int l16 = lane & 15;
+    const int brm_kr = 8 * h + (l16 >> 2);
+    const unsigned brm_rd = (unsigned)(brm_kr * RP + (((wn >> 5) ^ bsw(brm_kr)) << 6) + 32 * ((lane >> 4) & 1) +
+                                       8 * (l16 & 3));
+    // (The tile's LDS offset, a multiple of the row block, is added before the xor, so that the
+    // fragments' offsets are formed per k-tile rather than held in registers across the loop.)
+    auto frag_rm = [&](int tile, int s, int j) -> bf16x8 {
+        const unsigned char* q = smem + ((unsigned)(tile + brm_rd) ^ (unsigned)(j << 6)) + 16 * s * RP;
+        const s16x4 lo = lds_read_tr16((lds_s16x4*)q);
+        const s16x4 hi = lds_read_tr16((lds_s16x4*)(q + 4 * RP));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // B fragment j at k-step s of the B tile at LDS offset `tile`
+    auto frag_b = [&](int tile, int s, int j) -> Frag {
+        if constexpr (BRM) return frag_rm(tile, s, j);
+        else return frag_at(smem + tile + (wn + l32) * ROW + j * 32 * ROW, s);
+    };
     // fragment read `m` (A fragments first, then B) of k-step s of stage st into buffer b
     auto read_slot = [&](int st, int s, int m, int b) {
         const unsigned char* base = smem + st * C::STAGE;
         if (m < FM) fa[b][m] = frag_at(base + a_off + m * 32 * ROW, s);
-        else if (m < C::RD) fb[b][m - FM] = frag_at(base + b_off + (m - FM) * 32 * ROW, s);
+        else if (m < C::RD) fb[b][m - FM] = frag_b(st * C::STAGE + C::A_BYTES, s, m - FM);
     };
     auto mfma = [&](int m, int b) {
         const int i = m / FN, j = m % FN;
@@ -273,10 +356,9 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
         // against 2048 of matrix work).
         if (nk > 0) {                         // uniform
             const int last = nk - 1;
-            const int rb_off = b_off - C::A_BYTES;
             auto read_ring = [&](int abuf, int bbuf, int s, int m, int b) {
                 if (m < FM) fa[b][m] = frag_at(smem + abuf * C::A_BYTES + a_off + m * 32 * ROW, s);
-                else if (m < C::RD) fb[b][m - FM] = frag_at(smem + bbuf * C::A_BYTES + rb_off + (m - FM) * 32 * ROW, s);
+                else if (m < C::RD) fb[b][m - FM] = frag_b(bbuf * C::A_BYTES, s, m - FM);
             };
             auto issue_a = [&](int j, int kt, int buf) {
                 lds_void* dst = (lds_void*)(smem + buf * C::A_BYTES + (wave * C::A_DMA + j) * 1024);
@@ -284,7 +366,7 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
             };
             auto issue_b = [&](int j, int kt, int buf) {
                 lds_void* dst = (lds_void*)(smem + buf * C::A_BYTES + (wave * C::B_DMA + j) * 1024);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, boff[j & 1] + j * bstep, kt * ROW, 0, 0);
+                copy_b(j, kt, dst);
             };
             // instruction slots between two copies: B over the last k-step, A over the others
             constexpr int BSL = MF / C::B_DMA, ASL = (SUB - 1) * MF / C::A_DMA;
@@ -407,16 +489,35 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
             k = k0 + CE * ((lane % 8) ^ swz(lr + C::RPC * (jj & 1)));
             keep = grow < rows && k < p.K;
         };
+        // BRM: B chunk j of the copy plan, k-row kr of the tile: its source (clamped to an element
+        // of B) and whether it lies inside K and N
+        auto chunk_rm = [&](int jb, const unsigned char*& src, bool& keep) {
+            const int lt = lane_id();         // (formed anew, as in the epilogue)
+            const int kr = brm_row0 + jb * RPC2 + lt / (RP / 16);
+            const int n = n0 + 8 * ((lt % (RP / 16)) ^ (4 * bsw(kr)));
+            src = B + ((int64_t)min(k0 + kr, p.K - 1) * p.ldb + min(n, p.N - 8)) * 2;
+            keep = k0 + kr < p.K && n < p.N;
+        };
         if constexpr (!TK) {                  // K >= CE (16-bit inputs: K >= 64)
 #pragma unroll
             for (int j = 0; j < C::DMA; ++j) {    // all loads first
                 const unsigned char* src; int k; bool keep;
+                if (BRM && j >= C::A_DMA) {
+                    chunk_rm(j - C::A_DMA, src, keep);
+                    v[j] = load16(src);
+                    continue;
+                }
                 chunk(j, src, k, keep);
                 v[j] = load16(src + (int64_t)(k + CE <= p.K ? k : p.K - CE) * ES);
             }
 #pragma unroll
             for (int j = 0; j < C::DMA; ++j) {    // then keep, shift or clear, as arithmetic
                 const unsigned char* src; int k; bool keep;
+                if (BRM && j >= C::A_DMA) {       // whole k-rows: keep or clear
+                    chunk_rm(j - C::A_DMA, src, keep);
+                    if (!keep) v[j] = make_uint4(0u, 0u, 0u, 0u);
+                    continue;
+                }
                 chunk(j, src, k, keep);
                 // straddling chunk: its r valid elements are the top r of the last CE of the row
                 const int r = min(max(p.K - k, 1), CE - 1);
@@ -468,10 +569,12 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
     // where C allows (VEC_C) and the four columns lie inside, else element by element
     __builtin_amdgcn_s_barrier();          // every wavefront is done with the stages
     asm volatile("" ::: "memory");
+    // the lane's index formed anew rather than kept live across the k-loop
+    const int lane_e = lane_id(), l32e = lane_e & 31, he = lane_e >> 5;
     constexpr int LPR = C::WN / 4, RPI = 64 / LPR;   // lanes per C row, rows per store
     constexpr int Q = 32 / RPI;                       // stores per 32-row band
     float* band = reinterpret_cast<float*>(smem) + wave * 32 * C::EP;
-    const int cc = 4 * (lane % LPR), col = n0 + wn + cc;    // this lane's four columns, every store
+    const int cc = 4 * (lane_e % LPR), col = n0 + wn + cc;    // this lane's four columns, every store
     // fused epilogue: a column bias is the same for every store of the lane, loaded once
     float bcol[4] = {0.f, 0.f, 0.f, 0.f};
     if constexpr (EPI) {
@@ -487,8 +590,8 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                band[(8 * (r >> 2) + 4 * h + (r & 3)) * C::EP + 32 * j + l32] = acc[i][j][r];
-        const int row0 = m0 + wm + 32 * i + lane / LPR;     // row of store q: row0 + q RPI
+                band[(8 * (r >> 2) + 4 * he + (r & 3)) * C::EP + 32 * j + l32e] = acc[i][j][r];
+        const int row0 = m0 + wm + 32 * i + lane_e / LPR;     // row of store q: row0 + q RPI
         if constexpr (EPI) {
             // The fused epilogue on the staged values, four columns of a row per store.  C's previous
             // values (beta != 0) and a row bias are loaded one store ahead, so that their latency
@@ -528,7 +631,7 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
                     const float old[4] = {old_n[0], old_n[1], old_n[2], old_n[3]};
                     const float brow = brow_n;
                     if (q + 1 < Q) load_whole(q + 1, old_n, brow_n);
-                    const int rr = q * RPI + lane / LPR, row = row0 + q * RPI;
+                    const int rr = q * RPI + lane_e / LPR, row = row0 + q * RPI;
                     const f32x4 v = *reinterpret_cast<const f32x4*>(band + rr * C::EP + cc);
                     float y[4];
 #pragma unroll
@@ -551,7 +654,7 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
                 const float old[4] = {old_n[0], old_n[1], old_n[2], old_n[3]};
                 const float brow = brow_n;
                 if (q + 1 < Q) load_ahead(q + 1, old_n, brow_n);
-                const int rr = q * RPI + lane / LPR, row = row0 + q * RPI;
+                const int rr = q * RPI + lane_e / LPR, row = row0 + q * RPI;
                 const f32x4 v = *reinterpret_cast<const f32x4*>(band + rr * C::EP + cc);
                 const int64_t off = (int64_t)row * p.ldc + col;
                 float y[4];
@@ -568,7 +671,7 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
         } else {
 #pragma unroll
             for (int q = 0; q < Q; ++q) {
-                const int rr = q * RPI + lane / LPR, row = row0 + q * RPI;
+                const int rr = q * RPI + lane_e / LPR, row = row0 + q * RPI;
                 const f32x4 v = *reinterpret_cast<const f32x4*>(band + rr * C::EP + cc);
                 const int64_t off = (int64_t)row * p.ldc + col;
                 if (VEC_C && (interior || (row < p.M && col + 3 < p.N))) {
@@ -587,16 +690,20 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
 }
 
 // One launch of configuration C in mode MODE for input type `it`: tiles along x, grid_y K
-// slices, grid_z batch entries.
+// slices, grid_z batch entries.  16-bit inputs with row-major B take the BRM build.
 template <typename C, int MODE, int IT, bool TK = false>
 hipError_t launch_it(const typename ModeArgT<MODE>::type& p, const Launch& l, int grid_y) {
     const int tiles_m = (p.M + C::BM - 1) / C::BM, tiles_n = (p.N + C::BN - 1) / C::BN;
     const dim3 grid((unsigned)tiles_m * tiles_n, (unsigned)grid_y, MODE == kBatched ? l.batch : 1), block(C::THREADS);
-    if (l.vec_c)
-        hipLaunchKernelGGL((k_bf16_dma<C, true, IT, MODE, TK>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
-    else
-        hipLaunchKernelGGL((k_bf16_dma<C, false, IT, MODE, TK>), grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
-    return hipGetLastError();
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, block, 0, l.stream, p, tiles_m, tiles_n, l.group_m);
+        return hipGetLastError();
+    };
+    if constexpr (C::ES == 2) {
+        if (p.ob == kRow)
+            return l.vec_c ? go(k_bf16_dma<C, true, IT, MODE, TK, true>) : go(k_bf16_dma<C, false, IT, MODE, TK, true>);
+    }
+    return l.vec_c ? go(k_bf16_dma<C, true, IT, MODE, TK>) : go(k_bf16_dma<C, false, IT, MODE, TK>);
 }
 
 template <typename C, int MODE, bool TK = false>
@@ -627,10 +734,13 @@ int in16(bool f16) { return f16 ? kInF16 : kInBf16; }
 }  // namespace
 
 bool bf16_dma_applies(const Problem& p, const Launch&, int, int) {
-    // one bound for both configurations: 64 rows per wavefront copy block at most
+    // one bound for both configurations: 64 rows per wavefront copy block at most.  Row-major B
+    // (the BRM build): whole 8-column chunks (N % 8 == 0), and byte offsets into B up to element
+    // (K-1, N-1) below 2^31
     const int64_t lim = (int64_t)1 << 31;
-    return p.oa == kRow && p.ob == kCol && p.K >= 64 && (int64_t)64 * p.lda * 2 < lim &&
-           (int64_t)64 * p.ldb * 2 < lim;
+    if (p.oa != kRow || p.K < 64 || (int64_t)64 * p.lda * 2 >= lim) return false;
+    if (p.ob == kRow) return p.N % 8 == 0 && ((int64_t)(p.K - 1) * p.ldb + p.N) * 2 < lim;
+    return p.ob == kCol && (int64_t)64 * p.ldb * 2 < lim;
 }
 
 bool fp8_dma_applies(const Problem& p) {

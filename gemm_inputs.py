@@ -59,6 +59,8 @@ WORKLOADS = {
         Workload("square4096_f32_rc", 2, 4096, 4096, 4096, "f32", ROW_MAJOR, COL_MAJOR),
         Workload("square4096_bf16", 3, 4096, 4096, 4096, "bf16", ROW_MAJOR, COL_MAJOR),
         Workload("square4096_f16", 3, 4096, 4096, 4096, "f16", ROW_MAJOR, COL_MAJOR),
+        # PyTorch's `a @ b` layout: both operands row-major (B n-contiguous)
+        Workload("square4096_bf16_rr", 3, 4096, 4096, 4096, "bf16"),
         Workload("square4096_e4m3", 3, 4096, 4096, 4096, "e4m3", ROW_MAJOR, COL_MAJOR),
         Workload("square4096_e5m2", 3, 4096, 4096, 4096, "e5m2", ROW_MAJOR, COL_MAJOR),
         Workload("llm_ffn_up_2048x11008x4096_e4m3", 5, 2048, 11008, 4096, "e4m3", ROW_MAJOR, COL_MAJOR, ROW_MAJOR,

@@ -79,8 +79,9 @@ typedef enum {
  *                      wherever it applies, else the register-staged kernel
  *                      (v_mfma_f32_32x32x2_f32, 128 x 128 or 64 x 64 tiles, any layout).  BF16 /
  *                      FP16: the direct-copy kernel (v_mfma_f32_32x32x16_bf16 / _f16) for
- *                      row-major A with column-major B and K >= 64, else the register-staged
- *                      kernel (128 x 128, 64 x 64 or 256 x 128 tiles, any layout);
+ *                      row-major A with column-major B, or with row-major B and N % 8 == 0,
+ *                      and K >= 64, else the register-staged kernel (128 x 128, 64 x 64 or
+ *                      256 x 128 tiles, any layout);
  *   MFMA_256x256, MFMA_256x128, MFMA_128x128, MFMA_64x64
  *                      a block tile forced.  256x256: the direct-copy kernel at 256 x 256 (its
  *                      requirements below; GEMM_ERR_INVALID_VALUE otherwise).  256x128 (16-bit
@@ -103,8 +104,11 @@ typedef enum {
  *                      the register-staged kernel in the same call.  16-bit inputs:
  *                      v_mfma_f32_32x32x16, 256 x 256 tiles of four wavefronts (128 x 128 each,
  *                      a ring of five half-stage LDS buffers) or 256 x 128 of eight (64 x 64
- *                      each, three stages); needs row-major A, column-major B and K >= 64, any
- *                      M and N (tiles overhang both edges; rows past M or N read as zero).
+ *                      each, three stages); needs row-major A and K >= 64, with column-major B
+ *                      any M and N (tiles overhang both edges; rows past M or N read as zero),
+ *                      with row-major B (kept in LDS as laid out and read by gfx950's
+ *                      transposing LDS read) any M and N % 8 == 0, and element offsets into B
+ *                      below 2^30.
  *                      Conditions apply after the column-major-C swap; otherwise
  *                      GEMM_ERR_INVALID_VALUE.  AUTO picks these kernels wherever they apply and
  *                      the cost model prefers them (every workload of the benchmark suite).
@@ -239,7 +243,8 @@ gemm_status_t gemm_plan(int dtype, int64_t M, int64_t N, int64_t K, gemm_order_t
  * workgroups to occupy the device, K is also divided among workgroups -- by the small-problem
  * kernel for few rows (or few columns after the column-major-C swap), and by the direct-copy
  * kernels on 256 x 256 tiles when those leave CUs idle (FP32 inputs with M and N multiples of
- * 256; 16-bit inputs in that kernel's layout, row-major A and column-major B), where a time
+ * 256; 16-bit inputs in that kernel's layouts, row-major A with column-major B or with row-major
+ * B and N % 8 == 0), where a time
  * model prices the split below the unsplit plan (one GPU's 4096 x 512 x 4096 column shard of a
  * 4096^3 product, for one).  The slices' partial products go to the workspace (the tile kernels
  * write the first slice straight to C) and a second kernel adds them in slice order, so results
@@ -343,17 +348,17 @@ typedef struct {
 
 /* gemm_bf16_f32acc_fused / gemm_f16_f32acc_fused: C = epilogue(A.B) for bf16 or fp16 inputs,
  * FP32 products and sums.  C is `void *` (float or uint16_t per out_type); the rest as the plain
- * calls.  The epilogue runs in the 16-bit direct-copy kernel, which takes k-contiguous operands:
- * row-major A with column-major B (a PyTorch Linear: x . W^T), and K >= 64 (K == 0 gives
- * act(beta * C + bias)).  A core launch plus at most two edge strips on the same stream, all on
+ * calls.  The epilogue runs in the 16-bit direct-copy kernel: row-major A with column-major B (a
+ * PyTorch Linear: x . W^T) or with row-major B and N % 8 == 0 (x . W), and K >= 64 (K == 0
+ * gives act(beta * C + bias)).  A core launch plus at most two edge strips on the same stream, all on
  * that kernel; nothing is allocated.  An identity epilogue (alpha 1, beta 0, no bias or
  * activation, FP32 C) runs the plain kernel on the same plan.
  * gemm_f32_fused: the same for FP32 inputs on the FP32 direct-copy kernel: row-major A with
  * column-major B, K >= 32; an identity epilogue is gemm_f32.
  * Errors: as the plain calls, plus GEMM_ERR_INVALID_VALUE for a NULL epilogue, an unknown
  * activation or output type, a bias not 4-byte aligned, a C not aligned to its output element,
- * or operands the direct-copy kernels do not take (other orders, 0 < K < 64 for 16-bit inputs,
- * 0 < K < 32 for FP32 ones). */
+ * or operands the direct-copy kernels do not take (other orders, row-major B with N % 8 != 0
+ * for 16-bit inputs, 0 < K < 64 for 16-bit inputs, 0 < K < 32 for FP32 ones). */
 gemm_status_t gemm_bf16_f32acc_fused(int64_t M, int64_t N, int64_t K,
                                      const uint16_t *A, int64_t lda, gemm_order_t order_a,
                                      const uint16_t *B, int64_t ldb, gemm_order_t order_b,

@@ -224,6 +224,12 @@ KNOWN_KERNELS = {"f32_dma256x256", "f32_dma128x128", "f32_mfma128x128", "f32_mfm
     ("f32", (2054, 2048, 512), (C_, R, R), ("f32_dma128x128", 2048, 2048)),
     # column-major C: the library computes C^T (N x M)
     ("bf16", (4097, 4095, 1023), (R, C_, C_), ("bf16_dma256x256", 4095, 4096)),
+    # row-major B with N % 8 == 0 takes the direct-copy tiles (transposing LDS reads of B), also
+    # through the column-major-C swap from all column-major; N % 8 != 0 the register-staged ones
+    ("bf16", (4096, 4096, 4096), (R, R, R), ("bf16_dma256x256", 4096, 4096)),
+    ("bf16", (4096, 4096, 4096), (C_, C_, C_), ("bf16_dma256x256", 4096, 4096)),
+    ("bf16", (2048, 4096, 4096), (R, R, R), ("bf16_dma256x128", 2048, 4096)),
+    ("bf16", (4096, 4100, 4096), (R, R, R), ("bf16_mfma128x128", 4096, 4100)),
     ("f32", (64, 64, 0), (R, R, R), ("zero_c", 64, 64)),
     ("f32", (0, 64, 8), (R, R, R), ("none", 0, 0)),
 ], ids=lambda v: str(v))
@@ -245,7 +251,9 @@ def test_plan_rejects_invalid_arguments():
 def test_plan_invariants_on_random_shapes():
     """Over random shapes and orders: the core lies inside C; kernels that take any shape
     cover all of it; the FP32 direct-copy core ends on whole tiles except along the edge of a
-    k-contiguous operand (row-major A: M; column-major B: N), where its tiles may overhang."""
+    k-contiguous operand (row-major A: M; column-major B: N), where its tiles may overhang; the
+    16-bit direct-copy kernel runs on row-major A with column-major B, or row-major B and N a
+    multiple of 8."""
     import numpy as np
     rng = np.random.default_rng(2024)
     for _ in range(400):
@@ -267,7 +275,7 @@ def test_plan_invariants_on_random_shapes():
             assert rows % t == 0 or (an == R and rows == Mn), (kernel, M, N, oa, ob, oc, rows)
             assert cols % t == 0 or (bn == C_ and cols == Nn), (kernel, M, N, oa, ob, oc, cols)
         if kernel.startswith("bf16_dma"):
-            assert an == R and bn == C_
+            assert an == R and (bn == C_ or Nn % 8 == 0), (kernel, M, N, oa, ob, oc)
 
 
 @pytest.mark.parametrize("dtype,shape,orders,expected", [
@@ -373,7 +381,7 @@ def fargs(M=8, N=8, K=64, A=FAKE, lda=64, oa=R, B=FAKE, ldb=64, ob=C_, C=FAKE, l
 
 
 @pytest.mark.parametrize("bad", [
-    dict(call=dict(ob=R, ldb=8)),                 # B not k-contiguous: the kernel takes R,C only
+    dict(call=dict(N=6, ldc=6, ob=R, ldb=6)),     # row-major B needs N % 8 == 0 (FP32: R,C only)
     dict(call=dict(oa=C_, lda=8)),
     dict(call=dict(K=32, lda=32, ldb=32)),        # 0 < K < 64
     dict(call=dict(C=FAKE + 2)),                  # FP32 output needs 4-byte alignment
@@ -407,7 +415,7 @@ def test_fused_null_epilogue_rejected():
 
 
 @pytest.mark.skipif(gpu_available(), reason="checks the no-GPU path")
-@pytest.mark.parametrize("call", [dict(), dict(oc=C_), dict(K=0), dict(C=FAKE + 2, ldc=8)])
+@pytest.mark.parametrize("call", [dict(), dict(oc=C_), dict(K=0), dict(C=FAKE + 2, ldc=8), dict(ob=R, ldb=8)])
 def test_fused_valid_calls_reach_the_device_check(call):
     out = g.Out.BF16 if call.get("C") == FAKE + 2 else g.Out.F32
     assert _status(FUSED["bf16"], *fargs(**call), activation=g.Act.GELU, bias=FAKE,

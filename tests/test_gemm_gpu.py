@@ -417,7 +417,8 @@ def test_bf16_dma_closed_forms():
     assert np.array_equal(logical_c(pa, run(pa, g.Algo.MFMA_DMA)), B[:, perm])
 
 
-@pytest.mark.parametrize("bad", [dict(order_b=ROW_MAJOR), dict(order_a=COL_MAJOR),
+# (row-major B is taken when N % 8 == 0)
+@pytest.mark.parametrize("bad", [dict(order_b=ROW_MAJOR, N=260), dict(order_a=COL_MAJOR),
                                  dict(order_a=COL_MAJOR, order_b=ROW_MAJOR), dict(K=63)],
                          ids=lambda d: str(d))
 def test_bf16_dma_rejects_unsupported(bad):

@@ -157,11 +157,18 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, FM = C::FM, FN = C::FN, SUB = C::SUB;
     constexpr int ROW = C::ROW, MF = C::MF;
     __shared__ __align__(16) unsigned char smem[C::LDS];
-    if constexpr (BATCH) p.select(blockIdx.z);
     if constexpr (MODE == kSplitK) p.select(blockIdx.y, ES);
 
     int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    if constexpr (BATCH) {
+        int z;
+        batch_tile_coords(blockIdx.x, blockIdx.z, gridDim.z, tiles_m, tiles_n, group_m, z, tm, tn);
+        p.select(__builtin_amdgcn_readfirstlane(z));     // (uniform: keeps the pointers scalar)
+        tm = __builtin_amdgcn_readfirstlane(tm);
+        tn = __builtin_amdgcn_readfirstlane(tn);
+    } else {
+        tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    }
     const int m0 = tm * BM, n0 = tn * BN;
     const bool interior = m0 + BM <= p.M && n0 + BN <= p.N;
     const int lane = threadIdx.x & 63;

@@ -158,10 +158,17 @@ void k_bf16_mfma(KArg<BATCH> p, int tiles_m, int tiles_n, int group_m, int vec_a
     // the direct path issues one tile's copies in the first SUB * FM * FN instruction slots
     static_assert(T::SUB * T::FM * T::FN >= T::A_DMA + T::B_DMA, "too few slots for the copies");
     __shared__ __align__(16) unsigned char smem[T::LDS];
-    if constexpr (BATCH) p.select(blockIdx.z);
 
     int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    if constexpr (BATCH) {
+        int z;
+        batch_tile_coords(blockIdx.x, blockIdx.z, gridDim.z, tiles_m, tiles_n, group_m, z, tm, tn);
+        p.select(__builtin_amdgcn_readfirstlane(z));     // (uniform: keeps the pointers scalar)
+        tm = __builtin_amdgcn_readfirstlane(tm);
+        tn = __builtin_amdgcn_readfirstlane(tn);
+    } else {
+        tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    }
     const int m0 = tm * BM, n0 = tn * BN;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);

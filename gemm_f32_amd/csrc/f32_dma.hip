@@ -133,11 +133,18 @@ void k_f32_dma(std::conditional_t<SPLIT, SplitProblem, KArg<BATCH>> p, int tiles
     constexpr bool A_KC = C::A_KC, B_KC = C::B_KC;
     static_assert(!(BATCH && SPLIT), "a batch is not split");
     __shared__ __align__(16) unsigned char smem[S * C::STAGE];
-    if constexpr (BATCH) p.select(blockIdx.z);
     if constexpr (SPLIT) p.select(blockIdx.y, 4);
 
     int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    if constexpr (BATCH) {
+        int z;
+        batch_tile_coords(blockIdx.x, blockIdx.z, gridDim.z, tiles_m, tiles_n, group_m, z, tm, tn);
+        p.select(__builtin_amdgcn_readfirstlane(z));     // (uniform: keeps the pointers scalar)
+        tm = __builtin_amdgcn_readfirstlane(tm);
+        tn = __builtin_amdgcn_readfirstlane(tn);
+    } else {
+        tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    }
     const int m0 = tm * BM, n0 = tn * BN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -402,10 +409,17 @@ void k_f32_dma_edge(std::conditional_t<EPI, EpiProblem, KArg<BATCH>> p, int tile
     constexpr bool A_KC = C::A_KC, B_KC = C::B_KC;
     static_assert(!EPI || (A_KC && B_KC && !BATCH), "the fused epilogue takes k-contiguous operands");
     __shared__ __align__(16) unsigned char smem[S * C::STAGE];
-    if constexpr (BATCH) p.select(blockIdx.z);
 
     int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    if constexpr (BATCH) {
+        int z;
+        batch_tile_coords(blockIdx.x, blockIdx.z, gridDim.z, tiles_m, tiles_n, group_m, z, tm, tn);
+        p.select(__builtin_amdgcn_readfirstlane(z));     // (uniform: keeps the pointers scalar)
+        tm = __builtin_amdgcn_readfirstlane(tm);
+        tn = __builtin_amdgcn_readfirstlane(tn);
+    } else {
+        tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    }
     const int m0 = tm * BM, n0 = tn * BN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -97,10 +97,17 @@ void k_f32_mfma(KArg<BATCH> p, int tiles_m, int tiles_n, int group_m, int vec_a,
     using T = F32Tile<BM, BN, BK, WGM, WGN, PAD>;
     __shared__ __align__(16) float As[2][BK * T::PA];
     __shared__ __align__(16) float Bs[2][BK * T::PB];
-    if constexpr (BATCH) p.select(blockIdx.z);
 
     int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    if constexpr (BATCH) {
+        int z;
+        batch_tile_coords(blockIdx.x, blockIdx.z, gridDim.z, tiles_m, tiles_n, group_m, z, tm, tn);
+        p.select(__builtin_amdgcn_readfirstlane(z));     // (uniform: keeps the pointers scalar)
+        tm = __builtin_amdgcn_readfirstlane(tm);
+        tn = __builtin_amdgcn_readfirstlane(tn);
+    } else {
+        tile_coords(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    }
     const int m0 = tm * BM, n0 = tn * BN;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = (wave / WGN) * T::WM, wn = (wave % WGN) * T::WN;

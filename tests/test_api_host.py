@@ -181,6 +181,30 @@ int main() {
         gemm::tile_coords(w, 3, 5, 0, a, b);
         if (a != w / 5 || b != w % 5) { printf("plain order %d\n", w); return 1; }
     }
+    // strided batches: a bijection onto (entry, tile) for several tile grids (below and above 16
+    // tiles per entry), entry counts and
+    // group heights
+    const int bshapes[][3] = {{8, 1, 32}, {8, 8, 32}, {3, 5, 7}, {1, 1, 9}, {16, 16, 3}, {5, 2, 17}};
+    for (const auto& sh : bshapes)
+        for (int gm : {0, 1, 2, 4}) {
+            const int tm_ = sh[0], tn_ = sh[1], nz = sh[2];
+            std::vector<int> seen(tm_ * tn_ * nz, 0);
+            for (int z = 0; z < nz; ++z)
+                for (int x = 0; x < tm_ * tn_; ++x) {
+                    int e, a, b;
+                    gemm::batch_tile_coords(x, z, nz, tm_, tn_, gm, e, a, b);
+                    if (e < 0 || e >= nz || a < 0 || a >= tm_ || b < 0 || b >= tn_) { printf("batch range\n"); return 1; }
+                    if (seen[(e * tm_ + a) * tn_ + b]++) { printf("batch dup %d %d %d\n", tm_, tn_, nz); return 1; }
+                }
+        }
+    // attention P.V: 8 tiles per entry, 32 entries; the workgroups of XCD x (dispatch ids
+    // x, x + 8, ...) take entries 4x .. 4x+3 whole
+    for (int x = 0; x < 8; ++x)
+        for (int w = x; w < 256; w += 8) {
+            int e, a, b;
+            gemm::batch_tile_coords(w % 8, w / 8, 32, 8, 1, 8, e, a, b);
+            if (e / 4 != x) { printf("batch xcd %d entry %d\n", x, e); return 1; }
+        }
     printf("ok\n");
     return 0;
 }

@@ -1,5 +1,5 @@
-"""The direct-copy kernels' k-loops, as compiled for gfx950, wait for copies only where the source
-says so.
+"""The direct-copy kernels, as compiled for gfx950: their k-loops wait for copies only where the
+source says so, and their buffer resources stay in scalar registers.
 
 Each k-loop orders its global->LDS copies with explicit waits (`s_waitcnt vmcnt(N)` in inline
 assembly, N the copies allowed in flight) before a plain barrier.  The compiler adds its own
@@ -87,3 +87,25 @@ def test_k_loops_have_no_compiler_full_waits(src, pattern, tmp_path):
         assert _compiler_full_waits(loop) == 0, name
         checked += 1
     assert checked >= 8, f"only {checked} k-loops found in {src}"
+
+
+def _waterfall_loops(body: str) -> int:
+    """Loops that step through the lanes' values of a buffer resource: read one lane's resource,
+    run the load for the lanes holding the same value, repeat.  The compiler emits them around a
+    buffer load whose resource it cannot prove uniform (a strided batch's entry once came out of a
+    64-bit division that way), and they serialise every copy."""
+    n = 0
+    for loop in _loop_bodies(body):
+        text = "\n".join(loop)
+        if "v_readfirstlane" in text and "s_and_saveexec" in text and "buffer_load" in text:
+            n += 1
+    return n
+
+
+@pytest.mark.parametrize("src,pattern", [("bf16_dma.hip", "k_bf16_dma"), ("f32_dma.hip", "k_f32_dma")])
+def test_buffer_resources_stay_uniform(src, pattern, tmp_path):
+    asm = _assembly(src, tmp_path)
+    kernels = list(_kernels(asm, pattern))
+    assert len(kernels) >= 8
+    for name, body in kernels:
+        assert _waterfall_loops(body) == 0, name

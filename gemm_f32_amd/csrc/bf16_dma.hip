@@ -675,13 +675,33 @@ void k_bf16_dma(typename ModeArgT<MODE>::type p, int tiles_m, int tiles_n, int g
                         if (col + e < p.N) epi_store(p.e, p.C, off + e, y[e]);
                 }
             }
+        } else if constexpr (!VEC_C) {
+            // C rows not 16-byte aligned: 4-byte stores with lane l on column 64 c + l of a band
+            // row, so that each store instruction writes 256 contiguous bytes (four stores per lane
+            // on its own four columns wrote 16-byte-strided pieces: at 4095 x 4097 x 1023 the
+            // kernel took 64 us against about 38 for 16-byte rows)
+            static_assert(C::WN % 64 == 0, "whole 64-column chunks per band row");
+            const int rb = m0 + wm + 32 * i;
+#pragma unroll
+            for (int r = 0; r < 32; ++r) {
+#pragma unroll
+                for (int c = 0; c < C::WN / 64; ++c) {
+                    const int row = rb + r, cx = n0 + wn + 64 * c + lane_e;
+                    const float v = band[r * C::EP + 64 * c + lane_e];
+                    if (row < p.M && cx < p.N) {
+                        float* dst = p.C + (int64_t)row * p.ldc + cx;
+                        if constexpr (BATCH) __builtin_nontemporal_store(v, dst);
+                        else *dst = v;
+                    }
+                }
+            }
         } else {
 #pragma unroll
             for (int q = 0; q < Q; ++q) {
                 const int rr = q * RPI + lane_e / LPR, row = row0 + q * RPI;
                 const f32x4 v = *reinterpret_cast<const f32x4*>(band + rr * C::EP + cc);
                 const int64_t off = (int64_t)row * p.ldc + col;
-                if (VEC_C && (interior || (row < p.M && col + 3 < p.N))) {
+                if (interior || (row < p.M && col + 3 < p.N)) {
                     // a batch streams C once (attention's scores): non-temporal stores keep it from
                     // displacing the operands in the caches
                     if constexpr (BATCH) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p.C + off));

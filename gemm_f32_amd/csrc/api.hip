@@ -415,14 +415,16 @@ Plan choose_bf16_tiles(const Problem& p, gemm_algo_t algo, int cus) {
 // workspace and a second pass adds them to C.  S and the choice against the unsplit kernels come
 // from a time model fitted to measurements (rocprofv3 and HIP events, interleaved with the FP32
 // 4096^3 GEMM as the benchmark runs): per 64-deep k-tile and round, 1.5 us at 256 x 256 and
-// 0.87 us at 256 x 128 with every CU busy, times 0.75 + 0.25 u when only a fraction u of the
+// 1.0 us at 256 x 128 (0.65 of the 256 x 256 figure, as measured standalone: FFN-down 2048 x 4096
+// x 11008 against 4096^3) with every CU busy, times 0.75 + 0.25 u when only a fraction u of the
 // CUs holds a tile (the clock the power limit allows rises); 2 us per launch; C (or the slabs)
 // written at 5 TB/s; the slab pass 3 us plus (S+1) M N floats at 6 TB/s.  Measured against that:
 // 4096 x 512 x 4096, 4 slices 40.1 us (8: 45.7, unsplit 55.3); 2048 x 2048 x 8192, 4 slices
 // 78.4 us (unsplit 105.6); 1024 x 1024 x 8192, 8 slices 40.6 us (unsplit 88.8); no split where the
-// tiles fill the chip or K is short (2048 x 4096 x 4096: 2 slices 79.8 us, unsplit 67.0).
+// tiles fill the chip or K is short (2048 x 4096 x 4096: 2 slices 79.8 us, unsplit 67.0); FFN-down
+// 2048 x 4096 x 11008, 2 slices 176-180 us (unsplit 256 x 128: 185-190).
 constexpr int kMinSliceK = 512;
-constexpr double kTau256 = 1.5e-6, kTau128 = 0.87e-6, kLaunchSec = 2e-6, kWriteBps = 5e12, kSumSec = 3e-6,
+constexpr double kTau256 = 1.5e-6, kTau128 = 1.0e-6, kLaunchSec = 2e-6, kWriteBps = 5e12, kSumSec = 3e-6,
                  kSumBps = 6e12;
 
 double occupancy_factor(int64_t units, int cus) {

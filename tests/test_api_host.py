@@ -314,13 +314,14 @@ def test_plan_invariants_on_random_shapes():
     # column-major C: C^T has the few rows
     ("f32", (1024, 16, 16384), (C_, C_, C_), 16 * 16 * 1024 * 4),
     # 16-bit inputs on 256 x 256 tiles that leave CUs idle: one GPU's column shard of 4096^3 in
-    # 5 K slices, 2048^2 x 8192 in 4 (slices 1 .. S-1 as M x N FP32 slabs); none where the
+    # 5 K slices, 2048^2 x 8192 in 4 (slices 1 .. S-1 as M x N FP32 slabs), FFN-down 2048 x 4096
+    # x 11008 in 2 (128 tiles of 256^2 against one round of 256 x 128 tiles); none where the
     # tiles fill the chip or where the unsplit 256 x 128 kernel is estimated as fast
     ("bf16", (4096, 512, 4096), (R, C_, R), 4 * 4096 * 512 * 4),
     ("bf16", (2048, 2048, 8192), (R, C_, R), 3 * 2048 * 2048 * 4),
     ("bf16", (4096, 4096, 4096), (R, C_, R), 0),
     ("bf16", (2048, 4096, 4096), (R, C_, R), 0),
-    ("bf16", (2048, 4096, 11008), (R, C_, R), 0),
+    ("bf16", (2048, 4096, 11008), (R, C_, R), 1 * 2048 * 4096 * 4),
     # FP32: whole 256 x 256 tiles split into one round's worth of slices of at least 512 where the
     # time model prices that below the default plan: the shard's 32 tiles in 8 slices, 2048^2 in 4;
     # not 4096 x 768 x 2048 (short slices), not ragged M, not tiles that fill the chip

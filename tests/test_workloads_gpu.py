@@ -36,7 +36,11 @@ def test_workload_full_size_sampled(name):
     assert err <= TOL[p.dtype]
 
 
-@pytest.mark.parametrize("name", [n for n, w in gi.WORKLOADS.items() if n.startswith("fewcols")])
+# the workloads whose default plan splits K when given a workspace
+WS_WORKLOADS = [n for n in gi.WORKLOADS if n.startswith(("fewcols", "shard"))] + ["llm_ffn_down_2048x4096x11008"]
+
+
+@pytest.mark.parametrize("name", WS_WORKLOADS)
 def test_workload_full_size_sampled_with_workspace(name):
     """The workspace entry point (split-K across workgroups) at the workload's full size."""
     import torch

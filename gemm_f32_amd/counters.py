@@ -1,6 +1,6 @@
 """Hardware-counter evidence for libgemm's kernels: rocprofv3 passes over bench.py and their summary.
 
-    python -m gemm_f32_amd.counters collect --workload W --out DIR [--tile-order rowmajor]
+    python -m gemm_f32_amd.counters collect --workload W --out DIR [--tile-order rowmajor] [--algo A]
     python -m gemm_f32_amd.counters calibrate --out DIR
     python -m gemm_f32_amd.counters summarize --calib DIR DIR... [--traffic-json profiles/traffic.json]
 
@@ -57,8 +57,9 @@ def collect(args) -> None:
              "--tile-order", args.tile_order]
     if args.algo:
         bench += ["--algo", args.algo]
+    stem = f"{args.workload}@{args.tile_order}" + (f"~{args.algo}" if args.algo else "")
     for tag, ctr in PASSES.items():
-        _run_pass(f"{args.workload}@{args.tile_order}_{tag}", ctr, bench, args.out)
+        _run_pass(f"{stem}_{tag}", ctr, bench, args.out)
 
 
 def calibrate(args) -> None:
@@ -111,7 +112,7 @@ def summarize(args) -> None:
         if not tagged.endswith("_A"):
             continue
         stem = tagged[:-2]
-        workload, order = stem.split("@")
+        workload, order = stem.split("@")          # order[~algo]: an explicitly chosen algorithm
         w = gi.WORKLOADS[workload]
         e = 4 if w.dtype == "f32" else 1 if w.dtype in gi.FP8_DTYPES else 2
         compulsory = w.batch * (e * (w.M * w.K + w.K * w.N) + 4 * w.M * w.N)
@@ -122,7 +123,7 @@ def summarize(args) -> None:
             fetch, write = _mean(b.get("FETCH_SIZE", [])), _mean(c.get("WRITE_SIZE", []))
             hit, miss = _mean(b.get("TCC_HIT_sum", [])), _mean(c.get("TCC_MISS_sum", []))
             hbm = fetch * 1024 * calib["FETCH_SIZE"] + write * 1024 * calib["WRITE_SIZE"]
-            print(f"| {workload} | {order} | `{_short(k)}` | {_mean(a.get('MfmaUtil', [])):.1f} | "
+            print(f"| {workload} | {order.replace('~', ', algo ')} | `{_short(k)}` | {_mean(a.get('MfmaUtil', [])):.1f} | "
                   f"{_mean(a.get('VALUBusy', [])):.1f} | {_mean(a.get('LDSBankConflict', [])):.2f} | "
                   f"{100 * hit / (hit + miss):.1f} | {fetch:.0f} | {write:.0f} | {hbm:.4e} | {compulsory:.4e} | "
                   f"{hbm / compulsory:.3f} |")

@@ -76,7 +76,9 @@ __device__ __forceinline__ s16x4 lds_read_tr16(lds_s16x4* __restrict__ p) {
 }
 
 // the lane's index within its wavefront
-__device__ __forceinline__ int lane_id() { return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+__device__ __forceinline__ int lane_id() {
+    return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & 63;     // (the mask: a known range)
+}
 
 // chunk c of LDS row r is stored at c ^ swz(r): any 16 consecutive rows read at one
 // logical chunk hit 16 distinct 16-byte bank groups

@@ -45,6 +45,10 @@ SPECS = [
     ("square4096_bf16@MFMA_256x128", ["--workload", "square4096_bf16", "--algo", "MFMA_256x128"], 30),
     ("square4096_bf16@MFMA_128x128", ["--workload", "square4096_bf16", "--algo", "MFMA_128x128"], 30),
     ("square4096_f16", ["--workload", "square4096_f16"], 30),
+    # both operands row-major (B n-contiguous): the direct-copy kernel's transposing-read build,
+    # and the register-staged kernel this layout took before it
+    ("square4096_bf16_rr", ["--workload", "square4096_bf16_rr"], 30),
+    ("square4096_bf16_rr@MFMA_128x128", ["--workload", "square4096_bf16_rr", "--algo", "MFMA_128x128"], 30),
     ("square4096_e4m3", ["--workload", "square4096_e4m3"], 30),
     ("square4096_e5m2", ["--workload", "square4096_e5m2"], 30),
     # the same 4096 x 4096 outputs over K: fixed cost (launch, first loads, the 64 MB C write)
@@ -84,6 +88,9 @@ SPECS = [
     ("llm_ffn_down_2048x4096x11008@ws", ["--workload", "llm_ffn_down_2048x4096x11008", "--workspace"], 30),
     ("attn_scores_32x2048x2048x128_bf16", ["--workload", "attn_scores_32x2048x2048x128_bf16"], 30),
     ("attn_pv_32x2048x128x2048_bf16", ["--workload", "attn_pv_32x2048x128x2048_bf16"], 30),
+    # the tile scheduler's remaps off (entries' tiles spread over the XCDs in dispatch order)
+    ("attn_pv_32x2048x128x2048_bf16@rowmajor",
+     ["--workload", "attn_pv_32x2048x128x2048_bf16", "--tile-order", "rowmajor"], 30),
 ]
 
 

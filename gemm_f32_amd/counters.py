@@ -10,12 +10,18 @@ limits of the counter blocks):
   A  MfmaUtil, VALUBusy, LDSBankConflict (rocprofv3's derived percentages) and the raw SQ_INSTS_MFMA,
      SQ_INSTS_VALU, SQ_INSTS_LDS, SQ_WAVES, SQ_BUSY_CU_CYCLES;
   B  FETCH_SIZE (KiB the L2s fetched from the fabric: last-level cache or HBM) and TCC_HIT_sum;
-  C  WRITE_SIZE (KiB written) with TCC_MISS_sum and TCC_REQ_sum.
+  C  WRITE_SIZE (KiB written) with TCC_MISS_sum and TCC_REQ_sum;
+  D  GRBM_GUI_ACTIVE (GPU cycles, summed over the XCDs) with the matrix-core busy cycles and the waves'
+     resident and waiting cycles, in a run that also traces each dispatch's start and end (--kernel-trace):
+     cycles over duration give the shader clock the kernel actually ran at, and matrix-busy cycles over
+     GPU cycles the fraction of the matrix-core peak at that clock.
 `calibrate` runs passes B and C over bench.py's plain 256 MiB device copy, whose bytes are known:
 FETCH_SIZE and WRITE_SIZE of a kernel are scaled by (bytes copied) / (what the copy's counters read).
 `summarize` averages every library kernel's counters over its dispatches and prints one markdown row
 per kernel: matrix-core and vector-ALU busy, LDS bank-conflict stalls, L2 hit rate, HBM bytes per
-launch (scaled) against the compulsory bytes of the workload.
+launch (scaled) against the compulsory bytes of the workload; and, where pass D was collected, a second
+table of clock and cycles per kernel.  `--workload default` profiles bench.py's default step (the FP32
+and the BF16 4096^3 GEMM, interleaved).
 
 This is measurement tooling: it runs rocprofv3 and bench.py as child processes and reads CSV files;
 nothing here is on the GEMM path.
@@ -38,13 +44,18 @@ PASSES = {
           "SQ_WAVES", "SQ_BUSY_CU_CYCLES"],
     "B": ["FETCH_SIZE", "TCC_HIT_sum"],
     "C": ["WRITE_SIZE", "TCC_MISS_sum", "TCC_REQ_sum"],
+    "D": ["GRBM_GUI_ACTIVE", "GRBM_COUNT", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_WAVE_CYCLES",
+          "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_LDS"],
 }
+# passes that also record each dispatch's start and end
+TRACED = {"D"}
 COPY_BYTES = 256 * 1024 * 1024        # bench.py --copy-calibration: one 256 MiB device copy
 
 
 def _run_pass(tag: str, counters: list, bench_args: list, out: str) -> None:
     d = os.path.join(out, tag)
-    cmd = ["timeout", "-s", "KILL", "120", "rocprofv3", "--pmc", *counters, "--output-format", "csv",
+    trace = ["--kernel-trace"] if tag.rsplit("_", 1)[-1] in TRACED else []
+    cmd = ["timeout", "-s", "KILL", "120", "rocprofv3", *trace, "--pmc", *counters, "--output-format", "csv",
            "-d", d, "-o", "run", "--", sys.executable, os.path.join(ROOT, "bench.py"), *bench_args]
     print("+", " ".join(cmd), flush=True)
     r = subprocess.run(cmd)
@@ -53,13 +64,13 @@ def _run_pass(tag: str, counters: list, bench_args: list, out: str) -> None:
 
 
 def collect(args) -> None:
-    bench = ["--workload", args.workload, "--steps", "3", "--warmup", "1", "--no-cpu-baseline",
-             "--tile-order", args.tile_order]
+    bench = (["--workload", args.workload] if args.workload != "default" else []) + [
+        "--steps", "3", "--warmup", "1", "--no-cpu-baseline", "--tile-order", args.tile_order]
     if args.algo:
         bench += ["--algo", args.algo]
     stem = f"{args.workload}@{args.tile_order}" + (f"~{args.algo}" if args.algo else "")
-    for tag, ctr in PASSES.items():
-        _run_pass(f"{stem}_{tag}", ctr, bench, args.out)
+    for tag in args.passes:
+        _run_pass(f"{stem}_{tag}", PASSES[tag], bench, args.out)
 
 
 def calibrate(args) -> None:
@@ -75,6 +86,60 @@ def _read(dir_: str) -> dict:
             for row in csv.DictReader(fh):
                 vals[row["Kernel_Name"]][row["Counter_Name"]][row["Dispatch_Id"]] = float(row["Counter_Value"])
     return {k: {c: list(d.values()) for c, d in v.items()} for k, v in vals.items()}
+
+
+def _read_dispatches(dir_: str) -> dict:
+    """{kernel name: [(counters of one dispatch, duration ns, waves)]} from a traced counter run."""
+    durs = {}
+    for f in glob.glob(os.path.join(dir_, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                durs[row["Dispatch_Id"]] = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+    disp: dict = defaultdict(dict)
+    for f in glob.glob(os.path.join(dir_, "**", "*counter_collection.csv"), recursive=True):
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                d = disp[(row["Kernel_Name"], row["Dispatch_Id"])]
+                d[row["Counter_Name"]] = float(row["Counter_Value"])
+                d["_waves"] = int(row["Grid_Size"]) // 64
+    out: dict = defaultdict(list)
+    for (k, did), c in disp.items():
+        if did in durs:
+            out[k].append((c, durs[did], c.pop("_waves")))
+    return out
+
+
+def _agent(dir_: str) -> dict:
+    for f in glob.glob(os.path.join(dir_, "**", "*agent_info.csv"), recursive=True):
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Name", "").startswith("gfx"):
+                    return {"xcc": int(row["Num_Xcc"]), "simds": int(row["Simd_Count"]),
+                            "mhz": float(row["Max_Engine_Clk_Fcompute"])}
+    return {"xcc": 8, "simds": 1024, "mhz": 2400.0}
+
+
+def clock_table(dirs: list) -> None:
+    """Pass D: the shader clock each kernel ran at and its matrix-core busy fraction at that clock."""
+    print("\n| workload | kernel | dispatches | kernel µs | GPU cycles (per XCD) | shader clock GHz | "
+          "matrix busy % of GPU cycles (= % of the matrix peak at that clock) | peak at that clock / nominal | "
+          "waves resident % of GPU cycles | wave cycles waiting % |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for d in dirs:
+        stem = os.path.basename(os.path.normpath(d))[:-2]
+        workload = stem.split("@")[0]
+        ag = _agent(d)
+        for k, rows in sorted(_read_dispatches(d).items()):
+            if not _library_kernel(k):
+                continue
+            cyc = _mean([c["GRBM_GUI_ACTIVE"] / ag["xcc"] for c, _, _ in rows])
+            dur = _mean([t for _, t, _ in rows])
+            clk = _mean([c["GRBM_GUI_ACTIVE"] / ag["xcc"] / t for c, t, _ in rows])
+            busy = _mean([c["SQ_VALU_MFMA_BUSY_CYCLES"] / ag["simds"] / (c["GRBM_GUI_ACTIVE"] / ag["xcc"]) for c, _, _ in rows])
+            life = _mean([4 * c["SQ_WAVE_CYCLES"] / w / (c["GRBM_GUI_ACTIVE"] / ag["xcc"]) for c, _, w in rows])
+            wait = _mean([c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"] for c, _, _ in rows])
+            print(f"| {workload} | `{_short(k)}` | {len(rows)} | {dur / 1e3:.1f} | {cyc:.0f} | {clk:.3f} | {100 * busy:.1f} | "
+                  f"{clk * 1e3 / ag['mhz']:.3f} | {100 * life:.1f} | {100 * wait:.1f} |")
 
 
 def _mean(x):
@@ -113,7 +178,9 @@ def summarize(args) -> None:
             continue
         stem = tagged[:-2]
         workload, order = stem.split("@")          # order[~algo]: an explicitly chosen algorithm
-        w = gi.WORKLOADS[workload]
+        w = gi.WORKLOADS.get(workload)
+        if w is None:                              # the default step: two workloads, clock table only
+            continue
         e = 4 if w.dtype == "f32" else 1 if w.dtype in gi.FP8_DTYPES else 2
         compulsory = w.batch * (e * (w.M * w.K + w.K * w.N) + 4 * w.M * w.N)
         parts = {t: _read(os.path.join(os.path.dirname(os.path.normpath(base)), f"{stem}_{t}")) for t in "ABC"}
@@ -130,6 +197,11 @@ def summarize(args) -> None:
             traffic[(workload, order, k)] = (fetch, write, hbm, compulsory)
     if args.traffic_json:
         _update_traffic(args.traffic_json, traffic, calib)
+    clocks = [os.path.join(os.path.dirname(os.path.normpath(b)), os.path.basename(os.path.normpath(b))[:-2] + "_D")
+              for b in args.dirs if os.path.basename(os.path.normpath(b))[-2:] in ("_A", "_D")]
+    clocks = [d for d in clocks if os.path.isdir(d)]
+    if clocks:
+        clock_table(clocks)
 
 
 def _update_traffic(path: str, traffic: dict, calib: dict) -> None:
@@ -170,12 +242,13 @@ def main() -> None:
     c.add_argument("--algo", default=None)
     c.add_argument("--tile-order", default="swizzled", choices=["swizzled", "rowmajor"])
     c.add_argument("--out", required=True)
+    c.add_argument("--passes", default="ABCD", help="counter passes to run (letters of A, B, C, D)")
     k = sub.add_parser("calibrate")
     k.add_argument("--out", required=True)
     s = sub.add_parser("summarize")
     s.add_argument("--calib", required=True)
     s.add_argument("--traffic-json", default=None)
-    s.add_argument("dirs", nargs="+", help="the pass-A directories (…/<workload>@<order>_A)")
+    s.add_argument("dirs", nargs="+", help="the pass-A (or pass-D) directories (…/<workload>@<order>_A)")
     args = ap.parse_args()
     {"collect": collect, "calibrate": calibrate, "summarize": summarize}[args.cmd](args)
 

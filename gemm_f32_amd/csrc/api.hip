@@ -131,6 +131,19 @@ bool prefer_small(const Problem& p, int cus) {
     return p.M <= kSkinnyMaxM || t64 * 2 < c || (tiles(p.M, p.N, 128, 128) < c && t64 <= c);
 }
 
+// 16-bit inputs: where the small-problem kernel would run for lack of tiles, the register-staged
+// kernel's 64 x 64 tiles run faster whenever they occupy between half and all of the CUs in one
+// round and K is at most 2048 (rocprofv3 kernel times, BF16, small-problem -> 64 x 64 tiles: 1000^3
+// 14.7 -> 12.3 us, 768^3 19.3 -> 6.7, 1024^3 15.0 -> 8.2, 800 x 1200 x 1000 44.2 -> 12.4, 1024 x 1024
+// x 2048 22.5 -> 13.1, 512 x 2048 x 1024 15.1 -> 8.1, 2048 x 512 x 2048 22.8 -> 13.2); at K = 4000 the
+// small-problem kernel's K split over eight wavefronts keeps the lead (1000 x 1000 x 4000: 29.4
+// against 37.2 us).  Few rows (M <= 64) and fewer tiles than half the CUs stay with it.
+constexpr int64_t kSmallTileMaxK = 2048;
+bool small_tiles16(const Problem& p, int cus) {
+    const int64_t c = cus > 0 ? cus : 256, t64 = tiles(p.M, p.N, 64, 64);
+    return p.M > kSkinnyMaxM && 2 * t64 >= c && t64 <= c && p.K <= kSmallTileMaxK;
+}
+
 // Kernel names as gemm_last_kernel() reports them: the input type, then the kernel.
 const char* skinny_name(int et, int fn) {
     static const char* names[3][2] = {{"f32_skinny16", "f32_skinny64"}, {"bf16_skinny16", "bf16_skinny64"},
@@ -566,8 +579,10 @@ hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, int 
                 return run_f32_tiles(p, stream, algo, dev, name, st, b, ws);
         }
     }
-    if (algo == GEMM_ALGO_SKINNY ||
-        (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus) && skinny_applies(p, true))) {
+    const bool small = algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus) && skinny_applies(p, true);
+    if (small && b.n == 1 && small_tiles16(p, dev.cus))
+        return run_b16_tiles(p, stream, GEMM_ALGO_MFMA_64x64, et, dev, name, st, b);
+    if (algo == GEMM_ALGO_SKINNY || small) {
         if (!skinny_applies(p, true)) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
         return run_skinny(p, l, et, dev.cus, name, algo == GEMM_ALGO_AUTO ? ws : Workspace{});
     }
@@ -587,6 +602,7 @@ Problem query_problem(int64_t M, int64_t N, int64_t K, int oa, int ob, int oc) {
 size_t split_bytes(const Problem& p, int et, int cus) {
     if (p.M == 0 || p.N == 0 || p.K == 0 || et == kElemFp8) return 0;
     if (prefer_small(p, cus) && skinny_applies(p, et != kElemF32)) {
+        if (et != kElemF32 && small_tiles16(p, cus)) return 0;
         const SkinnySplit sp = skinny_split(p, et != kElemF32, cus);
         return sp.slices > 1 ? sp.bytes : 0;
     }
@@ -615,8 +631,10 @@ const char* plan_auto(const Problem& p, int et, int cus, int& mc, int& nc) {
     mc = p.M;
     nc = p.N;
     if (et == kElemFp8) return fp8_name(plan_fp8(p, cus).opt);
-    if (prefer_small(p, cus) && skinny_applies(p, !f32)) return skinny_name(et, skinny_blocks(p, cus));
-    const Plan pl = f32 ? choose_f32_tiles(p, GEMM_ALGO_AUTO, cus) : choose_bf16_tiles(p, GEMM_ALGO_AUTO, cus);
+    const bool small = prefer_small(p, cus) && skinny_applies(p, !f32);
+    if (small && (f32 || !small_tiles16(p, cus))) return skinny_name(et, skinny_blocks(p, cus));
+    const Plan pl = f32 ? choose_f32_tiles(p, GEMM_ALGO_AUTO, cus)
+                        : choose_bf16_tiles(p, small ? GEMM_ALGO_MFMA_64x64 : GEMM_ALGO_AUTO, cus);
     mc = pl.mc;
     nc = pl.nc;
     return f32 ? f32_name(pl.opt) : b16_name(pl.opt, et);

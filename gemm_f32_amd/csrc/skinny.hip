@@ -65,8 +65,13 @@ struct In16 {
     using Elem = u16;
     using Frag = uint4;
     static constexpr int KSTEP = 32, KL = 8;        // k per step, k per lane
+    // fast: the caller knows the lane's 8 elements lie inside K.  Otherwise each lane decides:
+    // 16 bytes when its elements lie inside K, zero past K, element by element for the one
+    // chunk that straddles K (a whole checked batch read element-wise doubled the time of a
+    // 4095 x 1 x 1023 product, whose last batch straddles K).
     __device__ static Frag load(const u16* row, int k, int K, bool fast) {
-        if (fast) return load16(row + k);
+        if (fast || k + 8 <= K) return load16(row + k);
+        if (k >= K) return make_uint4(0u, 0u, 0u, 0u);
         u16 v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = (k + e < K) ? row[k + e] : (u16)0;
@@ -86,7 +91,8 @@ struct F32 {
     using Frag = float4;
     static constexpr int KSTEP = 16, KL = 4;
     __device__ static Frag load(const float* row, int k, int K, bool fast) {
-        if (fast) return load16f(row + k);
+        if (fast || k + 4 <= K) return load16f(row + k);
+        if (k >= K) return make_float4(0.f, 0.f, 0.f, 0.f);
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (k + e < K) ? row[k + e] : 0.f;

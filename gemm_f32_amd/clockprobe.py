@@ -22,6 +22,8 @@ prints per leg, as medians over wavefronts and launches:
   * the epilogue (end of k-loop -> stores issued) in cycles and microseconds;
   * the spread of the wavefronts' start and end times over the launch.
 
+With --fp8 the step also runs the E4M3 4096^3 GEMM (same direct-copy kernel, 8-bit build).
+
 This is measurement tooling; the library itself is not changed by it.
 """
 from __future__ import annotations
@@ -62,7 +64,8 @@ def _replace_once(text: str, old: str, new: str, what: str) -> str:
 
 
 def instrument_bf16(text: str) -> str:
-    """bf16_dma.hip with timestamps in the plain 16-bit ring kernel (1024 wavefronts at 4096^2)."""
+    """bf16_dma.hip with timestamps in the plain ring kernel, 16- or 8-bit inputs (1024 wavefronts
+    at 4096^2; the two builds never run at the same time, so they share the array)."""
     t = _replace_once(text, "namespace gemm {\nnamespace {\n",
                       _ARRAY.format(tag="bf16", n=1024) + "namespace gemm {\nnamespace {\n", "namespace")
     t = _replace_once(t, "    __shared__ __align__(16) unsigned char smem[C::LDS];\n",
@@ -70,7 +73,7 @@ def instrument_bf16(text: str) -> str:
     t = _replace_once(t, "    // ---- epilogue: stores past M or N are skipped ----\n",
                       "    " + _stamp("P1") + "    // ---- epilogue: stores past M or N are skipped ----\n", "k-loop end")
     t = _replace_once(t, "\n}\n\n// One launch of configuration C",
-                      "\n" + _record("bf16", 1024, "MODE == kPlain && C::RING && C::ES == 2", "C::NW")
+                      "\n" + _record("bf16", 1024, "MODE == kPlain && C::RING", "C::NW")
                       + "}\n\n// One launch of configuration C", "kernel end")
     return t + ('\nextern "C" int gemm_probe_read_bf16(void* dst) {\n'
                 '    return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(g_clk_bf16), sizeof(g_clk_bf16));\n}\n')
@@ -119,7 +122,7 @@ def build() -> str:
     return LIB
 
 
-def run(reps: int) -> None:
+def run(reps: int, fp8: bool = False) -> None:
     import ctypes
 
     import numpy as np
@@ -135,7 +138,9 @@ def run(reps: int) -> None:
     lib.gemm_probe_read_bf16.argtypes = [vp]
     lib.gemm_probe_read_f32.argtypes = [vp]
     lib.gemm_last_kernel.restype = ctypes.c_char_p
+    lib.gemm_fp8_f32acc.argtypes = [i64, i64, i64, vp, i64, ci, ci, vp, i64, ci, ci, vp, i64, ci, vp]
     n = 4096
+    fp8_sets = 17 if fp8 else 0          # more than 512 MB of 8-bit operands
     gen = torch.Generator(device="cuda").manual_seed(0)
     # inputs rotate over 5 (FP32) and 9 (BF16) independently drawn sets, as in bench.py, so that
     # operands come from HBM rather than the last-level cache
@@ -144,6 +149,12 @@ def run(reps: int) -> None:
     ba = [(torch.rand(n * n, device="cuda", generator=gen) * 2 - 1).to(torch.bfloat16).view(torch.int16) for _ in range(9)]
     bb = [(torch.rand(n * n, device="cuda", generator=gen) * 2 - 1).to(torch.bfloat16).view(torch.int16) for _ in range(9)]
     c = torch.empty(n * n, device="cuda")
+    # E4M3 operands: uniform [-1, 1] rounded by torch's conversion (the timing does not depend on
+    # the rounding)
+    qa = [(torch.rand(n * n, device="cuda", generator=gen) * 2 - 1).to(torch.float8_e4m3fn).view(torch.uint8)
+          for _ in range(fp8_sets)]
+    qb = [(torch.rand(n * n, device="cuda", generator=gen) * 2 - 1).to(torch.float8_e4m3fn).view(torch.uint8)
+          for _ in range(fp8_sets)]
     st = torch.cuda.current_stream().cuda_stream
     legs = {
         "square4096_f32": (lambda s: lib.gemm_f32_algo(0, n, n, n, fa[s % 5].data_ptr(), n, 0, fb[s % 5].data_ptr(), n, 0,
@@ -153,6 +164,12 @@ def run(reps: int) -> None:
                                                                 n, 1, c.data_ptr(), n, 0, st),
                             lib.gemm_probe_read_bf16, 1024, 64, 64 * 32),
     }
+    if fp8_sets:
+        # 8-bit: a k-tile is 128 deep, 2 k-steps of 16 v_mfma_scale_f32_32x32x64_f8f6f4 of 64 cycles
+        legs["square4096_e4m3"] = (
+            lambda s: lib.gemm_fp8_f32acc(n, n, n, qa[s % fp8_sets].data_ptr(), n, 0, 0, qb[s % fp8_sets].data_ptr(), n,
+                                          1, 0, c.data_ptr(), n, 0, st),
+            lib.gemm_probe_read_bf16, 1024, 128, 32 * 64)
     stats = {k: [] for k in legs}
     kernels = {}
     warm = 3
@@ -196,12 +213,13 @@ def main() -> None:
     sub.add_parser("build")
     r = sub.add_parser("run")
     r.add_argument("--reps", type=int, default=20)
+    r.add_argument("--fp8", action="store_true", help="also the E4M3 4096^3 GEMM (gemm_fp8_f32acc)")
     a = ap.parse_args()
     if a.cmd == "build":
         print(build())
     else:
         sys.path.insert(0, ROOT)
-        run(a.reps)
+        run(a.reps, a.fp8)
 
 
 if __name__ == "__main__":

@@ -131,17 +131,17 @@ bool prefer_small(const Problem& p, int cus) {
     return p.M <= kSkinnyMaxM || t64 * 2 < c || (tiles(p.M, p.N, 128, 128) < c && t64 <= c);
 }
 
-// 16-bit inputs: where the small-problem kernel would run for lack of tiles, the register-staged
-// kernel's 64 x 64 tiles run faster whenever they occupy between half and all of the CUs in one
-// round and K is at most 2048 (rocprofv3 kernel times, BF16, small-problem -> 64 x 64 tiles: 1000^3
-// 14.7 -> 12.3 us, 768^3 19.3 -> 6.7, 1024^3 15.0 -> 8.2, 800 x 1200 x 1000 44.2 -> 12.4, 1024 x 1024
-// x 2048 22.5 -> 13.1, 512 x 2048 x 1024 15.1 -> 8.1, 2048 x 512 x 2048 22.8 -> 13.2); at K = 4000 the
-// small-problem kernel's K split over eight wavefronts keeps the lead (1000 x 1000 x 4000: 29.4
-// against 37.2 us).  Few rows (M <= 64) and fewer tiles than half the CUs stay with it.
+// 16-bit inputs: where the small-problem kernel would run for lack of tiles but its 64-column
+// blocks would not give every CU one (it then falls back to 16-column blocks, several rounds of
+// them), the register-staged kernel's 64 x 64 tiles run faster as long as they still occupy at
+// least half of the CUs in one round and K is at most 2048.  rocprofv3 kernel times, BF16, operands
+// rotating over more than 512 MB as in the benchmark (small-problem -> 64 x 64 tiles): 768^3 20.5 ->
+// 11.5 us, 800 x 1200 x 1000 28.9 -> 16.1.  Where the 64-column blocks fill the CUs the small-problem
+// kernel stays (1000^3 14.1 against 16.4 us, 1024 x 1024 x 2048 23.3 against 25.6).
 constexpr int64_t kSmallTileMaxK = 2048;
 bool small_tiles16(const Problem& p, int cus) {
     const int64_t c = cus > 0 ? cus : 256, t64 = tiles(p.M, p.N, 64, 64);
-    return p.M > kSkinnyMaxM && 2 * t64 >= c && t64 <= c && p.K <= kSmallTileMaxK;
+    return p.M > kSkinnyMaxM && 2 * t64 >= c && t64 < c && p.K <= kSmallTileMaxK;
 }
 
 // Kernel names as gemm_last_kernel() reports them: the input type, then the kernel.

@@ -241,11 +241,14 @@ KNOWN_KERNELS = {"f32_dma256x256", "f32_dma128x128", "f32_mfma128x128", "f32_mfm
     ("bf16", (2048, 4096, 4096), (R, C_, R), ("bf16_dma256x128", 2048, 4096)),
     ("bf16", (2048, 4096, 11008), (R, C_, R), ("bf16_dma256x128", 2048, 4096)),
     ("f32", (16, 4096, 4096), (R, R, R), ("f32_skinny16", 16, 4096)),
-    # 16-bit inputs: 64 x 64 register-staged tiles where they fill half to all of the CUs in one
-    # round and K <= 2048; the small-problem kernel for longer K, few rows or fewer tiles
-    ("bf16", (1000, 1000, 1000), (R, C_, R), ("bf16_mfma64x64", 1000, 1000)),
+    # 16-bit inputs: 64 x 64 register-staged tiles where the small-problem kernel's 64-column
+    # blocks would leave CUs idle but the tiles fill at least half of them in one round (K <= 2048);
+    # the small-problem kernel where its 64-column blocks fill the CUs, for longer K, few rows or
+    # fewer tiles
+    ("bf16", (1000, 1000, 1000), (R, C_, R), ("bf16_skinny64", 1000, 1000)),
     ("bf16", (768, 768, 768), (R, C_, R), ("bf16_mfma64x64", 768, 768)),
-    ("bf16", (1000, 1000, 4000), (R, C_, R), ("bf16_skinny64", 1000, 1000)),
+    ("bf16", (800, 1200, 1000), (R, C_, R), ("bf16_mfma64x64", 800, 1200)),
+    ("bf16", (768, 768, 4000), (R, C_, R), ("bf16_skinny16", 768, 768)),
     ("bf16", (512, 512, 1024), (R, C_, R), ("bf16_skinny16", 512, 512)),
     ("f32", (1000, 1000, 1000), (R, R, R), ("f32_skinny64", 1000, 1000)),
     # column-major A: no overhang along M, so the core stops at the last whole row of tiles
@@ -328,8 +331,10 @@ def test_plan_invariants_on_random_shapes():
     ("bf16", (4096, 4096, 4096), (R, C_, R), 0),
     ("bf16", (2048, 4096, 4096), (R, C_, R), 0),
     ("bf16", (2048, 4096, 11008), (R, C_, R), 1 * 2048 * 4096 * 4),
-    # 16-bit 1000^3 runs on 64 x 64 register-staged tiles (one round), which never split
+    # 16-bit 1000^3: the small-problem kernel's 64-column blocks fill the CUs (no split); 768^3
+    # runs on 64 x 64 register-staged tiles, which never split
     ("bf16", (1000, 1000, 1000), (R, C_, R), 0),
+    ("bf16", (768, 768, 768), (R, C_, R), 0),
     # FP32: whole 256 x 256 tiles split into one round's worth of slices of at least 512 where the
     # time model prices that below the default plan: the shard's 32 tiles in 8 slices, 2048^2 in 4;
     # not 4096 x 768 x 2048 (short slices), not ragged M, not tiles that fill the chip

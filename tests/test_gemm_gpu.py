@@ -268,14 +268,16 @@ def test_skinny_rejects_unsupported(bad):
     ("f32", (256, 256, 256), "f32_skinny16"), ("f32", (1000, 1000, 1000), "f32_skinny64"),
     ("f32", (2048, 2048, 256), "f32_dma128x128"), ("f32", (2047, 2049, 255), "f32_dma128x128"),
     ("f32", (4095, 4097, 1023), "f32_dma256x256"), ("bf16", (4095, 4097, 1023), "bf16_dma256x256"),
-    ("bf16", (1000, 1000, 1000), "bf16_mfma64x64"), ("bf16", (1000, 1000, 4000), "bf16_skinny64"),
+    ("bf16", (1000, 1000, 1000), "bf16_skinny64"), ("bf16", (768, 768, 768), "bf16_mfma64x64"),
+    ("bf16", (800, 1200, 1000), "bf16_mfma64x64"),
     ("f32", (1500, 1500, 512), "f32_mfma64x64"), ("f32", (4096, 4096, 64), "f32_dma256x256"),
     ("bf16", (4096, 4096, 64), "bf16_dma256x256"),
     ("bf16", (2048, 4096, 128), "bf16_dma256x128"), ("bf16", (2048, 11008, 128), "bf16_dma256x256")],
     ids=lambda v: str(v))
 def test_auto_kernel_choice(dtype, shape, kernel):
     """AUTO: few rows or too few 64 x 64 tiles -> small-problem kernel (for 16-bit inputs with
-    K <= 2048 and 64 x 64 tiles that fill half to all of the CUs: those tiles), else block tiles; a
+    K <= 2048 whose 64 x 64 tiles fill at least half but not all of the CUs: those tiles), else
+    block tiles; a
     tile kernel whose last tiles along an edge would start a second round stops at the last
     whole tile there and leaves the rest to a strip (4095 x 4097 on 256^2 tiles: 16 x 16
     tiles and a one-column strip)."""
@@ -670,7 +672,8 @@ def test_workspace_must_be_16_byte_aligned():
 
 # --- FP16 inputs (the same 16-bit kernels with the fp16 matrix instructions) --------------
 F16_AUTO = [((4096, 4096, 256), "f16_dma256x256"), ((2048, 4096, 128), "f16_dma256x128"),
-            ((1000, 1000, 1000), "f16_mfma64x64"), ((16, 4096, 4096), "f16_skinny16"),
+            ((1000, 1000, 1000), "f16_skinny64"), ((768, 768, 768), "f16_mfma64x64"),
+            ((16, 4096, 4096), "f16_skinny16"),
             ((4095, 4097, 72), "f16_dma256x256"), ((300, 264, 192), None), ((33, 300, 127), None)]
 
 

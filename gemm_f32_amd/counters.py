@@ -11,10 +11,10 @@ limits of the counter blocks):
      SQ_INSTS_VALU, SQ_INSTS_LDS, SQ_WAVES, SQ_BUSY_CU_CYCLES;
   B  FETCH_SIZE (KiB the L2s fetched from the fabric: last-level cache or HBM) and TCC_HIT_sum;
   C  WRITE_SIZE (KiB written) with TCC_MISS_sum and TCC_REQ_sum;
-  D  GRBM_GUI_ACTIVE (GPU cycles, summed over the XCDs) with the matrix-core busy cycles and the waves'
-     resident and waiting cycles, in a run that also traces each dispatch's start and end (--kernel-trace):
-     cycles over duration give the shader clock the kernel actually ran at, and matrix-busy cycles over
-     GPU cycles the fraction of the matrix-core peak at that clock.
+  D  cycle counts (GRBM_GUI_ACTIVE, SQ_BUSY_CU_CYCLES, the matrix-core busy cycles, the waves' resident
+     and waiting cycles) in a run that also traces each dispatch's start and end (--kernel-trace): the
+     CUs' busy cycles, the share of them the matrix cores worked, and a lower bound on the shader clock
+     (the clock itself: gemm_f32_amd/clockprobe.py).
 `calibrate` runs passes B and C over bench.py's plain 256 MiB device copy, whose bytes are known:
 FETCH_SIZE and WRITE_SIZE of a kernel are scaled by (bytes copied) / (what the copy's counters read).
 `summarize` averages every library kernel's counters over its dispatches and prints one markdown row
@@ -120,26 +120,33 @@ def _agent(dir_: str) -> dict:
 
 
 def clock_table(dirs: list) -> None:
-    """Pass D: the shader clock each kernel ran at and its matrix-core busy fraction at that clock."""
-    print("\n| workload | kernel | dispatches | kernel µs | GPU cycles (per XCD) | shader clock GHz | "
-          "matrix busy % of GPU cycles (= % of the matrix peak at that clock) | peak at that clock / nominal | "
-          "waves resident % of GPU cycles | wave cycles waiting % |")
+    """Pass D: per kernel, the cycles its CUs were busy and how much of them the matrix cores worked.
+
+    SQ_BUSY_CU_CYCLES (summed over the CUs) counts only cycles in which a CU holds a wavefront of the
+    kernel, so busy cycles per CU over the kernel's traced duration are a lower bound on the shader
+    clock.  GRBM_GUI_ACTIVE (summed over the XCDs) also counts the profiler's counter window around the
+    dispatch, about 21 k cycles per dispatch on this machine: a short kernel shows it as more cycles
+    than its duration allows, so it is reported but not turned into a clock."""
+    print("\n| workload | tile order | kernel | dispatches | kernel µs | GRBM cycles per XCD (incl. counter window) | "
+          "CU-busy cycles per CU | clock lower bound GHz (busy cycles / kernel time) | "
+          "matrix busy % of CU-busy cycles | wave cycles waiting % |")
     print("|---|---|---|---|---|---|---|---|---|---|")
     for d in dirs:
         stem = os.path.basename(os.path.normpath(d))[:-2]
-        workload = stem.split("@")[0]
+        workload, order = stem.split("@")
         ag = _agent(d)
+        cus = ag["simds"] // 4
         for k, rows in sorted(_read_dispatches(d).items()):
             if not _library_kernel(k):
                 continue
-            cyc = _mean([c["GRBM_GUI_ACTIVE"] / ag["xcc"] for c, _, _ in rows])
+            grbm = _mean([c["GRBM_GUI_ACTIVE"] / ag["xcc"] for c, _, _ in rows])
             dur = _mean([t for _, t, _ in rows])
-            clk = _mean([c["GRBM_GUI_ACTIVE"] / ag["xcc"] / t for c, t, _ in rows])
-            busy = _mean([c["SQ_VALU_MFMA_BUSY_CYCLES"] / ag["simds"] / (c["GRBM_GUI_ACTIVE"] / ag["xcc"]) for c, _, _ in rows])
-            life = _mean([4 * c["SQ_WAVE_CYCLES"] / w / (c["GRBM_GUI_ACTIVE"] / ag["xcc"]) for c, _, w in rows])
+            busy = _mean([c["SQ_BUSY_CU_CYCLES"] / cus for c, _, _ in rows])
+            low = _mean([c["SQ_BUSY_CU_CYCLES"] / cus / t for c, t, _ in rows])
+            mfma = _mean([c["SQ_VALU_MFMA_BUSY_CYCLES"] / ag["simds"] / (c["SQ_BUSY_CU_CYCLES"] / cus) for c, _, _ in rows])
             wait = _mean([c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"] for c, _, _ in rows])
-            print(f"| {workload} | `{_short(k)}` | {len(rows)} | {dur / 1e3:.1f} | {cyc:.0f} | {clk:.3f} | {100 * busy:.1f} | "
-                  f"{clk * 1e3 / ag['mhz']:.3f} | {100 * life:.1f} | {100 * wait:.1f} |")
+            print(f"| {workload} | {order.replace('~', ', algo ')} | `{_short(k)}` | {len(rows)} | {dur / 1e3:.1f} | {grbm:.0f} | {busy:.0f} | {low:.3f} | "
+                  f"{100 * mfma:.1f} | {100 * wait:.1f} |")
 
 
 def _mean(x):

@@ -159,6 +159,13 @@ void k_skinny(KArg<BATCH> p, int vec_a, int vec_b, int vec_c, int bbuf, int ksli
     const int li = lane & 15, lq = lane >> 4;
     const int K = p.K;
     const bool n_inside = n0 + BNW <= p.N;      // wavefront-uniform
+    // Row-major FP32 B read 16 bytes along N (RC4) with N % 4 == 0: in the last column slab each
+    // lane's four columns lie wholly inside N or wholly past it, and a lane past it reads the slab's
+    // last four valid columns instead (its products reach only columns of C that are never stored),
+    // so the slab takes the unchecked loads too.  (Checked loads in that one slab made the whole
+    // launch wait on it: 1000^3 FP32 40.8 -> 31.5 us, 1000 x 1000 x 4000 129 -> 95 us.)
+    const bool n_groups = RC4 && (p.N & 3) == 0 && p.N >= 4;     // uniform
+    const int col4 = n_groups ? min(n0 + 4 * li, p.N - 4) : n0 + 4 * li;
 
     // this lane's rows of A (one per 16-row strip) and columns of B, clamped into range
     const E* arow[FM];
@@ -219,7 +226,7 @@ void k_skinny(KArg<BATCH> p, int vec_a, int vec_b, int vec_c, int bbuf, int ksli
             } else if constexpr (RC4) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    fb[buf][s][e] = F32::load_row4(Bf, p.ldb, k + e, kend, n0 + 4 * li, p.N, FAST || (full && n_inside));
+                    fb[buf][s][e] = F32::load_row4(Bf, p.ldb, k + e, kend, col4, p.N, FAST || (full && (n_inside || n_groups)));
             } else if (FAST || (bbuf && full)) {
                 // kc is the same in every lane; saying so keeps the offset scalar (no waterfall)
                 const int soff = __builtin_amdgcn_readfirstlane((int)((int64_t)(kc + s * D::KSTEP) * p.ldb * 4));
@@ -257,7 +264,7 @@ void k_skinny(KArg<BATCH> p, int vec_a, int vec_b, int vec_c, int bbuf, int ksli
     // branch between checked and unchecked loads the compiler waits for all of them, the batch
     // ahead included, so each batch's memory latency was exposed in turn.  The rest of K (the
     // last rounds, or operands that need checked loads) runs the general round.
-    const bool unchecked = vec_a && (B_KC ? vec_b : RC4 ? n_inside : bbuf != 0);   // uniform
+    const bool unchecked = vec_a && (B_KC ? vec_b : RC4 ? (n_inside || n_groups) : bbuf != 0);   // uniform
 #pragma unroll
     for (int r = 0; r + 1 < RING; ++r)
         if (kbeg + r * SC < kend) load_chunk(r, kbeg + r * SC, std::false_type{});

@@ -241,6 +241,31 @@ def test_skinny64_padded_and_c_orders(oc, pad):
     assert g.gemm_last_kernel() == "f32_skinny64"
 
 
+@pytest.mark.parametrize("shape,pad", [((1000, 1004, 129), 3), ((1030, 1000, 300), 0), ((1000, 996, 4097), 5)],
+                         ids=lambda v: str(v))
+def test_skinny64_row_major_b_edge_slab_exact(shape, pad):
+    """Row-major FP32 B with N % 4 == 0 and a last column slab that N ends inside: that slab takes
+    the unchecked 16-byte loads, its lanes past N reading the slab's last valid columns.  Small
+    integers make every element exact; the check also covers C's padding and, with padded rows of
+    B, lanes that must not read past a row's N columns."""
+    M, N, K = shape
+    rng = np.random.default_rng(23)
+    A = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    B = rng.integers(-4, 5, (K, N)).astype(np.float32)
+    p = gi.make_problem(M, N, K, "f32", ROW_MAJOR, ROW_MAJOR, A_logical=A, B_logical=B, pad_b=pad, pad_c=pad)
+    check(p, g.Algo.SKINNY, exact=True)
+    assert g.gemm_last_kernel() == "f32_skinny64"
+
+
+def test_skinny64_row_major_b_edge_slab_split_k():
+    """The same edge slab with split-K through a workspace (partial tiles, then the slice sum)."""
+    p = gi.make_problem(16, 1000, 16384, "f32", ROW_MAJOR, ROW_MAJOR, wid=66)
+    flat, need, kernel = run_ws(p)
+    assert need > 0 and kernel == "f32_skinny64_splitk"
+    ref, D = oracle.gemm(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b)
+    assert oracle.normalised_error(logical_c(p, flat), ref, D) <= TOL["f32"]
+
+
 def test_skinny64_closed_forms():
     n = 1024
     perm = np.random.default_rng(11).permutation(n)

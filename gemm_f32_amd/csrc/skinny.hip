@@ -414,10 +414,13 @@ SkinnySplit skinny_split(const Problem& p, bool bf16, int cus) {
     // many K slices as it takes to give every CU a workgroup, each slice at least one batch
     // of k-steps per wavefront
     const int64_t c = cus > 0 ? cus : 256;
-    // only where the kernel's own blocks leave CUs without a workgroup (at 16 x 4096 x 4096
-    // its 256 blocks of 16 columns fill the chip, and a split measured slower there)
+    // not where the kernel's own blocks make exactly one round (at 16 x 4096 x 4096 its 256 blocks
+    // of 16 columns fill the chip, and a split measured slower there: 24.6 us plus 4.7 for the slice
+    // sum against 26.4).  Where they leave CUs without a workgroup, or need more than one round, the
+    // split's one round of 64-column blocks wins (rocprofv3, operands from HBM: 16 x 8192 x 8192 FP32
+    // 92.7 -> 63.7 us, 32 x 8192 x 4096 FP32 60.2 -> 37.4; their plain blocks take two rounds).
     const int fn0 = skinny_blocks(p, cus), fm0 = skinny_strips(p, fn0, cus);
-    if ((int64_t)((p.M + 16 * fm0 - 1) / (16 * fm0)) * ((p.N + 16 * fn0 - 1) / (16 * fn0)) >= c) return sp;
+    if ((int64_t)((p.M + 16 * fm0 - 1) / (16 * fm0)) * ((p.N + 16 * fn0 - 1) / (16 * fn0)) == c) return sp;
     const int fn = 4, fm = skinny_strips(p, fn, cus);
     const int64_t wgs = (int64_t)((p.M + 16 * fm - 1) / (16 * fm)) * ((p.N + 63) / 64);
     if (wgs >= c) return sp;

@@ -320,6 +320,12 @@ def test_plan_invariants_on_random_shapes():
     ("f32", (4096, 4096, 4096), (R, R, R), 0),
     # K too short for even two slices of one batch per wavefront
     ("f32", (16, 1024, 500), (R, R, R), 0),
+    # blocks of 16 columns that need two rounds: one round of 64-column blocks in 2 K slices; one
+    # exact round of them (16 x 4096 x 4096) stays unsplit
+    ("f32", (16, 8192, 8192), (R, R, R), 2 * 16 * 8192 * 4),
+    ("f32", (32, 8192, 4096), (R, R, R), 2 * 32 * 8192 * 4),
+    ("f32", (16, 4096, 4096), (R, R, R), 0),
+    ("bf16", (16, 4096, 4096), (R, C_, R), 0),
     # column-major C: C^T has the few rows
     ("f32", (1024, 16, 16384), (C_, C_, C_), 16 * 16 * 1024 * 4),
     # 16-bit inputs on 256 x 256 tiles that leave CUs idle: one GPU's column shard of 4096^3 in

@@ -266,6 +266,19 @@ def test_skinny64_row_major_b_edge_slab_split_k():
     assert oracle.normalised_error(logical_c(p, flat), ref, D) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("dtype,ob", [("f32", ROW_MAJOR), ("bf16", COL_MAJOR)], ids=["f32-RR", "bf16"])
+def test_split_k_for_two_rounds_of_skinny_blocks(dtype, ob):
+    """16 rows and 8192 columns: 512 blocks of 16 columns would take two rounds; with a workspace
+    the call runs one round of 64-column blocks in K slices and sums the slices in order."""
+    p = gi.make_problem(16, 8192, 2048, dtype, ROW_MAJOR, ob, wid=67)
+    flat, need, kernel = run_ws(p)
+    assert need > 0 and kernel == f"{dtype}_skinny64_splitk"
+    ref, D = oracle.gemm(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b)
+    assert oracle.normalised_error(logical_c(p, flat), ref, D) <= TOL[dtype]
+    again, _, _ = run_ws(p)
+    assert np.array_equal(flat, again)         # fixed slice order: bit-identical repeats
+
+
 def test_skinny64_closed_forms():
     n = 1024
     perm = np.random.default_rng(11).permutation(n)

@@ -14,7 +14,7 @@ kernel against MI355X's published matrix-core peak for its dtype.
 `--workload` picks another single workload from gemm_inputs.WORKLOADS (then one step is
 that one GEMM, or one strided batched call for a batch workload such as attention's per-head
 products); `--algo` forces a kernel (gemm_f32_amd.Algo name); `--epilogue NAME` calls the fused-epilogue entry point (bias, activation, bf16 output) for a
-workload with row-major A and column-major B; `--k K` replaces a single workload's K (a sweep over K separates a kernel's fixed
+workload whose layout the fused calls take (row-major A with column-major B, or row-major A and B with N % 8 == 0); `--k K` replaces a single workload's K (a sweep over K separates a kernel's fixed
 cost -- launch, first loads, the C write -- from its cost per k-tile); `--workspace` calls the
 workspace entry points (gemm_f32_ws / gemm_bf16_f32acc_ws, split-K across workgroups where
 the problem is too small to fill the device) with a workspace of the size the library asks

@@ -49,6 +49,7 @@ SPECS = [
     # and the register-staged kernel this layout took before it
     ("square4096_bf16_rr", ["--workload", "square4096_bf16_rr"], 30),
     ("square4096_bf16_rr@MFMA_128x128", ["--workload", "square4096_bf16_rr", "--algo", "MFMA_128x128"], 30),
+    ("square4096_bf16_rr@bias_gelu_bf16", ["--workload", "square4096_bf16_rr", "--epilogue", "bias_gelu_bf16"], 30),
     ("square4096_e4m3", ["--workload", "square4096_e4m3"], 30),
     ("square4096_e5m2", ["--workload", "square4096_e5m2"], 30),
     # the same 4096 x 4096 outputs over K: fixed cost (launch, first loads, the 64 MB C write)

@@ -223,3 +223,46 @@ def test_f32_fused_whole_tiles_and_edges(oc):
     Y, S = oracle.epilogue(ref[None, :], D[None, :], alpha=0.75, beta=0.5, C_old=old[rows, cols][None, :],
                            bias=bias[cols], activation=oracle.ACT_RELU)
     assert_close(got[rows, cols][None, :], Y, S, "f32", g.Out.F32)
+
+
+# --- row-major B (n-contiguous, PyTorch's x . W with W [K, N]): the direct-copy kernel keeps the B
+# k-tile as laid out and reads it with gfx950's transposing LDS read; N % 8 == 0 --------------------
+BRM_SHAPES = [(300, 264, 96), (512, 512, 64), (77, 1032, 128), (1000, 704, 1000)]
+
+
+@pytest.mark.parametrize("epi", list(EPILOGUES))
+@pytest.mark.parametrize("shape", BRM_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("orders", [(R, R, R), (C_, C_, C_)], ids=["RRR", "CCC"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_fused_row_major_b_matches_oracle(dtype, orders, shape, epi):
+    """All three operands row-major, or all three column-major (C^T = B^T A^T turns it into the
+    same row-major-B problem): every epilogue against the oracle, C's padding untouched."""
+    M, N, K = shape
+    oa, ob, oc = orders
+    if oc == C_:
+        M, N = N, M                 # the swapped problem's N is this problem's M: keep it % 8 == 0
+    p = gi.make_problem(M, N, K, dtype, oa, ob, oc, wid=83, pad_c=3)
+    got, Y, S, pad_ok = run_fused(p, EPILOGUES[epi], seed=M + 2 * N)
+    assert pad_ok, "C written outside the logical matrix"
+    kernel = g.gemm_last_kernel()
+    assert "_dma" in kernel and kernel.endswith("_fused") != (epi == "plain"), kernel
+    assert_close(got, Y, S, dtype, EPILOGUES[epi][4])
+
+
+@pytest.mark.parametrize("case", ["RRC", "N%8"])
+def test_fused_refuses_layouts_the_kernel_does_not_take(case):
+    """Row-major A and B with a column-major C (the swap makes A column-major), and row-major B with
+    N % 8 != 0: refused before anything is enqueued, C left as it was."""
+    import torch
+    if case == "RRC":
+        p = gi.make_problem(128, 256, 64, "bf16", R, R, C_)
+    else:
+        p = gi.make_problem(128, 260, 64, "bf16", R, R, R)
+    A, B = to_device(p.A), to_device(p.B)
+    C = torch.full((gi.c_buffer_size(p.M, p.N, p.ldc, p.order_c),), 7.0, dtype=torch.float32, device="cuda")
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_bf16_f32acc_fused(p.M, p.N, p.K, A.data_ptr(), p.lda, p.order_a, B.data_ptr(), p.ldb, p.order_b,
+                                 C.data_ptr(), p.ldc, p.order_c, alpha=2.0, activation=g.Act.RELU)
+    assert e.value.status == g.Status.ERR_INVALID_VALUE
+    torch.cuda.synchronize()
+    assert torch.all(C == 7.0).item()

@@ -151,6 +151,9 @@ const char* skinny_name(int et, int fn) {
     return names[et][fn == 4 ? 1 : 0];
 }
 
+// FP32, few rows, row-major B: two K halves of 32-column blocks added into a zeroed C
+constexpr const char* kSkinnyHalvesName = "f32_skinny32_halves";
+
 // A strided batch on the normalised problem (element strides; C's in floats); n == 1: one problem.
 struct Batch {
     int64_t n = 1, sa = 0, sb = 0, sc = 0;
@@ -169,14 +172,20 @@ SkinnySplit split_with(const Problem& p, int et, int cus, const Workspace& ws) {
     return sp.slices > 1 && sp.bytes <= ws.bytes ? sp : SkinnySplit{};
 }
 
-// The small-problem kernel, with 1 or 4 column blocks of 16 per workgroup.
+// The small-problem kernel, with 1 or 4 column blocks of 16 per workgroup; `choose`: the default
+// choice, which also takes the two-halves mode where it applies (a forced GEMM_ALGO_SKINNY keeps
+// the plain blocks).
 hipError_t run_skinny(const Problem& p, const Launch& l, int et, int cus, const char*& name,
-                      const Workspace& ws = Workspace{}) {
+                      const Workspace& ws = Workspace{}, bool choose = false) {
     const SkinnySplit sp = split_with(p, et, cus, ws);
     if (sp.slices > 1) {       // K split across workgroups too: partial products in the workspace
         static const char* names[3] = {"f32_skinny64_splitk", "bf16_skinny64_splitk", "f16_skinny64_splitk"};
         name = names[et];
         return launch_skinny(p, l, et, sp.fn, sp.fm, &sp, static_cast<float*>(ws.ptr));
+    }
+    if (choose && et == kElemF32 && l.batch == 1 && l.vec_a && skinny_halves_applies(p, cus)) {
+        name = kSkinnyHalvesName;
+        return launch_skinny_halves(p, l);
     }
     const int fn = skinny_blocks(p, cus);
     name = skinny_name(et, fn);
@@ -575,7 +584,7 @@ hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, int 
                 return run_skinny(p, l, kElemF32, dev.cus, name);
             default:
                 if (algo == GEMM_ALGO_AUTO && prefer_small(p, dev.cus) && skinny_applies(p, false))
-                    return run_skinny(p, l, kElemF32, dev.cus, name, ws);
+                    return run_skinny(p, l, kElemF32, dev.cus, name, ws, true);
                 return run_f32_tiles(p, stream, algo, dev, name, st, b, ws);
         }
     }
@@ -632,6 +641,7 @@ const char* plan_auto(const Problem& p, int et, int cus, int& mc, int& nc) {
     nc = p.N;
     if (et == kElemFp8) return fp8_name(plan_fp8(p, cus).opt);
     const bool small = prefer_small(p, cus) && skinny_applies(p, !f32);
+    if (small && f32 && skinny_halves_applies(p, cus)) return kSkinnyHalvesName;
     if (small && (f32 || !small_tiles16(p, cus))) return skinny_name(et, skinny_blocks(p, cus));
     const Plan pl = f32 ? choose_f32_tiles(p, GEMM_ALGO_AUTO, cus)
                         : choose_bf16_tiles(p, small ? GEMM_ALGO_MFMA_64x64 : GEMM_ALGO_AUTO, cus);

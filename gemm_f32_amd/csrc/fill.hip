@@ -8,13 +8,19 @@
 namespace gemm {
 namespace {
 
-__global__ __launch_bounds__(256) void k_zero_c(float* C, int M, int N, int64_t ldc, int64_t sc) {
-    C += blockIdx.y * sc;     // entry of a strided batch (0 for one problem)
-    const int64_t total = (int64_t)M * N;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-         e += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = e / N, c = e % N;
-        C[r * ldc + c] = 0.f;
+// C = 0 on an M x N block: four columns per thread (16-byte stores where `vec`), rows along
+// grid y (strided when M exceeds it), strided-batch entries along grid z.
+__global__ __launch_bounds__(256) void k_zero_c(float* C, int M, int N, int64_t ldc, int64_t sc, int vec) {
+    C += blockIdx.z * sc;     // entry of a strided batch (0 for one problem)
+    const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (c >= N) return;
+    for (int64_t r = blockIdx.y; r < M; r += gridDim.y) {
+        float* row = C + r * ldc;
+        if (vec && c + 3 < N) {
+            *reinterpret_cast<float4*>(row + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+        } else {
+            for (int e = 0; e < 4 && c + e < N; ++e) row[c + e] = 0.f;
+        }
     }
 }
 
@@ -80,12 +86,11 @@ hipError_t launch_epi_fill(const EpiProblem& p, const Launch& l) {
 }
 
 hipError_t launch_zero_c(const Problem& p, const Launch& l) {
-    const int64_t total = (int64_t)p.M * p.N;
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    if (l.batch > 1 && blocks > 64) blocks = 64;     // the batch fills the grid along y
-    hipLaunchKernelGGL(k_zero_c, dim3((unsigned)blocks, (unsigned)l.batch), dim3(256), 0, l.stream, p.C, p.M, p.N,
-                       p.ldc, l.batch > 1 ? l.sc : (int64_t)0);
+    if (p.M <= 0 || p.N <= 0) return hipSuccess;
+    const unsigned gx = (unsigned)(((int64_t)p.N + 1023) / 1024);
+    const unsigned gy = (unsigned)std::min<int64_t>(p.M, 1024);
+    hipLaunchKernelGGL(k_zero_c, dim3(gx, gy, (unsigned)l.batch), dim3(256), 0, l.stream, p.C, p.M, p.N, p.ldc,
+                       l.batch > 1 ? l.sc : (int64_t)0, (int)l.vec_c);
     return hipGetLastError();
 }
 

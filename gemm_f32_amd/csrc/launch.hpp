@@ -67,6 +67,14 @@ SkinnySplit skinny_split(const Problem& p, bool bf16, int cus);
 // the split; nullptr: one pass into C
 hipError_t launch_skinny(const Problem& p, const Launch& l, int et, int fn, int fm,
                          const SkinnySplit* sp = nullptr, float* part = nullptr);
+// Few rows of an FP32 product with row-major A and B (M <= 16, N and ldb even, B 8-byte
+// aligned): 32-column blocks over two K halves, C zeroed first and each half's sum added into
+// it atomically (exactly two contributions per output, so the result does not depend on their
+// order).  _applies: where the host prefers it to the 16-column blocks (K >= kSkinnyHalvesMinK).
+constexpr int kSkinnyHalvesMinK = 4096;
+bool skinny_halves_ok(const Problem& p);
+bool skinny_halves_applies(const Problem& p, int cus);
+hipError_t launch_skinny_halves(const Problem& p, const Launch& l);
 // C = 0 for K == 0 (fill.hip)
 hipError_t launch_zero_c(const Problem& p, const Launch& l);
 // Fused epilogue (epilogue.hpp): the 16-bit direct-copy kernel with the epilogue in its stores

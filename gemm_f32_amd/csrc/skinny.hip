@@ -136,15 +136,16 @@ struct F32 {
 // the epilogue writes the 4 columns of a lane with one 16-byte store.
 template <typename D, int FM, int FN, int WAVES, bool B_KC, bool BATCH = false>
 __global__ __launch_bounds__(64 * WAVES)
-void k_skinny(KArg<BATCH> p, int vec_a, int vec_b, int vec_c, int bbuf, int kslice, float* part) {
+void k_skinny(KArg<BATCH> p, int vec_a, int vec_b, int vec_c, int bbuf, int kslice, float* part, int accum) {
     if constexpr (BATCH) p.select(blockIdx.z);
     using E = typename D::Elem;
     using Frag = typename D::Frag;
     constexpr bool RC4 = !B_KC && FN == 4;     // row-major FP32 B read 16 bytes along N
+    constexpr bool RC2 = !B_KC && FN == 2;     // row-major FP32 B read 8 bytes along N
     constexpr int BNW = 16 * FN;               // columns per workgroup
     constexpr int NB = RC4 ? 4 : FN;           // B fragments per k-step
-    static_assert(FN == 1 || FN == 4, "one or four column blocks");
-    static_assert(!RC4 || D::KL == 4, "four column blocks of a row-major B: FP32 only");
+    static_assert(FN == 1 || FN == 2 || FN == 4, "one, two or four column blocks");
+    static_assert(!(RC4 || RC2) || D::KL == 4, "column blocks read along a row-major B: FP32 only");
     __shared__ f32x4 red[WAVES - 1][FM][FN][64];
 
     // (row block, column slab): the workgroups one XCD receives cover all row blocks of a
@@ -172,10 +173,13 @@ void k_skinny(KArg<BATCH> p, int vec_a, int vec_b, int vec_c, int bbuf, int ksli
 #pragma unroll
     for (int f = 0; f < FM; ++f)
         arow[f] = static_cast<const E*>(p.A) + (int64_t)min(m0 + 16 * f + li, p.M - 1) * p.lda;
+    // column of C that block q's lane li computes: n0 + 16 q + li, or n0 + 2 li + q for a
+    // row-major FP32 B read 8 bytes along N (two interleaved blocks)
+    auto col_of = [&](int q) { return RC2 ? n0 + 2 * li + q : n0 + 16 * q + li; };
     const E* bcol[FN];
 #pragma unroll
     for (int q = 0; q < FN; ++q) {
-        const int n = min(n0 + 16 * q + li, p.N - 1);
+        const int n = min(col_of(q), p.N - 1);
         bcol[q] = static_cast<const E*>(p.B) + (B_KC ? (int64_t)n * p.ldb : (int64_t)n);
     }
     const float* Bf = reinterpret_cast<const float*>(p.B);
@@ -187,6 +191,14 @@ void k_skinny(KArg<BATCH> p, int vec_a, int vec_b, int vec_c, int bbuf, int ksli
     const __amdgpu_buffer_rsrc_t rbuf = __builtin_amdgcn_make_buffer_rsrc((void*)Bf, (short)0, 0x7fffffff, 0x00020000);
     if constexpr (!B_KC && FN == 1) {
         const int n = min(n0 + li, p.N - 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bvoff[e] = (unsigned)(((lq * 4 + e) * p.ldb + n) * 4);
+    }
+    // two column blocks (RC2; the host guarantees an even N and ldb and an 8-byte aligned B):
+    // byte offsets of the lane's column pair in its four rows of a k-step, the pair clamped to
+    // the last one inside N (a lane past N reads it; its products reach no stored column)
+    if constexpr (RC2) {
+        const int n = min(n0 + 2 * li, p.N - 2);
 #pragma unroll
         for (int e = 0; e < 4; ++e) bvoff[e] = (unsigned)(((lq * 4 + e) * p.ldb + n) * 4);
     }
@@ -227,6 +239,21 @@ void k_skinny(KArg<BATCH> p, int vec_a, int vec_b, int vec_c, int bbuf, int ksli
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     fb[buf][s][e] = F32::load_row4(Bf, p.ldb, k + e, kend, col4, p.N, FAST || (full && (n_inside || n_groups)));
+            } else if constexpr (RC2) {
+                if (FAST || (bbuf && full)) {
+                    // 8-byte loads of the lane's two columns in its four rows: block 0 takes the
+                    // first column of each pair, block 1 the second
+                    const char* rowp = reinterpret_cast<const char*>(Bf) + (int64_t)(kc + s * D::KSTEP) * p.ldb * 4;
+                    float2 v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = *reinterpret_cast<const float2*>(rowp + bvoff[e]);
+                    fb[buf][s][0] = make_float4(v[0].x, v[1].x, v[2].x, v[3].x);
+                    fb[buf][s][1] = make_float4(v[0].y, v[1].y, v[2].y, v[3].y);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+                        fb[buf][s][q] = F32::load_strided(reinterpret_cast<const float*>(bcol[q]), p.ldb, k, kend);
+                }
             } else if (FAST || (bbuf && full)) {
                 // kc is the same in every lane; saying so keeps the offset scalar (no waterfall)
                 const int soff = __builtin_amdgcn_readfirstlane((int)((int64_t)(kc + s * D::KSTEP) * p.ldb * 4));
@@ -288,6 +315,13 @@ void k_skinny(KArg<BATCH> p, int vec_a, int vec_b, int vec_c, int bbuf, int ksli
     }
 
     // ---- fixed-order sum of the wavefronts' partial products ----
+    // accum: C was zeroed and two workgroups (the two K halves) each add their sum into it.
+    // Addition of two numbers is commutative, so 0 + x + y is the same whichever comes first:
+    // deterministic, unlike three or more atomic contributions.
+    auto put = [&](float* dst, float v) {
+        if (accum) unsafeAtomicAdd(dst, v);
+        else *dst = v;
+    };
     if (wave > 0)
 #pragma unroll
         for (int f = 0; f < FM; ++f)
@@ -312,18 +346,18 @@ void k_skinny(KArg<BATCH> p, int vec_a, int vec_b, int vec_c, int bbuf, int ksli
                 if constexpr (RC4) {
                     // block q's column li is column n0 + 4 li + q
                     const int col = n0 + 4 * li;
-                    if ((part ? (p.N & 3) == 0 : vec_c) && n_inside) {
+                    if (!accum && (part ? (p.N & 3) == 0 : vec_c) && n_inside) {
                         *reinterpret_cast<f32x4*>(crow + col) = f32x4{sum[0][r], sum[1][r], sum[2][r], sum[3][r]};
                     } else {
 #pragma unroll
                         for (int q = 0; q < 4; ++q)
-                            if (col + q < p.N) crow[col + q] = sum[q][r];
+                            if (col + q < p.N) put(crow + col + q, sum[q][r]);
                     }
                 } else {
 #pragma unroll
                     for (int q = 0; q < FN; ++q) {
-                        const int col = n0 + 16 * q + li;
-                        if (col < p.N) crow[col] = sum[q][r];
+                        const int col = col_of(q);
+                        if (col < p.N) put(crow + col, sum[q][r]);
                     }
                 }
             }
@@ -338,17 +372,18 @@ template <typename D> int batch_k(int fm, int fn) {
 }
 
 template <typename D, int FN, int WAVES, bool B_KC, bool BATCH>
-hipError_t launch_d(const KArg<BATCH>& p, const Launch& l, int fm, int kslice, int slices, float* part) {
+hipError_t launch_d(const KArg<BATCH>& p, const Launch& l, int fm, int kslice, int slices, float* part,
+                    int accum = 0) {
     const int slabs = (p.N + 16 * FN - 1) / (16 * FN), rblocks = (p.M + 16 * fm - 1) / (16 * fm);
     const dim3 grid((unsigned)(slabs * rblocks), (unsigned)slices, BATCH ? l.batch : 1), block(64 * WAVES);
     const int va = l.vec_a, vb = l.vec_b, vc = l.vec_c;
     // buffer offsets of a row-major B (rows up to K, plus 3 rows of one k-step's lane
     // spread) must fit in 31 bits
     const int bb = !B_KC && (int64_t)(p.K + 4) * p.ldb * 4 + (int64_t)p.N * 4 < ((int64_t)1 << 31);
-    if (fm == 1) hipLaunchKernelGGL((k_skinny<D, 1, FN, WAVES, B_KC, BATCH>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part);
-    else if (fm == 2) hipLaunchKernelGGL((k_skinny<D, 2, FN, WAVES, B_KC, BATCH>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part);
-    else if (fm == 3) hipLaunchKernelGGL((k_skinny<D, 3, FN, WAVES, B_KC, BATCH>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part);
-    else hipLaunchKernelGGL((k_skinny<D, 4, FN, WAVES, B_KC, BATCH>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part);
+    if (fm == 1) hipLaunchKernelGGL((k_skinny<D, 1, FN, WAVES, B_KC, BATCH>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part, accum);
+    else if (fm == 2) hipLaunchKernelGGL((k_skinny<D, 2, FN, WAVES, B_KC, BATCH>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part, accum);
+    else if (fm == 3) hipLaunchKernelGGL((k_skinny<D, 3, FN, WAVES, B_KC, BATCH>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part, accum);
+    else hipLaunchKernelGGL((k_skinny<D, 4, FN, WAVES, B_KC, BATCH>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part, accum);
     return hipGetLastError();
 }
 
@@ -455,6 +490,47 @@ hipError_t launch_e(const KArg<BATCH>& p, const Launch& l, int et, int fn, int f
     return launch_d<F32, 1, W, false, BATCH>(p, l, fm, kslice, slices, out);
 }
 }  // namespace
+
+// Two K halves of 32-column blocks added into a zeroed C (see launch.hpp).  The blocks of the
+// plain kernel on a row-major FP32 B read 64 bytes of each row of B per workgroup and the
+// whole of A; 32-column blocks read whole 128-byte lines of B and, over half of K, half of A,
+// for the same number of workgroups.  Stand-alone read patterns of 16 x 4096 x 4096 on MI355X
+// (B from HBM, A from L2): 16 columns with A 22.3 us, 32 columns over half of K with A 17.3.
+int skinny_halves_kslice(const Problem& p) {
+    const int bk = batch_k<F32>(1, 2) * kSkinnyWaves;
+    return ((p.K + 1) / 2 + bk - 1) / bk * bk;
+}
+
+// What the kernel itself needs: one 16-row strip, row-major A and B, column pairs whose 8-byte
+// loads are aligned, and a K that splits into exactly two slices (two partial sums per output).
+bool skinny_halves_ok(const Problem& p) {
+    const int kslice = skinny_halves_kslice(p);
+    return p.oa == kRow && p.ob == kRow && p.M >= 1 && p.M <= 16 && p.N >= 2 && (p.N & 1) == 0 &&
+           (p.ldb & 1) == 0 && (reinterpret_cast<uintptr_t>(p.B) & 7) == 0 && p.K > 0 &&
+           (p.K + kslice - 1) / kslice == 2;
+}
+
+bool skinny_halves_applies(const Problem& p, int cus) {
+    const int64_t c = cus > 0 ? cus : 256;
+    if (!skinny_halves_ok(p) || p.K < kSkinnyHalvesMinK || skinny_blocks(p, cus) != 1) return false;
+    // the unchecked loads address B with 32-bit offsets from the k-step's row
+    if ((int64_t)(p.K + 4) * p.ldb * 4 + (int64_t)p.N * 4 >= ((int64_t)1 << 31)) return false;
+    // as many workgroups as the plain kernel's 16-column blocks, and enough to occupy most CUs
+    const int64_t wgs = 2 * ((p.N + 31) / 32);
+    return 2 * wgs >= c && wgs <= c;
+}
+
+hipError_t launch_skinny_halves(const Problem& p, const Launch& l) {
+    if (!skinny_halves_ok(p)) return hipErrorInvalidValue;
+    const hipError_t e = launch_zero_c(p, l);
+    if (e != hipSuccess) return e;
+    // one 16-row strip: a workgroup per 32-column block and K half (grid y)
+    const int bb = (int64_t)(p.K + 4) * p.ldb * 4 + (int64_t)p.N * 4 < ((int64_t)1 << 31);
+    hipLaunchKernelGGL((k_skinny<F32, 1, 2, kSkinnyWaves, false, false>), dim3((unsigned)((p.N + 31) / 32), 2u),
+                       dim3(64 * kSkinnyWaves), 0, l.stream, p, (int)l.vec_a, (int)l.vec_b, (int)l.vec_c, bb,
+                       skinny_halves_kslice(p), nullptr, 1);
+    return hipGetLastError();
+}
 
 hipError_t launch_skinny(const Problem& p, const Launch& l, int et, int fn, int fm, const SkinnySplit* sp,
                          float* part) {

@@ -22,7 +22,9 @@
  *
  * Ownership.  All matrix pointers are device pointers owned by the caller; A and B are
  * only read and must not overlap C.  C is only written, except by the fused-epilogue calls
- * with beta != 0, which read C's previous contents first.  Pointers need only their element's
+ * with beta != 0, which read C's previous contents first, and by AUTO's two-halves mode for
+ * few FP32 rows (SKINNY below), which zeroes C and then adds two partial sums into it with
+ * device-scope atomic float adds (C must then be ordinary device memory, as from hipMalloc).  Pointers need only their element's
  * natural alignment (4 bytes for float, 2 for bf16/fp16, 1 for fp8); no kernel needs more.  The plain
  * calls allocate no device memory and keep no state beyond a per-device property cache; the
  * _ws calls use the caller's workspace, and gemm_bf16_f32acc_noalloc a static array of the
@@ -94,7 +96,14 @@ typedef enum {
  *                      in a fixed order; needs row-major A, and for 16-bit inputs a column-major
  *                      B (with a column-major C the roles of M/N and A/B swap, C^T = B^T A^T),
  *                      else GEMM_ERR_INVALID_VALUE.  AUTO uses it when it applies and M <= 64
- *                      or 64 x 64 tiles would fill less than half of the CUs;
+ *                      or 64 x 64 tiles would fill less than half of the CUs.  For FP32 with
+ *                      row-major A and B, M <= 16, K >= 4096, N and ldb even, B 8-byte aligned
+ *                      and 32-column blocks giving between half and all of the CUs a
+ *                      workgroup per K half, AUTO takes it in a two-halves mode instead (a
+ *                      split of K; "A06", "The next two rungs"): C is zeroed, then one
+ *                      workgroup per 32-column block and K half adds its sum into C (8-byte
+ *                      loads along each row of B; exactly two contributions per output, so
+ *                      the result does not depend on their order and repeats bit for bit);
  *   MFMA_DMA           the direct-copy kernels: operands copied global -> LDS as laid out in
  *                      memory by buffer loads straight into LDS, no register staging ("GEMM
  *                      Optimization", V3 staging), tile picked by the cost model.  FP32:

@@ -225,7 +225,7 @@ def test_tile_scheduler_is_a_bijection_with_xcd_blocks():
 
 # --- the default kernel choice, without a device (gemm_plan) -----------------------------
 KNOWN_KERNELS = {"f32_dma256x256", "f32_dma128x128", "f32_mfma128x128", "f32_mfma64x64",
-                 "f32_skinny16", "f32_skinny64", "bf16_dma256x256", "bf16_dma256x128",
+                 "f32_skinny16", "f32_skinny64", "f32_skinny32_halves", "bf16_dma256x256", "bf16_dma256x128",
                  "bf16_mfma256x128", "bf16_mfma128x128", "bf16_mfma64x64",
                  "bf16_skinny16", "bf16_skinny64", "zero_c", "none"}
 
@@ -240,7 +240,16 @@ KNOWN_KERNELS = {"f32_dma256x256", "f32_dma128x128", "f32_mfma128x128", "f32_mfm
     ("bf16", (2048, 11008, 4096), (R, C_, R), ("bf16_dma256x256", 2048, 8192)),
     ("bf16", (2048, 4096, 4096), (R, C_, R), ("bf16_dma256x128", 2048, 4096)),
     ("bf16", (2048, 4096, 11008), (R, C_, R), ("bf16_dma256x128", 2048, 4096)),
-    ("f32", (16, 4096, 4096), (R, R, R), ("f32_skinny16", 16, 4096)),
+    # few FP32 rows with row-major B: two K halves of 32-column blocks (as many workgroups as
+    # 16-column blocks) where K is long, N and ldb even; else 16-column blocks over the whole of K
+    ("f32", (16, 4096, 4096), (R, R, R), ("f32_skinny32_halves", 16, 4096)),
+    ("f32", (4096, 16, 4096), (C_, C_, C_), ("f32_skinny32_halves", 16, 4096)),
+    ("f32", (16, 2048, 8192), (R, R, R), ("f32_skinny32_halves", 16, 2048)),
+    ("f32", (16, 4096, 2048), (R, R, R), ("f32_skinny16", 16, 4096)),
+    ("f32", (16, 4095, 4096), (R, R, R), ("f32_skinny16", 16, 4095)),
+    ("f32", (17, 4096, 4096), (R, R, R), ("f32_skinny16", 17, 4096)),
+    ("f32", (16, 4096, 4096), (R, C_, R), ("f32_skinny16", 16, 4096)),
+    ("f32", (16, 8192, 4096), (R, R, R), ("f32_skinny16", 16, 8192)),
     # 16-bit inputs: 64 x 64 register-staged tiles where the small-problem kernel's 64-column
     # blocks would leave CUs idle but the tiles fill at least half of them in one round (K <= 2048);
     # the small-problem kernel where its 64-column blocks fill the CUs, for longer K, few rows or

@@ -279,6 +279,67 @@ def test_split_k_for_two_rounds_of_skinny_blocks(dtype, ob):
     assert np.array_equal(flat, again)         # fixed slice order: bit-identical repeats
 
 
+# --- few FP32 rows with row-major B: 32-column blocks over two K halves, added into a zeroed C
+HALVES_CASES = [((16, 4096, 4096), (ROW_MAJOR, ROW_MAJOR, ROW_MAJOR)),
+                ((1, 4096, 4096), (ROW_MAJOR, ROW_MAJOR, ROW_MAJOR)),
+                ((13, 4094, 4097), (ROW_MAJOR, ROW_MAJOR, ROW_MAJOR)),
+                ((16, 2048, 8192), (ROW_MAJOR, ROW_MAJOR, ROW_MAJOR)),
+                ((7, 3000, 6001), (ROW_MAJOR, ROW_MAJOR, ROW_MAJOR)),
+                ((16, 2080, 4096), (ROW_MAJOR, ROW_MAJOR, ROW_MAJOR)),
+                # column-major C: C^T = B^T A^T is the 16-row problem
+                ((4096, 16, 4096), (COL_MAJOR, COL_MAJOR, COL_MAJOR))]
+
+
+@pytest.mark.parametrize("shape,orders", HALVES_CASES, ids=lambda v: str(v))
+def test_skinny_halves_random(shape, orders):
+    """The default choice for few rows of an FP32 product with row-major A and B, a long K and
+    an even N and ldb: a workgroup per 32-column block and K half, each adding its sum into C
+    after C is zeroed; ragged N (the last block's lanes past N read the last valid column pair)
+    and ragged K (the second half shorter) included."""
+    M, N, K = shape
+    p = gi.make_problem(M, N, K, "f32", *orders, wid=68)
+    check(p, g.Algo.AUTO, key=("halves", shape, orders))
+    assert g.gemm_last_kernel() == "f32_skinny32_halves"
+
+
+def test_skinny_halves_small_integer_exact_and_repeatable():
+    """Small integers: exact under any order, so bit-exact; padded B (even ldb) and a padded,
+    misaligned C whose padding must stay untouched.  Random inputs: two calls give the same bits,
+    since each output gets exactly two atomic contributions and 0 + x + y = 0 + y + x."""
+    rng = np.random.default_rng(29)
+    M, N, K = 16, 4090, 4097
+    A = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    B = rng.integers(-4, 5, (K, N)).astype(np.float32)
+    p = gi.make_problem(M, N, K, "f32", ROW_MAJOR, ROW_MAJOR, A_logical=A, B_logical=B, pad_b=2, pad_c=3)
+    check(p, g.Algo.AUTO, exact=True)
+    assert g.gemm_last_kernel() == "f32_skinny32_halves"
+    q = gi.make_problem(16, 4096, 4096, "f32", ROW_MAJOR, ROW_MAJOR, wid=69)
+    first, again = run(q, g.Algo.AUTO), run(q, g.Algo.AUTO)
+    assert g.gemm_last_kernel() == "f32_skinny32_halves"
+    assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
+
+
+@pytest.mark.parametrize("shape,pad_b,ob", [((16, 4095, 4096), 0, ROW_MAJOR), ((16, 4094, 4096), 1, ROW_MAJOR),
+                                            ((16, 4096, 2048), 0, ROW_MAJOR), ((17, 4096, 4096), 0, ROW_MAJOR),
+                                            ((16, 4096, 4096), 0, COL_MAJOR)], ids=lambda v: str(v))
+def test_skinny_halves_not_taken(shape, pad_b, ob):
+    """Odd N, odd ldb (column pairs not 8-byte aligned), K below the split's minimum, two 16-row
+    strips, column-major B: 16-column blocks over the whole of K, as before."""
+    M, N, K = shape
+    p = gi.make_problem(M, N, K, "f32", ROW_MAJOR, ob, wid=70, pad_b=pad_b)
+    check(p, g.Algo.AUTO, key=("halves-not", shape, pad_b, ob))
+    assert g.gemm_last_kernel() == "f32_skinny16"
+
+
+def test_skinny_halves_through_the_workspace_call():
+    """A workspace does not change the choice where the 16-column blocks make one exact round."""
+    p = gi.make_problem(16, 4096, 4096, "f32", ROW_MAJOR, ROW_MAJOR, wid=71)
+    flat, need, kernel = run_ws(p)
+    assert need == 0 and kernel == "f32_skinny32_halves"
+    ref, D = oracle.gemm(p.M, p.N, p.K, p.A, p.lda, p.order_a, p.B, p.ldb, p.order_b)
+    assert oracle.normalised_error(logical_c(p, flat), ref, D) <= TOL["f32"]
+
+
 def test_skinny64_closed_forms():
     n = 1024
     perm = np.random.default_rng(11).permutation(n)
@@ -302,7 +363,7 @@ def test_skinny_rejects_unsupported(bad):
 
 
 @pytest.mark.parametrize("dtype,shape,kernel", [
-    ("f32", (16, 4096, 4096), "f32_skinny16"), ("bf16", (16, 4096, 4096), "bf16_skinny16"),
+    ("f32", (16, 4096, 4096), "f32_skinny32_halves"), ("bf16", (16, 4096, 4096), "bf16_skinny16"),
     ("f32", (256, 256, 256), "f32_skinny16"), ("f32", (1000, 1000, 1000), "f32_skinny64"),
     ("f32", (2048, 2048, 256), "f32_dma128x128"), ("f32", (2047, 2049, 255), "f32_dma128x128"),
     ("f32", (4095, 4097, 1023), "f32_dma256x256"), ("bf16", (4095, 4097, 1023), "bf16_dma256x256"),

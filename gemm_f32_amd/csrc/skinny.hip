@@ -9,9 +9,10 @@
 //
 //  * a workgroup owns 16 FN columns n0 .. and 16 FM rows m0 .. of C: FN = 4 (64 columns)
 //    when that still gives every CU a workgroup (1000 x 1000: 16 x 16), else FN = 1
-//    (16 x 4096: 256 workgroups of 16 x 16); FM = 4 (64 rows), or fewer when M is smaller
-//    or when fewer rows per block are needed to give every CU one (a 4095 x 1 column:
-//    256 blocks of 16 rows);
+//    (16 x 4096: 256 workgroups of 16 x 16); FN = 2 (32 columns, each lane two adjacent
+//    columns of a row-major FP32 B) only in the two-halves mode below; FM = 4 (64 rows), or
+//    fewer when M is smaller or when fewer rows per block are needed to give every CU one
+//    (a 4095 x 1 column: 256 blocks of 16 rows);
 //  * its 8 wavefronts split K among themselves (split-K inside the workgroup: batches of
 //    k-steps dealt in turn) and each streams its batches of those columns of B and of the
 //    FM 16-row strips of A (A stays in L2) straight from global memory into registers -- no LDS staging in
@@ -23,7 +24,8 @@
 //    of lanes is free as long as A and B use the same one, so lane l takes the 16-byte run
 //    of k that starts at 8 (l / 16) (BF16) or 4 (l / 16) (FP32) within each k-step;
 //  * the 8 partial products are summed through LDS in a fixed order (wave 0 + 1 + ... + 7):
-//    deterministic, no atomics, no workspace;
+//    deterministic, no workspace; only the two-halves mode then adds each workgroup's sum
+//    into a zeroed C with an atomic add (two contributions per output: still deterministic);
 //  * accumulator layout of a 16 x 16 result: lane l, register r holds row 4 (l / 16) + r,
 //    column l % 16.
 //
@@ -372,18 +374,17 @@ template <typename D> int batch_k(int fm, int fn) {
 }
 
 template <typename D, int FN, int WAVES, bool B_KC, bool BATCH>
-hipError_t launch_d(const KArg<BATCH>& p, const Launch& l, int fm, int kslice, int slices, float* part,
-                    int accum = 0) {
+hipError_t launch_d(const KArg<BATCH>& p, const Launch& l, int fm, int kslice, int slices, float* part) {
     const int slabs = (p.N + 16 * FN - 1) / (16 * FN), rblocks = (p.M + 16 * fm - 1) / (16 * fm);
     const dim3 grid((unsigned)(slabs * rblocks), (unsigned)slices, BATCH ? l.batch : 1), block(64 * WAVES);
     const int va = l.vec_a, vb = l.vec_b, vc = l.vec_c;
     // buffer offsets of a row-major B (rows up to K, plus 3 rows of one k-step's lane
     // spread) must fit in 31 bits
     const int bb = !B_KC && (int64_t)(p.K + 4) * p.ldb * 4 + (int64_t)p.N * 4 < ((int64_t)1 << 31);
-    if (fm == 1) hipLaunchKernelGGL((k_skinny<D, 1, FN, WAVES, B_KC, BATCH>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part, accum);
-    else if (fm == 2) hipLaunchKernelGGL((k_skinny<D, 2, FN, WAVES, B_KC, BATCH>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part, accum);
-    else if (fm == 3) hipLaunchKernelGGL((k_skinny<D, 3, FN, WAVES, B_KC, BATCH>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part, accum);
-    else hipLaunchKernelGGL((k_skinny<D, 4, FN, WAVES, B_KC, BATCH>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part, accum);
+    if (fm == 1) hipLaunchKernelGGL((k_skinny<D, 1, FN, WAVES, B_KC, BATCH>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part, 0);
+    else if (fm == 2) hipLaunchKernelGGL((k_skinny<D, 2, FN, WAVES, B_KC, BATCH>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part, 0);
+    else if (fm == 3) hipLaunchKernelGGL((k_skinny<D, 3, FN, WAVES, B_KC, BATCH>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part, 0);
+    else hipLaunchKernelGGL((k_skinny<D, 4, FN, WAVES, B_KC, BATCH>), grid, block, 0, l.stream, p, va, vb, vc, bb, kslice, part, 0);
     return hipGetLastError();
 }
 

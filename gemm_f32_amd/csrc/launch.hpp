@@ -75,6 +75,11 @@ constexpr int kSkinnyHalvesMinK = 4096;
 bool skinny_halves_ok(const Problem& p);
 bool skinny_halves_applies(const Problem& p, int cus);
 hipError_t launch_skinny_halves(const Problem& p, const Launch& l);
+// The same 32-column blocks over the whole of K with plain stores (no fill, no atomics), where
+// the 16-column blocks would take more than one round (N > 16 CUs) and K >= kSkinnyPairsMinK.
+constexpr int kSkinnyPairsMinK = 512;
+bool skinny_pairs_applies(const Problem& p, int cus);
+hipError_t launch_skinny_pairs(const Problem& p, const Launch& l);
 // C = 0 for K == 0 (fill.hip)
 hipError_t launch_zero_c(const Problem& p, const Launch& l);
 // Fused epilogue (epilogue.hpp): the 16-bit direct-copy kernel with the epilogue in its stores

@@ -521,6 +521,31 @@ bool skinny_halves_applies(const Problem& p, int cus) {
     return 2 * wgs >= c && wgs <= c;
 }
 
+// 32-column blocks over the whole of K (no split, plain stores): where the 16-column blocks would
+// take more than one round.  Operands from HBM, against those blocks: 16 x 8192 x 4096 51.5 ->
+// 31.7 us, 16 x 6144 x 4096 50.7 -> 31.2, 16 x 5120 x 4096 54.5 -> 31.7, 16 x 8192 x 512 10.0 ->
+// 7.7, 16 x 16384 x 4096 (two rounds either way) 58.6 -> 58.8; with exactly one round of
+// 16-column blocks (N = 4096) they lost (K = 3072: 18.9 -> 23.7 us).
+bool skinny_pairs_applies(const Problem& p, int cus) {
+    const int64_t c = cus > 0 ? cus : 256;
+    if (p.oa != kRow || p.ob != kRow || p.M < 1 || p.M > 16 || p.N < 2 || (p.N & 1) || (p.ldb & 1) ||
+        (reinterpret_cast<uintptr_t>(p.B) & 7) != 0 || p.K < kSkinnyPairsMinK || skinny_blocks(p, cus) != 1)
+        return false;
+    if ((int64_t)(p.K + 4) * p.ldb * 4 + (int64_t)p.N * 4 >= ((int64_t)1 << 31)) return false;
+    return (p.N + 15) / 16 > c;
+}
+
+hipError_t launch_skinny_pairs(const Problem& p, const Launch& l) {
+    if (p.oa != kRow || p.ob != kRow || p.M < 1 || p.M > 16 || p.N < 2 || (p.N & 1) || (p.ldb & 1) ||
+        (reinterpret_cast<uintptr_t>(p.B) & 7) != 0)
+        return hipErrorInvalidValue;
+    const int bb = (int64_t)(p.K + 4) * p.ldb * 4 + (int64_t)p.N * 4 < ((int64_t)1 << 31);
+    hipLaunchKernelGGL((k_skinny<F32, 1, 2, kSkinnyWaves, false, false>), dim3((unsigned)((p.N + 31) / 32), 1u),
+                       dim3(64 * kSkinnyWaves), 0, l.stream, p, (int)l.vec_a, (int)l.vec_b, (int)l.vec_c, bb, p.K,
+                       nullptr, 0);
+    return hipGetLastError();
+}
+
 hipError_t launch_skinny_halves(const Problem& p, const Launch& l) {
     if (!skinny_halves_ok(p)) return hipErrorInvalidValue;
     const hipError_t e = launch_zero_c(p, l);

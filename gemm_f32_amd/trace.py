@@ -68,6 +68,7 @@ SPECS = [
     ("skinny16x4096x4096_bf16@ws", ["--workload", "skinny16x4096x4096_bf16", "--workspace"], 30),
     ("fewcols16x1024x16384_f32@ws", ["--workload", "fewcols16x1024x16384_f32", "--workspace"], 30),
     ("fewcols16x1024x16384_bf16@ws", ["--workload", "fewcols16x1024x16384_bf16", "--workspace"], 30),
+    ("fewrows16x8192x4096_f32", ["--workload", "fewrows16x8192x4096_f32"], 30),
     ("shard4096x512x4096_f32", ["--workload", "shard4096x512x4096_f32"], 30),
     ("shard4096x512x4096_f32@ws", ["--workload", "shard4096x512x4096_f32", "--workspace"], 30),
     ("shard4096x512x4096_bf16", ["--workload", "shard4096x512x4096_bf16"], 30),

@@ -81,6 +81,8 @@ WORKLOADS = {
         # few columns of C and a long K: too few output blocks for the CUs (split-K's case)
         Workload("fewcols16x1024x16384_f32", 6, 16, 1024, 16384, "f32"),
         Workload("fewcols16x1024x16384_bf16", 6, 16, 1024, 16384, "bf16", ROW_MAJOR, COL_MAJOR),
+        # few rows and many columns: 16-column blocks of C would take two rounds of the CUs
+        Workload("fewrows16x8192x4096_f32", 6, 16, 8192, 4096, "f32"),
         # LLaMA-2-7B attention at 2K tokens, per head (32 heads of 128): the scores Q.K^T and the
         # scores times V as strided batches.  Q, K, V and the output are [tokens, heads, 128]
         # (leading dimension 4096, stride 128 per head); the scores are [heads, 2048, 2048].

@@ -103,7 +103,10 @@ typedef enum {
  *                      split of K; "A06", "The next two rungs"): C is zeroed, then one
  *                      workgroup per 32-column block and K half adds its sum into C (8-byte
  *                      loads along each row of B; exactly two contributions per output, so
- *                      the result does not depend on their order and repeats bit for bit);
+ *                      the result does not depend on their order and repeats bit for bit).
+ *                      Under the same conditions but with K >= 512 and N > 16 x CUs (16-column
+ *                      blocks would take more than one round), AUTO runs 32-column blocks over
+ *                      the whole of K instead, with plain stores;
  *   MFMA_DMA           the direct-copy kernels: operands copied global -> LDS as laid out in
  *                      memory by buffer loads straight into LDS, no register staging ("GEMM
  *                      Optimization", V3 staging), tile picked by the cost model.  FP32:

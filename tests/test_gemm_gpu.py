@@ -331,6 +331,29 @@ def test_skinny_halves_not_taken(shape, pad_b, ob):
     assert g.gemm_last_kernel() == "f32_skinny16"
 
 
+PAIRS_CASES = [((16, 8192, 4096), 0), ((1, 8192, 512), 0), ((13, 8190, 1025), 2), ((7, 9000, 5001), 0),
+               ((16, 5120, 777), 4)]
+
+
+@pytest.mark.parametrize("shape,pad", PAIRS_CASES, ids=lambda v: str(v))
+def test_skinny_pairs_random(shape, pad):
+    """Few FP32 rows whose 16-column blocks would take more than one round: 32-column blocks
+    over the whole of K, plain stores; ragged N and K, padded (even) ldb and padded C."""
+    M, N, K = shape
+    p = gi.make_problem(M, N, K, "f32", ROW_MAJOR, ROW_MAJOR, wid=72, pad_b=pad, pad_c=pad + 1)
+    check(p, g.Algo.AUTO, key=("pairs", shape, pad))
+    assert g.gemm_last_kernel() == "f32_skinny32"
+
+
+def test_skinny_pairs_small_integer_exact():
+    rng = np.random.default_rng(31)
+    M, N, K = 16, 8194, 1500
+    A = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    B = rng.integers(-4, 5, (K, N)).astype(np.float32)
+    check(gi.make_problem(M, N, K, "f32", ROW_MAJOR, ROW_MAJOR, A_logical=A, B_logical=B), g.Algo.AUTO, exact=True)
+    assert g.gemm_last_kernel() == "f32_skinny32"
+
+
 def test_skinny_halves_through_the_workspace_call():
     """A workspace does not change the choice where the 16-column blocks make one exact round."""
     p = gi.make_problem(16, 4096, 4096, "f32", ROW_MAJOR, ROW_MAJOR, wid=71)

@@ -153,8 +153,8 @@ const char* skinny_name(int et, int fn) {
 
 // FP32, few rows, row-major B: two K halves of 32-column blocks added into a zeroed C
 constexpr const char* kSkinnyHalvesName = "f32_skinny32_halves";
-// the same blocks over the whole of K where they alone fill the CUs
-constexpr const char* kSkinnyPairsName = "f32_skinny32";
+// 32-column blocks over the whole of K where 16-column blocks would take more than one round
+constexpr const char* kSkinnyPairsNames[3] = {"f32_skinny32", "bf16_skinny32", "f16_skinny32"};
 
 // A strided batch on the normalised problem (element strides; C's in floats); n == 1: one problem.
 struct Batch {
@@ -189,9 +189,9 @@ hipError_t run_skinny(const Problem& p, const Launch& l, int et, int cus, const 
         name = kSkinnyHalvesName;
         return launch_skinny_halves(p, l);
     }
-    if (choose && et == kElemF32 && l.batch == 1 && l.vec_a && skinny_pairs_applies(p, cus)) {
-        name = kSkinnyPairsName;
-        return launch_skinny_pairs(p, l);
+    if (choose && l.batch == 1 && l.vec_a && skinny_pairs_applies(p, et, cus)) {
+        name = kSkinnyPairsNames[et];
+        return launch_skinny_pairs(p, l, et);
     }
     const int fn = skinny_blocks(p, cus);
     name = skinny_name(et, fn);
@@ -599,7 +599,7 @@ hipError_t dispatch(const Problem& p, hipStream_t stream, gemm_algo_t algo, int 
         return run_b16_tiles(p, stream, GEMM_ALGO_MFMA_64x64, et, dev, name, st, b);
     if (algo == GEMM_ALGO_SKINNY || small) {
         if (!skinny_applies(p, true)) { st = GEMM_ERR_INVALID_VALUE; return hipSuccess; }
-        return run_skinny(p, l, et, dev.cus, name, algo == GEMM_ALGO_AUTO ? ws : Workspace{});
+        return run_skinny(p, l, et, dev.cus, name, algo == GEMM_ALGO_AUTO ? ws : Workspace{}, algo == GEMM_ALGO_AUTO);
     }
     return run_b16_tiles(p, stream, algo, et, dev, name, st, b, ws);
 }
@@ -648,7 +648,7 @@ const char* plan_auto(const Problem& p, int et, int cus, int& mc, int& nc) {
     if (et == kElemFp8) return fp8_name(plan_fp8(p, cus).opt);
     const bool small = prefer_small(p, cus) && skinny_applies(p, !f32);
     if (small && f32 && skinny_halves_applies(p, cus)) return kSkinnyHalvesName;
-    if (small && f32 && skinny_pairs_applies(p, cus)) return kSkinnyPairsName;
+    if (small && skinny_pairs_applies(p, et, cus) && (f32 || !small_tiles16(p, cus))) return kSkinnyPairsNames[et];
     if (small && (f32 || !small_tiles16(p, cus))) return skinny_name(et, skinny_blocks(p, cus));
     const Plan pl = f32 ? choose_f32_tiles(p, GEMM_ALGO_AUTO, cus)
                         : choose_bf16_tiles(p, small ? GEMM_ALGO_MFMA_64x64 : GEMM_ALGO_AUTO, cus);

@@ -78,8 +78,9 @@ hipError_t launch_skinny_halves(const Problem& p, const Launch& l);
 // The same 32-column blocks over the whole of K with plain stores (no fill, no atomics), where
 // the 16-column blocks would take more than one round (N > 16 CUs) and K >= kSkinnyPairsMinK.
 constexpr int kSkinnyPairsMinK = 512;
-bool skinny_pairs_applies(const Problem& p, int cus);
-hipError_t launch_skinny_pairs(const Problem& p, const Launch& l);
+// Also for a column-major B of any input type `et` (two plain 16-column blocks per workgroup).
+bool skinny_pairs_applies(const Problem& p, int et, int cus);
+hipError_t launch_skinny_pairs(const Problem& p, const Launch& l, int et);
 // C = 0 for K == 0 (fill.hip)
 hipError_t launch_zero_c(const Problem& p, const Launch& l);
 // Fused epilogue (epilogue.hpp): the 16-bit direct-copy kernel with the epilogue in its stores

@@ -526,23 +526,41 @@ bool skinny_halves_applies(const Problem& p, int cus) {
 // 31.7 us, 16 x 6144 x 4096 50.7 -> 31.2, 16 x 5120 x 4096 54.5 -> 31.7, 16 x 8192 x 512 10.0 ->
 // 7.7, 16 x 16384 x 4096 (two rounds either way) 58.6 -> 58.8; with exactly one round of
 // 16-column blocks (N = 4096) they lost (K = 3072: 18.9 -> 23.7 us).
-bool skinny_pairs_applies(const Problem& p, int cus) {
+// A row-major FP32 B read in column pairs needs an even N and ldb and an 8-byte aligned B; a
+// column-major B (any input type) takes two plain 16-column blocks per workgroup.
+static bool pairs_ok(const Problem& p, int et) {
+    if (p.oa != kRow || p.M < 1 || p.M > 16 || p.N < 2) return false;
+    if (p.ob == kCol) return true;
+    return et == kElemF32 && !(p.N & 1) && !(p.ldb & 1) && (reinterpret_cast<uintptr_t>(p.B) & 7) == 0;
+}
+
+bool skinny_pairs_applies(const Problem& p, int et, int cus) {
     const int64_t c = cus > 0 ? cus : 256;
-    if (p.oa != kRow || p.ob != kRow || p.M < 1 || p.M > 16 || p.N < 2 || (p.N & 1) || (p.ldb & 1) ||
-        (reinterpret_cast<uintptr_t>(p.B) & 7) != 0 || p.K < kSkinnyPairsMinK || skinny_blocks(p, cus) != 1)
-        return false;
-    if ((int64_t)(p.K + 4) * p.ldb * 4 + (int64_t)p.N * 4 >= ((int64_t)1 << 31)) return false;
+    if (!pairs_ok(p, et) || p.K < kSkinnyPairsMinK || skinny_blocks(p, cus) != 1) return false;
+    if (p.ob == kRow && (int64_t)(p.K + 4) * p.ldb * 4 + (int64_t)p.N * 4 >= ((int64_t)1 << 31)) return false;
     return (p.N + 15) / 16 > c;
 }
 
-hipError_t launch_skinny_pairs(const Problem& p, const Launch& l) {
-    if (p.oa != kRow || p.ob != kRow || p.M < 1 || p.M > 16 || p.N < 2 || (p.N & 1) || (p.ldb & 1) ||
-        (reinterpret_cast<uintptr_t>(p.B) & 7) != 0)
+hipError_t launch_skinny_pairs(const Problem& p, const Launch& l, int et) {
+    if (!pairs_ok(p, et)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((p.N + 31) / 32), 1u), block(64 * kSkinnyWaves);
+    const int va = l.vec_a, vb = l.vec_b, vc = l.vec_c;
+    if (p.ob == kRow) {
+        const int bb = (int64_t)(p.K + 4) * p.ldb * 4 + (int64_t)p.N * 4 < ((int64_t)1 << 31);
+        hipLaunchKernelGGL((k_skinny<F32, 1, 2, kSkinnyWaves, false, false>), grid, block, 0, l.stream, p, va, vb, vc,
+                           bb, p.K, nullptr, 0);
+    } else if (et == kElemBf16) {
+        hipLaunchKernelGGL((k_skinny<Bf16, 1, 2, kSkinnyWaves, true, false>), grid, block, 0, l.stream, p, va, vb, vc,
+                           0, p.K, nullptr, 0);
+    } else if (et == kElemF16) {
+        hipLaunchKernelGGL((k_skinny<F16, 1, 2, kSkinnyWaves, true, false>), grid, block, 0, l.stream, p, va, vb, vc,
+                           0, p.K, nullptr, 0);
+    } else if (et == kElemF32) {
+        hipLaunchKernelGGL((k_skinny<F32, 1, 2, kSkinnyWaves, true, false>), grid, block, 0, l.stream, p, va, vb, vc,
+                           0, p.K, nullptr, 0);
+    } else {
         return hipErrorInvalidValue;
-    const int bb = (int64_t)(p.K + 4) * p.ldb * 4 + (int64_t)p.N * 4 < ((int64_t)1 << 31);
-    hipLaunchKernelGGL((k_skinny<F32, 1, 2, kSkinnyWaves, false, false>), dim3((unsigned)((p.N + 31) / 32), 1u),
-                       dim3(64 * kSkinnyWaves), 0, l.stream, p, (int)l.vec_a, (int)l.vec_b, (int)l.vec_c, bb, p.K,
-                       nullptr, 0);
+    }
     return hipGetLastError();
 }
 

@@ -104,9 +104,11 @@ typedef enum {
  *                      workgroup per 32-column block and K half adds its sum into C (8-byte
  *                      loads along each row of B; exactly two contributions per output, so
  *                      the result does not depend on their order and repeats bit for bit).
- *                      Under the same conditions but with K >= 512 and N > 16 x CUs (16-column
- *                      blocks would take more than one round), AUTO runs 32-column blocks over
- *                      the whole of K instead, with plain stores;
+ *                      With M <= 16, K >= 512 and N > 16 x CUs (16-column blocks would take
+ *                      more than one round), AUTO runs one round of 32-column blocks over the
+ *                      whole of K instead, with plain stores: for a column-major B of any input
+ *                      type, and for a row-major FP32 B with N and ldb even and B 8-byte
+ *                      aligned;
  *   MFMA_DMA           the direct-copy kernels: operands copied global -> LDS as laid out in
  *                      memory by buffer loads straight into LDS, no register staging ("GEMM
  *                      Optimization", V3 staging), tile picked by the cost model.  FP32:

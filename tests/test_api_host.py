@@ -225,7 +225,7 @@ def test_tile_scheduler_is_a_bijection_with_xcd_blocks():
 
 # --- the default kernel choice, without a device (gemm_plan) -----------------------------
 KNOWN_KERNELS = {"f32_dma256x256", "f32_dma128x128", "f32_mfma128x128", "f32_mfma64x64",
-                 "f32_skinny16", "f32_skinny64", "f32_skinny32_halves", "f32_skinny32", "bf16_dma256x256", "bf16_dma256x128",
+                 "f32_skinny16", "f32_skinny64", "f32_skinny32_halves", "f32_skinny32", "bf16_skinny32", "bf16_dma256x256", "bf16_dma256x128",
                  "bf16_mfma256x128", "bf16_mfma128x128", "bf16_mfma64x64",
                  "bf16_skinny16", "bf16_skinny64", "zero_c", "none"}
 
@@ -254,6 +254,9 @@ KNOWN_KERNELS = {"f32_dma256x256", "f32_dma128x128", "f32_mfma128x128", "f32_mfm
     ("f32", (16, 5120, 512), (R, R, R), ("f32_skinny32", 16, 5120)),
     ("f32", (16, 8192, 511), (R, R, R), ("f32_skinny16", 16, 8192)),
     ("f32", (16, 8191, 4096), (R, R, R), ("f32_skinny16", 16, 8191)),
+    ("f32", (16, 8191, 4096), (R, C_, R), ("f32_skinny32", 16, 8191)),
+    ("bf16", (16, 8192, 1024), (R, C_, R), ("bf16_skinny32", 16, 8192)),
+    ("bf16", (16, 4096, 4096), (R, C_, R), ("bf16_skinny16", 16, 4096)),
     # 16-bit inputs: 64 x 64 register-staged tiles where the small-problem kernel's 64-column
     # blocks would leave CUs idle but the tiles fill at least half of them in one round (K <= 2048);
     # the small-problem kernel where its 64-column blocks fill the CUs, for longer K, few rows or

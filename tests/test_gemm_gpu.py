@@ -345,6 +345,17 @@ def test_skinny_pairs_random(shape, pad):
     assert g.gemm_last_kernel() == "f32_skinny32"
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("shape", [(16, 8192, 1024), (9, 8191, 777), (16, 5123, 2049)], ids=lambda s: "x".join(map(str, s)))
+def test_skinny_pairs_column_major_b(dtype, shape):
+    """The same one round of 32-column blocks for a column-major B: two plain 16-column blocks per
+    workgroup, any input type, odd N included (the last block's columns past N are clamped)."""
+    M, N, K = shape
+    p = gi.make_problem(M, N, K, dtype, ROW_MAJOR, COL_MAJOR, wid=73)
+    check(p, g.Algo.AUTO, key=("pairs-c", dtype, shape))
+    assert g.gemm_last_kernel() == f"{dtype}_skinny32"
+
+
 def test_skinny_pairs_small_integer_exact():
     rng = np.random.default_rng(31)
     M, N, K = 16, 8194, 1500
